@@ -1,0 +1,428 @@
+/*
+ * csa2_oracle.c -- plain, single-threaded CPU oracle for the CSA2 global branch.
+ *
+ * TEST INFRASTRUCTURE ONLY (see csa2_oracle.h).  Built with -O2 -ffp-contract=off and
+ * without fast-math so every fp32 operation below is one IEEE round-to-nearest op.
+ *
+ * What it computes, step by step, in the order the pages give it:
+ *   compressor pooling   [DF] §4.2 compressor equation; [ZB] §2.3.1 (no overlap, no
+ *                        absolute position embedding; m = 1 is per-token projection)
+ *   RoPE then quantise   [ZB] §2.4.4 (quantise after RoPE, same format for NoPE/RoPE)
+ *   main-KV FP4          [ZB] §2.4.4, [DF] §4.4-4.5: E2M1 with one E4M3 scale per 16
+ *   indexer-K            [ZB] §2.3.1 (indexer K projected from the main-KV entry),
+ *                        [DF] §4.4: MXFP4 = E2M1 with one E8M0 scale per 32
+ *   indexer scores       [ZB] §3.3.2 (indexer query with per-head weights)
+ *   block max / pool     [ZB] §2.3.4 (pad with -inf, amax over blocks of 8, newest
+ *                        block forced to +inf, expand selected blocks, truncate to width),
+ *                        [DF] §4.7 pool equations (g_r, TopM, union)
+ *   Top-K                [ZB] model table index_topk = 512
+ *   sparse attention     [ZB] §3.3.2.1 (key = value = c, one softmax over the selected
+ *                        entries joined with the SWA keys)
+ *
+ * Readings of points the pages leave open (each also listed in the design notes):
+ *   - pooling uses normalised weights a_i = w_i / sum(w), then sum a_i x_i (ascending i);
+ *     mathematically the compressor equation, and equal weights give exactly the mean.
+ *   - RoPE on channels 448..511 in adjacent pairs (448+2i, 449+2i), angle from a table.
+ *   - E4M3 scale = nearest-even E4M3 of fp32(amax / 6), saturating at 448; S = 0 -> all
+ *     codes 0.  Element code = grid point nearest to |e| / S (exact), ties to even code,
+ *     saturating at 6; sign bit only on a non-zero code.
+ *   - E8M0 scale code = floor(log2 amax) - 2 + 127 clamped to [0, 254]; amax = 0 -> 0.
+ *   - indexer K = ascending fmaf chain over the 512 post-RoPE fp32 channels.
+ *   - score = sum_h w_h * max(0, q_h . k): the lightning-indexer form; no extra scale.
+ *   - ties in block and entry selection go to the lower index; NaN ranks as -inf.
+ *   - attention logit = scale * q_h . key over all 512 dims; value = the same key.
+ */
+#include "csa2_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define D_LAT 512
+#define D_ROPE 64
+#define D_NOPE (D_LAT - D_ROPE)
+#define IDX_HEADS 32
+#define IDX_DIM 128
+#define N_HEADS 64
+#define KV_BYTES 288
+#define IDX_BYTES 68
+
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+int64_t csa2o_entry_bytes(int64_t D, int64_t G) { return D / 2 + D / G; }
+
+static float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* ------------------------------------------------------------------ formats */
+
+double csa2o_e2m1_value(int code4) {
+  double v = kE2M1[code4 & 7];
+  return (code4 & 8) ? -v : v;
+}
+
+double csa2o_e4m3_value(int byte) {
+  int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+  if (e == 15 && m == 7) return NAN;
+  /* normal: (1 + m/8) 2^(e-7); subnormal: (m/8) 2^(-6) */
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+double csa2o_e8m0_value(int byte) {
+  if ((byte & 255) == 255) return NAN;
+  return ldexp(1.0, (byte & 255) - 127);
+}
+
+/* Nearest non-negative E4M3 value by scanning every finite code, ties to the even code. */
+int csa2o_e4m3_encode(double x) {
+  if (!(x < 448.0)) return 0x7E; /* saturate (also +inf / NaN) */
+  if (x <= 0.0) return 0x00;
+  int best = 0;
+  double bestd = INFINITY;
+  for (int c = 0; c <= 0x7E; c++) {
+    double d = fabs(x - csa2o_e4m3_value(c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* Nearest grid point g*S to |e| over g in {0,0.5,1,1.5,2,3,4,6}, ties to the even code. */
+int csa2o_e2m1_encode(float e, double S) {
+  if (!(S > 0.0)) return 0;
+  double a = fabs((double)e);
+  int best = 0;
+  if (a >= 6.0 * S) {
+    best = 7;
+  } else {
+    double bestd = INFINITY;
+    for (int c = 0; c < 8; c++) {
+      double d = fabs(a - kE2M1[c] * S);
+      if (d < bestd || (d == bestd && (c & 1) == 0)) {
+        best = c;
+        bestd = d;
+      }
+    }
+  }
+  return (e < 0.0f && best != 0) ? (best | 8) : best;
+}
+
+int csa2o_e8m0_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ex;
+  frexpf(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+  int code = (ex - 1) - 2 + 127;
+  if (code < 0) code = 0;
+  if (code > 254) code = 254;
+  return code;
+}
+
+/* ------------------------------------------------------------------ RoPE table */
+
+void csa2o_rope_table(const int64_t *pos, int64_t n, double theta, float *out) {
+  for (int64_t j = 0; j < n; j++) {
+    for (int i = 0; i < D_ROPE / 2; i++) {
+      double inv_freq = pow(theta, -(double)(2 * i) / (double)D_ROPE);
+      double ang = (double)pos[j] * inv_freq;
+      out[j * D_ROPE + i] = (float)cos(ang);
+      out[j * D_ROPE + D_ROPE / 2 + i] = (float)sin(ang);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ stage 1 */
+
+static void pack_nibbles(const int *codes, int n, uint8_t *dst) {
+  for (int b = 0; b < n / 2; b++) dst[b] = (uint8_t)((codes[2 * b] & 15) | ((codes[2 * b + 1] & 15) << 4));
+}
+
+void csa2o_compress_pack(const uint16_t *latent, int64_t n_entries, int m, const float *pool_w,
+                         const float *rope_cs, const uint16_t *w_idx, uint8_t *kv_out,
+                         uint8_t *idx_out, float *pooled, float *rotated, float *kproj) {
+  float c[D_LAT];
+  float k[IDX_DIM];
+  int codes[D_LAT];
+  for (int64_t j = 0; j < n_entries; j++) {
+    /* a1: c_j[ch] = sum_i a_i[ch] x_{m j + i}[ch], a_i = w_i / sum_i' w_i' */
+    for (int ch = 0; ch < D_LAT; ch++) {
+      const uint16_t *x = latent + (j * m) * D_LAT + ch;
+      if (m == 1) {
+        c[ch] = bf16_to_f32(x[0]);
+      } else {
+        float wsum = pool_w[ch];
+        for (int i = 1; i < m; i++) wsum = wsum + pool_w[i * D_LAT + ch];
+        float acc = (pool_w[ch] / wsum) * bf16_to_f32(x[0]);
+        for (int i = 1; i < m; i++) acc = acc + (pool_w[i * D_LAT + ch] / wsum) * bf16_to_f32(x[i * D_LAT]);
+        c[ch] = acc;
+      }
+    }
+    if (pooled) memcpy(pooled + j * D_LAT, c, sizeof c);
+
+    /* a2: rotate the 64-channel rope tail in adjacent pairs */
+    const float *cs = rope_cs + j * D_ROPE;
+    for (int i = 0; i < D_ROPE / 2; i++) {
+      float x0 = c[D_NOPE + 2 * i], x1 = c[D_NOPE + 2 * i + 1];
+      float co = cs[i], si = cs[D_ROPE / 2 + i];
+      float t0 = x0 * co, t1 = x1 * si, t2 = x0 * si, t3 = x1 * co;
+      c[D_NOPE + 2 * i] = t0 - t1;
+      c[D_NOPE + 2 * i + 1] = t2 + t3;
+    }
+    if (rotated) memcpy(rotated + j * D_LAT, c, sizeof c);
+
+    /* a3: main KV, 32 groups of 16 channels, E4M3 scale + E2M1 codes */
+    uint8_t *kv = kv_out + j * KV_BYTES;
+    for (int g = 0; g < D_LAT / 16; g++) {
+      float amax = 0.0f;
+      for (int i = 0; i < 16; i++) {
+        float a = fabsf(c[16 * g + i]);
+        if (a > amax) amax = a;
+      }
+      float s_raw = amax / 6.0f;
+      int sc = csa2o_e4m3_encode((double)s_raw);
+      double S = csa2o_e4m3_value(sc);
+      kv[256 + g] = (uint8_t)sc;
+      for (int i = 0; i < 16; i++) codes[16 * g + i] = csa2o_e2m1_encode(c[16 * g + i], S);
+    }
+    pack_nibbles(codes, D_LAT, kv);
+
+    /* a4: indexer K = W_idx c (ascending fmaf chain), then MXFP4 in 4 groups of 32 */
+    for (int o = 0; o < IDX_DIM; o++) {
+      float acc = 0.0f;
+      for (int ch = 0; ch < D_LAT; ch++) acc = fmaf(bf16_to_f32(w_idx[o * D_LAT + ch]), c[ch], acc);
+      k[o] = acc;
+    }
+    if (kproj) memcpy(kproj + j * IDX_DIM, k, sizeof k);
+    uint8_t *ix = idx_out + j * IDX_BYTES;
+    for (int g = 0; g < IDX_DIM / 32; g++) {
+      float amax = 0.0f;
+      for (int i = 0; i < 32; i++) {
+        float a = fabsf(k[32 * g + i]);
+        if (a > amax) amax = a;
+      }
+      int sc = csa2o_e8m0_scale_code(amax);
+      double X = csa2o_e8m0_value(sc);
+      ix[64 + g] = (uint8_t)sc;
+      for (int i = 0; i < 32; i++) codes[32 * g + i] = csa2o_e2m1_encode(k[32 * g + i], X);
+    }
+    pack_nibbles(codes, IDX_DIM, ix);
+  }
+}
+
+void csa2o_dequant_kv(const uint8_t *e, double *out) {
+  for (int ch = 0; ch < D_LAT; ch++) {
+    int code = (e[ch / 2] >> (4 * (ch & 1))) & 15;
+    out[ch] = csa2o_e2m1_value(code) * csa2o_e4m3_value(e[256 + ch / 16]);
+  }
+}
+
+void csa2o_dequant_idx(const uint8_t *e, double *out) {
+  for (int ch = 0; ch < IDX_DIM; ch++) {
+    int code = (e[ch / 2] >> (4 * (ch & 1))) & 15;
+    out[ch] = csa2o_e2m1_value(code) * csa2o_e8m0_value(e[64 + ch / 32]);
+  }
+}
+
+/* ------------------------------------------------------------------ stage 2 */
+
+static double index_score_one(const uint16_t *q, const float *w, const uint8_t *entry) {
+  double k[IDX_DIM];
+  csa2o_dequant_idx(entry, k);
+  double s = 0.0;
+  for (int h = 0; h < IDX_HEADS; h++) {
+    double dot = 0.0;
+    for (int d = 0; d < IDX_DIM; d++) dot += (double)bf16_to_f32(q[h * IDX_DIM + d]) * k[d];
+    if (dot > 0.0) s += (double)w[h] * dot; /* ReLU, then the per-head weight */
+  }
+  return s;
+}
+
+void csa2o_index_score(const uint16_t *q_idx, const float *head_w, const uint8_t *idx_cache,
+                       const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
+                       int32_t M, int32_t n_q, int32_t width, float *scores) {
+  for (int32_t t = 0; t < n_q; t++) {
+    const uint16_t *q = q_idx + (int64_t)t * IDX_HEADS * IDX_DIM;
+    const float *w = head_w + (int64_t)t * IDX_HEADS;
+    float *row = scores + (int64_t)t * width;
+    for (int32_t p = 0; p < width; p++) row[p] = -INFINITY;
+    int32_t nvis = q_nvis[t];
+    if (!pool_blocks) {
+      for (int32_t j = 0; j < nvis && j < width; j++)
+        row[j] = (float)index_score_one(q, w, idx_cache + (q_base[t] + j) * IDX_BYTES);
+    } else {
+      for (int32_t slot = 0; slot < M; slot++) {
+        int32_t b = pool_blocks[(int64_t)t * M + slot];
+        if (b < 0) continue;
+        for (int o = 0; o < 8; o++) {
+          int64_t j = (int64_t)b * 8 + o;
+          if (j >= nvis || slot * 8 + o >= width) continue;
+          row[slot * 8 + o] = (float)index_score_one(q, w, idx_cache + (q_base[t] + j) * IDX_BYTES);
+        }
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ stage 3 */
+
+typedef struct {
+  double key; /* score, NaN mapped to -inf */
+  int64_t id; /* block id or entry id (for the tie rule) */
+} ranked_t;
+
+/* descending key, then ascending id */
+static int cmp_rank(const void *a, const void *b) {
+  const ranked_t *x = (const ranked_t *)a, *y = (const ranked_t *)b;
+  if (x->key > y->key) return -1;
+  if (x->key < y->key) return 1;
+  return (x->id < y->id) ? -1 : (x->id > y->id);
+}
+
+static int cmp_i32(const void *a, const void *b) {
+  int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+  return (x < y) ? -1 : (x > y);
+}
+
+static double rank_key(float s) { return isnan(s) ? -INFINITY : (double)s; }
+
+/* take the first min(n, K) of a ranked list, write their ids ascending, pad with -1 */
+static void emit_sorted(ranked_t *r, int64_t n, int32_t K, int32_t *out) {
+  qsort(r, (size_t)n, sizeof *r, cmp_rank);
+  int32_t take = (int32_t)(n < K ? n : K);
+  for (int32_t i = 0; i < take; i++) out[i] = (int32_t)r[i].id;
+  qsort(out, (size_t)take, sizeof *out, cmp_i32);
+  for (int32_t i = take; i < K; i++) out[i] = -1;
+}
+
+void csa2o_block_topk(const float *scores, int32_t n_q, int32_t width, const int32_t *q_nvis,
+                      const int32_t *pool_blocks, int32_t block, int32_t M, int32_t K,
+                      int32_t *pool_out, int32_t *topk_out) {
+  int32_t *pool = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1));
+  ranked_t *cand = (ranked_t *)malloc(sizeof(ranked_t) * (size_t)(width > 0 ? width : 1));
+  for (int32_t t = 0; t < n_q; t++) {
+    const float *row = scores + (int64_t)t * width;
+    int32_t nvis = q_nvis[t];
+    int64_t nc = 0;
+    if (!pool_blocks) {
+      if (nvis > width) nvis = width; /* a row holds at most width scores */
+      /* g_r = max of block r over visible positions (padding = -inf) */
+      int32_t nb = (nvis + block - 1) / block;
+      ranked_t *g = (ranked_t *)malloc(sizeof(ranked_t) * (size_t)(nb > 0 ? nb : 1));
+      for (int32_t r = 0; r < nb; r++) {
+        double mx = -INFINITY;
+        for (int32_t o = 0; o < block; o++) {
+          int32_t j = r * block + o;
+          double v = (j < nvis) ? rank_key(row[j]) : -INFINITY;
+          if (v > mx) mx = v;
+        }
+        g[r].key = mx;
+        g[r].id = r;
+      }
+      if (nb > 0) g[nb - 1].key = INFINITY; /* the newest block always takes a slot */
+      emit_sorted(g, nb, M, pool);
+      free(g);
+      if (pool_out) memcpy(pool_out + (int64_t)t * M, pool, sizeof(int32_t) * (size_t)M);
+      /* pool = union of selected blocks, truncated to the visible width */
+      for (int32_t s = 0; s < M; s++) {
+        if (pool[s] < 0) continue;
+        for (int32_t o = 0; o < block; o++) {
+          int32_t j = pool[s] * block + o;
+          if (j >= nvis) continue;
+          cand[nc].key = rank_key(row[j]);
+          cand[nc].id = j;
+          nc++;
+        }
+      }
+    } else {
+      const int32_t *pb = pool_blocks + (int64_t)t * M;
+      for (int32_t s = 0; s < M; s++) {
+        if (pb[s] < 0) continue;
+        for (int32_t o = 0; o < block; o++) {
+          int64_t j = (int64_t)pb[s] * block + o;
+          if (j >= nvis || s * block + o >= width) continue;
+          cand[nc].key = rank_key(row[s * block + o]);
+          cand[nc].id = j;
+          nc++;
+        }
+      }
+    }
+    emit_sorted(cand, nc, K, topk_out + (int64_t)t * K);
+  }
+  free(cand);
+  free(pool);
+}
+
+void csa2o_topk_bruteforce(const float *scores, int32_t n_q, int32_t width, const int32_t *q_nvis,
+                           int32_t K, int32_t *topk_out) {
+  ranked_t *cand = (ranked_t *)malloc(sizeof(ranked_t) * (size_t)(width > 0 ? width : 1));
+  for (int32_t t = 0; t < n_q; t++) {
+    int32_t n = q_nvis[t] < width ? q_nvis[t] : width;
+    for (int32_t j = 0; j < n; j++) {
+      cand[j].key = rank_key(scores[(int64_t)t * width + j]);
+      cand[j].id = j;
+    }
+    emit_sorted(cand, n, K, topk_out + (int64_t)t * K);
+  }
+  free(cand);
+}
+
+/* ------------------------------------------------------------------ stage 4 */
+
+void csa2o_sparse_attn(const uint16_t *q, const uint8_t *kv_cache, const int64_t *q_base,
+                       const int32_t *topk, int32_t K, const uint16_t *swa,
+                       const int64_t *swa_start, const int32_t *swa_len, float scale,
+                       float *out, float *lse, int32_t n_q) {
+  int32_t cap = K + 128;
+  double *keys = (double *)malloc(sizeof(double) * (size_t)cap * D_LAT);
+  double *logit = (double *)malloc(sizeof(double) * (size_t)cap);
+  double o[D_LAT];
+  for (int32_t t = 0; t < n_q; t++) {
+    /* gather: selected entries (dequantised exactly), then the window rows */
+    int32_t nk = 0;
+    for (int32_t i = 0; i < K; i++) {
+      int32_t id = topk[(int64_t)t * K + i];
+      if (id < 0) continue;
+      csa2o_dequant_kv(kv_cache + (q_base[t] + id) * KV_BYTES, keys + (int64_t)nk * D_LAT);
+      nk++;
+    }
+    int32_t nw = swa_len[t] < 128 ? swa_len[t] : 128;
+    for (int32_t r = 0; r < nw; r++) {
+      const uint16_t *row = swa + (swa_start[t] + r) * D_LAT;
+      for (int d = 0; d < D_LAT; d++) keys[(int64_t)nk * D_LAT + d] = (double)bf16_to_f32(row[d]);
+      nk++;
+    }
+    for (int h = 0; h < N_HEADS; h++) {
+      const uint16_t *qh = q + ((int64_t)t * N_HEADS + h) * D_LAT;
+      float *oh = out + ((int64_t)t * N_HEADS + h) * D_LAT;
+      if (nk == 0) {
+        for (int d = 0; d < D_LAT; d++) oh[d] = 0.0f;
+        if (lse) lse[(int64_t)t * N_HEADS + h] = -INFINITY;
+        continue;
+      }
+      double mx = -INFINITY;
+      for (int32_t k = 0; k < nk; k++) {
+        double dot = 0.0;
+        for (int d = 0; d < D_LAT; d++) dot += (double)bf16_to_f32(qh[d]) * keys[(int64_t)k * D_LAT + d];
+        logit[k] = (double)scale * dot;
+        if (logit[k] > mx) mx = logit[k];
+      }
+      double z = 0.0;
+      for (int d = 0; d < D_LAT; d++) o[d] = 0.0;
+      for (int32_t k = 0; k < nk; k++) {
+        double p = exp(logit[k] - mx);
+        z += p;
+        for (int d = 0; d < D_LAT; d++) o[d] += p * keys[(int64_t)k * D_LAT + d];
+      }
+      for (int d = 0; d < D_LAT; d++) oh[d] = (float)(o[d] / z);
+      if (lse) lse[(int64_t)t * N_HEADS + h] = (float)(mx + log(z));
+    }
+  }
+  free(logit);
+  free(keys);
+}
