@@ -1,0 +1,199 @@
+"""Thin Python binding over libcsa2.so (the C ABI declared in include/csa2.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels.  Tensors are
+torch tensors on the ROCm device; calls are enqueued on torch's current stream (or the
+stream passed in).  There is no CPU fallback: if libcsa2.so is missing or cannot be
+loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libcsa2.so not built at {LIB_PATH}: run `python -m fp4_kv_cache_csa2_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_L = ctypes.CDLL(LIB_PATH)
+_vp, _i32, _i64, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                     ctypes.c_double, ctypes.c_size_t)
+_L.csa2_abi_version.restype = ctypes.c_int
+_L.csa2_status_string.argtypes = [ctypes.c_int]
+_L.csa2_status_string.restype = ctypes.c_char_p
+_L.csa2_rope_table.argtypes = [_vp, _i64, _f64, _vp]
+_L.csa2_compress_pack.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
+_L.csa2_index_score.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+_L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
+_L.csa2_block_topk_workspace.restype = _sz
+_L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+_L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32]
+_L.csa2_sparse_attn_workspace.restype = _sz
+_L.csa2_sparse_attn.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp, _sz, _vp]
+
+SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_compress_pack",
+           "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
+           "csa2_sparse_attn_workspace", "csa2_sparse_attn")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+DEFAULT_SCALE = 512 ** -0.5
+ROPE_THETA = 160000.0
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({_L.csa2_status_string(status).decode()})")
+        self.status = status
+
+
+def _check(fn: str, st: int) -> None:
+    if st != OK:
+        raise Csa2Error(fn, st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def abi_version() -> int:
+    return _L.csa2_abi_version()
+
+
+def rope_table(pos, theta: float = ROPE_THETA) -> torch.Tensor:
+    """Host cos/sin table [n, 64] (fp32, CPU tensor) for entry positions `pos` (CPU int64)."""
+    pos = torch.as_tensor(pos, dtype=torch.int64).contiguous()
+    out = torch.empty((pos.numel(), 64), dtype=torch.float32)
+    _check("csa2_rope_table", _L.csa2_rope_table(_ptr(pos), pos.numel(), float(theta), _ptr(out)))
+    return out
+
+
+def compress_pack(latent, m: int, pool_w, rope_cs, w_idx, kv_out=None, idx_out=None, stream=None):
+    """latent bf16 [n*m, 512] -> (kv uint8 [n, 288], idx uint8 [n, 68]); outputs may be given."""
+    _dev(latent, torch.bfloat16, "latent", 2)
+    n = latent.shape[0] // m
+    _dev(pool_w, torch.float32, "pool_w")
+    _dev(rope_cs, torch.float32, "rope_cs", 2)
+    _dev(w_idx, torch.bfloat16, "w_idx", 2)
+    if kv_out is None:
+        kv_out = torch.empty((n, 288), dtype=torch.uint8, device=latent.device)
+    if idx_out is None:
+        idx_out = torch.empty((n, 68), dtype=torch.uint8, device=latent.device)
+    _dev(kv_out, torch.uint8, "kv_out")
+    _dev(idx_out, torch.uint8, "idx_out")
+    if rope_cs.shape[0] < n or kv_out.numel() < n * 288 or idx_out.numel() < n * 68:
+        raise ValueError("output / table too small")
+    _check("csa2_compress_pack", _L.csa2_compress_pack(
+        _ptr(latent), n, m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_out), _ptr(idx_out),
+        _stream(stream)))
+    return kv_out, idx_out
+
+
+def index_score(q_idx, head_w, idx_cache, q_base, q_nvis, width: int, pool_blocks=None,
+                scores=None, block_max=None, want_block_max: bool = True, stream=None):
+    """Indexer scores [n_q, width] (+ block maxima [n_q, ceil(width/8)] in Full mode)."""
+    _dev(q_idx, torch.bfloat16, "q_idx", 3)
+    _dev(head_w, torch.float32, "head_w", 2)
+    _dev(idx_cache, torch.uint8, "idx_cache")
+    _dev(q_base, torch.int64, "q_base", 1)
+    _dev(q_nvis, torch.int32, "q_nvis", 1)
+    _dev(pool_blocks, torch.int32, "pool_blocks", 2)
+    n_q = q_idx.shape[0]
+    M = 0 if pool_blocks is None else pool_blocks.shape[1]
+    dev = q_idx.device
+    if scores is None:
+        scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
+    if block_max is None and want_block_max and pool_blocks is None:
+        block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
+    _dev(scores, torch.float32, "scores")
+    _dev(block_max, torch.float32, "block_max")
+    _check("csa2_index_score", _L.csa2_index_score(
+        _ptr(q_idx), _ptr(head_w), _ptr(idx_cache), _ptr(q_base), _ptr(q_nvis), _ptr(pool_blocks),
+        M, n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
+    return scores, block_max
+
+
+def block_topk_workspace(n_q: int, width: int, M: int, K: int) -> int:
+    return int(_L.csa2_block_topk_workspace(n_q, width, M, K))
+
+
+def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool_blocks=None,
+               want_pool: bool = True, pool_out=None, topk_out=None, workspace=None, stream=None):
+    """(pool [n_q, M] or None, topk [n_q, K]): Full mode when pool_blocks is None."""
+    _dev(scores, torch.float32, "scores", 2)
+    _dev(q_nvis, torch.int32, "q_nvis", 1)
+    _dev(block_max, torch.float32, "block_max")
+    _dev(pool_blocks, torch.int32, "pool_blocks", 2)
+    n_q, width = scores.shape
+    dev = scores.device
+    if pool_blocks is not None:
+        M = pool_blocks.shape[1]
+        want_pool = False
+    if pool_out is None and want_pool:
+        pool_out = torch.empty((n_q, M), dtype=torch.int32, device=dev)
+    if topk_out is None:
+        topk_out = torch.empty((n_q, K), dtype=torch.int32, device=dev)
+    _dev(pool_out, torch.int32, "pool_out")
+    _dev(topk_out, torch.int32, "topk_out")
+    need = 0 if pool_blocks is not None else block_topk_workspace(n_q, width, M, K)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_block_topk", _L.csa2_block_topk(
+        _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(pool_blocks), 8, M, K,
+        _ptr(pool_out), _ptr(topk_out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return pool_out, topk_out
+
+
+def sparse_attn_workspace(n_q: int, K: int) -> int:
+    return int(_L.csa2_sparse_attn_workspace(n_q, K))
+
+
+def sparse_attn(q, kv_cache, q_base, topk, swa, swa_start, swa_len, scale: float = DEFAULT_SCALE,
+                out=None, lse=None, want_lse: bool = True, workspace=None, stream=None):
+    """Attention output fp32 [n_q, 64, 512] (+ lse [n_q, 64])."""
+    _dev(q, torch.bfloat16, "q", 3)
+    _dev(kv_cache, torch.uint8, "kv_cache")
+    _dev(q_base, torch.int64, "q_base", 1)
+    _dev(topk, torch.int32, "topk", 2)
+    _dev(swa, torch.bfloat16, "swa", 2)
+    _dev(swa_start, torch.int64, "swa_start", 1)
+    _dev(swa_len, torch.int32, "swa_len", 1)
+    n_q = q.shape[0]
+    K = topk.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_q, 64, 512), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
+    _dev(out, torch.float32, "out")
+    _dev(lse, torch.float32, "lse")
+    need = sparse_attn_workspace(n_q, K)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_sparse_attn", _L.csa2_sparse_attn(
+        _ptr(q), _ptr(kv_cache), _ptr(q_base), _ptr(topk), K, _ptr(swa), _ptr(swa_start), _ptr(swa_len),
+        float(scale), _ptr(out), _ptr(lse), n_q, _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse

@@ -1,0 +1,234 @@
+// compress_pack.hip -- compressor pooling, RoPE, main-KV FP4 pack, indexer-K projection
+// and MXFP4 pack, one fused kernel for gfx950.
+//
+// Follows [DF] "CSA2 与每 token 890 字节" §4.2 (compressor equation) and §4.4 (entry
+// formats); [ZB] "把 KV Cache 压缩推到极致" §2.3.1 (indexer K projected from the main-KV
+// entry) and §2.4.4 (RoPE then quantise; E2M1 with one E4M3 scale per 16 channels).
+//
+// Bit-exactness: every fp32 step is a single IEEE round-to-nearest operation in a fixed
+// order (contraction is off in this file, divisions are correctly rounded, the
+// projection is an explicit ascending fma chain), and the quantisers decide codes by
+// exact comparisons, so the packed bytes do not depend on instruction scheduling.
+#include "csa2_device.hpp"
+
+#pragma clang fp contract(off)
+
+namespace csa2 {
+namespace {
+
+constexpr int kEnt = 16;  // entries per workgroup
+constexpr int kThreads = 256;
+
+// Nearest-even E4M3 code of x >= 0, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  if (!(x < 448.0f)) return 0x7E;
+  if (x < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (code 8 is 2^-6)
+    return (uint32_t)__builtin_rintf(x * 512.0f);
+  }
+  const int E = (int)((__float_as_uint(x) >> 23) & 255) - 127;  // x is a normal fp32
+  const float r = __builtin_rintf(__builtin_ldexpf(x, 3 - E));   // [8, 16], ties to even
+  const uint32_t code = ((uint32_t)(E + 7) << 3) + ((uint32_t)r - 8u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E2M1 code of e on the grid {0,.5,1,1.5,2,3,4,6} * S by exact midpoint comparisons,
+// ties to the even code, saturating at 6; the sign bit only on a non-zero code.
+__device__ __forceinline__ uint32_t e2m1_encode(float e, float S) {
+  if (!(S > 0.0f)) return 0;
+  const float a = __builtin_fabsf(e);
+  uint32_t c = (a > 0.25f * S) + (a > 0.75f * S) + (a > 1.25f * S) + (a > 1.75f * S) +
+               (a > 2.5f * S) + (a > 3.5f * S) + (a > 5.0f * S);
+  c += (a == 0.75f * S) + (a == 1.75f * S) + (a == 3.5f * S);  // odd-side ties round up
+  return (e < 0.0f && c != 0) ? (c | 8u) : c;
+}
+
+// OCP MX shared-scale rule for E2M1 elements: floor(log2 amax) - 2 + 127, clamped.
+__device__ __forceinline__ uint32_t e8m0_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int eb = (int)((__float_as_uint(amax) >> 23) & 255);  // 0 for subnormal amax
+  const int code = eb == 0 ? 0 : eb - 2;
+  return (uint32_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
+}
+
+__global__ __launch_bounds__(kThreads) void compress_pack_kernel(
+    const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
+    const float* __restrict__ rope_cs, const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out,
+    uint8_t* __restrict__ idx_out) {
+  __shared__ float s_c[kEnt][kD];          // rotated fp32 entries
+  __shared__ float s_k[kEnt][kIdxDim];     // projected indexer keys
+  const int t = threadIdx.x;
+  const int64_t j0 = (int64_t)blockIdx.x * kEnt;
+
+  // ---- phase A: pooling, RoPE, main-KV pack.  thread -> (entry e, channels 32p..32p+31)
+  {
+    const int e = t >> 4, p = t & 15;
+    const int64_t j = j0 + e;
+    if (j < n_entries) {
+      float c[32];
+      const int ch0 = 32 * p;
+      if (m == 1) {
+        const uint4* src = reinterpret_cast<const uint4*>(latent + j * kD + ch0);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const uint4 u = src[v];
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            c[8 * v + 2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
+            c[8 * v + 2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
+          }
+        }
+      } else {
+        // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
+        const uint4* s0 = reinterpret_cast<const uint4*>(latent + (2 * j) * kD + ch0);
+        const uint4* s1 = reinterpret_cast<const uint4*>(latent + (2 * j + 1) * kD + ch0);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const uint4 u0 = s0[v], u1 = s1[v];
+          const uint32_t a4[4] = {u0.x, u0.y, u0.z, u0.w};
+          const uint32_t b4[4] = {u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+          for (int q = 0; q < 8; q++) {
+            const int ch = ch0 + 8 * v + q;
+            const float w0 = pool_w[ch], w1 = pool_w[kD + ch];
+            const float ws = w0 + w1;
+            const float a0 = w0 / ws, a1 = w1 / ws;
+            const uint32_t xa = (q & 1) ? (a4[q >> 1] >> 16) : (a4[q >> 1] & 0xFFFFu);
+            const uint32_t xb = (q & 1) ? (b4[q >> 1] >> 16) : (b4[q >> 1] & 0xFFFFu);
+            const float p0 = a0 * bf16_bits_to_f32(xa);
+            const float p1 = a1 * bf16_bits_to_f32(xb);
+            c[8 * v + q] = p0 + p1;
+          }
+        }
+      }
+      if (p >= kDNope / 32) {  // rope tail: pairs (448+2i, 449+2i)
+        const float* cs = rope_cs + j * kDRope;
+        const int i0 = (ch0 - kDNope) / 2;
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+          const float x0 = c[2 * q], x1 = c[2 * q + 1];
+          const float co = cs[i0 + q], si = cs[kDRope / 2 + i0 + q];
+          const float t0 = x0 * co, t1 = x1 * si, t2 = x0 * si, t3 = x1 * co;
+          c[2 * q] = t0 - t1;
+          c[2 * q + 1] = t2 + t3;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 32; q++) s_c[e][ch0 + q] = c[q];
+
+      // two groups of 16 channels: E4M3 scale + E2M1 codes
+      uint32_t pay[4];
+      uint32_t scl = 0;
+#pragma unroll
+      for (int g = 0; g < 2; g++) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; q++) amax = __builtin_fmaxf(amax, __builtin_fabsf(c[16 * g + q]));
+        const uint32_t sb = e4m3_encode(amax / 6.0f);
+        const float S = e4m3_value(sb);
+        scl |= sb << (8 * g);
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int q = 0; q < 8; q++) word |= e2m1_encode(c[16 * g + 8 * w + q], S) << (4 * q);
+          pay[2 * g + w] = word;
+        }
+      }
+      uint8_t* dst = kv_out + j * kKvBytes;
+      *reinterpret_cast<uint4*>(dst + 16 * p) = make_uint4(pay[0], pay[1], pay[2], pay[3]);
+      *reinterpret_cast<uint16_t*>(dst + 256 + 2 * p) = (uint16_t)scl;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase B: indexer projection k[o] = sum_ch W[o][ch] c~[ch], ascending fma chain.
+  // thread -> output o, entries 8h .. 8h+7
+  {
+    const int o = t & (kIdxDim - 1), h = t >> 7;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = 0.0f;
+    const uint4* wrow = reinterpret_cast<const uint4*>(w_idx + (int64_t)o * kD);
+    for (int cb = 0; cb < kD / 8; cb++) {
+      const uint4 u = wrow[cb];
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+      float wf[8];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        wf[2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
+        wf[2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float4 c0 = *reinterpret_cast<const float4*>(&s_c[8 * h + e][8 * cb]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&s_c[8 * h + e][8 * cb + 4]);
+        float a = acc[e];
+        a = __builtin_fmaf(wf[0], c0.x, a);
+        a = __builtin_fmaf(wf[1], c0.y, a);
+        a = __builtin_fmaf(wf[2], c0.z, a);
+        a = __builtin_fmaf(wf[3], c0.w, a);
+        a = __builtin_fmaf(wf[4], c1.x, a);
+        a = __builtin_fmaf(wf[5], c1.y, a);
+        a = __builtin_fmaf(wf[6], c1.z, a);
+        a = __builtin_fmaf(wf[7], c1.w, a);
+        acc[e] = a;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) s_k[8 * h + e][o] = acc[e];
+  }
+  __syncthreads();
+
+  // ---- phase C: MXFP4 pack.  4 threads per (entry, group of 32), 8 elements each
+  {
+    const int gi = t >> 2, sub = t & 3;
+    const int e = gi >> 2, g = gi & 3;
+    const int64_t j = j0 + e;
+    float v[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      v[q] = s_k[e][32 * g + 8 * sub + q];
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
+    }
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+    const uint32_t code = e8m0_scale_code(amax);
+    const float X = __builtin_ldexpf(1.0f, (int)code - 127);
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 8; q++) word |= e2m1_encode(v[q], X) << (4 * q);
+    if (j < n_entries) {
+      uint8_t* dst = idx_out + j * kIdxBytes;
+      *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
+      if (sub == 0) dst[64 + g] = (uint8_t)code;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace csa2
+
+extern "C" int csa2_compress_pack(const uint16_t* latent_bf16, int64_t n_entries, int m,
+                                  const float* pool_w, const float* rope_cs,
+                                  const uint16_t* w_idx_bf16, uint8_t* kv_out, uint8_t* idx_out,
+                                  void* stream) {
+  using namespace csa2;
+  if (n_entries < 0) return CSA2_ERR_INVALID_ARG;
+  if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
+  if (n_entries == 0) return CSA2_OK;
+  if (!latent_bf16 || !rope_cs || !w_idx_bf16 || !kv_out || !idx_out) return CSA2_ERR_INVALID_ARG;
+  if (m == 2 && !pool_w) return CSA2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(latent_bf16) | reinterpret_cast<uintptr_t>(w_idx_bf16) |
+       reinterpret_cast<uintptr_t>(kv_out) | reinterpret_cast<uintptr_t>(idx_out)) & 15)
+    return CSA2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(rope_cs) | reinterpret_cast<uintptr_t>(pool_w)) & 3)
+    return CSA2_ERR_INVALID_ARG;
+  const int64_t grid = (n_entries + kEnt - 1) / kEnt;
+  if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(compress_pack_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
+                     kv_out, idx_out);
+  return check_launch();
+}

@@ -1,0 +1,61 @@
+// csa2_device.hpp -- internal helpers shared by the gfx950 kernels of libcsa2.
+// Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+constexpr int kD = 512;       // latent width
+constexpr int kDRope = 64;    // rope tail
+constexpr int kDNope = kD - kDRope;
+constexpr int kHeads = 64;    // attention heads
+constexpr int kIdxHeads = 32; // indexer heads
+constexpr int kIdxDim = 128;  // indexer head dim
+constexpr int kKvBytes = 288;
+constexpr int kIdxBytes = 68;
+constexpr int kBlock = 8;     // candidate block size
+constexpr int kMaxPool = 2048;
+constexpr int kMaxTopK = 512;
+constexpr int kMaxSwa = 128;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// E2M1 magnitude code -> value (exact), 3-bit code.
+__device__ __forceinline__ float e2m1_mag(uint32_t c) {
+  // 0, .5, 1, 1.5, 2, 3, 4, 6
+  const uint32_t e = c >> 1, m = c & 1;
+  return e == 0 ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
+}
+
+// OCP E4M3FN byte -> value (exact; 0x7F / 0xFF are never produced by the packer).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15, m = b & 7;
+  float v = e == 0 ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf((float)(8 + m), (int)e - 10);
+  return (b & 0x80) ? -v : v;
+}
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key); NaN ranks as -inf.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) f = -__builtin_inff();
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+inline int check_launch() { return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+}  // namespace csa2

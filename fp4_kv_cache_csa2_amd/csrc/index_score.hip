@@ -1,0 +1,186 @@
+// index_score.hip -- lightning-indexer scoring over the MXFP4 indexer-K cache (gfx950).
+//
+// Computes s(t, j) = sum_h w[t,h] * max(0, q[t,h,:] . k^_j) ([ZB] "把 KV Cache 压缩推到极致"
+// §3.3.2: indexer query and per-head weights produce the Top-K set; §2.3.4 / [DF]
+// "CSA2 与每 token 890 字节" §4.7: a Full layer scores every visible entry and reduces
+// blocks of 8 by max, a Reindex layer scores only its candidate pool).
+//
+// Design.  One wavefront owns one query and streams tiles of 32 entries.  The 32 heads
+// x 128 dims contraction runs on v_mfma_f32_32x32x16_bf16 with the heads as the M
+// dimension: the query sits in registers as eight A fragments for the whole scan, and
+// each tile's B fragments are built in registers straight from the packed bytes: every
+// lane loads 32 contiguous payload bytes of one entry (half of its 64) plus the 4-byte
+// scale word, and v_cvt_scalef32_pk_bf16_fp4 turns two E2M1 nibbles and their E8M0
+// power-of-two scale into two exact bf16 values.  The K dimension is permuted so that
+// lane group g and step s hold dims 64g + 8s .. 64g + 8s + 7 for both operands, which
+// leaves the dot products unchanged and makes each lane's bytes contiguous.  ReLU, the
+// head weights and the head sum run on the accumulator registers; a 32-lane swap
+// finishes the sum.  HBM traffic per entry is its 68 bytes plus 4.5 bytes of output.
+#include "csa2_device.hpp"
+
+namespace csa2 {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;
+
+__device__ __forceinline__ bf16x8 cvt_fp4x8(uint32_t word, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ float e8m0_scale(uint32_t code) {
+  return __builtin_ldexpf(1.0f, (int)code - 127);
+}
+
+// indexer rows are 68 bytes, so a row's 16-byte pieces are only 4-byte aligned; gfx950
+// serves dword-aligned global dwordx4 loads
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+struct RawTile {
+  u32x4_a4 lo, hi;
+  uint32_t sc;
+};
+
+__global__ __launch_bounds__(kThreads) void index_score_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
+    const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
+    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
+    int32_t width, int32_t tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, g = lane >> 5;
+  const int32_t nvis = q_nvis[t];
+  const int64_t base = q_base[t];
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  const int32_t tile_begin = blockIdx.x * tiles_per_wg;
+  const int32_t tile_end = min(tile_begin + tiles_per_wg, ntiles);
+  if (tile_begin >= ntiles) return;
+
+  // query: head n, dims 64g .. 64g + 63 as eight bf16x8 A fragments
+  bf16x8 a[8];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const uint4 u = qp[s];
+      a[s] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  // head weight of each accumulator row held by this lane: row = 8(r/4) + 4g + r%4
+  float wr[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) wr[r] = head_w[(int64_t)t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)];
+
+  const int32_t nbw = (width + kBlock - 1) / kBlock;
+  float* srow = scores + (int64_t)t * width;
+
+  auto entry_of = [&](int32_t tile, bool& valid) -> int64_t {
+    const int32_t p = tile * kTile + n;
+    if (pool_blocks == nullptr) {
+      valid = p < nvis;
+      return p;
+    }
+    const int32_t slot = p >> 3;
+    const int32_t b = slot < M ? pool_blocks[(int64_t)t * M + slot] : -1;
+    const int64_t j = (int64_t)b * kBlock + (p & 7);
+    valid = b >= 0 && j < nvis;
+    return j;
+  };
+  auto load = [&](int32_t tile, bool& valid) -> RawTile {
+    RawTile r;
+    const int64_t j = entry_of(tile, valid);
+    if (valid) {
+      const uint8_t* row = idx_cache + (base + j) * kIdxBytes;
+      r.lo = *reinterpret_cast<const u32x4_a4*>(row + 32 * g);
+      r.hi = *reinterpret_cast<const u32x4_a4*>(row + 32 * g + 16);
+      r.sc = *reinterpret_cast<const uint32_t*>(row + 64);
+    } else {
+      r.lo = u32x4_a4{0u, 0u, 0u, 0u};
+      r.hi = r.lo;
+      r.sc = 127u * 0x01010101u;
+    }
+    return r;
+  };
+
+  int32_t tile = tile_begin + wave;
+  bool valid_cur = false;
+  RawTile cur = tile < tile_end ? load(tile, valid_cur) : RawTile{};
+  for (; tile < tile_end; tile += kWaves) {
+    // prefetch the next tile of this wave before working on the current one
+    bool valid_nxt = false;
+    const int32_t nxt = tile + kWaves;
+    RawTile next = nxt < tile_end ? load(nxt, valid_nxt) : RawTile{};
+
+    const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
+    const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
+    const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3], cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const bf16x8 b = cvt_fp4x8(words[s], s < 4 ? x0 : x1);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) part = __builtin_fmaf(wr[r], __builtin_fmaxf(acc[r], 0.0f), part);
+    const float tot = part + __shfl_xor(part, 32);
+    const float sc = valid_cur ? tot : -__builtin_inff();
+    const int32_t p = tile * kTile + n;
+    if (g == 0 && p < width) srow[p] = sc;
+    if (block_max != nullptr) {
+      float bm = __builtin_fmaxf(sc, __shfl_xor(sc, 1));
+      bm = __builtin_fmaxf(bm, __shfl_xor(bm, 2));
+      bm = __builtin_fmaxf(bm, __shfl_xor(bm, 4));
+      if (g == 0 && (n & 7) == 0 && p < width) block_max[(int64_t)t * nbw + (p >> 3)] = bm;
+    }
+    cur = next;
+    valid_cur = valid_nxt;
+  }
+}
+
+}  // namespace
+}  // namespace csa2
+
+extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
+                                const uint8_t* idx_cache, const int64_t* q_base,
+                                const int32_t* q_nvis, const int32_t* pool_blocks, int32_t M,
+                                int32_t n_q, int32_t width, float* scores, float* block_max,
+                                void* stream) {
+  using namespace csa2;
+  if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
+  if (n_q == 0 || width == 0) return CSA2_OK;
+  if (!q_idx_bf16 || !head_w || !idx_cache || !q_base || !q_nvis || !scores) return CSA2_ERR_INVALID_ARG;
+  if (pool_blocks) {
+    if (M < 1) return CSA2_ERR_INVALID_ARG;
+    if (M > kMaxPool) return CSA2_ERR_UNSUPPORTED;
+    if ((int64_t)width != 8LL * M) return CSA2_ERR_INVALID_ARG;
+    if (block_max) return CSA2_ERR_INVALID_ARG;
+  }
+  if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q_idx_bf16) | reinterpret_cast<uintptr_t>(idx_cache)) & 15)
+    return CSA2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(head_w) | reinterpret_cast<uintptr_t>(scores) |
+       reinterpret_cast<uintptr_t>(block_max)) & 3)
+    return CSA2_ERR_INVALID_ARG;
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  // aim for ~2048 workgroups in total; each wave gets an equal share of its workgroup's tiles
+  int64_t chunks = (2048 + n_q - 1) / n_q;
+  const int64_t max_chunks = (ntiles + kWaves - 1) / kWaves;
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks < 1) chunks = 1;
+  int32_t tiles_per_wg = (int32_t)((ntiles + chunks - 1) / chunks);
+  tiles_per_wg = (tiles_per_wg + kWaves - 1) / kWaves * kWaves;
+  const int32_t grid_x = (ntiles + tiles_per_wg - 1) / tiles_per_wg;
+  hipLaunchKernelGGL(index_score_kernel, dim3(grid_x, n_q), dim3(kThreads), 0, (hipStream_t)stream,
+                     q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width,
+                     tiles_per_wg, scores, block_max);
+  return check_launch();
+}

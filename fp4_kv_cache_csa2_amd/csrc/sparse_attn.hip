@@ -1,0 +1,339 @@
+// sparse_attn.hip -- sparse latent attention over the selected FP4 entries joined with the
+// sliding window, for gfx950.
+//
+// Follows [ZB] "把 KV Cache 压缩推到极致" §3.3.2.1 (key = value = c, the output is a convex
+// combination of the selected content vectors) and §3.3.2 (one joint sparse attention
+// over the selected main-KV entries and the layer's SWA KV).  FP4 is storage only: the
+// entries are dequantised before the matmuls ([ZB] §2.4.4).
+//
+// Design.  A workgroup of 4 waves serves one query; wave w owns heads 16w .. 16w+15.
+// Keys are processed in chunks of 64: the selected entries (gathered 288-byte rows) and
+// the window rows are decoded once into LDS as f16 (exact: an E2M1 code times an E4M3
+// scale has at most 6 significant bits; bf16 window values are exact in f16's normal
+// range), both row-major (QK^T operand) and transposed (PV operand).  QK^T and PV run on
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation; the softmax is online across chunks
+// in fp32.  For small batches the key chunks of a query are split across workgroups and
+// a merge kernel combines the partial (o, m, l) exactly like flash-decoding.
+#include "csa2_device.hpp"
+
+namespace csa2 {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 64;
+constexpr int kKStride = kD + 8;        // f16 elements per sK row
+constexpr int kVStride = kChunk + 8;    // f16 elements per sVT row
+constexpr int kPStride = kChunk + 8;
+
+struct AttnShared {
+  _Float16 k[kChunk * kKStride];        // keys row-major [key][dim]
+  _Float16 vt[kD * kVStride];           // keys transposed [dim][key]
+  _Float16 p[kWaves * 16 * kPStride];   // per-wave probabilities [head][key]
+  int32_t valid[kChunk];
+};
+
+__device__ __forceinline__ float e2m1_value(uint32_t c4) {
+  const float v = e2m1_mag(c4 & 7u);
+  return (c4 & 8u) ? -v : v;
+}
+
+__global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_cache,
+    const int64_t* __restrict__ q_base, const int32_t* __restrict__ topk, int32_t K,
+    const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_start,
+    const int32_t* __restrict__ swa_len, float scale, int32_t n_chunks, int32_t chunks_per_split,
+    int32_t n_splits, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml) {
+  __shared__ AttnShared sh;
+  const int t = blockIdx.y, split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int c_begin = split * chunks_per_split;
+  const int c_end = min(c_begin + chunks_per_split, n_chunks);
+  const int64_t base = q_base[t];
+  const int32_t nswa = min(max(swa_len[t], 0), kMaxSwa);
+  const int64_t swa0 = swa_start[t];
+
+  // query fragments: head 16w + i, dims 32s + 8g .. +7, as f16 (exact in the normal range)
+  f16x8 qa[16];
+  {
+    const uint16_t* qh = q + ((int64_t)t * kHeads + 16 * w + i) * kD + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 16; s++) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qh + 32 * s);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        qa[s][2 * v] = (_Float16)bf16_bits_to_f32(wd[v] & 0xFFFFu);
+        qa[s][2 * v + 1] = (_Float16)bf16_bits_to_f32(wd[v] >> 16);
+      }
+    }
+  }
+
+  f32x4 o[32];
+#pragma unroll
+  for (int d = 0; d < 32; d++) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    m_run[r] = -__builtin_inff();
+    l_run[r] = 0.0f;
+  }
+
+  for (int c = c_begin; c < c_end; c++) {
+    __syncthreads();
+    // ---- decode 64 keys: thread -> key kk, dims 128qq .. 128qq + 127
+    {
+      const int kk = tid >> 2, qq = tid & 3;
+      const int x = c * kChunk + kk;
+      _Float16* krow = sh.k + kk * kKStride + 128 * qq;
+      _Float16* vcol = sh.vt + (128 * qq) * kVStride + kk;
+      auto emit = [&](int d0, const f16x8& pk) {
+        *reinterpret_cast<f16x8*>(krow + d0) = pk;
+#pragma unroll
+        for (int e = 0; e < 8; e++) vcol[(d0 + e) * kVStride] = pk[e];
+      };
+      int kind = 0;  // 0 = empty slot, 1 = selected entry, 2 = window row
+      int32_t id = -1;
+      if (x < K) {
+        id = topk[(int64_t)t * K + x];
+        kind = id >= 0 ? 1 : 0;
+      } else if (x - K < nswa) {
+        kind = 2;
+      }
+      if (kind == 1) {
+        const uint8_t* row = kv_cache + (base + id) * kKvBytes;
+        const uint4* pay = reinterpret_cast<const uint4*>(row + 64 * qq);
+        const uint2 scw = *reinterpret_cast<const uint2*>(row + 256 + 8 * qq);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const uint4 u = pay[v];
+          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int q4 = 0; q4 < 4; q4++) {
+            const int grp = 2 * v + (q4 >> 1);  // local group of 16 dims
+            const uint32_t sb = ((grp < 4 ? scw.x : scw.y) >> (8 * (grp & 3))) & 255u;
+            const float S = e4m3_value(sb);
+            f16x8 pk;
+#pragma unroll
+            for (int nb = 0; nb < 8; nb++) pk[nb] = (_Float16)(e2m1_value((wd[q4] >> (4 * nb)) & 15u) * S);
+            emit(32 * v + 8 * q4, pk);
+          }
+        }
+      } else if (kind == 2) {
+        const uint4* src = reinterpret_cast<const uint4*>(swa + (swa0 + (x - K)) * kD + 128 * qq);
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const uint4 u = src[v];
+          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+          f16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
+            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
+          }
+          emit(8 * v, pk);
+        }
+      } else {
+        f16x8 z;
+#pragma unroll
+        for (int e = 0; e < 8; e++) z[e] = (_Float16)0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; v++) emit(8 * v, z);
+      }
+      if (qq == 0) sh.valid[kk] = kind != 0 ? 1 : 0;
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T for 4 tiles of 16 keys
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; s++) {
+#pragma unroll
+      for (int kt = 0; kt < 4; kt++) {
+        const f16x8 b = *reinterpret_cast<const f16x8*>(sh.k + (16 * kt + i) * kKStride + 32 * s + 8 * g);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], b, sacc[kt], 0, 0, 0);
+      }
+    }
+    // ---- online softmax over this chunk; lane holds rows (heads) 4g + r, column (key) 16kt + i
+    float pv[4][4];
+    float cmax[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) cmax[r] = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+      const bool ok = sh.valid[16 * kt + i] != 0;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        pv[kt][r] = ok ? sacc[kt][r] * scale : -__builtin_inff();
+        cmax[r] = __builtin_fmaxf(cmax[r], pv[kt][r]);
+      }
+    }
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      float mx = cmax[r];
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 4));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 8));
+      const float mn = __builtin_fmaxf(m_run[r], mx);
+      alpha[r] = (mn == -__builtin_inff()) ? 1.0f : __expf(m_run[r] - mn);
+      float rs = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; kt++) {
+        const float p = (pv[kt][r] == -__builtin_inff()) ? 0.0f : __expf(pv[kt][r] - mn);
+        pv[kt][r] = p;
+        rs += p;
+      }
+      rs += __shfl_xor(rs, 1);
+      rs += __shfl_xor(rs, 2);
+      rs += __shfl_xor(rs, 4);
+      rs += __shfl_xor(rs, 8);
+      l_run[r] = l_run[r] * alpha[r] + rs;
+      m_run[r] = mn;
+    }
+#pragma unroll
+    for (int d = 0; d < 32; d++) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) o[d][r] *= alpha[r];
+    }
+    _Float16* pw = sh.p + w * 16 * kPStride;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) pw[(4 * g + r) * kPStride + 16 * kt + i] = (_Float16)pv[kt][r];
+    }
+    __syncthreads();
+    // ---- O += P V: A = P [head i][keys 32ks + 8g ..], B = V^T rows (dims) 16dt + i
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      const f16x8 pa = *reinterpret_cast<const f16x8*>(pw + i * kPStride + 32 * ks + 8 * g);
+#pragma unroll
+      for (int dt = 0; dt < 32; dt++) {
+        const f16x8 vb = *reinterpret_cast<const f16x8*>(sh.vt + (16 * dt + i) * kVStride + 32 * ks + 8 * g);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds O[head 16w + 4g + r][dim 16dt + i]
+  if (n_splits == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int h = 16 * w + 4 * g + r;
+      const float inv = l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f;
+      float* orow = out + ((int64_t)t * kHeads + h) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 32; dt++) orow[16 * dt + i] = o[dt][r] * inv;
+      if (lse != nullptr && i == 0)
+        lse[(int64_t)t * kHeads + h] = l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
+    }
+  } else {
+    const int64_t slot = (int64_t)t * n_splits + split;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int h = 16 * w + 4 * g + r;
+      float* orow = ws_o + (slot * kHeads + h) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 32; dt++) orow[16 * dt + i] = o[dt][r];
+      if (i == 0) {
+        ws_ml[(slot * kHeads + h) * 2 + 0] = m_run[r];
+        ws_ml[(slot * kHeads + h) * 2 + 1] = l_run[r];
+      }
+    }
+  }
+}
+
+// Combine the split partials of one (query, head): out = sum_s o_s e^(m_s - M) / L.
+__global__ __launch_bounds__(128) void sparse_attn_merge_kernel(const float* __restrict__ ws_o,
+                                                                const float* __restrict__ ws_ml,
+                                                                int32_t n_splits, float* __restrict__ out,
+                                                                float* __restrict__ lse) {
+  const int t = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+  float M = -__builtin_inff();
+  for (int s = 0; s < n_splits; s++) {
+    const float m = ws_ml[(((int64_t)t * n_splits + s) * kHeads + h) * 2];
+    const float l = ws_ml[(((int64_t)t * n_splits + s) * kHeads + h) * 2 + 1];
+    if (l > 0.0f) M = __builtin_fmaxf(M, m);
+  }
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < n_splits; s++) {
+    const int64_t slot = ((int64_t)t * n_splits + s) * kHeads + h;
+    const float m = ws_ml[slot * 2], l = ws_ml[slot * 2 + 1];
+    if (!(l > 0.0f)) continue;
+    const float e = __expf(m - M);
+    L += l * e;
+    const float4 v = reinterpret_cast<const float4*>(ws_o + slot * kD)[tid];
+    acc.x += v.x * e;
+    acc.y += v.y * e;
+    acc.z += v.z * e;
+    acc.w += v.w * e;
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  reinterpret_cast<float4*>(out + ((int64_t)t * kHeads + h) * kD)[tid] =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (lse != nullptr && tid == 0) lse[(int64_t)t * kHeads + h] = L > 0.0f ? M + __logf(L) : -__builtin_inff();
+}
+
+struct Plan {
+  int32_t n_chunks, chunks_per_split, n_splits;
+};
+
+Plan make_plan(int32_t n_q, int32_t K) {
+  Plan p;
+  p.n_chunks = (K + kMaxSwa + kChunk - 1) / kChunk;
+  int32_t want = (512 + n_q - 1) / (n_q > 0 ? n_q : 1);
+  if (want < 1) want = 1;
+  if (want > p.n_chunks) want = p.n_chunks;
+  p.chunks_per_split = (p.n_chunks + want - 1) / want;
+  p.n_splits = (p.n_chunks + p.chunks_per_split - 1) / p.chunks_per_split;
+  return p;
+}
+
+}  // namespace
+}  // namespace csa2
+
+extern "C" size_t csa2_sparse_attn_workspace(int32_t n_q, int32_t K) {
+  using namespace csa2;
+  if (n_q <= 0 || K < 0) return 0;
+  const Plan p = make_plan(n_q, K);
+  if (p.n_splits <= 1) return 0;
+  return (size_t)n_q * p.n_splits * kHeads * (kD + 2) * sizeof(float);
+}
+
+extern "C" int csa2_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache,
+                                const int64_t* q_base, const int32_t* topk, int32_t K,
+                                const uint16_t* swa_bf16, const int64_t* swa_start,
+                                const int32_t* swa_len, float scale, float* out, float* lse,
+                                int32_t n_q, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csa2;
+  if (n_q < 0 || K < 0) return CSA2_ERR_INVALID_ARG;
+  if (K > kMaxTopK) return CSA2_ERR_UNSUPPORTED;
+  if (n_q == 0) return CSA2_OK;
+  if (!q_bf16 || !kv_cache || !q_base || !swa_bf16 || !swa_start || !swa_len || !out)
+    return CSA2_ERR_INVALID_ARG;
+  if (K > 0 && !topk) return CSA2_ERR_INVALID_ARG;
+  if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q_bf16) | reinterpret_cast<uintptr_t>(kv_cache) |
+       reinterpret_cast<uintptr_t>(swa_bf16) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return CSA2_ERR_INVALID_ARG;
+  const Plan p = make_plan(n_q, K);
+  const size_t need = csa2_sparse_attn_workspace(n_q, K);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+  float* ws_o = (float*)workspace;
+  float* ws_ml = need > 0 ? ws_o + (size_t)n_q * p.n_splits * kHeads * kD : nullptr;
+  hipLaunchKernelGGL(sparse_attn_kernel, dim3(p.n_splits, n_q), dim3(kThreads), 0,
+                     (hipStream_t)stream, q_bf16, kv_cache, q_base, topk, K, swa_bf16, swa_start,
+                     swa_len, scale, p.n_chunks, p.chunks_per_split, p.n_splits, out, lse, ws_o,
+                     ws_ml);
+  int st = check_launch();
+  if (st != CSA2_OK || p.n_splits <= 1) return st;
+  hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3(kHeads, n_q), dim3(128), 0, (hipStream_t)stream,
+                     ws_o, ws_ml, p.n_splits, out, lse);
+  return check_launch();
+}

@@ -1,0 +1,168 @@
+/*
+ * csa2.h -- C ABI of libcsa2.so: the CSA2 global-attention hot path with an FP4 KV
+ * cache, as hand-written HIP kernels for MI355X (gfx950).
+ *
+ * Page abbreviations used in the citations:
+ *   [ZB] zartbot.github.io   "DeepSeek-V4.1 Flash: 把 KV Cache 压缩推到极致"
+ *   [DF] dilfish.github.io   "4. 层维度(下):CSA2 与每 token 890 字节"
+ *   [SR] sarnas.ru           "DeepSeek-V4.1 Flash: как устроено сжатие KV-кэша"
+ *
+ * General contract
+ *   - Tensor pointers are DEVICE pointers owned by the caller unless a parameter says
+ *     "host".  Arrays are dense and row-major.  bf16 values travel as uint16 bit
+ *     patterns.  The library never allocates, frees or synchronises device memory and
+ *     keeps no mutable global state; calls on different streams are independent.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call
+ *     is asynchronous on it.  A kernel fault surfaces at the caller's next sync.
+ *   - Return value: CSA2_OK (0) or a negative status.  Argument errors are detected on
+ *     the host before anything is launched; CSA2_ERR_HIP reports a launch failure.
+ *   - Fixed method constants (from the model table of [ZB] §1.2): latent width 512 =
+ *     448 NoPE + 64 RoPE channels, 64 attention heads, 32 indexer heads x 128 dims,
+ *     block 8, at most 2048 pool blocks, Top-K at most 512, window at most 128 rows,
+ *     compression ratio m in {1, 2} ([DF] §4.2).
+ *
+ * Cache entry formats (bit-exact; [ZB] §2.4.4, [DF] §4.4 entry-size equation b(D,G))
+ *   main KV  (288 B): bytes 0..255 hold 512 E2M1 codes, channel 2b in the low nibble
+ *            of byte b (sign in the nibble's bit 3); bytes 256..287 hold one OCP E4M3
+ *            scale per 16 channels.  Rows must be 16-byte aligned (288 = 18 x 16).
+ *   indexer K (68 B): bytes 0..63 hold 128 E2M1 codes in the same nibble order, bytes
+ *            64..67 one E8M0 scale per 32 channels (MXFP4).  The cache base must be
+ *            16-byte aligned; rows are then 4-byte aligned.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer        */
+  CSA2_ERR_UNSUPPORTED = -2, /* a method constant outside what the library builds */
+  CSA2_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required         */
+  CSA2_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+};
+
+#define CSA2_ABI_VERSION 1
+
+int csa2_abi_version(void);
+const char *csa2_status_string(int status);
+
+/*
+ * csa2_rope_table -- HOST function: cos/sin table of the compressed-entry RoPE.
+ *   For each position p = pos[j] and pair i = 0..31:
+ *     out[j*64 + i] = (float)cos(p * theta^(-2i/64)), out[j*64 + 32 + i] = (float)sin(...)
+ *   evaluated in double.  [ZB] §1.2 model table (compress_rope_theta = 160000),
+ *   [ZB] §3.3.2 (RoPE acts on the rope tail only).
+ *   pos: host [n]; out: host [n, 64].  Errors: CSA2_ERR_INVALID_ARG for NULL / n < 0.
+ */
+int csa2_rope_table(const int64_t *pos, int64_t n, double theta, float *out);
+
+/*
+ * csa2_compress_pack -- compressor + RoPE + FP4 pack + indexer-K projection + MXFP4.
+ *   [DF] §4.2 compressor equation: entry j pools the m latents m*j .. m*j+m-1 with
+ *   per-channel non-negative weights, c_j = sum_i a_i x_{mj+i}, a_i = w_i / sum(w)
+ *   (m = 1: c_j = x_j, the per-token projection of [ZB] §3.3.2);
+ *   [ZB] §2.4.4: RoPE on channels 448..511 (adjacent pairs (448+2i, 449+2i)) before
+ *   quantisation, same FP4 format for NoPE and RoPE channels;
+ *   [ZB] §2.3.1: indexer K is a projection of the main-KV entry: k = W_idx c~ over the
+ *   512 rotated fp32 channels (one ascending fma chain per output);
+ *   [DF] §4.4: main KV E2M1 + E4M3 per 16, indexer K MXFP4 (E2M1 + E8M0 per 32).
+ *   Quantisation rules: E4M3 scale = nearest-even E4M3 of fp32(amax/6), saturating at
+ *   448; element = E2M1 grid point nearest to |e|/S (exact, ties to the even code,
+ *   saturating at 6), sign bit only on non-zero codes; E8M0 code = floor(log2 amax) - 2
+ *   + 127 clamped to [0, 254] (0 when amax = 0).  The output bytes are bit-exact.
+ *
+ *   latent_bf16 [n_entries*m, 512]; pool_w fp32 [m, 512] (not read when m = 1; weights
+ *   must be >= 0 with a positive sum per channel, which is not checked);
+ *   rope_cs fp32 [n_entries, 64] (cos[32], sin[32] at each entry's position, e.g. from
+ *   csa2_rope_table); w_idx_bf16 [128, 512];
+ *   kv_out [n_entries, 288] and idx_out [n_entries, 68] receive the packed entries.
+ *   n_entries = 0 is a no-op.  Errors: INVALID_ARG (NULL, n < 0, misaligned outputs),
+ *   UNSUPPORTED (m not 1 or 2).
+ */
+int csa2_compress_pack(const uint16_t *latent_bf16, int64_t n_entries, int m,
+                       const float *pool_w, const float *rope_cs, const uint16_t *w_idx_bf16,
+                       uint8_t *kv_out, uint8_t *idx_out, void *stream);
+
+/*
+ * csa2_index_score -- lightning-indexer scores over the MXFP4 indexer-K cache.
+ *   [ZB] §3.3.2 (indexer query q^I and per-head weights produce the Top-K set),
+ *   [ZB] §2.3.4 / [DF] §4.7 (the Full layer scores every causally visible entry; a
+ *   Reindex layer scores only its candidate pool):
+ *     s(t, j) = sum_{h<32} head_w[t,h] * max(0, q_idx[t,h,:] . k^_j)
+ *   with k^_j the exact dequantisation of entry j, bf16 products, fp32 accumulation.
+ *
+ *   q_idx_bf16 [n_q, 32, 128]; head_w fp32 [n_q, 32]; idx_cache flat [rows, 68];
+ *   q_base int64 [n_q]: cache row of entry 0 of query t's sequence;
+ *   q_nvis int32 [n_q]: visible entries of query t (entries 0 .. nvis-1);
+ *   pool_blocks: NULL  -> Full mode: scores[t, j] for j < nvis, -inf for nvis <= j < width;
+ *                [n_q, M] int32 block ids (-1 = empty) -> candidate mode: scores[t, 8s+o]
+ *                is the score of entry 8*pool[s]+o, -inf when empty or j >= nvis;
+ *                width must then equal 8*M.
+ *   scores fp32 [n_q, width] (every element is written);
+ *   block_max: NULL or fp32 [n_q, ceil(width/8)] (Full mode only): max of each block of
+ *   8 scores, -inf padding ([ZB] §2.3.4 pad-and-amax).
+ *   Errors: INVALID_ARG (NULL required pointer, n_q < 0, width < 0, width != 8*M in
+ *   candidate mode, misaligned idx_cache), UNSUPPORTED (M > 2048).
+ */
+int csa2_index_score(const uint16_t *q_idx_bf16, const float *head_w, const uint8_t *idx_cache,
+                     const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
+                     int32_t M, int32_t n_q, int32_t width, float *scores, float *block_max,
+                     void *stream);
+
+/*
+ * csa2_block_topk -- hierarchical selection: block max -> top-M block pool -> Top-K.
+ *   [ZB] §2.3.4 and [DF] §4.7: g_r = max over block r (b = `block` positions, -inf
+ *   padding); the block holding the newest visible position takes +inf; the M blocks
+ *   with the largest g_r form the pool P_t (|P_t| <= 8M); a layer's Top-K is taken
+ *   inside the pool.  Ties go to the lower block / entry index; NaN ranks as -inf.
+ *   Full mode (pool_blocks == NULL): scores [n_q, width] from csa2_index_score Full
+ *   mode; block_max may be NULL (recomputed) or the array index_score wrote.  The
+ *   visible count is min(q_nvis[t], width).  pool_out: NULL or [n_q, M] selected block
+ *   ids ascending, -1 padded.  The Top-K inside the pool equals the Top-K of the whole
+ *   row (every global Top-K member's block ranks within the first K+1 blocks).
+ *   Candidate mode (pool_blocks != NULL, [n_q, M]): scores [n_q, width = 8M] laid out as
+ *   csa2_index_score candidate mode; pool_out must be NULL.
+ *   topk_out [n_q, K]: selected entry ids (relative to the sequence) ascending, -1 pad.
+ *   workspace: device scratch of csa2_block_topk_workspace(...) bytes (may be NULL when
+ *   that size is 0).
+ *   Errors: INVALID_ARG, UNSUPPORTED (block != 8, M > 2048, K > 512, K < 1, M < 1),
+ *   WORKSPACE (workspace too small).
+ */
+size_t csa2_block_topk_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K);
+int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, int32_t width,
+                    const int32_t *q_nvis, const int32_t *pool_blocks, int32_t block,
+                    int32_t M, int32_t K, int32_t *pool_out, int32_t *topk_out,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * csa2_sparse_attn -- sparse latent attention over the selected FP4 entries joined with
+ *   the sliding window.  [ZB] §3.3.2.1: key = value = c (the 512-channel entry); one
+ *   softmax per head over the selected entries and the window rows ([ZB] §3.3.2, joint
+ *   sparse attention with the SWA KV):
+ *     o_h = sum_k p_k key_k,  p = softmax(scale * q_h . key_k)
+ *   q_bf16 [n_q, 64, 512] (RoPE already applied); kv_cache flat [rows, 288];
+ *   q_base int64 [n_q]; topk int32 [n_q, K] (entry ids relative to q_base, -1 = unused);
+ *   swa_bf16 [rows, 512]; swa_start int64 [n_q]: first window row of query t;
+ *   swa_len int32 [n_q]: window rows of query t (clamped to [0, 128]);
+ *   scale: logit scale (1/sqrt(512) is the library's documented default reading);
+ *   out fp32 [n_q, 64, 512]; lse: NULL or fp32 [n_q, 64], natural-log partition
+ *   function (max logit + log sum exp); a query with no keys gets out = 0, lse = -inf.
+ *   workspace: csa2_sparse_attn_workspace(n_q, K) bytes.
+ *   Errors: INVALID_ARG, UNSUPPORTED (K > 512), WORKSPACE.
+ */
+size_t csa2_sparse_attn_workspace(int32_t n_q, int32_t K);
+int csa2_sparse_attn(const uint16_t *q_bf16, const uint8_t *kv_cache, const int64_t *q_base,
+                     const int32_t *topk, int32_t K, const uint16_t *swa_bf16,
+                     const int64_t *swa_start, const int32_t *swa_len, float scale, float *out,
+                     float *lse, int32_t n_q, void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

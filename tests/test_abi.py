@@ -1,0 +1,68 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header declares,
+and its host-side argument validation returns the documented status codes before any
+launch.  No GPU compute is called."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "libcsa2.so")
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(csa2_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libcsa2.so is not built")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(lib, s), f"missing export {s}"
+
+
+def test_binding_names_match_header():
+    from fp4_kv_cache_csa2_amd import csa2
+    assert sorted(csa2.SYMBOLS) == declared_symbols()
+    for name in ("rope_table", "compress_pack", "index_score", "block_topk", "sparse_attn"):
+        assert callable(getattr(csa2, name))
+
+
+def test_version_and_status_strings(lib):
+    lib.csa2_status_string.restype = ctypes.c_char_p
+    assert lib.csa2_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert lib.csa2_status_string(st)
+
+
+def test_host_validation_rejects_before_launch(lib):
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.csa2_compress_pack.argtypes = [vp, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.csa2_index_score.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.csa2_block_topk.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.csa2_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, i32, vp, sz, vp]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.csa2_compress_pack(fake, 4, 3, fake, fake, fake, fake, fake, None) == -2
+    assert lib.csa2_compress_pack(fake, -1, 2, fake, fake, fake, fake, fake, None) == -1
+    assert lib.csa2_compress_pack(None, 4, 2, fake, fake, fake, fake, fake, None) == -1
+    assert lib.csa2_compress_pack(fake, 0, 2, None, None, None, None, None, None) == 0
+    assert lib.csa2_index_score(fake, fake, fake, fake, fake, fake, 4096, 1, 8 * 4096, fake, None, None) == -2
+    assert lib.csa2_index_score(fake, fake, fake, fake, fake, fake, 16, 1, 100, fake, None, None) == -1
+    assert lib.csa2_index_score(None, fake, fake, fake, fake, None, 0, 1, 100, fake, None, None) == -1
+    assert lib.csa2_block_topk(fake, None, 1, 100, fake, None, 4, 2048, 512, None, fake, None, 0, None) == -2
+    assert lib.csa2_block_topk(fake, None, 1, 100, fake, None, 8, 2048, 513, None, fake, None, 0, None) == -2
+    assert lib.csa2_block_topk(fake, None, 1, 200000, fake, None, 8, 2048, 512, None, fake, None, 0, None) == -3
+    assert lib.csa2_sparse_attn(fake, fake, fake, fake, 600, fake, fake, fake, 0.04, fake, None, 1,
+                                None, 0, None) == -2
+    assert lib.csa2_sparse_attn(fake, fake, fake, fake, 512, fake, fake, fake, 0.04, fake, None, 1,
+                                None, 0, None) == -3

@@ -1,0 +1,258 @@
+"""GPU parity: every stage of the HIP path against the oracle on the same seeded inputs.
+
+Stage tests feed both sides identical inputs (packed bytes bit-exact, selections
+bit-exact on identical scores, scores and attention within tolerance); chain tests run
+each side end to end from the latents."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_kv_cache_csa2_amd import synth
+from tests.gpu_util import bf16, check_attn, check_scores, check_selection, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def c():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp4_kv_cache_csa2_amd import csa2
+    return csa2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ compress + pack
+@pytest.mark.parametrize("n,m,seed", [(2048, 2, 0), (1000, 1, 1), (37, 2, 2), (1, 1, 3), (17, 2, 4)])
+def test_compress_pack_bit_exact(c, n, m, seed):
+    log(f"compress_pack n={n} m={m} seed={seed}")
+    ci = synth.compress_inputs(seed, n, m)
+    cs = oracle.rope_table(ci.positions)
+    kv_ref, ix_ref = oracle.compress_pack(ci.latent, m, ci.pool_w, cs, ci.w_idx)
+    kv, ix = c.compress_pack(bf16(ci.latent), m, dev(ci.pool_w), dev(c.rope_table(ci.positions).numpy()),
+                             bf16(ci.w_idx))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kv), kv_ref), f"main KV bytes differ in {np.sum(np.any(host(kv) != kv_ref, 1))} entries"
+    assert np.array_equal(host(ix), ix_ref), f"indexer bytes differ in {np.sum(np.any(host(ix) != ix_ref, 1))} entries"
+
+
+def test_compress_pack_edge_values(c):
+    log("compress_pack edge values")
+    rng = np.random.default_rng(11)
+    n = 64
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    x[0, :16] = 0.0  # all-zero group -> scale 0
+    x[1, :16] = 2688.0  # largest representable
+    x[2, 16:32] = 5000.0  # saturates
+    x[3, :] = 1e-3  # tiny groups (subnormal E4M3 scales)
+    x[4, :] = rng.choice([-1.5, 0.75, 3.5, -5.0], 512)  # exact ties in the E2M1 grid
+    x[5, :] = 0.0  # all-zero entry (indexer amax 0)
+    x[6, ::2] = -x[6, 1::2]
+    lat = synth.f32_to_bf16_bits(x)
+    w = synth.f32_to_bf16_bits(rng.standard_normal((128, 512)).astype(np.float32) / 22.6)
+    pos = np.arange(n, dtype=np.int64) * 977
+    kv_ref, ix_ref = oracle.compress_pack(lat, 1, None, oracle.rope_table(pos), w)
+    pw = torch.ones((1, 512), dtype=torch.float32, device="cuda")
+    kv, ix = c.compress_pack(bf16(lat), 1, pw, dev(c.rope_table(pos).numpy()), bf16(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kv), kv_ref)
+    assert np.array_equal(host(ix), ix_ref)
+
+
+# ------------------------------------------------------------------ index scores
+@pytest.mark.parametrize("n_q,n,width_pad,seed", [(1, 2048, 0, 5), (3, 1000, 77, 6), (4, 4096, 8, 7), (2, 33, 0, 8)])
+def test_index_score_full_mode(c, n_q, n, width_pad, seed):
+    log(f"index_score full n_q={n_q} n={n} seed={seed}")
+    kv, ix = synth.random_caches(seed, n * n_q)
+    d = synth.query_inputs(seed + 100, n_q)
+    base = np.arange(n_q, dtype=np.int64) * n
+    nvis = np.array([n - (7 * t) % max(n // 3, 1) for t in range(n_q)], np.int32)
+    width = n + width_pad
+    ref = oracle.index_score(d.q_idx, d.head_w, ix, base, nvis, width)
+    s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), dev(base), dev(nvis), width)
+    torch.cuda.synchronize()
+    s, bm = host(s), host(bm)
+    check_scores(s, ref)
+    # the block maxima are exactly the maxima of the GPU's own scores (-inf padding)
+    nbw = (width + 7) // 8
+    pad = np.full((n_q, nbw * 8), -np.inf, np.float32)
+    pad[:, :width] = s
+    assert np.array_equal(bm, pad.reshape(n_q, nbw, 8).max(axis=2))
+
+
+def test_index_score_candidate_mode(c):
+    log("index_score candidate mode")
+    n_q, n, M = 3, 5000, 64
+    kv, ix = synth.random_caches(9, n * n_q)
+    d = synth.query_inputs(10, n_q, q_idx_scale=1.0)
+    base = np.arange(n_q, dtype=np.int64) * n
+    nvis = np.array([n, n - 3, 4001], np.int32)
+    rng = np.random.default_rng(3)
+    pool = np.full((n_q, M), -1, np.int32)
+    for t in range(n_q):
+        nb = -(-nvis[t] // 8)
+        k = [M, M - 5, 17][t]
+        sel = np.sort(rng.choice(nb - 1, k - 1, replace=False))
+        pool[t, :k] = np.sort(np.append(sel, nb - 1))
+    ref = oracle.index_score(d.q_idx, d.head_w, ix, base, nvis, 8 * M, pool_blocks=pool)
+    s, _ = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), dev(base), dev(nvis), 8 * M,
+                         pool_blocks=dev(pool))
+    torch.cuda.synchronize()
+    check_scores(host(s), ref)
+
+
+# ------------------------------------------------------------------ selection (bit-exact on identical scores)
+@pytest.mark.parametrize("width,nvis,M,K,tie,levels,nan,seed", [
+    (2048, [2048], 2048, 512, 0.0, 0, 0.0, 12),
+    (40000, [40000, 39995, 1000], 2048, 512, 0.2, 0, 0.0, 13),
+    (40000, [40000, 30001], 2048, 512, 0.0, 5, 0.0, 14),
+    (12345, [12345, 700, 5, 0], 100, 64, 0.1, 0, 0.01, 15),
+    (200000, [200000, 150007], 2048, 512, 0.05, 0, 0.0, 16),
+    (34816, [34816, 32769], 2048, 512, 0.0, 0, 0.0, 17),
+])
+def test_block_topk_full_mode_exact(c, width, nvis, M, K, tie, levels, nan, seed):
+    log(f"block_topk full width={width} nvis={nvis} M={M} K={K}")
+    nvis = np.array(nvis, np.int32)
+    s = synth.random_scores(seed, len(nvis), width, tie_frac=tie, levels=levels, nan_frac=nan)
+    pool_ref, topk_ref = oracle.block_topk(s, nvis, K=K, M=M)
+    for use_bm in (False, True):
+        bm = None
+        if use_bm:
+            nbw = (width + 7) // 8
+            pad = np.full((len(nvis), nbw * 8), -np.inf, np.float32)
+            sv = np.where(np.isnan(s), -np.inf, s)
+            for t, nv in enumerate(nvis):
+                pad[t, :min(nv, width)] = sv[t, :min(nv, width)]
+            bm = dev(pad.reshape(len(nvis), nbw, 8).max(axis=2))
+        pool, topk = c.block_topk(dev(s), dev(nvis), K=K, M=M, block_max=bm)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(pool), pool_ref), "pool differs"
+        assert np.array_equal(host(topk), topk_ref), "topk differs"
+
+
+def test_block_topk_candidate_mode_exact(c):
+    log("block_topk candidate mode")
+    n_q, M, K = 3, 2048, 512
+    nvis = np.array([131072, 131070, 9000], np.int32)
+    pool = np.full((n_q, M), -1, np.int32)
+    rng = np.random.default_rng(21)
+    for t in range(n_q):
+        nb = -(-nvis[t] // 8)
+        k = min(M, nb)
+        pool[t, :k] = np.sort(rng.choice(nb, k, replace=False))
+    s = synth.random_scores(22, n_q, 8 * M, tie_frac=0.1)
+    _, topk_ref = oracle.block_topk(s, nvis, K=K, pool_blocks=pool)
+    _, topk = c.block_topk(dev(s), dev(nvis), K=K, pool_blocks=dev(pool))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(topk), topk_ref)
+
+
+# ------------------------------------------------------------------ sparse attention
+@pytest.mark.parametrize("n_q,K,n_entries,seed", [(1, 512, 4096, 30), (4, 512, 3000, 31), (3, 100, 500, 32),
+                                                   (600, 512, 2048, 33)])
+def test_sparse_attn(c, n_q, K, n_entries, seed):
+    log(f"sparse_attn n_q={n_q} K={K}")
+    kv, _ = synth.random_caches(seed, n_entries)
+    rng = np.random.default_rng(seed)
+    swa_len = rng.integers(0, 129, n_q).astype(np.int32)
+    swa_len[0] = 128
+    d = synth.query_inputs(seed + 1, n_q, swa_rows=128 * n_q, swa_len=swa_len)
+    topk = np.full((n_q, K), -1, np.int32)
+    for t in range(n_q):
+        k = K if t % 3 == 0 else int(rng.integers(0, K + 1))
+        topk[t, :k] = np.sort(rng.choice(n_entries, k, replace=False))
+    base = np.zeros(n_q, np.int64)
+    if n_q > 1:
+        topk[1] = -1  # window only
+    ref, lse_ref = oracle.sparse_attn(d.q, kv, base, topk, d.swa, d.swa_start, d.swa_len)
+    out, lse = c.sparse_attn(bf16(d.q), dev(kv), dev(base), dev(topk), bf16(d.swa), dev(d.swa_start),
+                             dev(d.swa_len))
+    torch.cuda.synchronize()
+    rel = check_attn(host(out), ref)
+    log(f"  max rel err {rel:.2e}")
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(host(lse)))
+    assert np.allclose(host(lse)[fin], lse_ref[fin], atol=2e-3)
+
+
+def test_sparse_attn_empty_query(c):
+    log("sparse_attn empty")
+    kv, _ = synth.random_caches(40, 64)
+    d = synth.query_inputs(41, 2, swa_len=[0, 0])
+    topk = np.full((2, 512), -1, np.int32)
+    out, lse = c.sparse_attn(bf16(d.q), dev(kv), dev(np.zeros(2, np.int64)), dev(topk), bf16(d.swa),
+                             dev(d.swa_start), dev(d.swa_len))
+    torch.cuda.synchronize()
+    assert np.all(host(out) == 0) and np.all(np.isneginf(host(lse)))
+
+
+# ------------------------------------------------------------------ chained decode from the latents
+def _decode_chain(c, ci, m, n_q, seeds, nvis_list, M=2048, K=512):
+    """Oracle and GPU each run compress -> index -> block_topk -> attention from the latents."""
+    n = ci.latent.shape[0] // m // n_q
+    cs = oracle.rope_table(ci.positions)
+    kv_ref, ix_ref = oracle.compress_pack(ci.latent, m, ci.pool_w, cs, ci.w_idx)
+    d = synth.query_inputs(seeds, n_q)
+    base = np.arange(n_q, dtype=np.int64) * n
+    nvis = np.asarray(nvis_list, np.int32)
+    s_ref = oracle.index_score(d.q_idx, d.head_w, ix_ref, base, nvis, n)
+    pool_ref, topk_ref = oracle.block_topk(s_ref, nvis, K=K, M=M)
+    out_ref, _ = oracle.sparse_attn(d.q, kv_ref, base, topk_ref, d.swa, d.swa_start, d.swa_len)
+
+    kv, ix = c.compress_pack(bf16(ci.latent), m, dev(ci.pool_w), dev(c.rope_table(ci.positions).numpy()),
+                             bf16(ci.w_idx))
+    s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), ix, dev(base), dev(nvis), n)
+    pool, topk = c.block_topk(s, dev(nvis), K=K, M=M, block_max=bm)
+    out, _ = c.sparse_attn(bf16(d.q), kv, dev(base), topk, bf16(d.swa), dev(d.swa_start), dev(d.swa_len))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kv), kv_ref) and np.array_equal(host(ix), ix_ref)
+    check_scores(host(s), s_ref)
+    same = 0
+    g_pool, g_topk, g_out = host(pool), host(topk), host(out)
+    for t in range(n_q):
+        nb = -(-nvis[t] // 8)
+        blk = np.full(nb * 8, -np.inf)
+        blk[:nvis[t]] = s_ref[t, :nvis[t]]
+        g = blk.reshape(nb, 8).max(axis=1)
+        g[nb - 1] = np.inf
+        check_selection(g_pool[t], pool_ref[t], lambda ids: g[ids], "pool")
+        diff = check_selection(g_topk[t], topk_ref[t], lambda ids: s_ref[t, ids].astype(np.float64), "topk")
+        if diff == 0:
+            check_attn(g_out[t], out_ref[t])
+            same += 1
+    assert same >= n_q - 1, "too many near-tie selection differences to compare attention"
+
+
+def test_chain_tiny_decode_m2(c):
+    log("chain: tiny decode m=2 (4096 tokens -> 2048 entries)")
+    ci = synth.compress_inputs(0, 2048, 2)
+    _decode_chain(c, ci, 2, 1, 1000, [2048])
+
+
+def test_chain_decode_m1_batch4(c):
+    log("chain: decode m=1 batch 4 x 32768")
+    ci = synth.compress_inputs(1, 4 * 32768, 1)
+    _decode_chain(c, ci, 1, 4, 1001, [32768, 32768, 32768, 32768])
+
+
+# ------------------------------------------------------------------ determinism
+def test_determinism(c):
+    log("determinism")
+    n_q, n = 4, 9000
+    kv, ix = synth.random_caches(50, n * n_q)
+    d = synth.query_inputs(51, n_q)
+    base = dev(np.arange(n_q, dtype=np.int64) * n)
+    nvis = dev(np.full(n_q, n, np.int32))
+    outs = []
+    for _ in range(2):
+        s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), base, nvis, n)
+        pool, topk = c.block_topk(s, nvis, block_max=bm)
+        out, lse = c.sparse_attn(bf16(d.q), dev(kv), base, topk, bf16(d.swa), dev(d.swa_start), dev(d.swa_len))
+        torch.cuda.synchronize()
+        outs.append([host(x) for x in (s, bm, pool, topk, out, lse)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
