@@ -156,9 +156,10 @@ def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool
         topk_out = torch.empty((n_q, K), dtype=torch.int32, device=dev)
     _dev(pool_out, torch.int32, "pool_out")
     _dev(topk_out, torch.int32, "topk_out")
-    need = 0 if pool_blocks is not None else block_topk_workspace(n_q, width, M, K)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    need = block_topk_workspace(n_q, width, M, K)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        # the histogram region must start zeroed; every call leaves it zeroed
+        workspace = torch.zeros(max(need, 4), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("csa2_block_topk", _L.csa2_block_topk(
         _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(pool_blocks), 8, M, K,

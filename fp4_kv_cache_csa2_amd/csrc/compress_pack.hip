@@ -16,8 +16,8 @@
 namespace csa2 {
 namespace {
 
-constexpr int kEnt = 16;  // entries per workgroup
 constexpr int kThreads = 256;
+constexpr int kWChunk = 64;  // channels of W_idx staged per step
 
 // Nearest-even E4M3 code of x >= 0, saturating at 448 (0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode(float x) {
@@ -50,12 +50,16 @@ __device__ __forceinline__ uint32_t e8m0_scale_code(float amax) {
   return (uint32_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
 }
 
+// kEnt entries per workgroup: 16 amortises the W_idx reads over many entries; 2 keeps one
+// fma chain per thread for the few-entry appends of a decode step.
+template <int kEnt>
 __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
     const float* __restrict__ rope_cs, const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out,
     uint8_t* __restrict__ idx_out) {
   __shared__ float s_c[kEnt][kD];          // rotated fp32 entries
   __shared__ float s_k[kEnt][kIdxDim];     // projected indexer keys
+  __shared__ uint16_t s_w[2][kWChunk][kIdxDim + 8];  // W_idx^T chunks (bf16 bits)
   const int t = threadIdx.x;
   const int64_t j0 = (int64_t)blockIdx.x * kEnt;
 
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
   {
     const int e = t >> 4, p = t & 15;
     const int64_t j = j0 + e;
-    if (j < n_entries) {
+    if (e < kEnt && j < n_entries) {
       float c[32];
       const int ch0 = 32 * p;
       if (m == 1) {
@@ -143,45 +147,67 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
   __syncthreads();
 
   // ---- phase B: indexer projection k[o] = sum_ch W[o][ch] c~[ch], ascending fma chain.
-  // thread -> output o, entries 8h .. 8h+7
+  // thread -> output o, entries h*kHalf .. h*kHalf + kHalf - 1.  W_idx streams through LDS
+  // in transposed chunks of 64 channels ([ch][o], double-buffered) so every chain step
+  // reads its weight from LDS without bank conflicts and no step waits on global memory.
   {
+    constexpr int kHalf = kEnt / 2;
     const int o = t & (kIdxDim - 1), h = t >> 7;
-    float acc[8];
+    float acc[kHalf];
 #pragma unroll
-    for (int e = 0; e < 8; e++) acc[e] = 0.0f;
-    const uint4* wrow = reinterpret_cast<const uint4*>(w_idx + (int64_t)o * kD);
-    for (int cb = 0; cb < kD / 8; cb++) {
-      const uint4 u = wrow[cb];
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-      float wf[8];
+    for (int e = 0; e < kHalf; e++) acc[e] = 0.0f;
+    uint4 stage[4];
+    auto fetch = [&](int chunk) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        wf[2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
-        wf[2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
+        const int u = t + kThreads * q;  // 1024 pieces of 8 bf16: row u/8, part u%8
+        stage[q] = *reinterpret_cast<const uint4*>(w_idx + (int64_t)(u >> 3) * kD + kWChunk * chunk + 8 * (u & 7));
       }
+    };
+    auto spill = [&](int buf) {
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const float4 c0 = *reinterpret_cast<const float4*>(&s_c[8 * h + e][8 * cb]);
-        const float4 c1 = *reinterpret_cast<const float4*>(&s_c[8 * h + e][8 * cb + 4]);
-        float a = acc[e];
-        a = __builtin_fmaf(wf[0], c0.x, a);
-        a = __builtin_fmaf(wf[1], c0.y, a);
-        a = __builtin_fmaf(wf[2], c0.z, a);
-        a = __builtin_fmaf(wf[3], c0.w, a);
-        a = __builtin_fmaf(wf[4], c1.x, a);
-        a = __builtin_fmaf(wf[5], c1.y, a);
-        a = __builtin_fmaf(wf[6], c1.z, a);
-        a = __builtin_fmaf(wf[7], c1.w, a);
-        acc[e] = a;
+      for (int q = 0; q < 4; q++) {
+        const int u = t + kThreads * q, row = u >> 3, part = u & 7;
+        const uint32_t w4[4] = {stage[q].x, stage[q].y, stage[q].z, stage[q].w};
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          s_w[buf][8 * part + 2 * v][row] = (uint16_t)(w4[v] & 0xFFFFu);
+          s_w[buf][8 * part + 2 * v + 1][row] = (uint16_t)(w4[v] >> 16);
+        }
       }
+    };
+    fetch(0);
+    spill(0);
+    __syncthreads();
+    for (int chunk = 0; chunk < kD / kWChunk; chunk++) {
+      const int buf = chunk & 1;
+      if (chunk + 1 < kD / kWChunk) fetch(chunk + 1);
+#pragma unroll 2
+      for (int cb = 0; cb < kWChunk; cb += 4) {
+        float wf[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) wf[q] = bf16_bits_to_f32(s_w[buf][cb + q][o]);
+#pragma unroll
+        for (int e = 0; e < kHalf; e++) {
+          const float4 cv = *reinterpret_cast<const float4*>(&s_c[kHalf * h + e][kWChunk * chunk + cb]);
+          float a = acc[e];
+          a = __builtin_fmaf(wf[0], cv.x, a);
+          a = __builtin_fmaf(wf[1], cv.y, a);
+          a = __builtin_fmaf(wf[2], cv.z, a);
+          a = __builtin_fmaf(wf[3], cv.w, a);
+          acc[e] = a;
+        }
+      }
+      if (chunk + 1 < kD / kWChunk) spill(buf ^ 1);
+      __syncthreads();
     }
 #pragma unroll
-    for (int e = 0; e < 8; e++) s_k[8 * h + e][o] = acc[e];
+    for (int e = 0; e < kHalf; e++) s_k[kHalf * h + e][o] = acc[e];
   }
   __syncthreads();
 
   // ---- phase C: MXFP4 pack.  4 threads per (entry, group of 32), 8 elements each
-  {
+  if (t < kEnt * 16) {
     const int gi = t >> 2, sub = t & 3;
     const int e = gi >> 2, g = gi & 3;
     const int64_t j = j0 + e;
@@ -225,10 +251,16 @@ extern "C" int csa2_compress_pack(const uint16_t* latent_bf16, int64_t n_entries
     return CSA2_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(rope_cs) | reinterpret_cast<uintptr_t>(pool_w)) & 3)
     return CSA2_ERR_INVALID_ARG;
-  const int64_t grid = (n_entries + kEnt - 1) / kEnt;
-  if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(compress_pack_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
-                     kv_out, idx_out);
+  if (n_entries <= 64) {
+    hipLaunchKernelGGL(compress_pack_kernel<2>, dim3((unsigned)((n_entries + 1) / 2)), dim3(kThreads), 0,
+                       (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
+                       kv_out, idx_out);
+  } else {
+    const int64_t grid = (n_entries + 15) / 16;
+    if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(compress_pack_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
+                       kv_out, idx_out);
+  }
   return check_launch();
 }

@@ -24,6 +24,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;
+constexpr int kDepth = 4;  // tiles in flight per wave
 
 __device__ __forceinline__ bf16x8 cvt_fp4x8(uint32_t word, float scale) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
@@ -110,15 +111,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     return r;
   };
 
-  int32_t tile = tile_begin + wave;
-  bool valid_cur = false;
-  RawTile cur = tile < tile_end ? load(tile, valid_cur) : RawTile{};
-  for (; tile < tile_end; tile += kWaves) {
-    // prefetch the next tile of this wave before working on the current one
-    bool valid_nxt = false;
-    const int32_t nxt = tile + kWaves;
-    RawTile next = nxt < tile_end ? load(nxt, valid_nxt) : RawTile{};
-
+  auto process = [&](const RawTile& cur, bool valid, int32_t tile) {
     const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
     const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
     const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3], cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
@@ -132,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
 #pragma unroll
     for (int r = 0; r < 16; r++) part = __builtin_fmaf(wr[r], __builtin_fmaxf(acc[r], 0.0f), part);
     const float tot = part + __shfl_xor(part, 32);
-    const float sc = valid_cur ? tot : -__builtin_inff();
+    const float sc = valid ? tot : -__builtin_inff();
     const int32_t p = tile * kTile + n;
     if (g == 0 && p < width) srow[p] = sc;
     if (block_max != nullptr) {
@@ -141,8 +134,30 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
       bm = __builtin_fmaxf(bm, __shfl_xor(bm, 4));
       if (g == 0 && (n & 7) == 0 && p < width) block_max[(int64_t)t * nbw + (p >> 3)] = bm;
     }
-    cur = next;
-    valid_cur = valid_nxt;
+  };
+
+  // software pipeline: kDepth tiles of this wave are in flight while one is processed
+  RawTile pipe[kDepth];
+  bool pv[kDepth];
+#pragma unroll
+  for (int u = 0; u < kDepth; u++) {
+    const int32_t tl = tile_begin + wave + u * kWaves;
+    pv[u] = false;
+    if (tl < tile_end) pipe[u] = load(tl, pv[u]);
+  }
+  for (int32_t base = tile_begin + wave; base < tile_end; base += kDepth * kWaves) {
+#pragma unroll
+    for (int u = 0; u < kDepth; u++) {
+      const int32_t tl = base + u * kWaves;
+      if (tl < tile_end) {
+        const RawTile cur = pipe[u];
+        const bool cv = pv[u];
+        const int32_t nx = tl + kDepth * kWaves;
+        pv[u] = false;
+        if (nx < tile_end) pipe[u] = load(nx, pv[u]);
+        process(cur, cv, tl);
+      }
+    }
   }
 }
 

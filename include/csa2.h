@@ -129,10 +129,13 @@ int csa2_index_score(const uint16_t *q_idx_bf16, const float *head_w, const uint
  *   Candidate mode (pool_blocks != NULL, [n_q, M]): scores [n_q, width = 8M] laid out as
  *   csa2_index_score candidate mode; pool_out must be NULL.
  *   topk_out [n_q, K]: selected entry ids (relative to the sequence) ascending, -1 pad.
- *   workspace: device scratch of csa2_block_topk_workspace(...) bytes (may be NULL when
- *   that size is 0).
- *   Errors: INVALID_ARG, UNSUPPORTED (block != 8, M > 2048, K > 512, K < 1, M < 1),
- *   WORKSPACE (workspace too small).
+ *   workspace: device scratch of at least csa2_block_topk_workspace(n_q, width, M, K)
+ *   bytes, 4-byte aligned.  Its histogram region must be all zero before the first call
+ *   (allocate it zero-filled); every call that completes leaves it zero again, so one
+ *   buffer can be reused by consecutive calls on the same stream.  Calls that overlap in
+ *   time must not share a workspace.
+ *   Errors: INVALID_ARG, UNSUPPORTED (block != 8, M > 2048, K > 512, K < 1, M < 1, rows
+ *   longer than 2^20 blocks), WORKSPACE (workspace missing or too small).
  */
 size_t csa2_block_topk_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K);
 int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, int32_t width,

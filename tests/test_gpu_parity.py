@@ -256,3 +256,28 @@ def test_determinism(c):
         outs.append([host(x) for x in (s, bm, pool, topk, out, lse)])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_block_topk_workspace_reuse_and_1m_rows(c):
+    log("block_topk workspace reuse, 524288-wide rows")
+    width, K, M = 524288, 512, 2048
+    ws = torch.zeros(c.block_topk_workspace(4, width, M, K), dtype=torch.uint8, device="cuda")
+    for seed, tie in ((60, 0.0), (61, 0.05), (62, 0.0)):
+        nvis = np.array([524288, 524287, 400001, 17], np.int32)
+        s = synth.random_scores(seed, 4, width, tie_frac=tie)
+        pool_ref, topk_ref = oracle.block_topk(s, nvis, K=K, M=M)
+        pool, topk = c.block_topk(dev(s), dev(nvis), K=K, M=M, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(pool), pool_ref), f"pool differs (seed {seed})"
+        assert np.array_equal(host(topk), topk_ref), f"topk differs (seed {seed})"
+    # the candidate mode shares the buffer too
+    nvis = np.array([524288] * 4, np.int32)
+    s = synth.random_scores(63, 4, 8 * M)
+    pool_in = np.sort(np.random.default_rng(0).choice(65536, (4, M)), axis=1).astype(np.int32)
+    for t in range(4):
+        pool_in[t] = np.sort(np.random.default_rng(t).choice(65536, M, replace=False))
+    _, topk_ref = oracle.block_topk(s, nvis, K=K, pool_blocks=pool_in)
+    _, topk = c.block_topk(dev(s), dev(nvis), K=K, pool_blocks=dev(pool_in), workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(topk), topk_ref)
+    assert int(ws[: 4 * 4096 * 4].view(torch.int32).abs().sum().item()) == 0, "histogram not returned to zero"
