@@ -57,17 +57,23 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin, bool active)
   if ((todo >> lane) & 1ull) atomicAdd(&h[bin], 1u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row broadcasts.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum of v over the threads of a workgroup of NT threads, in thread
 // order; total receives the sum over all threads.  s_w holds NT/64 ints.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = (int)wave_incl_scan((uint32_t)v);
   if (lane == 63) s_w[wave] = x;
   __syncthreads();
   int off = 0, tot = 0;
@@ -83,7 +89,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
 }
 
 struct SelScratch {
-  uint32_t hist[256];
+  uint32_t hist[2][256];  // double-buffered digit histogram
   int32_t wave_a[kFWaves];
   int32_t wave_b[kFWaves];
   uint32_t prefix;
@@ -107,33 +113,30 @@ __device__ int block_select(F key_at, int n, int k, SelScratch& s, int32_t* out)
     s.eq_total = -1;
     s.take_all = 0;
   }
+  if (tid < 256) s.hist[0][tid] = 0;
   uint32_t mask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  int buf = 0;
+  for (int shift = 24; shift >= 0; shift -= 8, buf ^= 1) {
     __syncthreads();
     // stop once every key sharing the prefix is needed (or every key is taken)
     if (s.take_all || s.eq_total == s.remain) break;
-    if (tid < 256) s.hist[tid] = 0;
-    __syncthreads();
     const uint32_t prefix = s.prefix;
+    if (tid < 256) s.hist[buf ^ 1][tid] = 0;  // the next pass's buffer
     for (int base = 0; base < n; base += kFThreads) {
       const int i = base + tid;
       const uint32_t key = i < n ? key_at(i) : 0u;
-      hist_add(s.hist, (key >> shift) & 255u, key != 0u && (key & mask) == prefix);
+      hist_add(s.hist[buf], (key >> shift) & 255u, key != 0u && (key & mask) == prefix);
     }
     __syncthreads();
     if (tid < 64) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
       uint32_t c[4], local = 0;
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        c[q] = s.hist[255 - 4 * tid - q];
+        c[q] = s.hist[buf][255 - 4 * tid - q];
         local += c[q];
       }
-      uint32_t incl = local;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (tid >= o) incl += y;
-      }
+      const uint32_t incl = wave_incl_scan(local);
       const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       uint32_t above = incl - local;
       const uint32_t rem = (uint32_t)s.remain;
@@ -163,7 +166,6 @@ __device__ int block_select(F key_at, int n, int k, SelScratch& s, int32_t* out)
     need_eq = n;
     eq_total = 0;
   }
-  __syncthreads();
   const bool all_eq = need_eq >= eq_total;
   // ---- ordered compaction: each wave owns a contiguous segment
   const int seg = (n + kFWaves - 1) / kFWaves;
@@ -181,18 +183,20 @@ __device__ int block_select(F key_at, int n, int k, SelScratch& s, int32_t* out)
     s.wave_b[wave] = eq;
   }
   __syncthreads();
-  int eq_acc = 0, sel_acc = 0, eq_off = 0, sel_off = 0;
-  for (int w = 0; w < kFWaves; w++) {
-    if (w == wave) {
-      eq_off = eq_acc;
-      sel_off = sel_acc;
-    }
-    const int e_w = s.wave_b[w];
-    eq_acc += e_w;
-    sel_acc += s.wave_a[w] + (all_eq ? e_w : max(0, min(e_w, need_eq - (eq_acc - e_w))));
+  // per-wave offsets among equal keys and among survivors, lanes 0..15 = waves 0..15
+  const uint32_t e_l = lane < kFWaves ? (uint32_t)s.wave_b[lane] : 0u;
+  const uint32_t e_incl = wave_incl_scan(e_l);
+  const uint32_t e_before = e_incl - e_l;
+  uint32_t take = e_l;
+  if (!all_eq) {
+    const int rest = need_eq - (int)e_before;
+    take = (uint32_t)max(0, min((int)e_l, rest));
   }
-  const int total = sel_acc;
-  __syncthreads();
+  const uint32_t s_l = lane < kFWaves ? (uint32_t)s.wave_a[lane] + take : 0u;
+  const uint32_t s_incl = wave_incl_scan(s_l);
+  const int total = __builtin_amdgcn_readlane((int)s_incl, kFWaves - 1);
+  const int eq_off = __builtin_amdgcn_readlane((int)e_before, wave);
+  const int sel_off = __builtin_amdgcn_readlane((int)(s_incl - s_l), wave);
   int run_eq = eq_off, run_sel = sel_off;
   for (int b = lo; b < hi; b += 64) {
     const int i = b + lane;

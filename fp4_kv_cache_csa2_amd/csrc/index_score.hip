@@ -24,7 +24,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;
-constexpr int kDepth = 4;  // tiles in flight per wave
+#ifndef CSA2_INDEX_DEPTH
+#define CSA2_INDEX_DEPTH 4
+#endif
+constexpr int kDepth = CSA2_INDEX_DEPTH;  // tiles in flight per wave
 
 __device__ __forceinline__ bf16x8 cvt_fp4x8(uint32_t word, float scale) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
@@ -50,68 +53,84 @@ struct RawTile {
   uint32_t sc;
 };
 
+// max over the 8 lanes of each aligned group of 8 (DPP within rows)
+__device__ __forceinline__ float max8_lanes(float v) {
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return v;
+}
+
+// v(lane) + v(lane ^ 32)
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+
 __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
     int32_t width, int32_t tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
   const int t = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 31, g = lane >> 5;
   const int32_t nvis = q_nvis[t];
   const int64_t base = q_base[t];
   const int32_t ntiles = (width + kTile - 1) / kTile;
   const int32_t tile_begin = blockIdx.x * tiles_per_wg;
   const int32_t tile_end = min(tile_begin + tiles_per_wg, ntiles);
-  if (tile_begin >= ntiles) return;
+  const int32_t first = tile_begin + wave;
+  const int32_t nt = first < tile_end ? (tile_end - first + kWaves - 1) / kWaves : 0;  // this wave's tiles
+  const int32_t nbw = (width + kBlock - 1) / kBlock;
+  float* srow = scores + (int64_t)t * width;
+
+  if (nvis <= 0) {  // nothing visible: the row is all -inf
+    for (int32_t k = 0; k < nt; k++) {
+      const int32_t p = (first + k * kWaves) * kTile + n;
+      if (g == 0 && p < width) srow[p] = -__builtin_inff();
+      if (block_max != nullptr && g == 0 && (n & 7) == 0 && p < width)
+        block_max[(int64_t)t * nbw + (p >> 3)] = -__builtin_inff();
+    }
+    return;
+  }
 
   // query: head n, dims 64g .. 64g + 63 as eight bf16x8 A fragments
   bf16x8 a[8];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
 #pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const uint4 u = qp[s];
-      a[s] = __builtin_bit_cast(bf16x8, u);
-    }
+    for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
   }
   // head weight of each accumulator row held by this lane: row = 8(r/4) + 4g + r%4
   float wr[16];
 #pragma unroll
   for (int r = 0; r < 16; r++) wr[r] = head_w[(int64_t)t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)];
 
-  const int32_t nbw = (width + kBlock - 1) / kBlock;
-  float* srow = scores + (int64_t)t * width;
-
-  auto entry_of = [&](int32_t tile, bool& valid) -> int64_t {
-    const int32_t p = tile * kTile + n;
+  const uint8_t* last_row = idx_cache + (base + nvis - 1) * kIdxBytes;
+  // the cache row of this lane's entry in tile k; invalid slots read the last visible row
+  auto row_of = [&](int32_t k, bool& valid) -> const uint8_t* {
+    const int32_t p = (first + k * kWaves) * kTile + n;
+    int64_t j;
     if (pool_blocks == nullptr) {
+      j = p;
       valid = p < nvis;
-      return p;
-    }
-    const int32_t slot = p >> 3;
-    const int32_t b = slot < M ? pool_blocks[(int64_t)t * M + slot] : -1;
-    const int64_t j = (int64_t)b * kBlock + (p & 7);
-    valid = b >= 0 && j < nvis;
-    return j;
-  };
-  auto load = [&](int32_t tile, bool& valid) -> RawTile {
-    RawTile r;
-    const int64_t j = entry_of(tile, valid);
-    if (valid) {
-      const uint8_t* row = idx_cache + (base + j) * kIdxBytes;
-      r.lo = *reinterpret_cast<const u32x4_a4*>(row + 32 * g);
-      r.hi = *reinterpret_cast<const u32x4_a4*>(row + 32 * g + 16);
-      r.sc = *reinterpret_cast<const uint32_t*>(row + 64);
     } else {
-      r.lo = u32x4_a4{0u, 0u, 0u, 0u};
-      r.hi = r.lo;
-      r.sc = 127u * 0x01010101u;
+      const int32_t slot = p >> 3;
+      const int32_t b = slot < M ? pool_blocks[(int64_t)t * M + slot] : -1;
+      j = (int64_t)b * kBlock + (p & 7);
+      valid = b >= 0 && j < nvis;
     }
-    return r;
+    return valid ? idx_cache + (base + j) * kIdxBytes : last_row;
   };
-
-  auto process = [&](const RawTile& cur, bool valid, int32_t tile) {
+  auto load = [&](int32_t k, RawTile& r, bool& valid) {
+    const uint8_t* row = row_of(k, valid);
+    r.lo = *reinterpret_cast<const u32x4_a4*>(row + 32 * g);
+    r.hi = *reinterpret_cast<const u32x4_a4*>(row + 32 * g + 16);
+    r.sc = *reinterpret_cast<const uint32_t*>(row + 64);
+  };
+  auto process = [&](const RawTile& cur, bool valid, int32_t k) {
     const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
     const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
     const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3], cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
@@ -121,18 +140,20 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
       const bf16x8 b = cvt_fp4x8(words[s], s < 4 ? x0 : x1);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
     }
-    float part = 0.0f;
+    // ReLU, head weight and the sum over this lane's 16 heads as four short chains
+    float part[4];
 #pragma unroll
-    for (int r = 0; r < 16; r++) part = __builtin_fmaf(wr[r], __builtin_fmaxf(acc[r], 0.0f), part);
-    const float tot = part + __shfl_xor(part, 32);
-    const float sc = valid ? tot : -__builtin_inff();
-    const int32_t p = tile * kTile + n;
-    if (g == 0 && p < width) srow[p] = sc;
+    for (int c = 0; c < 4; c++) {
+      part[c] = wr[4 * c] * __builtin_fmaxf(acc[4 * c], 0.0f);
+#pragma unroll
+      for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], __builtin_fmaxf(acc[4 * c + r], 0.0f), part[c]);
+    }
+    const float sc = valid ? sum_halves((part[0] + part[1]) + (part[2] + part[3])) : -__builtin_inff();
+    const int32_t p = (first + k * kWaves) * kTile + n;
+    if (g == 0 && p < width) __builtin_nontemporal_store(sc, srow + p);
     if (block_max != nullptr) {
-      float bm = __builtin_fmaxf(sc, __shfl_xor(sc, 1));
-      bm = __builtin_fmaxf(bm, __shfl_xor(bm, 2));
-      bm = __builtin_fmaxf(bm, __shfl_xor(bm, 4));
-      if (g == 0 && (n & 7) == 0 && p < width) block_max[(int64_t)t * nbw + (p >> 3)] = bm;
+      const float bm = max8_lanes(sc);
+      if (g == 0 && (n & 7) == 0 && p < width) __builtin_nontemporal_store(bm, block_max + (int64_t)t * nbw + (p >> 3));
     }
   };
 
@@ -140,22 +161,17 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
   RawTile pipe[kDepth];
   bool pv[kDepth];
 #pragma unroll
-  for (int u = 0; u < kDepth; u++) {
-    const int32_t tl = tile_begin + wave + u * kWaves;
-    pv[u] = false;
-    if (tl < tile_end) pipe[u] = load(tl, pv[u]);
-  }
-  for (int32_t base = tile_begin + wave; base < tile_end; base += kDepth * kWaves) {
+  for (int u = 0; u < kDepth; u++)
+    if (u < nt) load(u, pipe[u], pv[u]);
+  for (int32_t k0 = 0; k0 < nt; k0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; u++) {
-      const int32_t tl = base + u * kWaves;
-      if (tl < tile_end) {
+      const int32_t k = k0 + u;
+      if (k < nt) {
         const RawTile cur = pipe[u];
         const bool cv = pv[u];
-        const int32_t nx = tl + kDepth * kWaves;
-        pv[u] = false;
-        if (nx < tile_end) pipe[u] = load(nx, pv[u]);
-        process(cur, cv, tl);
+        if (k + kDepth < nt) load(k + kDepth, pipe[u], pv[u]);
+        process(cur, cv, k);
       }
     }
   }
@@ -163,6 +179,24 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
 
 }  // namespace
 }  // namespace csa2
+
+namespace {
+// workgroups of index_score_kernel that fit on the device at once (queried per device)
+int resident_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csa2::index_score_kernel, csa2::kThreads, 0) !=
+            hipSuccess || per_cu <= 0)
+      per_cu = 2;
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
+}
+}  // namespace
 
 extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
                                 const uint8_t* idx_cache, const int64_t* q_base,
@@ -186,8 +220,8 @@ extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
        reinterpret_cast<uintptr_t>(block_max)) & 3)
     return CSA2_ERR_INVALID_ARG;
   const int32_t ntiles = (width + kTile - 1) / kTile;
-  // aim for ~2048 workgroups in total; each wave gets an equal share of its workgroup's tiles
-  int64_t chunks = (2048 + n_q - 1) / n_q;
+  // one full round of resident workgroups, each streaming a long contiguous range
+  int64_t chunks = (resident_workgroups() + n_q - 1) / n_q;
   const int64_t max_chunks = (ntiles + kWaves - 1) / kWaves;
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
