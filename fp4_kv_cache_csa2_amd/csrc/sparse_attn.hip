@@ -7,13 +7,15 @@
 // entries are dequantised before the matmuls ([ZB] §2.4.4).
 //
 // Design.  A workgroup of 4 waves serves one query; wave w owns heads 16w .. 16w+15.
-// Keys are processed in chunks of 64: the selected entries (gathered 288-byte rows) and
-// the window rows are decoded once into LDS as f16 (exact: an E2M1 code times an E4M3
-// scale has at most 6 significant bits; bf16 window values are exact in f16's normal
-// range), both row-major (QK^T operand) and transposed (PV operand).  QK^T and PV run on
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation; the softmax is online across chunks
-// in fp32.  For small batches the key chunks of a query are split across workgroups and
-// a merge kernel combines the partial (o, m, l) exactly like flash-decoding.
+// Keys are processed in chunks of 64: the selected entries (gathered 288-byte rows,
+// prefetched one chunk ahead) and the window rows are decoded once into LDS as f16, row
+// major (exact: an E2M1 code times an E4M3 scale has at most 6 significant bits; bf16
+// window values are exact in f16's normal range).  QK^T reads the key rows directly; PV
+// takes its key-major operand from the same tile with transposing LDS reads
+// (ds_read_b64_tr_b16), so no second copy is stored.  Both matmuls run on
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation; the softmax is online across chunks in
+// fp32.  For small batches the key chunks of a query are split across workgroups and a
+// merge kernel combines the partial (o, m, l) exactly like flash-decoding.
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -22,13 +24,13 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 64;
-constexpr int kKStride = kD + 8;        // f16 elements per sK row
-constexpr int kVStride = kChunk + 8;    // f16 elements per sVT row
+constexpr int kKStride = kD + 8;        // f16 elements per key row in LDS (1040 B: 8-B aligned rows)
 constexpr int kPStride = kChunk + 8;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 struct AttnShared {
-  _Float16 k[kChunk * kKStride];        // keys row-major [key][dim]
-  _Float16 vt[kD * kVStride];           // keys transposed [dim][key]
+  _Float16 k[kChunk * kKStride];        // decoded keys of the chunk, row-major [key][dim]
   _Float16 p[kWaves * 16 * kPStride];   // per-wave probabilities [head][key]
   int32_t valid[kChunk];
 };
@@ -37,6 +39,15 @@ __device__ __forceinline__ float e2m1_value(uint32_t c4) {
   const float v = e2m1_mag(c4 & 7u);
   return (c4 & 8u) ? -v : v;
 }
+
+// Raw bytes of one key slot for one thread (a quarter of a key: 128 dims).  Selected
+// entries are prefetched a chunk ahead; window rows (bf16, 4x the bytes) load when staged.
+struct KeyRaw {
+  uint4 pay[4];   // FP4 payload of a selected entry
+  uint2 scw;      // its 8 E4M3 scale bytes
+  int kind;       // 0 empty, 1 selected entry, 2 window row
+  int row;        // window row index (kind 2)
+};
 
 __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_cache,
@@ -47,13 +58,75 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     float* __restrict__ ws_ml) {
   __shared__ AttnShared sh;
   const int t = blockIdx.y, split = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
   const int c_begin = split * chunks_per_split;
   const int c_end = min(c_begin + chunks_per_split, n_chunks);
   const int64_t base = q_base[t];
   const int32_t nswa = min(max(swa_len[t], 0), kMaxSwa);
   const int64_t swa0 = swa_start[t];
+  const int kk = tid >> 2, qq = tid & 3;  // key slot and quarter this thread decodes
+
+  // raw loads of this thread's key quarter for chunk c
+  auto fetch = [&](int c, KeyRaw& r) {
+    const int x = c * kChunk + kk;
+    r.kind = 0;
+    if (x < K) {
+      const int32_t id = topk[(int64_t)t * K + x];
+      if (id >= 0) {
+        r.kind = 1;
+        const uint8_t* row = kv_cache + (base + id) * kKvBytes;
+#pragma unroll
+        for (int v = 0; v < 4; v++) r.pay[v] = reinterpret_cast<const uint4*>(row + 64 * qq)[v];
+        r.scw = *reinterpret_cast<const uint2*>(row + 256 + 8 * qq);
+      }
+    } else if (x - K < nswa) {
+      r.kind = 2;
+      r.row = x - K;
+    }
+  };
+  // decode to f16 (exact) and store the key quarter row-major in LDS
+  auto stage = [&](const KeyRaw& r) {
+    _Float16* krow = sh.k + kk * kKStride + 128 * qq;
+    if (r.kind == 1) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const uint32_t wd[4] = {r.pay[v].x, r.pay[v].y, r.pay[v].z, r.pay[v].w};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+          const int grp = 2 * v + (q4 >> 1);  // local group of 16 dims
+          const uint32_t sb = ((grp < 4 ? r.scw.x : r.scw.y) >> (8 * (grp & 3))) & 255u;
+          const float S = e4m3_value(sb);
+          f16x8 pk;
+#pragma unroll
+          for (int nb = 0; nb < 8; nb++) pk[nb] = (_Float16)(e2m1_value((wd[q4] >> (4 * nb)) & 15u) * S);
+          *reinterpret_cast<f16x8*>(krow + 32 * v + 8 * q4) = pk;
+        }
+      }
+    } else if (r.kind == 2) {
+      const uint4* src = reinterpret_cast<const uint4*>(swa + (swa0 + r.row) * kD + 128 * qq);
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const uint4 u = src[v];
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+        f16x8 pk;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
+          pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
+        }
+        *reinterpret_cast<f16x8*>(krow + 8 * v) = pk;
+      }
+    } else {
+      f16x8 z;
+#pragma unroll
+      for (int e = 0; e < 8; e++) z[e] = (_Float16)0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; v++) *reinterpret_cast<f16x8*>(krow + 8 * v) = z;
+    }
+    if (qq == 0) sh.valid[kk] = r.kind != 0 ? 1 : 0;
+  };
 
   // query fragments: head 16w + i, dims 32s + 8g .. +7, as f16 (exact in the normal range)
   f16x8 qa[16];
@@ -81,69 +154,12 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     l_run[r] = 0.0f;
   }
 
+  KeyRaw raw;
+  if (c_begin < c_end) fetch(c_begin, raw);
   for (int c = c_begin; c < c_end; c++) {
-    __syncthreads();
-    // ---- decode 64 keys: thread -> key kk, dims 128qq .. 128qq + 127
-    {
-      const int kk = tid >> 2, qq = tid & 3;
-      const int x = c * kChunk + kk;
-      _Float16* krow = sh.k + kk * kKStride + 128 * qq;
-      _Float16* vcol = sh.vt + (128 * qq) * kVStride + kk;
-      auto emit = [&](int d0, const f16x8& pk) {
-        *reinterpret_cast<f16x8*>(krow + d0) = pk;
-#pragma unroll
-        for (int e = 0; e < 8; e++) vcol[(d0 + e) * kVStride] = pk[e];
-      };
-      int kind = 0;  // 0 = empty slot, 1 = selected entry, 2 = window row
-      int32_t id = -1;
-      if (x < K) {
-        id = topk[(int64_t)t * K + x];
-        kind = id >= 0 ? 1 : 0;
-      } else if (x - K < nswa) {
-        kind = 2;
-      }
-      if (kind == 1) {
-        const uint8_t* row = kv_cache + (base + id) * kKvBytes;
-        const uint4* pay = reinterpret_cast<const uint4*>(row + 64 * qq);
-        const uint2 scw = *reinterpret_cast<const uint2*>(row + 256 + 8 * qq);
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-          const uint4 u = pay[v];
-          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int q4 = 0; q4 < 4; q4++) {
-            const int grp = 2 * v + (q4 >> 1);  // local group of 16 dims
-            const uint32_t sb = ((grp < 4 ? scw.x : scw.y) >> (8 * (grp & 3))) & 255u;
-            const float S = e4m3_value(sb);
-            f16x8 pk;
-#pragma unroll
-            for (int nb = 0; nb < 8; nb++) pk[nb] = (_Float16)(e2m1_value((wd[q4] >> (4 * nb)) & 15u) * S);
-            emit(32 * v + 8 * q4, pk);
-          }
-        }
-      } else if (kind == 2) {
-        const uint4* src = reinterpret_cast<const uint4*>(swa + (swa0 + (x - K)) * kD + 128 * qq);
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-          const uint4 u = src[v];
-          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-          f16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
-            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
-          }
-          emit(8 * v, pk);
-        }
-      } else {
-        f16x8 z;
-#pragma unroll
-        for (int e = 0; e < 8; e++) z[e] = (_Float16)0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; v++) emit(8 * v, z);
-      }
-      if (qq == 0) sh.valid[kk] = kind != 0 ? 1 : 0;
-    }
+    __syncthreads();  // the previous chunk's LDS reads are done
+    stage(raw);
+    if (c + 1 < c_end) fetch(c + 1, raw);  // next chunk's gather overlaps this chunk's math
     __syncthreads();
 
     // ---- S = Q K^T for 4 tiles of 16 keys
@@ -157,6 +173,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
         const f16x8 b = *reinterpret_cast<const f16x8*>(sh.k + (16 * kt + i) * kKStride + 32 * s + 8 * g);
         sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], b, sacc[kt], 0, 0, 0);
       }
+      if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound how far LDS reads are hoisted
     }
     // ---- online softmax over this chunk; lane holds rows (heads) 4g + r, column (key) 16kt + i
     float pv[4][4];
@@ -207,14 +224,23 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
 #pragma unroll
       for (int r = 0; r < 4; r++) pw[(4 * g + r) * kPStride + 16 * kt + i] = (_Float16)pv[kt][r];
     }
-    __syncthreads();
-    // ---- O += P V: A = P [head i][keys 32ks + 8g ..], B = V^T rows (dims) 16dt + i
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P stores are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // ---- O += P V.  A = P [head i][keys 32ks + 8g ..].  B = V[keys][dim 16dt + i]: two
+    // transposing LDS reads give this lane 8 consecutive keys of its dim from the row-major tile
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
       const f16x8 pa = *reinterpret_cast<const f16x8*>(pw + i * kPStride + 32 * ks + 8 * g);
+      const int kb = 32 * ks + 8 * g + (i >> 2);
 #pragma unroll
       for (int dt = 0; dt < 32; dt++) {
-        const f16x8 vb = *reinterpret_cast<const f16x8*>(sh.vt + (16 * dt + i) * kVStride + 32 * ks + 8 * g);
+        if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+        const _Float16* p0 = sh.k + kb * kKStride + 16 * dt + 4 * (i & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(p0 + 4 * kKStride));
+        const f16x8 vb = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt], 0, 0, 0);
       }
     }
