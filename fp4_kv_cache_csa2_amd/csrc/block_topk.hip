@@ -7,23 +7,30 @@
 // union of the selected blocks, |P_t| <= 2048 x 8).  Ties go to the lower index, NaN
 // ranks as -inf, outputs are ascending and padded with -1.
 //
-// Design (three kernels, launched back to back on the caller's stream):
+// Design (three kernels, launched back to back on the caller's stream).  The ranking key
+// of a value is an order-preserving uint32 map of the fp32 value (NaN as -inf); its top
+// 12 bits are its histogram bin.
 //   K1 hist     many workgroups per query build a 4096-bin histogram of the ranking keys
-//               (top 12 bits of an order-preserving uint32 map of the fp32 value) in LDS
-//               and add it into a per-query histogram in the workspace.
-//   K2 collect  the same grid finds the bin that holds the k-th largest key and writes,
-//               in ascending order, the ids of every key in that bin or above into one
-//               segment per workgroup: a short ordered list that is a superset of the
-//               selection.
-//   K3 finalize one 1024-thread workgroup per query runs an exact 4-pass radix select on
-//               that list (ties by lower id), appends the forced newest block, writes the
-//               pool, and takes the Top-K among the entries of the K+1 highest pool blocks:
-//               every global Top-K member's block ranks within the first K+1 blocks, so
-//               this is the Top-K of the pool and of the whole row.  K3 returns the
-//               histogram to zero.  If the list overflows LDS (massive ties), K3 selects
-//               straight from the full key row instead, with the same exact rules.
-// The histogram region of the workspace must be zero before the first call; every call
-// leaves it zero.
+//               (older blocks' maxima in Full mode, pool entries in candidate mode) in
+//               LDS and add it into a per-query histogram in the workspace.
+//   K2 collect  the same grid finds the bin of the k-th largest key and writes, in
+//               ascending order, the ids and keys of every item in that bin or above into
+//               one segment per workgroup (list A).  In Full mode it also lists the
+//               entries of the blocks in or above the bin of the K-th largest older block,
+//               and of the newest block, whose keys reach that bin's lower edge (list B),
+//               and counts their keys in a second histogram.  Every global Top-K entry is
+//               in list B: the K highest older blocks alone hold K entries at or above
+//               that edge.  The Top-K of the pool equals the global Top-K of the row, since
+//               any entry outside the pool is outranked by the M-1 block maxima above it.
+//   K3 finalize one 1024-thread workgroup per query and role, the roles in parallel: the
+//               pool from list A, the Top-K from list B (or from list A in candidate
+//               mode).  Each reads its histogram (the count above the boundary bin and
+//               the bin's own count), returns it to zero, gathers its list and refines
+//               only the boundary bin's low 20 bits, with the keys held in registers (one
+//               barrier per 8-bit radix pass).  If a list overflows LDS (massive ties), K3
+//               selects straight from the full row instead, with the same exact rules.
+// The two histogram regions of the workspace must be zero before the first call; every
+// call leaves them zero.
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -37,24 +44,14 @@ constexpr int kFThreads = 1024;    // K3 workgroup size
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kListCap = 12288;    // ordered candidate list held in LDS by K3
 constexpr int kMaxG = 1024;        // workgroups per query row in K1 / K2 (rows up to 2^20 items)
+constexpr int kSegB = 1024;        // entries per K2 workgroup in the Top-K list (more: exact fallback)
 
 // ------------------------------------------------------------------ shared helpers
 
-// LDS histogram add; lanes of a wave that share a bin are merged (up to two bins) so a
-// concentrated key distribution does not serialise on one LDS address.
+// LDS histogram add.  Plain atomics: lanes that hit one bin serialise at about two cycles
+// a lane, which is still cheaper than merging equal bins with ballots and lane reads.
 __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin, bool active) {
-  const int lane = __lane_id();
-  uint64_t todo = __ballot(active);
-#pragma unroll
-  for (int it = 0; it < 2; it++) {
-    if (todo == 0) break;
-    const int leader = __ffsll((unsigned long long)todo) - 1;  // wave-uniform
-    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
-    const uint64_t same = __ballot(active && bin == lb) & todo;
-    if (lane == leader) atomicAdd(&h[lb], (uint32_t)__popcll(same));
-    todo &= ~same;
-  }
-  if ((todo >> lane) & 1ull) atomicAdd(&h[bin], 1u);
+  if (active) atomicAdd(&h[bin], 1u);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row broadcasts.
@@ -213,6 +210,186 @@ __device__ int block_select(F key_at, int n, int k, SelScratch& s, int32_t* out)
   return total;
 }
 
+constexpr int kPer = kListCap / kFThreads;  // list keys per K3 thread, held in registers
+constexpr int kBinsPer = kBins / kFThreads; // histogram bins per K3 thread
+constexpr int kSegPer = kMaxG / kFThreads;  // K2 segments per K3 thread
+
+struct ListScratch {
+  uint32_t hist[3][256];  // digit histograms, rotated so each pass needs one barrier
+  int32_t wcnt[2][kFWaves];
+  uint32_t red[3][kFWaves];
+};
+
+// Exact selection over a list of at most kListCap keys in LDS by the K3 workgroup.  The
+// list is in ascending id order and ties go to the earlier position.  The caller may pass
+// what it already knows: every key whose bits under `mask` exceed `prefix` is selected,
+// and `remain` more are wanted among the `eq_total` keys equal to `prefix` under `mask`
+// (eq_total < 0: not known); `shift` is the number of low bits not yet resolved.  With
+// mask == 0 the search starts below the common leading bits of the smallest and largest
+// key, so the first digit does not pile every key into one histogram bin.  Zero keys are
+// never selected.  Writes the chosen positions ascending to out[], returns their number,
+// and sets *thr to a lower bound of every selected key (the resolved prefix).  Wave w
+// owns the contiguous run [w*seg, (w+1)*seg) and holds it in registers, so a radix pass
+// is a burst of LDS atomics, one barrier and a scan that each wave does itself.
+__device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t prefix, uint32_t mask, int shift,
+                                           int remain, int eq_total, ListScratch& s, int32_t* out, uint32_t* thr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  prefix = __builtin_amdgcn_readfirstlane(prefix);
+  mask = __builtin_amdgcn_readfirstlane(mask);
+  shift = __builtin_amdgcn_readfirstlane(shift);
+  remain = __builtin_amdgcn_readfirstlane(remain);
+  eq_total = __builtin_amdgcn_readfirstlane(eq_total);
+  n = __builtin_amdgcn_readfirstlane(n);
+  if (tid < 256) {
+    s.hist[0][tid] = 0u;
+    s.hist[1][tid] = 0u;
+  }
+  const int seg = (n + kFWaves - 1) / kFWaves;
+  const int lo = min(n, wave * seg);
+  const int len = __builtin_amdgcn_readfirstlane(min(n, lo + seg) - lo);  // wave-uniform
+  *thr = 0u;
+  if (remain <= 0 || n <= 0) {
+    __syncthreads();
+    return 0;
+  }
+  uint32_t kr[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) kr[j] = (64 * j + lane < len) ? keys[lo + 64 * j + lane] : 0u;
+  if (mask == 0u) {
+    // smallest and largest non-zero key, and their count
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, cnt = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      if (64 * j >= len) continue;
+      const uint32_t key = kr[j];
+      kmin = min(kmin, key != 0u ? key : 0xFFFFFFFFu);
+      kmax = max(kmax, key);
+      cnt += key != 0u ? 1u : 0u;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+      cnt += (uint32_t)__shfl_xor((int)cnt, o);
+    }
+    if (lane == 0) {
+      s.red[0][wave] = kmin;
+      s.red[1][wave] = kmax;
+      s.red[2][wave] = cnt;
+    }
+    __syncthreads();
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
+    cnt = 0u;
+#pragma unroll
+    for (int w = 0; w < kFWaves; w++) {
+      kmin = min(kmin, s.red[0][w]);
+      kmax = max(kmax, s.red[1][w]);
+      cnt += s.red[2][w];
+    }
+    kmin = __builtin_amdgcn_readfirstlane(kmin);
+    kmax = __builtin_amdgcn_readfirstlane(kmax);
+    cnt = __builtin_amdgcn_readfirstlane(cnt);
+    if (cnt == 0u) {
+      __syncthreads();
+      return 0;
+    }
+    const int common = kmin == kmax ? 32 : __builtin_clz(kmin ^ kmax);
+    mask = common == 0 ? 0u : (common == 32 ? 0xFFFFFFFFu : ~0u << (32 - common));
+    prefix = kmax & mask;
+    shift = 32 - common;
+    eq_total = (int)cnt;
+  }
+  __syncthreads();
+  for (int p = 0; shift > 0 && (eq_total < 0 || remain < eq_total); p++) {
+    const int nshift = max(shift - 8, 0);
+    const uint32_t dmask = (1u << (shift - nshift)) - 1u;
+    uint32_t* h = s.hist[p % 3];
+    if (tid < 256) s.hist[(p + 1) % 3][tid] = 0u;  // last read two passes ago
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      if (64 * j >= len) continue;  // uniform: the wave's remaining slots are empty
+      const uint32_t key = kr[j];
+      if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> nshift) & dmask], 1u);
+    }
+    __syncthreads();
+    // lane l owns digits 255-4l .. 252-4l (descending)
+    uint32_t c[4], local = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      c[q] = h[255 - 4 * lane - q];
+      local += c[q];
+    }
+    const uint32_t incl = wave_incl_scan(local);
+    const int total = __builtin_amdgcn_readlane((int)incl, 63);
+    uint32_t above = incl - local;
+    int hit = -1, hit_rem = 0, hit_cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      if ((int)above < remain && remain <= (int)(above + c[q])) {
+        hit = 255 - 4 * lane - q;
+        hit_rem = remain - (int)above;
+        hit_cnt = (int)c[q];
+      }
+      above += c[q];
+    }
+    const uint64_t hb = __ballot(hit >= 0);
+    if (hb == 0ull) {  // fewer matching keys than wanted: take them all
+      remain = total;
+      eq_total = total;
+      break;
+    }
+    const int src = __ffsll((unsigned long long)hb) - 1;
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(hit, src);
+    remain = __builtin_amdgcn_readlane(hit_rem, src);
+    eq_total = __builtin_amdgcn_readlane(hit_cnt, src);
+    prefix |= d << nshift;
+    mask |= dmask << nshift;
+    shift = nshift;
+  }
+  *thr = prefix;
+  const bool all_eq = eq_total >= 0 && remain >= eq_total;
+  // ordered compaction: counts per wave, then each wave writes its run of the output
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    if (64 * j >= len) continue;
+    const uint32_t key = kr[j];
+    gt += __popcll(__ballot(key != 0u && (key & mask) > prefix));
+    eq += __popcll(__ballot(key != 0u && (key & mask) == prefix));
+  }
+  if (lane == 0) {
+    s.wcnt[0][wave] = gt;
+    s.wcnt[1][wave] = eq;
+  }
+  __syncthreads();
+  const uint32_t e_l = lane < kFWaves ? (uint32_t)s.wcnt[1][lane] : 0u;
+  const uint32_t e_incl = wave_incl_scan(e_l);
+  const uint32_t e_before = e_incl - e_l;
+  const uint32_t take = all_eq ? e_l : (uint32_t)max(0, min((int)e_l, remain - (int)e_before));
+  const uint32_t s_l = lane < kFWaves ? (uint32_t)s.wcnt[0][lane] + take : 0u;
+  const uint32_t s_incl = wave_incl_scan(s_l);
+  const int total_sel = __builtin_amdgcn_readlane((int)s_incl, kFWaves - 1);
+  int run_eq = __builtin_amdgcn_readlane((int)e_before, wave);
+  int run_sel = __builtin_amdgcn_readlane((int)(s_incl - s_l), wave);
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    if (64 * j >= len) continue;
+    const uint32_t key = kr[j];
+    const bool is_eq = key != 0u && (key & mask) == prefix;
+    const uint64_t eqb = __ballot(is_eq);
+    const bool sel = key != 0u && ((key & mask) > prefix ||
+                                   (is_eq && (all_eq || run_eq + __popcll(eqb & lt) < remain)));
+    const uint64_t selb = __ballot(sel);
+    if (sel) out[run_sel + __popcll(selb & lt)] = lo + 64 * j + lane;
+    run_eq += __popcll(eqb);
+    run_sel += __popcll(selb);
+  }
+  __syncthreads();
+  return total_sel;
+}
+
 // Per-query view of the selection problem shared by the three kernels.
 struct Row {
   bool cand;
@@ -222,17 +399,18 @@ struct Row {
   int32_t n;            // visible positions
   int32_t nb;           // visible blocks (full mode)
   int32_t M, K;
-  // number of ranking items handled by K1 / K2 and how many of them are selected
+  // ranking items of the histogram: the pool's positions (candidate mode) or the older
+  // blocks 0 .. nb-2 (full mode; the newest block is handled apart)
   __device__ int32_t items() const { return cand ? 8 * M : max(nb - 1, 0); }
-  __device__ bool needs_hist() const { return cand ? true : nb > M; }
   __device__ uint32_t item_key(int32_t i) const {  // 0 = not a candidate
     if (cand) {
       const int32_t b = pool[i >> 3];
       const int64_t j = (int64_t)b * kBlock + (i & 7);
       return (b >= 0 && j < n) ? order_key(scores[i]) : 0u;
     }
-    return order_key(bm[i]);  // blocks 0 .. nb-2 (the newest block is handled apart)
+    return order_key(bm[i]);
   }
+  __device__ uint32_t entry_key(int32_t j) const { return j < n ? order_key(scores[j]) : 0u; }
 };
 
 __device__ __forceinline__ Row make_row(int t, bool cand, const float* scores, const float* bm, int32_t width,
@@ -255,20 +433,33 @@ __device__ __forceinline__ Row make_row(int t, bool cand, const float* scores, c
   return r;
 }
 
+// Workspace views shared by the kernels (byte offsets are fixed by make_layout).
+struct Ws {
+  uint32_t* hist;    // [n_q][kBins] ranking keys of the items
+  uint32_t* hist_e;  // [n_q][kBins] keys of the entry list (full mode)
+  int32_t* cnt_a;    // [n_q][G] per-workgroup lengths of list A
+  int32_t* cnt_b;    // [n_q][G] per-workgroup lengths of list B
+  int32_t* ids_a;    // [n_q][G * kSlice]
+  uint32_t* keys_a;
+  int32_t* ids_b;    // [n_q][G * kSegB]
+  uint32_t* keys_b;
+  float* bm;         // [n_q][nbw] block maxima when the caller gives none
+  int32_t G;
+};
+
 // ------------------------------------------------------------------ K1: histogram
 
 __global__ __launch_bounds__(kGThreads) void topk_hist_kernel(
     bool cand, const float* __restrict__ scores, const float* __restrict__ block_max, int32_t width,
-    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K,
-    uint32_t* __restrict__ ws_hist, float* __restrict__ ws_bm) {
+    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
   __shared__ uint32_t h[kBins];
   const int t = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   const int32_t nbw = (width + kBlock - 1) / kBlock;
-  Row r = make_row(t, cand, scores, block_max ? block_max : ws_bm, width, q_nvis, pool_blocks, M, K);
+  Row r = make_row(t, cand, scores, block_max ? block_max : ws.bm, width, q_nvis, pool_blocks, M, K);
   const int32_t lo = g * kSlice;
   if (!cand && block_max == nullptr) {
     // block maxima from the scores (NaN never wins a comparison, so it ranks as -inf)
-    float* bmw = ws_bm + (int64_t)t * nbw;
+    float* bmw = ws.bm + (int64_t)t * nbw;
     for (int32_t b = lo + tid; b < min(lo + kSlice, r.nb); b += kGThreads) {
       float mx = -__builtin_inff();
       for (int o = 0; o < kBlock; o++) {
@@ -282,7 +473,6 @@ __global__ __launch_bounds__(kGThreads) void topk_hist_kernel(
     }
     __syncthreads();
   }
-  if (!r.needs_hist()) return;
   const int32_t hi = min(lo + kSlice, r.items());
   if (lo >= hi) return;
   for (int b = tid; b < kBins; b += kGThreads) h[b] = 0;
@@ -293,193 +483,306 @@ __global__ __launch_bounds__(kGThreads) void topk_hist_kernel(
     hist_add(h, key >> kBinShift, key != 0u);
   }
   __syncthreads();
-  uint32_t* gh = ws_hist + (int64_t)t * kBins;
+  uint32_t* gh = ws.hist + (int64_t)t * kBins;
   for (int b = tid; b < kBins; b += kGThreads)
     if (h[b]) atomicAdd(&gh[b], h[b]);
 }
 
 // ------------------------------------------------------------------ K2: ordered collection
 
+// Each workgroup covers kSlice items of one query; wave w holds items lo + 256w .. +255 in
+// registers, four per lane.  List A: the items in the bin of the kA-th largest key or
+// above (kA = M-1 for the pool, K in candidate mode), in ascending order.  List B (full
+// mode): for every block of the slice in or above the bin of the K-th largest older-block
+// maximum, and for the newest block, its 8 entries in order, with the keys below that
+// bin's lower edge (and invisible positions) set to 0.  The K highest older blocks alone
+// hold K entries at or above that edge, so every Top-K entry keeps its key.  The non-zero
+// list B keys are also counted in a second histogram.
+constexpr int kItemsPerLane = kSlice / kGThreads;
+
 __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
-    bool cand, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
-    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K,
-    int32_t G, int32_t row_cap, const uint32_t* __restrict__ ws_hist, int32_t* __restrict__ ws_cnt,
-    int32_t* __restrict__ ws_ids) {
+    bool cand, bool want_pool, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
+    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
   __shared__ int32_t s_wave[kGThreads / 64];
-  __shared__ uint32_t s_b1;
+  __shared__ int32_t s_cnt[2][kGThreads / 64];
+  __shared__ int32_t s_bnd[2];
+  __shared__ int32_t s_cb[kSlice];
   const int t = blockIdx.y, g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = ws.G;
   Row r = make_row(t, cand, scores, bm, width, q_nvis, pool_blocks, M, K);
-  int32_t* cnt = ws_cnt + (int64_t)t * G + g;
-  if (!r.needs_hist()) {
-    if (tid == 0) *cnt = 0;
-    return;
+  const int32_t lo = g * kSlice;
+  const int32_t hi_a = min(lo + kSlice, r.items());             // ranked items of the slice
+  const int32_t hi_b = cand ? lo : min(lo + kSlice, r.nb);       // blocks of the slice, newest included
+  // the slice's keys and the histogram load together
+  uint32_t key[kItemsPerLane];
+#pragma unroll
+  for (int j = 0; j < kItemsPerLane; j++) {
+    const int32_t i = lo + 256 * wave + 64 * j + lane;
+    key[j] = i < hi_a ? r.item_key(i) : 0u;
   }
-  // thread tid owns bins [16 tid, 16 tid + 16); find the bin holding the kk-th largest
-  const uint32_t* gh = ws_hist + (int64_t)t * kBins;
+  const uint32_t* gh = ws.hist + (int64_t)t * kBins;
   uint32_t hb[16], local = 0;
 #pragma unroll
   for (int q = 0; q < 16; q++) {
     hb[q] = gh[16 * tid + q];
     local += hb[q];
   }
-  if (tid == 0) s_b1 = 0xFFFFFFFFu;
+  if (tid < 2) s_bnd[tid] = -1;
   int tot_i;
   const int before = block_excl_scan<kGThreads>((int)local, s_wave, tot_i);
-  const uint32_t total = (uint32_t)tot_i;
-  uint32_t above = total - (uint32_t)before - local;  // keys in bins above this thread's range
-  const uint32_t kk = cand ? min((uint32_t)K, total) : (uint32_t)(M - 1);
-  if (kk > 0) {
+  const int total = tot_i;
+  // list A is needed when the selection does not take every item
+  const int kA = cand ? min(K, total) : ((want_pool && total > M - 1) ? M - 1 : 0);
+  const int kB = (!cand && total >= K) ? K : 0;  // 0: every older block is a candidate
+  {
+    uint32_t above = (uint32_t)(total - before) - local;  // keys in bins above this thread's range
 #pragma unroll
     for (int q = 15; q >= 0; q--) {
-      if (above < kk && kk <= above + hb[q]) s_b1 = 16u * tid + q;
+      if (kA > 0 && (int)above < kA && kA <= (int)(above + hb[q])) s_bnd[0] = 16 * tid + q;
+      if (kB > 0 && (int)above < kB && kB <= (int)(above + hb[q])) s_bnd[1] = 16 * tid + q;
       above += hb[q];
     }
   }
   __syncthreads();
-  const uint32_t b1 = s_b1;
-  // ordered collection of this slice: wave w owns a quarter of the slice
-  const int32_t lo = g * kSlice, hi = min(lo + kSlice, r.items());
-  const int32_t q4 = kSlice / (kGThreads / 64);
-  const int32_t wlo = min(hi, lo + wave * q4), whi = min(hi, wlo + q4);
+  const int32_t b1 = s_bnd[0], b2 = s_bnd[1];
+  const uint32_t floor_key = b2 >= 0 ? (uint32_t)b2 << kBinShift : 0u;
+  // flags and per-wave counts for list A and the candidate blocks
+  uint64_t ba[kItemsPerLane], bb[kItemsPerLane];
+  int ca = 0, cb = 0;
+#pragma unroll
+  for (int j = 0; j < kItemsPerLane; j++) {
+    const int32_t i = lo + 256 * wave + 64 * j + lane;
+    const uint32_t k = key[j];
+    ba[j] = __ballot(b1 >= 0 && k != 0u && (int32_t)(k >> kBinShift) >= b1);
+    bb[j] = __ballot(i < hi_b && (i == r.nb - 1 || k >= floor_key));
+    ca += __popcll(ba[j]);
+    cb += __popcll(bb[j]);
+  }
+  if (lane == 0) {
+    s_cnt[0][wave] = ca;
+    s_cnt[1][wave] = cb;
+  }
+  __syncthreads();
+  int oa = 0, ob = 0, na = 0, ncb = 0;
+#pragma unroll
+  for (int w = 0; w < kGThreads / 64; w++) {
+    oa += w < wave ? s_cnt[0][w] : 0;
+    ob += w < wave ? s_cnt[1][w] : 0;
+    na += s_cnt[0][w];
+    ncb += s_cnt[1][w];
+  }
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int32_t mine = 0;
-  if (b1 != 0xFFFFFFFFu) {
-    for (int32_t b = wlo; b < whi; b += 64) {
-      const int32_t i = b + lane;
-      const uint32_t key = i < whi ? r.item_key(i) : 0u;
-      mine += __popcll(__ballot(key != 0u && (key >> kBinShift) >= b1));
+  int32_t* oid = ws.ids_a + ((int64_t)t * G + g) * kSlice;
+  uint32_t* okey = ws.keys_a + ((int64_t)t * G + g) * kSlice;
+#pragma unroll
+  for (int j = 0; j < kItemsPerLane; j++) {
+    const int32_t i = lo + 256 * wave + 64 * j + lane;
+    if ((ba[j] >> lane) & 1ull) {
+      const int pos = oa + __popcll(ba[j] & lt);
+      oid[pos] = i;
+      okey[pos] = key[j];
+    }
+    if ((bb[j] >> lane) & 1ull) s_cb[ob + __popcll(bb[j] & lt)] = i;
+    oa += __popcll(ba[j]);
+    ob += __popcll(bb[j]);
+  }
+  if (tid == 0) ws.cnt_a[(int64_t)t * G + g] = na;
+  if (cand) return;
+  __syncthreads();
+  // ---- list B: 8 slots per candidate block
+  const int nslots = ncb * kBlock;
+  if (nslots > kSegB) {  // segment overflow: the finalize falls back to the full row
+    if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = kListCap + 1;
+    return;
+  }
+  int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * kSegB;
+  uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * kSegB;
+  uint32_t* ghe = ws.hist_e + (int64_t)t * kBins;
+  constexpr int kSlotRounds = kSegB / kGThreads;
+  float v[kSlotRounds];
+#pragma unroll
+  for (int u = 0; u < kSlotRounds; u++) {  // every score load in flight at once
+    const int c = u * kGThreads + tid;
+    const int32_t j = c < nslots ? s_cb[c >> 3] * kBlock + (c & 7) : 0;
+    v[u] = (c < nslots && j < r.n) ? r.scores[j] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < kSlotRounds; u++) {
+    const int c = u * kGThreads + tid;
+    if (c < nslots) {
+      const int32_t j = s_cb[c >> 3] * kBlock + (c & 7);
+      uint32_t k = j < r.n ? order_key(v[u]) : 0u;
+      if (k < floor_key) k = 0u;
+      bid[c] = j;
+      bkey[c] = k;
+      if (k != 0u) atomicAdd(&ghe[k >> kBinShift], 1u);
     }
   }
-  int32_t all;
-  int32_t off = block_excl_scan<kGThreads>(lane == 0 ? mine : 0, s_wave, all);
-  off = __shfl(off, 0);
-  int32_t* seg = ws_ids + (int64_t)t * row_cap + (int64_t)g * kSlice;
-  if (b1 != 0xFFFFFFFFu) {
-    for (int32_t b = wlo; b < whi; b += 64) {
-      const int32_t i = b + lane;
-      const uint32_t key = i < whi ? r.item_key(i) : 0u;
-      const bool f = key != 0u && (key >> kBinShift) >= b1;
-      const uint64_t fb = __ballot(f);
-      if (f) seg[off + __popcll(fb & lt)] = i;
-      off += __popcll(fb);
-    }
-  }
-  if (tid == 0) *cnt = all;
+  if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = nslots;
 }
 
 // ------------------------------------------------------------------ K3: exact finalize
 
 struct FinShared {
-  int32_t ids[kListCap];       // ordered candidate ids
-  uint32_t keys[kListCap];     // their keys
-  int32_t pool[kMaxPool];      // pool block ids, ascending
-  int32_t sel[kMaxPool];       // selection indices
+  int32_t ids[kListCap];       // the gathered list
+  uint32_t keys[kListCap];
+  int32_t sel[kMaxPool];       // selected positions (every selection takes <= M-1 or K)
   int32_t seg_off[kMaxG + 1];
-  int32_t scan[kFWaves];
+  int32_t scan[2 * kFWaves];
+  int32_t bnd[4];              // boundary bin, count above it, its count, total
+  ListScratch ls;
   SelScratch s;
 };
 
+// One workgroup per (role, query).  Role 0 builds the pool from list A (Full mode); role
+// 1 takes the Top-K from list B (Full mode) or list A (candidate mode).  Each reads the
+// matching histogram, returns it to zero, gathers its list (a superset of the selection
+// in ascending id order) and refines the boundary bin's low 20 bits over it.
 __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
-    bool cand, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
-    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K,
-    int32_t G, int32_t row_cap, uint32_t* __restrict__ ws_hist, const int32_t* __restrict__ ws_cnt,
-    const int32_t* __restrict__ ws_ids, int32_t* __restrict__ pool_out, int32_t* __restrict__ topk_out) {
+    bool cand, bool want_pool, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
+    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws,
+    int32_t* __restrict__ pool_out, int32_t* __restrict__ topk_out) {
   __shared__ FinShared sh;
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int role = (cand || !want_pool) ? 1 : (int)blockIdx.x;
+  const int G = ws.G;
   Row r = make_row(t, cand, scores, bm, width, q_nvis, pool_blocks, M, K);
-  int32_t* tk = topk_out + (int64_t)t * K;
+  // the list, its histogram and the rank wanted
+  const bool use_a = role == 0 || cand;
+  uint32_t* gh = (use_a ? ws.hist : ws.hist_e) + (int64_t)t * kBins;
+  const int32_t* cnts = (use_a ? ws.cnt_a : ws.cnt_b) + (int64_t)t * G;
+  const int64_t seg_stride = use_a ? kSlice : kSegB;
+  const int32_t* lids = (use_a ? ws.ids_a : ws.ids_b) + (int64_t)t * G * seg_stride;
+  const uint32_t* lkeys = (use_a ? ws.keys_a : ws.keys_b) + (int64_t)t * G * seg_stride;
+  const int want = role == 0 ? M - 1 : K;
 
-  // gather the ordered candidate list (the K2 segments, in workgroup order)
-  int32_t total = 0;
-  if (r.needs_hist()) {
-    // segment offsets: a parallel scan of the G per-workgroup counts (G <= 1024)
-    const int c = tid < G ? ws_cnt[(int64_t)t * G + tid] : 0;
-    int all;
-    const int off = block_excl_scan<kFThreads>(c, sh.scan, all);
-    if (tid < G) sh.seg_off[tid] = off;
-    if (tid == 0) sh.seg_off[G] = all;
-    __syncthreads();
-    total = sh.seg_off[G];
-    if (total <= kListCap) {
-      // every element finds its segment by binary search, so all loads are in flight at once
-      const int32_t* rowids = ws_ids + (int64_t)t * row_cap;
-      for (int e = tid; e < total; e += kFThreads) {
-        int lo = 0, hi = G - 1;  // last segment whose offset is <= e
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sh.seg_off[mid] <= e) lo = mid; else hi = mid - 1;
-        }
-        const int32_t id = rowids[(int64_t)lo * kSlice + (e - sh.seg_off[lo])];
-        sh.ids[e] = id;
-        sh.keys[e] = r.item_key(id);
+  // ---- histogram boundary and segment offsets, in one pass of two scans
+  uint32_t c[kBinsPer];
+  uint32_t local = 0;
+#pragma unroll
+  for (int q = 0; q < kBinsPer; q++) {
+    c[q] = gh[kBins - 1 - kBinsPer * tid - q];
+    local += c[q];
+  }
+  int cs[kSegPer], cl = 0;
+#pragma unroll
+  for (int q = 0; q < kSegPer; q++) {
+    const int g = kSegPer * tid + q;
+    cs[q] = g < G ? cnts[g] : 0;
+    cl += cs[q];
+  }
+  const uint32_t xa = wave_incl_scan(local), xb = wave_incl_scan((uint32_t)cl);
+  if (lane == 63) {
+    sh.scan[wave] = (int)xa;
+    sh.scan[kFWaves + wave] = (int)xb;
+  }
+  if (tid < 4) sh.bnd[tid] = -1;
+  __syncthreads();
+  int offa = 0, offb = 0, tota = 0, totb = 0;
+#pragma unroll
+  for (int w = 0; w < kFWaves; w++) {
+    const int a = sh.scan[w], b = sh.scan[kFWaves + w];
+    offa += (w < wave) ? a : 0;
+    offb += (w < wave) ? b : 0;
+    tota += a;
+    totb += b;
+  }
+  const int kk = min(want, tota);
+  {
+    uint32_t above = (uint32_t)(offa + (int)xa - (int)local);
+#pragma unroll
+    for (int q = 0; q < kBinsPer; q++) {
+      if (kk > 0 && (int)above < kk && kk <= (int)(above + c[q])) {
+        sh.bnd[0] = kBins - 1 - kBinsPer * tid - q;
+        sh.bnd[1] = (int)above;
+        sh.bnd[2] = (int)c[q];
+      }
+      above += c[q];
+    }
+  }
+  int run = offb + (int)xb - cl;
+#pragma unroll
+  for (int q = 0; q < kSegPer; q++) {
+    const int g = kSegPer * tid + q;
+    if (g < G) sh.seg_off[g] = run;
+    run += cs[q];
+  }
+  if (tid == 0) sh.seg_off[G] = totb;
+  // every bin has been read: return the histogram(s) to zero for the next call
+#pragma unroll
+  for (int q = 0; q < kBinsPer; q++) gh[kBins - 1 - kBinsPer * tid - q] = 0u;
+  if (!cand && !want_pool) {
+#pragma unroll
+    for (int q = 0; q < kBinsPer; q++) ws.hist[(int64_t)t * kBins + kBins - 1 - kBinsPer * tid - q] = 0u;
+  }
+  __syncthreads();
+  const int total = sh.seg_off[G];
+  // Full-mode pool with no more older blocks than M-1: every older block is in
+  const bool take_all_blocks = role == 0 && tota <= M - 1;
+  const bool listed = !take_all_blocks && total <= kListCap;
+
+  int cnt = 0;
+  if (take_all_blocks) {
+    cnt = max(r.nb - 1, 0);
+  } else if (listed) {
+    // gather the list: all segment searches side by side, then all loads in flight
+    int64_t at[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      const int e = u * kFThreads + tid;
+      int lo = 0, hi = e < total ? G - 1 : 0;  // last segment whose offset is <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh.seg_off[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      at[u] = e < total ? (int64_t)lo * seg_stride + (e - sh.seg_off[lo]) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      if (at[u] >= 0) {
+        sh.ids[u * kFThreads + tid] = lids[at[u]];
+        sh.keys[u * kFThreads + tid] = lkeys[at[u]];
       }
     }
     __syncthreads();
-  }
-
-  if (cand) {
-    int cnt;
-    if (total <= kListCap) {
-      cnt = block_select([&](int i) { return sh.keys[i]; }, total, K, sh.s, sh.sel);
+    const int b1 = sh.bnd[0];
+    uint32_t thr;
+    if (b1 >= 0) {
+      cnt = list_select(sh.keys, total, (uint32_t)b1 << kBinShift, ~0u << kBinShift, kBinShift, kk - sh.bnd[1],
+                        sh.bnd[2], sh.ls, sh.sel, &thr);
       for (int i = tid; i < cnt; i += kFThreads) sh.sel[i] = sh.ids[sh.sel[i]];
-    } else {
-      cnt = block_select([&](int i) { return r.item_key(i); }, r.items(), K, sh.s, sh.sel);
     }
-    __syncthreads();
-    for (int i = tid; i < K; i += kFThreads) {
-      const int32_t p = i < cnt ? sh.sel[i] : -1;
-      tk[i] = p < 0 ? -1 : r.pool[p >> 3] * kBlock + (p & 7);
-    }
+  } else if (role == 0) {
+    cnt = block_select([&](int i) { return r.item_key(i); }, r.items(), M - 1, sh.s, sh.sel);
+  } else if (cand) {
+    cnt = block_select([&](int i) { return r.item_key(i); }, r.items(), K, sh.s, sh.sel);
   } else {
-    // ---- the pool: top M-1 of the older blocks plus the forced newest block
-    int32_t npool = 0;
-    if (r.nb > 0) {
-      if (!r.needs_hist()) {
-        for (int i = tid; i < r.nb - 1; i += kFThreads) sh.pool[i] = i;
-        npool = r.nb - 1;
-      } else if (total <= kListCap) {
-        npool = block_select([&](int i) { return sh.keys[i]; }, total, M - 1, sh.s, sh.sel);
-        for (int i = tid; i < npool; i += kFThreads) sh.pool[i] = sh.ids[sh.sel[i]];
-      } else {
-        npool = block_select([&](int i) { return r.item_key(i); }, r.nb - 1, M - 1, sh.s, sh.pool);
-      }
-      if (tid == 0) sh.pool[npool] = r.nb - 1;
-      npool += 1;
-      __syncthreads();
-    }
-    if (pool_out != nullptr) {
-      int32_t* po = pool_out + (int64_t)t * M;
-      for (int i = tid; i < M; i += kFThreads) po[i] = i < npool ? sh.pool[i] : -1;
-    }
-    // ---- the K+1 highest pool blocks hold every Top-K entry
-    for (int i = tid; i < npool; i += kFThreads) {
-      const int32_t b = sh.pool[i];
-      sh.keys[i] = (b == r.nb - 1) ? 0xFFFFFFFFu : order_key(r.bm[b]);
-    }
-    __syncthreads();
-    const int nsb = block_select([&](int i) { return sh.keys[i]; }, npool, K + 1, sh.s, sh.sel);
-    for (int i = tid; i < nsb; i += kFThreads) sh.ids[i] = sh.pool[sh.sel[i]];  // ascending block ids
-    __syncthreads();
-    const int nc = nsb * kBlock;
-    for (int c = tid; c < nc; c += kFThreads) {
-      const int32_t j = sh.ids[c >> 3] * kBlock + (c & 7);
-      sh.keys[kMaxPool + c] = j < r.n ? order_key(r.scores[j]) : 0u;
-    }
-    __syncthreads();
-    const int cnt = block_select([&](int i) { return sh.keys[kMaxPool + i]; }, nc, K, sh.s, sh.sel);
-    for (int i = tid; i < K; i += kFThreads) {
-      const int32_t c = i < cnt ? sh.sel[i] : -1;
-      tk[i] = c < 0 ? -1 : sh.ids[c >> 3] * kBlock + (c & 7);
-    }
+    cnt = block_select([&](int j) { return r.entry_key(j); }, r.n, K, sh.s, sh.sel);
   }
-  // return the histogram to zero for the next call
-  if (r.needs_hist())
-    for (int b = tid; b < kBins; b += kFThreads) ws_hist[(int64_t)t * kBins + b] = 0u;
+  __syncthreads();
+
+  if (role == 0) {
+    // the pool: the selected older blocks plus the forced newest block, ascending
+    int32_t* po = pool_out + (int64_t)t * M;
+    const int npool = r.nb > 0 ? cnt + 1 : 0;
+    for (int i = tid; i < M; i += kFThreads) {
+      int32_t v = -1;
+      if (i < cnt) v = take_all_blocks ? i : sh.sel[i];
+      else if (i == cnt && npool > 0) v = r.nb - 1;
+      po[i] = v;
+    }
+    return;
+  }
+  int32_t* tk = topk_out + (int64_t)t * K;
+  for (int i = tid; i < K; i += kFThreads) {
+    const int32_t p = i < cnt ? sh.sel[i] : -1;
+    tk[i] = p < 0 ? -1 : (cand ? r.pool[p >> 3] * kBlock + (p & 7) : p);
+  }
 }
 
 struct Layout {
-  int32_t G, row_cap;
-  size_t hist, cnt, ids, bm, total;  // byte offsets
+  int32_t G;
+  size_t hist, hist_e, cnt_a, cnt_b, ids_a, keys_a, ids_b, keys_b, bm, total;  // byte offsets
 };
 
 Layout make_layout(int32_t n_q, int32_t width, int32_t M, bool cand) {
@@ -488,12 +791,17 @@ Layout make_layout(int32_t n_q, int32_t width, int32_t M, bool cand) {
   const int64_t items = cand ? 8LL * M : nbw;
   L.G = (int32_t)((items + kSlice - 1) / kSlice);
   if (L.G < 1) L.G = 1;
-  L.row_cap = L.G * kSlice;
+  const size_t nq = (size_t)n_q, G = (size_t)L.G;
   L.hist = 0;
-  L.cnt = L.hist + (size_t)n_q * kBins * 4;
-  L.ids = L.cnt + (size_t)n_q * L.G * 4;
-  L.bm = L.ids + (size_t)n_q * L.row_cap * 4;
-  L.total = L.bm + (cand ? 0 : (size_t)n_q * nbw * 4);
+  L.hist_e = L.hist + nq * kBins * 4;
+  L.cnt_a = L.hist_e + nq * kBins * 4;
+  L.cnt_b = L.cnt_a + nq * G * 4;
+  L.ids_a = L.cnt_b + nq * G * 4;
+  L.keys_a = L.ids_a + nq * G * kSlice * 4;
+  L.ids_b = L.keys_a + nq * G * kSlice * 4;
+  L.keys_b = L.ids_b + (cand ? 0 : nq * G * kSegB * 4);
+  L.bm = L.keys_b + (cand ? 0 : nq * G * kSegB * 4);
+  L.total = L.bm + (cand ? 0 : nq * (size_t)nbw * 4);
   return L;
 }
 
@@ -528,22 +836,30 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   const Layout L = make_layout(n_q, width, M, cand);
   if (L.G > kMaxG) return CSA2_ERR_UNSUPPORTED;  // rows longer than 2^20 blocks
   if (!workspace || ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
-  char* ws = (char*)workspace;
-  uint32_t* ws_hist = (uint32_t*)(ws + L.hist);
-  int32_t* ws_cnt = (int32_t*)(ws + L.cnt);
-  int32_t* ws_ids = (int32_t*)(ws + L.ids);
-  float* ws_bm = cand ? nullptr : (float*)(ws + L.bm);
-  const float* bm = block_max ? block_max : ws_bm;
+  char* w = (char*)workspace;
+  Ws ws;
+  ws.hist = (uint32_t*)(w + L.hist);
+  ws.hist_e = (uint32_t*)(w + L.hist_e);
+  ws.cnt_a = (int32_t*)(w + L.cnt_a);
+  ws.cnt_b = (int32_t*)(w + L.cnt_b);
+  ws.ids_a = (int32_t*)(w + L.ids_a);
+  ws.keys_a = (uint32_t*)(w + L.keys_a);
+  ws.ids_b = (int32_t*)(w + L.ids_b);
+  ws.keys_b = (uint32_t*)(w + L.keys_b);
+  ws.bm = cand ? nullptr : (float*)(w + L.bm);
+  ws.G = L.G;
+  const float* bm = block_max ? block_max : ws.bm;
+  const bool want_pool = pool_out != nullptr;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, scores, block_max,
-                     width, q_nvis, pool_blocks, M, K, ws_hist, ws_bm);
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, scores, block_max, width,
+                     q_nvis, pool_blocks, M, K, ws);
   int st = check_launch();
   if (st != CSA2_OK) return st;
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, scores, bm, width,
-                     q_nvis, pool_blocks, M, K, L.G, L.row_cap, ws_hist, ws_cnt, ws_ids);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, want_pool, scores, bm,
+                     width, q_nvis, pool_blocks, M, K, ws);
   st = check_launch();
   if (st != CSA2_OK) return st;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(n_q), dim3(kFThreads), 0, s, cand, scores, bm, width, q_nvis,
-                     pool_blocks, M, K, L.G, L.row_cap, ws_hist, ws_cnt, ws_ids, pool_out, topk_out);
+  hipLaunchKernelGGL(topk_final_kernel, dim3((!cand && want_pool) ? 2 : 1, n_q), dim3(kFThreads), 0, s, cand,
+                     want_pool, scores, bm, width, q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
   return check_launch();
 }

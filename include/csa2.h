@@ -125,13 +125,14 @@ int csa2_index_score(const uint16_t *q_idx_bf16, const float *head_w, const uint
  *   mode; block_max may be NULL (recomputed) or the array index_score wrote.  The
  *   visible count is min(q_nvis[t], width).  pool_out: NULL or [n_q, M] selected block
  *   ids ascending, -1 padded.  The Top-K inside the pool equals the Top-K of the whole
- *   row (every global Top-K member's block ranks within the first K+1 blocks).
+ *   row (an entry outside the pool is outranked by the maxima of the M-1 older blocks
+ *   above its block), which is how it is computed.
  *   Candidate mode (pool_blocks != NULL, [n_q, M]): scores [n_q, width = 8M] laid out as
  *   csa2_index_score candidate mode; pool_out must be NULL.
  *   topk_out [n_q, K]: selected entry ids (relative to the sequence) ascending, -1 pad.
  *   workspace: device scratch of at least csa2_block_topk_workspace(n_q, width, M, K)
- *   bytes, 4-byte aligned.  Its histogram region must be all zero before the first call
- *   (allocate it zero-filled); every call that completes leaves it zero again, so one
+ *   bytes, 4-byte aligned.  Its two histogram regions must be all zero before the first
+ *   call (allocate it zero-filled); every call that completes leaves them zero, so one
  *   buffer can be reused by consecutive calls on the same stream.  Calls that overlap in
  *   time must not share a workspace.
  *   Errors: INVALID_ARG, UNSUPPORTED (block != 8, M > 2048, K > 512, K < 1, M < 1, rows
