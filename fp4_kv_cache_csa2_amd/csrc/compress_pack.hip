@@ -51,7 +51,9 @@ __device__ __forceinline__ uint32_t e8m0_scale_code(float amax) {
 }
 
 // kEnt entries per workgroup: 16 amortises the W_idx reads over many entries; 2 keeps one
-// fma chain per thread for the few-entry appends of a decode step.
+// fma chain per thread for the few-entry appends of a decode step.  There the whole of
+// W_idx (128 KB) is copied into LDS at kernel entry by direct-to-LDS loads, one 1 KB row
+// per wave instruction (coalesced, no registers), overlapping phase A.
 template <int kEnt>
 __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
@@ -59,12 +61,84 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     uint8_t* __restrict__ idx_out) {
   __shared__ float s_c[kEnt][kD];          // rotated fp32 entries
   __shared__ float s_k[kEnt][kIdxDim];     // projected indexer keys
-  __shared__ uint16_t s_w[2][kWChunk][kIdxDim + 8];  // W_idx^T chunks (bf16 bits)
+  constexpr bool kDirect = kEnt == 2;
+  constexpr int kWRow = kD + 8;  // bf16 per W_idx row in LDS (1040 B: conflict-free row reads)
+  __shared__ uint16_t s_w[kDirect ? 1 : 2][kWChunk][kIdxDim + 8];  // W_idx^T chunks (bf16 bits)
+  __shared__ __attribute__((aligned(16))) uint16_t s_wl[kDirect ? kIdxDim * kWRow : 8];  // all of W_idx
   const int t = threadIdx.x;
   const int64_t j0 = (int64_t)blockIdx.x * kEnt;
+  constexpr int kRowPieces = kD / 8;  // a W_idx row as 64 pieces of 8 bf16
+  if constexpr (kDirect) {
+    const int lane = t & 63, wave = t >> 6;
+    for (int r = wave; r < kIdxDim; r += kThreads / 64)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(w_idx + (int64_t)r * kD + 8 * lane),
+          (void __attribute__((address_space(3)))*)&s_wl[r * kWRow], 16, 0, 0);
+  }
 
-  // ---- phase A: pooling, RoPE, main-KV pack.  thread -> (entry e, channels 32p..32p+31)
-  {
+  // ---- phase A: pooling, RoPE, main-KV pack
+  if constexpr (kDirect) {
+    // thread -> (entry t / 128, channels 4q .. 4q+3, q = t % 128); the 4 threads of a
+    // 16-channel group share their amax through lane shuffles
+    const int e = t >> 7, q = t & 127, ch0 = 4 * q;
+    const int64_t j = j0 + e;
+    const bool live = j < n_entries;
+    const int64_t jr = live ? j : j0;  // rows read by a padding thread stay in bounds
+    float c[4];
+    if (m == 1) {
+      const uint2 u = *reinterpret_cast<const uint2*>(latent + jr * kD + ch0);
+      c[0] = bf16_bits_to_f32(u.x & 0xFFFFu);
+      c[1] = bf16_bits_to_f32(u.x >> 16);
+      c[2] = bf16_bits_to_f32(u.y & 0xFFFFu);
+      c[3] = bf16_bits_to_f32(u.y >> 16);
+    } else {
+      // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
+      const uint2 u0 = *reinterpret_cast<const uint2*>(latent + (2 * jr) * kD + ch0);
+      const uint2 u1 = *reinterpret_cast<const uint2*>(latent + (2 * jr + 1) * kD + ch0);
+      const uint32_t xa[4] = {u0.x & 0xFFFFu, u0.x >> 16, u0.y & 0xFFFFu, u0.y >> 16};
+      const uint32_t xb[4] = {u1.x & 0xFFFFu, u1.x >> 16, u1.y & 0xFFFFu, u1.y >> 16};
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const float w0 = pool_w[ch0 + v], w1 = pool_w[kD + ch0 + v];
+        const float ws = w0 + w1;
+        const float a0 = w0 / ws, a1 = w1 / ws;
+        const float p0 = a0 * bf16_bits_to_f32(xa[v]);
+        const float p1 = a1 * bf16_bits_to_f32(xb[v]);
+        c[v] = p0 + p1;
+      }
+    }
+    if (ch0 >= kDNope) {  // rope tail: pairs (448+2i, 449+2i)
+      const float* cs = rope_cs + jr * kDRope;
+      const int i0 = (ch0 - kDNope) / 2;
+#pragma unroll
+      for (int v = 0; v < 2; v++) {
+        const float x0 = c[2 * v], x1 = c[2 * v + 1];
+        const float co = cs[i0 + v], si = cs[kDRope / 2 + i0 + v];
+        const float t0 = x0 * co, t1 = x1 * si, t2 = x0 * si, t3 = x1 * co;
+        c[2 * v] = t0 - t1;
+        c[2 * v + 1] = t2 + t3;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v++) s_c[e][ch0 + v] = c[v];
+    float amax = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; v++) amax = __builtin_fmaxf(amax, __builtin_fabsf(c[v]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+    const uint32_t sb = e4m3_encode(amax / 6.0f);
+    const float S = e4m3_value(sb);
+    uint32_t half = 0;
+#pragma unroll
+    for (int v = 0; v < 4; v++) half |= e2m1_encode(c[v], S) << (4 * v);
+    if (live) {
+      uint8_t* dst = kv_out + j * kKvBytes;
+      *reinterpret_cast<uint16_t*>(dst + 2 * q) = (uint16_t)half;
+      if ((q & 3) == 0) dst[256 + (q >> 2)] = (uint8_t)sb;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's W_idx rows have landed in LDS
+  } else {
+    // thread -> (entry e, channels 32p..32p+31)
     const int e = t >> 4, p = t & 15;
     const int64_t j = j0 + e;
     if (e < kEnt && j < n_entries) {
@@ -147,10 +221,31 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
   __syncthreads();
 
   // ---- phase B: indexer projection k[o] = sum_ch W[o][ch] c~[ch], ascending fma chain.
-  // thread -> output o, entries h*kHalf .. h*kHalf + kHalf - 1.  W_idx streams through LDS
-  // in transposed chunks of 64 channels ([ch][o], double-buffered) so every chain step
-  // reads its weight from LDS without bank conflicts and no step waits on global memory.
-  {
+  if constexpr (kDirect) {
+    // thread -> output o = t % 128 of entry t / 128, its W_idx row read from LDS
+    const int o = t & (kIdxDim - 1), e = t >> 7;
+    float a = 0.0f;
+#pragma unroll 8
+    for (int v = 0; v < kRowPieces; v++) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(&s_wl[o * kWRow + 8 * v]);
+      const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+      const float4 c0 = *reinterpret_cast<const float4*>(&s_c[e][8 * v]);
+      const float4 c1 = *reinterpret_cast<const float4*>(&s_c[e][8 * v + 4]);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] & 0xFFFFu), c0.x, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] >> 16), c0.y, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] & 0xFFFFu), c0.z, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] >> 16), c0.w, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] & 0xFFFFu), c1.x, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] >> 16), c1.y, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] & 0xFFFFu), c1.z, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] >> 16), c1.w, a);
+    }
+    s_k[e][o] = a;
+  } else {
+    // thread -> output o, entries h*kHalf .. h*kHalf + kHalf - 1.  W_idx streams through
+    // LDS in transposed chunks of 64 channels ([ch][o], double-buffered) so every chain
+    // step reads its weight from LDS without bank conflicts and no step waits on global
+    // memory.
     constexpr int kHalf = kEnt / 2;
     const int o = t & (kIdxDim - 1), h = t >> 7;
     float acc[kHalf];

@@ -29,9 +29,9 @@ constexpr int kPStride = kChunk + 8;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-struct AttnShared {
-  _Float16 k[kChunk * kKStride];        // decoded keys of the chunk, row-major [key][dim]
-  _Float16 p[kWaves * 16 * kPStride];   // per-wave probabilities [head][key]
+struct __attribute__((aligned(16))) AttnShared {
+  _Float16 k[kChunk * kKStride] __attribute__((aligned(16)));  // decoded keys, row-major [key][dim]
+  _Float16 p[kWaves * 16 * kPStride] __attribute__((aligned(16)));  // per-wave probabilities [head][key]
   int32_t valid[kChunk];
 };
 
@@ -274,31 +274,43 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   }
 }
 
-// Combine the split partials of one (query, head): out = sum_s o_s e^(m_s - M) / L.
+// Combine the split partials of one (query, head): out = sum_s o_s e^(m_s - M) / L.  Every
+// split's (m, l) and o slice load at once (splits <= kMaxSplits), then one pass combines.
+constexpr int kMaxSplits = (kMaxTopK + kMaxSwa + kChunk - 1) / kChunk;
+
 __global__ __launch_bounds__(128) void sparse_attn_merge_kernel(const float* __restrict__ ws_o,
                                                                 const float* __restrict__ ws_ml,
                                                                 int32_t n_splits, float* __restrict__ out,
                                                                 float* __restrict__ lse) {
   const int t = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
-  float M = -__builtin_inff();
-  for (int s = 0; s < n_splits; s++) {
-    const float m = ws_ml[(((int64_t)t * n_splits + s) * kHeads + h) * 2];
-    const float l = ws_ml[(((int64_t)t * n_splits + s) * kHeads + h) * 2 + 1];
-    if (l > 0.0f) M = __builtin_fmaxf(M, m);
+  float m[kMaxSplits], l[kMaxSplits];
+  float4 v[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++) {
+    if (s < n_splits) {
+      const int64_t slot = ((int64_t)t * n_splits + s) * kHeads + h;
+      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);
+      m[s] = ml.x;
+      l[s] = ml.y;
+      v[s] = reinterpret_cast<const float4*>(ws_o + slot * kD)[tid];
+    }
   }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++)
+    if (s < n_splits && l[s] > 0.0f) M = __builtin_fmaxf(M, m[s]);
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < n_splits; s++) {
-    const int64_t slot = ((int64_t)t * n_splits + s) * kHeads + h;
-    const float m = ws_ml[slot * 2], l = ws_ml[slot * 2 + 1];
-    if (!(l > 0.0f)) continue;
-    const float e = __expf(m - M);
-    L += l * e;
-    const float4 v = reinterpret_cast<const float4*>(ws_o + slot * kD)[tid];
-    acc.x += v.x * e;
-    acc.y += v.y * e;
-    acc.z += v.z * e;
-    acc.w += v.w * e;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++) {
+    if (s < n_splits && l[s] > 0.0f) {
+      const float e = __expf(m[s] - M);
+      L += l[s] * e;
+      acc.x += v[s].x * e;
+      acc.y += v[s].y * e;
+      acc.z += v[s].z * e;
+      acc.w += v[s].w * e;
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   reinterpret_cast<float4*>(out + ((int64_t)t * kHeads + h) * kD)[tid] =
@@ -346,7 +358,8 @@ extern "C" int csa2_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache,
   if (K > 0 && !topk) return CSA2_ERR_INVALID_ARG;
   if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(q_bf16) | reinterpret_cast<uintptr_t>(kv_cache) |
-       reinterpret_cast<uintptr_t>(swa_bf16) | reinterpret_cast<uintptr_t>(out)) & 15)
+       reinterpret_cast<uintptr_t>(swa_bf16) | reinterpret_cast<uintptr_t>(out) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
     return CSA2_ERR_INVALID_ARG;
   const Plan p = make_plan(n_q, K);
   const size_t need = csa2_sparse_attn_workspace(n_q, K);

@@ -157,7 +157,8 @@ int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, in
  *   scale: logit scale (1/sqrt(512) is the library's documented default reading);
  *   out fp32 [n_q, 64, 512]; lse: NULL or fp32 [n_q, 64], natural-log partition
  *   function (max logit + log sum exp); a query with no keys gets out = 0, lse = -inf.
- *   workspace: csa2_sparse_attn_workspace(n_q, K) bytes.
+ *   workspace: csa2_sparse_attn_workspace(n_q, K) bytes, 16-byte aligned (may be NULL when
+ *   that size is 0).  Pointers q_bf16, kv_cache, swa_bf16 and out are 16-byte aligned.
  *   Errors: INVALID_ARG, UNSUPPORTED (K > 512), WORKSPACE.
  */
 size_t csa2_sparse_attn_workspace(int32_t n_q, int32_t K);
