@@ -15,7 +15,9 @@
 // lane group g and step s hold dims 64g + 8s .. 64g + 8s + 7 for both operands, which
 // leaves the dot products unchanged and makes each lane's bytes contiguous.  ReLU, the
 // head weights and the head sum run on the accumulator registers; a 32-lane swap
-// finishes the sum.  HBM traffic per entry is its 68 bytes plus 4.5 bytes of output.
+// finishes the sum.  HBM traffic per entry is its 68 bytes plus 4.5 bytes of output.  The
+// waves of the grid walk a query's tiles in grid-stride order, so the whole grid streams
+// one front of the row at a time.
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
-    int32_t width, int32_t tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
+    int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -79,16 +81,16 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
   const int32_t nvis = q_nvis[t];
   const int64_t base = q_base[t];
   const int32_t ntiles = (width + kTile - 1) / kTile;
-  const int32_t tile_begin = blockIdx.x * tiles_per_wg;
-  const int32_t tile_end = min(tile_begin + tiles_per_wg, ntiles);
-  const int32_t first = tile_begin + wave;
-  const int32_t nt = first < tile_end ? (tile_end - first + kWaves - 1) / kWaves : 0;  // this wave's tiles
+  // grid-stride tile order: at any moment the grid streams one front of the row
+  const int32_t first = (int32_t)blockIdx.x * kWaves + wave;
+  const int32_t tstride = (int32_t)gridDim.x * kWaves;
+  const int32_t nt = first < ntiles ? (ntiles - first + tstride - 1) / tstride : 0;  // this wave's tiles
   const int32_t nbw = (width + kBlock - 1) / kBlock;
   float* srow = scores + (int64_t)t * width;
 
   if (nvis <= 0) {  // nothing visible: the row is all -inf
     for (int32_t k = 0; k < nt; k++) {
-      const int32_t p = (first + k * kWaves) * kTile + n;
+      const int32_t p = (first + k * tstride) * kTile + n;
       if (g == 0 && p < width) srow[p] = -__builtin_inff();
       if (block_max != nullptr && g == 0 && (n & 7) == 0 && p < width)
         block_max[(int64_t)t * nbw + (p >> 3)] = -__builtin_inff();
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
   const uint8_t* last_row = idx_cache + (base + nvis - 1) * kIdxBytes;
   // the cache row of this lane's entry in tile k; invalid slots read the last visible row
   auto row_of = [&](int32_t k, bool& valid) -> const uint8_t* {
-    const int32_t p = (first + k * kWaves) * kTile + n;
+    const int32_t p = (first + k * tstride) * kTile + n;
     int64_t j;
     if (pool_blocks == nullptr) {
       j = p;
@@ -149,11 +151,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
       for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], __builtin_fmaxf(acc[4 * c + r], 0.0f), part[c]);
     }
     const float sc = valid ? sum_halves((part[0] + part[1]) + (part[2] + part[3])) : -__builtin_inff();
-    const int32_t p = (first + k * kWaves) * kTile + n;
-    if (g == 0 && p < width) __builtin_nontemporal_store(sc, srow + p);
+    const int32_t p = (first + k * tstride) * kTile + n;
+    if (g == 0 && p < width) srow[p] = sc;
     if (block_max != nullptr) {
       const float bm = max8_lanes(sc);
-      if (g == 0 && (n & 7) == 0 && p < width) __builtin_nontemporal_store(bm, block_max + (int64_t)t * nbw + (p >> 3));
+      if (g == 0 && (n & 7) == 0 && p < width) block_max[(int64_t)t * nbw + (p >> 3)] = bm;
     }
   };
 
@@ -220,16 +222,12 @@ extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
        reinterpret_cast<uintptr_t>(block_max)) & 3)
     return CSA2_ERR_INVALID_ARG;
   const int32_t ntiles = (width + kTile - 1) / kTile;
-  // one full round of resident workgroups, each streaming a long contiguous range
-  int64_t chunks = (resident_workgroups() + n_q - 1) / n_q;
-  const int64_t max_chunks = (ntiles + kWaves - 1) / kWaves;
-  if (chunks > max_chunks) chunks = max_chunks;
-  if (chunks < 1) chunks = 1;
-  int32_t tiles_per_wg = (int32_t)((ntiles + chunks - 1) / chunks);
-  tiles_per_wg = (tiles_per_wg + kWaves - 1) / kWaves * kWaves;
-  const int32_t grid_x = (ntiles + tiles_per_wg - 1) / tiles_per_wg;
-  hipLaunchKernelGGL(index_score_kernel, dim3(grid_x, n_q), dim3(kThreads), 0, (hipStream_t)stream,
-                     q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width,
-                     tiles_per_wg, scores, block_max);
+  // one full round of resident workgroups; each wave strides over its query's tiles
+  int64_t grid_x = (resident_workgroups() + n_q - 1) / n_q;
+  const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
+  if (grid_x > max_x) grid_x = max_x;
+  if (grid_x < 1) grid_x = 1;
+  hipLaunchKernelGGL(index_score_kernel, dim3((unsigned)grid_x, n_q), dim3(kThreads), 0, (hipStream_t)stream,
+                     q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width, scores, block_max);
   return check_launch();
 }
