@@ -14,11 +14,15 @@ from the 256 MB Infinity Cache left warm by the previous step.
 Prints one JSON line (rank 0, N = 1).  `value` is queries/s; `roofline` prices the
 dominant kernel (index_score) at 68 algorithmic bytes per scored entry against 8 TB/s,
 timed with HIP events on the launch stream; `cpu_baseline` times the oracle (plain C,
-one host thread) on the same per-query work.
+one host thread) on the same per-query work.  `roofline.traffic` is the HBM bytes per
+index_score launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (each scaled by what the
+counter reads for a torch copy of known size), read from profiles/index_score_traffic.json
+and reported only while the kernel source still hashes to the one those counters measured.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -41,6 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--tokens", type=int, default=1048576, help="tokens per sequence")
+    p.add_argument("--calibration-copy-mib", type=int, default=0,
+                   help="run one device copy of this many MiB before timing (counter calibration)")
     return p.parse_args()
 
 
@@ -149,6 +155,21 @@ class Decode1M:
 
 
 STAGES = ("compress_newest", "index_score", "block_topk", "sparse_attn")
+INDEX_SRC = os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "csrc", "index_score.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per index_score launch from the committed counter summary, or None when
+    it is missing or was taken on a different kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(INDEX_SRC, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha or rec.get("workload") != WORKLOAD:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def main():
@@ -161,6 +182,13 @@ def main():
     from fp4_kv_cache_csa2_amd import csa2
 
     torch.cuda.set_device(0)
+    if args.calibration_copy_mib > 0:  # a plain copy of known size for counter calibration
+        nb = args.calibration_copy_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = Decode1M(torch, csa2, args.tokens)
     n_seq, m, tokens, n, K, M = wl.n_seq, wl.m, wl.tokens, wl.n, wl.K, wl.M
     stages = STAGES
@@ -238,7 +266,7 @@ def main():
         "gpu_ms_timed_region": round(gpu_ms, 4), "wall_s_timed_region": round(wall_s, 4),
         "roofline": {"kernel": "index_score", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": idx_bytes},
     }
     if not args.no_cpu_baseline:
