@@ -17,20 +17,21 @@
 //               ascending order, the ids and keys of every item in that bin or above into
 //               one segment per workgroup (list A).  In Full mode it also lists the
 //               entries of the blocks in or above the bin of the K-th largest older block,
-//               and of the newest block, whose keys reach that bin's lower edge (list B),
-//               and counts their keys in a second histogram.  Every global Top-K entry is
+//               and of the newest block, 8 slots per block with the keys below that bin's
+//               lower edge set to 0 (list B).  Every global Top-K entry is
 //               in list B: the K highest older blocks alone hold K entries at or above
 //               that edge.  The Top-K of the pool equals the global Top-K of the row, since
 //               any entry outside the pool is outranked by the M-1 block maxima above it.
 //   K3 finalize one 1024-thread workgroup per query and role, the roles in parallel: the
 //               pool from list A, the Top-K from list B (or from list A in candidate
-//               mode).  Each reads its histogram (the count above the boundary bin and
-//               the bin's own count), returns it to zero, gathers its list and refines
-//               only the boundary bin's low 20 bits, with the keys held in registers (one
-//               barrier per 8-bit radix pass).  If a list overflows LDS (massive ties), K3
+//               mode).  The list-A roles read K1's histogram (the count above the boundary
+//               bin and the bin's own count) and return it to zero; the list-B role
+//               histograms its gathered list in LDS.  Each then refines only the boundary
+//               bin's low 20 bits, with the keys held in registers (one barrier per 8-bit
+//               radix pass).  If a list overflows LDS (massive ties), K3
 //               selects straight from the full row instead, with the same exact rules.
-// The two histogram regions of the workspace must be zero before the first call; every
-// call leaves them zero.
+// The histogram region of the workspace must be zero before the first call; every call
+// leaves it zero.
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -436,7 +437,6 @@ __device__ __forceinline__ Row make_row(int t, bool cand, const float* scores, c
 // Workspace views shared by the kernels (byte offsets are fixed by make_layout).
 struct Ws {
   uint32_t* hist;    // [n_q][kBins] ranking keys of the items
-  uint32_t* hist_e;  // [n_q][kBins] keys of the entry list (full mode)
   int32_t* cnt_a;    // [n_q][G] per-workgroup lengths of list A
   int32_t* cnt_b;    // [n_q][G] per-workgroup lengths of list B
   int32_t* ids_a;    // [n_q][G * kSlice]
@@ -496,8 +496,7 @@ __global__ __launch_bounds__(kGThreads) void topk_hist_kernel(
 // mode): for every block of the slice in or above the bin of the K-th largest older-block
 // maximum, and for the newest block, its 8 entries in order, with the keys below that
 // bin's lower edge (and invisible positions) set to 0.  The K highest older blocks alone
-// hold K entries at or above that edge, so every Top-K entry keeps its key.  The non-zero
-// list B keys are also counted in a second histogram.
+// hold K entries at or above that edge, so every Top-K entry keeps its key.
 constexpr int kItemsPerLane = kSlice / kGThreads;
 
 __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
@@ -597,7 +596,6 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
   }
   int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * kSegB;
   uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * kSegB;
-  uint32_t* ghe = ws.hist_e + (int64_t)t * kBins;
   constexpr int kSlotRounds = kSegB / kGThreads;
   float v[kSlotRounds];
 #pragma unroll
@@ -615,13 +613,28 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
       if (k < floor_key) k = 0u;
       bid[c] = j;
       bkey[c] = k;
-      if (k != 0u) atomicAdd(&ghe[k >> kBinShift], 1u);
     }
   }
   if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = nslots;
 }
 
 // ------------------------------------------------------------------ K3: exact finalize
+
+// Thread tid owns the kBinsPer bins below kBins-1-kBinsPer*tid (descending) with counts c[]
+// and `above` keys in higher bins.  If rank k (1-based, from the top) falls in one of them,
+// records that bin, the count above it and its own count at bnd[slot..slot+2].
+__device__ __forceinline__ void hist_boundary(const uint32_t* c, uint32_t above, int k, int slot, int32_t* bnd) {
+  if (k <= 0) return;
+#pragma unroll
+  for (int q = 0; q < kBinsPer; q++) {
+    if ((int)above < k && k <= (int)(above + c[q])) {
+      bnd[slot] = kBins - 1 - kBinsPer * (int)threadIdx.x - q;
+      bnd[slot + 1] = (int)above;
+      bnd[slot + 2] = (int)c[q];
+    }
+    above += c[q];
+  }
+}
 
 struct FinShared {
   int32_t ids[kListCap];       // the gathered list
@@ -630,6 +643,7 @@ struct FinShared {
   int32_t seg_off[kMaxG + 1];
   int32_t scan[2 * kFWaves];
   int32_t bnd[4];              // boundary bin, count above it, its count, total
+  uint32_t lhist[kBins];       // histogram of list B's keys (Full-mode Top-K role)
   ListScratch ls;
   SelScratch s;
 };
@@ -647,21 +661,24 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   const int role = (cand || !want_pool) ? 1 : (int)blockIdx.x;
   const int G = ws.G;
   Row r = make_row(t, cand, scores, bm, width, q_nvis, pool_blocks, M, K);
-  // the list, its histogram and the rank wanted
+  // the list, its histogram and the rank wanted.  Roles on list A use K1's histogram; the
+  // Full-mode Top-K role counts its gathered list B in LDS
   const bool use_a = role == 0 || cand;
-  uint32_t* gh = (use_a ? ws.hist : ws.hist_e) + (int64_t)t * kBins;
+  uint32_t* gh = ws.hist + (int64_t)t * kBins;
   const int32_t* cnts = (use_a ? ws.cnt_a : ws.cnt_b) + (int64_t)t * G;
   const int64_t seg_stride = use_a ? kSlice : kSegB;
   const int32_t* lids = (use_a ? ws.ids_a : ws.ids_b) + (int64_t)t * G * seg_stride;
   const uint32_t* lkeys = (use_a ? ws.keys_a : ws.keys_b) + (int64_t)t * G * seg_stride;
   const int want = role == 0 ? M - 1 : K;
+  if (!use_a)
+    for (int b = tid; b < kBins; b += kFThreads) sh.lhist[b] = 0u;
 
-  // ---- histogram boundary and segment offsets, in one pass of two scans
+  // ---- histogram boundary (list A) and segment offsets, in one pass of two scans
   uint32_t c[kBinsPer];
   uint32_t local = 0;
 #pragma unroll
   for (int q = 0; q < kBinsPer; q++) {
-    c[q] = gh[kBins - 1 - kBinsPer * tid - q];
+    c[q] = use_a ? gh[kBins - 1 - kBinsPer * tid - q] : 0u;
     local += c[q];
   }
   int cs[kSegPer], cl = 0;
@@ -687,19 +704,7 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
     tota += a;
     totb += b;
   }
-  const int kk = min(want, tota);
-  {
-    uint32_t above = (uint32_t)(offa + (int)xa - (int)local);
-#pragma unroll
-    for (int q = 0; q < kBinsPer; q++) {
-      if (kk > 0 && (int)above < kk && kk <= (int)(above + c[q])) {
-        sh.bnd[0] = kBins - 1 - kBinsPer * tid - q;
-        sh.bnd[1] = (int)above;
-        sh.bnd[2] = (int)c[q];
-      }
-      above += c[q];
-    }
-  }
+  if (use_a) hist_boundary(c, (uint32_t)(offa + (int)xa - (int)local), min(want, tota), 0, sh.bnd);
   int run = offb + (int)xb - cl;
 #pragma unroll
   for (int q = 0; q < kSegPer; q++) {
@@ -708,12 +713,10 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
     run += cs[q];
   }
   if (tid == 0) sh.seg_off[G] = totb;
-  // every bin has been read: return the histogram(s) to zero for the next call
+  // K1's histogram has been read (or is not needed): return it to zero for the next call
+  if (use_a || !want_pool) {
 #pragma unroll
-  for (int q = 0; q < kBinsPer; q++) gh[kBins - 1 - kBinsPer * tid - q] = 0u;
-  if (!cand && !want_pool) {
-#pragma unroll
-    for (int q = 0; q < kBinsPer; q++) ws.hist[(int64_t)t * kBins + kBins - 1 - kBinsPer * tid - q] = 0u;
+    for (int q = 0; q < kBinsPer; q++) gh[kBins - 1 - kBinsPer * tid - q] = 0u;
   }
   __syncthreads();
   const int total = sh.seg_off[G];
@@ -745,6 +748,36 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
       }
     }
     __syncthreads();
+    int kk = min(want, tota);
+    if (!use_a) {
+      // histogram of list B's non-zero keys, then its boundary bin for rank min(K, count)
+#pragma unroll
+      for (int u = 0; u < kPer; u++) {
+        const int e = u * kFThreads + tid;
+        const uint32_t key = e < total ? sh.keys[e] : 0u;
+        if (key != 0u) atomicAdd(&sh.lhist[key >> kBinShift], 1u);
+      }
+      __syncthreads();
+      uint32_t lc[kBinsPer], ll = 0;
+#pragma unroll
+      for (int q = 0; q < kBinsPer; q++) {
+        lc[q] = sh.lhist[kBins - 1 - kBinsPer * tid - q];
+        ll += lc[q];
+      }
+      const uint32_t xl = wave_incl_scan(ll);
+      if (lane == 63) sh.scan[wave] = (int)xl;
+      __syncthreads();
+      int offl = 0, totl = 0;
+#pragma unroll
+      for (int w = 0; w < kFWaves; w++) {
+        const int a = sh.scan[w];
+        offl += (w < wave) ? a : 0;
+        totl += a;
+      }
+      kk = min(K, totl);
+      hist_boundary(lc, (uint32_t)(offl + (int)xl - (int)ll), kk, 0, sh.bnd);
+      __syncthreads();
+    }
     const int b1 = sh.bnd[0];
     uint32_t thr;
     if (b1 >= 0) {
@@ -782,7 +815,7 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
 
 struct Layout {
   int32_t G;
-  size_t hist, hist_e, cnt_a, cnt_b, ids_a, keys_a, ids_b, keys_b, bm, total;  // byte offsets
+  size_t hist, cnt_a, cnt_b, ids_a, keys_a, ids_b, keys_b, bm, total;  // byte offsets
 };
 
 Layout make_layout(int32_t n_q, int32_t width, int32_t M, bool cand) {
@@ -793,8 +826,7 @@ Layout make_layout(int32_t n_q, int32_t width, int32_t M, bool cand) {
   if (L.G < 1) L.G = 1;
   const size_t nq = (size_t)n_q, G = (size_t)L.G;
   L.hist = 0;
-  L.hist_e = L.hist + nq * kBins * 4;
-  L.cnt_a = L.hist_e + nq * kBins * 4;
+  L.cnt_a = L.hist + nq * kBins * 4;
   L.cnt_b = L.cnt_a + nq * G * 4;
   L.ids_a = L.cnt_b + nq * G * 4;
   L.keys_a = L.ids_a + nq * G * kSlice * 4;
@@ -839,7 +871,6 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   char* w = (char*)workspace;
   Ws ws;
   ws.hist = (uint32_t*)(w + L.hist);
-  ws.hist_e = (uint32_t*)(w + L.hist_e);
   ws.cnt_a = (int32_t*)(w + L.cnt_a);
   ws.cnt_b = (int32_t*)(w + L.cnt_b);
   ws.ids_a = (int32_t*)(w + L.ids_a);

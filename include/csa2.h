@@ -131,8 +131,8 @@ int csa2_index_score(const uint16_t *q_idx_bf16, const float *head_w, const uint
  *   csa2_index_score candidate mode; pool_out must be NULL.
  *   topk_out [n_q, K]: selected entry ids (relative to the sequence) ascending, -1 pad.
  *   workspace: device scratch of at least csa2_block_topk_workspace(n_q, width, M, K)
- *   bytes, 4-byte aligned.  Its two histogram regions must be all zero before the first
- *   call (allocate it zero-filled); every call that completes leaves them zero, so one
+ *   bytes, 4-byte aligned.  Its histogram region must be all zero before the first call
+ *   (allocate it zero-filled); every call that completes leaves it zero again, so one
  *   buffer can be reused by consecutive calls on the same stream.  Calls that overlap in
  *   time must not share a workspace.
  *   Errors: INVALID_ARG, UNSUPPORTED (block != 8, M > 2048, K > 512, K < 1, M < 1, rows
