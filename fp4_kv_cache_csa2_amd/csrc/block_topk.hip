@@ -10,10 +10,11 @@
 // Design (three kernels, launched back to back on the caller's stream).  The ranking key
 // of a value is an order-preserving uint32 map of the fp32 value (NaN as -inf); its top
 // 12 bits are its histogram bin.
-//   K1 hist     many workgroups per query build a 4096-bin histogram of the ranking keys
-//               (older blocks' maxima in Full mode, pool entries in candidate mode) in
-//               LDS and add it into a per-query histogram in the workspace.
-//   K2 collect  the same grid finds the bin of the k-th largest key and writes, in
+//   K1 hist     1024-thread workgroups of 4096 keys each build a 4096-bin histogram of
+//               the ranking keys (older blocks' maxima in Full mode, pool entries in
+//               candidate mode) in LDS and add it into a per-query histogram in the
+//               workspace (few, large workgroups: every global add is a slow atomic).
+//   K2 collect  workgroups of 1024 items find the bin of the k-th largest key and write, in
 //               ascending order, the ids and keys of every item in that bin or above into
 //               one segment per workgroup (list A).  In Full mode it also lists the
 //               entries of the blocks in or above the bin of the K-th largest older block,
@@ -39,7 +40,9 @@ namespace {
 
 constexpr int kBins = 4096;        // 12-bit histogram digit
 constexpr int kBinShift = 20;
-constexpr int kSlice = 1024;       // keys per workgroup in K1 / K2
+constexpr int kSlice = 1024;       // keys per workgroup in K2
+constexpr int kHSlice = 4096;      // keys per workgroup in K1 (fewer global histogram adds)
+constexpr int kHThreads = 1024;    // K1 workgroup size
 constexpr int kGThreads = 256;     // K1 / K2 workgroup size
 constexpr int kFThreads = 1024;    // K3 workgroup size
 constexpr int kFWaves = kFThreads / 64;
@@ -449,18 +452,18 @@ struct Ws {
 
 // ------------------------------------------------------------------ K1: histogram
 
-__global__ __launch_bounds__(kGThreads) void topk_hist_kernel(
+__global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
     bool cand, const float* __restrict__ scores, const float* __restrict__ block_max, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
   __shared__ uint32_t h[kBins];
   const int t = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   const int32_t nbw = (width + kBlock - 1) / kBlock;
   Row r = make_row(t, cand, scores, block_max ? block_max : ws.bm, width, q_nvis, pool_blocks, M, K);
-  const int32_t lo = g * kSlice;
+  const int32_t lo = g * kHSlice;
   if (!cand && block_max == nullptr) {
     // block maxima from the scores (NaN never wins a comparison, so it ranks as -inf)
     float* bmw = ws.bm + (int64_t)t * nbw;
-    for (int32_t b = lo + tid; b < min(lo + kSlice, r.nb); b += kGThreads) {
+    for (int32_t b = lo + tid; b < min(lo + kHSlice, r.nb); b += kHThreads) {
       float mx = -__builtin_inff();
       for (int o = 0; o < kBlock; o++) {
         const int32_t j = b * kBlock + o;
@@ -473,18 +476,22 @@ __global__ __launch_bounds__(kGThreads) void topk_hist_kernel(
     }
     __syncthreads();
   }
-  const int32_t hi = min(lo + kSlice, r.items());
+  const int32_t hi = min(lo + kHSlice, r.items());
   if (lo >= hi) return;
-  for (int b = tid; b < kBins; b += kGThreads) h[b] = 0;
+  for (int b = tid; b < kBins; b += kHThreads) h[b] = 0;
   __syncthreads();
-  for (int32_t base = lo; base < hi; base += kGThreads) {
-    const int32_t i = base + tid;
-    const uint32_t key = i < hi ? r.item_key(i) : 0u;
-    hist_add(h, key >> kBinShift, key != 0u);
+  constexpr int kPerH = kHSlice / kHThreads;
+  uint32_t keys[kPerH];
+#pragma unroll
+  for (int u = 0; u < kPerH; u++) {  // every key load in flight at once
+    const int32_t i = lo + u * kHThreads + tid;
+    keys[u] = i < hi ? r.item_key(i) : 0u;
   }
+#pragma unroll
+  for (int u = 0; u < kPerH; u++) hist_add(h, keys[u] >> kBinShift, keys[u] != 0u);
   __syncthreads();
   uint32_t* gh = ws.hist + (int64_t)t * kBins;
-  for (int b = tid; b < kBins; b += kGThreads)
+  for (int b = tid; b < kBins; b += kHThreads)
     if (h[b]) atomicAdd(&gh[b], h[b]);
 }
 
@@ -882,7 +889,8 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   const float* bm = block_max ? block_max : ws.bm;
   const bool want_pool = pool_out != nullptr;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, scores, block_max, width,
+  const int32_t G1 = (L.G * kSlice + kHSlice - 1) / kHSlice;
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(G1, n_q), dim3(kHThreads), 0, s, cand, scores, block_max, width,
                      q_nvis, pool_blocks, M, K, ws);
   int st = check_launch();
   if (st != CSA2_OK) return st;
