@@ -28,17 +28,13 @@ constexpr int kKStride = kD + 8;        // f16 elements per key row in LDS (1040
 constexpr int kPStride = kChunk + 8;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct __attribute__((aligned(16))) AttnShared {
   _Float16 k[kChunk * kKStride] __attribute__((aligned(16)));  // decoded keys, row-major [key][dim]
   _Float16 p[kWaves * 16 * kPStride] __attribute__((aligned(16)));  // per-wave probabilities [head][key]
   int32_t valid[kChunk];
 };
-
-__device__ __forceinline__ float e2m1_value(uint32_t c4) {
-  const float v = e2m1_mag(c4 & 7u);
-  return (c4 & 8u) ? -v : v;
-}
 
 // Raw bytes of one key slot for one thread (a quarter of a key: 128 dims).  Selected
 // entries are prefetched a chunk ahead; window rows (bf16, 4x the bytes) load when staged.
@@ -90,6 +86,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   auto stage = [&](const KeyRaw& r) {
     _Float16* krow = sh.k + kk * kKStride + 128 * qq;
     if (r.kind == 1) {
+      // v_cvt_scalef32_pk_f16_fp4 applies only a power-of-two scale, so the codes convert
+      // at scale 1 and a packed f16 multiply applies the E4M3 scale (exact: at most 6
+      // significant bits, inside f16's normal range)
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const uint32_t wd[4] = {r.pay[v].x, r.pay[v].y, r.pay[v].z, r.pay[v].w};
@@ -97,10 +96,13 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
         for (int q4 = 0; q4 < 4; q4++) {
           const int grp = 2 * v + (q4 >> 1);  // local group of 16 dims
           const uint32_t sb = ((grp < 4 ? r.scw.x : r.scw.y) >> (8 * (grp & 3))) & 255u;
-          const float S = e4m3_value(sb);
-          f16x8 pk;
-#pragma unroll
-          for (int nb = 0; nb < 8; nb++) pk[nb] = (_Float16)(e2m1_value((wd[q4] >> (4 * nb)) & 15u) * S);
+          const _Float16 S = (_Float16)e4m3_value(sb);
+          const f16x2 S2 = {S, S};
+          const f16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 0) * S2;
+          const f16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 1) * S2;
+          const f16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 2) * S2;
+          const f16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 3) * S2;
+          const f16x8 pk = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
           *reinterpret_cast<f16x8*>(krow + 32 * v + 8 * q4) = pk;
         }
       }
