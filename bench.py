@@ -17,7 +17,7 @@ timed with HIP events on the launch stream; `cpu_baseline` times the oracle (pla
 one host thread) on the same per-query work.  `roofline.traffic` is the HBM bytes per
 index_score launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (each scaled by what the
 counter reads for a torch copy of known size), read from profiles/index_score_traffic.json
-and reported only while the kernel source still hashes to the one those counters measured.
+and reported only while the kernel's sources still hash to the ones those counters measured.
 """
 from __future__ import annotations
 
@@ -155,8 +155,17 @@ class Decode1M:
 
 
 STAGES = ("compress_newest", "index_score", "block_topk", "sparse_attn")
-INDEX_SRC = os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "csrc", "index_score.hip")
+# the sources the decode-path index kernel is built from
+INDEX_SRCS = [os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "csrc", f)
+              for f in ("index_score.hip", "index_common.hpp", "csa2_device.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_traffic.json")
+
+
+def index_source_sha():
+    h = hashlib.sha256()
+    for f in INDEX_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -164,7 +173,7 @@ def measured_traffic():
     it is missing or was taken on a different kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        sha = hashlib.sha256(open(INDEX_SRC, "rb").read()).hexdigest()
+        sha = index_source_sha()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != sha or rec.get("workload") != WORKLOAD:

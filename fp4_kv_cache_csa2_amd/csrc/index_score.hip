@@ -18,56 +18,16 @@
 // finishes the sum.  HBM traffic per entry is its 68 bytes plus 4.5 bytes of output.  The
 // waves of the grid walk a query's tiles in grid-stride order, so the whole grid streams
 // one front of the row at a time.
-#include "csa2_device.hpp"
+#include "index_common.hpp"
 
 namespace csa2 {
 namespace {
+using namespace idx;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32;
 #ifndef CSA2_INDEX_DEPTH
 #define CSA2_INDEX_DEPTH 4
 #endif
 constexpr int kDepth = CSA2_INDEX_DEPTH;  // tiles in flight per wave
-
-__device__ __forceinline__ bf16x8 cvt_fp4x8(uint32_t word, float scale) {
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
-  bf16x8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-__device__ __forceinline__ float e8m0_scale(uint32_t code) {
-  return __builtin_ldexpf(1.0f, (int)code - 127);
-}
-
-// indexer rows are 68 bytes, so a row's 16-byte pieces are only 4-byte aligned; gfx950
-// serves dword-aligned global dwordx4 loads
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-
-struct RawTile {
-  u32x4_a4 lo, hi;
-  uint32_t sc;
-};
-
-// max over the 8 lanes of each aligned group of 8 (DPP within rows)
-__device__ __forceinline__ float max8_lanes(float v) {
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
-  return v;
-}
-
-// v(lane) + v(lane ^ 32)
-__device__ __forceinline__ float sum_halves(float v) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return __int_as_float(p[0]) + __int_as_float(p[1]);
-}
 
 __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
@@ -222,6 +182,9 @@ extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
        reinterpret_cast<uintptr_t>(block_max)) & 3)
     return CSA2_ERR_INVALID_ARG;
   const int32_t ntiles = (width + kTile - 1) / kTile;
+  if (pool_blocks == nullptr && n_q >= kMqMinQueries)  // many queries: shared K-tile decode
+    return launch_index_score_mq(q_idx_bf16, head_w, idx_cache, q_base, q_nvis, n_q, width, scores, block_max,
+                                 stream);
   // one full round of resident workgroups; each wave strides over its query's tiles
   int64_t grid_x = (resident_workgroups() + n_q - 1) / n_q;
   const int64_t max_x = (ntiles + kWaves - 1) / kWaves;

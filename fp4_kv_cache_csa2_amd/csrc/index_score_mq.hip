@@ -1,0 +1,203 @@
+// index_score_mq.hip -- lightning-indexer scoring for many queries over one sequence
+// (a prefill chunk) on gfx950.
+//
+// Same score as the single-query kernel ([ZB] "把 KV Cache 压缩推到极致" §3.3.2: s = sum_h
+// w_h max(0, q_h . k^_j); [DF] "CSA2 与每 token 890 字节" §4.1 causal visibility), organised
+// for the MFMA-bound case where every query reads the same K rows.
+#include "index_common.hpp"
+
+namespace csa2 {
+namespace {
+using namespace idx;
+
+// ---------------------------------------------------------------------------------------
+// Many queries over one sequence (a prefill chunk).  Every query of a workgroup reads the
+// same K rows, so each tile of 32 entries is decoded once, into LDS as the bf16 B fragments
+// of the eight MFMA steps, and every wave runs its two queries against it: one fragment read
+// feeds two MFMAs and the FP4 conversion is shared by the eight queries of the workgroup.
+// Tiles are double-buffered in LDS and their raw bytes prefetched kMqDepth tiles ahead.  A
+// workgroup whose queries belong to different sequences scores each query from its own rows
+// instead (the single-query path, one wave per query).
+constexpr int kMqQPW = 2;                      // queries per wave
+constexpr int kMqQB = kMqQPW * kWaves;         // queries per workgroup
+constexpr int kMqTiles = 32;                   // tiles of 32 entries per workgroup
+constexpr int kMqDepth = 3;                    // raw tiles in flight per wave
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void index_score_mq_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
+    const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
+    const int32_t* __restrict__ q_nvis, int32_t n_q, int32_t width, float* __restrict__ scores,
+    float* __restrict__ block_max) {
+  __shared__ __attribute__((aligned(16))) bf16x8 s_b[2][8][64];  // [buffer][MFMA step][lane]
+  __shared__ int64_t s_base[kMqQB];
+  __shared__ int32_t s_nvis[kMqQB];
+  __shared__ __attribute__((aligned(16))) float s_w[kMqQB][kIdxHeads];  // head weights
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  const int qb0 = blockIdx.y * kMqQB;
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  const int32_t tile0 = blockIdx.x * kMqTiles;
+  const int32_t tile1 = min(tile0 + kMqTiles, ntiles);
+  const int32_t nbw = (width + kBlock - 1) / kBlock;
+  if (threadIdx.x < kMqQB) {
+    const int t = qb0 + threadIdx.x;
+    s_base[threadIdx.x] = t < n_q ? q_base[t] : -1;
+    s_nvis[threadIdx.x] = t < n_q ? q_nvis[t] : 0;
+  }
+  {
+    const int j = threadIdx.x >> 5, h = threadIdx.x & 31;  // 256 threads = 8 queries x 32 heads
+    const int t = qb0 + j;
+    s_w[j][h] = t < n_q ? head_w[(int64_t)t * kIdxHeads + h] : 0.0f;
+  }
+  __syncthreads();
+  const int64_t base0 = s_base[0];
+  int32_t max_nvis = 0;
+  bool shared = true;
+  for (int j = 0; j < kMqQB; j++) {
+    if (qb0 + j >= n_q) break;
+    max_nvis = max(max_nvis, s_nvis[j]);
+    shared = shared && s_base[j] == base0;
+  }
+  // this wave's queries: A fragments (head n, dims 64g + 8s ..) and head weights
+  bf16x8 a[kMqQPW][8];
+  int32_t nv[kMqQPW];
+  int tq[kMqQPW];
+#pragma unroll
+  for (int j = 0; j < kMqQPW; j++) {
+    const int t = qb0 + wave * kMqQPW + j;
+    tq[j] = t;
+    const int tt = t < n_q ? t : qb0;  // a padding slot reads a real query and writes nothing
+    nv[j] = t < n_q ? s_nvis[wave * kMqQPW + j] : 0;
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)tt * kIdxHeads + n) * kIdxDim + 64 * g);
+#pragma unroll
+    for (int s = 0; s < 8; s++) a[j][s] = __builtin_bit_cast(bf16x8, qp[s]);
+  }
+  // scores of one query for one tile from its accumulators: ReLU, head weights (accumulator
+  // row 4c + r of this lane is head 8c + 4g + r), head sum
+  auto finish = [&](int j, const f32x16& acc, int32_t k) {
+    const float* wj = &s_w[wave * kMqQPW + j][4 * g];
+    float part[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const float4 w4 = *reinterpret_cast<const float4*>(wj + 8 * c);
+      part[c] = w4.x * __builtin_fmaxf(acc[4 * c], 0.0f);
+      part[c] = __builtin_fmaf(w4.y, __builtin_fmaxf(acc[4 * c + 1], 0.0f), part[c]);
+      part[c] = __builtin_fmaf(w4.z, __builtin_fmaxf(acc[4 * c + 2], 0.0f), part[c]);
+      part[c] = __builtin_fmaf(w4.w, __builtin_fmaxf(acc[4 * c + 3], 0.0f), part[c]);
+    }
+    const int32_t p = k * kTile + n;
+    const float sum = sum_halves((part[0] + part[1]) + (part[2] + part[3]));
+    const float sc = p < nv[j] ? sum : -__builtin_inff();
+    if (tq[j] < n_q) {
+      if (g == 0 && p < width) scores[(int64_t)tq[j] * width + p] = sc;
+      if (block_max != nullptr) {
+        const float bm = max8_lanes(sc);
+        if (g == 0 && (n & 7) == 0 && p < width) block_max[(int64_t)tq[j] * nbw + (p >> 3)] = bm;
+      }
+    }
+  };
+
+  if (shared && max_nvis > 0) {
+    // wave w decodes MFMA steps 2w and 2w+1 of every tile: lane (n, g) takes payload bytes
+    // 32g + 8w .. +7 of entry n and the E8M0 byte of that 32-dim group
+    const uint8_t* last_row = idx_cache + (base0 + max_nvis - 1) * kIdxBytes;
+    struct Raw { u32x2_a4 w; uint32_t sc; };
+    auto load = [&](int32_t k, Raw& r) {
+      const int32_t p = k * kTile + n;
+      const uint8_t* row = p < max_nvis ? idx_cache + (base0 + p) * kIdxBytes : last_row;
+      r.w = *reinterpret_cast<const u32x2_a4*>(row + 32 * g + 8 * wave);
+      r.sc = row[64 + 2 * g + (wave >= 2 ? 1 : 0)];
+    };
+    auto stage = [&](const Raw& r, int buf) {
+      const float x = e8m0_scale(r.sc);
+      s_b[buf][2 * wave][lane] = cvt_fp4x8(r.w[0], x);
+      s_b[buf][2 * wave + 1][lane] = cvt_fp4x8(r.w[1], x);
+    };
+    // tiles that some query of the block can see
+    const int32_t tend = min(tile1, (max_nvis + kTile - 1) / kTile);
+    Raw pipe[kMqDepth];
+#pragma unroll
+    for (int u = 0; u < kMqDepth; u++)
+      if (tile0 + u < tend) load(tile0 + u, pipe[u]);
+    if (tile0 < tend) {
+      stage(pipe[0], 0);
+      if (tile0 + kMqDepth < tend) load(tile0 + kMqDepth, pipe[0]);
+    }
+    __syncthreads();
+    for (int32_t k0 = tile0; k0 < tend; k0 += kMqDepth) {
+#pragma unroll
+      for (int u = 0; u < kMqDepth; u++) {
+        const int32_t k = k0 + u;
+        if (k < tend) {
+          const int buf = (k - tile0) & 1;
+          // stage the next tile into the other buffer, then refill its pipeline slot
+          if (k + 1 < tend) {
+            const int un = (u + 1) % kMqDepth;
+            stage(pipe[un], buf ^ 1);
+            if (k + 1 + kMqDepth < tend) load(k + 1 + kMqDepth, pipe[un]);
+          }
+          f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+          for (int s = 0; s < 8; s++) {
+            const bf16x8 b = s_b[buf][s][lane];
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], b, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], b, acc1, 0, 0, 0);
+          }
+          finish(0, acc0, k);
+          finish(1, acc1, k);
+          __syncthreads();  // buffer buf is free again; buf ^ 1 is complete
+        }
+      }
+    }
+    // tiles past every query's visible range
+    for (int32_t k = max(tend, tile0); k < tile1; k++) {
+#pragma unroll
+      for (int j = 0; j < kMqQPW; j++) {
+        const f32x16 z = {};
+        finish(j, z, k);
+      }
+    }
+    return;
+  }
+  // mixed sequences (or nothing visible): each query from its own rows, one tile at a time
+  for (int j = 0; j < kMqQPW; j++) {
+    const int t = tq[j];
+    if (t >= n_q) continue;
+    const int64_t base = s_base[wave * kMqQPW + j];
+    const uint8_t* last_row = idx_cache + (base + max(nv[j], 1) - 1) * kIdxBytes;
+    for (int32_t k = tile0; k < tile1; k++) {
+      const int32_t p = k * kTile + n;
+      f32x16 acc = {};
+      if (nv[j] > 0 && k * kTile < nv[j]) {
+        const uint8_t* row = p < nv[j] ? idx_cache + (base + p) * kIdxBytes : last_row;
+        const u32x4_a4 lo = *reinterpret_cast<const u32x4_a4*>(row + 32 * g);
+        const u32x4_a4 hi = *reinterpret_cast<const u32x4_a4*>(row + 32 * g + 16);
+        const uint32_t scw = *reinterpret_cast<const uint32_t*>(row + 64);
+        const float x0 = e8m0_scale((scw >> (16 * g)) & 255u);
+        const float x1 = e8m0_scale((scw >> (16 * g + 8)) & 255u);
+        const uint32_t words[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int s = 0; s < 8; s++)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][s], cvt_fp4x8(words[s], s < 4 ? x0 : x1), acc, 0, 0, 0);
+      }
+      finish(j, acc, k);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_index_score_mq(const uint16_t* q_idx_bf16, const float* head_w, const uint8_t* idx_cache,
+                          const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
+                          float* block_max, void* stream) {
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  const int64_t gx = (ntiles + kMqTiles - 1) / kMqTiles, gy = (n_q + kMqQB - 1) / kMqQB;
+  if (gx > 0x7FFFFFFF || gy > 65535) return CSA2_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(index_score_mq_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
+                     (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, n_q, width, scores,
+                     block_max);
+  return check_launch();
+}
+
+}  // namespace csa2

@@ -84,6 +84,40 @@ def test_index_score_full_mode(c, n_q, n, width_pad, seed):
     assert np.array_equal(bm, pad.reshape(n_q, nbw, 8).max(axis=2))
 
 
+@pytest.mark.parametrize("shared", [True, False])
+def test_index_score_many_queries(c, shared):
+    """Batches of >= 64 queries take the many-query kernel: one sequence shared by every query
+    (a prefill chunk, causal visibility, tiles decoded once per workgroup of 8 queries), or
+    one sequence per query (each query from its own rows).  72 / 66 queries are not
+    multiples of 8, the widths end in a ragged tile, and some queries see nothing."""
+    n_q = 72 if shared else 66
+    n = 3001 if shared else 611
+    log(f"index_score many queries shared={shared} n_q={n_q} n={n}")
+    kv, ix = synth.random_caches(41 if shared else 42, n if shared else n * n_q)
+    d = synth.query_inputs(43, n_q)
+    if shared:
+        base = np.zeros(n_q, np.int64)
+        nvis = np.array([n - 37 * t for t in range(n_q)], np.int32)
+        nvis[5] = 0
+        nvis[6] = 1
+        nvis[70] = 33
+        width = n + 5
+    else:
+        base = np.arange(n_q, dtype=np.int64) * n
+        nvis = np.array([n - (13 * t) % 97 for t in range(n_q)], np.int32)
+        nvis[3] = 0
+        width = n
+    ref = oracle.index_score(d.q_idx, d.head_w, ix, base, nvis, width)
+    s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), dev(base), dev(nvis), width)
+    torch.cuda.synchronize()
+    s, bm = host(s), host(bm)
+    check_scores(s, ref)
+    nbw = (width + 7) // 8
+    pad = np.full((n_q, nbw * 8), -np.inf, np.float32)
+    pad[:, :width] = s
+    assert np.array_equal(bm, pad.reshape(n_q, nbw, 8).max(axis=2))
+
+
 def test_index_score_candidate_mode(c):
     log("index_score candidate mode")
     n_q, n, M = 3, 5000, 64
