@@ -18,8 +18,8 @@
 //               ascending order, the ids and keys of every item in that bin or above into
 //               one segment per workgroup (list A).  In Full mode it also lists the
 //               entries of the blocks in or above the bin of the K-th largest older block,
-//               and of the newest block, 8 slots per block with the keys below that bin's
-//               lower edge set to 0 (list B).  Every global Top-K entry is
+//               and of the newest block, whose keys reach that bin's lower edge (list B).
+//               Every global Top-K entry is
 //               in list B: the K highest older blocks alone hold K entries at or above
 //               that edge.  The Top-K of the pool equals the global Top-K of the row, since
 //               any entry outside the pool is outranked by the M-1 block maxima above it.
@@ -500,9 +500,9 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
 // Each workgroup covers kSlice items of one query; wave w holds items lo + 256w .. +255 in
 // registers, four per lane.  List A: the items in the bin of the kA-th largest key or
 // above (kA = M-1 for the pool, K in candidate mode), in ascending order.  List B (full
-// mode): for every block of the slice in or above the bin of the K-th largest older-block
-// maximum, and for the newest block, its 8 entries in order, with the keys below that
-// bin's lower edge (and invisible positions) set to 0.  The K highest older blocks alone
+// mode): of every block of the slice in or above the bin of the K-th largest older-block
+// maximum, and of the newest block, the visible entries whose keys reach that bin's lower
+// edge, in ascending order.  The K highest older blocks alone
 // hold K entries at or above that edge, so every Top-K entry keeps its key.
 constexpr int kItemsPerLane = kSlice / kGThreads;
 
@@ -595,34 +595,51 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
   if (tid == 0) ws.cnt_a[(int64_t)t * G + g] = na;
   if (cand) return;
   __syncthreads();
-  // ---- list B: 8 slots per candidate block
+  // ---- list B: the 8 entries of every candidate block whose keys reach the floor, in
+  // order; wave w scores slots 256w .. 256w+255 (4 rounds of 64)
   const int nslots = ncb * kBlock;
   if (nslots > kSegB) {  // segment overflow: the finalize falls back to the full row
     if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = kListCap + 1;
     return;
   }
-  int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * kSegB;
-  uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * kSegB;
   constexpr int kSlotRounds = kSegB / kGThreads;
-  float v[kSlotRounds];
+  uint32_t bk[kSlotRounds];
+  uint64_t bf[kSlotRounds];
+  int cw = 0;
 #pragma unroll
   for (int u = 0; u < kSlotRounds; u++) {  // every score load in flight at once
-    const int c = u * kGThreads + tid;
+    const int c = 256 * wave + 64 * u + lane;
     const int32_t j = c < nslots ? s_cb[c >> 3] * kBlock + (c & 7) : 0;
-    v[u] = (c < nslots && j < r.n) ? r.scores[j] : 0.0f;
+    const float v = (c < nslots && j < r.n) ? r.scores[j] : 0.0f;
+    uint32_t k = (c < nslots && j < r.n) ? order_key(v) : 0u;
+    bk[u] = k >= floor_key ? k : 0u;
   }
 #pragma unroll
   for (int u = 0; u < kSlotRounds; u++) {
-    const int c = u * kGThreads + tid;
-    if (c < nslots) {
-      const int32_t j = s_cb[c >> 3] * kBlock + (c & 7);
-      uint32_t k = j < r.n ? order_key(v[u]) : 0u;
-      if (k < floor_key) k = 0u;
-      bid[c] = j;
-      bkey[c] = k;
-    }
+    bf[u] = __ballot(bk[u] != 0u);
+    cw += __popcll(bf[u]);
   }
-  if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = nslots;
+  if (lane == 0) s_cnt[0][wave] = cw;
+  __syncthreads();
+  int ob2 = 0, nbv = 0;
+#pragma unroll
+  for (int w = 0; w < kGThreads / 64; w++) {
+    ob2 += w < wave ? s_cnt[0][w] : 0;
+    nbv += s_cnt[0][w];
+  }
+  int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * kSegB;
+  uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * kSegB;
+#pragma unroll
+  for (int u = 0; u < kSlotRounds; u++) {
+    if ((bf[u] >> lane) & 1ull) {
+      const int c = 256 * wave + 64 * u + lane;
+      const int pos = ob2 + __popcll(bf[u] & lt);
+      bid[pos] = s_cb[c >> 3] * kBlock + (c & 7);
+      bkey[pos] = bk[u];
+    }
+    ob2 += __popcll(bf[u]);
+  }
+  if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = nbv;
 }
 
 // ------------------------------------------------------------------ K3: exact finalize
