@@ -45,14 +45,17 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--tokens", type=int, default=1048576, help="tokens per sequence")
+    p.add_argument("--no-secondary", action="store_true", help="skip the other seeded workloads")
     p.add_argument("--calibration-copy-mib", type=int, default=0,
                    help="run one device copy of this many MiB before timing (counter calibration)")
     return p.parse_args()
 
 
-def make_batch(csa2, torch, copy_id, n_seq, tokens, m, chunk_tokens=1 << 19):
+def make_batch(csa2, torch, copy_id, n_seq, tokens, m, chunk_tokens=1 << 19, extra_layers=0):
     """Builds one batch copy on the GPU: latents drawn with torch's seeded generator (N(0,1),
-    RMS-normalised, bf16), packed into the caches by csa2_compress_pack."""
+    RMS-normalised, bf16), packed into the caches by csa2_compress_pack.  extra_layers > 0
+    adds a Reindex layer (fresh q_idx ~ N(0,1), head weights, q, window rows) and
+    extra_layers - 1 Reuse layers (fresh q and window rows)."""
     dev = torch.device("cuda")
     n = tokens // m
     gen = torch.Generator(device=dev)
@@ -82,9 +85,19 @@ def make_batch(csa2, torch, copy_id, n_seq, tokens, m, chunk_tokens=1 << 19):
     q = torch.randn((n_seq, 64, 512), generator=gen, device=dev).to(torch.bfloat16)
     sw = torch.randn((n_seq * 128, 512), generator=gen, device=dev)
     swa = (sw / torch.sqrt(torch.mean(sw * sw, dim=1, keepdim=True) + 1e-6)).to(torch.bfloat16)
+    layers = []
+    for li in range(extra_layers):
+        q_l = torch.randn((n_seq, 64, 512), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+        sw = torch.randn((n_seq * 128, 512), generator=gen, device=dev)
+        sw_l = (sw / torch.sqrt(torch.mean(sw * sw, dim=1, keepdim=True) + 1e-6)).to(torch.bfloat16).contiguous()
+        lay = dict(q=q_l, swa=sw_l)
+        if li == 0:
+            lay["q_idx"] = torch.randn((n_seq, 32, 128), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+            lay["head_w"] = (torch.randn((n_seq, 32), generator=gen, device=dev) / 32 ** 0.5).contiguous()
+        layers.append(lay)
     return dict(kv=kv, ix=ix, last_lat=last_lat.contiguous(), pool_w=pool_w, w_idx=w_idx,
                 cs_last=cs_all[n - 1:n].contiguous(), q_idx=q_idx.contiguous(), head_w=head_w.contiguous(),
-                q=q.contiguous(), swa=swa.contiguous())
+                q=q.contiguous(), swa=swa.contiguous(), layers=layers)
 
 
 def cpu_baseline(n_entries, n_q):
@@ -109,16 +122,19 @@ def cpu_baseline(n_entries, n_q):
 
 
 class Decode1M:
-    """Device state for the 1M-context decode workload and its four stages."""
+    """Device state for a decode workload: one Full layer (compress the newest entry, score,
+    select, attend), optionally followed by a Reindex layer (re-score the pool, select inside
+    it, attend) and Reuse layers (attend with the Reindex indices)."""
 
-    def __init__(self, torch, csa2, tokens, n_seq=4, m=2, K=512, M=2048, ncopy=NCOPY):
+    def __init__(self, torch, csa2, tokens, n_seq=4, m=2, K=512, M=2048, ncopy=NCOPY, extra_layers=0):
         self.torch, self.csa2 = torch, csa2
         self.n_seq, self.m, self.tokens, self.K, self.M, self.ncopy = n_seq, m, tokens, K, M, ncopy
+        self.extra = extra_layers
         n = self.n = tokens // m
         dev = torch.device("cuda")
         print(f"[bench] building {ncopy} batch copies of {n_seq} x {tokens} tokens (m={m})", file=sys.stderr,
               flush=True)
-        self.copies = [make_batch(csa2, torch, c, n_seq, tokens, m) for c in range(ncopy)]
+        self.copies = [make_batch(csa2, torch, c, n_seq, tokens, m, extra_layers=extra_layers) for c in range(ncopy)]
         torch.cuda.synchronize()
         self.q_base = torch.arange(n_seq, dtype=torch.int64, device=dev) * n
         self.q_nvis = torch.full((n_seq,), n, dtype=torch.int32, device=dev)
@@ -136,6 +152,10 @@ class Decode1M:
         self.new_kv = [torch.empty((n_seq, 288), dtype=torch.uint8, device=dev) for _ in range(ncopy)]
         self.new_ix = [torch.empty((n_seq, 68), dtype=torch.uint8, device=dev) for _ in range(ncopy)]
         self.cs_new = [c["cs_last"].expand(n_seq, 64).contiguous() for c in self.copies]
+        if extra_layers:
+            self.scores_r = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
+            self.topk_r = torch.empty((n_seq, K), dtype=torch.int32, device=dev)
+        self.n_stages = 4 + (2 + extra_layers if extra_layers else 0)
 
     def run_stage(self, ci, st):
         """One stage of the step for batch copy ci, on torch's current stream."""
@@ -149,12 +169,121 @@ class Decode1M:
         elif st == 2:
             csa2.block_topk(self.scores, self.q_nvis, K=self.K, M=self.M, block_max=self.bmax, pool_out=self.pool,
                             topk_out=self.topk, workspace=self.ws_sel)
-        else:
+        elif st == 3:
             csa2.sparse_attn(c["q"], c["kv"], self.q_base, self.topk, c["swa"], self.swa_start, self.swa_len,
+                             out=self.out, lse=self.lse, workspace=self.ws_att)
+        elif st == 4:  # Reindex layer: re-score the pool with its own indexer query
+            lay = c["layers"][0]
+            csa2.index_score(lay["q_idx"], lay["head_w"], c["ix"], self.q_base, self.q_nvis, 8 * self.M,
+                             pool_blocks=self.pool, scores=self.scores_r)
+        elif st == 5:
+            csa2.block_topk(self.scores_r, self.q_nvis, K=self.K, pool_blocks=self.pool, topk_out=self.topk_r,
+                            workspace=self.ws_sel)
+        else:  # Reindex attention (st 6) and Reuse attention (st 7 ..) on the Reindex indices
+            lay = c["layers"][st - 6]
+            csa2.sparse_attn(lay["q"], c["kv"], self.q_base, self.topk_r, lay["swa"], self.swa_start, self.swa_len,
                              out=self.out, lse=self.lse, workspace=self.ws_att)
 
 
 STAGES = ("compress_newest", "index_score", "block_topk", "sparse_attn")
+
+
+def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3):
+    """Whole-step throughput of a secondary decode workload: one HIP graph per batch copy
+    holding every stage of the step, replayed `steps` times between two synchronisations."""
+    wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers)
+    for i in range(warmup):
+        for st in range(wl.n_stages):
+            wl.run_stage(i % NCOPY, st)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    graphs = []
+    for ci in range(NCOPY):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for st in range(wl.n_stages):
+                wl.run_stage(ci, st)
+        graphs.append(g)
+    for i in range(2 * NCOPY):
+        graphs[i % NCOPY].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % NCOPY].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {"queries_per_s": round(n_seq * steps / wall, 1), "us_per_step": round(wall * 1e6 / steps, 2),
+           "sequences": n_seq, "tokens_per_sequence": tokens, "compress_ratio": m, "entries_per_sequence": wl.n,
+           "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else "")}
+    del graphs, wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=3):
+    """The chunked-prefill workload, one launch per stage timed with HIP events: compress the
+    chunk's 2048 new entries from latents, causal scoring of 4096 queries over <= 34816
+    entries, per-query Top-512, attention for every query.  The history caches are drawn
+    directly (uniform FP4 codes, scale bytes of the synthetic range)."""
+    from fp4_kv_cache_csa2_amd import synth
+    dev = torch.device("cuda")
+    hist = hist_tokens // m
+    n = hist + chunk // m
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    kv = torch.randint(0, 256, (n, 288), dtype=torch.uint8, device=dev, generator=g)
+    kv[:, 256:] = 0x30
+    ix = torch.randint(0, 256, (n, 68), dtype=torch.uint8, device=dev, generator=g)
+    ix[:, 64:] = 126
+    nvis = torch.from_numpy(synth.prefill_nvis(hist_tokens, chunk, m)).to(dev)
+    q_idx = (torch.randn((chunk, 32, 128), device=dev, generator=g) / 128 ** 0.5).to(torch.bfloat16)
+    head_w = torch.randn((chunk, 32), device=dev, generator=g) / 32 ** 0.5
+    q = torch.randn((chunk, 64, 512), device=dev, generator=g).to(torch.bfloat16)
+    sw = torch.randn((chunk + 127, 512), device=dev, generator=g)
+    swa = (sw / torch.sqrt(torch.mean(sw * sw, dim=1, keepdim=True) + 1e-6)).to(torch.bfloat16)
+    base = torch.zeros(chunk, dtype=torch.int64, device=dev)
+    swa_start = torch.arange(chunk, dtype=torch.int64, device=dev)
+    swa_len = torch.full((chunk,), 128, dtype=torch.int32, device=dev)
+    x = torch.randn((chunk, 512), device=dev, generator=g)
+    lat = (x / torch.sqrt(torch.mean(x * x, dim=1, keepdim=True) + 1e-6)).to(torch.bfloat16)
+    pool_w = torch.nn.functional.softplus(torch.randn((m, 512), device=dev, generator=g)).contiguous()
+    w_idx = (torch.randn((128, 512), device=dev, generator=g) / 512 ** 0.5).to(torch.bfloat16)
+    cs = csa2.rope_table(np.arange(hist, n, dtype=np.int64) * m).to(dev)
+    scores = torch.empty((chunk, n), dtype=torch.float32, device=dev)
+    topk = torch.empty((chunk, 512), dtype=torch.int32, device=dev)
+    out = torch.empty((chunk, 64, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((chunk, 64), dtype=torch.float32, device=dev)
+    ws = torch.zeros(csa2.block_topk_workspace(chunk, n, 2048, 512), dtype=torch.uint8, device=dev)
+    wsa = torch.empty(max(16, csa2.sparse_attn_workspace(chunk, 512)), dtype=torch.uint8, device=dev)
+    stages = {
+        "compress_2048_entries": lambda: csa2.compress_pack(lat, m, pool_w, cs, w_idx, kv_out=kv[hist:],
+                                                           idx_out=ix[hist:]),
+        "index_4096_queries": lambda: csa2.index_score(q_idx, head_w, ix, base, nvis, n, scores=scores,
+                                                       want_block_max=False),
+        "select_4096_queries": lambda: csa2.block_topk(scores, nvis, want_pool=False, topk_out=topk, workspace=ws),
+        "attn_4096_queries": lambda: csa2.sparse_attn(q, kv, base, topk, swa, swa_start, swa_len, out=out,
+                                                      lse=lse, workspace=wsa),
+    }
+    ms = {}
+    for name, fn in stages.items():
+        fn()
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms[name] = round(a.elapsed_time(b) / reps, 4)
+    flops = 2.0 * 32 * 128 * float(nvis.sum().item())
+    res = {"ms": ms, "total_ms": round(sum(ms.values()), 4),
+           "index_mfma": {"achieved_tflops": round(flops / (ms["index_4096_queries"] * 1e-3) / 1e12, 1),
+                          "peak_tflops": 2500.0, "dtype": "bf16",
+                          "frac": round(flops / (ms["index_4096_queries"] * 1e-3) / 2.5e15, 4)}}
+    del kv, ix, scores, out, ws, wsa
+    torch.cuda.empty_cache()
+    return res
 # the sources the decode-path index kernel is built from
 INDEX_SRCS = [os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "csrc", f)
               for f in ("index_score.hip", "index_common.hpp", "csa2_device.hpp")]
@@ -278,6 +407,18 @@ def main():
                      "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": idx_bytes},
     }
+    if not args.no_secondary:
+        # the other seeded workloads, each in its own graphs after the timed region above
+        del step_graph, stage_graph, wl
+        torch.cuda.empty_cache()
+        print("[bench] secondary workloads", file=sys.stderr, flush=True)
+        sec = {
+            "decode_128k_b16_m1": time_decode(torch, csa2, 131072, 16, 1, extra_layers=4),
+            "decode_32k_b4_m1": time_decode(torch, csa2, 32768, 4, 1),
+            "tiny_4k_b1_m2": time_decode(torch, csa2, 4096, 1, 2),
+            "prefill_chunk4096_hist65536_m2": time_prefill(torch, csa2),
+        }
+        line["secondary"] = sec
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(n, n_seq)

@@ -248,31 +248,47 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     }
   }
 
-  // ---- epilogue: lane holds O[head 16w + 4g + r][dim 16dt + i]
-  if (n_splits == 1) {
+  // ---- epilogue: lane holds O[head 16w + 4g + r][dim 16dt + i].  The rows go out through
+  // the (now idle) key tile in LDS: each wave writes its 16 heads x 256 dims in fp32, then
+  // reads back whole rows as float4, so every global store instruction covers 1 KB.
+  const bool single = n_splits == 1;
+  const int64_t slot = (int64_t)t * n_splits + split;
+  float scale_r[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) scale_r[r] = single ? (l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f) : 1.0f;
+  if (i == 0) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int h = 16 * w + 4 * g + r;
-      const float inv = l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f;
-      float* orow = out + ((int64_t)t * kHeads + h) * kD;
-#pragma unroll
-      for (int dt = 0; dt < 32; dt++) orow[16 * dt + i] = o[dt][r] * inv;
-      if (lse != nullptr && i == 0)
-        lse[(int64_t)t * kHeads + h] = l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
-    }
-  } else {
-    const int64_t slot = (int64_t)t * n_splits + split;
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int h = 16 * w + 4 * g + r;
-      float* orow = ws_o + (slot * kHeads + h) * kD;
-#pragma unroll
-      for (int dt = 0; dt < 32; dt++) orow[16 * dt + i] = o[dt][r];
-      if (i == 0) {
+      if (single) {
+        if (lse != nullptr)
+          lse[(int64_t)t * kHeads + h] = l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
+      } else {
         ws_ml[(slot * kHeads + h) * 2 + 0] = m_run[r];
         ws_ml[(slot * kHeads + h) * 2 + 1] = l_run[r];
       }
     }
+  }
+  constexpr int kOStride = 256 + 4;  // floats per staged row (padding spreads the banks)
+  float* stage_o = reinterpret_cast<float*>(sh.k) + w * 16 * kOStride;  // 16.3 KB per wave
+  float* orow0 = single ? out + ((int64_t)t * kHeads + 16 * w) * kD : ws_o + (slot * kHeads + 16 * w) * kD;
+  __syncthreads();  // every wave is done reading the key tile
+#pragma unroll
+  for (int half = 0; half < 2; half++) {
+#pragma unroll
+    for (int dt = 0; dt < 16; dt++) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) stage_o[(4 * g + r) * kOStride + 16 * dt + i] = o[16 * half + dt][r] * scale_r[r];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int row = 0; row < 16; row++) {
+      const float4 v = *reinterpret_cast<const float4*>(stage_o + row * kOStride + 4 * lane);
+      *reinterpret_cast<float4*>(orow0 + (int64_t)row * kD + 256 * half + 4 * lane) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next half overwrites the rows
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
