@@ -10,10 +10,11 @@
 // Design (three kernels, launched back to back on the caller's stream).  The ranking key
 // of a value is an order-preserving uint32 map of the fp32 value (NaN as -inf); its top
 // 12 bits are its histogram bin.
-//   K1 hist     1024-thread workgroups of 4096 keys each build a 4096-bin histogram of
+//   K1 hist     1024-thread workgroups of 8192 keys each build a 4096-bin histogram of
 //               the ranking keys (older blocks' maxima in Full mode, pool entries in
 //               candidate mode) in LDS and add it into a per-query histogram in the
-//               workspace (few, large workgroups: every global add is a slow atomic).
+//               workspace (few, large workgroups: every global add is a slow atomic; a
+//               row that one workgroup covers is written with plain stores).
 //   K2 collect  workgroups of 1024 items find the bin of the k-th largest key and write, in
 //               ascending order, the ids and keys of every item in that bin or above into
 //               one segment per workgroup (list A).  In Full mode it also lists the
@@ -41,7 +42,7 @@ namespace {
 constexpr int kBins = 4096;        // 12-bit histogram digit
 constexpr int kBinShift = 20;
 constexpr int kSlice = 1024;       // keys per workgroup in K2
-constexpr int kHSlice = 4096;      // keys per workgroup in K1 (fewer global histogram adds)
+constexpr int kHSlice = 8192;      // keys per workgroup in K1 (fewer global histogram adds)
 constexpr int kHThreads = 1024;    // K1 workgroup size
 constexpr int kGThreads = 256;     // K1 / K2 workgroup size
 constexpr int kFThreads = 1024;    // K3 workgroup size
@@ -491,8 +492,13 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
   for (int u = 0; u < kPerH; u++) hist_add(h, keys[u] >> kBinShift, keys[u] != 0u);
   __syncthreads();
   uint32_t* gh = ws.hist + (int64_t)t * kBins;
-  for (int b = tid; b < kBins; b += kHThreads)
-    if (h[b]) atomicAdd(&gh[b], h[b]);
+  if (gridDim.x == 1) {  // the only workgroup of its row: plain stores (the region starts zeroed)
+    for (int b = tid; b < kBins; b += kHThreads)
+      if (h[b]) gh[b] = h[b];
+  } else {
+    for (int b = tid; b < kBins; b += kHThreads)
+      if (h[b]) atomicAdd(&gh[b], h[b]);
+  }
 }
 
 // ------------------------------------------------------------------ K2: ordered collection
@@ -595,49 +601,55 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
   if (tid == 0) ws.cnt_a[(int64_t)t * G + g] = na;
   if (cand) return;
   __syncthreads();
-  // ---- list B: the 8 entries of every candidate block whose keys reach the floor, in
-  // order; wave w scores slots 256w .. 256w+255 (4 rounds of 64)
+  // ---- list B: of every candidate block, the entries whose keys reach the floor, in
+  // order.  Slots (8 per block) go in chunks of 1024: wave w scores slots 256w .. 256w+255
+  // of the chunk (4 rounds of 64), and the chunk's survivors append after the last ones.
   const int nslots = ncb * kBlock;
-  if (nslots > kSegB) {  // segment overflow: the finalize falls back to the full row
-    if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = kListCap + 1;
-    return;
-  }
   constexpr int kSlotRounds = kSegB / kGThreads;
-  uint32_t bk[kSlotRounds];
-  uint64_t bf[kSlotRounds];
-  int cw = 0;
-#pragma unroll
-  for (int u = 0; u < kSlotRounds; u++) {  // every score load in flight at once
-    const int c = 256 * wave + 64 * u + lane;
-    const int32_t j = c < nslots ? s_cb[c >> 3] * kBlock + (c & 7) : 0;
-    const float v = (c < nslots && j < r.n) ? r.scores[j] : 0.0f;
-    uint32_t k = (c < nslots && j < r.n) ? order_key(v) : 0u;
-    bk[u] = k >= floor_key ? k : 0u;
-  }
-#pragma unroll
-  for (int u = 0; u < kSlotRounds; u++) {
-    bf[u] = __ballot(bk[u] != 0u);
-    cw += __popcll(bf[u]);
-  }
-  if (lane == 0) s_cnt[0][wave] = cw;
-  __syncthreads();
-  int ob2 = 0, nbv = 0;
-#pragma unroll
-  for (int w = 0; w < kGThreads / 64; w++) {
-    ob2 += w < wave ? s_cnt[0][w] : 0;
-    nbv += s_cnt[0][w];
-  }
   int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * kSegB;
   uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * kSegB;
+  int nbv = 0;
+  for (int c0 = 0; c0 < nslots; c0 += kSegB) {
+    uint32_t bk[kSlotRounds];
+    uint64_t bf[kSlotRounds];
+    int cw = 0;
 #pragma unroll
-  for (int u = 0; u < kSlotRounds; u++) {
-    if ((bf[u] >> lane) & 1ull) {
-      const int c = 256 * wave + 64 * u + lane;
-      const int pos = ob2 + __popcll(bf[u] & lt);
-      bid[pos] = s_cb[c >> 3] * kBlock + (c & 7);
-      bkey[pos] = bk[u];
+    for (int u = 0; u < kSlotRounds; u++) {  // every score load of the chunk in flight at once
+      const int c = c0 + 256 * wave + 64 * u + lane;
+      const int32_t j = c < nslots ? s_cb[c >> 3] * kBlock + (c & 7) : 0;
+      const float v = (c < nslots && j < r.n) ? r.scores[j] : 0.0f;
+      const uint32_t k = (c < nslots && j < r.n) ? order_key(v) : 0u;
+      bk[u] = k >= floor_key ? k : 0u;
     }
-    ob2 += __popcll(bf[u]);
+#pragma unroll
+    for (int u = 0; u < kSlotRounds; u++) {
+      bf[u] = __ballot(bk[u] != 0u);
+      cw += __popcll(bf[u]);
+    }
+    if (lane == 0) s_cnt[0][wave] = cw;
+    __syncthreads();
+    int ob2 = nbv, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kGThreads / 64; w++) {
+      ob2 += w < wave ? s_cnt[0][w] : 0;
+      tot += s_cnt[0][w];
+    }
+    __syncthreads();  // s_cnt is rewritten by the next chunk
+    if (nbv + tot > kSegB) {  // segment overflow: the finalize falls back to the full row
+      if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = kListCap + 1;
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < kSlotRounds; u++) {
+      if ((bf[u] >> lane) & 1ull) {
+        const int c = c0 + 256 * wave + 64 * u + lane;
+        const int pos = ob2 + __popcll(bf[u] & lt);
+        bid[pos] = s_cb[c >> 3] * kBlock + (c & 7);
+        bkey[pos] = bk[u];
+      }
+      ob2 += __popcll(bf[u]);
+    }
+    nbv += tot;
   }
   if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = nbv;
 }
