@@ -71,6 +71,13 @@ def lib():
         L.csa2o_block_topk.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, vp, vp]
         L.csa2o_topk_bruteforce.argtypes = [vp, i32, i32, vp, i32, vp]
         L.csa2o_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_float, vp, vp, i32]
+        L.csa2o_swa_fp8_row_bytes.argtypes = []
+        L.csa2o_swa_fp8_row_bytes.restype = i64
+        L.csa2o_e8m0_scale_code_e4m3.argtypes = [ctypes.c_float]
+        L.csa2o_e8m0_scale_code_e4m3.restype = ctypes.c_int
+        L.csa2o_swa_fp8_pack.argtypes = [vp, i64, vp]
+        L.csa2o_dequant_swa_fp8.argtypes = [vp, vp]
+        L.csa2o_sparse_attn_swa_fp8.argtypes = [vp, vp, vp, vp, i32, vp, i64, vp, vp, ctypes.c_float, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -218,4 +225,49 @@ def sparse_attn(q_bf16, kv_cache, q_base, topk, swa_bf16, swa_start, swa_len,
     lse = np.empty((n_q, N_HEADS), np.float32)
     lib().csa2o_sparse_attn(_p(q), _p(cache), _p(base), _p(tk), K, _p(swa), _p(ss), _p(sl),
                             float(scale), _p(out), _p(lse), n_q)
+    return out, lse
+
+
+# ---- FP8 window rows: the sliding-window KV kept in FP8 ([ZB] §2.4.4; the 584-byte FP8 KV
+# entry of [ZB] §3.1 and [DF] §4.6)
+def swa_fp8_row_bytes() -> int:
+    return int(lib().csa2o_swa_fp8_row_bytes())
+
+
+def e8m0_scale_code_e4m3(amax: float) -> int:
+    return int(lib().csa2o_e8m0_scale_code_e4m3(float(amax)))
+
+
+def swa_fp8_pack(rows_bf16):
+    """bf16 rows [n, 512] (uint16 bits) -> FP8 window rows [n, 584] u8."""
+    rows = _c(rows_bf16, np.uint16)
+    n = rows.shape[0]
+    out = np.empty((n, swa_fp8_row_bytes()), np.uint8)
+    lib().csa2o_swa_fp8_pack(_p(rows), n, _p(out))
+    return out
+
+
+def dequant_swa_fp8(rows8):
+    rows8 = _c(rows8, np.uint8)
+    out = np.empty((rows8.shape[0], D_LAT), np.float64)
+    for r in range(rows8.shape[0]):
+        lib().csa2o_dequant_swa_fp8(_p(rows8[r]), _p(out[r]))
+    return out
+
+
+def sparse_attn_swa_fp8(q_bf16, kv_cache, q_base, topk, swa8, swa_start, swa_len, swa_ring: int = 0,
+                        scale: float = 1.0 / np.sqrt(512.0)):
+    q = _c(q_bf16, np.uint16)
+    n_q = q.shape[0]
+    cache = _c(kv_cache, np.uint8)
+    base = _c(q_base, np.int64)
+    tk = _c(topk, np.int32)
+    K = tk.shape[1]
+    w8 = _c(swa8, np.uint8)
+    ss = _c(swa_start, np.int64)
+    sl = _c(swa_len, np.int32)
+    out = np.empty((n_q, N_HEADS, D_LAT), np.float32)
+    lse = np.empty((n_q, N_HEADS), np.float32)
+    lib().csa2o_sparse_attn_swa_fp8(_p(q), _p(cache), _p(base), _p(tk), K, _p(w8), int(swa_ring), _p(ss), _p(sl),
+                                    float(scale), _p(out), _p(lse), n_q)
     return out, lse

@@ -374,10 +374,86 @@ void csa2o_topk_bruteforce(const float *scores, int32_t n_q, int32_t width, cons
 
 /* ------------------------------------------------------------------ stage 4 */
 
-void csa2o_sparse_attn(const uint16_t *q, const uint8_t *kv_cache, const int64_t *q_base,
-                       const int32_t *topk, int32_t K, const uint16_t *swa,
-                       const int64_t *swa_start, const int32_t *swa_len, float scale,
-                       float *out, float *lse, int32_t n_q) {
+/* ------------------------------------------------------------------ FP8 window rows */
+
+/* A window row in FP8 ([ZB] §2.4.4 and [SR] "FP4 Main KV Cache": the sliding-window KV
+ * keeps FP8 precision; [ZB] §3.1 and [DF] §4.6 give DeepSeek-V4's FP8 KV entry as 448 FP8 NoPE
+ * channels + 64 BF16 RoPE channels + 8 bytes of FP8 scales = 584 B, the layout taken
+ * here): bytes [0, 448) E4M3 codes of channels 0..447, [448, 576) the BF16 bits of
+ * channels 448..511, [576, 583) one E8M0 scale per 64 NoPE channels, byte 583 zero.
+ * Scale: the OCP MX rule with E4M3's largest exponent (8), X = 2^(floor(log2 amax) - 8);
+ * element: nearest-even E4M3 of x / X, saturating at 448, sign only on non-zero codes. */
+int64_t csa2o_swa_fp8_row_bytes(void) { return D_NOPE + 2 * D_ROPE + 8; }
+
+int csa2o_e8m0_scale_code_e4m3(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ex;
+  frexpf(amax, &ex); /* floor(log2 amax) = ex - 1 */
+  int code = (ex - 1) - 8 + 127;
+  if (code < 0) code = 0;
+  if (code > 254) code = 254;
+  return code;
+}
+
+void csa2o_swa_fp8_pack(const uint16_t *rows, int64_t n, uint8_t *out) {
+  const int64_t rb = csa2o_swa_fp8_row_bytes();
+  for (int64_t r = 0; r < n; r++) {
+    const uint16_t *x = rows + r * D_LAT;
+    uint8_t *o = out + r * rb;
+    for (int g = 0; g < D_NOPE / 64; g++) {
+      float amax = 0.0f;
+      for (int c = 64 * g; c < 64 * g + 64; c++) {
+        float a = fabsf(bf16_to_f32(x[c]));
+        if (a > amax) amax = a;
+      }
+      const int code = csa2o_e8m0_scale_code_e4m3(amax);
+      o[D_NOPE + 2 * D_ROPE + g] = (uint8_t)code;
+      for (int c = 64 * g; c < 64 * g + 64; c++) {
+        const double v = (double)bf16_to_f32(x[c]);
+        const int e = csa2o_e4m3_encode(ldexp(fabs(v), 127 - code));
+        o[c] = (uint8_t)((v < 0.0 && e != 0) ? (e | 0x80) : e);
+      }
+    }
+    for (int c = D_NOPE; c < D_LAT; c++) {
+      o[D_NOPE + 2 * (c - D_NOPE)] = (uint8_t)(x[c] & 0xFF);
+      o[D_NOPE + 2 * (c - D_NOPE) + 1] = (uint8_t)(x[c] >> 8);
+    }
+    o[rb - 1] = 0;
+  }
+}
+
+void csa2o_dequant_swa_fp8(const uint8_t *row, double *out) {
+  for (int c = 0; c < D_NOPE; c++)
+    out[c] = csa2o_e4m3_value(row[c]) * csa2o_e8m0_value(row[D_NOPE + 2 * D_ROPE + c / 64]);
+  for (int c = D_NOPE; c < D_LAT; c++) {
+    const uint16_t b = (uint16_t)(row[D_NOPE + 2 * (c - D_NOPE)] | (row[D_NOPE + 2 * (c - D_NOPE) + 1] << 8));
+    out[c] = (double)bf16_to_f32(b);
+  }
+}
+
+/* ------------------------------------------------------------------ stage 4 */
+
+/* one window row into doubles: bf16 rows, or FP8 rows when swa8 != NULL */
+typedef struct {
+  const uint16_t *swa;
+  const uint8_t *swa8;
+  int64_t ring;
+} window_src;
+
+static void window_row(const window_src *w, int64_t row, double *out) {
+  if (w->ring > 0) row %= w->ring;
+  if (w->swa8 != NULL) {
+    csa2o_dequant_swa_fp8(w->swa8 + row * csa2o_swa_fp8_row_bytes(), out);
+  } else {
+    const uint16_t *r = w->swa + row * D_LAT;
+    for (int d = 0; d < D_LAT; d++) out[d] = (double)bf16_to_f32(r[d]);
+  }
+}
+
+static void sparse_attn_core(const uint16_t *q, const uint8_t *kv_cache, const int64_t *q_base,
+                             const int32_t *topk, int32_t K, const window_src *win,
+                             const int64_t *swa_start, const int32_t *swa_len, float scale,
+                             float *out, float *lse, int32_t n_q) {
   int32_t cap = K + 128;
   double *keys = (double *)malloc(sizeof(double) * (size_t)cap * D_LAT);
   double *logit = (double *)malloc(sizeof(double) * (size_t)cap);
@@ -393,8 +469,7 @@ void csa2o_sparse_attn(const uint16_t *q, const uint8_t *kv_cache, const int64_t
     }
     int32_t nw = swa_len[t] < 128 ? swa_len[t] : 128;
     for (int32_t r = 0; r < nw; r++) {
-      const uint16_t *row = swa + (swa_start[t] + r) * D_LAT;
-      for (int d = 0; d < D_LAT; d++) keys[(int64_t)nk * D_LAT + d] = (double)bf16_to_f32(row[d]);
+      window_row(win, swa_start[t] + r, keys + (int64_t)nk * D_LAT);
       nk++;
     }
     for (int h = 0; h < N_HEADS; h++) {
@@ -425,4 +500,20 @@ void csa2o_sparse_attn(const uint16_t *q, const uint8_t *kv_cache, const int64_t
   }
   free(logit);
   free(keys);
+}
+
+void csa2o_sparse_attn(const uint16_t *q, const uint8_t *kv_cache, const int64_t *q_base,
+                       const int32_t *topk, int32_t K, const uint16_t *swa,
+                       const int64_t *swa_start, const int32_t *swa_len, float scale,
+                       float *out, float *lse, int32_t n_q) {
+  const window_src w = {swa, NULL, 0};
+  sparse_attn_core(q, kv_cache, q_base, topk, K, &w, swa_start, swa_len, scale, out, lse, n_q);
+}
+
+void csa2o_sparse_attn_swa_fp8(const uint16_t *q, const uint8_t *kv_cache, const int64_t *q_base,
+                               const int32_t *topk, int32_t K, const uint8_t *swa8, int64_t swa_ring,
+                               const int64_t *swa_start, const int32_t *swa_len, float scale,
+                               float *out, float *lse, int32_t n_q) {
+  const window_src w = {NULL, swa8, swa_ring};
+  sparse_attn_core(q, kv_cache, q_base, topk, K, &w, swa_start, swa_len, scale, out, lse, n_q);
 }

@@ -92,6 +92,23 @@ void csa2o_sparse_attn(const uint16_t *q, const uint8_t *kv_cache, const int64_t
                        const int64_t *swa_start, const int32_t *swa_len, float scale,
                        float *out, float *lse, int32_t n_q);
 
+/* ---- FP8 window rows (the sliding-window KV kept in FP8: [ZB] §2.4.4, [SR] "FP4 Main
+ * KV Cache"; the 584-byte FP8 KV entry of [ZB] §3.1 and [DF] §4.6) ------------------------
+ * row: [0,448) E4M3 codes of channels 0..447 | [448,576) BF16 bits of channels 448..511 |
+ * [576,583) E8M0 scale per 64 NoPE channels | byte 583 = 0.
+ * Scale X = 2^(floor(log2 amax) - 8) (OCP MX rule, E4M3 emax 8); codes nearest-even of
+ * x / X, saturating at 448, sign only on non-zero codes. */
+int64_t csa2o_swa_fp8_row_bytes(void);
+int csa2o_e8m0_scale_code_e4m3(float amax);
+void csa2o_swa_fp8_pack(const uint16_t *rows_bf16, int64_t n, uint8_t *out);
+void csa2o_dequant_swa_fp8(const uint8_t *row, double *out512);
+/* stage 4 with an FP8 window cache: window row r of query t is swa_start[t] + r, taken
+ * modulo swa_ring when swa_ring > 0 (a ring buffer of swa_ring rows). */
+void csa2o_sparse_attn_swa_fp8(const uint16_t *q, const uint8_t *kv_cache, const int64_t *q_base,
+                               const int32_t *topk, int32_t K, const uint8_t *swa8, int64_t swa_ring,
+                               const int64_t *swa_start, const int32_t *swa_len, float scale,
+                               float *out, float *lse, int32_t n_q);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,186 @@
+"""Pins for the oracle's FP8 sliding-window rows and the attention that reads them (CPU only).
+
+The window rows keep FP8 precision ([ZB] §2.4.4 "FP4 Main KV Cache"; the 584-byte
+FP8 KV entry of [ZB] §3.1 and [DF] §4.6).  Each test pins the oracle to something
+other than itself: the byte count the pages print, numpy's frexp for the scale rule,
+torch's own float8_e4m3fn conversion for the element codes, exact round trips of rows
+built from representable values, the half-spacing error bound of nearest rounding, and
+the already-pinned bf16-window attention on the dequantised rows."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_kv_cache_csa2_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.txt")
+
+
+def _golden(key):
+    for line in open(GOLDEN):
+        line = line.split("|")[0].strip()
+        if line and not line.startswith("#"):
+            k, v = [s.strip() for s in line.split("=")]
+            if k == key:
+                return float(v)
+    raise KeyError(key)
+
+
+E4M3 = np.array([oracle.e4m3_value(c) for c in range(0x7F)])  # finite non-negative grid
+
+
+def test_row_bytes_is_the_v4_fp8_entry():
+    assert oracle.swa_fp8_row_bytes() == _golden("v4flash_main_entry_bytes") == 448 * 1 + 64 * 2 + 8
+
+
+@pytest.mark.parametrize("amax", [1e-30, 2.0 ** -126, 0.0137, 0.5, 1.0, 1.75, 2.0, 7.99, 448.0, 3.0e5,
+                                  2.0 ** 126 * 1.5, 3.0e38])
+def test_scale_code_is_floor_log2_minus_8(amax):
+    m, e = np.frexp(np.float32(amax))  # amax = m 2^e with m in [0.5, 1)
+    want = int(np.clip(e - 1 - 8 + 127, 0, 254))
+    assert oracle.e8m0_scale_code_e4m3(amax) == want
+    if 0 < want < 254:  # unclamped: amax / X lands in [256, 512)
+        assert 256.0 <= amax / 2.0 ** (want - 127) < 512.0
+
+
+def test_scale_code_of_zero_and_nan():
+    assert oracle.e8m0_scale_code_e4m3(0.0) == 0
+    assert oracle.e8m0_scale_code_e4m3(float("nan")) == 0
+
+
+def _random_rows(seed, n, spread=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    if spread:  # groups of very different magnitude, some all-zero, a few tiny values
+        x *= (2.0 ** rng.integers(-12, 12, size=(n, 8))).repeat(64, axis=1).astype(np.float32)
+        x[rng.random((n, 512)) < 0.02] = 0.0
+        x[0, 64:128] = 0.0
+    return synth.f32_to_bf16_bits(x)
+
+
+def test_layout_rope_tail_and_pad_byte():
+    rows = _random_rows(1, 17)
+    out = oracle.swa_fp8_pack(rows)
+    assert out.shape == (17, 584)
+    # channels 448..511 are kept as their bf16 bits, little-endian
+    assert np.array_equal(out[:, 448:576].view(np.uint16), rows[:, 448:512])
+    assert np.all(out[:, 583] == 0)
+    for r in range(17):
+        x = synth.bf16_bits_to_f32(rows[r]).astype(np.float64)
+        for g in range(7):
+            assert out[r, 576 + g] == oracle.e8m0_scale_code_e4m3(np.max(np.abs(x[64 * g:64 * g + 64])))
+
+
+def test_element_codes_match_torch_float8_e4m3fn():
+    rows = _random_rows(2, 33)
+    out = oracle.swa_fp8_pack(rows)
+    x = synth.bf16_bits_to_f32(rows).astype(np.float64)
+    checked = 0
+    for g in range(7):
+        X = 2.0 ** (out[:, 576 + g].astype(np.float64) - 127)
+        y = x[:, 64 * g:64 * g + 64] / X[:, None]  # exact: X is a power of two
+        codes = out[:, 64 * g:64 * g + 64]
+        inside = np.abs(y) <= 448.0
+        ref = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        ref = np.where(ref == 0x80, 0, ref)  # the format stores no negative zero
+        assert np.array_equal(codes[inside], ref[inside])
+        # above the grid: the magnitude saturates to 448 with the value's sign
+        sat = ~inside
+        assert np.all((codes[sat] & 0x7F) == 0x7E)
+        assert np.all((codes[sat] >> 7) == (y[sat] < 0))
+        checked += inside.sum()
+    assert checked > 33 * 448 * 0.8
+
+
+def test_saturated_values_exist_and_error_bound():
+    rows = _random_rows(3, 64)
+    out = oracle.swa_fp8_pack(rows)
+    deq = oracle.dequant_swa_fp8(out)
+    x = synth.bf16_bits_to_f32(rows).astype(np.float64)
+    X = np.repeat(2.0 ** (out[:, 576:583].astype(np.float64) - 127), 64, axis=1)
+    err = np.abs(deq[:, :448] - x[:, :448])
+    ax = np.abs(x[:, :448])
+    inside = ax <= 448.0 * X
+    # nearest rounding: half a spacing (3 mantissa bits; subnormal spacing 2^-9 X)
+    assert np.all(err[inside] <= np.maximum(ax[inside] * 2.0 ** -4, X[inside] * 2.0 ** -10))
+    # saturation: the group maximum can sit up to 512 X and is clipped to 448 X
+    assert np.any(~inside)
+    assert np.allclose(np.abs(deq[:, :448][~inside]), 448.0 * X[~inside], rtol=0, atol=0)
+    assert np.all(err[~inside] < 64.0 * X[~inside])
+    # the RoPE channels are carried exactly
+    assert np.array_equal(deq[:, 448:], x[:, 448:])
+
+
+def test_representable_rows_round_trip_exactly():
+    rng = np.random.default_rng(4)
+    n = 24
+    codes = rng.integers(0, 0x7F, size=(n, 448)).astype(np.uint8)
+    signs = rng.random((n, 448)) < 0.5
+    s = rng.integers(-20, 10, size=(n, 7))
+    for g in range(7):  # one element per group on the top binade (256..448) fixes the scale
+        codes[:, 64 * g + rng.integers(64)] = rng.integers(0x78, 0x7F, size=n)
+    vals = E4M3[codes] * np.repeat(2.0 ** s, 64, axis=1)
+    vals = np.where(signs, -vals, vals)
+    tail = rng.standard_normal((n, 64)).astype(np.float32)
+    x = np.concatenate([vals.astype(np.float32), tail], axis=1)
+    bits = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(synth.bf16_bits_to_f32(bits)[:, :448], vals)  # 4 significant bits fit bf16
+    out = oracle.swa_fp8_pack(bits)
+    assert np.array_equal(out[:, 576:583], s + 127)
+    want = np.where(signs & (codes != 0), codes | 0x80, codes)
+    assert np.array_equal(out[:, :448], want)
+    assert np.array_equal(oracle.dequant_swa_fp8(out)[:, :448], vals)
+
+
+def test_negative_zero_and_all_zero_group():
+    x = np.zeros((1, 512), np.float32)
+    x[0, :64] = -0.0
+    x[0, 64] = -1.0
+    out = oracle.swa_fp8_pack(synth.f32_to_bf16_bits(x))
+    assert np.all(out[0, :64] == 0) and out[0, 576] == 0
+    assert out[0, 64] == 0x80 | 0x78 and out[0, 577] == 127 - 8  # -1 = -256 * 2^-8
+    assert np.array_equal(oracle.dequant_swa_fp8(out)[0], synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x))[0])
+
+
+def _attn_inputs(seed, n_q, n_entries=96, window_rows=256):
+    kv, _ = synth.random_caches(seed, n_entries)
+    d = synth.query_inputs(seed + 1, n_q, swa_rows=window_rows)
+    rng = np.random.default_rng(seed)
+    topk = np.full((n_q, 512), -1, np.int32)
+    for t in range(n_q):
+        k = int(rng.integers(0, 90))
+        topk[t, :k] = rng.choice(n_entries, k, replace=False)
+    return kv, d, topk
+
+
+def test_fp8_window_attention_equals_bf16_window_of_dequantised_rows():
+    n_q = 3
+    kv, d, topk = _attn_inputs(41, n_q)
+    swa8 = oracle.swa_fp8_pack(d.swa)
+    deq = oracle.dequant_swa_fp8(swa8)
+    deq_bits = synth.f32_to_bf16_bits(deq.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f32(deq_bits), deq)  # dequantised rows are bf16 values
+    start = np.array([0, 57, 128], np.int64)
+    length = np.array([128, 100, 0], np.int32)
+    o8, l8 = oracle.sparse_attn_swa_fp8(d.q, kv, np.zeros(n_q, np.int64), topk, swa8, start, length)
+    ob, lb = oracle.sparse_attn(d.q, kv, np.zeros(n_q, np.int64), topk, deq_bits, start, length)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+    # and FP8 storage moves the output away from the bf16-window output only a little
+    o16, _ = oracle.sparse_attn(d.q, kv, np.zeros(n_q, np.int64), topk, d.swa, start, length)
+    assert np.max(np.abs(o8 - o16)) < 0.1 * np.max(np.abs(o16))
+
+
+def test_ring_window_equals_rolled_buffer():
+    n_q, ring = 2, 160
+    kv, d, topk = _attn_inputs(43, n_q, window_rows=ring)
+    swa8 = oracle.swa_fp8_pack(d.swa)
+    start = np.array([100, 1000], np.int64)  # 100..227 wraps at 160; 1000 mod 160 = 40
+    length = np.array([128, 90], np.int32)
+    o, l = oracle.sparse_attn_swa_fp8(d.q, kv, np.zeros(n_q, np.int64), topk, swa8, start, length, swa_ring=ring)
+    for t in range(n_q):
+        rows = (start[t] + np.arange(128)) % ring
+        flat = np.ascontiguousarray(swa8[rows])
+        o1, l1 = oracle.sparse_attn_swa_fp8(d.q[t:t + 1], kv, [0], topk[t:t + 1], flat, [0], length[t:t + 1])
+        assert np.array_equal(o[t], o1[0]) and np.array_equal(l[t], l1[0])
