@@ -34,13 +34,17 @@ _L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32,
 _L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32]
 _L.csa2_sparse_attn_workspace.restype = _sz
 _L.csa2_sparse_attn.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp, _sz, _vp]
+_L.csa2_swa_pack_fp8.argtypes = [_vp, _i64, _vp, _vp, _vp]
+_L.csa2_sparse_attn_swa_fp8.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
+                                        _sz, _vp]
 
 SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_compress_pack",
            "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
-           "csa2_sparse_attn_workspace", "csa2_sparse_attn")
+           "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DEFAULT_SCALE = 512 ** -0.5
+SWA_FP8_ROW_BYTES = 584
 ROPE_THETA = 160000.0
 
 
@@ -197,4 +201,50 @@ def sparse_attn(q, kv_cache, q_base, topk, swa, swa_start, swa_len, scale: float
     _check("csa2_sparse_attn", _L.csa2_sparse_attn(
         _ptr(q), _ptr(kv_cache), _ptr(q_base), _ptr(topk), K, _ptr(swa), _ptr(swa_start), _ptr(swa_len),
         float(scale), _ptr(out), _ptr(lse), n_q, _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def swa_pack_fp8(rows, out=None, dst_rows=None, stream=None):
+    """bf16 window rows [n, 512] -> FP8 window rows uint8 [n, 584] (or into `out` at dst_rows)."""
+    _dev(rows, torch.bfloat16, "rows", 2)
+    _dev(dst_rows, torch.int64, "dst_rows", 1)
+    n = rows.shape[0]
+    if out is None:
+        out = torch.empty((n, SWA_FP8_ROW_BYTES), dtype=torch.uint8, device=rows.device)
+    _dev(out, torch.uint8, "out")
+    if dst_rows is None and out.numel() < n * SWA_FP8_ROW_BYTES:
+        raise ValueError("out too small")
+    if dst_rows is not None and dst_rows.numel() != n:
+        raise ValueError("dst_rows must hold one row index per input row")
+    _check("csa2_swa_pack_fp8", _L.csa2_swa_pack_fp8(_ptr(rows), n, _ptr(dst_rows), _ptr(out), _stream(stream)))
+    return out
+
+
+def sparse_attn_swa_fp8(q, kv_cache, q_base, topk, swa8, swa_start, swa_len, swa_ring: int = 0,
+                        scale: float = DEFAULT_SCALE, out=None, lse=None, want_lse: bool = True,
+                        workspace=None, stream=None):
+    """sparse_attn with the window read from FP8 window rows (optionally per-sequence rings)."""
+    _dev(q, torch.bfloat16, "q", 3)
+    _dev(kv_cache, torch.uint8, "kv_cache")
+    _dev(q_base, torch.int64, "q_base", 1)
+    _dev(topk, torch.int32, "topk", 2)
+    _dev(swa8, torch.uint8, "swa8")
+    _dev(swa_start, torch.int64, "swa_start", 1)
+    _dev(swa_len, torch.int32, "swa_len", 1)
+    n_q = q.shape[0]
+    K = topk.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_q, 64, 512), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
+    _dev(out, torch.float32, "out")
+    _dev(lse, torch.float32, "lse")
+    need = sparse_attn_workspace(n_q, K)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_sparse_attn_swa_fp8", _L.csa2_sparse_attn_swa_fp8(
+        _ptr(q), _ptr(kv_cache), _ptr(q_base), _ptr(topk), K, _ptr(swa8), int(swa_ring), _ptr(swa_start),
+        _ptr(swa_len), float(scale), _ptr(out), _ptr(lse), n_q, _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse

@@ -19,18 +19,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWChunk = 64;  // channels of W_idx staged per step
 
-// Nearest-even E4M3 code of x >= 0, saturating at 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  if (!(x < 448.0f)) return 0x7E;
-  if (x < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (code 8 is 2^-6)
-    return (uint32_t)__builtin_rintf(x * 512.0f);
-  }
-  const int E = (int)((__float_as_uint(x) >> 23) & 255) - 127;  // x is a normal fp32
-  const float r = __builtin_rintf(__builtin_ldexpf(x, 3 - E));   // [8, 16], ties to even
-  const uint32_t code = ((uint32_t)(E + 7) << 3) + ((uint32_t)r - 8u);
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
 // E2M1 code of e on the grid {0,.5,1,1.5,2,3,4,6} * S by exact midpoint comparisons,
 // ties to the even code, saturating at 6; the sign bit only on a non-zero code.
 __device__ __forceinline__ uint32_t e2m1_encode(float e, float S) {

@@ -17,6 +17,7 @@ constexpr int kIdxHeads = 32; // indexer heads
 constexpr int kIdxDim = 128;  // indexer head dim
 constexpr int kKvBytes = 288;
 constexpr int kIdxBytes = 68;
+constexpr int kSwa8Bytes = 584;  // FP8 window row: 448 E4M3 codes, 64 bf16, 7 scale bytes, 1 pad
 constexpr int kBlock = 8;     // candidate block size
 constexpr int kMaxPool = 2048;
 constexpr int kMaxTopK = 512;
@@ -43,6 +44,19 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   const uint32_t e = (b >> 3) & 15, m = b & 7;
   float v = e == 0 ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf((float)(8 + m), (int)e - 10);
   return (b & 0x80) ? -v : v;
+}
+
+// Nearest-even E4M3 code of x >= 0, saturating at 448 (0x7E); NaN and +inf also give 0x7E.
+// One rounding step (rint after an exact power-of-two scaling), so the code is exact.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  if (!(x < 448.0f)) return 0x7E;
+  if (x < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (code 8 is 2^-6)
+    return (uint32_t)__builtin_rintf(x * 512.0f);
+  }
+  const int E = (int)((__float_as_uint(x) >> 23) & 255) - 127;  // x is a normal fp32
+  const float r = __builtin_rintf(__builtin_ldexpf(x, 3 - E));   // [8, 16], ties to even
+  const uint32_t code = ((uint32_t)(E + 7) << 3) + ((uint32_t)r - 8u);
+  return code > 0x7Eu ? 0x7Eu : code;
 }
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); NaN ranks as -inf.

@@ -16,6 +16,13 @@
 // v_mfma_f32_16x16x32_f16 with fp32 accumulation; the softmax is online across chunks in
 // fp32.  For small batches the key chunks of a query are split across workgroups and a
 // merge kernel combines the partial (o, m, l) exactly like flash-decoding.
+//
+// The window rows come either as bf16 rows or as 584-byte FP8 window rows (the window KV
+// kept in FP8, [ZB] §2.4.4; DeepSeek-V4's FP8 KV entry, [ZB] §3.1 and [DF] §4.6), read
+// consecutively or from per-sequence ring buffers.  An FP8 row decodes exactly into f16
+// (an E4M3 value times a power-of-two scale has 4 significant bits) as long as the
+// products stay in f16's range (groups with amax >= 2^-10 or so; smaller groups lose their
+// smallest values to f16 underflow).
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -29,6 +36,7 @@ constexpr int kPStride = kChunk + 8;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));  // 16 B at an 8-B boundary
 
 struct __attribute__((aligned(16))) AttnShared {
   _Float16 k[kChunk * kKStride] __attribute__((aligned(16)));  // decoded keys, row-major [key][dim]
@@ -45,10 +53,12 @@ struct KeyRaw {
   int row;        // window row index (kind 2)
 };
 
+// Window rows: kFp8Win selects 584-byte FP8 rows instead of bf16 rows.
+template <bool kFp8Win>
 __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_cache,
     const int64_t* __restrict__ q_base, const int32_t* __restrict__ topk, int32_t K,
-    const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_start,
+    const void* __restrict__ swa_v, int64_t swa_ring, const int64_t* __restrict__ swa_start,
     const int32_t* __restrict__ swa_len, float scale, int32_t n_chunks, int32_t chunks_per_split,
     int32_t n_splits, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
@@ -61,7 +71,13 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   const int c_end = min(c_begin + chunks_per_split, n_chunks);
   const int64_t base = q_base[t];
   const int32_t nswa = min(max(swa_len[t], 0), kMaxSwa);
-  const int64_t swa0 = swa_start[t];
+  // window row r lives at wseg + (woff + r) wrapped into the ring (no ring: wseg + woff + r)
+  int64_t woff = swa_start[t], wseg = 0;
+  if (swa_ring > 0) {
+    woff %= swa_ring;
+    if (woff < 0) woff += swa_ring;
+    wseg = swa_start[t] - woff;
+  }
   const int kk = tid >> 2, qq = tid & 3;  // key slot and quarter this thread decodes
 
   // raw loads of this thread's key quarter for chunk c
@@ -107,18 +123,58 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
         }
       }
     } else if (r.kind == 2) {
-      const uint4* src = reinterpret_cast<const uint4*>(swa + (swa0 + r.row) * kD + 128 * qq);
+      int64_t row = woff + r.row;
+      if (swa_ring > 0 && row >= swa_ring) row -= swa_ring;  // r.row < 128 <= swa_ring
+      row += wseg;
+      if constexpr (kFp8Win) {
+        // this thread decodes NoPE dims 112 qq .. 112 qq + 111 (codes at the same byte
+        // offsets) and RoPE dims 448 + 16 qq .. + 15 (bf16 at bytes 448 + 32 qq)
+        const uint8_t* src = static_cast<const uint8_t*>(swa_v) + row * kSwa8Bytes;
+        const uint64_t scb = *reinterpret_cast<const uint64_t*>(src + kDNope + 2 * kDRope);
+        _Float16* kq = sh.k + kk * kKStride;
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const uint4 u = src[v];
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-        f16x8 pk;
+        for (int j = 0; j < 7; j++) {
+          const u32x4_a8 c = *reinterpret_cast<const u32x4_a8*>(src + 112 * qq + 16 * j);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
-          pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
+          for (int h = 0; h < 2; h++) {
+            const int grp = (112 * qq + 16 * j + 8 * h) >> 6;  // scale group of these 8 dims
+            const uint32_t code = (uint32_t)(scb >> (8 * grp)) & 255u;
+            const _Float16 X = (_Float16)__builtin_ldexpf(1.0f, (int)code - 127);
+            const f16x2 X2 = {X, X};
+            const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, false) * X2;
+            const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, true) * X2;
+            const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, false) * X2;
+            const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, true) * X2;
+            const f16x8 pk = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+            *reinterpret_cast<f16x8*>(kq + 112 * qq + 16 * j + 8 * h) = pk;
+          }
         }
-        *reinterpret_cast<f16x8*>(krow + 8 * v) = pk;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+          const u32x4_a8 u = *reinterpret_cast<const u32x4_a8*>(src + kDNope + 32 * qq + 16 * j);
+          f16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            pk[2 * e] = (_Float16)bf16_bits_to_f32(u[e] & 0xFFFFu);
+            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(u[e] >> 16);
+          }
+          *reinterpret_cast<f16x8*>(kq + kDNope + 16 * qq + 8 * j) = pk;
+        }
+      } else {
+        const uint4* src =
+            reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(swa_v) + row * kD + 128 * qq);
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const uint4 u = src[v];
+          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+          f16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
+            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
+          }
+          *reinterpret_cast<f16x8*>(krow + 8 * v) = pk;
+        }
       }
     } else {
       f16x8 z;
@@ -362,30 +418,33 @@ extern "C" size_t csa2_sparse_attn_workspace(int32_t n_q, int32_t K) {
   return (size_t)n_q * p.n_splits * kHeads * (kD + 2) * sizeof(float);
 }
 
-extern "C" int csa2_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache,
-                                const int64_t* q_base, const int32_t* topk, int32_t K,
-                                const uint16_t* swa_bf16, const int64_t* swa_start,
-                                const int32_t* swa_len, float scale, float* out, float* lse,
-                                int32_t n_q, void* workspace, size_t ws_bytes, void* stream) {
-  using namespace csa2;
-  if (n_q < 0 || K < 0) return CSA2_ERR_INVALID_ARG;
+namespace csa2 {
+namespace {
+
+template <bool kFp8Win>
+int launch_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache, const int64_t* q_base,
+                       const int32_t* topk, int32_t K, const void* swa, int64_t swa_ring,
+                       const int64_t* swa_start, const int32_t* swa_len, float scale, float* out,
+                       float* lse, int32_t n_q, void* workspace, size_t ws_bytes, void* stream) {
+  if (n_q < 0 || K < 0 || swa_ring < 0) return CSA2_ERR_INVALID_ARG;
+  if (swa_ring > 0 && swa_ring < kMaxSwa) return CSA2_ERR_INVALID_ARG;  // a ring holds the window
   if (K > kMaxTopK) return CSA2_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
-  if (!q_bf16 || !kv_cache || !q_base || !swa_bf16 || !swa_start || !swa_len || !out)
+  if (!q_bf16 || !kv_cache || !q_base || !swa || !swa_start || !swa_len || !out)
     return CSA2_ERR_INVALID_ARG;
   if (K > 0 && !topk) return CSA2_ERR_INVALID_ARG;
   if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(q_bf16) | reinterpret_cast<uintptr_t>(kv_cache) |
-       reinterpret_cast<uintptr_t>(swa_bf16) | reinterpret_cast<uintptr_t>(out) |
-       reinterpret_cast<uintptr_t>(workspace)) & 15)
+       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(workspace)) & 15)
     return CSA2_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(swa) & (kFp8Win ? 7 : 15)) return CSA2_ERR_INVALID_ARG;
   const Plan p = make_plan(n_q, K);
   const size_t need = csa2_sparse_attn_workspace(n_q, K);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   float* ws_o = (float*)workspace;
   float* ws_ml = need > 0 ? ws_o + (size_t)n_q * p.n_splits * kHeads * kD : nullptr;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3(p.n_splits, n_q), dim3(kThreads), 0,
-                     (hipStream_t)stream, q_bf16, kv_cache, q_base, topk, K, swa_bf16, swa_start,
+  hipLaunchKernelGGL(sparse_attn_kernel<kFp8Win>, dim3(p.n_splits, n_q), dim3(kThreads), 0,
+                     (hipStream_t)stream, q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start,
                      swa_len, scale, p.n_chunks, p.chunks_per_split, p.n_splits, out, lse, ws_o,
                      ws_ml);
   int st = check_launch();
@@ -393,4 +452,26 @@ extern "C" int csa2_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache,
   hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3(kHeads, n_q), dim3(128), 0, (hipStream_t)stream,
                      ws_o, ws_ml, p.n_splits, out, lse);
   return check_launch();
+}
+
+}  // namespace
+}  // namespace csa2
+
+extern "C" int csa2_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache,
+                                const int64_t* q_base, const int32_t* topk, int32_t K,
+                                const uint16_t* swa_bf16, const int64_t* swa_start,
+                                const int32_t* swa_len, float scale, float* out, float* lse,
+                                int32_t n_q, void* workspace, size_t ws_bytes, void* stream) {
+  return csa2::launch_sparse_attn<false>(q_bf16, kv_cache, q_base, topk, K, swa_bf16, 0, swa_start,
+                                         swa_len, scale, out, lse, n_q, workspace, ws_bytes, stream);
+}
+
+extern "C" int csa2_sparse_attn_swa_fp8(const uint16_t* q_bf16, const uint8_t* kv_cache,
+                                        const int64_t* q_base, const int32_t* topk, int32_t K,
+                                        const uint8_t* swa8, int64_t swa_ring,
+                                        const int64_t* swa_start, const int32_t* swa_len, float scale,
+                                        float* out, float* lse, int32_t n_q, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+  return csa2::launch_sparse_attn<true>(q_bf16, kv_cache, q_base, topk, K, swa8, swa_ring, swa_start,
+                                        swa_len, scale, out, lse, n_q, workspace, ws_bytes, stream);
 }

@@ -28,6 +28,15 @@
  *   indexer K (68 B): bytes 0..63 hold 128 E2M1 codes in the same nibble order, bytes
  *            64..67 one E8M0 scale per 32 channels (MXFP4).  The cache base must be
  *            16-byte aligned; rows are then 4-byte aligned.
+ *   FP8 window row (584 B; the window KV kept in FP8, [ZB] §2.4.4, in DeepSeek-V4's FP8
+ *            KV entry layout, [ZB] §3.1 and [DF] §4.6 equation 448 x 1 + 64 x 2 + 8):
+ *            bytes 0..447 OCP E4M3 codes of channels 0..447; bytes 448..575 the bf16 bits
+ *            of channels 448..511 (little-endian); bytes 576..582 one E8M0 scale per 64
+ *            channels, X = 2^(floor(log2 amax) - 8) clamped to codes [0, 254] (the OCP MX
+ *            rule with E4M3's largest exponent; 254 for a group holding an infinity);
+ *            byte 583 zero.  Codes are nearest-even E4M3 of x / X saturating at 448
+ *            (magnitudes in (448 X, 512 X) clip), the sign only on non-zero codes.  The
+ *            buffer base must be 8-byte aligned (584 = 8 x 73).
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -166,6 +175,36 @@ int csa2_sparse_attn(const uint16_t *q_bf16, const uint8_t *kv_cache, const int6
                      const int32_t *topk, int32_t K, const uint16_t *swa_bf16,
                      const int64_t *swa_start, const int32_t *swa_len, float scale, float *out,
                      float *lse, int32_t n_q, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * csa2_swa_pack_fp8 -- packs bf16 window rows into FP8 window rows (format above).
+ *   [ZB] §2.4.4: the sliding-window KV stays FP8 while the compressed entries go FP4.
+ *   rows_bf16 [n, 512] (16-byte aligned); dst_rows: NULL (row r goes to out row r) or
+ *   int64 [n], the out row of row r (negative: row r is skipped), so a decode step can
+ *   append its new tokens at their ring slots; out: FP8 rows, 8-byte aligned, large
+ *   enough for every destination row.  Bit-exact: the codes do not depend on rounding
+ *   order.  Errors: INVALID_ARG (null pointer, n < 0, misalignment).
+ */
+int csa2_swa_pack_fp8(const uint16_t *rows_bf16, int64_t n, const int64_t *dst_rows, uint8_t *out,
+                      void *stream);
+
+/*
+ * csa2_sparse_attn_swa_fp8 -- csa2_sparse_attn with the window read from FP8 window rows.
+ *   Same computation and arguments as csa2_sparse_attn, the window rows being the
+ *   dequantised FP8 rows (value = E4M3 code x 2^(scale code - 127); RoPE channels as
+ *   stored).  swa8: FP8 window rows (8-byte aligned).  swa_ring: 0 = window row r of query
+ *   t is swa_start[t] + r; R >= 128 = the buffer is a sequence of rings of R rows (one per
+ *   sequence) and the window wraps inside the ring that holds swa_start[t]:
+ *     row = s + (swa_start[t] - s + r) mod R,  s = swa_start[t] - swa_start[t] mod R.
+ *   Decoding is exact in f16 for window values of magnitude 2^-14 .. 65504 (groups whose
+ *   smallest codes fall below f16's range lose them to underflow).
+ *   Errors: INVALID_ARG (also 0 < swa_ring < 128), UNSUPPORTED (K > 512), WORKSPACE.
+ */
+int csa2_sparse_attn_swa_fp8(const uint16_t *q_bf16, const uint8_t *kv_cache, const int64_t *q_base,
+                             const int32_t *topk, int32_t K, const uint8_t *swa8, int64_t swa_ring,
+                             const int64_t *swa_start, const int32_t *swa_len, float scale,
+                             float *out, float *lse, int32_t n_q, void *workspace, size_t ws_bytes,
+                             void *stream);
 
 #ifdef __cplusplus
 }

@@ -387,6 +387,7 @@ int64_t csa2o_swa_fp8_row_bytes(void) { return D_NOPE + 2 * D_ROPE + 8; }
 
 int csa2o_e8m0_scale_code_e4m3(float amax) {
   if (!(amax > 0.0f)) return 0;
+  if (isinf(amax)) return 254; /* a group holding an infinity takes the largest finite scale */
   int ex;
   frexpf(amax, &ex); /* floor(log2 amax) = ex - 1 */
   int code = (ex - 1) - 8 + 127;
@@ -440,8 +441,15 @@ typedef struct {
   int64_t ring;
 } window_src;
 
-static void window_row(const window_src *w, int64_t row, double *out) {
-  if (w->ring > 0) row %= w->ring;
+/* Window row r of a window that starts at row `start`.  Without a ring the rows are
+ * consecutive.  With a ring of R rows the buffer is a sequence of rings (one per
+ * sequence); the window stays inside the ring holding `start` and wraps at its end. */
+static void window_row(const window_src *w, int64_t start, int32_t r, double *out) {
+  int64_t row = start + r;
+  if (w->ring > 0) {
+    const int64_t seg = start - start % w->ring;
+    row = seg + (start - seg + r) % w->ring;
+  }
   if (w->swa8 != NULL) {
     csa2o_dequant_swa_fp8(w->swa8 + row * csa2o_swa_fp8_row_bytes(), out);
   } else {
@@ -469,7 +477,7 @@ static void sparse_attn_core(const uint16_t *q, const uint8_t *kv_cache, const i
     }
     int32_t nw = swa_len[t] < 128 ? swa_len[t] : 128;
     for (int32_t r = 0; r < nw; r++) {
-      window_row(win, swa_start[t] + r, keys + (int64_t)nk * D_LAT);
+      window_row(win, swa_start[t], r, keys + (int64_t)nk * D_LAT);
       nk++;
     }
     for (int h = 0; h < N_HEADS; h++) {

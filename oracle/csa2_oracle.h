@@ -102,8 +102,10 @@ int64_t csa2o_swa_fp8_row_bytes(void);
 int csa2o_e8m0_scale_code_e4m3(float amax);
 void csa2o_swa_fp8_pack(const uint16_t *rows_bf16, int64_t n, uint8_t *out);
 void csa2o_dequant_swa_fp8(const uint8_t *row, double *out512);
-/* stage 4 with an FP8 window cache: window row r of query t is swa_start[t] + r, taken
- * modulo swa_ring when swa_ring > 0 (a ring buffer of swa_ring rows). */
+/* stage 4 with an FP8 window cache: window row r of query t is swa_start[t] + r when
+ * swa_ring == 0; when swa_ring = R > 0 the buffer is a sequence of rings of R rows (one per
+ * sequence) and the window wraps inside the ring that holds row swa_start[t]:
+ * row = s + (swa_start[t] - s + r) mod R with s = swa_start[t] - swa_start[t] mod R. */
 void csa2o_sparse_attn_swa_fp8(const uint16_t *q, const uint8_t *kv_cache, const int64_t *q_base,
                                const int32_t *topk, int32_t K, const uint8_t *swa8, int64_t swa_ring,
                                const int64_t *swa_start, const int32_t *swa_len, float scale,

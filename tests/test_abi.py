@@ -66,3 +66,21 @@ def test_host_validation_rejects_before_launch(lib):
                                 None, 0, None) == -2
     assert lib.csa2_sparse_attn(fake, fake, fake, fake, 512, fake, fake, fake, 0.04, fake, None, 1,
                                 None, 0, None) == -3
+
+
+def test_fp8_window_entry_points_validate_before_launch(lib):
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.csa2_swa_pack_fp8.argtypes = [vp, i64, vp, vp, vp]
+    lib.csa2_sparse_attn_swa_fp8.argtypes = [vp, vp, vp, vp, i32, vp, i64, vp, vp, f32, vp, vp, i32, vp, sz, vp]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.csa2_swa_pack_fp8(fake, -1, None, fake, None) == -1
+    assert lib.csa2_swa_pack_fp8(fake, 0, None, None, None) == 0
+    assert lib.csa2_swa_pack_fp8(ctypes.c_void_p((1 << 20) + 8), 4, None, fake, None) == -1  # rows not 16-B aligned
+    assert lib.csa2_swa_pack_fp8(fake, 4, None, ctypes.c_void_p((1 << 20) + 4), None) == -1  # out not 8-B aligned
+    attn = lib.csa2_sparse_attn_swa_fp8
+    assert attn(fake, fake, fake, fake, 600, fake, 0, fake, fake, 0.04, fake, None, 1, None, 0, None) == -2
+    assert attn(fake, fake, fake, fake, 512, fake, 64, fake, fake, 0.04, fake, None, 1, None, 0, None) == -1
+    assert attn(fake, fake, fake, fake, 512, fake, -1, fake, fake, 0.04, fake, None, 1, None, 0, None) == -1
+    assert attn(fake, fake, fake, fake, 512, ctypes.c_void_p((1 << 20) + 4), 0, fake, fake, 0.04, fake, None, 1,
+                None, 0, None) == -1
+    assert attn(fake, fake, fake, fake, 512, fake, 128, fake, fake, 0.04, fake, None, 1, None, 0, None) == -3

@@ -48,6 +48,7 @@ def test_scale_code_is_floor_log2_minus_8(amax):
 def test_scale_code_of_zero_and_nan():
     assert oracle.e8m0_scale_code_e4m3(0.0) == 0
     assert oracle.e8m0_scale_code_e4m3(float("nan")) == 0
+    assert oracle.e8m0_scale_code_e4m3(float("inf")) == 254  # the largest finite E8M0 scale
 
 
 def _random_rows(seed, n, spread=True):
@@ -173,14 +174,22 @@ def test_fp8_window_attention_equals_bf16_window_of_dequantised_rows():
 
 
 def test_ring_window_equals_rolled_buffer():
+    # two rings of 160 rows (one per sequence); query 0 starts in ring 0 and wraps at row
+    # 160 back to row 0, query 1 starts at row 310 of ring 1 and wraps to row 160
     n_q, ring = 2, 160
-    kv, d, topk = _attn_inputs(43, n_q, window_rows=ring)
+    kv, d, topk = _attn_inputs(43, n_q, window_rows=2 * ring)
     swa8 = oracle.swa_fp8_pack(d.swa)
-    start = np.array([100, 1000], np.int64)  # 100..227 wraps at 160; 1000 mod 160 = 40
+    start = np.array([100, 310], np.int64)
     length = np.array([128, 90], np.int32)
     o, l = oracle.sparse_attn_swa_fp8(d.q, kv, np.zeros(n_q, np.int64), topk, swa8, start, length, swa_ring=ring)
     for t in range(n_q):
-        rows = (start[t] + np.arange(128)) % ring
+        seg = (start[t] // ring) * ring
+        rows = seg + (start[t] - seg + np.arange(128)) % ring
         flat = np.ascontiguousarray(swa8[rows])
         o1, l1 = oracle.sparse_attn_swa_fp8(d.q[t:t + 1], kv, [0], topk[t:t + 1], flat, [0], length[t:t + 1])
         assert np.array_equal(o[t], o1[0]) and np.array_equal(l[t], l1[0])
+    # a window that does not reach the ring's end reads the same rows as without a ring
+    o2, l2 = oracle.sparse_attn_swa_fp8(d.q, kv, np.zeros(n_q, np.int64), topk, swa8, [0, 165], length,
+                                         swa_ring=ring)
+    o3, l3 = oracle.sparse_attn_swa_fp8(d.q, kv, np.zeros(n_q, np.int64), topk, swa8, [0, 165], length)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
