@@ -126,8 +126,10 @@ class Decode1M:
     select, attend), optionally followed by a Reindex layer (re-score the pool, select inside
     it, attend) and Reuse layers (attend with the Reindex indices)."""
 
-    def __init__(self, torch, csa2, tokens, n_seq=4, m=2, K=512, M=2048, ncopy=NCOPY, extra_layers=0):
+    def __init__(self, torch, csa2, tokens, n_seq=4, m=2, K=512, M=2048, ncopy=NCOPY, extra_layers=0,
+                 fp8_window=False):
         self.torch, self.csa2 = torch, csa2
+        self.fp8 = fp8_window
         self.n_seq, self.m, self.tokens, self.K, self.M, self.ncopy = n_seq, m, tokens, K, M, ncopy
         self.extra = extra_layers
         n = self.n = tokens // m
@@ -156,6 +158,20 @@ class Decode1M:
             self.scores_r = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
             self.topk_r = torch.empty((n_seq, K), dtype=torch.int32, device=dev)
         self.n_stages = 4 + (2 + extra_layers if extra_layers else 0)
+        if fp8_window:
+            # per-sequence FP8 window rings of 128 rows; each step packs the newest token's
+            # row into its slot, then attends over the ring (oldest row first)
+            slot = torch.arange(n_seq, dtype=torch.int64, device=dev) * 128 + (tokens - 1) % 128
+            self.ring_slot = slot.contiguous()
+            self.ring_start = (torch.arange(n_seq, dtype=torch.int64, device=dev) * 128 + tokens % 128).contiguous()
+            for ci, c in enumerate(self.copies):
+                c["swa8"] = csa2.swa_pack_fp8(c["swa"])
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(2000 + ci)
+                x = torch.randn((n_seq, 512), generator=gen, device=dev)
+                c["new_row"] = (x / torch.sqrt(torch.mean(x * x, dim=1, keepdim=True) + 1e-6)).to(
+                    torch.bfloat16).contiguous()
+            torch.cuda.synchronize()
 
     def run_stage(self, ci, st):
         """One stage of the step for batch copy ci, on torch's current stream."""
@@ -169,6 +185,10 @@ class Decode1M:
         elif st == 2:
             csa2.block_topk(self.scores, self.q_nvis, K=self.K, M=self.M, block_max=self.bmax, pool_out=self.pool,
                             topk_out=self.topk, workspace=self.ws_sel)
+        elif st == 3 and self.fp8:
+            csa2.swa_pack_fp8(c["new_row"], out=c["swa8"], dst_rows=self.ring_slot)
+            csa2.sparse_attn_swa_fp8(c["q"], c["kv"], self.q_base, self.topk, c["swa8"], self.ring_start,
+                                     self.swa_len, swa_ring=128, out=self.out, lse=self.lse, workspace=self.ws_att)
         elif st == 3:
             csa2.sparse_attn(c["q"], c["kv"], self.q_base, self.topk, c["swa"], self.swa_start, self.swa_len,
                              out=self.out, lse=self.lse, workspace=self.ws_att)
@@ -188,10 +208,10 @@ class Decode1M:
 STAGES = ("compress_newest", "index_score", "block_topk", "sparse_attn")
 
 
-def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3):
+def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3, fp8_window=False):
     """Whole-step throughput of a secondary decode workload: one HIP graph per batch copy
     holding every stage of the step, replayed `steps` times between two synchronisations."""
-    wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers)
+    wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers, fp8_window=fp8_window)
     for i in range(warmup):
         for st in range(wl.n_stages):
             wl.run_stage(i % NCOPY, st)
@@ -214,7 +234,8 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
     wall = time.perf_counter() - t0
     res = {"queries_per_s": round(n_seq * steps / wall, 1), "us_per_step": round(wall * 1e6 / steps, 2),
            "sequences": n_seq, "tokens_per_sequence": tokens, "compress_ratio": m, "entries_per_sequence": wl.n,
-           "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else "")}
+           "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else ""),
+           "window": "FP8 rings (append + attend)" if fp8_window else "bf16"}
     del graphs, wl
     torch.cuda.empty_cache()
     return res
@@ -413,6 +434,7 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] secondary workloads", file=sys.stderr, flush=True)
         sec = {
+            "decode_1m_b4_m2_fp8_window": time_decode(torch, csa2, 1 << 20, 4, 2, fp8_window=True),
             "decode_128k_b16_m1": time_decode(torch, csa2, 131072, 16, 1, extra_layers=4),
             "decode_32k_b4_m1": time_decode(torch, csa2, 32768, 4, 1),
             "tiny_4k_b1_m2": time_decode(torch, csa2, 4096, 1, 2),

@@ -16,6 +16,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # no packed-fp32 instructions in any device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (gfx950's unified register file) rather than AGPRs, so
+    # epilogues read accumulators without v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -34,13 +34,22 @@ typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 struct RawTile {
   u32x4_a4 lo, hi;
   uint32_t sc;
+  bool valid;
 };
+
+// max(a, b) as one v_med3_f32 (the median of a, b and FLT_MAX): a NaN operand is ignored
+// like fmaxf does, without the quieting instructions fmaxf costs on these operands; +inf
+// saturates to FLT_MAX (only infinite inputs make one)
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __FLT_MAX__); }
+
+// ReLU as one v_med3_f32: clamp(x, 0, FLT_MAX); a NaN gives 0, like a comparison x > 0
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, __FLT_MAX__); }
 
 // max over the 8 lanes of each aligned group of 8 (DPP within rows)
 __device__ __forceinline__ float max8_lanes(float v) {
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = max2(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = max2(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = max2(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
   return v;
 }
 
@@ -51,6 +60,10 @@ __device__ __forceinline__ float sum_halves(float v) {
 }
 
 }  // namespace idx
+
+// longest score row (entries) of csa2_index_score: byte offsets into a sequence's cache
+// (68 B per entry) stay below 2^31
+constexpr int32_t kMaxIndexWidth = 1 << 23;
 
 // batches of at least this many Full-mode queries take the many-query kernel
 constexpr int kMqMinQueries = 64;

@@ -18,6 +18,14 @@
 // finishes the sum.  HBM traffic per entry is its 68 bytes plus 4.5 bytes of output.  The
 // waves of the grid walk a query's tiles in grid-stride order, so the whole grid streams
 // one front of the row at a time.
+//
+// Streaming.  All cache reads and score writes go through buffer resources whose sizes
+// bound the row: loads past the end return zeros and stores past the end are dropped.
+// That keeps the tile loop free of branches, so the compiler's memory-counter waits
+// leave the younger tiles in flight, and lets duplicate lanes drop their stores by
+// aiming past the end.  Measured on the 1M-context batch-4 decode, the stores are the
+// costly part beyond the read stream (9.4 MB written against 143 MB read costs about
+// as much as the MFMA and VALU work).
 #include "index_common.hpp"
 
 namespace csa2 {
@@ -25,10 +33,14 @@ namespace {
 using namespace idx;
 
 #ifndef CSA2_INDEX_DEPTH
-#define CSA2_INDEX_DEPTH 4
+#define CSA2_INDEX_DEPTH 5
 #endif
 constexpr int kDepth = CSA2_INDEX_DEPTH;  // tiles in flight per wave
+constexpr int kRawBuf = 0x00020000;        // buffer descriptor word 3: raw 32-bit dwords
 
+// kPool: Reindex layers score their candidate pool (entry j of slot p is block
+// pool_blocks[p / 8] * 8 + p % 8); Full layers score entries 0 .. width-1 directly.
+template <bool kPool>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
@@ -58,41 +70,50 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     return;
   }
 
-  // query: head n, dims 64g .. 64g + 63 as eight bf16x8 A fragments
+  // the query (head n, dims 64g .. 64g + 63 as eight bf16x8 A fragments) and the head
+  // weight of each accumulator row this lane holds (row 8(r/4) + 4g + r%4); both are
+  // loaded after the first cache tiles, so the stream from HBM starts first
   bf16x8 a[8];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
-#pragma unroll
-    for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
-  }
-  // head weight of each accumulator row held by this lane: row = 8(r/4) + 4g + r%4
   float wr[16];
-#pragma unroll
-  for (int r = 0; r < 16; r++) wr[r] = head_w[(int64_t)t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)];
 
-  const uint8_t* last_row = idx_cache + (base + nvis - 1) * kIdxBytes;
-  // the cache row of this lane's entry in tile k; invalid slots read the last visible row
-  auto row_of = [&](int32_t k, bool& valid) -> const uint8_t* {
+  // Buffer resources bound the sequence's visible cache rows, the score row and the
+  // block-max row (empty when block_max is NULL): loads past the end return zeros and
+  // stores past the end are dropped,
+  // so the streaming loop below needs no branches (and the compiler's memory-counter
+  // waits stay exact).  Offsets are 32-bit: the host limits width to 2^23 entries.
+  const int32_t nv = min(nvis, kMaxIndexWidth);  // rows past 2^23 are never addressed
+  const __amdgpu_buffer_rsrc_t rs_cache =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(idx_cache + base * kIdxBytes), (short)0, nv * kIdxBytes, kRawBuf);
+  const __amdgpu_buffer_rsrc_t rs_score = __builtin_amdgcn_make_buffer_rsrc(srow, (short)0, width * 4, kRawBuf);
+  const __amdgpu_buffer_rsrc_t rs_bmax = __builtin_amdgcn_make_buffer_rsrc(
+      block_max != nullptr ? (void*)(block_max + (int64_t)t * nbw) : (void*)srow, (short)0,
+      block_max != nullptr ? nbw * 4 : 0, kRawBuf);
+  const __amdgpu_buffer_rsrc_t rs_pool = __builtin_amdgcn_make_buffer_rsrc(
+      kPool ? (void*)(pool_blocks + (int64_t)t * M) : (void*)srow, (short)0, kPool ? M * 4 : 0, kRawBuf);
+  constexpr int32_t kOut = 1 << 30;  // a byte offset past every buffer's end
+
+  // byte offset of this lane's cache row in tile k (past the end when the slot is empty)
+  auto row_off = [&](int32_t k, bool& valid) -> int32_t {
     const int32_t p = (first + k * tstride) * kTile + n;
-    int64_t j;
-    if (pool_blocks == nullptr) {
-      j = p;
-      valid = p < nvis;
+    int32_t j;
+    if constexpr (kPool) {
+      const int32_t b = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs_pool, 4 * (p >> 3), 0, 0);
+      const int64_t jj = (int64_t)b * kBlock + (p & 7);
+      valid = (p >> 3) < M && b >= 0 && jj < nv;
+      j = (int32_t)jj;
     } else {
-      const int32_t slot = p >> 3;
-      const int32_t b = slot < M ? pool_blocks[(int64_t)t * M + slot] : -1;
-      j = (int64_t)b * kBlock + (p & 7);
-      valid = b >= 0 && j < nvis;
+      j = p;
+      valid = p < nv;
     }
-    return valid ? idx_cache + (base + j) * kIdxBytes : last_row;
+    return valid ? j * kIdxBytes : kOut;
   };
-  auto load = [&](int32_t k, RawTile& r, bool& valid) {
-    const uint8_t* row = row_of(k, valid);
-    r.lo = *reinterpret_cast<const u32x4_a4*>(row + 32 * g);
-    r.hi = *reinterpret_cast<const u32x4_a4*>(row + 32 * g + 16);
-    r.sc = *reinterpret_cast<const uint32_t*>(row + 64);
+  auto load = [&](int32_t k, RawTile& r) {
+    const int32_t off = row_off(k, r.valid);
+    r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, off + 32 * g, 0, 0));
+    r.hi = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, off + 32 * g + 16, 0, 0));
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs_cache, off + 64, 0, 0);
   };
-  auto process = [&](const RawTile& cur, bool valid, int32_t k) {
+  auto process = [&](const RawTile& cur, int32_t k) {
     const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
     const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
     const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3], cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
@@ -106,37 +127,55 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     float part[4];
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      part[c] = wr[4 * c] * __builtin_fmaxf(acc[4 * c], 0.0f);
+      part[c] = wr[4 * c] * relu(acc[4 * c]);
 #pragma unroll
-      for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], __builtin_fmaxf(acc[4 * c + r], 0.0f), part[c]);
+      for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], relu(acc[4 * c + r]), part[c]);
     }
-    const float sc = valid ? sum_halves((part[0] + part[1]) + (part[2] + part[3])) : -__builtin_inff();
+    const float sc = cur.valid ? sum_halves((part[0] + part[1]) + (part[2] + part[3])) : -__builtin_inff();
+    // both lane halves hold the entry's score and all 8 lanes of a block its maximum; one
+    // lane writes each value and the others aim past the buffer's end, so their stores
+    // are dropped without a branch (as are slots past the row's end)
     const int32_t p = (first + k * tstride) * kTile + n;
-    if (g == 0 && p < width) srow[p] = sc;
-    if (block_max != nullptr) {
-      const float bm = max8_lanes(sc);
-      if (g == 0 && (n & 7) == 0 && p < width) block_max[(int64_t)t * nbw + (p >> 3)] = bm;
-    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, g ? kOut : 4 * p, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax,
+                                          (g | (n & 7)) ? kOut : 4 * (p >> 3), 0, 0);
   };
 
-  // software pipeline: kDepth tiles of this wave are in flight while one is processed
+  // software pipeline: kDepth - 1 tiles of this wave are in flight while one is processed.
+  // Full groups of kDepth tiles stream through the loop; loads past the wave's last tile
+  // return zeros and are never processed; the last partial group is finished after it.
+  // (the scheduling barriers keep the tiles' loads in tile order, so each tile's wait
+  // counts only older loads)
   RawTile pipe[kDepth];
-  bool pv[kDepth];
 #pragma unroll
-  for (int u = 0; u < kDepth; u++)
-    if (u < nt) load(u, pipe[u], pv[u]);
-  for (int32_t k0 = 0; k0 < nt; k0 += kDepth) {
+  for (int u = 0; u < kDepth; u++) {
+    load(u, pipe[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
 #pragma unroll
-    for (int u = 0; u < kDepth; u++) {
-      const int32_t k = k0 + u;
-      if (k < nt) {
-        const RawTile cur = pipe[u];
-        const bool cv = pv[u];
-        if (k + kDepth < nt) load(k + kDepth, pipe[u], pv[u]);
-        process(cur, cv, k);
-      }
+    for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
+    typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+    const f32x4_a4* wp = reinterpret_cast<const f32x4_a4*>(head_w + (int64_t)t * kIdxHeads);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const f32x4_a4 v = wp[2 * c + g];  // rows 8c + 4g .. 8c + 4g + 3
+#pragma unroll
+      for (int r = 0; r < 4; r++) wr[4 * c + r] = v[r];
     }
   }
+  int32_t k0 = 0;
+  for (; k0 + kDepth <= nt; k0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; u++) {
+      process(pipe[u], k0 + u);
+      load(k0 + u + kDepth, pipe[u]);  // reuses this tile's registers, so none are copied
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kDepth - 1; u++)
+    if (k0 + u < nt) process(pipe[u], k0 + u);
 }
 
 }  // namespace
@@ -151,7 +190,7 @@ int resident_workgroups() {
   if (cached[dev] == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csa2::index_score_kernel, csa2::kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csa2::index_score_kernel<false>, csa2::kThreads, 0) !=
             hipSuccess || per_cu <= 0)
       per_cu = 2;
     cached[dev] = cus * per_cu;
@@ -175,7 +214,7 @@ extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
     if ((int64_t)width != 8LL * M) return CSA2_ERR_INVALID_ARG;
     if (block_max) return CSA2_ERR_INVALID_ARG;
   }
-  if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
+  if (n_q > 65535 || width > kMaxIndexWidth) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(q_idx_bf16) | reinterpret_cast<uintptr_t>(idx_cache)) & 15)
     return CSA2_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(head_w) | reinterpret_cast<uintptr_t>(scores) |
@@ -190,7 +229,13 @@ extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
   const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
   if (grid_x > max_x) grid_x = max_x;
   if (grid_x < 1) grid_x = 1;
-  hipLaunchKernelGGL(index_score_kernel, dim3((unsigned)grid_x, n_q), dim3(kThreads), 0, (hipStream_t)stream,
-                     q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width, scores, block_max);
+  if (pool_blocks != nullptr)
+    hipLaunchKernelGGL(index_score_kernel<true>, dim3((unsigned)grid_x, n_q), dim3(kThreads), 0,
+                       (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width,
+                       scores, block_max);
+  else
+    hipLaunchKernelGGL(index_score_kernel<false>, dim3((unsigned)grid_x, n_q), dim3(kThreads), 0,
+                       (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width,
+                       scores, block_max);
   return check_launch();
 }

@@ -81,10 +81,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       const float4 w4 = *reinterpret_cast<const float4*>(wj + 8 * c);
-      part[c] = w4.x * __builtin_fmaxf(acc[4 * c], 0.0f);
-      part[c] = __builtin_fmaf(w4.y, __builtin_fmaxf(acc[4 * c + 1], 0.0f), part[c]);
-      part[c] = __builtin_fmaf(w4.z, __builtin_fmaxf(acc[4 * c + 2], 0.0f), part[c]);
-      part[c] = __builtin_fmaf(w4.w, __builtin_fmaxf(acc[4 * c + 3], 0.0f), part[c]);
+      part[c] = w4.x * relu(acc[4 * c]);
+      part[c] = __builtin_fmaf(w4.y, relu(acc[4 * c + 1]), part[c]);
+      part[c] = __builtin_fmaf(w4.z, relu(acc[4 * c + 2]), part[c]);
+      part[c] = __builtin_fmaf(w4.w, relu(acc[4 * c + 3]), part[c]);
     }
     const int32_t p = k * kTile + n;
     const float sum = sum_halves((part[0] + part[1]) + (part[2] + part[3]));
