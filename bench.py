@@ -305,6 +305,72 @@ def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=3):
     del kv, ix, scores, out, ws, wsa
     torch.cuda.empty_cache()
     return res
+def time_schedule(torch, csa2, tokens=1 << 20, n_seq=4, steps=10, warmup=2):
+    """Decode tokens through all 38 CSA2 layers of the 40-layer stack at `tokens` context:
+    3 Encoder caches (m = 2) and the Decoder cache (m = 1) packed from GPU-drawn latents,
+    per-layer query / indexer query / head weights / window rows drawn once.  Two tokens
+    are timed alternately, at positions `tokens` (the Decoder cache appends an entry) and
+    `tokens + 1` (every cache appends), each as one HIP graph of the whole token."""
+    from fp4_kv_cache_csa2_amd import schedule
+    dev = torch.device("cuda")
+    caps = {c: tokens // m + 2 for c, m in schedule.RATIO.items()}
+    g = schedule.GlobalBranch(n_seq, caps)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+
+    def rms_bf16(shape):
+        x = torch.randn(shape, generator=gen, device=dev)
+        return (x / torch.sqrt(torch.mean(x * x, dim=-1, keepdim=True) + 1e-6)).to(torch.bfloat16).contiguous()
+
+    print(f"[bench] schedule: packing 4 caches of {n_seq} x {tokens} tokens", file=sys.stderr, flush=True)
+    chunk = 1 << 18
+    for c, m in schedule.RATIO.items():
+        pool_w = torch.nn.functional.softplus(torch.randn((m, 512), generator=gen, device=dev)).contiguous()
+        w_idx = (torch.randn((128, 512), generator=gen, device=dev) / 512 ** 0.5).to(torch.bfloat16).contiguous()
+        g.set_params(c, pool_w, w_idx)
+        for t0 in range(0, tokens, chunk):
+            g.fill(c, rms_bf16((n_seq, min(chunk, tokens - t0), 512)), first_entry=t0 // m)
+    layers = schedule.csa2_layers()
+    swa_start = (torch.arange(n_seq, dtype=torch.int64, device=dev) * 128).contiguous()
+    swa_len = torch.full((n_seq,), 128, dtype=torch.int32, device=dev)
+    inputs = {l: {"q": torch.randn((n_seq, 64, 512), generator=gen, device=dev).to(torch.bfloat16).contiguous(),
+                  "swa": rms_bf16((n_seq * 128, 512)), "swa_start": swa_start, "swa_len": swa_len,
+                  "q_idx": (torch.randn((n_seq, 32, 128), generator=gen, device=dev) / 128 ** 0.5).to(
+                      torch.bfloat16).contiguous(),
+                  "head_w": (torch.randn((n_seq, 32), generator=gen, device=dev) / 32 ** 0.5).contiguous()}
+              for l in layers}
+    new = {c: rms_bf16((n_seq * m, 512)) for c, m in schedule.RATIO.items()}
+    outs = {l: torch.empty((n_seq, 64, 512), dtype=torch.float32, device=dev) for l in layers}
+    positions = (tokens, tokens + 1)
+    for _ in range(warmup):
+        for p in positions:
+            g.decode_token(p, new, inputs, outs)
+    torch.cuda.synchronize()
+    cap_stream = torch.cuda.Stream()
+    graphs = []
+    for p in positions:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap_stream):
+            g.decode_token(p, new, inputs, outs)
+        graphs.append(gr)
+    for gr in graphs:
+        gr.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {"tokens_per_s": round(n_seq * steps / wall, 1), "us_per_token_step": round(wall * 1e6 / steps, 1),
+           "sequences": n_seq, "context_tokens": tokens,
+           "caches": {c: {"m": m, "entries_per_sequence": tokens // m} for c, m in schedule.RATIO.items()},
+           "layers": "40 (2 SWA-only skipped): 4 Full, 4 Reindex, 30 Reuse; 38 attention calls per token",
+           "window": "bf16 rows, drawn once per layer"}
+    del graphs, g, inputs, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 # the sources the decode-path index kernel is built from
 INDEX_SRCS = [os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "csrc", f)
               for f in ("index_score.hip", "index_common.hpp", "csa2_device.hpp")]
@@ -434,6 +500,7 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] secondary workloads", file=sys.stderr, flush=True)
         sec = {
+            "decode_token_40layer_1m_b4": time_schedule(torch, csa2),
             "decode_1m_b4_m2_fp8_window": time_decode(torch, csa2, 1 << 20, 4, 2, fp8_window=True),
             "decode_128k_b16_m1": time_decode(torch, csa2, 131072, 16, 1, extra_layers=4),
             "decode_32k_b4_m1": time_decode(torch, csa2, 32768, 4, 1),

@@ -27,6 +27,7 @@ _L.csa2_status_string.argtypes = [ctypes.c_int]
 _L.csa2_status_string.restype = ctypes.c_char_p
 _L.csa2_rope_table.argtypes = [_vp, _i64, _f64, _vp]
 _L.csa2_compress_pack.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
+_L.csa2_compress_append.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _L.csa2_index_score.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
@@ -38,7 +39,7 @@ _L.csa2_swa_pack_fp8.argtypes = [_vp, _i64, _vp, _vp, _vp]
 _L.csa2_sparse_attn_swa_fp8.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
                                         _sz, _vp]
 
-SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_compress_pack",
+SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_compress_pack", "csa2_compress_append",
            "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
            "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8")
 
@@ -112,6 +113,23 @@ def compress_pack(latent, m: int, pool_w, rope_cs, w_idx, kv_out=None, idx_out=N
         _ptr(latent), n, m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_out), _ptr(idx_out),
         _stream(stream)))
     return kv_out, idx_out
+
+
+def compress_append(latent, m: int, pool_w, rope_cs, w_idx, dst_rows, kv_cache, idx_cache, stream=None):
+    """Pack entries from latent bf16 [n*m, 512] into cache rows dst_rows (int64 [n], -1 drops)."""
+    _dev(latent, torch.bfloat16, "latent", 2)
+    n = latent.shape[0] // m
+    _dev(pool_w, torch.float32, "pool_w")
+    _dev(rope_cs, torch.float32, "rope_cs", 2)
+    _dev(w_idx, torch.bfloat16, "w_idx", 2)
+    _dev(dst_rows, torch.int64, "dst_rows", 1)
+    _dev(kv_cache, torch.uint8, "kv_cache")
+    _dev(idx_cache, torch.uint8, "idx_cache")
+    if rope_cs.shape[0] < n or dst_rows.numel() != n:
+        raise ValueError("rope_cs / dst_rows must cover every new entry")
+    _check("csa2_compress_append", _L.csa2_compress_append(
+        _ptr(latent), n, m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(dst_rows), _ptr(kv_cache),
+        _ptr(idx_cache), _stream(stream)))
 
 
 def index_score(q_idx, head_w, idx_cache, q_base, q_nvis, width: int, pool_blocks=None,

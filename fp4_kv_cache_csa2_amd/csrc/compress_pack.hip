@@ -46,7 +46,7 @@ template <int kEnt>
 __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
     const float* __restrict__ rope_cs, const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out,
-    uint8_t* __restrict__ idx_out) {
+    uint8_t* __restrict__ idx_out, const int64_t* __restrict__ dst_rows) {
   __shared__ float s_c[kEnt][kD];          // rotated fp32 entries
   __shared__ float s_k[kEnt][kIdxDim];     // projected indexer keys
   constexpr bool kDirect = kEnt == 2;
@@ -55,6 +55,8 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t s_wl[kDirect ? kIdxDim * kWRow : 8];  // all of W_idx
   const int t = threadIdx.x;
   const int64_t j0 = (int64_t)blockIdx.x * kEnt;
+  // cache row that entry j is written to (a negative row drops the entry)
+  auto out_row = [&](int64_t j) -> int64_t { return dst_rows != nullptr ? dst_rows[j] : j; };
   constexpr int kRowPieces = kD / 8;  // a W_idx row as 64 pieces of 8 bf16
   if constexpr (kDirect) {
     const int lane = t & 63, wave = t >> 6;
@@ -119,8 +121,9 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     uint32_t half = 0;
 #pragma unroll
     for (int v = 0; v < 4; v++) half |= e2m1_encode(c[v], S) << (4 * v);
-    if (live) {
-      uint8_t* dst = kv_out + j * kKvBytes;
+    const int64_t row = live ? out_row(j) : -1;
+    if (row >= 0) {
+      uint8_t* dst = kv_out + row * kKvBytes;
       *reinterpret_cast<uint16_t*>(dst + 2 * q) = (uint16_t)half;
       if ((q & 3) == 0) dst[256 + (q >> 2)] = (uint8_t)sb;
     }
@@ -201,9 +204,12 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
           pay[2 * g + w] = word;
         }
       }
-      uint8_t* dst = kv_out + j * kKvBytes;
-      *reinterpret_cast<uint4*>(dst + 16 * p) = make_uint4(pay[0], pay[1], pay[2], pay[3]);
-      *reinterpret_cast<uint16_t*>(dst + 256 + 2 * p) = (uint16_t)scl;
+      const int64_t row = out_row(j);
+      if (row >= 0) {
+        uint8_t* dst = kv_out + row * kKvBytes;
+        *reinterpret_cast<uint4*>(dst + 16 * p) = make_uint4(pay[0], pay[1], pay[2], pay[3]);
+        *reinterpret_cast<uint16_t*>(dst + 256 + 2 * p) = (uint16_t)scl;
+      }
     }
   }
   __syncthreads();
@@ -308,8 +314,9 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     uint32_t word = 0;
 #pragma unroll
     for (int q = 0; q < 8; q++) word |= e2m1_encode(v[q], X) << (4 * q);
-    if (j < n_entries) {
-      uint8_t* dst = idx_out + j * kIdxBytes;
+    const int64_t row = j < n_entries ? out_row(j) : -1;
+    if (row >= 0) {
+      uint8_t* dst = idx_out + row * kIdxBytes;
       *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
       if (sub == 0) dst[64 + g] = (uint8_t)code;
     }
@@ -319,10 +326,10 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
 }  // namespace
 }  // namespace csa2
 
-extern "C" int csa2_compress_pack(const uint16_t* latent_bf16, int64_t n_entries, int m,
-                                  const float* pool_w, const float* rope_cs,
-                                  const uint16_t* w_idx_bf16, uint8_t* kv_out, uint8_t* idx_out,
-                                  void* stream) {
+namespace {
+int launch_compress(const uint16_t* latent_bf16, int64_t n_entries, int m, const float* pool_w,
+                    const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_out, uint8_t* idx_out,
+                    const int64_t* dst_rows, void* stream) {
   using namespace csa2;
   if (n_entries < 0) return CSA2_ERR_INVALID_ARG;
   if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
@@ -332,18 +339,37 @@ extern "C" int csa2_compress_pack(const uint16_t* latent_bf16, int64_t n_entries
   if ((reinterpret_cast<uintptr_t>(latent_bf16) | reinterpret_cast<uintptr_t>(w_idx_bf16) |
        reinterpret_cast<uintptr_t>(kv_out) | reinterpret_cast<uintptr_t>(idx_out)) & 15)
     return CSA2_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(rope_cs) | reinterpret_cast<uintptr_t>(pool_w)) & 3)
+  if ((reinterpret_cast<uintptr_t>(rope_cs) | reinterpret_cast<uintptr_t>(pool_w)) & 3 ||
+      reinterpret_cast<uintptr_t>(dst_rows) & 7)
     return CSA2_ERR_INVALID_ARG;
   if (n_entries <= 64) {
     hipLaunchKernelGGL(compress_pack_kernel<2>, dim3((unsigned)((n_entries + 1) / 2)), dim3(kThreads), 0,
                        (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
-                       kv_out, idx_out);
+                       kv_out, idx_out, dst_rows);
   } else {
     const int64_t grid = (n_entries + 15) / 16;
     if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(compress_pack_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0,
                        (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
-                       kv_out, idx_out);
+                       kv_out, idx_out, dst_rows);
   }
   return check_launch();
+}
+}  // namespace
+
+extern "C" int csa2_compress_pack(const uint16_t* latent_bf16, int64_t n_entries, int m,
+                                  const float* pool_w, const float* rope_cs,
+                                  const uint16_t* w_idx_bf16, uint8_t* kv_out, uint8_t* idx_out,
+                                  void* stream) {
+  return launch_compress(latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16, kv_out, idx_out, nullptr,
+                         stream);
+}
+
+extern "C" int csa2_compress_append(const uint16_t* latent_bf16, int64_t n_entries, int m,
+                                    const float* pool_w, const float* rope_cs,
+                                    const uint16_t* w_idx_bf16, const int64_t* dst_rows,
+                                    uint8_t* kv_cache, uint8_t* idx_cache, void* stream) {
+  if (!dst_rows && n_entries > 0) return CSA2_ERR_INVALID_ARG;
+  return launch_compress(latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+                         dst_rows, stream);
 }

@@ -99,6 +99,20 @@ int csa2_compress_pack(const uint16_t *latent_bf16, int64_t n_entries, int m,
                        uint8_t *kv_out, uint8_t *idx_out, void *stream);
 
 /*
+ * csa2_compress_append -- csa2_compress_pack writing entry i to cache row dst_rows[i].
+ *   [DF] §4.3: a Full layer writes its own main KV and indexer K; a decoding token at
+ *   position p completes an entry of a ratio-m cache when p + 1 is a multiple of m, and
+ *   the batch's new entries land at each sequence's next row, which need not be adjacent.
+ *   Same arguments and results as csa2_compress_pack, with kv_out / idx_out replaced by
+ *   the caches (16-byte aligned bases) and dst_rows: device int64 [n_entries] (8-byte
+ *   aligned), the row of each entry; a negative row drops that entry.
+ *   Errors: as csa2_compress_pack, and INVALID_ARG for a NULL dst_rows.
+ */
+int csa2_compress_append(const uint16_t *latent_bf16, int64_t n_entries, int m, const float *pool_w,
+                         const float *rope_cs, const uint16_t *w_idx_bf16, const int64_t *dst_rows,
+                         uint8_t *kv_cache, uint8_t *idx_cache, void *stream);
+
+/*
  * csa2_index_score -- lightning-indexer scores over the MXFP4 indexer-K cache.
  *   [ZB] §3.3.2 (indexer query q^I and per-head weights produce the Top-K set),
  *   [ZB] §2.3.4 / [DF] §4.7 (the Full layer scores every causally visible entry; a

@@ -84,3 +84,14 @@ def test_fp8_window_entry_points_validate_before_launch(lib):
     assert attn(fake, fake, fake, fake, 512, ctypes.c_void_p((1 << 20) + 4), 0, fake, fake, 0.04, fake, None, 1,
                 None, 0, None) == -1
     assert attn(fake, fake, fake, fake, 512, fake, 128, fake, fake, 0.04, fake, None, 1, None, 0, None) == -3
+
+
+def test_compress_append_validates_before_launch(lib):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.csa2_compress_append.argtypes = [vp, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.csa2_compress_append(fake, 4, 1, None, fake, fake, None, fake, fake, None) == -1  # no rows
+    assert lib.csa2_compress_append(fake, 4, 3, fake, fake, fake, fake, fake, fake, None) == -2
+    assert lib.csa2_compress_append(fake, 4, 1, None, fake, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake,
+                                    None) == -1  # rows not 8-B aligned
+    assert lib.csa2_compress_append(fake, 0, 1, None, None, None, None, None, None, None) == 0
