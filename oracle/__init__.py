@@ -71,6 +71,8 @@ def lib():
         L.csa2o_block_topk.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, vp, vp]
         L.csa2o_topk_bruteforce.argtypes = [vp, i32, i32, vp, i32, vp]
         L.csa2o_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_float, vp, vp, i32]
+        L.csa2o_quantize_q_mxfp4.argtypes = [vp, i64, vp]
+        L.csa2o_index_score_fp4q.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
         L.csa2o_swa_fp8_row_bytes.argtypes = []
         L.csa2o_swa_fp8_row_bytes.restype = i64
         L.csa2o_e8m0_scale_code_e4m3.argtypes = [ctypes.c_float]
@@ -181,6 +183,31 @@ def index_score(q_idx_bf16, head_w, idx_cache, q_base, q_nvis, width: int,
         M = pb.shape[1]
     out = np.empty((n_q, width), np.float32)
     lib().csa2o_index_score(_p(q), _p(w), _p(cache), _p(base), _p(nvis), _p(pb), M, n_q, width, _p(out))
+    return out
+
+
+def quantize_q_mxfp4(q_bf16):
+    """Indexer query bf16 bits [n_q, 32, 128] -> MXFP4 head vectors uint8 [n_q, 32, 68]."""
+    q = _c(q_bf16, np.uint16)
+    n_q = q.shape[0]
+    out = np.empty((n_q, IDX_HEADS, IDX_BYTES), np.uint8)
+    lib().csa2o_quantize_q_mxfp4(_p(q), n_q * IDX_HEADS, _p(out))
+    return out
+
+
+def index_score_fp4q(q_fp4, head_w, idx_cache, q_base, q_nvis, width: int, pool_blocks=None, M: int = 0):
+    q = _c(q_fp4, np.uint8)
+    w = _c(head_w, np.float32)
+    cache = _c(idx_cache, np.uint8)
+    base = _c(q_base, np.int64)
+    nvis = _c(q_nvis, np.int32)
+    n_q = base.size
+    pb = None
+    if pool_blocks is not None:
+        pb = _c(pool_blocks, np.int32)
+        M = pb.shape[1]
+    out = np.empty((n_q, width), np.float32)
+    lib().csa2o_index_score_fp4q(_p(q), _p(w), _p(cache), _p(base), _p(nvis), _p(pb), M, n_q, width, _p(out))
     return out
 
 

@@ -231,23 +231,24 @@ void csa2o_dequant_idx(const uint8_t *e, double *out) {
 
 /* ------------------------------------------------------------------ stage 2 */
 
-static double index_score_one(const uint16_t *q, const float *w, const uint8_t *entry) {
+/* s = sum_h w_h max(0, q_h . k): q given as exact doubles [32 x 128] */
+static double index_score_one(const double *q, const float *w, const uint8_t *entry) {
   double k[IDX_DIM];
   csa2o_dequant_idx(entry, k);
   double s = 0.0;
   for (int h = 0; h < IDX_HEADS; h++) {
     double dot = 0.0;
-    for (int d = 0; d < IDX_DIM; d++) dot += (double)bf16_to_f32(q[h * IDX_DIM + d]) * k[d];
+    for (int d = 0; d < IDX_DIM; d++) dot += q[h * IDX_DIM + d] * k[d];
     if (dot > 0.0) s += (double)w[h] * dot; /* ReLU, then the per-head weight */
   }
   return s;
 }
 
-void csa2o_index_score(const uint16_t *q_idx, const float *head_w, const uint8_t *idx_cache,
-                       const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
-                       int32_t M, int32_t n_q, int32_t width, float *scores) {
+static void index_score_rows(const double *qd, const float *head_w, const uint8_t *idx_cache,
+                             const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
+                             int32_t M, int32_t n_q, int32_t width, float *scores) {
   for (int32_t t = 0; t < n_q; t++) {
-    const uint16_t *q = q_idx + (int64_t)t * IDX_HEADS * IDX_DIM;
+    const double *q = qd + (int64_t)t * IDX_HEADS * IDX_DIM;
     const float *w = head_w + (int64_t)t * IDX_HEADS;
     float *row = scores + (int64_t)t * width;
     for (int32_t p = 0; p < width; p++) row[p] = -INFINITY;
@@ -267,6 +268,53 @@ void csa2o_index_score(const uint16_t *q_idx, const float *head_w, const uint8_t
       }
     }
   }
+}
+
+void csa2o_index_score(const uint16_t *q_idx, const float *head_w, const uint8_t *idx_cache,
+                       const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
+                       int32_t M, int32_t n_q, int32_t width, float *scores) {
+  const int64_t nv = (int64_t)n_q * IDX_HEADS * IDX_DIM;
+  double *qd = (double *)malloc(sizeof(double) * (size_t)(nv > 0 ? nv : 1));
+  for (int64_t i = 0; i < nv; i++) qd[i] = (double)bf16_to_f32(q_idx[i]);
+  index_score_rows(qd, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, n_q, width, scores);
+  free(qd);
+}
+
+/* ------------------------------------------------------------------ FP4 indexer query */
+
+/* The indexer query in MXFP4 ([ZB] §2.4.4: DeepSeek-V4 already trains the indexer Q and K
+ * for FP4; the format is OCP MXFP4): each head's 128 channels are packed like an
+ * indexer-K entry -- E2M1 codes, channel 2b in the low nibble of byte b, one E8M0 scale
+ * per 32 channels by the MX rule -- into 68 bytes.  n_vec = n_q * 32 head vectors. */
+void csa2o_quantize_q_mxfp4(const uint16_t *q_bf16, int64_t n_vec, uint8_t *out) {
+  int codes[IDX_DIM];
+  for (int64_t v = 0; v < n_vec; v++) {
+    const uint16_t *x = q_bf16 + v * IDX_DIM;
+    uint8_t *o = out + v * IDX_BYTES;
+    for (int g = 0; g < IDX_DIM / 32; g++) {
+      float amax = 0.0f;
+      for (int i = 0; i < 32; i++) {
+        float a = fabsf(bf16_to_f32(x[32 * g + i]));
+        if (a > amax) amax = a;
+      }
+      int sc = csa2o_e8m0_scale_code(amax);
+      double X = csa2o_e8m0_value(sc);
+      o[64 + g] = (uint8_t)sc;
+      for (int i = 0; i < 32; i++) codes[32 * g + i] = csa2o_e2m1_encode(bf16_to_f32(x[32 * g + i]), X);
+    }
+    pack_nibbles(codes, IDX_DIM, o);
+  }
+}
+
+/* Stage 2 with the MXFP4 query: the same score, q_h the dequantised head vector. */
+void csa2o_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8_t *idx_cache,
+                            const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
+                            int32_t M, int32_t n_q, int32_t width, float *scores) {
+  const int64_t nh = (int64_t)n_q * IDX_HEADS;
+  double *qd = (double *)malloc(sizeof(double) * (size_t)(nh > 0 ? nh * IDX_DIM : 1));
+  for (int64_t v = 0; v < nh; v++) csa2o_dequant_idx(q_fp4 + v * IDX_BYTES, qd + v * IDX_DIM);
+  index_score_rows(qd, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, n_q, width, scores);
+  free(qd);
 }
 
 /* ------------------------------------------------------------------ stage 3 */

@@ -92,6 +92,14 @@ void csa2o_sparse_attn(const uint16_t *q, const uint8_t *kv_cache, const int64_t
                        const int64_t *swa_start, const int32_t *swa_len, float scale,
                        float *out, float *lse, int32_t n_q);
 
+/* ---- FP4 indexer query ([ZB] §2.4.4: FP4 indexer Q and K; OCP MXFP4) ---------------
+ * q head vectors packed exactly like indexer-K entries (68 B: 64 B of E2M1 codes, 4 E8M0
+ * scales); the score is stage 2's with q_h dequantised. */
+void csa2o_quantize_q_mxfp4(const uint16_t *q_bf16, int64_t n_vec, uint8_t *out68);
+void csa2o_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8_t *idx_cache,
+                            const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
+                            int32_t M, int32_t n_q, int32_t width, float *scores);
+
 /* ---- FP8 window rows (the sliding-window KV kept in FP8: [ZB] §2.4.4, [SR] "FP4 Main
  * KV Cache"; the 584-byte FP8 KV entry of [ZB] §3.1 and [DF] §4.6) ------------------------
  * row: [0,448) E4M3 codes of channels 0..447 | [448,576) BF16 bits of channels 448..511 |
