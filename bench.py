@@ -127,9 +127,10 @@ class Decode1M:
     it, attend) and Reuse layers (attend with the Reindex indices)."""
 
     def __init__(self, torch, csa2, tokens, n_seq=4, m=2, K=512, M=2048, ncopy=NCOPY, extra_layers=0,
-                 fp8_window=False):
+                 fp8_window=False, fp4q=False):
         self.torch, self.csa2 = torch, csa2
         self.fp8 = fp8_window
+        self.fp4q = fp4q
         self.n_seq, self.m, self.tokens, self.K, self.M, self.ncopy = n_seq, m, tokens, K, M, ncopy
         self.extra = extra_layers
         n = self.n = tokens // m
@@ -158,6 +159,8 @@ class Decode1M:
             self.scores_r = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
             self.topk_r = torch.empty((n_seq, K), dtype=torch.int32, device=dev)
         self.n_stages = 4 + (2 + extra_layers if extra_layers else 0)
+        if fp4q:  # the step packs the layer's bf16 indexer query into MXFP4 records, then scores
+            self.q_fp4 = torch.empty((n_seq, 32, 68), dtype=torch.uint8, device=dev)
         if fp8_window:
             # per-sequence FP8 window rings of 128 rows; each step packs the newest token's
             # row into its slot, then attends over the ring (oldest row first)
@@ -179,6 +182,10 @@ class Decode1M:
         if st == 0:  # the newest entry of every sequence from its two latest latents
             csa2.compress_pack(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"], self.cs_new[ci],
                                c["w_idx"], kv_out=self.new_kv[ci], idx_out=self.new_ix[ci])
+        elif st == 1 and self.fp4q:
+            csa2.quantize_q_mxfp4(c["q_idx"], out=self.q_fp4)
+            csa2.index_score_fp4q(self.q_fp4, c["head_w"], c["ix"], self.q_base, self.q_nvis, n, scores=self.scores,
+                                  block_max=self.bmax)
         elif st == 1:
             csa2.index_score(c["q_idx"], c["head_w"], c["ix"], self.q_base, self.q_nvis, n, scores=self.scores,
                              block_max=self.bmax)
@@ -208,10 +215,10 @@ class Decode1M:
 STAGES = ("compress_newest", "index_score", "block_topk", "sparse_attn")
 
 
-def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3, fp8_window=False):
+def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3, fp8_window=False, fp4q=False):
     """Whole-step throughput of a secondary decode workload: one HIP graph per batch copy
     holding every stage of the step, replayed `steps` times between two synchronisations."""
-    wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers, fp8_window=fp8_window)
+    wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers, fp8_window=fp8_window, fp4q=fp4q)
     for i in range(warmup):
         for st in range(wl.n_stages):
             wl.run_stage(i % NCOPY, st)
@@ -235,7 +242,8 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
     res = {"queries_per_s": round(n_seq * steps / wall, 1), "us_per_step": round(wall * 1e6 / steps, 2),
            "sequences": n_seq, "tokens_per_sequence": tokens, "compress_ratio": m, "entries_per_sequence": wl.n,
            "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else ""),
-           "window": "FP8 rings (append + attend)" if fp8_window else "bf16"}
+           "window": "FP8 rings (append + attend)" if fp8_window else "bf16",
+           "indexer_query": "MXFP4 (packed in the step)" if fp4q else "bf16"}
     del graphs, wl
     torch.cuda.empty_cache()
     return res
@@ -284,7 +292,12 @@ def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=3):
         "select_4096_queries": lambda: csa2.block_topk(scores, nvis, want_pool=False, topk_out=topk, workspace=ws),
         "attn_4096_queries": lambda: csa2.sparse_attn(q, kv, base, topk, swa, swa_start, swa_len, out=out,
                                                       lse=lse, workspace=wsa),
+        # the same scoring with the indexer query packed to MXFP4 (FP4 x FP4 block-scaled MFMA)
+        "pack_q_mxfp4": lambda: csa2.quantize_q_mxfp4(q_idx, out=q_fp4),
+        "index_4096_queries_fp4q": lambda: csa2.index_score_fp4q(q_fp4, head_w, ix, base, nvis, n, scores=scores,
+                                                                 want_block_max=False),
     }
+    q_fp4 = torch.empty((chunk, 32, 68), dtype=torch.uint8, device=dev)
     ms = {}
     for name, fn in stages.items():
         fn()
@@ -298,10 +311,16 @@ def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=3):
         torch.cuda.synchronize()
         ms[name] = round(a.elapsed_time(b) / reps, 4)
     flops = 2.0 * 32 * 128 * float(nvis.sum().item())
-    res = {"ms": ms, "total_ms": round(sum(ms.values()), 4),
-           "index_mfma": {"achieved_tflops": round(flops / (ms["index_4096_queries"] * 1e-3) / 1e12, 1),
-                          "peak_tflops": 2500.0, "dtype": "bf16",
-                          "frac": round(flops / (ms["index_4096_queries"] * 1e-3) / 2.5e15, 4)}}
+    bf16_path = ("compress_2048_entries", "index_4096_queries", "select_4096_queries", "attn_4096_queries")
+    fp4_path = ("compress_2048_entries", "pack_q_mxfp4", "index_4096_queries_fp4q", "select_4096_queries",
+                "attn_4096_queries")
+    t_b, t_f = ms["index_4096_queries"] * 1e-3, ms["index_4096_queries_fp4q"] * 1e-3
+    res = {"ms": ms, "total_ms": round(sum(ms[k] for k in bf16_path), 4),
+           "total_ms_fp4q": round(sum(ms[k] for k in fp4_path), 4),
+           "index_mfma": {"achieved_tflops": round(flops / t_b / 1e12, 1), "peak_tflops": 2500.0, "dtype": "bf16",
+                          "frac": round(flops / t_b / 2.5e15, 4)},
+           "index_mfma_fp4q": {"achieved_tflops": round(flops / t_f / 1e12, 1), "peak_tflops": 10100.0,
+                               "dtype": "fp4", "frac": round(flops / t_f / 10.1e15, 4)}}
     del kv, ix, scores, out, ws, wsa
     torch.cuda.empty_cache()
     return res
@@ -502,6 +521,7 @@ def main():
         sec = {
             "decode_token_40layer_1m_b4": time_schedule(torch, csa2),
             "decode_1m_b4_m2_fp8_window": time_decode(torch, csa2, 1 << 20, 4, 2, fp8_window=True),
+            "decode_1m_b4_m2_fp4q": time_decode(torch, csa2, 1 << 20, 4, 2, fp4q=True),
             "decode_128k_b16_m1": time_decode(torch, csa2, 131072, 16, 1, extra_layers=4),
             "decode_32k_b4_m1": time_decode(torch, csa2, 32768, 4, 1),
             "tiny_4k_b1_m2": time_decode(torch, csa2, 4096, 1, 2),

@@ -29,6 +29,8 @@ _L.csa2_rope_table.argtypes = [_vp, _i64, _f64, _vp]
 _L.csa2_compress_pack.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
 _L.csa2_compress_append.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _L.csa2_index_score.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+_L.csa2_quantize_q_mxfp4.argtypes = [_vp, _i64, _vp, _vp]
+_L.csa2_index_score_fp4q.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
 _L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
@@ -41,7 +43,8 @@ _L.csa2_sparse_attn_swa_fp8.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp
 
 SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_compress_pack", "csa2_compress_append",
            "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
-           "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8")
+           "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8",
+           "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DEFAULT_SCALE = 512 ** -0.5
@@ -152,6 +155,47 @@ def index_score(q_idx, head_w, idx_cache, q_base, q_nvis, width: int, pool_block
     _dev(block_max, torch.float32, "block_max")
     _check("csa2_index_score", _L.csa2_index_score(
         _ptr(q_idx), _ptr(head_w), _ptr(idx_cache), _ptr(q_base), _ptr(q_nvis), _ptr(pool_blocks),
+        M, n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
+    return scores, block_max
+
+
+def quantize_q_mxfp4(q_idx, out=None, stream=None):
+    """bf16 head vectors [..., 128] -> MXFP4 records uint8 [..., 68] (the indexer-K format)."""
+    _dev(q_idx, torch.bfloat16, "q_idx")
+    if q_idx.shape[-1] != 128:
+        raise ValueError("q_idx must end in 128 channels")
+    n_vec = q_idx.numel() // 128
+    if out is None:
+        out = torch.empty((*q_idx.shape[:-1], 68), dtype=torch.uint8, device=q_idx.device)
+    _dev(out, torch.uint8, "out")
+    if out.numel() != n_vec * 68:
+        raise ValueError("out must hold 68 bytes per head vector")
+    _check("csa2_quantize_q_mxfp4", _L.csa2_quantize_q_mxfp4(_ptr(q_idx), n_vec, _ptr(out), _stream(stream)))
+    return out
+
+
+def index_score_fp4q(q_fp4, head_w, idx_cache, q_base, q_nvis, width: int, pool_blocks=None,
+                     scores=None, block_max=None, want_block_max: bool = True, stream=None):
+    """index_score with MXFP4 queries q_fp4 uint8 [n_q, 32, 68] (from quantize_q_mxfp4)."""
+    _dev(q_fp4, torch.uint8, "q_fp4", 3)
+    if tuple(q_fp4.shape[1:]) != (32, 68):
+        raise ValueError("q_fp4 must be [n_q, 32, 68]")
+    _dev(head_w, torch.float32, "head_w", 2)
+    _dev(idx_cache, torch.uint8, "idx_cache")
+    _dev(q_base, torch.int64, "q_base", 1)
+    _dev(q_nvis, torch.int32, "q_nvis", 1)
+    _dev(pool_blocks, torch.int32, "pool_blocks", 2)
+    n_q = q_fp4.shape[0]
+    M = 0 if pool_blocks is None else pool_blocks.shape[1]
+    dev = q_fp4.device
+    if scores is None:
+        scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
+    if block_max is None and want_block_max and pool_blocks is None:
+        block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
+    _dev(scores, torch.float32, "scores")
+    _dev(block_max, torch.float32, "block_max")
+    _check("csa2_index_score_fp4q", _L.csa2_index_score_fp4q(
+        _ptr(q_fp4), _ptr(head_w), _ptr(idx_cache), _ptr(q_base), _ptr(q_nvis), _ptr(pool_blocks),
         M, n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
     return scores, block_max
 

@@ -19,25 +19,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWChunk = 64;  // channels of W_idx staged per step
 
-// E2M1 code of e on the grid {0,.5,1,1.5,2,3,4,6} * S by exact midpoint comparisons,
-// ties to the even code, saturating at 6; the sign bit only on a non-zero code.
-__device__ __forceinline__ uint32_t e2m1_encode(float e, float S) {
-  if (!(S > 0.0f)) return 0;
-  const float a = __builtin_fabsf(e);
-  uint32_t c = (a > 0.25f * S) + (a > 0.75f * S) + (a > 1.25f * S) + (a > 1.75f * S) +
-               (a > 2.5f * S) + (a > 3.5f * S) + (a > 5.0f * S);
-  c += (a == 0.75f * S) + (a == 1.75f * S) + (a == 3.5f * S);  // odd-side ties round up
-  return (e < 0.0f && c != 0) ? (c | 8u) : c;
-}
-
-// OCP MX shared-scale rule for E2M1 elements: floor(log2 amax) - 2 + 127, clamped.
-__device__ __forceinline__ uint32_t e8m0_scale_code(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  const int eb = (int)((__float_as_uint(amax) >> 23) & 255);  // 0 for subnormal amax
-  const int code = eb == 0 ? 0 : eb - 2;
-  return (uint32_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
-}
-
 // kEnt entries per workgroup: 16 amortises the W_idx reads over many entries; 2 keeps one
 // fma chain per thread for the few-entry appends of a decode step.  There the whole of
 // W_idx (128 KB) is copied into LDS at kernel entry by direct-to-LDS loads, one 1 KB row

@@ -59,6 +59,35 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// E2M1 code of e on the grid {0,.5,1,1.5,2,3,4,6} * S by exact midpoint comparisons,
+// ties to the even code, saturating at 6; the sign bit only on a non-zero code.
+// An infinite element saturates explicitly: at the largest scale (2^127, a group holding an
+// infinity) the upper midpoints overflow to +inf, which every finite |e| (at most FLT_MAX <
+// 2.5 * 2^127) correctly stays below.
+__device__ __forceinline__ uint32_t e2m1_encode(float e, float S) {
+  if (!(S > 0.0f)) return 0;
+  const float a = __builtin_fabsf(e);
+  uint32_t c;
+  if (a == __builtin_inff()) {
+    c = 7;
+  } else {
+    c = (a > 0.25f * S) + (a > 0.75f * S) + (a > 1.25f * S) + (a > 1.75f * S) + (a > 2.5f * S) +
+        (a > 3.5f * S) + (a > 5.0f * S);
+    c += (a == 0.75f * S) + (a == 1.75f * S) + (a == 3.5f * S);  // odd-side ties round up
+  }
+  return (e < 0.0f && c != 0) ? (c | 8u) : c;
+}
+
+// OCP MX shared-scale rule for E2M1 elements: floor(log2 amax) - 2 + 127, clamped; a
+// group holding an infinity takes the largest finite scale, 254.
+__device__ __forceinline__ uint32_t e8m0_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int eb = (int)((__float_as_uint(amax) >> 23) & 255);  // 0 for subnormal amax
+  if (eb == 255) return 254;
+  const int code = eb == 0 ? 0 : eb - 2;
+  return (uint32_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); NaN ranks as -inf.
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) f = -__builtin_inff();

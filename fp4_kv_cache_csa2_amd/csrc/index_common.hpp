@@ -31,6 +31,38 @@ __device__ __forceinline__ float e8m0_scale(uint32_t code) {
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 
+// 32 E2M1 codes (16 bytes) in the order the payload stores them: an FP4 MFMA operand
+typedef int32_t fp4x32 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// One 32-entry tile of q . k on the block-scaled FP4 MFMA (32 heads x 32 entries x 64 dims
+// per instruction).  Lane (n, g) holds, for both operands, the 64 codes of dims
+// 64g .. 64g + 63 of its head / entry as two 32-code MX blocks (blocks 2g and 2g + 1, each
+// block one instruction) and the row's scale word shifted so that byte 0 is block 2g's E8M0
+// code and byte 1 block 2g + 1's.  Operand A is the query, B the entries.  The dot products
+// are the MX definition: E2M1 values times 2^(code - 127), exact products, fp32 sums.
+__device__ __forceinline__ f32x16 mfma_fp4_tile(const fp4x32 (&qa)[2], uint32_t qsc, const u32x4_a4& lo,
+                                                const u32x4_a4& hi, uint32_t ksc, f32x16 acc) {
+  const i32x8 a0 = {qa[0][0], qa[0][1], qa[0][2], qa[0][3], 0, 0, 0, 0};
+  const i32x8 a1 = {qa[1][0], qa[1][1], qa[1][2], qa[1][3], 0, 0, 0, 0};
+  const i32x8 b0 = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+  const i32x8 b1 = {(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3], 0, 0, 0, 0};
+  // format 4 = E2M1 for both operands; scale byte 0 (block 2g), then byte 1 (block 2g + 1)
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, acc, 4, 4, 0, (int)qsc, 0, (int)ksc);
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, acc, 4, 4, 1, (int)qsc, 1, (int)ksc);
+  return acc;
+}
+
+// the MXFP4 query record of one head (68 B: 64 code bytes, 4 E8M0 bytes): lane group g
+// takes code bytes 32g .. 32g + 31 and the scale bytes of blocks 2g, 2g + 1
+__device__ __forceinline__ void load_fp4_query(const uint8_t* rec, int g, fp4x32 (&qa)[2], uint32_t& qsc) {
+  const u32x4_a4 lo = *reinterpret_cast<const u32x4_a4*>(rec + 32 * g);
+  const u32x4_a4 hi = *reinterpret_cast<const u32x4_a4*>(rec + 32 * g + 16);
+  qa[0] = fp4x32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+  qa[1] = fp4x32{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  qsc = *reinterpret_cast<const uint32_t*>(rec + 64) >> (16 * g);
+}
+
 struct RawTile {
   u32x4_a4 lo, hi;
   uint32_t sc;
@@ -53,6 +85,15 @@ __device__ __forceinline__ float max8_lanes(float v) {
   return v;
 }
 
+// the score of a lane, or -inf for a slot with no visible entry.  Written as an addition so
+// that every lane needs the sum: a select lets the compiler move the whole tile computation
+// (the wave-wide MFMAs and the cross-lane head sum) under the valid lanes' exec mask, which
+// it does for the block-scaled FP4 MFMA.  sum is finite for a valid slot (sum + 0 = sum,
+// -0 becoming +0) and 0 for an empty one (loads past the end return zeros).
+__device__ __forceinline__ float masked_score(float sum, bool valid) {
+  return sum + (valid ? 0.0f : -__builtin_inff());
+}
+
 // v(lane) + v(lane ^ 32)
 __device__ __forceinline__ float sum_halves(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
@@ -67,6 +108,9 @@ constexpr int32_t kMaxIndexWidth = 1 << 23;
 
 // batches of at least this many Full-mode queries take the many-query kernel
 constexpr int kMqMinQueries = 64;
+int launch_index_score_mq_fp4q(const uint8_t* q_fp4, const float* head_w, const uint8_t* idx_cache,
+                               const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
+                               float* scores, float* block_max, void* stream);
 int launch_index_score_mq(const uint16_t* q_idx_bf16, const float* head_w, const uint8_t* idx_cache,
                           const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
                           float* block_max, void* stream);

@@ -40,9 +40,13 @@ constexpr int kRawBuf = 0x00020000;        // buffer descriptor word 3: raw 32-b
 
 // kPool: Reindex layers score their candidate pool (entry j of slot p is block
 // pool_blocks[p / 8] * 8 + p % 8); Full layers score entries 0 .. width-1 directly.
-template <bool kPool>
+// kFp4Q: the indexer query arrives in MXFP4 (each head vector a 68-byte record like an
+// indexer-K entry, [ZB] §2.4.4: the indexer Q and K are both trained for FP4), and the
+// contraction runs on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands' E2M1 codes and
+// E8M0 scales fed to the instruction as stored: two MFMAs per tile, no conversions.
+template <bool kPool, bool kFp4Q>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
+    const void* __restrict__ q_in, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
     int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
@@ -70,10 +74,13 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     return;
   }
 
-  // the query (head n, dims 64g .. 64g + 63 as eight bf16x8 A fragments) and the head
-  // weight of each accumulator row this lane holds (row 8(r/4) + 4g + r%4); both are
-  // loaded after the first cache tiles, so the stream from HBM starts first
+  // the query (head n, dims 64g .. 64g + 63: eight bf16x8 A fragments, or for an MXFP4
+  // query two 32-code fragments and the head's scale word) and the head weight of each
+  // accumulator row this lane holds (row 8(r/4) + 4g + r%4); both are loaded after the
+  // first cache tiles, so the stream from HBM starts first
   bf16x8 a[8];
+  fp4x32 qa[2];
+  uint32_t qsc = 0;
   float wr[16];
 
   // Buffer resources bound the sequence's visible cache rows, the score row and the
@@ -114,14 +121,19 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs_cache, off + 64, 0, 0);
   };
   auto process = [&](const RawTile& cur, int32_t k) {
-    const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
-    const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
-    const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3], cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
     f32x16 acc = {};
+    if constexpr (kFp4Q) {
+      acc = mfma_fp4_tile(qa, qsc, cur.lo, cur.hi, cur.sc >> (16 * g), acc);
+    } else {
+      const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
+      const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
+      const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3],
+                                 cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
 #pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const bf16x8 b = cvt_fp4x8(words[s], s < 4 ? x0 : x1);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
+      for (int s = 0; s < 8; s++) {
+        const bf16x8 b = cvt_fp4x8(words[s], s < 4 ? x0 : x1);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
+      }
     }
     // ReLU, head weight and the sum over this lane's 16 heads as four short chains
     float part[4];
@@ -131,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
 #pragma unroll
       for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], relu(acc[4 * c + r]), part[c]);
     }
-    const float sc = cur.valid ? sum_halves((part[0] + part[1]) + (part[2] + part[3])) : -__builtin_inff();
+    const float sc = masked_score(sum_halves((part[0] + part[1]) + (part[2] + part[3])), cur.valid);
     // both lane halves hold the entry's score and all 8 lanes of a block its maximum; one
     // lane writes each value and the others aim past the buffer's end, so their stores
     // are dropped without a branch (as are slots past the row's end)
@@ -153,9 +165,14 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
+    if constexpr (kFp4Q) {
+      load_fp4_query(static_cast<const uint8_t*>(q_in) + ((int64_t)t * kIdxHeads + n) * kIdxBytes, g, qa, qsc);
+    } else {
+      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_in) +
+                                                       ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
 #pragma unroll
-    for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
+      for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
+    }
     typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
     const f32x4_a4* wp = reinterpret_cast<const f32x4_a4*>(head_w + (int64_t)t * kIdxHeads);
 #pragma unroll
@@ -190,12 +207,60 @@ int resident_workgroups() {
   if (cached[dev] == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csa2::index_score_kernel<false>, csa2::kThreads, 0) !=
-            hipSuccess || per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csa2::index_score_kernel<false, false>, csa2::kThreads,
+                                                     0) != hipSuccess ||
+        per_cu <= 0)
       per_cu = 2;
     cached[dev] = cus * per_cu;
   }
   return cached[dev];
+}
+
+// argument checks and launch shared by the bf16-query and MXFP4-query entry points
+template <bool kFp4Q>
+int index_score_entry(const void* q, const float* head_w, const uint8_t* idx_cache, const int64_t* q_base,
+                      const int32_t* q_nvis, const int32_t* pool_blocks, int32_t M, int32_t n_q, int32_t width,
+                      float* scores, float* block_max, void* stream) {
+  using namespace csa2;
+  if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
+  if (n_q == 0 || width == 0) return CSA2_OK;
+  if (!q || !head_w || !idx_cache || !q_base || !q_nvis || !scores) return CSA2_ERR_INVALID_ARG;
+  if (pool_blocks) {
+    if (M < 1) return CSA2_ERR_INVALID_ARG;
+    if (M > kMaxPool) return CSA2_ERR_UNSUPPORTED;
+    if ((int64_t)width != 8LL * M) return CSA2_ERR_INVALID_ARG;
+    if (block_max) return CSA2_ERR_INVALID_ARG;
+  }
+  if (n_q > 65535 || width > kMaxIndexWidth) return CSA2_ERR_UNSUPPORTED;
+  // bf16 queries are read as 16-byte pieces; MXFP4 query records (68 B) as dwords
+  if ((reinterpret_cast<uintptr_t>(q) & (kFp4Q ? 3 : 15)) | (reinterpret_cast<uintptr_t>(idx_cache) & 15))
+    return CSA2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(head_w) | reinterpret_cast<uintptr_t>(scores) |
+       reinterpret_cast<uintptr_t>(block_max)) & 3)
+    return CSA2_ERR_INVALID_ARG;
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  if (pool_blocks == nullptr && n_q >= kMqMinQueries) {  // many queries: shared K tiles
+    if constexpr (kFp4Q)
+      return launch_index_score_mq_fp4q(static_cast<const uint8_t*>(q), head_w, idx_cache, q_base, q_nvis, n_q,
+                                        width, scores, block_max, stream);
+    else
+      return launch_index_score_mq(static_cast<const uint16_t*>(q), head_w, idx_cache, q_base, q_nvis, n_q, width,
+                                   scores, block_max, stream);
+  }
+  // one full round of resident workgroups; each wave strides over its query's tiles
+  int64_t grid_x = (resident_workgroups() + n_q - 1) / n_q;
+  const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
+  if (grid_x > max_x) grid_x = max_x;
+  if (grid_x < 1) grid_x = 1;
+  if (pool_blocks != nullptr)
+    hipLaunchKernelGGL((index_score_kernel<true, kFp4Q>), dim3((unsigned)grid_x, n_q), dim3(kThreads), 0,
+                       (hipStream_t)stream, q, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width, scores,
+                       block_max);
+  else
+    hipLaunchKernelGGL((index_score_kernel<false, kFp4Q>), dim3((unsigned)grid_x, n_q), dim3(kThreads), 0,
+                       (hipStream_t)stream, q, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width, scores,
+                       block_max);
+  return check_launch();
 }
 }  // namespace
 
@@ -204,38 +269,14 @@ extern "C" int csa2_index_score(const uint16_t* q_idx_bf16, const float* head_w,
                                 const int32_t* q_nvis, const int32_t* pool_blocks, int32_t M,
                                 int32_t n_q, int32_t width, float* scores, float* block_max,
                                 void* stream) {
-  using namespace csa2;
-  if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
-  if (n_q == 0 || width == 0) return CSA2_OK;
-  if (!q_idx_bf16 || !head_w || !idx_cache || !q_base || !q_nvis || !scores) return CSA2_ERR_INVALID_ARG;
-  if (pool_blocks) {
-    if (M < 1) return CSA2_ERR_INVALID_ARG;
-    if (M > kMaxPool) return CSA2_ERR_UNSUPPORTED;
-    if ((int64_t)width != 8LL * M) return CSA2_ERR_INVALID_ARG;
-    if (block_max) return CSA2_ERR_INVALID_ARG;
-  }
-  if (n_q > 65535 || width > kMaxIndexWidth) return CSA2_ERR_UNSUPPORTED;
-  if ((reinterpret_cast<uintptr_t>(q_idx_bf16) | reinterpret_cast<uintptr_t>(idx_cache)) & 15)
-    return CSA2_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(head_w) | reinterpret_cast<uintptr_t>(scores) |
-       reinterpret_cast<uintptr_t>(block_max)) & 3)
-    return CSA2_ERR_INVALID_ARG;
-  const int32_t ntiles = (width + kTile - 1) / kTile;
-  if (pool_blocks == nullptr && n_q >= kMqMinQueries)  // many queries: shared K-tile decode
-    return launch_index_score_mq(q_idx_bf16, head_w, idx_cache, q_base, q_nvis, n_q, width, scores, block_max,
-                                 stream);
-  // one full round of resident workgroups; each wave strides over its query's tiles
-  int64_t grid_x = (resident_workgroups() + n_q - 1) / n_q;
-  const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
-  if (grid_x > max_x) grid_x = max_x;
-  if (grid_x < 1) grid_x = 1;
-  if (pool_blocks != nullptr)
-    hipLaunchKernelGGL(index_score_kernel<true>, dim3((unsigned)grid_x, n_q), dim3(kThreads), 0,
-                       (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width,
-                       scores, block_max);
-  else
-    hipLaunchKernelGGL(index_score_kernel<false>, dim3((unsigned)grid_x, n_q), dim3(kThreads), 0,
-                       (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width,
-                       scores, block_max);
-  return check_launch();
+  return index_score_entry<false>(q_idx_bf16, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, n_q, width, scores,
+                                  block_max, stream);
+}
+
+extern "C" int csa2_index_score_fp4q(const uint8_t* q_fp4, const float* head_w, const uint8_t* idx_cache,
+                                     const int64_t* q_base, const int32_t* q_nvis, const int32_t* pool_blocks,
+                                     int32_t M, int32_t n_q, int32_t width, float* scores, float* block_max,
+                                     void* stream) {
+  return index_score_entry<true>(q_fp4, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, n_q, width, scores,
+                                 block_max, stream);
 }

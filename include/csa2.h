@@ -139,6 +139,34 @@ int csa2_index_score(const uint16_t *q_idx_bf16, const float *head_w, const uint
                      void *stream);
 
 /*
+ * csa2_quantize_q_mxfp4 -- packs indexer-query head vectors into MXFP4 records.
+ *   [ZB] §2.4.4: DeepSeek-V4 trains the indexer Q and K for FP4; the format is OCP MXFP4,
+ *   the indexer-K format above: each 128-channel head vector becomes 68 bytes (64 bytes
+ *   of E2M1 codes, channel 2b in the low nibble of byte b; 4 E8M0 scales, one per 32
+ *   channels) by the same rules as the indexer-K packer of csa2_compress_pack (E8M0 code
+ *   floor(log2 amax) - 2 + 127 clamped to [0, 254], 0 for an all-zero group, 254 for a
+ *   group holding an infinity; nearest-even E2M1 of x / X saturating at 6; NaN -> code 0).
+ *   q_bf16 [n_vec, 128] (16-byte aligned); out [n_vec, 68] (4-byte aligned).  Bit-exact.
+ *   For the indexer query n_vec = n_q * 32 and out is [n_q, 32, 68].
+ *   Errors: INVALID_ARG (NULL, n_vec < 0, misalignment).
+ */
+int csa2_quantize_q_mxfp4(const uint16_t *q_bf16, int64_t n_vec, uint8_t *out, void *stream);
+
+/*
+ * csa2_index_score_fp4q -- csa2_index_score with the indexer query in MXFP4.
+ *   [ZB] §2.4.4 (FP4 indexer Q and K): s(t, j) = sum_h head_w[t,h] max(0, q^_{t,h} . k^_j)
+ *   with q^_{t,h} the dequantised 68-byte query record of head h (csa2_quantize_q_mxfp4)
+ *   and k^_j as in csa2_index_score; products are exact, sums fp32.  The contraction runs
+ *   on gfx950's block-scaled FP4 matrix instructions.
+ *   q_fp4 [n_q, 32, 68] (4-byte aligned); every other argument, the modes, outputs and
+ *   errors are those of csa2_index_score.
+ */
+int csa2_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8_t *idx_cache,
+                          const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
+                          int32_t M, int32_t n_q, int32_t width, float *scores, float *block_max,
+                          void *stream);
+
+/*
  * csa2_block_topk -- hierarchical selection: block max -> top-M block pool -> Top-K.
  *   [ZB] §2.3.4 and [DF] §4.7: g_r = max over block r (b = `block` positions, -inf
  *   padding); the block holding the newest visible position takes +inf; the M blocks

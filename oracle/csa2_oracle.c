@@ -116,6 +116,7 @@ int csa2o_e2m1_encode(float e, double S) {
 
 int csa2o_e8m0_scale_code(float amax) {
   if (!(amax > 0.0f)) return 0;
+  if (isinf(amax)) return 254; /* a group holding an infinity takes the largest finite scale */
   int ex;
   frexpf(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
   int code = (ex - 1) - 2 + 127;

@@ -95,3 +95,22 @@ def test_compress_append_validates_before_launch(lib):
     assert lib.csa2_compress_append(fake, 4, 1, None, fake, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake,
                                     None) == -1  # rows not 8-B aligned
     assert lib.csa2_compress_append(fake, 0, 1, None, None, None, None, None, None, None) == 0
+
+
+def test_fp4_query_entry_points_validate_before_launch(lib):
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.csa2_quantize_q_mxfp4.argtypes = [vp, i64, vp, vp]
+    lib.csa2_index_score_fp4q.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.csa2_quantize_q_mxfp4(fake, -1, fake, None) == -1
+    assert lib.csa2_quantize_q_mxfp4(fake, 0, None, None) == 0
+    assert lib.csa2_quantize_q_mxfp4(None, 4, fake, None) == -1
+    assert lib.csa2_quantize_q_mxfp4(ctypes.c_void_p((1 << 20) + 8), 4, fake, None) == -1  # q not 16-B aligned
+    assert lib.csa2_quantize_q_mxfp4(fake, 4, ctypes.c_void_p((1 << 20) + 2), None) == -1  # out not 4-B aligned
+    score = lib.csa2_index_score_fp4q
+    assert score(fake, fake, fake, fake, fake, fake, 4096, 1, 8 * 4096, fake, None, None) == -2
+    assert score(fake, fake, fake, fake, fake, fake, 16, 1, 100, fake, None, None) == -1
+    assert score(None, fake, fake, fake, fake, None, 0, 1, 100, fake, None, None) == -1
+    assert score(ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, fake, None, 0, 1, 100, fake, None, None) == -1
+    assert score(fake, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake, None, 0, 1, 100, fake, None, None) == -1
+    assert score(fake, fake, fake, fake, fake, None, 0, 0, 100, fake, None, None) == 0

@@ -93,3 +93,22 @@ def test_fp4_query_score_equals_bf16_score_of_dequantised_query():
     pool[:, :5] = [[0, 3, 7, 9, 60], [1, 2, 5, 50, 53], [0, 1, -1, -1, -1]]
     assert np.array_equal(oracle.index_score_fp4q(q4, d.head_w, ix, base, nvis, 64, pool_blocks=pool),
                           oracle.index_score(qdeq, d.head_w, ix, base, nvis, 64, pool_blocks=pool))
+
+
+def test_group_holding_an_infinity_takes_the_largest_finite_scale():
+    """floor(log2 amax) has no value for amax = inf: such a group takes E8M0 code 254 (the
+    largest finite scale, as the FP8 window rows do) and the infinite element saturates to
+    the largest E2M1 magnitude; finite elements are coded against X = 2^127."""
+    x = np.zeros((1, 32, 128), np.float32)
+    x[0, 0, :32] = 1.0
+    x[0, 0, 3] = np.inf
+    x[0, 1, 32:64] = -2.0 ** 126
+    x[0, 1, 40] = -np.inf
+    out = oracle.quantize_q_mxfp4(synth.f32_to_bf16_bits(x))
+    assert out[0, 0, 64] == 254 and out[0, 1, 65] == 254
+    assert (out[0, 0, 1] >> 4) & 15 == 7                 # channel 3: +inf -> +6X
+    assert out[0, 1, 20] & 15 == 15                       # channel 40: -inf -> -6X
+    # -2^126 = -0.5 X: the E2M1 midpoint between 0 and 0.5 X is 0.25 X, so code 1 (0.5) with the sign
+    assert (out[0, 1, 16] & 15) == 9
+    # 1.0 = 2^-127 X rounds to zero
+    assert out[0, 0, 0] == 0
