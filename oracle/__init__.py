@@ -73,6 +73,8 @@ def lib():
         L.csa2o_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_float, vp, vp, i32]
         L.csa2o_quantize_q_mxfp4.argtypes = [vp, i64, vp]
         L.csa2o_index_score_fp4q.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+        L.csa2o_block_mean_pack.argtypes = [vp, i64, i32, vp]
+        L.csa2o_pool_from_block_scores.argtypes = [vp, i32, i32, vp, i32, i32, vp]
         L.csa2o_swa_fp8_row_bytes.argtypes = []
         L.csa2o_swa_fp8_row_bytes.restype = i64
         L.csa2o_e8m0_scale_code_e4m3.argtypes = [ctypes.c_float]
@@ -208,6 +210,25 @@ def index_score_fp4q(q_fp4, head_w, idx_cache, q_base, q_nvis, width: int, pool_
         M = pb.shape[1]
     out = np.empty((n_q, width), np.float32)
     lib().csa2o_index_score_fp4q(_p(q), _p(w), _p(cache), _p(base), _p(nvis), _p(pb), M, n_q, width, _p(out))
+    return out
+
+
+def block_mean_pack(idx_cache, block: int = 8):
+    """HISA block means of one sequence's indexer keys: uint8 [n, 68] -> [ceil(n/block), 68]."""
+    cache = _c(idx_cache, np.uint8)
+    n = cache.shape[0]
+    out = np.empty(((n + block - 1) // block, IDX_BYTES), np.uint8)
+    lib().csa2o_block_mean_pack(_p(cache), n, block, _p(out))
+    return out
+
+
+def pool_from_block_scores(block_scores, q_nvis, M: int = 2048, block: int = 8):
+    """Top-M blocks of block_scores [n_q, nbw] (newest visible block forced), ascending, -1 pad."""
+    bs = _c(block_scores, np.float32)
+    nvis = _c(q_nvis, np.int32)
+    n_q, nbw = bs.shape
+    out = np.empty((n_q, M), np.int32)
+    lib().csa2o_pool_from_block_scores(_p(bs), n_q, nbw, _p(nvis), block, M, _p(out))
     return out
 
 

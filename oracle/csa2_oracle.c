@@ -421,6 +421,70 @@ void csa2o_topk_bruteforce(const float *scores, int32_t n_q, int32_t width, cons
   free(cand);
 }
 
+/* ------------------------------------------------------------------ HISA block means */
+
+/* HISA's coarse filter ([ZB] §2.3.4, the HISA paragraphs): the prefix is cut into blocks of
+ * consecutive positions and every block keeps the mean of its indexer keys, an auxiliary
+ * for the search (the token keys stay).  The mean is taken over the exact dequantised keys
+ * of the block's entries: an fp32 sum in ascending position order (what a running sum of a
+ * decoding block holds), then one fp32 division by the entry count (a partial last block
+ * divides by its own count).  It is stored in the indexer-K format (MXFP4, 68 bytes) by the
+ * same rules as the indexer keys. */
+static void pack_mxfp4_128(const float *x, uint8_t *o) {
+  int codes[IDX_DIM];
+  for (int g = 0; g < IDX_DIM / 32; g++) {
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++) {
+      float a = fabsf(x[32 * g + i]);
+      if (a > amax) amax = a;
+    }
+    int sc = csa2o_e8m0_scale_code(amax);
+    double X = csa2o_e8m0_value(sc);
+    o[64 + g] = (uint8_t)sc;
+    for (int i = 0; i < 32; i++) codes[32 * g + i] = csa2o_e2m1_encode(x[32 * g + i], X);
+  }
+  pack_nibbles(codes, IDX_DIM, o);
+}
+
+void csa2o_block_mean_pack(const uint8_t *idx_cache, int64_t n_entries, int32_t block, uint8_t *out) {
+  double k[IDX_DIM];
+  float sum[IDX_DIM], mean[IDX_DIM];
+  const int64_t nb = (n_entries + block - 1) / block;
+  for (int64_t b = 0; b < nb; b++) {
+    const int64_t j0 = b * block;
+    const int64_t j1 = (j0 + block < n_entries) ? j0 + block : n_entries;
+    for (int64_t j = j0; j < j1; j++) {
+      csa2o_dequant_idx(idx_cache + j * IDX_BYTES, k); /* exact in fp32 */
+      for (int d = 0; d < IDX_DIM; d++) sum[d] = (j == j0) ? (float)k[d] : sum[d] + (float)k[d];
+    }
+    const float cnt = (float)(j1 - j0);
+    for (int d = 0; d < IDX_DIM; d++) mean[d] = sum[d] / cnt;
+    pack_mxfp4_128(mean, out + b * IDX_BYTES);
+  }
+}
+
+/* The candidate pool from caller-given block scores (HISA: the scores of the block means):
+ * the M blocks with the largest scores among the ceil(min(nvis, nbw*block)/block) visible
+ * blocks, the newest visible block forced in as in the HSI pool ([ZB] §2.3.4 boundary
+ * policy), ties to the lower block, NaN as -inf; ascending, padded with -1. */
+void csa2o_pool_from_block_scores(const float *bscores, int32_t n_q, int32_t nbw, const int32_t *q_nvis,
+                                  int32_t block, int32_t M, int32_t *pool_out) {
+  ranked_t *g = (ranked_t *)malloc(sizeof(ranked_t) * (size_t)(nbw > 0 ? nbw : 1));
+  for (int32_t t = 0; t < n_q; t++) {
+    int64_t nvis = q_nvis[t];
+    if (nvis > (int64_t)nbw * block) nvis = (int64_t)nbw * block;
+    if (nvis < 0) nvis = 0;
+    const int32_t nb = (int32_t)((nvis + block - 1) / block);
+    for (int32_t r = 0; r < nb; r++) {
+      g[r].key = rank_key(bscores[(int64_t)t * nbw + r]);
+      g[r].id = r;
+    }
+    if (nb > 0) g[nb - 1].key = INFINITY;
+    emit_sorted(g, nb, M, pool_out + (int64_t)t * M);
+  }
+  free(g);
+}
+
 /* ------------------------------------------------------------------ stage 4 */
 
 /* ------------------------------------------------------------------ FP8 window rows */

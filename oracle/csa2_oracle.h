@@ -100,6 +100,16 @@ void csa2o_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uin
                             const int64_t *q_base, const int32_t *q_nvis, const int32_t *pool_blocks,
                             int32_t M, int32_t n_q, int32_t width, float *scores);
 
+/* ---- HISA block-mean keys ([ZB] §2.3.4, HISA: block means of the indexer keys as a search
+ * auxiliary; block-level coarse scoring, then token-level scoring of the expanded blocks) --
+ * out[b] (68 B, indexer-K format) = MXFP4 of (fp32 ascending sum of the exact dequantised
+ * keys of entries b*block .. min(b*block+block, n)-1) / count, for b < ceil(n / block). */
+void csa2o_block_mean_pack(const uint8_t *idx_cache, int64_t n_entries, int32_t block, uint8_t *out);
+/* pool = top-M of bscores [n_q, nbw] over the visible blocks, newest visible block forced in,
+ * ties to the lower block, NaN as -inf; ascending, -1 padded (pool_out [n_q, M]). */
+void csa2o_pool_from_block_scores(const float *bscores, int32_t n_q, int32_t nbw, const int32_t *q_nvis,
+                                  int32_t block, int32_t M, int32_t *pool_out);
+
 /* ---- FP8 window rows (the sliding-window KV kept in FP8: [ZB] §2.4.4, [SR] "FP4 Main
  * KV Cache"; the 584-byte FP8 KV entry of [ZB] §3.1 and [DF] §4.6) ------------------------
  * row: [0,448) E4M3 codes of channels 0..447 | [448,576) BF16 bits of channels 448..511 |
