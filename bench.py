@@ -127,10 +127,11 @@ class Decode1M:
     it, attend) and Reuse layers (attend with the Reindex indices)."""
 
     def __init__(self, torch, csa2, tokens, n_seq=4, m=2, K=512, M=2048, ncopy=NCOPY, extra_layers=0,
-                 fp8_window=False, fp4q=False):
+                 fp8_window=False, fp4q=False, hisa=False):
         self.torch, self.csa2 = torch, csa2
         self.fp8 = fp8_window
         self.fp4q = fp4q
+        self.hisa = hisa
         self.n_seq, self.m, self.tokens, self.K, self.M, self.ncopy = n_seq, m, tokens, K, M, ncopy
         self.extra = extra_layers
         n = self.n = tokens // m
@@ -161,6 +162,20 @@ class Decode1M:
         self.n_stages = 4 + (2 + extra_layers if extra_layers else 0)
         if fp4q:  # the step packs the layer's bf16 indexer query into MXFP4 records, then scores
             self.q_fp4 = torch.empty((n_seq, 32, 68), dtype=torch.uint8, device=dev)
+        if hisa:
+            # HISA: every batch copy keeps the block-mean records of its caches; a step re-packs
+            # the newest block of each sequence, scores the block means, keeps the top-M blocks,
+            # then scores their entries and takes the Top-K inside them
+            self.nbw = (n + 7) // 8
+            self.mbase = (torch.arange(n_seq, dtype=torch.int64, device=dev) * self.nbw).contiguous()
+            self.nb_vis = torch.full((n_seq,), self.nbw, dtype=torch.int32, device=dev)
+            self.newest_block = torch.full((n_seq,), (n - 1) // 8, dtype=torch.int32, device=dev)
+            self.s_blk = torch.empty((n_seq, self.nbw), dtype=torch.float32, device=dev)
+            self.scores_c = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
+            for c in self.copies:
+                c["means"] = torch.empty((n_seq * self.nbw, 68), dtype=torch.uint8, device=dev)
+                csa2.block_mean_pack(c["ix"], self.q_base, self.q_nvis, self.nbw, c["means"], self.mbase)
+            torch.cuda.synchronize()
         if fp8_window:
             # per-sequence FP8 window rings of 128 rows; each step packs the newest token's
             # row into its slot, then attends over the ring (oldest row first)
@@ -182,6 +197,18 @@ class Decode1M:
         if st == 0:  # the newest entry of every sequence from its two latest latents
             csa2.compress_pack(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"], self.cs_new[ci],
                                c["w_idx"], kv_out=self.new_kv[ci], idx_out=self.new_ix[ci])
+        elif st == 1 and self.hisa:
+            csa2.block_mean_pack(c["ix"], self.q_base, self.q_nvis, 1, c["means"], self.mbase,
+                                 first_block=self.newest_block)
+            csa2.index_score(c["q_idx"], c["head_w"], c["means"], self.mbase, self.nb_vis, self.nbw,
+                             scores=self.s_blk, want_block_max=False)
+        elif st == 2 and self.hisa:
+            csa2.block_topk(None, self.q_nvis, K=self.K, M=self.M, block_max=self.s_blk, pool_out=self.pool,
+                            want_topk=False, workspace=self.ws_sel)
+            csa2.index_score(c["q_idx"], c["head_w"], c["ix"], self.q_base, self.q_nvis, 8 * self.M,
+                             pool_blocks=self.pool, scores=self.scores_c)
+            csa2.block_topk(self.scores_c, self.q_nvis, K=self.K, pool_blocks=self.pool, topk_out=self.topk,
+                            workspace=self.ws_sel)
         elif st == 1 and self.fp4q:
             csa2.quantize_q_mxfp4(c["q_idx"], out=self.q_fp4)
             csa2.index_score_fp4q(self.q_fp4, c["head_w"], c["ix"], self.q_base, self.q_nvis, n, scores=self.scores,
@@ -215,10 +242,12 @@ class Decode1M:
 STAGES = ("compress_newest", "index_score", "block_topk", "sparse_attn")
 
 
-def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3, fp8_window=False, fp4q=False):
+def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3, fp8_window=False, fp4q=False,
+                hisa=False):
     """Whole-step throughput of a secondary decode workload: one HIP graph per batch copy
     holding every stage of the step, replayed `steps` times between two synchronisations."""
-    wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers, fp8_window=fp8_window, fp4q=fp4q)
+    wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers, fp8_window=fp8_window, fp4q=fp4q,
+                  hisa=hisa)
     for i in range(warmup):
         for st in range(wl.n_stages):
             wl.run_stage(i % NCOPY, st)
@@ -244,6 +273,22 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
            "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else ""),
            "window": "FP8 rings (append + attend)" if fp8_window else "bf16",
            "indexer_query": "MXFP4 (packed in the step)" if fp4q else "bf16"}
+    if hisa:
+        # recall of the exact Top-K (the Full layer's, over every entry) by HISA's Top-K, on the
+        # last replayed copy's inputs
+        ci = (steps - 1) % NCOPY
+        hisa_topk = wl.topk.clone()
+        c = wl.copies[ci]
+        csa2.index_score(c["q_idx"], c["head_w"], c["ix"], wl.q_base, wl.q_nvis, wl.n, scores=wl.scores,
+                         block_max=wl.bmax)
+        csa2.block_topk(wl.scores, wl.q_nvis, K=wl.K, M=wl.M, block_max=wl.bmax, pool_out=wl.pool,
+                        topk_out=wl.topk, workspace=wl.ws_sel)
+        torch.cuda.synchronize()
+        a, b = hisa_topk.cpu().numpy(), wl.topk.cpu().numpy()
+        rec = [len(np.intersect1d(a[t][a[t] >= 0], b[t][b[t] >= 0])) / max(1, int((b[t] >= 0).sum()))
+               for t in range(n_seq)]
+        res["layers"] = "Full with HISA selection (block means -> top-2048 blocks -> Top-512 inside)"
+        res["recall_of_exact_topk"] = round(float(np.mean(rec)), 4)
     del graphs, wl
     torch.cuda.empty_cache()
     return res
@@ -522,6 +567,7 @@ def main():
             "decode_token_40layer_1m_b4": time_schedule(torch, csa2),
             "decode_1m_b4_m2_fp8_window": time_decode(torch, csa2, 1 << 20, 4, 2, fp8_window=True),
             "decode_1m_b4_m2_fp4q": time_decode(torch, csa2, 1 << 20, 4, 2, fp4q=True),
+            "decode_1m_b4_m2_hisa": time_decode(torch, csa2, 1 << 20, 4, 2, hisa=True),
             "decode_128k_b16_m1": time_decode(torch, csa2, 131072, 16, 1, extra_layers=4),
             "decode_32k_b4_m1": time_decode(torch, csa2, 32768, 4, 1),
             "tiny_4k_b1_m2": time_decode(torch, csa2, 4096, 1, 2),

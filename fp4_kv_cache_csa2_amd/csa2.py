@@ -31,6 +31,7 @@ _L.csa2_compress_append.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
 _L.csa2_index_score.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_quantize_q_mxfp4.argtypes = [_vp, _i64, _vp, _vp]
 _L.csa2_index_score_fp4q.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+_L.csa2_block_mean_pack.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
 _L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
@@ -44,7 +45,7 @@ _L.csa2_sparse_attn_swa_fp8.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp
 SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_compress_pack", "csa2_compress_append",
            "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
            "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8",
-           "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q")
+           "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q", "csa2_block_mean_pack")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DEFAULT_SCALE = 512 ** -0.5
@@ -205,20 +206,29 @@ def block_topk_workspace(n_q: int, width: int, M: int, K: int) -> int:
 
 
 def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool_blocks=None,
-               want_pool: bool = True, pool_out=None, topk_out=None, workspace=None, stream=None):
-    """(pool [n_q, M] or None, topk [n_q, K]): Full mode when pool_blocks is None."""
+               want_pool: bool = True, pool_out=None, topk_out=None, workspace=None, stream=None,
+               want_topk: bool = True):
+    """(pool [n_q, M] or None, topk [n_q, K] or None): Full mode when pool_blocks is None.
+    want_topk=False is the pool-only mode: the pool from block_max [n_q, nbw] (the caller's
+    block scores); scores may then be None (the row width is 8 * nbw)."""
     _dev(scores, torch.float32, "scores", 2)
     _dev(q_nvis, torch.int32, "q_nvis", 1)
-    _dev(block_max, torch.float32, "block_max")
+    _dev(block_max, torch.float32, "block_max", 2 if scores is None else None)
     _dev(pool_blocks, torch.int32, "pool_blocks", 2)
-    n_q, width = scores.shape
-    dev = scores.device
+    if scores is not None:
+        n_q, width = scores.shape
+        dev = scores.device
+    else:
+        if want_topk or block_max is None:
+            raise ValueError("scores may be None only in pool-only mode (want_topk=False, block_max given)")
+        n_q, width = block_max.shape[0], 8 * block_max.shape[1]
+        dev = block_max.device
     if pool_blocks is not None:
         M = pool_blocks.shape[1]
         want_pool = False
     if pool_out is None and want_pool:
         pool_out = torch.empty((n_q, M), dtype=torch.int32, device=dev)
-    if topk_out is None:
+    if topk_out is None and want_topk:
         topk_out = torch.empty((n_q, K), dtype=torch.int32, device=dev)
     _dev(pool_out, torch.int32, "pool_out")
     _dev(topk_out, torch.int32, "topk_out")
@@ -231,6 +241,23 @@ def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool
         _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(pool_blocks), 8, M, K,
         _ptr(pool_out), _ptr(topk_out), _ptr(workspace), ws_bytes, _stream(stream)))
     return pool_out, topk_out
+
+
+def block_mean_pack(idx_cache, seq_base, seq_n, n_blocks: int, mean_cache, mean_base, first_block=None,
+                    stream=None):
+    """HISA block-mean records of blocks first_block[s] .. + n_blocks - 1 into mean_cache."""
+    for t, name, dt in ((idx_cache, "idx_cache", torch.uint8), (seq_base, "seq_base", torch.int64),
+                        (seq_n, "seq_n", torch.int32), (mean_cache, "mean_cache", torch.uint8),
+                        (mean_base, "mean_base", torch.int64), (first_block, "first_block", torch.int32)):
+        _dev(t, dt, name)
+    n_seq = seq_base.numel()
+    if seq_n.numel() != n_seq or mean_base.numel() != n_seq or (first_block is not None and
+                                                                first_block.numel() != n_seq):
+        raise ValueError("seq_base, seq_n, mean_base and first_block need one element per sequence")
+    _check("csa2_block_mean_pack", _L.csa2_block_mean_pack(
+        _ptr(idx_cache), _ptr(seq_base), _ptr(seq_n), _ptr(first_block), n_seq, n_blocks, _ptr(mean_cache),
+        _ptr(mean_base), _stream(stream)))
+    return mean_cache
 
 
 def sparse_attn_workspace(n_q: int, K: int) -> int:

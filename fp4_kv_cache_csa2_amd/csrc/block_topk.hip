@@ -422,7 +422,7 @@ __device__ __forceinline__ Row make_row(int t, bool cand, const float* scores, c
                                         const int32_t* q_nvis, const int32_t* pool_blocks, int32_t M, int32_t K) {
   Row r;
   r.cand = cand;
-  r.scores = scores + (int64_t)t * width;
+  r.scores = scores ? scores + (int64_t)t * width : nullptr;  // NULL in pool-only mode
   const int32_t nbw = (width + kBlock - 1) / kBlock;
   r.bm = bm ? bm + (int64_t)t * nbw : nullptr;
   r.pool = cand ? pool_blocks + (int64_t)t * M : nullptr;
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
 constexpr int kItemsPerLane = kSlice / kGThreads;
 
 __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
-    bool cand, bool want_pool, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
+    bool cand, bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
   __shared__ int32_t s_wave[kGThreads / 64];
   __shared__ int32_t s_cnt[2][kGThreads / 64];
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
   const int total = tot_i;
   // list A is needed when the selection does not take every item
   const int kA = cand ? min(K, total) : ((want_pool && total > M - 1) ? M - 1 : 0);
-  const int kB = (!cand && total >= K) ? K : 0;  // 0: every older block is a candidate
+  const int kB = (!cand && want_topk && total >= K) ? K : 0;  // 0: every older block is a candidate
   {
     uint32_t above = (uint32_t)(total - before) - local;  // keys in bins above this thread's range
 #pragma unroll
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
     ob += __popcll(bb[j]);
   }
   if (tid == 0) ws.cnt_a[(int64_t)t * G + g] = na;
-  if (cand) return;
+  if (cand || !want_topk) return;  // pool-only mode needs no list B
   __syncthreads();
   // ---- list B: of every candidate block, the entries whose keys reach the floor, in
   // order.  Slots (8 per block) go in chunks of 1024: wave w scores slots 256w .. 256w+255
@@ -689,12 +689,12 @@ struct FinShared {
 // matching histogram, returns it to zero, gathers its list (a superset of the selection
 // in ascending id order) and refines the boundary bin's low 20 bits over it.
 __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
-    bool cand, bool want_pool, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
+    bool cand, bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws,
     int32_t* __restrict__ pool_out, int32_t* __restrict__ topk_out) {
   __shared__ FinShared sh;
   const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int role = (cand || !want_pool) ? 1 : (int)blockIdx.x;
+  const int role = !want_topk ? 0 : ((cand || !want_pool) ? 1 : (int)blockIdx.x);
   const int G = ws.G;
   Row r = make_row(t, cand, scores, bm, width, q_nvis, pool_blocks, M, K);
   // the list, its histogram and the rank wanted.  Roles on list A use K1's histogram; the
@@ -893,8 +893,10 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
   if (block != kBlock || M < 1 || M > kMaxPool || K < 1 || K > kMaxTopK) return CSA2_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
-  if (!scores || !q_nvis || !topk_out) return CSA2_ERR_INVALID_ARG;
   const bool cand = pool_blocks != nullptr;
+  const bool want_topk = topk_out != nullptr;
+  // pool-only mode (no Top-K): the pool from the caller's block scores; scores may be NULL
+  if (!q_nvis || (want_topk ? !scores : (cand || !pool_out || !block_max))) return CSA2_ERR_INVALID_ARG;
   if (cand && (pool_out || block_max || (int64_t)width != 8LL * M)) return CSA2_ERR_INVALID_ARG;
   if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(block_max) |
@@ -923,11 +925,11 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
                      q_nvis, pool_blocks, M, K, ws);
   int st = check_launch();
   if (st != CSA2_OK) return st;
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, want_pool, scores, bm,
-                     width, q_nvis, pool_blocks, M, K, ws);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, want_pool, want_topk, scores,
+                     bm, width, q_nvis, pool_blocks, M, K, ws);
   st = check_launch();
   if (st != CSA2_OK) return st;
-  hipLaunchKernelGGL(topk_final_kernel, dim3((!cand && want_pool) ? 2 : 1, n_q), dim3(kFThreads), 0, s, cand,
-                     want_pool, scores, bm, width, q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
+  hipLaunchKernelGGL(topk_final_kernel, dim3((!cand && want_pool && want_topk) ? 2 : 1, n_q), dim3(kFThreads), 0, s,
+                     cand, want_pool, want_topk, scores, bm, width, q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
   return check_launch();
 }

@@ -190,10 +190,37 @@ int csa2_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8
  *   longer than 2^20 blocks), WORKSPACE (workspace missing or too small).
  */
 size_t csa2_block_topk_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K);
+/*   Pool-only mode (topk_out == NULL, Full mode): the pool alone, built from the caller's
+ *   block scores in block_max ([n_q, ceil(width/8)], required) by the same rules (top M-1
+ *   older blocks plus the forced newest block); scores may be NULL; K must still be in
+ *   range.  HISA's coarse filter uses it with the scores of its block means. */
 int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, int32_t width,
                     const int32_t *q_nvis, const int32_t *pool_blocks, int32_t block,
                     int32_t M, int32_t K, int32_t *pool_out, int32_t *topk_out,
                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * csa2_block_mean_pack -- HISA's block-mean indexer keys.
+ *   [ZB] §2.3.4 (the HISA paragraphs): the prefix is cut into blocks of consecutive
+ *   entries; every block keeps the mean of its indexer keys as an auxiliary for the search,
+ *   updated for the newest block only while decoding; the block means are scored with the
+ *   same indexer query and head weights and the best blocks expanded for token-level
+ *   scoring.  Record b of sequence s, for the entries e = 8b .. min(8b + 8, n_s) - 1 at cache
+ *   rows seq_base[s] + e: the fp32 sum of their exact dequantised keys in ascending order,
+ *   divided once (IEEE) by their count, packed in the indexer-K format (68 B, MXFP4 rules
+ *   of csa2_compress_pack).  Bit-exact.
+ *   idx_cache: indexer-K rows (4-byte aligned); seq_base int64 [n_seq], seq_n int32 [n_seq]
+ *   (entries of sequence s); first_block: NULL (0) or int32 [n_seq]; the call writes blocks
+ *   first_block[s] .. first_block[s] + n_blocks - 1 that hold at least one entry, to
+ *   mean_cache rows mean_base[s] + b (int64 [n_seq]; mean_cache 4-byte aligned).  A decode
+ *   step passes first_block = (n_s - 1) / 8 and n_blocks = 1.  Scoring the block means is
+ *   csa2_index_score over mean_cache with q_nvis = ceil(n / 8); the pool is csa2_block_topk's
+ *   pool-only mode on those scores; the final Top-K is candidate mode inside it.
+ *   Errors: INVALID_ARG (NULL, negative counts, misalignment), UNSUPPORTED (n_seq > 65535).
+ */
+int csa2_block_mean_pack(const uint8_t *idx_cache, const int64_t *seq_base, const int32_t *seq_n,
+                         const int32_t *first_block, int32_t n_seq, int32_t n_blocks,
+                         uint8_t *mean_cache, const int64_t *mean_base, void *stream);
 
 /*
  * csa2_sparse_attn -- sparse latent attention over the selected FP4 entries joined with

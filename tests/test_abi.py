@@ -114,3 +114,25 @@ def test_fp4_query_entry_points_validate_before_launch(lib):
     assert score(ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, fake, None, 0, 1, 100, fake, None, None) == -1
     assert score(fake, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake, None, 0, 1, 100, fake, None, None) == -1
     assert score(fake, fake, fake, fake, fake, None, 0, 0, 100, fake, None, None) == 0
+
+
+def test_hisa_entry_points_validate_before_launch(lib):
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.csa2_block_mean_pack.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
+    lib.csa2_block_topk.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    mean = lib.csa2_block_mean_pack
+    assert mean(fake, fake, fake, None, -1, 4, fake, fake, None) == -1
+    assert mean(fake, fake, fake, None, 2, -1, fake, fake, None) == -1
+    assert mean(fake, fake, fake, None, 0, 4, fake, fake, None) == 0
+    assert mean(None, fake, fake, None, 2, 4, fake, fake, None) == -1
+    assert mean(fake, fake, fake, None, 2, 4, None, fake, None) == -1
+    assert mean(ctypes.c_void_p((1 << 20) + 2), fake, fake, None, 2, 4, fake, fake, None) == -1
+    assert mean(fake, fake, fake, None, 70000, 4, fake, fake, None) == -2
+    topk = lib.csa2_block_topk
+    # pool-only mode needs block scores and a pool output; scores may be NULL
+    assert topk(None, None, 1, 800, fake, None, 8, 64, 16, fake, None, fake, 1 << 20, None) == -1
+    assert topk(None, fake, 1, 800, fake, None, 8, 64, 16, None, None, fake, 1 << 20, None) == -1
+    assert topk(None, fake, 1, 800, fake, fake, 8, 64, 16, None, None, fake, 1 << 20, None) == -1
+    assert topk(None, fake, 1, 800, fake, None, 8, 64, 16, fake, fake, fake, 1 << 20, None) == -1  # Top-K needs scores
+    assert topk(None, fake, 1, 800, fake, None, 8, 64, 16, fake, None, None, 0, None) == -3
