@@ -13,16 +13,17 @@
 
 #pragma clang fp contract(off)
 
+#ifndef CSA2_FEW_OUT
+#define CSA2_FEW_OUT 32  // indexer outputs per workgroup in the few-entry kernel
+#endif
+
 namespace csa2 {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWChunk = 64;  // channels of W_idx staged per step
 
-// kEnt entries per workgroup: 16 amortises the W_idx reads over many entries; 2 keeps one
-// fma chain per thread for the few-entry appends of a decode step.  There the whole of
-// W_idx (128 KB) is copied into LDS at kernel entry by direct-to-LDS loads, one 1 KB row
-// per wave instruction (coalesced, no registers), overlapping phase A.
+// Bulk packing: kEnt entries per workgroup amortise the W_idx reads over many entries.
 template <int kEnt>
 __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
@@ -30,251 +31,154 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     uint8_t* __restrict__ idx_out, const int64_t* __restrict__ dst_rows) {
   __shared__ float s_c[kEnt][kD];          // rotated fp32 entries
   __shared__ float s_k[kEnt][kIdxDim];     // projected indexer keys
-  constexpr bool kDirect = kEnt == 2;
-  constexpr int kWRow = kD + 8;  // bf16 per W_idx row in LDS (1040 B: conflict-free row reads)
-  __shared__ uint16_t s_w[kDirect ? 1 : 2][kWChunk][kIdxDim + 8];  // W_idx^T chunks (bf16 bits)
-  __shared__ __attribute__((aligned(16))) uint16_t s_wl[kDirect ? kIdxDim * kWRow : 8];  // all of W_idx
+  __shared__ uint16_t s_w[2][kWChunk][kIdxDim + 8];  // W_idx^T chunks (bf16 bits)
   const int t = threadIdx.x;
   const int64_t j0 = (int64_t)blockIdx.x * kEnt;
   // cache row that entry j is written to (a negative row drops the entry)
   auto out_row = [&](int64_t j) -> int64_t { return dst_rows != nullptr ? dst_rows[j] : j; };
-  constexpr int kRowPieces = kD / 8;  // a W_idx row as 64 pieces of 8 bf16
-  if constexpr (kDirect) {
-    const int lane = t & 63, wave = t >> 6;
-    for (int r = wave; r < kIdxDim; r += kThreads / 64)
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(w_idx + (int64_t)r * kD + 8 * lane),
-          (void __attribute__((address_space(3)))*)&s_wl[r * kWRow], 16, 0, 0);
-  }
-
   // ---- phase A: pooling, RoPE, main-KV pack
-  if constexpr (kDirect) {
-    // thread -> (entry t / 128, channels 4q .. 4q+3, q = t % 128); the 4 threads of a
-    // 16-channel group share their amax through lane shuffles
-    const int e = t >> 7, q = t & 127, ch0 = 4 * q;
-    const int64_t j = j0 + e;
-    const bool live = j < n_entries;
-    const int64_t jr = live ? j : j0;  // rows read by a padding thread stay in bounds
-    float c[4];
+  // thread -> (entry e, channels 32p..32p+31)
+  const int e = t >> 4, p = t & 15;
+  const int64_t j = j0 + e;
+  if (e < kEnt && j < n_entries) {
+    float c[32];
+    const int ch0 = 32 * p;
     if (m == 1) {
-      const uint2 u = *reinterpret_cast<const uint2*>(latent + jr * kD + ch0);
-      c[0] = bf16_bits_to_f32(u.x & 0xFFFFu);
-      c[1] = bf16_bits_to_f32(u.x >> 16);
-      c[2] = bf16_bits_to_f32(u.y & 0xFFFFu);
-      c[3] = bf16_bits_to_f32(u.y >> 16);
-    } else {
-      // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
-      const uint2 u0 = *reinterpret_cast<const uint2*>(latent + (2 * jr) * kD + ch0);
-      const uint2 u1 = *reinterpret_cast<const uint2*>(latent + (2 * jr + 1) * kD + ch0);
-      const uint32_t xa[4] = {u0.x & 0xFFFFu, u0.x >> 16, u0.y & 0xFFFFu, u0.y >> 16};
-      const uint32_t xb[4] = {u1.x & 0xFFFFu, u1.x >> 16, u1.y & 0xFFFFu, u1.y >> 16};
+      const uint4* src = reinterpret_cast<const uint4*>(latent + j * kD + ch0);
 #pragma unroll
       for (int v = 0; v < 4; v++) {
-        const float w0 = pool_w[ch0 + v], w1 = pool_w[kD + ch0 + v];
-        const float ws = w0 + w1;
-        const float a0 = w0 / ws, a1 = w1 / ws;
-        const float p0 = a0 * bf16_bits_to_f32(xa[v]);
-        const float p1 = a1 * bf16_bits_to_f32(xb[v]);
-        c[v] = p0 + p1;
+        const uint4 u = src[v];
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          c[8 * v + 2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
+          c[8 * v + 2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
+        }
+      }
+    } else {
+      // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
+      const uint4* s0 = reinterpret_cast<const uint4*>(latent + (2 * j) * kD + ch0);
+      const uint4* s1 = reinterpret_cast<const uint4*>(latent + (2 * j + 1) * kD + ch0);
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const uint4 u0 = s0[v], u1 = s1[v];
+        const uint32_t a4[4] = {u0.x, u0.y, u0.z, u0.w};
+        const uint32_t b4[4] = {u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+          const int ch = ch0 + 8 * v + q;
+          const float w0 = pool_w[ch], w1 = pool_w[kD + ch];
+          const float ws = w0 + w1;
+          const float a0 = w0 / ws, a1 = w1 / ws;
+          const uint32_t xa = (q & 1) ? (a4[q >> 1] >> 16) : (a4[q >> 1] & 0xFFFFu);
+          const uint32_t xb = (q & 1) ? (b4[q >> 1] >> 16) : (b4[q >> 1] & 0xFFFFu);
+          const float p0 = a0 * bf16_bits_to_f32(xa);
+          const float p1 = a1 * bf16_bits_to_f32(xb);
+          c[8 * v + q] = p0 + p1;
+        }
       }
     }
-    if (ch0 >= kDNope) {  // rope tail: pairs (448+2i, 449+2i)
-      const float* cs = rope_cs + jr * kDRope;
+    if (p >= kDNope / 32) {  // rope tail: pairs (448+2i, 449+2i)
+      const float* cs = rope_cs + j * kDRope;
       const int i0 = (ch0 - kDNope) / 2;
 #pragma unroll
-      for (int v = 0; v < 2; v++) {
-        const float x0 = c[2 * v], x1 = c[2 * v + 1];
-        const float co = cs[i0 + v], si = cs[kDRope / 2 + i0 + v];
+      for (int q = 0; q < 16; q++) {
+        const float x0 = c[2 * q], x1 = c[2 * q + 1];
+        const float co = cs[i0 + q], si = cs[kDRope / 2 + i0 + q];
         const float t0 = x0 * co, t1 = x1 * si, t2 = x0 * si, t3 = x1 * co;
-        c[2 * v] = t0 - t1;
-        c[2 * v + 1] = t2 + t3;
+        c[2 * q] = t0 - t1;
+        c[2 * q + 1] = t2 + t3;
       }
     }
 #pragma unroll
-    for (int v = 0; v < 4; v++) s_c[e][ch0 + v] = c[v];
-    float amax = 0.0f;
+    for (int q = 0; q < 32; q++) s_c[e][ch0 + q] = c[q];
+
+    // two groups of 16 channels: E4M3 scale + E2M1 codes
+    uint32_t pay[4];
+    uint32_t scl = 0;
 #pragma unroll
-    for (int v = 0; v < 4; v++) amax = __builtin_fmaxf(amax, __builtin_fabsf(c[v]));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
-    const uint32_t sb = e4m3_encode(amax / 6.0f);
-    const float S = e4m3_value(sb);
-    uint32_t half = 0;
+    for (int g = 0; g < 2; g++) {
+      float amax = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 4; v++) half |= e2m1_encode(c[v], S) << (4 * v);
-    const int64_t row = live ? out_row(j) : -1;
+      for (int q = 0; q < 16; q++) amax = __builtin_fmaxf(amax, __builtin_fabsf(c[16 * g + q]));
+      const uint32_t sb = e4m3_encode(amax / 6.0f);
+      const float S = e4m3_value(sb);
+      scl |= sb << (8 * g);
+#pragma unroll
+      for (int w = 0; w < 2; w++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 8; q++) word |= e2m1_encode(c[16 * g + 8 * w + q], S) << (4 * q);
+        pay[2 * g + w] = word;
+      }
+    }
+    const int64_t row = out_row(j);
     if (row >= 0) {
       uint8_t* dst = kv_out + row * kKvBytes;
-      *reinterpret_cast<uint16_t*>(dst + 2 * q) = (uint16_t)half;
-      if ((q & 3) == 0) dst[256 + (q >> 2)] = (uint8_t)sb;
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's W_idx rows have landed in LDS
-  } else {
-    // thread -> (entry e, channels 32p..32p+31)
-    const int e = t >> 4, p = t & 15;
-    const int64_t j = j0 + e;
-    if (e < kEnt && j < n_entries) {
-      float c[32];
-      const int ch0 = 32 * p;
-      if (m == 1) {
-        const uint4* src = reinterpret_cast<const uint4*>(latent + j * kD + ch0);
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-          const uint4 u = src[v];
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            c[8 * v + 2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
-            c[8 * v + 2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
-          }
-        }
-      } else {
-        // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
-        const uint4* s0 = reinterpret_cast<const uint4*>(latent + (2 * j) * kD + ch0);
-        const uint4* s1 = reinterpret_cast<const uint4*>(latent + (2 * j + 1) * kD + ch0);
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-          const uint4 u0 = s0[v], u1 = s1[v];
-          const uint32_t a4[4] = {u0.x, u0.y, u0.z, u0.w};
-          const uint32_t b4[4] = {u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-          for (int q = 0; q < 8; q++) {
-            const int ch = ch0 + 8 * v + q;
-            const float w0 = pool_w[ch], w1 = pool_w[kD + ch];
-            const float ws = w0 + w1;
-            const float a0 = w0 / ws, a1 = w1 / ws;
-            const uint32_t xa = (q & 1) ? (a4[q >> 1] >> 16) : (a4[q >> 1] & 0xFFFFu);
-            const uint32_t xb = (q & 1) ? (b4[q >> 1] >> 16) : (b4[q >> 1] & 0xFFFFu);
-            const float p0 = a0 * bf16_bits_to_f32(xa);
-            const float p1 = a1 * bf16_bits_to_f32(xb);
-            c[8 * v + q] = p0 + p1;
-          }
-        }
-      }
-      if (p >= kDNope / 32) {  // rope tail: pairs (448+2i, 449+2i)
-        const float* cs = rope_cs + j * kDRope;
-        const int i0 = (ch0 - kDNope) / 2;
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-          const float x0 = c[2 * q], x1 = c[2 * q + 1];
-          const float co = cs[i0 + q], si = cs[kDRope / 2 + i0 + q];
-          const float t0 = x0 * co, t1 = x1 * si, t2 = x0 * si, t3 = x1 * co;
-          c[2 * q] = t0 - t1;
-          c[2 * q + 1] = t2 + t3;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 32; q++) s_c[e][ch0 + q] = c[q];
-
-      // two groups of 16 channels: E4M3 scale + E2M1 codes
-      uint32_t pay[4];
-      uint32_t scl = 0;
-#pragma unroll
-      for (int g = 0; g < 2; g++) {
-        float amax = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 16; q++) amax = __builtin_fmaxf(amax, __builtin_fabsf(c[16 * g + q]));
-        const uint32_t sb = e4m3_encode(amax / 6.0f);
-        const float S = e4m3_value(sb);
-        scl |= sb << (8 * g);
-#pragma unroll
-        for (int w = 0; w < 2; w++) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int q = 0; q < 8; q++) word |= e2m1_encode(c[16 * g + 8 * w + q], S) << (4 * q);
-          pay[2 * g + w] = word;
-        }
-      }
-      const int64_t row = out_row(j);
-      if (row >= 0) {
-        uint8_t* dst = kv_out + row * kKvBytes;
-        *reinterpret_cast<uint4*>(dst + 16 * p) = make_uint4(pay[0], pay[1], pay[2], pay[3]);
-        *reinterpret_cast<uint16_t*>(dst + 256 + 2 * p) = (uint16_t)scl;
-      }
+      *reinterpret_cast<uint4*>(dst + 16 * p) = make_uint4(pay[0], pay[1], pay[2], pay[3]);
+      *reinterpret_cast<uint16_t*>(dst + 256 + 2 * p) = (uint16_t)scl;
     }
   }
-  __syncthreads();
+    __syncthreads();
 
   // ---- phase B: indexer projection k[o] = sum_ch W[o][ch] c~[ch], ascending fma chain.
-  if constexpr (kDirect) {
-    // thread -> output o = t % 128 of entry t / 128, its W_idx row read from LDS
-    const int o = t & (kIdxDim - 1), e = t >> 7;
-    float a = 0.0f;
-#pragma unroll 8
-    for (int v = 0; v < kRowPieces; v++) {
-      const uint4 wv = *reinterpret_cast<const uint4*>(&s_wl[o * kWRow + 8 * v]);
-      const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-      const float4 c0 = *reinterpret_cast<const float4*>(&s_c[e][8 * v]);
-      const float4 c1 = *reinterpret_cast<const float4*>(&s_c[e][8 * v + 4]);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] & 0xFFFFu), c0.x, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] >> 16), c0.y, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] & 0xFFFFu), c0.z, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] >> 16), c0.w, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] & 0xFFFFu), c1.x, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] >> 16), c1.y, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] & 0xFFFFu), c1.z, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] >> 16), c1.w, a);
+  // thread -> output o, entries h*kHalf .. h*kHalf + kHalf - 1.  W_idx streams through
+  // LDS in transposed chunks of 64 channels ([ch][o], double-buffered) so every chain
+  // step reads its weight from LDS without bank conflicts and no step waits on global
+  // memory.
+  constexpr int kHalf = kEnt / 2;
+  const int o = t & (kIdxDim - 1), h = t >> 7;
+  float acc[kHalf];
+#pragma unroll
+  for (int e = 0; e < kHalf; e++) acc[e] = 0.0f;
+  uint4 stage[4];
+  auto fetch = [&](int chunk) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int u = t + kThreads * q;  // 1024 pieces of 8 bf16: row u/8, part u%8
+      stage[q] = *reinterpret_cast<const uint4*>(w_idx + (int64_t)(u >> 3) * kD + kWChunk * chunk + 8 * (u & 7));
     }
-    s_k[e][o] = a;
-  } else {
-    // thread -> output o, entries h*kHalf .. h*kHalf + kHalf - 1.  W_idx streams through
-    // LDS in transposed chunks of 64 channels ([ch][o], double-buffered) so every chain
-    // step reads its weight from LDS without bank conflicts and no step waits on global
-    // memory.
-    constexpr int kHalf = kEnt / 2;
-    const int o = t & (kIdxDim - 1), h = t >> 7;
-    float acc[kHalf];
+  };
+  auto spill = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < kHalf; e++) acc[e] = 0.0f;
-    uint4 stage[4];
-    auto fetch = [&](int chunk) {
+    for (int q = 0; q < 4; q++) {
+      const int u = t + kThreads * q, row = u >> 3, part = u & 7;
+      const uint32_t w4[4] = {stage[q].x, stage[q].y, stage[q].z, stage[q].w};
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int u = t + kThreads * q;  // 1024 pieces of 8 bf16: row u/8, part u%8
-        stage[q] = *reinterpret_cast<const uint4*>(w_idx + (int64_t)(u >> 3) * kD + kWChunk * chunk + 8 * (u & 7));
+      for (int v = 0; v < 4; v++) {
+        s_w[buf][8 * part + 2 * v][row] = (uint16_t)(w4[v] & 0xFFFFu);
+        s_w[buf][8 * part + 2 * v + 1][row] = (uint16_t)(w4[v] >> 16);
       }
-    };
-    auto spill = [&](int buf) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int u = t + kThreads * q, row = u >> 3, part = u & 7;
-        const uint32_t w4[4] = {stage[q].x, stage[q].y, stage[q].z, stage[q].w};
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-          s_w[buf][8 * part + 2 * v][row] = (uint16_t)(w4[v] & 0xFFFFu);
-          s_w[buf][8 * part + 2 * v + 1][row] = (uint16_t)(w4[v] >> 16);
-        }
-      }
-    };
-    fetch(0);
-    spill(0);
-    __syncthreads();
-    for (int chunk = 0; chunk < kD / kWChunk; chunk++) {
-      const int buf = chunk & 1;
-      if (chunk + 1 < kD / kWChunk) fetch(chunk + 1);
-#pragma unroll 2
-      for (int cb = 0; cb < kWChunk; cb += 4) {
-        float wf[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) wf[q] = bf16_bits_to_f32(s_w[buf][cb + q][o]);
-#pragma unroll
-        for (int e = 0; e < kHalf; e++) {
-          const float4 cv = *reinterpret_cast<const float4*>(&s_c[kHalf * h + e][kWChunk * chunk + cb]);
-          float a = acc[e];
-          a = __builtin_fmaf(wf[0], cv.x, a);
-          a = __builtin_fmaf(wf[1], cv.y, a);
-          a = __builtin_fmaf(wf[2], cv.z, a);
-          a = __builtin_fmaf(wf[3], cv.w, a);
-          acc[e] = a;
-        }
-      }
-      if (chunk + 1 < kD / kWChunk) spill(buf ^ 1);
-      __syncthreads();
     }
-#pragma unroll
-    for (int e = 0; e < kHalf; e++) s_k[kHalf * h + e][o] = acc[e];
-  }
+  };
+  fetch(0);
+  spill(0);
   __syncthreads();
+  for (int chunk = 0; chunk < kD / kWChunk; chunk++) {
+    const int buf = chunk & 1;
+    if (chunk + 1 < kD / kWChunk) fetch(chunk + 1);
+#pragma unroll 2
+    for (int cb = 0; cb < kWChunk; cb += 4) {
+      float wf[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) wf[q] = bf16_bits_to_f32(s_w[buf][cb + q][o]);
+#pragma unroll
+      for (int e = 0; e < kHalf; e++) {
+        const float4 cv = *reinterpret_cast<const float4*>(&s_c[kHalf * h + e][kWChunk * chunk + cb]);
+        float a = acc[e];
+        a = __builtin_fmaf(wf[0], cv.x, a);
+        a = __builtin_fmaf(wf[1], cv.y, a);
+        a = __builtin_fmaf(wf[2], cv.z, a);
+        a = __builtin_fmaf(wf[3], cv.w, a);
+        acc[e] = a;
+      }
+    }
+    if (chunk + 1 < kD / kWChunk) spill(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < kHalf; e++) s_k[kHalf * h + e][o] = acc[e];
+    __syncthreads();
 
   // ---- phase C: MXFP4 pack.  4 threads per (entry, group of 32), 8 elements each
   if (t < kEnt * 16) {
@@ -304,6 +208,147 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Few entries (the appends of a decode step): one wave per (entry, kOut consecutive
+// indexer outputs), so each workgroup copies only its kOut rows of W_idx (kOut KB, one
+// direct-to-LDS 1 KB row per instruction, issued first) while it pools, rotates and packs
+// its entry (lane l owns channels 8l .. 8l + 7; the workgroup of outputs 0 .. kOut-1 writes
+// the main-KV entry).  Lane o < kOut then runs output o's 512-step ascending fma chain from
+// LDS, and the kOut outputs (whole MXFP4 groups) are packed by lanes 0 .. kOut/8 - 1.
+template <int kOut>
+__global__ __launch_bounds__(64) void compress_few_kernel(
+    const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
+    const float* __restrict__ rope_cs, const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out,
+    uint8_t* __restrict__ idx_out, const int64_t* __restrict__ dst_rows) {
+  constexpr int kWRow = kD + 8;  // bf16 per W_idx row in LDS (1040 B: rows start 4 banks apart)
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[kOut * kWRow];
+  __shared__ __attribute__((aligned(16))) float s_c[kD];
+  __shared__ float s_k[kOut];
+  const int lane = threadIdx.x;
+  const int64_t j = blockIdx.x;
+  const int o0 = blockIdx.y * kOut;
+  for (int r = 0; r < kOut; r++)
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(w_idx + (int64_t)(o0 + r) * kD + 8 * lane),
+        (void __attribute__((address_space(3)))*)&s_w[r * kWRow], 16, 0, 0);
+  const int64_t row = dst_rows != nullptr ? dst_rows[j] : j;
+
+  // ---- pooling, RoPE, main-KV pack (lane owns channels ch0 .. ch0 + 7)
+  const int ch0 = 8 * lane;
+  float c[8];
+  if (m == 1) {
+    const uint4 u = *reinterpret_cast<const uint4*>(latent + j * kD + ch0);
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      c[2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
+      c[2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
+    }
+  } else {
+    // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
+    const uint4 u0 = *reinterpret_cast<const uint4*>(latent + (2 * j) * kD + ch0);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(latent + (2 * j + 1) * kD + ch0);
+    typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));  // pool_w is 4-byte aligned
+    const f32x4_a4 wa0 = *reinterpret_cast<const f32x4_a4*>(pool_w + ch0);
+    const f32x4_a4 wa1 = *reinterpret_cast<const f32x4_a4*>(pool_w + ch0 + 4);
+    const f32x4_a4 wb0 = *reinterpret_cast<const f32x4_a4*>(pool_w + kD + ch0);
+    const f32x4_a4 wb1 = *reinterpret_cast<const f32x4_a4*>(pool_w + kD + ch0 + 4);
+    const float w0[8] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w};
+    const float w1[8] = {wb0.x, wb0.y, wb0.z, wb0.w, wb1.x, wb1.y, wb1.z, wb1.w};
+    const uint32_t xa[4] = {u0.x, u0.y, u0.z, u0.w}, xb[4] = {u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const float ws = w0[q] + w1[q];
+      const float a0 = w0[q] / ws, a1 = w1[q] / ws;
+      const uint32_t ba = (q & 1) ? (xa[q >> 1] >> 16) : (xa[q >> 1] & 0xFFFFu);
+      const uint32_t bb = (q & 1) ? (xb[q >> 1] >> 16) : (xb[q >> 1] & 0xFFFFu);
+      const float p0 = a0 * bf16_bits_to_f32(ba);
+      const float p1 = a1 * bf16_bits_to_f32(bb);
+      c[q] = p0 + p1;
+    }
+  }
+  if (ch0 >= kDNope) {  // rope tail: pairs (448+2i, 449+2i)
+    const float* cs = rope_cs + j * kDRope;
+    const int i0 = (ch0 - kDNope) / 2;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float x0 = c[2 * q], x1 = c[2 * q + 1];
+      const float co = cs[i0 + q], si = cs[kDRope / 2 + i0 + q];
+      const float t0 = x0 * co, t1 = x1 * si, t2 = x0 * si, t3 = x1 * co;
+      c[2 * q] = t0 - t1;
+      c[2 * q + 1] = t2 + t3;
+    }
+  }
+  *reinterpret_cast<float4*>(&s_c[ch0]) = make_float4(c[0], c[1], c[2], c[3]);
+  *reinterpret_cast<float4*>(&s_c[ch0 + 4]) = make_float4(c[4], c[5], c[6], c[7]);
+  if (o0 == 0) {  // one workgroup per entry writes its main-KV bytes
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; q++) amax = __builtin_fmaxf(amax, __builtin_fabsf(c[q]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));  // the 2 lanes of a 16-channel group
+    const uint32_t sb = e4m3_encode(amax / 6.0f);
+    const float S = e4m3_value(sb);
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 8; q++) word |= e2m1_encode(c[q], S) << (4 * q);
+    if (row >= 0) {
+      uint8_t* dst = kv_out + row * kKvBytes;
+      *reinterpret_cast<uint32_t*>(dst + 4 * lane) = word;
+      if ((lane & 1) == 0) dst[256 + (lane >> 1)] = (uint8_t)sb;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the W_idx rows have landed in LDS
+  __syncthreads();
+
+  // ---- indexer projection: output o0 + lane, one ascending fma chain from +0
+  if (lane < kOut) {
+    float a = 0.0f;
+    const uint16_t* wr = &s_w[lane * kWRow];
+#pragma unroll 8
+    for (int v = 0; v < kD / 8; v++) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(wr + 8 * v);
+      const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+      const float4 c0 = *reinterpret_cast<const float4*>(&s_c[8 * v]);
+      const float4 c1 = *reinterpret_cast<const float4*>(&s_c[8 * v + 4]);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] & 0xFFFFu), c0.x, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] >> 16), c0.y, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] & 0xFFFFu), c0.z, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] >> 16), c0.w, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] & 0xFFFFu), c1.x, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] >> 16), c1.y, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] & 0xFFFFu), c1.z, a);
+      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] >> 16), c1.w, a);
+    }
+    s_k[lane] = a;
+  }
+  __syncthreads();
+
+  // ---- MXFP4 pack of these kOut outputs: 4 lanes per group of 32, 8 outputs each
+  if (lane < kOut / 8) {
+    const int g = lane >> 2, sub = lane & 3;
+    float v[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      v[q] = s_k[32 * g + 8 * sub + q];
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
+    }
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+    const uint32_t code = e8m0_scale_code(amax);
+    const float X = __builtin_ldexpf(1.0f, (int)code - 127);
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 8; q++) word |= e2m1_encode(v[q], X) << (4 * q);
+    if (row >= 0) {
+      const int gg = o0 / 32 + g;  // global group of 32 outputs
+      uint8_t* dst = idx_out + row * kIdxBytes;
+      *reinterpret_cast<uint32_t*>(dst + 16 * gg + 4 * sub) = word;
+      if (sub == 0) dst[64 + gg] = (uint8_t)code;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace csa2
 
@@ -324,9 +369,9 @@ int launch_compress(const uint16_t* latent_bf16, int64_t n_entries, int m, const
       reinterpret_cast<uintptr_t>(dst_rows) & 7)
     return CSA2_ERR_INVALID_ARG;
   if (n_entries <= 64) {
-    hipLaunchKernelGGL(compress_pack_kernel<2>, dim3((unsigned)((n_entries + 1) / 2)), dim3(kThreads), 0,
-                       (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
-                       kv_out, idx_out, dst_rows);
+    hipLaunchKernelGGL(compress_few_kernel<CSA2_FEW_OUT>, dim3((unsigned)n_entries, kIdxDim / CSA2_FEW_OUT), dim3(64),
+                       0, (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16, kv_out,
+                       idx_out, dst_rows);
   } else {
     const int64_t grid = (n_entries + 15) / 16;
     if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;

@@ -38,19 +38,205 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));  // 16 B at an 8-B boundary
 
+constexpr int kMaxKeys = kMaxTopK + kMaxSwa;
+
 struct __attribute__((aligned(16))) AttnShared {
   _Float16 k[kChunk * kKStride] __attribute__((aligned(16)));  // decoded keys, row-major [key][dim]
   _Float16 p[kWaves * 16 * kPStride] __attribute__((aligned(16)));  // per-wave probabilities [head][key]
   int32_t valid[kChunk];
+  int32_t ids[kMaxKeys];  // the workgroup's selected-entry ids, loaded once
 };
 
-// Raw bytes of one key slot for one thread (a quarter of a key: 128 dims).  Selected
-// entries are prefetched a chunk ahead; window rows (bf16, 4x the bytes) load when staged.
+// Raw bytes of one key slot for one thread (a quarter of a key), prefetched a chunk ahead:
+// a selected entry's 64 payload bytes and 8 E4M3 scale bytes, or a window row's quarter
+// (256 bytes of bf16, or 152 bytes of an FP8 row: 112 code bytes, 32 bf16 bytes, the
+// 8-byte scale word).
 struct KeyRaw {
-  uint4 pay[4];   // FP4 payload of a selected entry
-  uint2 scw;      // its 8 E4M3 scale bytes
+  uint4 d[16];
   int kind;       // 0 empty, 1 selected entry, 2 window row
-  int row;        // window row index (kind 2)
+};
+
+// Gather and decode of one query's keys: thread (kk, qq) of a 256-thread workgroup handles
+// quarter qq (dims 128 qq .. 128 qq + 127) of key slot kk of every 64-key chunk.  Keys 0 .. K-1 are the selected entries
+// (topk ids relative to the sequence's first cache row), keys K .. K + nswa - 1 the window
+// rows.  Window rows are bf16 rows, or 584-byte FP8 rows (kFp8Win), read consecutively or
+// from per-sequence rings.
+template <bool kFp8Win>
+struct KeyStager {
+  const uint8_t* kv_cache;
+  const int32_t* topk_row;
+  const int32_t* ids;  // LDS copy of topk_row[x_begin ..] (load_ids)
+  int32_t x_begin;
+  int32_t K;
+  const void* swa_v;
+  int64_t swa_ring;
+  int64_t base, woff, wseg;
+  int32_t nswa;
+  int kk, qq;
+
+  __device__ __forceinline__ KeyStager(const uint8_t* kv_cache_, const int32_t* topk, int32_t K_, const void* swa_v_,
+                                       int64_t swa_ring_, int64_t base_, int64_t swa_start, int32_t swa_len, int tid)
+      : kv_cache(kv_cache_), topk_row(topk), K(K_), swa_v(swa_v_), swa_ring(swa_ring_), base(base_) {
+    nswa = min(max(swa_len, 0), kMaxSwa);
+    // window row r lives at wseg + (woff + r) wrapped into the ring (no ring: wseg + woff + r)
+    woff = swa_start;
+    wseg = 0;
+    if (swa_ring > 0) {
+      woff %= swa_ring;
+      if (woff < 0) woff += swa_ring;
+      wseg = swa_start - woff;
+    }
+    // wave qq stages quarter qq of all 64 keys: consecutive lanes write consecutive key
+    // rows, which start 4 banks apart, so the 16-byte LDS stores of a wave do not conflict
+    kk = tid & 63;
+    qq = tid >> 6;
+    ids = nullptr;
+    x_begin = 0;
+  }
+
+  // copies the selected ids of chunks c_begin .. c_end - 1 into LDS (all threads take part;
+  // the caller synchronises before the first fetch)
+  __device__ __forceinline__ void load_ids(int c_begin, int c_end, AttnShared& sh, int tid) {
+    x_begin = c_begin * kChunk;
+    const int x_end = min(c_end * kChunk, K);
+    for (int x = x_begin + tid; x < x_end; x += kThreads) sh.ids[x - x_begin] = topk_row[x];
+    ids = sh.ids;
+  }
+
+  // buffer row of window row r (wrapped inside the sequence's ring when there is one)
+  __device__ __forceinline__ int64_t window_row(int r) const {
+    int64_t row = woff + r;
+    if (swa_ring > 0 && row >= swa_ring) row -= swa_ring;  // r < 128 <= swa_ring
+    return row + wseg;
+  }
+
+  // raw loads of this thread's key quarter for chunk c
+  __device__ __forceinline__ void fetch(int c, KeyRaw& r) const {
+    const int x = c * kChunk + kk;
+    r.kind = 0;
+    if (x < K) {
+      const int32_t id = ids[x - x_begin];
+      if (id >= 0) {
+        r.kind = 1;
+        const uint8_t* row = kv_cache + (base + id) * kKvBytes;
+#pragma unroll
+        for (int v = 0; v < 4; v++) r.d[v] = reinterpret_cast<const uint4*>(row + 64 * qq)[v];
+        const uint2 sw = *reinterpret_cast<const uint2*>(row + 256 + 8 * qq);
+        r.d[4] = make_uint4(sw.x, sw.y, 0u, 0u);
+      }
+    } else if (x - K < nswa) {
+      r.kind = 2;
+      const int64_t row = window_row(x - K);
+      if constexpr (kFp8Win) {
+        // NoPE codes of dims 112 qq .. 112 qq + 111, RoPE bf16 of dims 448 + 16 qq .. + 15, scales
+        const uint8_t* src = static_cast<const uint8_t*>(swa_v) + row * kSwa8Bytes;
+#pragma unroll
+        for (int j = 0; j < 7; j++) {
+          const u32x4_a8 v = *reinterpret_cast<const u32x4_a8*>(src + 112 * qq + 16 * j);
+          r.d[j] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+          const u32x4_a8 v = *reinterpret_cast<const u32x4_a8*>(src + kDNope + 32 * qq + 16 * j);
+          r.d[7 + j] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+        const uint2 sw = *reinterpret_cast<const uint2*>(src + kDNope + 2 * kDRope);
+        r.d[9] = make_uint4(sw.x, sw.y, 0u, 0u);
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(swa_v) + row * kD + 128 * qq);
+#pragma unroll
+        for (int v = 0; v < 16; v++) r.d[v] = src[v];
+      }
+    }
+  }
+
+  // decode to f16 (exact) and store the key quarter row-major in LDS
+  __device__ __forceinline__ void stage(const KeyRaw& r, AttnShared& sh) const {
+    _Float16* krow = sh.k + kk * kKStride + 128 * qq;
+    if (r.kind == 1) {
+      // v_cvt_scalef32_pk_f16_fp4 applies only a power-of-two scale, so the codes convert
+      // at scale 1 and a packed f16 multiply applies the E4M3 scale (exact: at most 6
+      // significant bits, inside f16's normal range)
+      // the 8 E4M3 scales of this quarter as f16 (every E4M3 value is exact in f16)
+      f16x2 sc2[4];
+      sc2[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].x, 1.0f, false);
+      sc2[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].x, 1.0f, true);
+      sc2[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].y, 1.0f, false);
+      sc2[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].y, 1.0f, true);
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const uint32_t wd[4] = {r.d[v].x, r.d[v].y, r.d[v].z, r.d[v].w};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+          const int grp = 2 * v + (q4 >> 1);  // local group of 16 dims
+          const _Float16 S = sc2[grp >> 1][grp & 1];
+          const f16x2 S2 = {S, S};
+          const f16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 0) * S2;
+          const f16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 1) * S2;
+          const f16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 2) * S2;
+          const f16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 3) * S2;
+          const f16x8 pk = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+          *reinterpret_cast<f16x8*>(krow + 32 * v + 8 * q4) = pk;
+        }
+      }
+    } else if (r.kind == 2) {
+      if constexpr (kFp8Win) {
+        // this thread decodes NoPE dims 112 qq .. 112 qq + 111 (codes at the same byte
+        // offsets) and RoPE dims 448 + 16 qq .. + 15 (bf16 at bytes 448 + 32 qq)
+        const uint64_t scb = (uint64_t)r.d[9].x | ((uint64_t)r.d[9].y << 32);
+        _Float16* kq = sh.k + kk * kKStride;
+#pragma unroll
+        for (int j = 0; j < 7; j++) {
+          const uint4 c4 = r.d[j];
+          const uint32_t c[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            const int grp = (112 * qq + 16 * j + 8 * h) >> 6;  // scale group of these 8 dims
+            const uint32_t code = (uint32_t)(scb >> (8 * grp)) & 255u;
+            const _Float16 X = (_Float16)__builtin_ldexpf(1.0f, (int)code - 127);
+            const f16x2 X2 = {X, X};
+            const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, false) * X2;
+            const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, true) * X2;
+            const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, false) * X2;
+            const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, true) * X2;
+            const f16x8 pk = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+            *reinterpret_cast<f16x8*>(kq + 112 * qq + 16 * j + 8 * h) = pk;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+          const uint4 u4 = r.d[7 + j];
+          const uint32_t u[4] = {u4.x, u4.y, u4.z, u4.w};
+          f16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            pk[2 * e] = (_Float16)bf16_bits_to_f32(u[e] & 0xFFFFu);
+            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(u[e] >> 16);
+          }
+          *reinterpret_cast<f16x8*>(kq + kDNope + 16 * qq + 8 * j) = pk;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const uint32_t wd[4] = {r.d[v].x, r.d[v].y, r.d[v].z, r.d[v].w};
+          f16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
+            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
+          }
+          *reinterpret_cast<f16x8*>(krow + 8 * v) = pk;
+        }
+      }
+    } else {
+      f16x8 z;
+#pragma unroll
+      for (int e = 0; e < 8; e++) z[e] = (_Float16)0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; v++) *reinterpret_cast<f16x8*>(krow + 8 * v) = z;
+    }
+    if (qq == 0) sh.valid[kk] = r.kind != 0 ? 1 : 0;
+  }
 };
 
 // Window rows: kFp8Win selects 584-byte FP8 rows instead of bf16 rows.
@@ -69,122 +255,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   const int i = lane & 15, g = lane >> 4;
   const int c_begin = split * chunks_per_split;
   const int c_end = min(c_begin + chunks_per_split, n_chunks);
-  const int64_t base = q_base[t];
-  const int32_t nswa = min(max(swa_len[t], 0), kMaxSwa);
-  // window row r lives at wseg + (woff + r) wrapped into the ring (no ring: wseg + woff + r)
-  int64_t woff = swa_start[t], wseg = 0;
-  if (swa_ring > 0) {
-    woff %= swa_ring;
-    if (woff < 0) woff += swa_ring;
-    wseg = swa_start[t] - woff;
-  }
-  const int kk = tid >> 2, qq = tid & 3;  // key slot and quarter this thread decodes
-
-  // raw loads of this thread's key quarter for chunk c
-  auto fetch = [&](int c, KeyRaw& r) {
-    const int x = c * kChunk + kk;
-    r.kind = 0;
-    if (x < K) {
-      const int32_t id = topk[(int64_t)t * K + x];
-      if (id >= 0) {
-        r.kind = 1;
-        const uint8_t* row = kv_cache + (base + id) * kKvBytes;
-#pragma unroll
-        for (int v = 0; v < 4; v++) r.pay[v] = reinterpret_cast<const uint4*>(row + 64 * qq)[v];
-        r.scw = *reinterpret_cast<const uint2*>(row + 256 + 8 * qq);
-      }
-    } else if (x - K < nswa) {
-      r.kind = 2;
-      r.row = x - K;
-    }
-  };
-  // decode to f16 (exact) and store the key quarter row-major in LDS
-  auto stage = [&](const KeyRaw& r) {
-    _Float16* krow = sh.k + kk * kKStride + 128 * qq;
-    if (r.kind == 1) {
-      // v_cvt_scalef32_pk_f16_fp4 applies only a power-of-two scale, so the codes convert
-      // at scale 1 and a packed f16 multiply applies the E4M3 scale (exact: at most 6
-      // significant bits, inside f16's normal range)
-#pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const uint32_t wd[4] = {r.pay[v].x, r.pay[v].y, r.pay[v].z, r.pay[v].w};
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-          const int grp = 2 * v + (q4 >> 1);  // local group of 16 dims
-          const uint32_t sb = ((grp < 4 ? r.scw.x : r.scw.y) >> (8 * (grp & 3))) & 255u;
-          const _Float16 S = (_Float16)e4m3_value(sb);
-          const f16x2 S2 = {S, S};
-          const f16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 0) * S2;
-          const f16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 1) * S2;
-          const f16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 2) * S2;
-          const f16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 3) * S2;
-          const f16x8 pk = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-          *reinterpret_cast<f16x8*>(krow + 32 * v + 8 * q4) = pk;
-        }
-      }
-    } else if (r.kind == 2) {
-      int64_t row = woff + r.row;
-      if (swa_ring > 0 && row >= swa_ring) row -= swa_ring;  // r.row < 128 <= swa_ring
-      row += wseg;
-      if constexpr (kFp8Win) {
-        // this thread decodes NoPE dims 112 qq .. 112 qq + 111 (codes at the same byte
-        // offsets) and RoPE dims 448 + 16 qq .. + 15 (bf16 at bytes 448 + 32 qq)
-        const uint8_t* src = static_cast<const uint8_t*>(swa_v) + row * kSwa8Bytes;
-        const uint64_t scb = *reinterpret_cast<const uint64_t*>(src + kDNope + 2 * kDRope);
-        _Float16* kq = sh.k + kk * kKStride;
-#pragma unroll
-        for (int j = 0; j < 7; j++) {
-          const u32x4_a8 c = *reinterpret_cast<const u32x4_a8*>(src + 112 * qq + 16 * j);
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            const int grp = (112 * qq + 16 * j + 8 * h) >> 6;  // scale group of these 8 dims
-            const uint32_t code = (uint32_t)(scb >> (8 * grp)) & 255u;
-            const _Float16 X = (_Float16)__builtin_ldexpf(1.0f, (int)code - 127);
-            const f16x2 X2 = {X, X};
-            const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, false) * X2;
-            const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, true) * X2;
-            const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, false) * X2;
-            const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, true) * X2;
-            const f16x8 pk = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-            *reinterpret_cast<f16x8*>(kq + 112 * qq + 16 * j + 8 * h) = pk;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          const u32x4_a8 u = *reinterpret_cast<const u32x4_a8*>(src + kDNope + 32 * qq + 16 * j);
-          f16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            pk[2 * e] = (_Float16)bf16_bits_to_f32(u[e] & 0xFFFFu);
-            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(u[e] >> 16);
-          }
-          *reinterpret_cast<f16x8*>(kq + kDNope + 16 * qq + 8 * j) = pk;
-        }
-      } else {
-        const uint4* src =
-            reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(swa_v) + row * kD + 128 * qq);
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-          const uint4 u = src[v];
-          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-          f16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
-            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
-          }
-          *reinterpret_cast<f16x8*>(krow + 8 * v) = pk;
-        }
-      }
-    } else {
-      f16x8 z;
-#pragma unroll
-      for (int e = 0; e < 8; e++) z[e] = (_Float16)0.0f;
-#pragma unroll
-      for (int v = 0; v < 16; v++) *reinterpret_cast<f16x8*>(krow + 8 * v) = z;
-    }
-    if (qq == 0) sh.valid[kk] = r.kind != 0 ? 1 : 0;
-  };
+  KeyStager<kFp8Win> ks(kv_cache, topk + (int64_t)t * K, K, swa_v, swa_ring, q_base[t], swa_start[t], swa_len[t],
+                         tid);
 
   // query fragments: head 16w + i, dims 32s + 8g .. +7, as f16 (exact in the normal range)
   f16x8 qa[16];
@@ -212,26 +284,39 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     l_run[r] = 0.0f;
   }
 
+  ks.load_ids(c_begin, c_end, sh, tid);
+  __syncthreads();
   KeyRaw raw;
-  if (c_begin < c_end) fetch(c_begin, raw);
+  if (c_begin < c_end) ks.fetch(c_begin, raw);
   for (int c = c_begin; c < c_end; c++) {
     __syncthreads();  // the previous chunk's LDS reads are done
-    stage(raw);
-    if (c + 1 < c_end) fetch(c + 1, raw);  // next chunk's gather overlaps this chunk's math
+    ks.stage(raw, sh);
+    if (c + 1 < c_end) ks.fetch(c + 1, raw);  // next chunk's gather overlaps this chunk's math
     __syncthreads();
 
     // ---- S = Q K^T for 4 tiles of 16 keys
     f32x4 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // groups of 4 dim steps: the group's 16 B fragments are read before its 16 MFMAs, so the
+    // reads overlap one another instead of each MFMA waiting for its own LDS round trip
 #pragma unroll
-    for (int s = 0; s < 16; s++) {
+    for (int s0 = 0; s0 < 16; s0 += 4) {
+      f16x8 kb[4][4];
 #pragma unroll
-      for (int kt = 0; kt < 4; kt++) {
-        const f16x8 b = *reinterpret_cast<const f16x8*>(sh.k + (16 * kt + i) * kKStride + 32 * s + 8 * g);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], b, sacc[kt], 0, 0, 0);
+      for (int s = 0; s < 4; s++) {
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+          kb[s][kt] = *reinterpret_cast<const f16x8*>(sh.k + (16 * kt + i) * kKStride + 32 * (s0 + s) + 8 * g);
       }
-      if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound how far LDS reads are hoisted
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s0 + s], kb[s][kt], sacc[kt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- online softmax over this chunk; lane holds rows (heads) 4g + r, column (key) 16kt + i
     float pv[4][4];
@@ -290,16 +375,23 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     for (int ks = 0; ks < 2; ks++) {
       const f16x8 pa = *reinterpret_cast<const f16x8*>(pw + i * kPStride + 32 * ks + 8 * g);
       const int kb = 32 * ks + 8 * g + (i >> 2);
+      // groups of 8 dim tiles: 16 transposing reads, then the group's 8 MFMAs
 #pragma unroll
-      for (int dt = 0; dt < 32; dt++) {
-        if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
-        const _Float16* p0 = sh.k + kb * kKStride + 16 * dt + 4 * (i & 3);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(p0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(p0 + 4 * kKStride));
-        const f16x8 vb = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt], 0, 0, 0);
+      for (int dt0 = 0; dt0 < 32; dt0 += 8) {
+        s16x4 lo[8], hi[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const _Float16* p0 = sh.k + kb * kKStride + 16 * (dt0 + u) + 4 * (i & 3);
+          lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0));
+          hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0 + 4 * kKStride));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const f16x8 vb = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo[u], hi[u], 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dt0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt0 + u], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
