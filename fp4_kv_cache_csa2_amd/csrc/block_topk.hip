@@ -407,6 +407,13 @@ struct Row {
   // ranking items of the histogram: the pool's positions (candidate mode) or the older
   // blocks 0 .. nb-2 (full mode; the newest block is handled apart)
   __device__ int32_t items() const { return cand ? 8 * M : max(nb - 1, 0); }
+  // the key of item i for any i (out-of-range items read item 0 and give 0): the loads do
+  // not sit behind a branch, so a caller's unrolled loads are all in flight at once
+  __device__ __forceinline__ uint32_t item_key_clamped(int32_t i, int32_t hi) const {
+    const int32_t ic = i < hi ? i : 0;
+    const uint32_t k = item_key(ic);
+    return i < hi ? k : 0u;
+  }
   __device__ uint32_t item_key(int32_t i) const {  // 0 = not a candidate
     if (cand) {
       const int32_t b = pool[i >> 3];
@@ -453,8 +460,9 @@ struct Ws {
 
 // ------------------------------------------------------------------ K1: histogram
 
+template <bool cand>
 __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
-    bool cand, const float* __restrict__ scores, const float* __restrict__ block_max, int32_t width,
+    const float* __restrict__ scores, const float* __restrict__ block_max, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
   __shared__ uint32_t h[kBins];
   const int t = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
@@ -465,14 +473,16 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
     // block maxima from the scores (NaN never wins a comparison, so it ranks as -inf)
     float* bmw = ws.bm + (int64_t)t * nbw;
     for (int32_t b = lo + tid; b < min(lo + kHSlice, r.nb); b += kHThreads) {
-      float mx = -__builtin_inff();
-      for (int o = 0; o < kBlock; o++) {
+      float v[kBlock];
+#pragma unroll
+      for (int o = 0; o < kBlock; o++) {  // the block's loads in flight together (j < n for o = 0)
         const int32_t j = b * kBlock + o;
-        if (j < r.n) {
-          const float v = r.scores[j];
-          mx = v > mx ? v : mx;
-        }
+        v[o] = r.scores[j < r.n ? j : b * kBlock];
       }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int o = 0; o < kBlock; o++)
+        if (b * kBlock + o < r.n) mx = v[o] > mx ? v[o] : mx;
       bmw[b] = mx;
     }
     __syncthreads();
@@ -486,7 +496,7 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
 #pragma unroll
   for (int u = 0; u < kPerH; u++) {  // every key load in flight at once
     const int32_t i = lo + u * kHThreads + tid;
-    keys[u] = i < hi ? r.item_key(i) : 0u;
+    keys[u] = r.item_key_clamped(i, hi);
   }
 #pragma unroll
   for (int u = 0; u < kPerH; u++) hist_add(h, keys[u] >> kBinShift, keys[u] != 0u);
@@ -512,8 +522,9 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
 // hold K entries at or above that edge, so every Top-K entry keeps its key.
 constexpr int kItemsPerLane = kSlice / kGThreads;
 
+template <bool cand>
 __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
-    bool cand, bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
+    bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
   __shared__ int32_t s_wave[kGThreads / 64];
   __shared__ int32_t s_cnt[2][kGThreads / 64];
@@ -530,7 +541,7 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
 #pragma unroll
   for (int j = 0; j < kItemsPerLane; j++) {
     const int32_t i = lo + 256 * wave + 64 * j + lane;
-    key[j] = i < hi_a ? r.item_key(i) : 0u;
+    key[j] = hi_a > 0 ? r.item_key_clamped(i, hi_a) : 0u;
   }
   const uint32_t* gh = ws.hist + (int64_t)t * kBins;
   uint32_t hb[16], local = 0;
@@ -688,8 +699,9 @@ struct FinShared {
 // 1 takes the Top-K from list B (Full mode) or list A (candidate mode).  Each reads the
 // matching histogram, returns it to zero, gathers its list (a superset of the selection
 // in ascending id order) and refines the boundary bin's low 20 bits over it.
+template <bool cand>
 __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
-    bool cand, bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
+    bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws,
     int32_t* __restrict__ pool_out, int32_t* __restrict__ topk_out) {
   __shared__ FinShared sh;
@@ -714,14 +726,16 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   uint32_t local = 0;
 #pragma unroll
   for (int q = 0; q < kBinsPer; q++) {
-    c[q] = use_a ? gh[kBins - 1 - kBinsPer * tid - q] : 0u;
+    const uint32_t hv = gh[kBins - 1 - kBinsPer * tid - q];  // read by both roles, used by list-A roles
+    c[q] = use_a ? hv : 0u;
     local += c[q];
   }
   int cs[kSegPer], cl = 0;
 #pragma unroll
   for (int q = 0; q < kSegPer; q++) {
     const int g = kSegPer * tid + q;
-    cs[q] = g < G ? cnts[g] : 0;
+    const int32_t cv = cnts[g < G ? g : 0];
+    cs[q] = g < G ? cv : 0;
     cl += cs[q];
   }
   const uint32_t xa = wave_incl_scan(local), xb = wave_incl_scan((uint32_t)cl);
@@ -776,11 +790,19 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
       }
       at[u] = e < total ? (int64_t)lo * seg_stride + (e - sh.seg_off[lo]) : -1;
     }
+    int32_t gid[kPer];
+    uint32_t gkey[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {  // every list load in flight at once (slot 0 stands in for empty ones)
+      const int64_t a = at[u] >= 0 ? at[u] : 0;
+      gid[u] = lids[a];
+      gkey[u] = lkeys[a];
+    }
 #pragma unroll
     for (int u = 0; u < kPer; u++) {
       if (at[u] >= 0) {
-        sh.ids[u * kFThreads + tid] = lids[at[u]];
-        sh.keys[u * kFThreads + tid] = lkeys[at[u]];
+        sh.ids[u * kFThreads + tid] = gid[u];
+        sh.keys[u * kFThreads + tid] = gkey[u];
       }
     }
     __syncthreads();
@@ -921,15 +943,28 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   const bool want_pool = pool_out != nullptr;
   hipStream_t s = (hipStream_t)stream;
   const int32_t G1 = (L.G * kSlice + kHSlice - 1) / kHSlice;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(G1, n_q), dim3(kHThreads), 0, s, cand, scores, block_max, width,
-                     q_nvis, pool_blocks, M, K, ws);
+  if (cand)
+    hipLaunchKernelGGL(topk_hist_kernel<true>, dim3(G1, n_q), dim3(kHThreads), 0, s, scores, block_max, width, q_nvis,
+                       pool_blocks, M, K, ws);
+  else
+    hipLaunchKernelGGL(topk_hist_kernel<false>, dim3(G1, n_q), dim3(kHThreads), 0, s, scores, block_max, width, q_nvis,
+                       pool_blocks, M, K, ws);
   int st = check_launch();
   if (st != CSA2_OK) return st;
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(L.G, n_q), dim3(kGThreads), 0, s, cand, want_pool, want_topk, scores,
-                     bm, width, q_nvis, pool_blocks, M, K, ws);
+  if (cand)
+    hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(L.G, n_q), dim3(kGThreads), 0, s, want_pool, want_topk, scores,
+                       bm, width, q_nvis, pool_blocks, M, K, ws);
+  else
+    hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(L.G, n_q), dim3(kGThreads), 0, s, want_pool, want_topk, scores,
+                       bm, width, q_nvis, pool_blocks, M, K, ws);
   st = check_launch();
   if (st != CSA2_OK) return st;
-  hipLaunchKernelGGL(topk_final_kernel, dim3((!cand && want_pool && want_topk) ? 2 : 1, n_q), dim3(kFThreads), 0, s,
-                     cand, want_pool, want_topk, scores, bm, width, q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
+  const dim3 gf((!cand && want_pool && want_topk) ? 2 : 1, n_q);
+  if (cand)
+    hipLaunchKernelGGL(topk_final_kernel<true>, gf, dim3(kFThreads), 0, s, want_pool, want_topk, scores, bm, width,
+                       q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
+  else
+    hipLaunchKernelGGL(topk_final_kernel<false>, gf, dim3(kFThreads), 0, s, want_pool, want_topk, scores, bm, width,
+                       q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
   return check_launch();
 }
