@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
 #pragma unroll
   for (int j = 0; j < kItemsPerLane; j++) {
     const int32_t i = lo + 256 * wave + 64 * j + lane;
-    key[j] = hi_a > 0 ? r.item_key_clamped(i, hi_a) : 0u;
+    key[j] = r.item_key_clamped(i, hi_a);  // item 0 of the row always exists
   }
   const uint32_t* gh = ws.hist + (int64_t)t * kBins;
   uint32_t hb[16], local = 0;
