@@ -778,31 +778,36 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   if (take_all_blocks) {
     cnt = max(r.nb - 1, 0);
   } else if (listed) {
-    // gather the list: all segment searches side by side, then all loads in flight
-    int64_t at[kPer];
+    // gather the list: wave w copies segments w, w + 16, ... (one lane per item), four
+    // segments' loads in flight at a time; segments longer than 64 items loop on
+    for (int g0 = wave; g0 < G; g0 += 4 * kFWaves) {
+      int32_t gid[4], dst[4], cnt4[4], off4[4];
+      uint32_t gkey[4];
 #pragma unroll
-    for (int u = 0; u < kPer; u++) {
-      const int e = u * kFThreads + tid;
-      int lo = 0, hi = e < total ? G - 1 : 0;  // last segment whose offset is <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sh.seg_off[mid] <= e) lo = mid; else hi = mid - 1;
+      for (int k = 0; k < 4; k++) {
+        const int g = g0 + k * kFWaves;
+        off4[k] = g < G ? sh.seg_off[g] : 0;
+        cnt4[k] = g < G ? sh.seg_off[g + 1] - off4[k] : 0;
+        const bool ok = lane < cnt4[k];
+        const int64_t src = (int64_t)(g < G ? g : 0) * seg_stride + (ok ? lane : 0);  // slot 0 stands in
+        gid[k] = lids[src];
+        gkey[k] = lkeys[src];
+        dst[k] = ok ? off4[k] + lane : -1;
       }
-      at[u] = e < total ? (int64_t)lo * seg_stride + (e - sh.seg_off[lo]) : -1;
-    }
-    int32_t gid[kPer];
-    uint32_t gkey[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; u++) {  // every list load in flight at once (slot 0 stands in for empty ones)
-      const int64_t a = at[u] >= 0 ? at[u] : 0;
-      gid[u] = lids[a];
-      gkey[u] = lkeys[a];
-    }
+      for (int k = 0; k < 4; k++) {
+        if (dst[k] >= 0) {
+          sh.ids[dst[k]] = gid[k];
+          sh.keys[dst[k]] = gkey[k];
+        }
+      }
 #pragma unroll
-    for (int u = 0; u < kPer; u++) {
-      if (at[u] >= 0) {
-        sh.ids[u * kFThreads + tid] = gid[u];
-        sh.keys[u * kFThreads + tid] = gkey[u];
+      for (int k = 0; k < 4; k++) {
+        const int64_t g = g0 + k * kFWaves;
+        for (int e = 64 + lane; e < cnt4[k]; e += 64) {
+          sh.ids[off4[k] + e] = lids[g * seg_stride + e];
+          sh.keys[off4[k] + e] = lkeys[g * seg_stride + e];
+        }
       }
     }
     __syncthreads();
