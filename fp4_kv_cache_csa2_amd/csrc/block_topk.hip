@@ -26,11 +26,12 @@
 //               any entry outside the pool is outranked by the M-1 block maxima above it.
 //   K3 finalize one 1024-thread workgroup per query and role, the roles in parallel: the
 //               pool from list A, the Top-K from list B (or from list A in candidate
-//               mode).  The list-A roles read K1's histogram (the count above the boundary
-//               bin and the bin's own count) and return it to zero; the list-B role
-//               histograms its gathered list in LDS.  Each then refines only the boundary
-//               bin's low 20 bits, with the keys held in registers (one barrier per 8-bit
-//               radix pass).  If a list overflows LDS (massive ties), K3
+//               mode).  Each gathers its list into LDS, one wave per run of segments.
+//               The list-A roles read K1's histogram (the count above the boundary bin
+//               and the bin's own count), return it to zero, and refine only the boundary
+//               bin's low 20 bits; the list-B role starts below the common leading bits of
+//               its keys.  Keys are held in registers (one barrier per 8-bit radix
+//               pass).  If a list overflows LDS (massive ties), K3
 //               selects straight from the full row instead, with the same exact rules.
 // The histogram region of the workspace must be zero before the first call; every call
 // leaves it zero.
@@ -690,7 +691,6 @@ struct FinShared {
   int32_t seg_off[kMaxG + 1];
   int32_t scan[2 * kFWaves];
   int32_t bnd[4];              // boundary bin, count above it, its count, total
-  uint32_t lhist[kBins];       // histogram of list B's keys (Full-mode Top-K role)
   ListScratch ls;
   SelScratch s;
 };
@@ -709,8 +709,7 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   const int role = !want_topk ? 0 : ((cand || !want_pool) ? 1 : (int)blockIdx.x);
   const int G = ws.G;
   Row r = make_row(t, cand, scores, bm, width, q_nvis, pool_blocks, M, K);
-  // the list, its histogram and the rank wanted.  Roles on list A use K1's histogram; the
-  // Full-mode Top-K role counts its gathered list B in LDS
+  // the list, its histogram and the rank wanted.  Roles on list A use K1's histogram
   const bool use_a = role == 0 || cand;
   uint32_t* gh = ws.hist + (int64_t)t * kBins;
   const int32_t* cnts = (use_a ? ws.cnt_a : ws.cnt_b) + (int64_t)t * G;
@@ -718,8 +717,6 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   const int32_t* lids = (use_a ? ws.ids_a : ws.ids_b) + (int64_t)t * G * seg_stride;
   const uint32_t* lkeys = (use_a ? ws.keys_a : ws.keys_b) + (int64_t)t * G * seg_stride;
   const int want = role == 0 ? M - 1 : K;
-  if (!use_a)
-    for (int b = tid; b < kBins; b += kFThreads) sh.lhist[b] = 0u;
 
   // ---- histogram boundary (list A) and segment offsets, in one pass of two scans
   uint32_t c[kBinsPer];
@@ -812,41 +809,18 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
     }
     __syncthreads();
     int kk = min(want, tota);
-    if (!use_a) {
-      // histogram of list B's non-zero keys, then its boundary bin for rank min(K, count)
-#pragma unroll
-      for (int u = 0; u < kPer; u++) {
-        const int e = u * kFThreads + tid;
-        const uint32_t key = e < total ? sh.keys[e] : 0u;
-        if (key != 0u) atomicAdd(&sh.lhist[key >> kBinShift], 1u);
-      }
-      __syncthreads();
-      uint32_t lc[kBinsPer], ll = 0;
-#pragma unroll
-      for (int q = 0; q < kBinsPer; q++) {
-        lc[q] = sh.lhist[kBins - 1 - kBinsPer * tid - q];
-        ll += lc[q];
-      }
-      const uint32_t xl = wave_incl_scan(ll);
-      if (lane == 63) sh.scan[wave] = (int)xl;
-      __syncthreads();
-      int offl = 0, totl = 0;
-#pragma unroll
-      for (int w = 0; w < kFWaves; w++) {
-        const int a = sh.scan[w];
-        offl += (w < wave) ? a : 0;
-        totl += a;
-      }
-      kk = min(K, totl);
-      hist_boundary(lc, (uint32_t)(offl + (int)xl - (int)ll), kk, 0, sh.bnd);
-      __syncthreads();
-    }
-    const int b1 = sh.bnd[0];
     uint32_t thr;
-    if (b1 >= 0) {
-      cnt = list_select(sh.keys, total, (uint32_t)b1 << kBinShift, ~0u << kBinShift, kBinShift, kk - sh.bnd[1],
-                        sh.bnd[2], sh.ls, sh.sel, &thr);
+    if (!use_a) {
+      // Top-K of list B: the selection starts below the common leading bits of its keys
+      cnt = list_select(sh.keys, total, 0u, 0u, 32, K, -1, sh.ls, sh.sel, &thr);
       for (int i = tid; i < cnt; i += kFThreads) sh.sel[i] = sh.ids[sh.sel[i]];
+    } else {
+      const int b1 = sh.bnd[0];
+      if (b1 >= 0) {
+        cnt = list_select(sh.keys, total, (uint32_t)b1 << kBinShift, ~0u << kBinShift, kBinShift, kk - sh.bnd[1],
+                          sh.bnd[2], sh.ls, sh.sel, &thr);
+        for (int i = tid; i < cnt; i += kFThreads) sh.sel[i] = sh.ids[sh.sel[i]];
+      }
     }
   } else if (role == 0) {
     cnt = block_select([&](int i) { return r.item_key(i); }, r.items(), M - 1, sh.s, sh.sel);
