@@ -239,6 +239,26 @@ struct KeyStager {
   }
 };
 
+// Reductions over the 16 lanes of a DPP row (data movement on the VALU instead of LDS
+// shuffles): rotations by 8 and 4 inside the row, then two quad permutations; every lane
+// ends with the row's result.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = __builtin_fmaxf(v, dpp<0x128>(v));    // row_ror:8
+  v = __builtin_fmaxf(v, dpp<0x124>(v));    // row_ror:4
+  v = __builtin_fmaxf(v, dpp<0xB1>(v));     // quad_perm [1,0,3,2]
+  return __builtin_fmaxf(v, dpp<0x4E>(v));  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0x128>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0xB1>(v);
+  return v + dpp<0x4E>(v);
+}
+
 // Window rows: kFp8Win selects 584-byte FP8 rows instead of bf16 rows.
 template <bool kFp8Win>
 __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
@@ -335,12 +355,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     float alpha[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      float mx = cmax[r];
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1));
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2));
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 4));
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 8));
-      const float mn = __builtin_fmaxf(m_run[r], mx);
+      const float mn = __builtin_fmaxf(m_run[r], row16_max(cmax[r]));
       alpha[r] = (mn == -__builtin_inff()) ? 1.0f : __expf(m_run[r] - mn);
       float rs = 0.0f;
 #pragma unroll
@@ -349,17 +364,16 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
         pv[kt][r] = p;
         rs += p;
       }
-      rs += __shfl_xor(rs, 1);
-      rs += __shfl_xor(rs, 2);
-      rs += __shfl_xor(rs, 4);
-      rs += __shfl_xor(rs, 8);
-      l_run[r] = l_run[r] * alpha[r] + rs;
+      l_run[r] = l_run[r] * alpha[r] + row16_sum(rs);
       m_run[r] = mn;
     }
+    // rescale O only when some head's running maximum moved (later chunks rarely move it)
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f || alpha[2] != 1.0f || alpha[3] != 1.0f)) {
 #pragma unroll
-    for (int d = 0; d < 32; d++) {
+      for (int d = 0; d < 32; d++) {
 #pragma unroll
-      for (int r = 0; r < 4; r++) o[d][r] *= alpha[r];
+        for (int r = 0; r < 4; r++) o[d][r] *= alpha[r];
+      }
     }
     _Float16* pw = sh.p + w * 16 * kPStride;
 #pragma unroll
