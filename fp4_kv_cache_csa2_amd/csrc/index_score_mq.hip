@@ -23,6 +23,9 @@ constexpr int kMqQB = kMqQPW * kWaves;         // queries per workgroup
 constexpr int kMqTiles = 32;                   // tiles of 32 entries per workgroup
 constexpr int kMqDepth = 3;                    // raw tiles in flight per wave
 
+constexpr int kRawBuf = 0x00020000;  // buffer descriptor word 3: raw 32-bit dwords
+
+template <bool kBmax>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void index_score_mq_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
@@ -59,22 +62,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     max_nvis = max(max_nvis, s_nvis[j]);
     shared = shared && s_base[j] == base0;
   }
-  // this wave's queries: A fragments (head n, dims 64g + 8s ..) and head weights
+  // this wave's queries: A fragments (head n, dims 64g + 8s ..), visible counts and output
+  // rows as buffer resources (empty for a padding slot, so its stores are dropped)
+  constexpr int32_t kOut = 1 << 30;  // a byte offset past every buffer's end
   bf16x8 a[kMqQPW][8];
   int32_t nv[kMqQPW];
   int tq[kMqQPW];
+  __amdgpu_buffer_rsrc_t rs_s[kMqQPW], rs_b[kMqQPW];
 #pragma unroll
   for (int j = 0; j < kMqQPW; j++) {
     const int t = qb0 + wave * kMqQPW + j;
     tq[j] = t;
-    const int tt = t < n_q ? t : qb0;  // a padding slot reads a real query and writes nothing
-    nv[j] = t < n_q ? s_nvis[wave * kMqQPW + j] : 0;
+    const bool real = t < n_q;
+    const int tt = real ? t : qb0;  // a padding slot reads a real query and writes nothing
+    nv[j] = real ? s_nvis[wave * kMqQPW + j] : 0;
     const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)tt * kIdxHeads + n) * kIdxDim + 64 * g);
 #pragma unroll
     for (int s = 0; s < 8; s++) a[j][s] = __builtin_bit_cast(bf16x8, qp[s]);
+    rs_s[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)tt * width, (short)0, real ? width * 4 : 0, kRawBuf);
+    rs_b[j] = __builtin_amdgcn_make_buffer_rsrc(kBmax ? (void*)(block_max + (int64_t)tt * nbw) : (void*)scores,
+                                                (short)0, (kBmax && real) ? nbw * 4 : 0, kRawBuf);
   }
   // scores of one query for one tile from its accumulators: ReLU, head weights (accumulator
-  // row 4c + r of this lane is head 8c + 4g + r), head sum
+  // row 4c + r of this lane is head 8c + 4g + r), head sum, causal mask, block maximum; one
+  // lane stores each value, the others aim past the end of the buffer (no branches)
   auto finish = [&](int j, const f32x16& acc, int32_t k) {
     const float* wj = &s_w[wave * kMqQPW + j][4 * g];
     float part[4];
@@ -87,15 +98,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
       part[c] = __builtin_fmaf(w4.w, relu(acc[4 * c + 3]), part[c]);
     }
     const int32_t p = k * kTile + n;
-    const float sum = sum_halves((part[0] + part[1]) + (part[2] + part[3]));
-    const float sc = p < nv[j] ? sum : -__builtin_inff();
-    if (tq[j] < n_q) {
-      if (g == 0 && p < width) scores[(int64_t)tq[j] * width + p] = sc;
-      if (block_max != nullptr) {
-        const float bm = max8_lanes(sc);
-        if (g == 0 && (n & 7) == 0 && p < width) block_max[(int64_t)tq[j] * nbw + (p >> 3)] = bm;
-      }
-    }
+    const float sc = masked_score(sum_halves((part[0] + part[1]) + (part[2] + part[3])), p < nv[j]);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_s[j], g ? kOut : 4 * p, 0, 0);
+    if constexpr (kBmax)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_b[j],
+                                            (g | (n & 7)) ? kOut : 4 * (p >> 3), 0, 0);
   };
 
   if (shared && max_nvis > 0) {
@@ -116,13 +123,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     };
     // tiles that some query of the block can see
     const int32_t tend = min(tile1, (max_nvis + kTile - 1) / kTile);
+    // (loads past the visible rows read the last one, so they need no guard)
     Raw pipe[kMqDepth];
 #pragma unroll
-    for (int u = 0; u < kMqDepth; u++)
-      if (tile0 + u < tend) load(tile0 + u, pipe[u]);
+    for (int u = 0; u < kMqDepth; u++) load(tile0 + u, pipe[u]);
     if (tile0 < tend) {
       stage(pipe[0], 0);
-      if (tile0 + kMqDepth < tend) load(tile0 + kMqDepth, pipe[0]);
+      load(tile0 + kMqDepth, pipe[0]);
     }
     __syncthreads();
     for (int32_t k0 = tile0; k0 < tend; k0 += kMqDepth) {
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
           if (k + 1 < tend) {
             const int un = (u + 1) % kMqDepth;
             stage(pipe[un], buf ^ 1);
-            if (k + 1 + kMqDepth < tend) load(k + 1 + kMqDepth, pipe[un]);
+            load(k + 1 + kMqDepth, pipe[un]);
           }
           f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -194,9 +201,14 @@ int launch_index_score_mq(const uint16_t* q_idx_bf16, const float* head_w, const
   const int32_t ntiles = (width + kTile - 1) / kTile;
   const int64_t gx = (ntiles + kMqTiles - 1) / kMqTiles, gy = (n_q + kMqQB - 1) / kMqQB;
   if (gx > 0x7FFFFFFF || gy > 65535) return CSA2_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(index_score_mq_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
-                     (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, n_q, width, scores,
-                     block_max);
+  if (block_max != nullptr)
+    hipLaunchKernelGGL(index_score_mq_kernel<true>, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
+                       (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, n_q, width, scores,
+                       block_max);
+  else
+    hipLaunchKernelGGL(index_score_mq_kernel<false>, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
+                       (hipStream_t)stream, q_idx_bf16, head_w, idx_cache, q_base, q_nvis, n_q, width, scores,
+                       block_max);
   return check_launch();
 }
 
