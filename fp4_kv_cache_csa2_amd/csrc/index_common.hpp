@@ -63,6 +63,11 @@ __device__ __forceinline__ void load_fp4_query(const uint8_t* rec, int g, fp4x32
   qsc = *reinterpret_cast<const uint32_t*>(rec + 64) >> (16 * g);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
+// outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their no-wait maxima).
+// Vector memory operations complete in issue order, so this waits for all but the n youngest.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 struct RawTile {
   u32x4_a4 lo, hi;
   uint32_t sc;

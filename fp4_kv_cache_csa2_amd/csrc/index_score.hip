@@ -153,17 +153,10 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
                                           (g | (n & 7)) ? kOut : 4 * (p >> 3), 0, 0);
   };
 
-  // software pipeline: kDepth - 1 tiles of this wave are in flight while one is processed.
-  // Full groups of kDepth tiles stream through the loop; loads past the wave's last tile
-  // return zeros and are never processed; the last partial group is finished after it.
-  // (the scheduling barriers keep the tiles' loads in tile order, so each tile's wait
-  // counts only older loads)
-  RawTile pipe[kDepth];
-#pragma unroll
-  for (int u = 0; u < kDepth; u++) {
-    load(u, pipe[u]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  // The query and head weights are loaded first, then the first kDepth tiles, and a wait
+  // for all but the tiles' loads completes the query before the loop.  The compiler then
+  // knows the query registers are ready inside the loop; otherwise it re-checks them on
+  // every pass with a wait that drains this wave's tiles in flight (loads complete in order).
   {
     if constexpr (kFp4Q) {
       load_fp4_query(static_cast<const uint8_t*>(q_in) + ((int64_t)t * kIdxHeads + n) * kIdxBytes, g, qa, qsc);
@@ -182,12 +175,29 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
       for (int r = 0; r < 4; r++) wr[4 * c + r] = v[r];
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // software pipeline: kDepth - 1 tiles of this wave are in flight while one is processed.
+  // Full groups of kDepth tiles stream through the loop; loads past the wave's last tile
+  // return zeros and are never processed; the last partial group is finished after it.
+  // (the scheduling barriers keep the tiles' loads in tile order, so each tile's wait
+  // counts only older loads)
+  RawTile pipe[kDepth];
+#pragma unroll
+  for (int u = 0; u < kDepth; u++) {
+    load(u, pipe[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Full mode issues three loads per tile; a pool tile's block-id load precedes its three
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDepth * (kPool ? 4 : 3)));
   int32_t k0 = 0;
   for (; k0 + kDepth <= nt; k0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; u++) {
       process(pipe[u], k0 + u);
       load(k0 + u + kDepth, pipe[u]);  // reuses this tile's registers, so none are copied
+      // the MXFP4-query body leaves the scheduler room to interleave different tiles' loads,
+      // which would make each tile's wait cover younger tiles too: keep them in tile order
+      if constexpr (kFp4Q) __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
