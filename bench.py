@@ -3,8 +3,10 @@
 Workload (decode_1m_b4_m2): 4 sequences x 1,048,576 tokens compressed at m = 2 into
 524,288 FP4 entries each (main KV 288 B + indexer K 68 B per entry), 4 decode queries,
 one Full layer.  One step runs the whole hot path once for the batch:
-  compress_pack of each sequence's newest entry (pool 2 latents, RoPE, FP4 + MXFP4 pack)
-  -> index_score over all 524,288 entries per query (+ block maxima)
+  append of each sequence's newest entry into its cache row (pool 2 latents, RoPE, FP4 +
+  MXFP4 pack) fused with index_score over all 524,288 entries per query (+ block maxima),
+  one launch (csa2_append_index_score: the append runs beside the scan, and the tile
+  holding the new entry is scored once the entry is written)
   -> block_topk (top-2048 blocks of 8 -> pool -> Top-512)
   -> sparse_attn (64 heads over the 512 selected entries + 128 window rows).
 Inputs are resident in HBM before timing starts.  The batch exists in NCOPY distinct
@@ -14,13 +16,15 @@ from the 256 MB Infinity Cache left warm by the previous step.
 Prints one JSON line (rank 0, N = 1).  `value` is queries/s over exactly K steps, replayed
 from a HIP graph that holds NCOPY consecutive steps (one per batch copy), as a decoding
 token's layers run inside one graph; `ms_per_step_one_step_graphs` is the same K steps with
-one graph launch per step; `roofline` prices the
-dominant kernel (index_score) at 68 algorithmic bytes per scored entry against 8 TB/s,
-timed with HIP events on the launch stream; `cpu_baseline` times the oracle (plain C,
-one host thread) on the same per-query work.  `roofline.traffic` is the HBM bytes per
-index_score launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (each scaled by what the
-counter reads for a torch copy of known size), read from profiles/index_score_traffic.json
-and reported only while the kernel's sources still hash to the ones those counters measured.
+one graph launch per step; `stages_us` times each stage of the step alone and
+`replaced_stages_us` the separate append and scan launches the fused stage replaces;
+`roofline` prices the dominant kernel (the fused append + scan) at 68 algorithmic bytes
+per scored entry against 8 TB/s, timed with HIP events on the launch stream; `cpu_baseline`
+times the oracle (plain C, one host thread) on the same per-query work.  `roofline.traffic`
+is the HBM bytes per launch of that kernel from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
+(each scaled by what the counter reads for a torch copy of known size), read from
+profiles/append_index_traffic.json and reported only while the kernel's sources still hash
+to the ones those counters measured.
 """
 from __future__ import annotations
 
@@ -156,13 +160,20 @@ class Decode1M:
         # the selection workspace starts zeroed and every call leaves its histogram zeroed
         self.ws_sel = torch.zeros(max(4, csa2.block_topk_workspace(n_seq, n, M, K)), dtype=torch.uint8, device=dev)
         self.ws_att = torch.empty(max(1, csa2.sparse_attn_workspace(n_seq, K)), dtype=torch.uint8, device=dev)
-        self.new_kv = [torch.empty((n_seq, 288), dtype=torch.uint8, device=dev) for _ in range(ncopy)]
-        self.new_ix = [torch.empty((n_seq, 68), dtype=torch.uint8, device=dev) for _ in range(ncopy)]
+        # the step appends each sequence's newest entry into its cache slot, the last visible row
+        # (the batch's caches were packed from the same latents, so every replay rewrites the same
+        # bytes)
+        self.new_rows = (self.q_base + (n - 1)).contiguous()
         self.cs_new = [c["cs_last"].expand(n_seq, 64).contiguous() for c in self.copies]
         if extra_layers:
             self.scores_r = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
             self.topk_r = torch.empty((n_seq, K), dtype=torch.int32, device=dev)
-        self.n_stages = 4 + (2 + extra_layers if extra_layers else 0)
+        # the stages of one step: the append fused with the Full layer's scan (HISA scores block
+        # means after the append, so it keeps them apart), selection, attention, then the
+        # Reindex and Reuse layers
+        self.fused = not hisa
+        self.step_stages = ([FUSED] if self.fused else [0, 1]) + [2, 3] + (
+            list(range(4, 6 + extra_layers)) if extra_layers else [])
         if fp4q:  # the step packs the layer's bf16 indexer query into MXFP4 records, then scores
             self.q_fp4 = torch.empty((n_seq, 32, 68), dtype=torch.uint8, device=dev)
         if hisa:
@@ -197,9 +208,16 @@ class Decode1M:
     def run_stage(self, ci, st):
         """One stage of the step for batch copy ci, on torch's current stream."""
         c, csa2, n = self.copies[ci], self.csa2, self.n
-        if st == 0:  # the newest entry of every sequence from its two latest latents
-            csa2.compress_pack(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"], self.cs_new[ci],
-                               c["w_idx"], kv_out=self.new_kv[ci], idx_out=self.new_ix[ci])
+        if st == FUSED:  # append each sequence's newest entry and score every entry, one launch
+            q = c["q_idx"]
+            if self.fp4q:
+                q = csa2.quantize_q_mxfp4(c["q_idx"], out=self.q_fp4)
+            csa2.append_index_score(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"],
+                                    self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], q, c["head_w"], self.q_base,
+                                    self.q_nvis, n, scores=self.scores, block_max=self.bmax)
+        elif st == 0:  # append the newest entry of every sequence, from its m latest latents
+            csa2.compress_append(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"], self.cs_new[ci],
+                                 c["w_idx"], self.new_rows, c["kv"], c["ix"])
         elif st == 1 and self.hisa:
             csa2.block_mean_pack(c["ix"], self.q_base, self.q_nvis, 1, c["means"], self.mbase,
                                  first_block=self.newest_block)
@@ -242,7 +260,9 @@ class Decode1M:
                              out=self.out, lse=self.lse, workspace=self.ws_att)
 
 
-STAGES = ("compress_newest", "index_score", "block_topk", "sparse_attn")
+FUSED = -1  # the stage that appends and scores in one launch (csa2_append_index_score)
+STAGE_NAMES = {FUSED: "append_index_score", 0: "compress_newest", 1: "index_score", 2: "block_topk",
+               3: "sparse_attn"}
 
 
 def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3, fp8_window=False, fp4q=False,
@@ -252,7 +272,7 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
     wl = Decode1M(torch, csa2, tokens, n_seq=n_seq, m=m, extra_layers=extra_layers, fp8_window=fp8_window, fp4q=fp4q,
                   hisa=hisa)
     for i in range(warmup):
-        for st in range(wl.n_stages):
+        for st in wl.step_stages:
             wl.run_stage(i % NCOPY, st)
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
@@ -260,7 +280,7 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
     for ci in range(NCOPY):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            for st in range(wl.n_stages):
+            for st in wl.step_stages:
                 wl.run_stage(ci, st)
         graphs.append(g)
     for i in range(2 * NCOPY):
@@ -438,10 +458,11 @@ def time_schedule(torch, csa2, tokens=1 << 20, n_seq=4, steps=10, warmup=2):
     return res
 
 
-# the sources the decode-path index kernel is built from
+# the sources the fused append + scan kernel is built from
 INDEX_SRCS = [os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "csrc", f)
-              for f in ("index_score.hip", "index_common.hpp", "csa2_device.hpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_traffic.json")
+              for f in ("append_index.hip", "index_tiles.hpp", "index_common.hpp", "compress_few.hpp",
+                        "csa2_device.hpp")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_index_traffic.json")
 
 
 def index_source_sha():
@@ -452,8 +473,8 @@ def index_source_sha():
 
 
 def measured_traffic():
-    """HBM bytes per index_score launch from the committed counter summary, or None when
-    it is missing or was taken on a different kernel source."""
+    """HBM bytes per launch of the fused append + scan kernel from the committed counter
+    summary, or None when it is missing or was taken on a different kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
         sha = index_source_sha()
@@ -483,10 +504,12 @@ def main():
         del src, dst
     wl = Decode1M(torch, csa2, args.tokens)
     n_seq, m, tokens, n, K, M = wl.n_seq, wl.m, wl.tokens, wl.n, wl.K, wl.M
-    stages = STAGES
+    step = wl.step_stages  # the fused append + scan, selection, attention
+    # stages timed on their own: the step's, and the two launches the fused stage replaces
+    timed = step + [0, 1]
     run_stage = wl.run_stage
     for i in range(args.warmup):  # eager warm-up
-        for st in range(4):
+        for st in timed:
             run_stage(i % NCOPY, st)
     torch.cuda.synchronize()
     # One HIP graph holds NCOPY consecutive steps, one per batch copy, as the layers of a
@@ -498,19 +521,19 @@ def main():
     multi_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(multi_graph, stream=cap):
         for ci in range(NCOPY):
-            for st in range(4):
+            for st in step:
                 run_stage(ci, st)
     step_graph = []
     for ci in range(NCOPY):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            for st in range(4):
+            for st in step:
                 run_stage(ci, st)
         step_graph.append(g)
     # per-stage graphs of back-to-back launches (rotating copies) for the stage timings
     reps = 4 * NCOPY
     stage_graph = []
-    for st in range(4):
+    for st in timed:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             for r in range(reps):
@@ -552,17 +575,18 @@ def main():
 
     # ---- stage timings: HIP events around graphs of back-to-back launches of one stage
     stage_rounds = 3
-    st_us = []
-    for st in range(4):
+    st_us = {}
+    for st, g in zip(timed, stage_graph):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
         for _ in range(stage_rounds):
-            stage_graph[st].replay()
+            g.replay()
         b.record()
         torch.cuda.synchronize()
-        st_us.append(a.elapsed_time(b) * 1e3 / (stage_rounds * reps))
-    idx_us = st_us[1]
+        st_us[st] = a.elapsed_time(b) * 1e3 / (stage_rounds * reps)
+    # the dominant kernel: the fused append + scan; its algorithmic bytes are the scan's
+    idx_us = st_us[FUSED]
     idx_bytes = n_seq * n * 68
     achieved = idx_bytes / (idx_us * 1e-6) / 1e9
     line = {
@@ -574,10 +598,11 @@ def main():
                    "compress_ratio": m, "entries_per_sequence": n, "index_heads": 32, "index_dim": 128,
                    "pool_blocks": M, "block": 8, "topk": K, "heads": 64, "head_dim": 512,
                    "swa": 128, "batch_copies": NCOPY},
-        "stages_us": {k: round(float(v), 2) for k, v in zip(stages, st_us)},
+        "stages_us": {STAGE_NAMES[st]: round(float(st_us[st]), 2) for st in step},
+        "replaced_stages_us": {STAGE_NAMES[st]: round(float(st_us[st]), 2) for st in (0, 1)},
         "gpu_ms_timed_region": round(gpu_ms, 4), "wall_s_timed_region": round(wall_s, 4),
         "steps_per_graph": NCOPY, "ms_per_step_one_step_graphs": round(ms_single, 4),
-        "roofline": {"kernel": "index_score", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "append_index_score", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": idx_bytes},

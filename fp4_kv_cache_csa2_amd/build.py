@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
 SOURCES = ["csa2_abi.hip", "compress_pack.hip", "index_score.hip", "index_score_mq.hip", "block_topk.hip", "sparse_attn.hip",
-           "swa_fp8.hip", "index_fp4q.hip", "hisa.hip"]
+           "swa_fp8.hip", "index_fp4q.hip", "hisa.hip", "append_index.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

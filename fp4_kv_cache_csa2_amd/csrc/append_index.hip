@@ -1,0 +1,120 @@
+// append_index.hip -- a decode step's append and its indexer scores in one launch (gfx950).
+//
+// A decoding step appends each sequence's newest entry (pooling, RoPE and both FP4 packs:
+// [DF] "CSA2 与每 token 890 字节" §4.2 and §4.4, [ZB] "把 KV Cache 压缩推到极致" §2.3.1 and
+// §2.4.4) and then scores every visible entry for the step's query ([ZB] §3.3.2, §2.3.4; [DF]
+// §4.7).  Only the scores of the tile of 32 slots holding the new entry depend on it, so one
+// launch does both:
+//   - workgroup 0 of query t compresses the newest entry of t's sequence into row
+//     q_base[t] + q_nvis[t] - 1 (compress_entry_wg of compress_few.hpp), then scores that
+//     tile, taking the new entry's indexer row from its own LDS (index_tiles.hpp,
+//     kNewestSlots);
+//   - the other workgroups score every other tile of t's row and read none of that tile's
+//     entries (kOlderSlots).
+// No workgroup reads what another writes, so there is no cross-workgroup synchronisation
+// (a device-scope fence here costs a write-back of the L2 while the scan streams).  The
+// bytes and scores are those of csa2_compress_append followed by csa2_index_score: the
+// append's latency chain (the 512-step projection) runs beside the scan instead of before it.
+#include "compress_few.hpp"
+#include "index_tiles.hpp"
+
+namespace csa2 {
+namespace {
+using namespace idx;
+
+constexpr int kAppendWgs = 1;  // append workgroups per query
+
+template <bool kFp4Q>
+__global__ __launch_bounds__(kThreads) void append_index_kernel(
+    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
+    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
+    const void* __restrict__ q_in, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
+    const int32_t* __restrict__ q_nvis, int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
+  const int t = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  if (blockIdx.x >= kAppendWgs) {
+    score_tiles<false, kFp4Q, kOlderSlots>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
+                                           block_max, t, (int32_t)(blockIdx.x - kAppendWgs) * kWaves + wave,
+                                           (int32_t)(gridDim.x - kAppendWgs) * kWaves);
+    return;
+  }
+  __shared__ EntryShared sh;
+  const int32_t nvis = q_nvis[t];
+  const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
+  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
+                    idx_cache, sh);
+  score_tiles<false, kFp4Q, kNewestSlots>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
+                                          block_max, t, wave, kWaves, sh.idx_row);
+}
+
+// workgroups of append_index_kernel that fit on the device at once (queried per device)
+int resident_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_index_kernel<false>, kThreads, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      per_cu = 2;
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
+}
+
+template <bool kFp4Q>
+int append_index_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
+                       const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const void* q,
+                       const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
+                       float* scores, float* block_max, void* stream) {
+  if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
+  if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
+  if (n_q == 0) return CSA2_OK;
+  if (width == 0) return CSA2_ERR_INVALID_ARG;  // every query appends into a visible slot
+  if (!latent || !rope_cs || !w_idx || !kv_cache || !idx_cache || !q || !head_w || !q_base || !q_nvis ||
+      !scores)
+    return CSA2_ERR_INVALID_ARG;
+  if (m == 2 && !pool_w) return CSA2_ERR_INVALID_ARG;
+  if (n_q > 65535 || width > kMaxIndexWidth) return CSA2_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(w_idx) |
+       reinterpret_cast<uintptr_t>(kv_cache) | reinterpret_cast<uintptr_t>(idx_cache)) & 15)
+    return CSA2_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(q) & (kFp4Q ? 3 : 15)) return CSA2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(rope_cs) | reinterpret_cast<uintptr_t>(pool_w) |
+       reinterpret_cast<uintptr_t>(head_w) | reinterpret_cast<uintptr_t>(scores) |
+       reinterpret_cast<uintptr_t>(block_max)) & 3)
+    return CSA2_ERR_INVALID_ARG;
+  // one round of resident workgroups: the append workgroups, then the scan's share of the rest
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  int64_t scan_x = resident_workgroups() / n_q - kAppendWgs;
+  const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
+  if (scan_x > max_x) scan_x = max_x;
+  if (scan_x < 1) scan_x = 1;
+  hipLaunchKernelGGL(append_index_kernel<kFp4Q>, dim3((unsigned)(kAppendWgs + scan_x), (unsigned)n_q), dim3(kThreads),
+                     0, (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w,
+                     q_base, q_nvis, width, scores, block_max);
+  return check_launch();
+}
+
+}  // namespace
+}  // namespace csa2
+
+extern "C" int csa2_append_index_score(const uint16_t* latent_bf16, int m, const float* pool_w, const float* rope_cs,
+                                       const uint16_t* w_idx_bf16, uint8_t* kv_cache, uint8_t* idx_cache,
+                                       const uint16_t* q_idx_bf16, const float* head_w, const int64_t* q_base,
+                                       const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
+                                       float* block_max, void* stream) {
+  return csa2::append_index_entry<false>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_idx_bf16,
+                                         head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
+}
+
+extern "C" int csa2_append_index_score_fp4q(const uint16_t* latent_bf16, int m, const float* pool_w,
+                                            const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
+                                            uint8_t* idx_cache, const uint8_t* q_fp4, const float* head_w,
+                                            const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
+                                            float* scores, float* block_max, void* stream) {
+  return csa2::append_index_entry<true>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_fp4,
+                                        head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
+}

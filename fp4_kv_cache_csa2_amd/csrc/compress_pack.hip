@@ -9,13 +9,9 @@
 // order (contraction is off in this file, divisions are correctly rounded, the
 // projection is an explicit ascending fma chain), and the quantisers decide codes by
 // exact comparisons, so the packed bytes do not depend on instruction scheduling.
-#include "csa2_device.hpp"
+#include "compress_few.hpp"
 
 #pragma clang fp contract(off)
-
-#ifndef CSA2_FEW_OUT
-#define CSA2_FEW_OUT 32  // indexer outputs per workgroup in the few-entry kernel
-#endif
 
 namespace csa2 {
 namespace {
@@ -209,144 +205,17 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Few entries (the appends of a decode step): one wave per (entry, kOut consecutive
-// indexer outputs), so each workgroup copies only its kOut rows of W_idx (kOut KB, one
-// direct-to-LDS 1 KB row per instruction, issued first) while it pools, rotates and packs
-// its entry (lane l owns channels 8l .. 8l + 7; the workgroup of outputs 0 .. kOut-1 writes
-// the main-KV entry).  Lane o < kOut then runs output o's 512-step ascending fma chain from
-// LDS, and the kOut outputs (whole MXFP4 groups) are packed by lanes 0 .. kOut/8 - 1.
-template <int kOut>
+// Few entries (the appends of a decode step): one workgroup of one wave per (entry, 32
+// consecutive indexer outputs), the body in compress_few.hpp.
 __global__ __launch_bounds__(64) void compress_few_kernel(
-    const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
-    const float* __restrict__ rope_cs, const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out,
-    uint8_t* __restrict__ idx_out, const int64_t* __restrict__ dst_rows) {
-  constexpr int kWRow = kD + 8;  // bf16 per W_idx row in LDS (1040 B: rows start 4 banks apart)
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[kOut * kWRow];
-  __shared__ __attribute__((aligned(16))) float s_c[kD];
-  __shared__ float s_k[kOut];
-  const int lane = threadIdx.x;
+    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
+    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out, uint8_t* __restrict__ idx_out,
+    const int64_t* __restrict__ dst_rows) {
+  __shared__ FewShared sh;
   const int64_t j = blockIdx.x;
-  const int o0 = blockIdx.y * kOut;
-  for (int r = 0; r < kOut; r++)
-    __builtin_amdgcn_global_load_lds(
-        (const void __attribute__((address_space(1)))*)(w_idx + (int64_t)(o0 + r) * kD + 8 * lane),
-        (void __attribute__((address_space(3)))*)&s_w[r * kWRow], 16, 0, 0);
   const int64_t row = dst_rows != nullptr ? dst_rows[j] : j;
-
-  // ---- pooling, RoPE, main-KV pack (lane owns channels ch0 .. ch0 + 7)
-  const int ch0 = 8 * lane;
-  float c[8];
-  if (m == 1) {
-    const uint4 u = *reinterpret_cast<const uint4*>(latent + j * kD + ch0);
-    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      c[2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
-      c[2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
-    }
-  } else {
-    // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
-    const uint4 u0 = *reinterpret_cast<const uint4*>(latent + (2 * j) * kD + ch0);
-    const uint4 u1 = *reinterpret_cast<const uint4*>(latent + (2 * j + 1) * kD + ch0);
-    typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));  // pool_w is 4-byte aligned
-    const f32x4_a4 wa0 = *reinterpret_cast<const f32x4_a4*>(pool_w + ch0);
-    const f32x4_a4 wa1 = *reinterpret_cast<const f32x4_a4*>(pool_w + ch0 + 4);
-    const f32x4_a4 wb0 = *reinterpret_cast<const f32x4_a4*>(pool_w + kD + ch0);
-    const f32x4_a4 wb1 = *reinterpret_cast<const f32x4_a4*>(pool_w + kD + ch0 + 4);
-    const float w0[8] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w};
-    const float w1[8] = {wb0.x, wb0.y, wb0.z, wb0.w, wb1.x, wb1.y, wb1.z, wb1.w};
-    const uint32_t xa[4] = {u0.x, u0.y, u0.z, u0.w}, xb[4] = {u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      const float ws = w0[q] + w1[q];
-      const float a0 = w0[q] / ws, a1 = w1[q] / ws;
-      const uint32_t ba = (q & 1) ? (xa[q >> 1] >> 16) : (xa[q >> 1] & 0xFFFFu);
-      const uint32_t bb = (q & 1) ? (xb[q >> 1] >> 16) : (xb[q >> 1] & 0xFFFFu);
-      const float p0 = a0 * bf16_bits_to_f32(ba);
-      const float p1 = a1 * bf16_bits_to_f32(bb);
-      c[q] = p0 + p1;
-    }
-  }
-  if (ch0 >= kDNope) {  // rope tail: pairs (448+2i, 449+2i)
-    const float* cs = rope_cs + j * kDRope;
-    const int i0 = (ch0 - kDNope) / 2;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const float x0 = c[2 * q], x1 = c[2 * q + 1];
-      const float co = cs[i0 + q], si = cs[kDRope / 2 + i0 + q];
-      const float t0 = x0 * co, t1 = x1 * si, t2 = x0 * si, t3 = x1 * co;
-      c[2 * q] = t0 - t1;
-      c[2 * q + 1] = t2 + t3;
-    }
-  }
-  *reinterpret_cast<float4*>(&s_c[ch0]) = make_float4(c[0], c[1], c[2], c[3]);
-  *reinterpret_cast<float4*>(&s_c[ch0 + 4]) = make_float4(c[4], c[5], c[6], c[7]);
-  if (o0 == 0) {  // one workgroup per entry writes its main-KV bytes
-    float amax = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; q++) amax = __builtin_fmaxf(amax, __builtin_fabsf(c[q]));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));  // the 2 lanes of a 16-channel group
-    const uint32_t sb = e4m3_encode(amax / 6.0f);
-    const float S = e4m3_value(sb);
-    uint32_t word = 0;
-#pragma unroll
-    for (int q = 0; q < 8; q++) word |= e2m1_encode(c[q], S) << (4 * q);
-    if (row >= 0) {
-      uint8_t* dst = kv_out + row * kKvBytes;
-      *reinterpret_cast<uint32_t*>(dst + 4 * lane) = word;
-      if ((lane & 1) == 0) dst[256 + (lane >> 1)] = (uint8_t)sb;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // the W_idx rows have landed in LDS
-  __syncthreads();
-
-  // ---- indexer projection: output o0 + lane, one ascending fma chain from +0
-  if (lane < kOut) {
-    float a = 0.0f;
-    const uint16_t* wr = &s_w[lane * kWRow];
-#pragma unroll 8
-    for (int v = 0; v < kD / 8; v++) {
-      const uint4 wv = *reinterpret_cast<const uint4*>(wr + 8 * v);
-      const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-      const float4 c0 = *reinterpret_cast<const float4*>(&s_c[8 * v]);
-      const float4 c1 = *reinterpret_cast<const float4*>(&s_c[8 * v + 4]);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] & 0xFFFFu), c0.x, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[0] >> 16), c0.y, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] & 0xFFFFu), c0.z, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[1] >> 16), c0.w, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] & 0xFFFFu), c1.x, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[2] >> 16), c1.y, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] & 0xFFFFu), c1.z, a);
-      a = __builtin_fmaf(bf16_bits_to_f32(w4[3] >> 16), c1.w, a);
-    }
-    s_k[lane] = a;
-  }
-  __syncthreads();
-
-  // ---- MXFP4 pack of these kOut outputs: 4 lanes per group of 32, 8 outputs each
-  if (lane < kOut / 8) {
-    const int g = lane >> 2, sub = lane & 3;
-    float v[8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      v[q] = s_k[32 * g + 8 * sub + q];
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
-    }
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
-    const uint32_t code = e8m0_scale_code(amax);
-    const float X = __builtin_ldexpf(1.0f, (int)code - 127);
-    uint32_t word = 0;
-#pragma unroll
-    for (int q = 0; q < 8; q++) word |= e2m1_encode(v[q], X) << (4 * q);
-    if (row >= 0) {
-      const int gg = o0 / 32 + g;  // global group of 32 outputs
-      uint8_t* dst = idx_out + row * kIdxBytes;
-      *reinterpret_cast<uint32_t*>(dst + 16 * gg + 4 * sub) = word;
-      if (sub == 0) dst[64 + gg] = (uint8_t)code;
-    }
-  }
+  compress_few_entry(latent + j * m * kD, m, pool_w, rope_cs + j * kDRope, w_idx, blockIdx.y * kFewOut, row, kv_out,
+                     idx_out, sh);
 }
 
 }  // namespace
@@ -369,9 +238,8 @@ int launch_compress(const uint16_t* latent_bf16, int64_t n_entries, int m, const
       reinterpret_cast<uintptr_t>(dst_rows) & 7)
     return CSA2_ERR_INVALID_ARG;
   if (n_entries <= 64) {
-    hipLaunchKernelGGL(compress_few_kernel<CSA2_FEW_OUT>, dim3((unsigned)n_entries, kIdxDim / CSA2_FEW_OUT), dim3(64),
-                       0, (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16, kv_out,
-                       idx_out, dst_rows);
+    hipLaunchKernelGGL(compress_few_kernel, dim3((unsigned)n_entries, kIdxDim / kFewOut), dim3(64), 0,
+                       (hipStream_t)stream, latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_out, idx_out, dst_rows);
   } else {
     const int64_t grid = (n_entries + 15) / 16;
     if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;

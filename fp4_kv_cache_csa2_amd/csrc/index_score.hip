@@ -1,208 +1,26 @@
-// index_score.hip -- lightning-indexer scoring over the MXFP4 indexer-K cache (gfx950).
+// index_score.hip -- csa2_index_score and csa2_index_score_fp4q: lightning-indexer scores
+// s(t, j) = sum_h w[t,h] * max(0, q[t,h,:] . k^_j) over the MXFP4 indexer-K cache (gfx950).
 //
-// Computes s(t, j) = sum_h w[t,h] * max(0, q[t,h,:] . k^_j) ([ZB] "把 KV Cache 压缩推到极致"
-// §3.3.2: indexer query and per-head weights produce the Top-K set; §2.3.4 / [DF]
-// "CSA2 与每 token 890 字节" §4.7: a Full layer scores every visible entry and reduces
-// blocks of 8 by max, a Reindex layer scores only its candidate pool).
-//
-// Design.  One wavefront owns one query and streams tiles of 32 entries.  The 32 heads
-// x 128 dims contraction runs on v_mfma_f32_32x32x16_bf16 with the heads as the M
-// dimension: the query sits in registers as eight A fragments for the whole scan, and
-// each tile's B fragments are built in registers straight from the packed bytes: every
-// lane loads 32 contiguous payload bytes of one entry (half of its 64) plus the 4-byte
-// scale word, and v_cvt_scalef32_pk_bf16_fp4 turns two E2M1 nibbles and their E8M0
-// power-of-two scale into two exact bf16 values.  The K dimension is permuted so that
-// lane group g and step s hold dims 64g + 8s .. 64g + 8s + 7 for both operands, which
-// leaves the dot products unchanged and makes each lane's bytes contiguous.  ReLU, the
-// head weights and the head sum run on the accumulator registers; a 32-lane swap
-// finishes the sum.  HBM traffic per entry is its 68 bytes plus 4.5 bytes of output.  The
-// waves of the grid walk a query's tiles in grid-stride order, so the whole grid streams
-// one front of the row at a time.
-//
-// Streaming.  All cache reads and score writes go through buffer resources whose sizes
-// bound the row: loads past the end return zeros and stores past the end are dropped.
-// That keeps the tile loop free of branches, so the compiler's memory-counter waits
-// leave the younger tiles in flight, and lets duplicate lanes drop their stores by
-// aiming past the end.  Measured on the 1M-context batch-4 decode, the stores are the
-// costly part beyond the read stream (9.4 MB written against 143 MB read costs about
-// as much as the MFMA and VALU work).
-#include "index_common.hpp"
+// [ZB] "把 KV Cache 压缩推到极致" §3.3.2 and §2.3.4, [DF] "CSA2 与每 token 890 字节" §4.7.
+// Few queries (decode, Reindex pools) run the wave-per-query tile loop of index_tiles.hpp
+// over a grid of one round of resident workgroups; batches of many Full-mode queries
+// (prefill chunks) take the shared-tile kernels of index_score_mq.hip / index_fp4q.hip.
+#include "index_tiles.hpp"
 
 namespace csa2 {
 namespace {
 using namespace idx;
 
-#ifndef CSA2_INDEX_DEPTH
-#define CSA2_INDEX_DEPTH 5
-#endif
-constexpr int kDepth = CSA2_INDEX_DEPTH;  // tiles in flight per wave
-constexpr int kRawBuf = 0x00020000;        // buffer descriptor word 3: raw 32-bit dwords
-
-// kPool: Reindex layers score their candidate pool (entry j of slot p is block
-// pool_blocks[p / 8] * 8 + p % 8); Full layers score entries 0 .. width-1 directly.
-// kFp4Q: the indexer query arrives in MXFP4 (each head vector a 68-byte record like an
-// indexer-K entry, [ZB] §2.4.4: the indexer Q and K are both trained for FP4), and the
-// contraction runs on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands' E2M1 codes and
-// E8M0 scales fed to the instruction as stored: two MFMAs per tile, no conversions.
 template <bool kPool, bool kFp4Q>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const void* __restrict__ q_in, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
     int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
-  const int t = blockIdx.y;
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int n = lane & 31, g = lane >> 5;
-  const int32_t nvis = q_nvis[t];
-  const int64_t base = q_base[t];
-  const int32_t ntiles = (width + kTile - 1) / kTile;
-  // grid-stride tile order: at any moment the grid streams one front of the row
-  const int32_t first = (int32_t)blockIdx.x * kWaves + wave;
-  const int32_t tstride = (int32_t)gridDim.x * kWaves;
-  const int32_t nt = first < ntiles ? (ntiles - first + tstride - 1) / tstride : 0;  // this wave's tiles
-  const int32_t nbw = (width + kBlock - 1) / kBlock;
-  float* srow = scores + (int64_t)t * width;
-
-  if (nvis <= 0) {  // nothing visible: the row is all -inf
-    for (int32_t k = 0; k < nt; k++) {
-      const int32_t p = (first + k * tstride) * kTile + n;
-      if (g == 0 && p < width) srow[p] = -__builtin_inff();
-      if (block_max != nullptr && g == 0 && (n & 7) == 0 && p < width)
-        block_max[(int64_t)t * nbw + (p >> 3)] = -__builtin_inff();
-    }
-    return;
-  }
-
-  // the query (head n, dims 64g .. 64g + 63: eight bf16x8 A fragments, or for an MXFP4
-  // query two 32-code fragments and the head's scale word) and the head weight of each
-  // accumulator row this lane holds (row 8(r/4) + 4g + r%4); both are loaded after the
-  // first cache tiles, so the stream from HBM starts first
-  bf16x8 a[8];
-  fp4x32 qa[2];
-  uint32_t qsc = 0;
-  float wr[16];
-
-  // Buffer resources bound the sequence's visible cache rows, the score row and the
-  // block-max row (empty when block_max is NULL): loads past the end return zeros and
-  // stores past the end are dropped,
-  // so the streaming loop below needs no branches (and the compiler's memory-counter
-  // waits stay exact).  Offsets are 32-bit: the host limits width to 2^23 entries.
-  const int32_t nv = min(nvis, kMaxIndexWidth);  // rows past 2^23 are never addressed
-  const __amdgpu_buffer_rsrc_t rs_cache =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(idx_cache + base * kIdxBytes), (short)0, nv * kIdxBytes, kRawBuf);
-  const __amdgpu_buffer_rsrc_t rs_score = __builtin_amdgcn_make_buffer_rsrc(srow, (short)0, width * 4, kRawBuf);
-  const __amdgpu_buffer_rsrc_t rs_bmax = __builtin_amdgcn_make_buffer_rsrc(
-      block_max != nullptr ? (void*)(block_max + (int64_t)t * nbw) : (void*)srow, (short)0,
-      block_max != nullptr ? nbw * 4 : 0, kRawBuf);
-  const __amdgpu_buffer_rsrc_t rs_pool = __builtin_amdgcn_make_buffer_rsrc(
-      kPool ? (void*)(pool_blocks + (int64_t)t * M) : (void*)srow, (short)0, kPool ? M * 4 : 0, kRawBuf);
-  constexpr int32_t kOut = 1 << 30;  // a byte offset past every buffer's end
-
-  // byte offset of this lane's cache row in tile k (past the end when the slot is empty)
-  auto row_off = [&](int32_t k, bool& valid) -> int32_t {
-    const int32_t p = (first + k * tstride) * kTile + n;
-    int32_t j;
-    if constexpr (kPool) {
-      const int32_t b = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs_pool, 4 * (p >> 3), 0, 0);
-      const int64_t jj = (int64_t)b * kBlock + (p & 7);
-      valid = (p >> 3) < M && b >= 0 && jj < nv;
-      j = (int32_t)jj;
-    } else {
-      j = p;
-      valid = p < nv;
-    }
-    return valid ? j * kIdxBytes : kOut;
-  };
-  auto load = [&](int32_t k, RawTile& r) {
-    const int32_t off = row_off(k, r.valid);
-    r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, off + 32 * g, 0, 0));
-    r.hi = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, off + 32 * g + 16, 0, 0));
-    r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs_cache, off + 64, 0, 0);
-  };
-  auto process = [&](const RawTile& cur, int32_t k) {
-    f32x16 acc = {};
-    if constexpr (kFp4Q) {
-      acc = mfma_fp4_tile(qa, qsc, cur.lo, cur.hi, cur.sc >> (16 * g), acc);
-    } else {
-      const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
-      const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
-      const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3],
-                                 cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
-#pragma unroll
-      for (int s = 0; s < 8; s++) {
-        const bf16x8 b = cvt_fp4x8(words[s], s < 4 ? x0 : x1);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
-      }
-    }
-    // ReLU, head weight and the sum over this lane's 16 heads as four short chains
-    float part[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      part[c] = wr[4 * c] * relu(acc[4 * c]);
-#pragma unroll
-      for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], relu(acc[4 * c + r]), part[c]);
-    }
-    const float sc = masked_score(sum_halves((part[0] + part[1]) + (part[2] + part[3])), cur.valid);
-    // both lane halves hold the entry's score and all 8 lanes of a block its maximum; one
-    // lane writes each value and the others aim past the buffer's end, so their stores
-    // are dropped without a branch (as are slots past the row's end)
-    const int32_t p = (first + k * tstride) * kTile + n;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, g ? kOut : 4 * p, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax,
-                                          (g | (n & 7)) ? kOut : 4 * (p >> 3), 0, 0);
-  };
-
-  // The query and head weights are loaded first, then the first kDepth tiles, and a wait
-  // for all but the tiles' loads completes the query before the loop.  The compiler then
-  // knows the query registers are ready inside the loop; otherwise it re-checks them on
-  // every pass with a wait that drains this wave's tiles in flight (loads complete in order).
-  {
-    if constexpr (kFp4Q) {
-      load_fp4_query(static_cast<const uint8_t*>(q_in) + ((int64_t)t * kIdxHeads + n) * kIdxBytes, g, qa, qsc);
-    } else {
-      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_in) +
-                                                       ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
-#pragma unroll
-      for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
-    }
-    typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-    const f32x4_a4* wp = reinterpret_cast<const f32x4_a4*>(head_w + (int64_t)t * kIdxHeads);
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const f32x4_a4 v = wp[2 * c + g];  // rows 8c + 4g .. 8c + 4g + 3
-#pragma unroll
-      for (int r = 0; r < 4; r++) wr[4 * c + r] = v[r];
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // software pipeline: kDepth - 1 tiles of this wave are in flight while one is processed.
-  // Full groups of kDepth tiles stream through the loop; loads past the wave's last tile
-  // return zeros and are never processed; the last partial group is finished after it.
-  // (the scheduling barriers keep the tiles' loads in tile order, so each tile's wait
-  // counts only older loads)
-  RawTile pipe[kDepth];
-#pragma unroll
-  for (int u = 0; u < kDepth; u++) {
-    load(u, pipe[u]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // Full mode issues three loads per tile; a pool tile's block-id load precedes its three
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDepth * (kPool ? 4 : 3)));
-  int32_t k0 = 0;
-  for (; k0 + kDepth <= nt; k0 += kDepth) {
-#pragma unroll
-    for (int u = 0; u < kDepth; u++) {
-      process(pipe[u], k0 + u);
-      load(k0 + u + kDepth, pipe[u]);  // reuses this tile's registers, so none are copied
-      // the MXFP4-query body leaves the scheduler room to interleave different tiles' loads,
-      // which would make each tile's wait cover younger tiles too: keep them in tile order
-      if constexpr (kFp4Q) __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kDepth - 1; u++)
-    if (k0 + u < nt) process(pipe[u], k0 + u);
+  score_tiles<kPool, kFp4Q, kAllSlots>(q_in, head_w, idx_cache, q_base, q_nvis, pool_blocks, M, width, scores,
+                                       block_max, blockIdx.y, (int32_t)blockIdx.x * kWaves + wave,
+                                       (int32_t)gridDim.x * kWaves);
 }
 
 }  // namespace

@@ -167,6 +167,46 @@ int csa2_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8
                           void *stream);
 
 /*
+ * csa2_append_index_score -- a decode step's append and indexer scores in one launch:
+ *   the result of csa2_compress_append of each query's newest entry followed by
+ *   csa2_index_score in Full mode.
+ *   [DF] §4.3 (a decoding token completes the newest entry of its sequence, and the Full
+ *   layer then scores every visible entry, the newest included), [DF] §4.2 / §4.4 and
+ *   [ZB] §2.3.1 / §2.4.4 (the entry, as in csa2_compress_pack), [ZB] §3.3.2 / §2.3.4 (the
+ *   scores and block maxima, as in csa2_index_score).  Only the scores of the tile of 32
+ *   slots holding the newest entry depend on the append; one workgroup per query packs the
+ *   entry and then scores that tile, while the others score every other tile.
+ *
+ *   Query t appends one entry: latent_bf16 rows [t*m, t*m + m) (bf16 [n_q*m, 512],
+ *   16-byte aligned), pool_w fp32 [m, 512] (not read when m = 1), rope_cs fp32 [n_q, 64]
+ *   (the entry's cos[32], sin[32]), w_idx_bf16 [128, 512] (16-byte aligned), written to
+ *   row q_base[t] + q_nvis[t] - 1 of kv_cache [rows, 288] and idx_cache [rows, 68]
+ *   (16-byte aligned bases); q_nvis[t] counts the new entry.  Queries must append to
+ *   distinct rows.  A query with q_nvis[t] <= 0 appends nothing and gets an all -inf row.
+ *   q_idx_bf16, head_w, q_base, q_nvis, width, scores and block_max are those of
+ *   csa2_index_score in Full mode (no pool), with the same results bit for bit; the
+ *   cache bytes are those of csa2_compress_append.
+ *   Errors: INVALID_ARG (NULL required pointer, n_q < 0, width <= 0 with n_q > 0,
+ *   misalignment), UNSUPPORTED (m not 1 or 2, n_q > 65535, width > 2^23).
+ */
+int csa2_append_index_score(const uint16_t *latent_bf16, int m, const float *pool_w, const float *rope_cs,
+                            const uint16_t *w_idx_bf16, uint8_t *kv_cache, uint8_t *idx_cache,
+                            const uint16_t *q_idx_bf16, const float *head_w, const int64_t *q_base,
+                            const int32_t *q_nvis, int32_t n_q, int32_t width, float *scores,
+                            float *block_max, void *stream);
+
+/*
+ * csa2_append_index_score_fp4q -- csa2_append_index_score with the indexer query in MXFP4
+ *   (q_fp4 [n_q, 32, 68], 4-byte aligned, from csa2_quantize_q_mxfp4): the scores of
+ *   csa2_index_score_fp4q.  Every other argument, result and error as above.
+ */
+int csa2_append_index_score_fp4q(const uint16_t *latent_bf16, int m, const float *pool_w,
+                                 const float *rope_cs, const uint16_t *w_idx_bf16, uint8_t *kv_cache,
+                                 uint8_t *idx_cache, const uint8_t *q_fp4, const float *head_w,
+                                 const int64_t *q_base, const int32_t *q_nvis, int32_t n_q, int32_t width,
+                                 float *scores, float *block_max, void *stream);
+
+/*
  * csa2_block_topk -- hierarchical selection: block max -> top-M block pool -> Top-K.
  *   [ZB] §2.3.4 and [DF] §4.7: g_r = max over block r (b = `block` positions, -inf
  *   padding); the block holding the newest visible position takes +inf; the M blocks

@@ -1,0 +1,151 @@
+"""GPU parity of the fused decode append + indexer scoring (csa2_append_index_score and its
+MXFP4-query twin): bit for bit what csa2_compress_append followed by csa2_index_score
+produce (cache bytes, scores, block maxima), the appended bytes against the oracle's
+compressor, the scores against the oracle's indexer over the updated cache, two calls in a
+row, ragged rows, an empty row, rows whose newest entry opens a block or a tile, rows
+shorter than the score width, and the 1M-context batch-4 decode in the launch geometry the
+bench uses.  The appended rows start out holding other bytes,
+so a score computed from stale bytes would show."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_kv_cache_csa2_amd import synth
+from tests.gpu_util import bf16, check_scores, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def c():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp4_kv_cache_csa2_amd import csa2
+    return csa2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+class Case:
+    """n_q sequences of rows_per_seq cache rows each, query t appending entry nvis[t] - 1."""
+
+    def __init__(self, c, seed, nvis, width, m, rows_per_seq=None):
+        self.nvis = np.array(nvis, np.int32)
+        self.n_q = n_q = len(nvis)
+        self.width, self.m = width, m
+        self.rows = rows_per_seq or max(1, int(self.nvis.max()))
+        self.kv, self.ix = synth.random_caches(seed, n_q * self.rows)
+        self.base = np.arange(n_q, dtype=np.int64) * self.rows
+        self.ci = synth.compress_inputs(seed + 1, n_q, m)
+        self.pos = (np.maximum(self.nvis, 1) - 1).astype(np.int64) * m
+        self.cs = c.rope_table(self.pos).numpy()
+        self.d = synth.query_inputs(seed + 2, n_q)
+        self.dst = np.where(self.nvis > 0, self.base + self.nvis - 1, -1).astype(np.int64)
+
+
+def _separate(c, k, fp4):
+    kv, ix = dev(k.kv), dev(k.ix)
+    c.compress_append(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), dev(k.dst), kv, ix)
+    q = c.quantize_q_mxfp4(bf16(k.d.q_idx)) if fp4 else bf16(k.d.q_idx)
+    score = c.index_score_fp4q if fp4 else c.index_score
+    s, b = score(q, dev(k.d.head_w), ix, dev(k.base), dev(k.nvis), k.width)
+    return kv, ix, s, b
+
+
+def _fused(c, k, fp4, kv=None, ix=None):
+    kv = dev(k.kv) if kv is None else kv
+    ix = dev(k.ix) if ix is None else ix
+    q = c.quantize_q_mxfp4(bf16(k.d.q_idx)) if fp4 else bf16(k.d.q_idx)
+    s, b = c.append_index_score(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), kv, ix, q,
+                                dev(k.d.head_w), dev(k.base), dev(k.nvis), k.width)
+    return kv, ix, s, b
+
+
+def _same(a, b):
+    for x, y, what in zip(a, b, ("main-KV cache", "indexer cache", "scores", "block maxima")):
+        gx, gy = host(x), host(y)
+        if gx.dtype == np.float32:
+            gx, gy = gx.view(np.uint32), gy.view(np.uint32)
+        bad = np.argwhere(gx != gy)
+        assert bad.size == 0, f"{what}: {len(bad)} elements differ, first {bad[:4].tolist()}"
+
+
+CASES = [
+    # nvis per query, width, m
+    ([1000, 8, 9, 33, 1, 0, 4096], 4096, 2),  # blocks opened by the new entry, a lone entry, an empty row
+    ([777, 32, 64, 65], 800, 1),               # rows shorter than the width, tile edges
+    ([5000, 4999, 4993, 4992], 5000, 2),
+]
+
+
+@pytest.mark.parametrize("fp4", [False, True], ids=["bf16_q", "fp4_q"])
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_fused_equals_append_then_score(c, ci, fp4):
+    nvis, width, m = CASES[ci]
+    log(f"append_index nvis={nvis} width={width} m={m} fp4={fp4}")
+    k = Case(c, 500 + 10 * ci, nvis, width, m)
+    ref = _separate(c, k, fp4)
+    got = _fused(c, k, fp4)
+    torch.cuda.synchronize()
+    _same(ref, got)
+    # a second call on the result appends the same entries again: same results
+    again = _fused(c, k, fp4, kv=got[0], ix=got[1])
+    torch.cuda.synchronize()
+    _same(ref, again)
+
+
+@pytest.mark.parametrize("fp4", [False, True], ids=["bf16_q", "fp4_q"])
+def test_fused_against_the_oracle(c, fp4):
+    nvis, width, m = CASES[0]
+    log(f"append_index vs oracle fp4={fp4}")
+    k = Case(c, 530, nvis, width, m)
+    kv, ix, s, b = _fused(c, k, fp4)
+    torch.cuda.synchronize()
+    kv, ix, s, b = host(kv), host(ix), host(s), host(b)
+    kv_ref, ix_ref = oracle.compress_pack(k.ci.latent, m, k.ci.pool_w, oracle.rope_table(k.pos), k.ci.w_idx)
+    for t in range(k.n_q):
+        r = k.dst[t]
+        if r < 0:
+            continue
+        assert np.array_equal(kv[r], kv_ref[t]), f"query {t}: main-KV bytes"
+        assert np.array_equal(ix[r], ix_ref[t]), f"query {t}: indexer bytes"
+    untouched = np.setdiff1d(np.arange(len(k.kv)), k.dst[k.dst >= 0])
+    assert np.array_equal(kv[untouched], k.kv[untouched]) and np.array_equal(ix[untouched], k.ix[untouched])
+    if fp4:
+        ref = oracle.index_score_fp4q(oracle.quantize_q_mxfp4(k.d.q_idx), k.d.head_w, ix, k.base, k.nvis, width)
+    else:
+        ref = oracle.index_score(k.d.q_idx, k.d.head_w, ix, k.base, k.nvis, width)
+    check_scores(s, ref)
+    nbw = -(-width // 8)
+    pad = np.full((k.n_q, nbw * 8), -np.inf, np.float32)
+    pad[:, :width] = s
+    assert np.array_equal(b, pad.reshape(k.n_q, nbw, 8).max(axis=2)), "block maxima are not those of the scores"
+
+
+@pytest.mark.parametrize("fp4", [False, True], ids=["bf16_q", "fp4_q"])
+def test_fused_decode_1m_b4(c, fp4):
+    """4 x 524288 entries, each query appending its sequence's last entry, as the bench's step."""
+    n, n_q = 524288, 4
+    log(f"append_index 1M: drawing caches fp4={fp4}")
+    k = Case(c, 540 + fp4, [n] * n_q, n, 2)
+    ref = _separate(c, k, fp4)
+    log("append_index 1M: fused")
+    got = _fused(c, k, fp4)
+    torch.cuda.synchronize()
+    _same(ref, got)
+    # the newest tile of each row against the oracle (the rest is the plain scan, equal above)
+    ix = host(got[1])
+    s = host(got[2])
+    lo = n - 32
+    for t in range(n_q):
+        sub = ix[k.base[t] + lo:k.base[t] + n]
+        q = k.d.q_idx[t:t + 1]
+        if fp4:
+            r = oracle.index_score_fp4q(oracle.quantize_q_mxfp4(q), k.d.head_w[t:t + 1], sub, np.zeros(1, np.int64),
+                                        np.array([32], np.int32), 32)
+        else:
+            r = oracle.index_score(q, k.d.head_w[t:t + 1], sub, np.zeros(1, np.int64), np.array([32], np.int32), 32)
+        check_scores(s[t:t + 1, lo:], r)
