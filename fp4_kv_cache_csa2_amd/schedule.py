@@ -11,7 +11,9 @@ Layer plan ([DF] "4. Â±ÇÁª¥Â∫¶(‰∏ã):CSA2 ‰∏éÊØè token 890 Â≠óËäÇ" ¬ß4.3; [ZB] "Ê
 The SWA-only layers touch no global cache and are not part of this path.
 
 A token at position p completes an entry of a ratio-m cache when p + 1 is a multiple of
-m; the Full layer of that cache then packs it from the m newest latents of its source.
+m; the Full layer of that cache then packs it from the m newest latents of its source, in
+the same launch as its scan of the cache (csa2_append_index_score) when the new entry is
+the newest visible one.
 Device tensors only: every step runs in the library's kernels; the host decides which
 call comes next from the plan and the position.
 """
@@ -107,17 +109,25 @@ class GlobalBranch:
             inp = inputs[layer]
             if mode == "full":
                 m = RATIO[c]
-                if (p + 1) % m == 0:  # this token completes entry j of cache c
-                    j = (p + 1) // m - 1
-                    rows = self._const(("rows", c, j), lambda: self.base[c] + j)
-                    cs = self._const(("rope", c, j), lambda: csa2.rope_table(np.full(ns, m * j, np.int64)).to(self.dev))
-                    pool_w, w_idx = self.params[c]
-                    csa2.compress_append(new_latents[c], m, pool_w, cs, w_idx, rows, self.kv[c], self.ix[c])
+                j = (p + 1) // m - 1 if (p + 1) % m == 0 else None  # this token completes entry j of cache c
+                if j is not None:
                     self.n[c] = max(self.n[c], j + 1)
                 n = self.n[c]
                 nvis = self._nvis(n)
-                csa2.index_score(inp["q_idx"], inp["head_w"], self.ix[c], self.base[c], nvis, n,
-                                 scores=self._row_view(n), block_max=self._bmax_view(n))
+                if j is not None:
+                    cs = self._const(("rope", c, j), lambda: csa2.rope_table(np.full(ns, m * j, np.int64)).to(self.dev))
+                    pool_w, w_idx = self.params[c]
+                if j is not None and j == n - 1:
+                    # the new entry is the newest visible one: append it and score in one launch
+                    csa2.append_index_score(new_latents[c], m, pool_w, cs, w_idx, self.kv[c], self.ix[c],
+                                            inp["q_idx"], inp["head_w"], self.base[c], nvis, n,
+                                            scores=self._row_view(n), block_max=self._bmax_view(n))
+                else:
+                    if j is not None:
+                        rows = self._const(("rows", c, j), lambda: self.base[c] + j)
+                        csa2.compress_append(new_latents[c], m, pool_w, cs, w_idx, rows, self.kv[c], self.ix[c])
+                    csa2.index_score(inp["q_idx"], inp["head_w"], self.ix[c], self.base[c], nvis, n,
+                                     scores=self._row_view(n), block_max=self._bmax_view(n))
                 csa2.block_topk(self._row_view(n), nvis, K=K, M=M, block_max=self._bmax_view(n),
                                 pool_out=self.pool, topk_out=self.topk, workspace=self.ws_sel)
             elif mode == "reindex":
