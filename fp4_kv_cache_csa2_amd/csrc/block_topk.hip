@@ -718,6 +718,23 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   const uint32_t* lkeys = (use_a ? ws.keys_a : ws.keys_b) + (int64_t)t * G * seg_stride;
   const int want = role == 0 ? M - 1 : K;
 
+  // The first round of the list gather (segments wave + 16k) loads its segments' first 128
+  // slots now, before their counts and offsets are known, so these loads and the
+  // histogram's are in flight together.  Slots past a segment's count hold stale values
+  // and are never used; every slot read lies inside the segment's fixed-size region.
+  int32_t pre_id[4][2];
+  uint32_t pre_key[4][2];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int g = wave + k * kFWaves;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int64_t src = (int64_t)(g < G ? g : 0) * seg_stride + 64 * h + lane;
+      pre_id[k][h] = lids[src];
+      pre_key[k][h] = lkeys[src];
+    }
+  }
+
   // ---- histogram boundary (list A) and segment offsets, in one pass of two scans
   uint32_t c[kBinsPer];
   uint32_t local = 0;
@@ -775,9 +792,27 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   if (take_all_blocks) {
     cnt = max(r.nb - 1, 0);
   } else if (listed) {
-    // gather the list: wave w copies segments w, w + 16, ... (one lane per item), four
-    // segments' loads in flight at a time; segments longer than 64 items loop on
-    for (int g0 = wave; g0 < G; g0 += 4 * kFWaves) {
+    // gather the list: wave w copies segments w, w + 16, ... (one lane per item).  The first
+    // round's first 128 slots are already in registers; the rest loads four segments at a
+    // time, and segments longer than that loop on
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int g = wave + k * kFWaves;
+      const int off = g < G ? sh.seg_off[g] : 0;
+      const int n = g < G ? sh.seg_off[g + 1] - off : 0;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        if (64 * h + lane < n) {
+          sh.ids[off + 64 * h + lane] = pre_id[k][h];
+          sh.keys[off + 64 * h + lane] = pre_key[k][h];
+        }
+      }
+      for (int e = 128 + lane; e < n; e += 64) {
+        sh.ids[off + e] = lids[(int64_t)g * seg_stride + e];
+        sh.keys[off + e] = lkeys[(int64_t)g * seg_stride + e];
+      }
+    }
+    for (int g0 = wave + 4 * kFWaves; g0 < G; g0 += 4 * kFWaves) {
       int32_t gid[4], dst[4], cnt4[4], off4[4];
       uint32_t gkey[4];
 #pragma unroll
