@@ -71,6 +71,21 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// Maximum and minimum over the 64 lanes of a wave with the same DPP pattern, returned to
+// every lane (lane 63 holds the result after the row broadcasts)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return ~wave_max_u32(~x);
+}
+
 // Exclusive prefix sum of v over the threads of a workgroup of NT threads, in thread
 // order; total receives the sum over all threads.  s_w holds NT/64 ints.
 template <int NT>
@@ -221,9 +236,10 @@ constexpr int kBinsPer = kBins / kFThreads; // histogram bins per K3 thread
 constexpr int kSegPer = kMaxG / kFThreads;  // K2 segments per K3 thread
 
 struct ListScratch {
-  uint32_t hist[3][256];  // digit histograms, rotated so each pass needs one barrier
+  uint32_t hist[3][256];  // digit histograms, rotated so no pass waits to clear one
   int32_t wcnt[2][kFWaves];
   uint32_t red[3][kFWaves];
+  int32_t dec[4];  // a pass's decision: digit (-1: take every matching key), remain, eq_total, total
 };
 
 // Exact selection over a list of at most kListCap keys in LDS by the K3 workgroup.  The
@@ -236,7 +252,9 @@ struct ListScratch {
 // never selected.  Writes the chosen positions ascending to out[], returns their number,
 // and sets *thr to a lower bound of every selected key (the resolved prefix).  Wave w
 // owns the contiguous run [w*seg, (w+1)*seg) and holds it in registers, so a radix pass
-// is a burst of LDS atomics, one barrier and a scan that each wave does itself.
+// is a burst of LDS atomics, a barrier, wave 0's scan of the 256 digit counts and a
+// second barrier that hands its decision to every wave (sixteen waves repeating the scan
+// would queue four deep on each SIMD).
 __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t prefix, uint32_t mask, int shift,
                                            int remain, int eq_total, ListScratch& s, int32_t* out, uint32_t* thr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -272,12 +290,9 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
       kmax = max(kmax, key);
       cnt += key != 0u ? 1u : 0u;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-      cnt += (uint32_t)__shfl_xor((int)cnt, o);
-    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), 63);
     if (lane == 0) {
       s.red[0][wave] = kmin;
       s.red[1][wave] = kmax;
@@ -319,36 +334,50 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
       if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> nshift) & dmask], 1u);
     }
     __syncthreads();
-    // lane l owns digits 255-4l .. 252-4l (descending)
-    uint32_t c[4], local = 0;
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      uint32_t c[4], local = 0;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      c[q] = h[255 - 4 * lane - q];
-      local += c[q];
-    }
-    const uint32_t incl = wave_incl_scan(local);
-    const int total = __builtin_amdgcn_readlane((int)incl, 63);
-    uint32_t above = incl - local;
-    int hit = -1, hit_rem = 0, hit_cnt = 0;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      if ((int)above < remain && remain <= (int)(above + c[q])) {
-        hit = 255 - 4 * lane - q;
-        hit_rem = remain - (int)above;
-        hit_cnt = (int)c[q];
+      for (int q = 0; q < 4; q++) {
+        c[q] = h[255 - 4 * lane - q];
+        local += c[q];
       }
-      above += c[q];
+      const uint32_t incl = wave_incl_scan(local);
+      const int total = __builtin_amdgcn_readlane((int)incl, 63);
+      uint32_t above = incl - local;
+      int hit = -1, hit_rem = 0, hit_cnt = 0;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        if ((int)above < remain && remain <= (int)(above + c[q])) {
+          hit = 255 - 4 * lane - q;
+          hit_rem = remain - (int)above;
+          hit_cnt = (int)c[q];
+        }
+        above += c[q];
+      }
+      const uint64_t hb = __ballot(hit >= 0);
+      const int src = hb == 0ull ? 0 : __ffsll((unsigned long long)hb) - 1;
+      // the lane reads run with the whole wave active: under a lane-0 branch the compiler
+      // may compute hit and its companions for lane 0 alone
+      const int d0 = hb == 0ull ? -1 : __builtin_amdgcn_readlane(hit, src);
+      const int d1 = __builtin_amdgcn_readlane(hit_rem, src);
+      const int d2 = __builtin_amdgcn_readlane(hit_cnt, src);
+      if (lane == 0) {
+        s.dec[0] = d0;
+        s.dec[1] = d1;
+        s.dec[2] = d2;
+        s.dec[3] = total;
+      }
     }
-    const uint64_t hb = __ballot(hit >= 0);
-    if (hb == 0ull) {  // fewer matching keys than wanted: take them all
-      remain = total;
-      eq_total = total;
+    __syncthreads();
+    const int dd = __builtin_amdgcn_readfirstlane(s.dec[0]);
+    if (dd < 0) {  // fewer matching keys than wanted: take them all
+      remain = eq_total = __builtin_amdgcn_readfirstlane(s.dec[3]);
       break;
     }
-    const int src = __ffsll((unsigned long long)hb) - 1;
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(hit, src);
-    remain = __builtin_amdgcn_readlane(hit_rem, src);
-    eq_total = __builtin_amdgcn_readlane(hit_cnt, src);
+    const uint32_t d = (uint32_t)dd;
+    remain = __builtin_amdgcn_readfirstlane(s.dec[1]);
+    eq_total = __builtin_amdgcn_readfirstlane(s.dec[2]);
     prefix |= d << nshift;
     mask |= dmask << nshift;
     shift = nshift;
