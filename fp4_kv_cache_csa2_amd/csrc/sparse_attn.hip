@@ -38,13 +38,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));  // 16 B at an 8-B boundary
 
-constexpr int kMaxKeys = kMaxTopK + kMaxSwa;
 
 struct __attribute__((aligned(16))) AttnShared {
   _Float16 k[kChunk * kKStride] __attribute__((aligned(16)));  // decoded keys, row-major [key][dim]
   _Float16 p[kWaves * 16 * kPStride] __attribute__((aligned(16)));  // per-wave probabilities [head][key]
   int32_t valid[kChunk];
-  int32_t ids[kMaxKeys];  // the workgroup's selected-entry ids, loaded once
 };
 
 // Raw bytes of one key slot for one thread (a quarter of a key), prefetched a chunk ahead:
@@ -65,8 +63,6 @@ template <bool kFp8Win>
 struct KeyStager {
   const uint8_t* kv_cache;
   const int32_t* topk_row;
-  const int32_t* ids;  // LDS copy of topk_row[x_begin ..] (load_ids)
-  int32_t x_begin;
   int32_t K;
   const void* swa_v;
   int64_t swa_ring;
@@ -90,17 +86,13 @@ struct KeyStager {
     // rows, which start 4 banks apart, so the 16-byte LDS stores of a wave do not conflict
     kk = tid & 63;
     qq = tid >> 6;
-    ids = nullptr;
-    x_begin = 0;
   }
 
-  // copies the selected ids of chunks c_begin .. c_end - 1 into LDS (all threads take part;
-  // the caller synchronises before the first fetch)
-  __device__ __forceinline__ void load_ids(int c_begin, int c_end, AttnShared& sh, int tid) {
-    x_begin = c_begin * kChunk;
-    const int x_end = min(c_end * kChunk, K);
-    for (int x = x_begin + tid; x < x_end; x += kThreads) sh.ids[x - x_begin] = topk_row[x];
-    ids = sh.ids;
+  // the selected-entry id of this thread's key slot in chunk c (a window row or past the
+  // end: -1), read straight into a register so the key loads need no barrier
+  __device__ __forceinline__ int32_t load_id(int c) const {
+    const int x = c * kChunk + kk;
+    return x < K ? topk_row[x] : -1;
   }
 
   // buffer row of window row r (wrapped inside the sequence's ring when there is one)
@@ -110,12 +102,11 @@ struct KeyStager {
     return row + wseg;
   }
 
-  // raw loads of this thread's key quarter for chunk c
-  __device__ __forceinline__ void fetch(int c, KeyRaw& r) const {
+  // raw loads of this thread's key quarter for chunk c (id: load_id(c))
+  __device__ __forceinline__ void fetch(int c, int32_t id, KeyRaw& r) const {
     const int x = c * kChunk + kk;
     r.kind = 0;
     if (x < K) {
-      const int32_t id = ids[x - x_begin];
       if (id >= 0) {
         r.kind = 1;
         const uint8_t* row = kv_cache + (base + id) * kKvBytes;
@@ -278,19 +269,31 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   KeyStager<kFp8Win> ks(kv_cache, topk + (int64_t)t * K, K, swa_v, swa_ring, q_base[t], swa_start[t], swa_len[t],
                          tid);
 
+  // Loads go out in dependency order so that their round trips overlap: this thread's
+  // entry ids of the first two chunks, the query, then the first chunk's key rows (which
+  // wait only for the first id), and the query is converted after the key loads are out.
+  int32_t id_next = c_begin < c_end ? ks.load_id(c_begin) : -1;
+  int32_t id_after = c_begin + 1 < c_end ? ks.load_id(c_begin + 1) : -1;
+  __builtin_amdgcn_sched_barrier(0);
   // query fragments: head 16w + i, dims 32s + 8g .. +7, as f16 (exact in the normal range)
-  f16x8 qa[16];
+  uint4 qraw[16];
   {
     const uint16_t* qh = q + ((int64_t)t * kHeads + 16 * w + i) * kD + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 16; s++) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qh + 32 * s);
-      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+    for (int s = 0; s < 16; s++) qraw[s] = *reinterpret_cast<const uint4*>(qh + 32 * s);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  KeyRaw raw;
+  if (c_begin < c_end) ks.fetch(c_begin, id_next, raw);
+  __builtin_amdgcn_sched_barrier(0);
+  f16x8 qa[16];
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        qa[s][2 * v] = (_Float16)bf16_bits_to_f32(wd[v] & 0xFFFFu);
-        qa[s][2 * v + 1] = (_Float16)bf16_bits_to_f32(wd[v] >> 16);
-      }
+  for (int s = 0; s < 16; s++) {
+    const uint32_t wd[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      qa[s][2 * v] = (_Float16)bf16_bits_to_f32(wd[v] & 0xFFFFu);
+      qa[s][2 * v + 1] = (_Float16)bf16_bits_to_f32(wd[v] >> 16);
     }
   }
 
@@ -304,14 +307,13 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     l_run[r] = 0.0f;
   }
 
-  ks.load_ids(c_begin, c_end, sh, tid);
-  __syncthreads();
-  KeyRaw raw;
-  if (c_begin < c_end) ks.fetch(c_begin, raw);
   for (int c = c_begin; c < c_end; c++) {
     __syncthreads();  // the previous chunk's LDS reads are done
     ks.stage(raw, sh);
-    if (c + 1 < c_end) ks.fetch(c + 1, raw);  // next chunk's gather overlaps this chunk's math
+    if (c + 1 < c_end) {  // next chunk's gather overlaps this chunk's math; its id was loaded a chunk ago
+      ks.fetch(c + 1, id_after, raw);
+      id_after = c + 2 < c_end ? ks.load_id(c + 2) : -1;
+    }
     __syncthreads();
 
     // ---- S = Q K^T for 4 tiles of 16 keys
