@@ -47,10 +47,13 @@ struct __attribute__((aligned(16))) AttnShared {
 
 // Raw bytes of one key slot for one thread (a quarter of a key), prefetched a chunk ahead:
 // a selected entry's 64 payload bytes and 8 E4M3 scale bytes, or a window row's quarter
-// (256 bytes of bf16, or 152 bytes of an FP8 row: 112 code bytes, 32 bf16 bytes, the
-// 8-byte scale word).
+// (256 bytes of bf16, or 144 bytes of an FP8 row: 112 code bytes, 32 bf16 bytes), with the
+// FP8 row's 8-byte scale word.  The scale words of both kinds sit in sw, so the two loads
+// that fill it write one place (with different array slots the compiler merged them into
+// a store at a computed index, which put the array in scratch memory).
 struct KeyRaw {
   uint4 d[16];
+  uint2 sw;
   int kind;       // 0 empty, 1 selected entry, 2 window row
 };
 
@@ -113,7 +116,7 @@ struct KeyStager {
 #pragma unroll
         for (int v = 0; v < 4; v++) r.d[v] = reinterpret_cast<const uint4*>(row + 64 * qq)[v];
         const uint2 sw = *reinterpret_cast<const uint2*>(row + 256 + 8 * qq);
-        r.d[4] = make_uint4(sw.x, sw.y, 0u, 0u);
+        r.sw = sw;
       }
     } else if (x - K < nswa) {
       r.kind = 2;
@@ -132,7 +135,7 @@ struct KeyStager {
           r.d[7 + j] = make_uint4(v[0], v[1], v[2], v[3]);
         }
         const uint2 sw = *reinterpret_cast<const uint2*>(src + kDNope + 2 * kDRope);
-        r.d[9] = make_uint4(sw.x, sw.y, 0u, 0u);
+        r.sw = sw;
       } else {
         const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(swa_v) + row * kD + 128 * qq);
 #pragma unroll
@@ -150,10 +153,10 @@ struct KeyStager {
       // significant bits, inside f16's normal range)
       // the 8 E4M3 scales of this quarter as f16 (every E4M3 value is exact in f16)
       f16x2 sc2[4];
-      sc2[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].x, 1.0f, false);
-      sc2[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].x, 1.0f, true);
-      sc2[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].y, 1.0f, false);
-      sc2[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.d[4].y, 1.0f, true);
+      sc2[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.x, 1.0f, false);
+      sc2[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.x, 1.0f, true);
+      sc2[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.y, 1.0f, false);
+      sc2[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.y, 1.0f, true);
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const uint32_t wd[4] = {r.d[v].x, r.d[v].y, r.d[v].z, r.d[v].w};
@@ -174,7 +177,7 @@ struct KeyStager {
       if constexpr (kFp8Win) {
         // this thread decodes NoPE dims 112 qq .. 112 qq + 111 (codes at the same byte
         // offsets) and RoPE dims 448 + 16 qq .. + 15 (bf16 at bytes 448 + 32 qq)
-        const uint64_t scb = (uint64_t)r.d[9].x | ((uint64_t)r.d[9].y << 32);
+        const uint64_t scb = (uint64_t)r.sw.x | ((uint64_t)r.sw.y << 32);
         _Float16* kq = sh.k + kk * kKStride;
 #pragma unroll
         for (int j = 0; j < 7; j++) {
