@@ -234,7 +234,11 @@ __device__ __forceinline__ void score_tiles(
 #pragma unroll
     for (int u = 0; u < kPipe; u++) {
       process(pipe[u], k0 + u);
+      // the next tile's loads issue at raised wave priority, so they leave ahead of the other
+      // waves' compute on this SIMD (33.1 -> 32.8 us on the 1M-context batch-4 scan)
+      __builtin_amdgcn_s_setprio(2);
       load(k0 + u + kPipe, pipe[u]);  // reuses this tile's registers, so none are copied
+      __builtin_amdgcn_s_setprio(0);
       // the MXFP4-query body leaves the scheduler room to interleave different tiles' loads,
       // which would make each tile's wait cover younger tiles too: keep them in tile order
       if constexpr (kFp4Q) __builtin_amdgcn_sched_barrier(0);
