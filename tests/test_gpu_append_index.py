@@ -3,8 +3,8 @@ MXFP4-query twin): bit for bit what csa2_compress_append followed by csa2_index_
 produce (cache bytes, scores, block maxima), the appended bytes against the oracle's
 compressor, the scores against the oracle's indexer over the updated cache, two calls in a
 row, ragged rows, an empty row, rows whose newest entry opens a block or a tile, rows
-shorter than the score width, and the 1M-context batch-4 decode in the launch geometry the
-bench uses.  The appended rows start out holding other bytes,
+shorter or longer than the score width, 70 queries at once, and the 1M-context batch-4
+decode in the launch geometry the bench uses.  The appended rows start out holding other bytes,
 so a score computed from stale bytes would show."""
 import numpy as np
 import pytest
@@ -78,6 +78,8 @@ CASES = [
     ([1000, 8, 9, 33, 1, 0, 4096], 4096, 2),  # blocks opened by the new entry, a lone entry, an empty row
     ([777, 32, 64, 65], 800, 1),               # rows shorter than the width, tile edges
     ([5000, 4999, 4993, 4992], 5000, 2),
+    ([900, 850, 800, 799, 33], 800, 2),        # rows longer than the width: the new entry has no slot
+    ([200 - (i % 9) for i in range(70)], 256, 1),  # 70 queries, one sequence each
 ]
 
 
