@@ -168,22 +168,20 @@ class Decode1M:
         if extra_layers:
             self.scores_r = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
             self.topk_r = torch.empty((n_seq, K), dtype=torch.int32, device=dev)
-        # the stages of one step: the append fused with the Full layer's scan (HISA scores block
-        # means after the append, so it keeps them apart), selection, attention, then the
-        # Reindex and Reuse layers
-        self.fused = not hisa
-        self.step_stages = ([FUSED] if self.fused else [0, 1]) + [2, 3] + (
+        # the stages of one step: the append fused with the Full layer's scan (with HISA, the
+        # append, the newest block's mean and the scan of the block means in one launch),
+        # selection, attention, then the Reindex and Reuse layers
+        self.step_stages = ([FUSED_HISA] if hisa else [FUSED]) + [2, 3] + (
             list(range(4, 6 + extra_layers)) if extra_layers else [])
         if fp4q:  # the step packs the layer's bf16 indexer query into MXFP4 records, then scores
             self.q_fp4 = torch.empty((n_seq, 32, 68), dtype=torch.uint8, device=dev)
         if hisa:
-            # HISA: every batch copy keeps the block-mean records of its caches; a step re-packs
-            # the newest block of each sequence, scores the block means, keeps the top-M blocks,
-            # then scores their entries and takes the Top-K inside them
+            # HISA: every batch copy keeps the block-mean records of its caches; a step appends
+            # the newest entry, re-packs its block's mean and scores the block means (one
+            # launch), keeps the top-M blocks, then scores their entries and takes the Top-K
+            # inside them
             self.nbw = (n + 7) // 8
             self.mbase = (torch.arange(n_seq, dtype=torch.int64, device=dev) * self.nbw).contiguous()
-            self.nb_vis = torch.full((n_seq,), self.nbw, dtype=torch.int32, device=dev)
-            self.newest_block = torch.full((n_seq,), (n - 1) // 8, dtype=torch.int32, device=dev)
             self.s_blk = torch.empty((n_seq, self.nbw), dtype=torch.float32, device=dev)
             self.scores_c = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
             for c in self.copies:
@@ -215,14 +213,14 @@ class Decode1M:
             csa2.append_index_score(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"],
                                     self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], q, c["head_w"], self.q_base,
                                     self.q_nvis, n, scores=self.scores, block_max=self.bmax)
+        elif st == FUSED_HISA:  # append, re-pack the newest block's mean, score the block means
+            csa2.append_mean_index_score(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"],
+                                         self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], c["means"], self.mbase,
+                                         c["q_idx"], c["head_w"], self.q_base, self.q_nvis, self.nbw,
+                                         scores=self.s_blk)
         elif st == 0:  # append the newest entry of every sequence, from its m latest latents
             csa2.compress_append(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"], self.cs_new[ci],
                                  c["w_idx"], self.new_rows, c["kv"], c["ix"])
-        elif st == 1 and self.hisa:
-            csa2.block_mean_pack(c["ix"], self.q_base, self.q_nvis, 1, c["means"], self.mbase,
-                                 first_block=self.newest_block)
-            csa2.index_score(c["q_idx"], c["head_w"], c["means"], self.mbase, self.nb_vis, self.nbw,
-                             scores=self.s_blk, want_block_max=False)
         elif st == 2 and self.hisa:
             csa2.block_topk(None, self.q_nvis, K=self.K, M=self.M, block_max=self.s_blk, pool_out=self.pool,
                             want_topk=False, workspace=self.ws_sel)
@@ -261,8 +259,9 @@ class Decode1M:
 
 
 FUSED = -1  # the stage that appends and scores in one launch (csa2_append_index_score)
-STAGE_NAMES = {FUSED: "append_index_score", 0: "compress_newest", 1: "index_score", 2: "block_topk",
-               3: "sparse_attn"}
+FUSED_HISA = -2  # HISA's append + newest block mean + scan of the means (csa2_append_mean_index_score)
+STAGE_NAMES = {FUSED: "append_index_score", FUSED_HISA: "append_mean_index_score", 0: "compress_newest",
+               1: "index_score", 2: "block_topk", 3: "sparse_attn"}
 
 
 def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=3, fp8_window=False, fp4q=False,

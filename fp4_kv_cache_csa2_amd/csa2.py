@@ -35,6 +35,9 @@ _L.csa2_block_mean_pack.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _v
 _L.csa2_append_index_score.argtypes = [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                        _vp, _vp, _vp]
 _L.csa2_append_index_score_fp4q.argtypes = _L.csa2_append_index_score.argtypes
+_L.csa2_append_mean_index_score.argtypes = [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _i32, _i32, _vp, _vp, _vp]
+_L.csa2_append_mean_index_score_fp4q.argtypes = _L.csa2_append_mean_index_score.argtypes
 _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
 _L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
@@ -49,7 +52,7 @@ SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_co
            "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
            "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8",
            "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q", "csa2_block_mean_pack", "csa2_append_index_score",
-           "csa2_append_index_score_fp4q")
+           "csa2_append_index_score_fp4q", "csa2_append_mean_index_score", "csa2_append_mean_index_score_fp4q")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DEFAULT_SCALE = 512 ** -0.5
@@ -199,6 +202,48 @@ def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cac
     _check("csa2_append_index_score" + ("_fp4q" if fp4 else ""), fn(
         _ptr(latent), m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache), _ptr(q_idx),
         _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
+    return scores, block_max
+
+
+def append_mean_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cache, mean_cache, mean_base,
+                            q_idx, head_w, q_base, q_nvis, width: int, scores=None, block_max=None,
+                            want_block_max: bool = False, stream=None):
+    """HISA's decode step in one launch: appends query t's newest entry as append_index_score
+    does, re-packs the mean record of the block holding it (mean_cache row
+    mean_base[t] + (q_nvis[t] - 1) // 8), then scores the ceil(q_nvis[t] / 8) visible block
+    means: compress_append, block_mean_pack and index_score over mean_cache."""
+    fp4 = q_idx.dtype == torch.uint8
+    _dev(q_idx, torch.uint8 if fp4 else torch.bfloat16, "q_idx", 3)
+    if fp4 and tuple(q_idx.shape[1:]) != (32, 68):
+        raise ValueError("an MXFP4 q_idx must be [n_q, 32, 68]")
+    n_q = q_idx.shape[0]
+    _dev(latent, torch.bfloat16, "latent", 2)
+    if latent.shape[0] != n_q * m:
+        raise ValueError("latent must hold m rows per query")
+    _dev(pool_w, torch.float32, "pool_w")
+    _dev(rope_cs, torch.float32, "rope_cs", 2)
+    if rope_cs.shape[0] < n_q:
+        raise ValueError("rope_cs must cover every new entry")
+    _dev(w_idx, torch.bfloat16, "w_idx", 2)
+    _dev(kv_cache, torch.uint8, "kv_cache")
+    _dev(idx_cache, torch.uint8, "idx_cache")
+    _dev(mean_cache, torch.uint8, "mean_cache")
+    _dev(mean_base, torch.int64, "mean_base", 1)
+    _dev(head_w, torch.float32, "head_w", 2)
+    _dev(q_base, torch.int64, "q_base", 1)
+    _dev(q_nvis, torch.int32, "q_nvis", 1)
+    dev = q_idx.device
+    if scores is None:
+        scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
+    if block_max is None and want_block_max:
+        block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
+    _dev(scores, torch.float32, "scores")
+    _dev(block_max, torch.float32, "block_max")
+    fn = _L.csa2_append_mean_index_score_fp4q if fp4 else _L.csa2_append_mean_index_score
+    _check("csa2_append_mean_index_score" + ("_fp4q" if fp4 else ""), fn(
+        _ptr(latent), m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache),
+        _ptr(mean_cache), _ptr(mean_base), _ptr(q_idx), _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width,
+        _ptr(scores), _ptr(block_max), _stream(stream)))
     return scores, block_max
 
 

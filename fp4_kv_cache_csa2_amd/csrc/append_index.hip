@@ -15,6 +15,14 @@
 // (a device-scope fence here costs a write-back of the L2 while the scan streams).  The
 // bytes and scores are those of csa2_compress_append followed by csa2_index_score: the
 // append's latency chain (the 512-step projection) runs beside the scan instead of before it.
+//
+// HISA's decode step ([ZB] §2.3.4, the HISA paragraphs) scores block means instead of
+// entries, and the only mean the new entry changes is that of its own block.  Its launch
+// has the same shape: workgroup 0 of query t appends the entry, re-packs the mean record
+// of the newest block (the block's older entries from the cache, the new one from LDS,
+// block_mean.hpp) and scores the tile of block means that holds it, taking that record
+// from LDS; the other workgroups score every other tile of block means.
+#include "block_mean.hpp"
 #include "compress_few.hpp"
 #include "index_tiles.hpp"
 
@@ -47,28 +55,86 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
                                           block_max, t, wave, kWaves, sh.idx_row);
 }
 
-// workgroups of append_index_kernel that fit on the device at once (queried per device)
-int resident_workgroups() {
-  static int cached[64] = {0};
+struct MeanEntryShared {
+  EntryShared e;
+  __attribute__((aligned(16))) uint8_t mean_row[kIdxBytes + 12];  // the newest block's record (68 B)
+};
+
+// mean_cache rows mean_base[t] .. hold query t's block means (block b = entries 8b .. 8b + 7
+// of its sequence); the scores are those of the ceil(q_nvis[t] / 8) visible block means
+template <bool kFp4Q>
+__global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
+    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
+    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
+    uint8_t* __restrict__ mean_cache, const int64_t* __restrict__ mean_base, const void* __restrict__ q_in,
+    const float* __restrict__ head_w, const int64_t* __restrict__ q_base, const int32_t* __restrict__ q_nvis,
+    int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
+  const int t = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  if (blockIdx.x >= kAppendWgs) {
+    score_tiles<false, kFp4Q, kOlderSlots, true>(q_in, head_w, mean_cache, mean_base, q_nvis, nullptr, 0, width,
+                                                 scores, block_max, t,
+                                                 (int32_t)(blockIdx.x - kAppendWgs) * kWaves + wave,
+                                                 (int32_t)(gridDim.x - kAppendWgs) * kWaves);
+    return;
+  }
+  __shared__ MeanEntryShared sh;
+  const int32_t nvis = q_nvis[t];
+  const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
+  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
+                    idx_cache, sh.e);
+  if (nvis > 0 && threadIdx.x < 16) {  // lane 4g + sub: channels 32g + 8sub .. + 7
+    const int g = threadIdx.x >> 2, sub = threadIdx.x & 3;
+    const int32_t b = (nvis - 1) / kBlock;  // the newest block
+    const int cnt = nvis - b * kBlock;
+    uint32_t code;
+    const uint32_t word =
+        block_mean_word(idx_cache + (q_base[t] + (int64_t)b * kBlock) * kIdxBytes, cnt, sh.e.idx_row, g, sub, code);
+    uint8_t* dst = mean_cache + (mean_base[t] + b) * kIdxBytes;
+    *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
+    *reinterpret_cast<uint32_t*>(&sh.mean_row[16 * g + 4 * sub]) = word;
+    if (sub == 0) {
+      dst[64 + g] = (uint8_t)code;
+      sh.mean_row[64 + g] = (uint8_t)code;
+    }
+  }
+  __syncthreads();
+  score_tiles<false, kFp4Q, kNewestSlots, true>(q_in, head_w, mean_cache, mean_base, q_nvis, nullptr, 0, width,
+                                                scores, block_max, t, wave, kWaves, sh.mean_row);
+}
+
+// workgroups of a kernel of this file that fit on the device at once (queried per device)
+template <typename Kernel>
+int resident_workgroups(Kernel kernel, int (&cached)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_index_kernel<false>, kThreads, 0) !=
-            hipSuccess ||
-        per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu <= 0)
       per_cu = 2;
     cached[dev] = cus * per_cu;
   }
   return cached[dev];
 }
+int resident_entry[64], resident_mean[64];
 
+// workgroups along x: the append workgroup, then the scan's share of one round of resident
+// workgroups (at least one, at most what the row's tiles can use)
+int64_t grid_x(int resident, int32_t n_q, int32_t width) {
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  int64_t scan_x = resident / n_q - kAppendWgs;
+  const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
+  if (scan_x > max_x) scan_x = max_x;
+  if (scan_x < 1) scan_x = 1;
+  return kAppendWgs + scan_x;
+}
+
+// the checks both fused calls share
 template <bool kFp4Q>
-int append_index_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
-                       const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const void* q,
-                       const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
-                       float* scores, float* block_max, void* stream) {
+int check_args(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs, const uint16_t* w_idx,
+               uint8_t* kv_cache, uint8_t* idx_cache, const void* q, const float* head_w, const int64_t* q_base,
+               const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores, float* block_max) {
   if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
   if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
@@ -86,15 +152,38 @@ int append_index_entry(const uint16_t* latent, int m, const float* pool_w, const
        reinterpret_cast<uintptr_t>(head_w) | reinterpret_cast<uintptr_t>(scores) |
        reinterpret_cast<uintptr_t>(block_max)) & 3)
     return CSA2_ERR_INVALID_ARG;
-  // one round of resident workgroups: the append workgroups, then the scan's share of the rest
-  const int32_t ntiles = (width + kTile - 1) / kTile;
-  int64_t scan_x = resident_workgroups() / n_q - kAppendWgs;
-  const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
-  if (scan_x > max_x) scan_x = max_x;
-  if (scan_x < 1) scan_x = 1;
-  hipLaunchKernelGGL(append_index_kernel<kFp4Q>, dim3((unsigned)(kAppendWgs + scan_x), (unsigned)n_q), dim3(kThreads),
+  return CSA2_OK;
+}
+
+template <bool kFp4Q>
+int append_index_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
+                       const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const void* q,
+                       const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
+                       float* scores, float* block_max, void* stream) {
+  const int rc = check_args<kFp4Q>(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
+                                  n_q, width, scores, block_max);
+  if (rc != CSA2_OK || n_q == 0) return rc;
+  const int64_t gx = grid_x(resident_workgroups(append_index_kernel<false>, resident_entry), n_q, width);
+  hipLaunchKernelGGL(append_index_kernel<kFp4Q>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads),
                      0, (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w,
                      q_base, q_nvis, width, scores, block_max);
+  return check_launch();
+}
+
+template <bool kFp4Q>
+int append_mean_index_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
+                            const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, uint8_t* mean_cache,
+                            const int64_t* mean_base, const void* q, const float* head_w, const int64_t* q_base,
+                            const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores, float* block_max,
+                            void* stream) {
+  const int rc = check_args<kFp4Q>(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
+                                  n_q, width, scores, block_max);
+  if (rc != CSA2_OK || n_q == 0) return rc;
+  if (!mean_cache || !mean_base || (reinterpret_cast<uintptr_t>(mean_cache) & 15)) return CSA2_ERR_INVALID_ARG;
+  const int64_t gx = grid_x(resident_workgroups(append_mean_index_kernel<false>, resident_mean), n_q, width);
+  hipLaunchKernelGGL(append_mean_index_kernel<kFp4Q>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
+                     (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, mean_cache,
+                     mean_base, q, head_w, q_base, q_nvis, width, scores, block_max);
   return check_launch();
 }
 
@@ -117,4 +206,26 @@ extern "C" int csa2_append_index_score_fp4q(const uint16_t* latent_bf16, int m, 
                                             float* scores, float* block_max, void* stream) {
   return csa2::append_index_entry<true>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_fp4,
                                         head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
+}
+
+extern "C" int csa2_append_mean_index_score(const uint16_t* latent_bf16, int m, const float* pool_w,
+                                            const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
+                                            uint8_t* idx_cache, uint8_t* mean_cache, const int64_t* mean_base,
+                                            const uint16_t* q_idx_bf16, const float* head_w, const int64_t* q_base,
+                                            const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
+                                            float* block_max, void* stream) {
+  return csa2::append_mean_index_entry<false>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+                                              mean_cache, mean_base, q_idx_bf16, head_w, q_base, q_nvis, n_q, width,
+                                              scores, block_max, stream);
+}
+
+extern "C" int csa2_append_mean_index_score_fp4q(const uint16_t* latent_bf16, int m, const float* pool_w,
+                                                 const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
+                                                 uint8_t* idx_cache, uint8_t* mean_cache, const int64_t* mean_base,
+                                                 const uint8_t* q_fp4, const float* head_w, const int64_t* q_base,
+                                                 const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
+                                                 float* block_max, void* stream) {
+  return csa2::append_mean_index_entry<true>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+                                             mean_cache, mean_base, q_fp4, head_w, q_base, q_nvis, n_q, width, scores,
+                                             block_max, stream);
 }

@@ -13,9 +13,7 @@
 // position order, divided once by the entry count (what a decoding block's running sum and
 // count give), then packed by the indexer-K rules.  A decode step re-packs only the block
 // that holds the newest entry; completed blocks keep their records.
-#include "csa2_device.hpp"
-
-#pragma clang fp contract(off)  // the sums are the same IEEE operations, in the same order, as the definition
+#include "block_mean.hpp"
 
 namespace csa2 {
 namespace {
@@ -34,35 +32,10 @@ __global__ __launch_bounds__(kThreads) void block_mean_pack_kernel(
   const int32_t b = (first_block ? first_block[s] : 0) + i;
   // the 16 lanes of a record share b: they leave together
   if (i >= n_blocks || b < 0 || (int64_t)b * kBlock >= n) return;
-  const int64_t j0 = seq_base[s] + (int64_t)b * kBlock;
+  const uint8_t* rows = idx_cache + (seq_base[s] + (int64_t)b * kBlock) * kIdxBytes;
   const int cnt = min(kBlock, n - b * kBlock);
-  float sum[8];
-  for (int e = 0; e < cnt; e++) {  // ascending positions: the fp32 running sum
-    const uint8_t* row = idx_cache + (j0 + e) * kIdxBytes;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 16 * g + 4 * sub);
-    const float X = __builtin_ldexpf(1.0f, (int)row[64 + g] - 127);
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      const uint32_t c = (w >> (4 * q)) & 15u;
-      const float m = e2m1_mag(c & 7u) * X;  // exact: at most 3 significant bits times 2^k
-      const float v = (c & 8u) ? -m : m;
-      sum[q] = e == 0 ? v : sum[q] + v;
-    }
-  }
-  float mean[8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 8; q++) {
-    mean[q] = sum[q] / (float)cnt;  // IEEE division (exact for a full block of 8)
-    amax = __builtin_fmaxf(amax, __builtin_fabsf(mean[q]));
-  }
-  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
-  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
-  const uint32_t code = e8m0_scale_code(amax);
-  const float X = __builtin_ldexpf(1.0f, (int)code - 127);
-  uint32_t word = 0;
-#pragma unroll
-  for (int q = 0; q < 8; q++) word |= e2m1_encode(mean[q], X) << (4 * q);
+  uint32_t code;
+  const uint32_t word = block_mean_word(rows, cnt, rows + (cnt - 1) * kIdxBytes, g, sub, code);
   uint8_t* dst = mean_cache + (mean_base[s] + b) * kIdxBytes;
   *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
   if (sub == 0) dst[64 + g] = (uint8_t)code;

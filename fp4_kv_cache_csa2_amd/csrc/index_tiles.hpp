@@ -54,8 +54,10 @@ enum : int { kAllSlots = 0, kOlderSlots = 1, kNewestSlots = 2 };
 // indexer-K entry, [ZB] §2.4.4: the indexer Q and K are both trained for FP4), and the
 // contraction runs on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands' E2M1 codes and
 // E8M0 scales fed to the instruction as stored: two MFMAs per tile, no conversions.
+// kMeans: the rows scored are HISA's block means (one per 8 entries); q_nvis counts
+// entries and the row's visible means are ceil(q_nvis[t] / 8).
 // The wave is tile `first` of the grid-stride order with stride `tstride` (wave-uniform).
-template <bool kPool, bool kFp4Q, int kPart>
+template <bool kPool, bool kFp4Q, int kPart, bool kMeans = false>
 __device__ __forceinline__ void score_tiles(
     const void* __restrict__ q_in, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
@@ -67,7 +69,8 @@ __device__ __forceinline__ void score_tiles(
   constexpr int kPipe = kPart == kNewestSlots ? 1 : kDepth;
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int32_t nvis = q_nvis[t];
+  const int32_t nvis_in = q_nvis[t];
+  const int32_t nvis = kMeans ? (nvis_in > 0 ? (nvis_in - 1) / kBlock + 1 : 0) : nvis_in;
   const int64_t base = q_base[t];
   const int32_t ntiles = (width + kTile - 1) / kTile;
   // the tile of 32 slots that holds the newest visible entry, or -1 when nothing is visible

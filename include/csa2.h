@@ -263,6 +263,49 @@ int csa2_block_mean_pack(const uint8_t *idx_cache, const int64_t *seq_base, cons
                          uint8_t *mean_cache, const int64_t *mean_base, void *stream);
 
 /*
+ * csa2_append_mean_index_score -- HISA's decode step in one launch: the result of
+ *   csa2_compress_append of each query's newest entry, then csa2_block_mean_pack of the
+ *   block holding it, then csa2_index_score (Full mode) over the block means.
+ *   [ZB] §2.3.4 (the HISA paragraphs: block-mean keys, the newest block's mean updated while
+ *   decoding, the block means scored with the indexer query and head weights), [DF] §4.3
+ *   (a decoding token completes the newest entry of its sequence).  Only the newest block's
+ *   record, and so only the scores of the tile of 32 block means holding it, depend on the
+ *   append: one workgroup per query packs the entry, re-packs that block's record (its
+ *   older entries from idx_cache, the new one as just packed) and scores that tile, while
+ *   the others score every other tile of block means.
+ *
+ *   The appended entry (latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+ *   q_base, q_nvis) is that of csa2_append_index_score: row q_base[t] + q_nvis[t] - 1, with
+ *   q_nvis[t] counting it.  Block b of query t covers its entries 8b .. 8b + 7 (rows
+ *   q_base[t] + 8b ..); its record is mean_cache row mean_base[t] + b (int64 [n_q];
+ *   mean_cache [rows, 68], 16-byte aligned), and the call rewrites that of block
+ *   (q_nvis[t] - 1) / 8 by the rules of csa2_block_mean_pack.  The scores are those of
+ *   csa2_index_score over mean_cache with q_base = mean_base and ceil(q_nvis[t] / 8)
+ *   visible rows: scores fp32 [n_q, width] and block_max (NULL, or fp32 [n_q,
+ *   ceil(width / 8)]), bit for bit.  A query with q_nvis[t] <= 0 writes nothing and gets an
+ *   all -inf row.  Queries must append to distinct rows and own distinct mean rows.
+ *   Errors: those of csa2_append_index_score, and INVALID_ARG for a NULL or misaligned
+ *   mean_cache or a NULL mean_base.
+ */
+int csa2_append_mean_index_score(const uint16_t *latent_bf16, int m, const float *pool_w, const float *rope_cs,
+                                 const uint16_t *w_idx_bf16, uint8_t *kv_cache, uint8_t *idx_cache,
+                                 uint8_t *mean_cache, const int64_t *mean_base, const uint16_t *q_idx_bf16,
+                                 const float *head_w, const int64_t *q_base, const int32_t *q_nvis, int32_t n_q,
+                                 int32_t width, float *scores, float *block_max, void *stream);
+
+/*
+ * csa2_append_mean_index_score_fp4q -- csa2_append_mean_index_score with the indexer query
+ *   in MXFP4 (q_fp4 [n_q, 32, 68], 4-byte aligned): the scores of csa2_index_score_fp4q.
+ *   Every other argument, result and error as above.
+ */
+int csa2_append_mean_index_score_fp4q(const uint16_t *latent_bf16, int m, const float *pool_w,
+                                      const float *rope_cs, const uint16_t *w_idx_bf16, uint8_t *kv_cache,
+                                      uint8_t *idx_cache, uint8_t *mean_cache, const int64_t *mean_base,
+                                      const uint8_t *q_fp4, const float *head_w, const int64_t *q_base,
+                                      const int32_t *q_nvis, int32_t n_q, int32_t width, float *scores,
+                                      float *block_max, void *stream);
+
+/*
  * csa2_sparse_attn -- sparse latent attention over the selected FP4 entries joined with
  *   the sliding window.  [ZB] §3.3.2.1: key = value = c (the 512-channel entry); one
  *   softmax per head over the selected entries and the window rows ([ZB] §3.3.2, joint

@@ -161,3 +161,29 @@ def test_append_index_entry_points_validate_before_launch(lib):
         assert call(ix=f + 4) == -1
         assert call(q=f + q_align // 2) == -1
         assert call(bmax=f + 2) == -1
+
+
+def test_append_mean_index_entry_points_validate_before_launch(lib):
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    f = 1 << 20  # never dereferenced: validation fails first
+    for name, q_align in (("csa2_append_mean_index_score", 16), ("csa2_append_mean_index_score_fp4q", 4)):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp]
+
+        def call(latent=f, m=2, pool_w=f, rope=f, w=f, kv=f, ix=f, mc=f, mbase=f, q=f, hw=f, base=f, nvis=f, n_q=4,
+                 width=1 << 16, scores=f, bmax=f):
+            return fn(latent, m, pool_w, rope, w, kv, ix, mc, mbase, q, hw, base, nvis, n_q, width, scores, bmax, None)
+
+        assert call(n_q=0, latent=None, mc=None, q=None) == 0
+        assert call(n_q=-1) == -1
+        assert call(m=0) == -2
+        assert call(width=0) == -1
+        assert call(mc=None) == -1
+        assert call(mbase=None) == -1
+        assert call(mc=f + 4) == -1
+        assert call(pool_w=None) == -1
+        assert call(n_q=70000) == -2
+        assert call(width=(1 << 23) + 1) == -2
+        assert call(ix=f + 4) == -1
+        assert call(q=f + q_align // 2) == -1
+        assert call(scores=f + 2) == -1
