@@ -173,7 +173,8 @@ class Decode1M:
         # selection, attention, then the Reindex and Reuse layers
         self.step_stages = ([FUSED_HISA] if hisa else [FUSED]) + [2, 3] + (
             list(range(4, 6 + extra_layers)) if extra_layers else [])
-        if fp4q:  # the step packs the layer's bf16 indexer query into MXFP4 records, then scores
+        if fp4q:  # the fused launch packs the layer's bf16 indexer query into MXFP4 records itself
+            # (the buffer serves the separate packer + scan, stage 1)
             self.q_fp4 = torch.empty((n_seq, 32, 68), dtype=torch.uint8, device=dev)
         if hisa:
             # HISA: every batch copy keeps the block-mean records of its caches; a step appends
@@ -207,12 +208,11 @@ class Decode1M:
         """One stage of the step for batch copy ci, on torch's current stream."""
         c, csa2, n = self.copies[ci], self.csa2, self.n
         if st == FUSED:  # append each sequence's newest entry and score every entry, one launch
-            q = c["q_idx"]
-            if self.fp4q:
-                q = csa2.quantize_q_mxfp4(c["q_idx"], out=self.q_fp4)
+            # (with the MXFP4 query, the launch packs the bf16 query itself)
             csa2.append_index_score(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"],
-                                    self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], q, c["head_w"], self.q_base,
-                                    self.q_nvis, n, scores=self.scores, block_max=self.bmax)
+                                    self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], c["q_idx"], c["head_w"],
+                                    self.q_base, self.q_nvis, n, scores=self.scores, block_max=self.bmax,
+                                    pack_q=self.fp4q)
         elif st == FUSED_HISA:  # append, re-pack the newest block's mean, score the block means
             csa2.append_mean_index_score(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"],
                                          self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], c["means"], self.mbase,
@@ -294,7 +294,7 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
            "sequences": n_seq, "tokens_per_sequence": tokens, "compress_ratio": m, "entries_per_sequence": wl.n,
            "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else ""),
            "window": "FP8 rings (append + attend)" if fp8_window else "bf16",
-           "indexer_query": "MXFP4 (packed in the step)" if fp4q else "bf16"}
+           "indexer_query": "MXFP4 (packed inside the fused launch)" if fp4q else "bf16"}
     if hisa:
         # recall of the exact Top-K (the Full layer's, over every entry) by HISA's Top-K, on the
         # last replayed copy's inputs

@@ -35,6 +35,7 @@ _L.csa2_block_mean_pack.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _v
 _L.csa2_append_index_score.argtypes = [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                        _vp, _vp, _vp]
 _L.csa2_append_index_score_fp4q.argtypes = _L.csa2_append_index_score.argtypes
+_L.csa2_append_index_score_packq.argtypes = _L.csa2_append_index_score.argtypes
 _L.csa2_append_mean_index_score.argtypes = [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _vp, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_append_mean_index_score_fp4q.argtypes = _L.csa2_append_mean_index_score.argtypes
@@ -52,7 +53,7 @@ SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_co
            "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
            "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8",
            "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q", "csa2_block_mean_pack", "csa2_append_index_score",
-           "csa2_append_index_score_fp4q", "csa2_append_mean_index_score", "csa2_append_mean_index_score_fp4q")
+           "csa2_append_index_score_fp4q", "csa2_append_index_score_packq", "csa2_append_mean_index_score", "csa2_append_mean_index_score_fp4q")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DEFAULT_SCALE = 512 ** -0.5
@@ -168,12 +169,16 @@ def index_score(q_idx, head_w, idx_cache, q_base, q_nvis, width: int, pool_block
 
 
 def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q_idx, head_w, q_base, q_nvis,
-                       width: int, scores=None, block_max=None, want_block_max: bool = True, stream=None):
+                       width: int, scores=None, block_max=None, want_block_max: bool = True, stream=None,
+                       pack_q: bool = False):
     """Appends query t's newest entry (latent bf16 [n_q*m, 512]) at cache row
     q_base[t] + q_nvis[t] - 1, then scores every visible entry: compress_append followed by
     Full-mode index_score, in one launch.  q_idx is bf16 [n_q, 32, 128] or MXFP4 uint8
-    [n_q, 32, 68] (from quantize_q_mxfp4)."""
+    [n_q, 32, 68] (from quantize_q_mxfp4); pack_q=True with a bf16 q_idx packs it to MXFP4
+    inside the launch (quantize_q_mxfp4 followed by the MXFP4-query call)."""
     fp4 = q_idx.dtype == torch.uint8
+    if pack_q and fp4:
+        raise ValueError("pack_q takes a bf16 q_idx")
     _dev(q_idx, torch.uint8 if fp4 else torch.bfloat16, "q_idx", 3)
     if fp4 and tuple(q_idx.shape[1:]) != (32, 68):
         raise ValueError("an MXFP4 q_idx must be [n_q, 32, 68]")
@@ -198,8 +203,9 @@ def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cac
         block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
     _dev(scores, torch.float32, "scores")
     _dev(block_max, torch.float32, "block_max")
-    fn = _L.csa2_append_index_score_fp4q if fp4 else _L.csa2_append_index_score
-    _check("csa2_append_index_score" + ("_fp4q" if fp4 else ""), fn(
+    name = "csa2_append_index_score" + ("_fp4q" if fp4 else "_packq" if pack_q else "")
+    fn = getattr(_L, name)
+    _check(name, fn(
         _ptr(latent), m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache), _ptr(q_idx),
         _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
     return scores, block_max

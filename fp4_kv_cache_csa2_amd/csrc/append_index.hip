@@ -55,6 +55,49 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
                                           block_max, t, wave, kWaves, sh.idx_row);
 }
 
+// The query of t packed to MXFP4 into LDS by the whole workgroup, by the rules of
+// csa2_quantize_q_mxfp4 (mxfp4_pack8): 512 (head, group of 32 channels, quarter) tasks over
+// the 256 threads, 4 consecutive lanes per group.
+__device__ __forceinline__ void pack_query_lds(const uint16_t* __restrict__ q, uint8_t* rec) {
+#pragma unroll
+  for (int it = 0; it < kIdxHeads * 16 / kThreads; it++) {
+    const int task = it * kThreads + threadIdx.x;
+    const int v = task >> 4, grp = (task >> 2) & 3, sub = task & 3;
+    uint32_t code;
+    const uint32_t word =
+        mxfp4_pack8(*reinterpret_cast<const uint4*>(q + v * kIdxDim + 32 * grp + 8 * sub), code);
+    *reinterpret_cast<uint32_t*>(rec + v * kIdxBytes + 16 * grp + 4 * sub) = word;
+    if (sub == 0) rec[v * kIdxBytes + 64 + grp] = (uint8_t)code;
+  }
+  __syncthreads();
+}
+
+// append_index_kernel<true> with the bf16 query packed inside the launch: every workgroup
+// packs it into LDS first (a few hundred bytes of work), which saves the packer's launch
+__global__ __launch_bounds__(kThreads) void append_index_packq_kernel(
+    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
+    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
+    const uint16_t* __restrict__ q_bf16, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
+    const int32_t* __restrict__ q_nvis, int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
+  const int t = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  __shared__ __attribute__((aligned(16))) uint8_t q_rec[kIdxHeads * kIdxBytes];
+  pack_query_lds(q_bf16 + (int64_t)t * kIdxHeads * kIdxDim, q_rec);
+  if (blockIdx.x >= kAppendWgs) {
+    score_tiles<false, true, kOlderSlots>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
+                                          block_max, t, (int32_t)(blockIdx.x - kAppendWgs) * kWaves + wave,
+                                          (int32_t)(gridDim.x - kAppendWgs) * kWaves, nullptr, q_rec);
+    return;
+  }
+  __shared__ EntryShared sh;
+  const int32_t nvis = q_nvis[t];
+  const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
+  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
+                    idx_cache, sh);
+  score_tiles<false, true, kNewestSlots>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
+                                         block_max, t, wave, kWaves, sh.idx_row, q_rec);
+}
+
 struct MeanEntryShared {
   EntryShared e;
   __attribute__((aligned(16))) uint8_t mean_row[kIdxBytes + 12];  // the newest block's record (68 B)
@@ -117,7 +160,7 @@ int resident_workgroups(Kernel kernel, int (&cached)[64]) {
   }
   return cached[dev];
 }
-int resident_entry[64], resident_mean[64];
+int resident_entry[64], resident_packq[64], resident_mean[64];
 
 // workgroups along x: the append workgroup, then the scan's share of one round of resident
 // workgroups (at least one, at most what the row's tiles can use)
@@ -170,6 +213,20 @@ int append_index_entry(const uint16_t* latent, int m, const float* pool_w, const
   return check_launch();
 }
 
+int append_index_packq_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
+                             const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const uint16_t* q,
+                             const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q,
+                             int32_t width, float* scores, float* block_max, void* stream) {
+  const int rc = check_args<false>(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
+                                   n_q, width, scores, block_max);
+  if (rc != CSA2_OK || n_q == 0) return rc;
+  const int64_t gx = grid_x(resident_workgroups(append_index_packq_kernel, resident_packq), n_q, width);
+  hipLaunchKernelGGL(append_index_packq_kernel, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
+                     (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
+                     q_nvis, width, scores, block_max);
+  return check_launch();
+}
+
 template <bool kFp4Q>
 int append_mean_index_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
                             const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, uint8_t* mean_cache,
@@ -205,6 +262,15 @@ extern "C" int csa2_append_index_score_fp4q(const uint16_t* latent_bf16, int m, 
                                             const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
                                             float* scores, float* block_max, void* stream) {
   return csa2::append_index_entry<true>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_fp4,
+                                        head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
+}
+
+extern "C" int csa2_append_index_score_packq(const uint16_t* latent_bf16, int m, const float* pool_w,
+                                             const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
+                                             uint8_t* idx_cache, const uint16_t* q_idx_bf16, const float* head_w,
+                                             const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
+                                             float* scores, float* block_max, void* stream) {
+  return csa2::append_index_packq_entry(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_idx_bf16,
                                         head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
 }
 

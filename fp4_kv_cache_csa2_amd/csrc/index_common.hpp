@@ -63,6 +63,31 @@ __device__ __forceinline__ void load_fp4_query(const uint8_t* rec, int g, fp4x32
   qsc = *reinterpret_cast<const uint32_t*>(rec + 64) >> (16 * g);
 }
 
+// MXFP4 packing of 8 channels of a 32-channel group held by 4 consecutive lanes (the OCP
+// MXFP4 rules of the indexer-K packer): raw holds the 8 bf16 values; returns their 8 E2M1
+// codes (channel 8i + q in bits 4q .. 4q + 3) and sets code to the group's E8M0 scale.  The
+// group's amax comes from two shuffles inside the 4 lanes, which must all run it together.
+__device__ __forceinline__ uint32_t mxfp4_pack8(const uint4 raw, uint32_t& code) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+  code = e8m0_scale_code(amax);
+  const float X = __builtin_ldexpf(1.0f, (int)code - 127);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) word |= e2m1_encode(x[i], X) << (4 * i);
+  return word;
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
 // outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their no-wait maxima).
 // Vector memory operations complete in issue order, so this waits for all but the n youngest.

@@ -32,24 +32,8 @@ __global__ __launch_bounds__(kPackThreads) void quantize_q_mxfp4_kernel(const ui
   const int64_t v = gi >> 2;
   const int g = (int)(gi & 3);
   if (v >= n_vec) return;  // the 4 lanes of a group share v: all leave or none
-  const uint4 raw = *reinterpret_cast<const uint4*>(q + v * kIdxDim + 32 * g + 8 * sub);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  float x[8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
-  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
-  const uint32_t code = e8m0_scale_code(amax);
-  const float X = __builtin_ldexpf(1.0f, (int)code - 127);
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i++) word |= e2m1_encode(x[i], X) << (4 * i);
+  uint32_t code;
+  const uint32_t word = mxfp4_pack8(*reinterpret_cast<const uint4*>(q + v * kIdxDim + 32 * g + 8 * sub), code);
   uint8_t* dst = out + v * kIdxBytes;
   *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
   if (sub == 0) dst[64 + g] = (uint8_t)code;

@@ -63,7 +63,7 @@ __device__ __forceinline__ void score_tiles(
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
     int32_t width, float* __restrict__ scores, float* __restrict__ block_max, int t, int32_t first,
-    int32_t tstride, const uint8_t* fresh_row = nullptr) {
+    int32_t tstride, const uint8_t* fresh_row = nullptr, const uint8_t* q_rec = nullptr) {
   static_assert(!kPool || kPart == kAllSlots, "a candidate pool is scored whole");
   // tiles in flight per wave: the newest-tile part visits one tile
   constexpr int kPipe = kPart == kNewestSlots ? 1 : kDepth;
@@ -202,7 +202,10 @@ __device__ __forceinline__ void score_tiles(
   // every pass with a wait that drains this wave's tiles in flight (loads complete in order).
   {
     if constexpr (kFp4Q) {
-      load_fp4_query(static_cast<const uint8_t*>(q_in) + ((int64_t)t * kIdxHeads + n) * kIdxBytes, g, qa, qsc);
+      // q_rec: the query's 32 records, already packed by the caller (in LDS)
+      load_fp4_query(q_rec != nullptr ? q_rec + n * kIdxBytes
+                                      : static_cast<const uint8_t*>(q_in) + ((int64_t)t * kIdxHeads + n) * kIdxBytes,
+                     g, qa, qsc);
     } else {
       const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_in) +
                                                        ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);

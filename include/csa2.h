@@ -207,6 +207,20 @@ int csa2_append_index_score_fp4q(const uint16_t *latent_bf16, int m, const float
                                  float *scores, float *block_max, void *stream);
 
 /*
+ * csa2_append_index_score_packq -- csa2_append_index_score_fp4q with the indexer query
+ *   packed inside the launch: the result of csa2_quantize_q_mxfp4 of q_idx_bf16 followed by
+ *   csa2_append_index_score_fp4q, bit for bit ([ZB] §2.4.4, the FP4 indexer query).  Each
+ *   workgroup packs its query's 32 head vectors into its own LDS; the packed records are
+ *   not written out.  Arguments, results and errors are those of csa2_append_index_score
+ *   (q_idx_bf16 [n_q, 32, 128], 16-byte aligned).
+ */
+int csa2_append_index_score_packq(const uint16_t *latent_bf16, int m, const float *pool_w, const float *rope_cs,
+                                  const uint16_t *w_idx_bf16, uint8_t *kv_cache, uint8_t *idx_cache,
+                                  const uint16_t *q_idx_bf16, const float *head_w, const int64_t *q_base,
+                                  const int32_t *q_nvis, int32_t n_q, int32_t width, float *scores,
+                                  float *block_max, void *stream);
+
+/*
  * csa2_block_topk -- hierarchical selection: block max -> top-M block pool -> Top-K.
  *   [ZB] §2.3.4 and [DF] §4.7: g_r = max over block r (b = `block` positions, -inf
  *   padding); the block holding the newest visible position takes +inf; the M blocks

@@ -141,7 +141,8 @@ def test_hisa_entry_points_validate_before_launch(lib):
 def test_append_index_entry_points_validate_before_launch(lib):
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     f = 1 << 20  # never dereferenced: validation fails first
-    for name, q_align in (("csa2_append_index_score", 16), ("csa2_append_index_score_fp4q", 4)):
+    for name, q_align in (("csa2_append_index_score", 16), ("csa2_append_index_score_fp4q", 4),
+                          ("csa2_append_index_score_packq", 16)):
         fn = getattr(lib, name)
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp]
 

@@ -3,9 +3,11 @@ MXFP4-query twin): bit for bit what csa2_compress_append followed by csa2_index_
 produce (cache bytes, scores, block maxima), the appended bytes against the oracle's
 compressor, the scores against the oracle's indexer over the updated cache, two calls in a
 row, ragged rows, an empty row, rows whose newest entry opens a block or a tile, rows
-shorter or longer than the score width, 70 queries at once, and the 1M-context batch-4
-decode in the launch geometry the bench uses.  The appended rows start out holding other bytes,
+shorter or longer than the score width, 70 queries at once, the MXFP4 query packed inside
+the launch (special scales included), and the 1M-context batch-4 decode in the launch geometry the bench uses.  The appended rows start out holding other bytes,
 so a score computed from stale bytes would show."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -55,12 +57,13 @@ def _separate(c, k, fp4):
     return kv, ix, s, b
 
 
-def _fused(c, k, fp4, kv=None, ix=None):
+def _fused(c, k, fp4, kv=None, ix=None, pack_q=False):
+    """fp4 with pack_q: the bf16 query goes in and the launch packs it to MXFP4 itself."""
     kv = dev(k.kv) if kv is None else kv
     ix = dev(k.ix) if ix is None else ix
-    q = c.quantize_q_mxfp4(bf16(k.d.q_idx)) if fp4 else bf16(k.d.q_idx)
+    q = c.quantize_q_mxfp4(bf16(k.d.q_idx)) if fp4 and not pack_q else bf16(k.d.q_idx)
     s, b = c.append_index_score(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), kv, ix, q,
-                                dev(k.d.head_w), dev(k.base), dev(k.nvis), k.width)
+                                dev(k.d.head_w), dev(k.base), dev(k.nvis), k.width, pack_q=pack_q)
     return kv, ix, s, b
 
 
@@ -83,20 +86,43 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fp4", [False, True], ids=["bf16_q", "fp4_q"])
+QFORMATS = [(False, False), (True, False), (True, True)]
+QIDS = ["bf16_q", "fp4_q", "fp4_q_packed_in_launch"]
+
+
+@pytest.mark.parametrize("fp4,pack_q", QFORMATS, ids=QIDS)
 @pytest.mark.parametrize("ci", range(len(CASES)))
-def test_fused_equals_append_then_score(c, ci, fp4):
+def test_fused_equals_append_then_score(c, ci, fp4, pack_q):
     nvis, width, m = CASES[ci]
-    log(f"append_index nvis={nvis} width={width} m={m} fp4={fp4}")
+    log(f"append_index nvis={nvis} width={width} m={m} fp4={fp4} pack_q={pack_q}")
     k = Case(c, 500 + 10 * ci, nvis, width, m)
     ref = _separate(c, k, fp4)
-    got = _fused(c, k, fp4)
+    got = _fused(c, k, fp4, pack_q=pack_q)
     torch.cuda.synchronize()
     _same(ref, got)
     # a second call on the result appends the same entries again: same results
-    again = _fused(c, k, fp4, kv=got[0], ix=got[1])
+    again = _fused(c, k, fp4, kv=got[0], ix=got[1], pack_q=pack_q)
     torch.cuda.synchronize()
     _same(ref, again)
+
+
+def test_query_packed_in_launch_takes_every_scale_path(c):
+    """Head vectors whose groups hit the packer's special scales (all zero, a huge and a tiny
+    amax, values that round to a tie) give the same scores packed in the launch as packed by
+    csa2_quantize_q_mxfp4 first."""
+    nvis, width, m = CASES[1]
+    log("append_index packed query, special scales")
+    k = Case(c, 560, nvis, width, m)
+    q = k.d.q_idx.copy()  # bf16 bit patterns
+    q[0, 0, :32] = 0
+    q[0, 1, 32:64] = synth.f32_to_bf16_bits(np.linspace(-3.0e38, 3.0e38, 32, dtype=np.float32))
+    q[1, 2, 64:96] = synth.f32_to_bf16_bits(np.linspace(1e-30, 7e-30, 32, dtype=np.float32))
+    q[2, 3, :] = synth.f32_to_bf16_bits((0.25 * np.arange(128) % 1.75).astype(np.float32))
+    k.d = dataclasses.replace(k.d, q_idx=q)
+    ref = _separate(c, k, True)
+    got = _fused(c, k, True, pack_q=True)
+    torch.cuda.synchronize()
+    _same(ref, got)
 
 
 @pytest.mark.parametrize("fp4", [False, True], ids=["bf16_q", "fp4_q"])
