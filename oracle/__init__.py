@@ -64,7 +64,7 @@ def lib():
         L.csa2o_e8m0_scale_code.argtypes = [ctypes.c_float]
         L.csa2o_e8m0_scale_code.restype = ctypes.c_int
         L.csa2o_rope_table.argtypes = [vp, i64, f64, vp]
-        L.csa2o_compress_pack.argtypes = [vp, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.csa2o_compress_pack.argtypes = [vp, i64, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
         L.csa2o_dequant_kv.argtypes = [vp, vp]
         L.csa2o_dequant_idx.argtypes = [vp, vp]
         L.csa2o_index_score.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
@@ -133,10 +133,15 @@ def rope_table(pos, theta: float = 160000.0) -> np.ndarray:
 
 # ---------------------------------------------------------------- stage 1
 def compress_pack(latent_bf16, m: int, pool_w, rope_cs, w_idx_bf16, intermediates: bool = False):
-    """latent_bf16 uint16 [n*m, 512] -> (kv uint8 [n, 288], idx uint8 [n, 68][, pooled, rotated, k])."""
+    """latent_bf16 uint16 [n*m, 512] -> (kv uint8 [n, 288], idx uint8 [n, 68][, pooled, rotated, k]).
+
+    pool_w is fp32 [m, 512] (static per-channel weights) or [n*m, 512] (one weight row per
+    latent token: per-token gates, same formula)."""
     latent = _c(latent_bf16, np.uint16)
     n = latent.shape[0] // m
     pw = None if pool_w is None else _c(pool_w, np.float32)
+    per_token = pw is not None and m > 1 and pw.shape[0] == n * m and n * m != m
+    assert pw is None or pw.shape[0] in (m, n * m)
     cs = _c(rope_cs, np.float32)
     w = _c(w_idx_bf16, np.uint16)
     assert cs.shape == (n, 64) and w.shape == (128, 512)
@@ -147,7 +152,7 @@ def compress_pack(latent_bf16, m: int, pool_w, rope_cs, w_idx_bf16, intermediate
         pooled = np.empty((n, D_LAT), np.float32)
         rotated = np.empty((n, D_LAT), np.float32)
         kproj = np.empty((n, IDX_DIM), np.float32)
-    lib().csa2o_compress_pack(_p(latent), n, m, _p(pw), _p(cs), _p(w), _p(kv), _p(ix),
+    lib().csa2o_compress_pack(_p(latent), n, m, _p(pw), int(per_token), _p(cs), _p(w), _p(kv), _p(ix),
                               _p(pooled), _p(rotated), _p(kproj))
     if intermediates:
         return kv, ix, pooled, rotated, kproj

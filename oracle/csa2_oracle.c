@@ -145,22 +145,26 @@ static void pack_nibbles(const int *codes, int n, uint8_t *dst) {
 }
 
 void csa2o_compress_pack(const uint16_t *latent, int64_t n_entries, int m, const float *pool_w,
-                         const float *rope_cs, const uint16_t *w_idx, uint8_t *kv_out,
+                         int per_token_w, const float *rope_cs, const uint16_t *w_idx, uint8_t *kv_out,
                          uint8_t *idx_out, float *pooled, float *rotated, float *kproj) {
   float c[D_LAT];
   float k[IDX_DIM];
   int codes[D_LAT];
   for (int64_t j = 0; j < n_entries; j++) {
-    /* a1: c_j[ch] = sum_i a_i[ch] x_{m j + i}[ch], a_i = w_i / sum_i' w_i' */
+    /* a1: c_j[ch] = sum_i a_i[ch] x_{m j + i}[ch], a_i = w_i / sum_i' w_i'.  The weights
+     * are static per channel ([m, 512]) or, with per_token_w, one row per latent token
+     * ([n_entries * m, 512]: the gate of token m j + i is row m j + i), the same formula
+     * ([DF] §4.2 remarks that the pooling weights may be projected from the input). */
+    const float *w = per_token_w ? pool_w + (j * m) * D_LAT : pool_w;
     for (int ch = 0; ch < D_LAT; ch++) {
       const uint16_t *x = latent + (j * m) * D_LAT + ch;
       if (m == 1) {
         c[ch] = bf16_to_f32(x[0]);
       } else {
-        float wsum = pool_w[ch];
-        for (int i = 1; i < m; i++) wsum = wsum + pool_w[i * D_LAT + ch];
-        float acc = (pool_w[ch] / wsum) * bf16_to_f32(x[0]);
-        for (int i = 1; i < m; i++) acc = acc + (pool_w[i * D_LAT + ch] / wsum) * bf16_to_f32(x[i * D_LAT]);
+        float wsum = w[ch];
+        for (int i = 1; i < m; i++) wsum = wsum + w[i * D_LAT + ch];
+        float acc = (w[ch] / wsum) * bf16_to_f32(x[0]);
+        for (int i = 1; i < m; i++) acc = acc + (w[i * D_LAT + ch] / wsum) * bf16_to_f32(x[i * D_LAT]);
         c[ch] = acc;
       }
     }

@@ -44,13 +44,14 @@ void csa2o_rope_table(const int64_t *pos, int64_t n, double theta, float *out);
 
 /* ---- stage 1: compressor + RoPE + FP4 pack + indexer-K projection + MXFP4 pack --
  * latent   : bf16 [n_entries * m, 512] (complete groups only)
- * pool_w   : fp32 [m, 512], non-negative, per-channel weights (unused when m == 1)
+ * pool_w   : fp32 non-negative weights (unused when m == 1): [m, 512] per channel, or with
+ *            per_token_w != 0 one row per latent token, [n_entries * m, 512]
  * rope_cs  : fp32 [n_entries, 64] (cos[32], sin[32]) at each entry's position
  * w_idx    : bf16 [128, 512] indexer-K projection
  * kv_out   : [n_entries, 288]; idx_out : [n_entries, 68]
  * pooled/rotated/kproj (each may be NULL): fp32 intermediates [n, 512] / [n, 512] / [n, 128]. */
 void csa2o_compress_pack(const uint16_t *latent, int64_t n_entries, int m,
-                         const float *pool_w, const float *rope_cs, const uint16_t *w_idx,
+                         const float *pool_w, int per_token_w, const float *rope_cs, const uint16_t *w_idx,
                          uint8_t *kv_out, uint8_t *idx_out,
                          float *pooled, float *rotated, float *kproj);
 

@@ -58,6 +58,51 @@ def test_pooling_is_convex_and_matches_quotient_formula():
     assert np.max(np.abs(pooled - quot)) <= 4 * np.finfo(np.float32).eps * np.max(np.abs(x))
 
 
+def test_per_token_weights_repeating_the_static_rows_give_the_static_result():
+    # per-token gates ([DF] §4.2: the pooling weights may be projected from the input) use the
+    # static formula with each token's own row: rows that repeat the static weights reproduce
+    # the static entries bit for bit
+    n = 96
+    ci, (kv, ix, pooled, rot, k) = _compress(n, 2, seed=31)
+    w_tok = np.tile(ci.pool_w, (n, 1))
+    kv2, ix2, pooled2, _, _ = oracle.compress_pack(ci.latent, 2, w_tok, oracle.rope_table(ci.positions), ci.w_idx,
+                                                   intermediates=True)
+    assert np.array_equal(kv2, kv) and np.array_equal(ix2, ix) and np.array_equal(pooled2, pooled)
+
+
+def test_per_token_equal_weights_give_the_fp32_mean():
+    # a different positive constant per token pair: each entry is still exactly the fp32 mean
+    n = 64
+    ci = synth.compress_inputs(32, n, 2)
+    c = np.exp2(RNG.integers(-20, 20, n)).astype(np.float32) * np.float32(0.37)
+    w_tok = np.repeat(np.repeat(c, 2)[:, None], 512, axis=1).astype(np.float32)
+    _, _, pooled, _, _ = oracle.compress_pack(ci.latent, 2, w_tok, oracle.rope_table(ci.positions), ci.w_idx,
+                                              intermediates=True)
+    x = synth.bf16_bits_to_f32(ci.latent).reshape(n, 2, 512)
+    assert np.array_equal(pooled.view(np.uint32), np.mean(x, axis=1, dtype=np.float32).view(np.uint32))
+
+
+def test_per_token_weights_belong_to_their_own_entry():
+    # entry j of a per-token call equals a one-entry static call with rows 2j, 2j+1 as weights;
+    # swapping an entry's two latents together with their weight rows changes nothing
+    n = 24
+    ci = synth.compress_inputs(33, n, 2)
+    w_tok = synth.softplus_weights(np.random.default_rng(7), 2 * n)
+    cs = oracle.rope_table(ci.positions)
+    kv, ix = oracle.compress_pack(ci.latent, 2, w_tok, cs, ci.w_idx)
+    for j in (0, 5, n - 1):
+        kv1, ix1 = oracle.compress_pack(ci.latent[2 * j:2 * j + 2], 2, w_tok[2 * j:2 * j + 2], cs[j:j + 1], ci.w_idx)
+        assert np.array_equal(kv1[0], kv[j]) and np.array_equal(ix1[0], ix[j])
+    sw = np.arange(2 * n).reshape(n, 2)[:, ::-1].reshape(-1)
+    kv_s, ix_s = oracle.compress_pack(ci.latent[sw], 2, w_tok[sw], cs, ci.w_idx)
+    assert np.array_equal(kv_s, kv) and np.array_equal(ix_s, ix)
+    # a zero weight on one token selects the other token exactly (the convex-combination ends)
+    w_sel = w_tok.copy()
+    w_sel[1::2] = 0.0
+    _, _, pooled, _, _ = oracle.compress_pack(ci.latent, 2, w_sel, cs, ci.w_idx, intermediates=True)
+    assert np.array_equal(pooled, synth.bf16_bits_to_f32(ci.latent)[0::2])
+
+
 def test_rope_position_zero_identity_and_norm():
     n = 16
     ci, (kv, ix, pooled, rot, k) = _compress(n, 2, table=rope_id_table(n))
