@@ -434,11 +434,15 @@ def time_schedule(torch, csa2, tokens=1 << 20, n_seq=4, steps=10, warmup=2):
     torch.cuda.synchronize()
     cap_stream = torch.cuda.Stream()
     graphs = []
+    states = []
     for p in positions:
+        st = g.token_state(p)  # the device state the graph of position p reads
+        torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=cap_stream):
-            g.decode_token(p, new, inputs, outs)
+            g.decode_token(p, new, inputs, outs, state=st)
         graphs.append(gr)
+        states.append(st)
     for gr in graphs:
         gr.replay()
     torch.cuda.synchronize()
@@ -452,7 +456,7 @@ def time_schedule(torch, csa2, tokens=1 << 20, n_seq=4, steps=10, warmup=2):
            "caches": {c: {"m": m, "entries_per_sequence": tokens // m} for c, m in schedule.RATIO.items()},
            "layers": "40 (2 SWA-only skipped): 4 Full, 4 Reindex, 30 Reuse; 38 attention calls per token",
            "window": "bf16 rows, drawn once per layer"}
-    del graphs, g, inputs, outs
+    del graphs, states, g, inputs, outs
     torch.cuda.empty_cache()
     return res
 

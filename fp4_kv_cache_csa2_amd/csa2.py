@@ -2,11 +2,18 @@
 
 Argument marshalling only: every step of the path runs in the HIP kernels.  Tensors are
 torch tensors on the ROCm device; calls are enqueued on torch's current stream (or the
-stream passed in).  There is no CPU fallback: if libcsa2.so is missing or cannot be
-loaded, importing this module raises.
+stream passed in).  Every wrapper checks the dtype, device, contiguity and shape of each
+tensor it passes against the sizes of the call (n_q, width, M, K, ...) and raises
+ValueError before anything is launched, so no kernel reads or writes past a tensor it was
+given.  Index values held inside device tensors (cache rows, entry ids) are the caller's
+to keep in range: checking them would need a device synchronisation per call.  Tensors the
+binding allocates (outputs not given, workspaces) are allocated on the launch stream.
+There is no CPU fallback: if libcsa2.so is missing or cannot be loaded, importing this
+module raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -26,18 +33,18 @@ _L.csa2_abi_version.restype = ctypes.c_int
 _L.csa2_status_string.argtypes = [ctypes.c_int]
 _L.csa2_status_string.restype = ctypes.c_char_p
 _L.csa2_rope_table.argtypes = [_vp, _i64, _f64, _vp]
-_L.csa2_compress_pack.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
-_L.csa2_compress_append.argtypes = [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_L.csa2_compress_pack.argtypes = [_vp, _i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]
+_L.csa2_compress_append.argtypes = [_vp, _i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
 _L.csa2_index_score.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_quantize_q_mxfp4.argtypes = [_vp, _i64, _vp, _vp]
 _L.csa2_index_score_fp4q.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_block_mean_pack.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
-_L.csa2_append_index_score.argtypes = [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
-                                       _vp, _vp, _vp]
+_L.csa2_append_index_score.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_append_index_score_fp4q.argtypes = _L.csa2_append_index_score.argtypes
 _L.csa2_append_index_score_packq.argtypes = _L.csa2_append_index_score.argtypes
-_L.csa2_append_mean_index_score.argtypes = [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                            _vp, _i32, _i32, _vp, _vp, _vp]
+_L.csa2_append_mean_index_score.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_append_mean_index_score_fp4q.argtypes = _L.csa2_append_mean_index_score.argtypes
 _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
@@ -81,17 +88,39 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _dev(t, dtype, name, ndim=None):
+def _on(stream):
+    """Allocation context: tensors the binding makes are allocated on the launch stream."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _is_device(t) -> bool:
+    return t.is_cuda
+
+
+def _dev(t, dtype, name, shape=None):
+    """Checks a device tensor: dtype, contiguity and, when given, its exact shape (a tuple
+    whose None entries match any size)."""
     if t is None:
         return
-    if not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or not _is_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and g != w for g, w in zip(t.shape, shape)):
+            want = tuple("*" if w is None else w for w in shape)
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+
+
+def _need(t, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+
+
+def _bytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def abi_version() -> int:
@@ -106,66 +135,140 @@ def rope_table(pos, theta: float = ROPE_THETA) -> torch.Tensor:
     return out
 
 
+def _pool_weights(pool_w, m: int, n_rows: int) -> int:
+    """Checks the pooling weights of n_rows latent rows: [m, 512] static (returns 0) or
+    [n_rows, 512] per token (returns 1); m = 1 reads none and may pass None."""
+    if pool_w is None:
+        if m != 1:
+            raise ValueError("pool_w is required when m > 1")
+        return 0
+    _dev(pool_w, torch.float32, "pool_w", (None, 512))
+    if pool_w.shape[0] == m:
+        return 0
+    if pool_w.shape[0] == n_rows:
+        return 1
+    raise ValueError(f"pool_w must be [m, 512] (static) or [{n_rows}, 512] (one row per latent token), "
+                     f"got {tuple(pool_w.shape)}")
+
+
+def _latent_rows(latent, m: int) -> int:
+    _dev(latent, torch.bfloat16, "latent", (None, 512))
+    if m not in (1, 2):
+        raise ValueError("m must be 1 or 2")
+    if latent.shape[0] % m:
+        raise ValueError("latent must hold complete groups of m rows")
+    return latent.shape[0] // m
+
+
+def _cache(t, name, row_bytes):
+    _need(t, name)
+    _dev(t, torch.uint8, name, (None, row_bytes))
+
+
 def compress_pack(latent, m: int, pool_w, rope_cs, w_idx, kv_out=None, idx_out=None, stream=None):
-    """latent bf16 [n*m, 512] -> (kv uint8 [n, 288], idx uint8 [n, 68]); outputs may be given."""
-    _dev(latent, torch.bfloat16, "latent", 2)
-    n = latent.shape[0] // m
-    _dev(pool_w, torch.float32, "pool_w")
-    _dev(rope_cs, torch.float32, "rope_cs", 2)
-    _dev(w_idx, torch.bfloat16, "w_idx", 2)
-    if kv_out is None:
-        kv_out = torch.empty((n, 288), dtype=torch.uint8, device=latent.device)
-    if idx_out is None:
-        idx_out = torch.empty((n, 68), dtype=torch.uint8, device=latent.device)
-    _dev(kv_out, torch.uint8, "kv_out")
-    _dev(idx_out, torch.uint8, "idx_out")
-    if rope_cs.shape[0] < n or kv_out.numel() < n * 288 or idx_out.numel() < n * 68:
-        raise ValueError("output / table too small")
+    """latent bf16 [n*m, 512] -> (kv uint8 [n, 288], idx uint8 [n, 68]); outputs may be given
+    (at least n rows).  pool_w: fp32 [m, 512], or [n*m, 512] for one weight row per token."""
+    n = _latent_rows(latent, m)
+    per_token = _pool_weights(pool_w, m, n * m)
+    _dev(rope_cs, torch.float32, "rope_cs", (None, 64))
+    _dev(w_idx, torch.bfloat16, "w_idx", (128, 512))
+    with _on(stream):
+        if kv_out is None:
+            kv_out = torch.empty((n, 288), dtype=torch.uint8, device=latent.device)
+        if idx_out is None:
+            idx_out = torch.empty((n, 68), dtype=torch.uint8, device=latent.device)
+    _cache(kv_out, "kv_out", 288)
+    _cache(idx_out, "idx_out", 68)
+    if rope_cs.shape[0] < n or kv_out.shape[0] < n or idx_out.shape[0] < n:
+        raise ValueError("rope_cs, kv_out and idx_out need a row per entry")
     _check("csa2_compress_pack", _L.csa2_compress_pack(
-        _ptr(latent), n, m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_out), _ptr(idx_out),
+        _ptr(latent), n, m, _ptr(pool_w), per_token, _ptr(rope_cs), _ptr(w_idx), _ptr(kv_out), _ptr(idx_out),
         _stream(stream)))
     return kv_out, idx_out
 
 
 def compress_append(latent, m: int, pool_w, rope_cs, w_idx, dst_rows, kv_cache, idx_cache, stream=None):
-    """Pack entries from latent bf16 [n*m, 512] into cache rows dst_rows (int64 [n], -1 drops)."""
-    _dev(latent, torch.bfloat16, "latent", 2)
-    n = latent.shape[0] // m
-    _dev(pool_w, torch.float32, "pool_w")
-    _dev(rope_cs, torch.float32, "rope_cs", 2)
-    _dev(w_idx, torch.bfloat16, "w_idx", 2)
-    _dev(dst_rows, torch.int64, "dst_rows", 1)
-    _dev(kv_cache, torch.uint8, "kv_cache")
-    _dev(idx_cache, torch.uint8, "idx_cache")
-    if rope_cs.shape[0] < n or dst_rows.numel() != n:
-        raise ValueError("rope_cs / dst_rows must cover every new entry")
+    """Pack entries from latent bf16 [n*m, 512] into cache rows dst_rows (int64 [n], -1 drops;
+    every row must lie inside both caches)."""
+    n = _latent_rows(latent, m)
+    per_token = _pool_weights(pool_w, m, n * m)
+    _dev(rope_cs, torch.float32, "rope_cs", (None, 64))
+    _dev(w_idx, torch.bfloat16, "w_idx", (128, 512))
+    _need(dst_rows, "dst_rows")
+    _dev(dst_rows, torch.int64, "dst_rows", (n,))
+    _cache(kv_cache, "kv_cache", 288)
+    _cache(idx_cache, "idx_cache", 68)
+    if rope_cs.shape[0] < n:
+        raise ValueError("rope_cs must cover every new entry")
     _check("csa2_compress_append", _L.csa2_compress_append(
-        _ptr(latent), n, m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(dst_rows), _ptr(kv_cache),
+        _ptr(latent), n, m, _ptr(pool_w), per_token, _ptr(rope_cs), _ptr(w_idx), _ptr(dst_rows), _ptr(kv_cache),
         _ptr(idx_cache), _stream(stream)))
+
+
+def _query_rows(q_base, q_nvis, n_q):
+    _need(q_base, "q_base")
+    _need(q_nvis, "q_nvis")
+    _dev(q_base, torch.int64, "q_base", (n_q,))
+    _dev(q_nvis, torch.int32, "q_nvis", (n_q,))
+
+
+def _score_outputs(scores, block_max, want_block_max, n_q, width, dev, stream, full_mode=True):
+    with _on(stream):
+        if scores is None:
+            scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
+        if block_max is None and want_block_max and full_mode:
+            block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
+    _dev(scores, torch.float32, "scores", (n_q, width))
+    if block_max is not None and not full_mode:
+        raise ValueError("block_max is written in Full mode only")
+    _dev(block_max, torch.float32, "block_max", (n_q, (width + 7) // 8))
+    return scores, block_max
+
+
+def _index_args(q, q_kind, head_w, idx_cache, q_base, q_nvis, width, pool_blocks):
+    if q_kind == "fp4":
+        _dev(q, torch.uint8, "q_fp4", (None, 32, 68))
+    else:
+        _dev(q, torch.bfloat16, "q_idx", (None, 32, 128))
+    n_q = q.shape[0]
+    _dev(head_w, torch.float32, "head_w", (n_q, 32))
+    _cache(idx_cache, "idx_cache", 68)
+    _query_rows(q_base, q_nvis, n_q)
+    M = 0
+    if pool_blocks is not None:
+        _dev(pool_blocks, torch.int32, "pool_blocks", (n_q, None))
+        M = pool_blocks.shape[1]
+        if width != 8 * M:
+            raise ValueError(f"candidate mode scores 8 slots per pool block: width must be {8 * M}")
+    if width < 0:
+        raise ValueError("width must be >= 0")
+    return n_q, M
 
 
 def index_score(q_idx, head_w, idx_cache, q_base, q_nvis, width: int, pool_blocks=None,
                 scores=None, block_max=None, want_block_max: bool = True, stream=None):
     """Indexer scores [n_q, width] (+ block maxima [n_q, ceil(width/8)] in Full mode)."""
-    _dev(q_idx, torch.bfloat16, "q_idx", 3)
-    _dev(head_w, torch.float32, "head_w", 2)
-    _dev(idx_cache, torch.uint8, "idx_cache")
-    _dev(q_base, torch.int64, "q_base", 1)
-    _dev(q_nvis, torch.int32, "q_nvis", 1)
-    _dev(pool_blocks, torch.int32, "pool_blocks", 2)
-    n_q = q_idx.shape[0]
-    M = 0 if pool_blocks is None else pool_blocks.shape[1]
-    dev = q_idx.device
-    if scores is None:
-        scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
-    if block_max is None and want_block_max and pool_blocks is None:
-        block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
-    _dev(scores, torch.float32, "scores")
-    _dev(block_max, torch.float32, "block_max")
+    n_q, M = _index_args(q_idx, "bf16", head_w, idx_cache, q_base, q_nvis, width, pool_blocks)
+    scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_idx.device, stream,
+                                       full_mode=pool_blocks is None)
     _check("csa2_index_score", _L.csa2_index_score(
         _ptr(q_idx), _ptr(head_w), _ptr(idx_cache), _ptr(q_base), _ptr(q_nvis), _ptr(pool_blocks),
         M, n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
     return scores, block_max
+
+
+def _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q):
+    n = _latent_rows(latent, m)
+    if n != n_q:
+        raise ValueError("latent must hold m rows per query")
+    per_token = _pool_weights(pool_w, m, n_q * m)
+    _dev(rope_cs, torch.float32, "rope_cs", (None, 64))
+    if rope_cs.shape[0] < n_q:
+        raise ValueError("rope_cs must cover every new entry")
+    _dev(w_idx, torch.bfloat16, "w_idx", (128, 512))
+    _cache(kv_cache, "kv_cache", 288)
+    _cache(idx_cache, "idx_cache", 68)
+    return per_token
 
 
 def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q_idx, head_w, q_base, q_nvis,
@@ -175,39 +278,20 @@ def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cac
     q_base[t] + q_nvis[t] - 1, then scores every visible entry: compress_append followed by
     Full-mode index_score, in one launch.  q_idx is bf16 [n_q, 32, 128] or MXFP4 uint8
     [n_q, 32, 68] (from quantize_q_mxfp4); pack_q=True with a bf16 q_idx packs it to MXFP4
-    inside the launch (quantize_q_mxfp4 followed by the MXFP4-query call)."""
-    fp4 = q_idx.dtype == torch.uint8
+    inside the launch (quantize_q_mxfp4 followed by the MXFP4-query call).  pool_w: fp32
+    [m, 512], or [n_q*m, 512] for one weight row per latent token."""
+    fp4 = isinstance(q_idx, torch.Tensor) and q_idx.dtype == torch.uint8
     if pack_q and fp4:
         raise ValueError("pack_q takes a bf16 q_idx")
-    _dev(q_idx, torch.uint8 if fp4 else torch.bfloat16, "q_idx", 3)
-    if fp4 and tuple(q_idx.shape[1:]) != (32, 68):
-        raise ValueError("an MXFP4 q_idx must be [n_q, 32, 68]")
-    n_q = q_idx.shape[0]
-    _dev(latent, torch.bfloat16, "latent", 2)
-    if latent.shape[0] != n_q * m:
-        raise ValueError("latent must hold m rows per query")
-    _dev(pool_w, torch.float32, "pool_w")
-    _dev(rope_cs, torch.float32, "rope_cs", 2)
-    if rope_cs.shape[0] < n_q:
-        raise ValueError("rope_cs must cover every new entry")
-    _dev(w_idx, torch.bfloat16, "w_idx", 2)
-    _dev(kv_cache, torch.uint8, "kv_cache")
-    _dev(idx_cache, torch.uint8, "idx_cache")
-    _dev(head_w, torch.float32, "head_w", 2)
-    _dev(q_base, torch.int64, "q_base", 1)
-    _dev(q_nvis, torch.int32, "q_nvis", 1)
-    dev = q_idx.device
-    if scores is None:
-        scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
-    if block_max is None and want_block_max:
-        block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
-    _dev(scores, torch.float32, "scores")
-    _dev(block_max, torch.float32, "block_max")
+    n_q, _ = _index_args(q_idx, "fp4" if fp4 else "bf16", head_w, idx_cache, q_base, q_nvis, width, None)
+    per_token = _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q)
+    scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_idx.device, stream)
     name = "csa2_append_index_score" + ("_fp4q" if fp4 else "_packq" if pack_q else "")
     fn = getattr(_L, name)
     _check(name, fn(
-        _ptr(latent), m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache), _ptr(q_idx),
-        _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
+        _ptr(latent), m, _ptr(pool_w), per_token, _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache),
+        _ptr(q_idx), _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width, _ptr(scores), _ptr(block_max),
+        _stream(stream)))
     return scores, block_max
 
 
@@ -218,36 +302,16 @@ def append_mean_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, id
     does, re-packs the mean record of the block holding it (mean_cache row
     mean_base[t] + (q_nvis[t] - 1) // 8), then scores the ceil(q_nvis[t] / 8) visible block
     means: compress_append, block_mean_pack and index_score over mean_cache."""
-    fp4 = q_idx.dtype == torch.uint8
-    _dev(q_idx, torch.uint8 if fp4 else torch.bfloat16, "q_idx", 3)
-    if fp4 and tuple(q_idx.shape[1:]) != (32, 68):
-        raise ValueError("an MXFP4 q_idx must be [n_q, 32, 68]")
-    n_q = q_idx.shape[0]
-    _dev(latent, torch.bfloat16, "latent", 2)
-    if latent.shape[0] != n_q * m:
-        raise ValueError("latent must hold m rows per query")
-    _dev(pool_w, torch.float32, "pool_w")
-    _dev(rope_cs, torch.float32, "rope_cs", 2)
-    if rope_cs.shape[0] < n_q:
-        raise ValueError("rope_cs must cover every new entry")
-    _dev(w_idx, torch.bfloat16, "w_idx", 2)
-    _dev(kv_cache, torch.uint8, "kv_cache")
-    _dev(idx_cache, torch.uint8, "idx_cache")
-    _dev(mean_cache, torch.uint8, "mean_cache")
-    _dev(mean_base, torch.int64, "mean_base", 1)
-    _dev(head_w, torch.float32, "head_w", 2)
-    _dev(q_base, torch.int64, "q_base", 1)
-    _dev(q_nvis, torch.int32, "q_nvis", 1)
-    dev = q_idx.device
-    if scores is None:
-        scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
-    if block_max is None and want_block_max:
-        block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
-    _dev(scores, torch.float32, "scores")
-    _dev(block_max, torch.float32, "block_max")
+    fp4 = isinstance(q_idx, torch.Tensor) and q_idx.dtype == torch.uint8
+    n_q, _ = _index_args(q_idx, "fp4" if fp4 else "bf16", head_w, idx_cache, q_base, q_nvis, width, None)
+    per_token = _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q)
+    _cache(mean_cache, "mean_cache", 68)
+    _need(mean_base, "mean_base")
+    _dev(mean_base, torch.int64, "mean_base", (n_q,))
+    scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_idx.device, stream)
     fn = _L.csa2_append_mean_index_score_fp4q if fp4 else _L.csa2_append_mean_index_score
     _check("csa2_append_mean_index_score" + ("_fp4q" if fp4 else ""), fn(
-        _ptr(latent), m, _ptr(pool_w), _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache),
+        _ptr(latent), m, _ptr(pool_w), per_token, _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache),
         _ptr(mean_cache), _ptr(mean_base), _ptr(q_idx), _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width,
         _ptr(scores), _ptr(block_max), _stream(stream)))
     return scores, block_max
@@ -256,14 +320,13 @@ def append_mean_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, id
 def quantize_q_mxfp4(q_idx, out=None, stream=None):
     """bf16 head vectors [..., 128] -> MXFP4 records uint8 [..., 68] (the indexer-K format)."""
     _dev(q_idx, torch.bfloat16, "q_idx")
-    if q_idx.shape[-1] != 128:
+    if q_idx.dim() < 1 or q_idx.shape[-1] != 128:
         raise ValueError("q_idx must end in 128 channels")
     n_vec = q_idx.numel() // 128
-    if out is None:
-        out = torch.empty((*q_idx.shape[:-1], 68), dtype=torch.uint8, device=q_idx.device)
-    _dev(out, torch.uint8, "out")
-    if out.numel() != n_vec * 68:
-        raise ValueError("out must hold 68 bytes per head vector")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((*q_idx.shape[:-1], 68), dtype=torch.uint8, device=q_idx.device)
+    _dev(out, torch.uint8, "out", (*q_idx.shape[:-1], 68))
     _check("csa2_quantize_q_mxfp4", _L.csa2_quantize_q_mxfp4(_ptr(q_idx), n_vec, _ptr(out), _stream(stream)))
     return out
 
@@ -271,23 +334,9 @@ def quantize_q_mxfp4(q_idx, out=None, stream=None):
 def index_score_fp4q(q_fp4, head_w, idx_cache, q_base, q_nvis, width: int, pool_blocks=None,
                      scores=None, block_max=None, want_block_max: bool = True, stream=None):
     """index_score with MXFP4 queries q_fp4 uint8 [n_q, 32, 68] (from quantize_q_mxfp4)."""
-    _dev(q_fp4, torch.uint8, "q_fp4", 3)
-    if tuple(q_fp4.shape[1:]) != (32, 68):
-        raise ValueError("q_fp4 must be [n_q, 32, 68]")
-    _dev(head_w, torch.float32, "head_w", 2)
-    _dev(idx_cache, torch.uint8, "idx_cache")
-    _dev(q_base, torch.int64, "q_base", 1)
-    _dev(q_nvis, torch.int32, "q_nvis", 1)
-    _dev(pool_blocks, torch.int32, "pool_blocks", 2)
-    n_q = q_fp4.shape[0]
-    M = 0 if pool_blocks is None else pool_blocks.shape[1]
-    dev = q_fp4.device
-    if scores is None:
-        scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
-    if block_max is None and want_block_max and pool_blocks is None:
-        block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
-    _dev(scores, torch.float32, "scores")
-    _dev(block_max, torch.float32, "block_max")
+    n_q, M = _index_args(q_fp4, "fp4", head_w, idx_cache, q_base, q_nvis, width, pool_blocks)
+    scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_fp4.device, stream,
+                                       full_mode=pool_blocks is None)
     _check("csa2_index_score_fp4q", _L.csa2_index_score_fp4q(
         _ptr(q_fp4), _ptr(head_w), _ptr(idx_cache), _ptr(q_base), _ptr(q_nvis), _ptr(pool_blocks),
         M, n_q, width, _ptr(scores), _ptr(block_max), _stream(stream)))
@@ -303,50 +352,57 @@ def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool
                want_topk: bool = True):
     """(pool [n_q, M] or None, topk [n_q, K] or None): Full mode when pool_blocks is None.
     want_topk=False is the pool-only mode: the pool from block_max [n_q, nbw] (the caller's
-    block scores); scores may then be None (the row width is 8 * nbw)."""
-    _dev(scores, torch.float32, "scores", 2)
-    _dev(q_nvis, torch.int32, "q_nvis", 1)
-    _dev(block_max, torch.float32, "block_max", 2 if scores is None else None)
-    _dev(pool_blocks, torch.int32, "pool_blocks", 2)
+    block scores); scores may then be None (the row width is 8 * nbw).  A given workspace
+    must hold block_topk_workspace(...) bytes and start zeroed (every call leaves it so)."""
+    _dev(scores, torch.float32, "scores", (None, None))
     if scores is not None:
         n_q, width = scores.shape
         dev = scores.device
     else:
         if want_topk or block_max is None:
             raise ValueError("scores may be None only in pool-only mode (want_topk=False, block_max given)")
+        _dev(block_max, torch.float32, "block_max", (None, None))
         n_q, width = block_max.shape[0], 8 * block_max.shape[1]
         dev = block_max.device
+    _need(q_nvis, "q_nvis")
+    _dev(q_nvis, torch.int32, "q_nvis", (n_q,))
+    _dev(block_max, torch.float32, "block_max", (n_q, (width + 7) // 8))
     if pool_blocks is not None:
+        _dev(pool_blocks, torch.int32, "pool_blocks", (n_q, None))
         M = pool_blocks.shape[1]
         want_pool = False
-    if pool_out is None and want_pool:
-        pool_out = torch.empty((n_q, M), dtype=torch.int32, device=dev)
-    if topk_out is None and want_topk:
-        topk_out = torch.empty((n_q, K), dtype=torch.int32, device=dev)
-    _dev(pool_out, torch.int32, "pool_out")
-    _dev(topk_out, torch.int32, "topk_out")
-    need = block_topk_workspace(n_q, width, M, K)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        # the histogram region must start zeroed; every call leaves it zeroed
-        workspace = torch.zeros(max(need, 4), dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        if width != 8 * M or block_max is not None or pool_out is not None:
+            raise ValueError("candidate mode: scores [n_q, 8 * M], no block_max and no pool output")
+    with _on(stream):
+        if pool_out is None and want_pool:
+            pool_out = torch.empty((n_q, M), dtype=torch.int32, device=dev)
+        if topk_out is None and want_topk:
+            topk_out = torch.empty((n_q, K), dtype=torch.int32, device=dev)
+        need = block_topk_workspace(n_q, width, M, K)
+        if workspace is None:
+            # the histogram region must start zeroed; every call leaves it zeroed
+            workspace = torch.zeros(max(need, 4), dtype=torch.uint8, device=dev)
+    _dev(pool_out, torch.int32, "pool_out", (n_q, M))
+    _dev(topk_out, torch.int32, "topk_out", (n_q, K))
+    _dev(workspace, workspace.dtype, "workspace")
     _check("csa2_block_topk", _L.csa2_block_topk(
         _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(pool_blocks), 8, M, K,
-        _ptr(pool_out), _ptr(topk_out), _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(pool_out), _ptr(topk_out), _ptr(workspace), _bytes(workspace), _stream(stream)))
     return pool_out, topk_out
 
 
 def block_mean_pack(idx_cache, seq_base, seq_n, n_blocks: int, mean_cache, mean_base, first_block=None,
                     stream=None):
     """HISA block-mean records of blocks first_block[s] .. + n_blocks - 1 into mean_cache."""
-    for t, name, dt in ((idx_cache, "idx_cache", torch.uint8), (seq_base, "seq_base", torch.int64),
-                        (seq_n, "seq_n", torch.int32), (mean_cache, "mean_cache", torch.uint8),
-                        (mean_base, "mean_base", torch.int64), (first_block, "first_block", torch.int32)):
-        _dev(t, dt, name)
+    _cache(idx_cache, "idx_cache", 68)
+    _cache(mean_cache, "mean_cache", 68)
+    _need(seq_base, "seq_base")
     n_seq = seq_base.numel()
-    if seq_n.numel() != n_seq or mean_base.numel() != n_seq or (first_block is not None and
-                                                                first_block.numel() != n_seq):
-        raise ValueError("seq_base, seq_n, mean_base and first_block need one element per sequence")
+    for t, name, dt in ((seq_base, "seq_base", torch.int64), (seq_n, "seq_n", torch.int32),
+                        (mean_base, "mean_base", torch.int64), (first_block, "first_block", torch.int32)):
+        if t is None and name != "first_block":
+            raise ValueError(f"{name} is required")
+        _dev(t, dt, name, (n_seq,))
     _check("csa2_block_mean_pack", _L.csa2_block_mean_pack(
         _ptr(idx_cache), _ptr(seq_base), _ptr(seq_n), _ptr(first_block), n_seq, n_blocks, _ptr(mean_cache),
         _ptr(mean_base), _stream(stream)))
@@ -357,47 +413,60 @@ def sparse_attn_workspace(n_q: int, K: int) -> int:
     return int(_L.csa2_sparse_attn_workspace(n_q, K))
 
 
+def _attn_args(q, kv_cache, q_base, topk, swa_start, swa_len):
+    _dev(q, torch.bfloat16, "q", (None, 64, 512))
+    n_q = q.shape[0]
+    _cache(kv_cache, "kv_cache", 288)
+    _need(q_base, "q_base")
+    _dev(q_base, torch.int64, "q_base", (n_q,))
+    _need(topk, "topk")
+    _dev(topk, torch.int32, "topk", (n_q, None))
+    for t, name, dt in ((swa_start, "swa_start", torch.int64), (swa_len, "swa_len", torch.int32)):
+        _need(t, name)
+        _dev(t, dt, name, (n_q,))
+    return n_q, topk.shape[1]
+
+
+def _attn_outputs(out, lse, want_lse, workspace, n_q, K, dev, stream):
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n_q, 64, 512), dtype=torch.float32, device=dev)
+        if lse is None and want_lse:
+            lse = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
+        need = sparse_attn_workspace(n_q, K)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(out, torch.float32, "out", (n_q, 64, 512))
+    _dev(lse, torch.float32, "lse", (n_q, 64))
+    if workspace is not None:
+        _dev(workspace, workspace.dtype, "workspace")
+    return out, lse, workspace
+
+
 def sparse_attn(q, kv_cache, q_base, topk, swa, swa_start, swa_len, scale: float = DEFAULT_SCALE,
                 out=None, lse=None, want_lse: bool = True, workspace=None, stream=None):
     """Attention output fp32 [n_q, 64, 512] (+ lse [n_q, 64])."""
-    _dev(q, torch.bfloat16, "q", 3)
-    _dev(kv_cache, torch.uint8, "kv_cache")
-    _dev(q_base, torch.int64, "q_base", 1)
-    _dev(topk, torch.int32, "topk", 2)
-    _dev(swa, torch.bfloat16, "swa", 2)
-    _dev(swa_start, torch.int64, "swa_start", 1)
-    _dev(swa_len, torch.int32, "swa_len", 1)
-    n_q = q.shape[0]
-    K = topk.shape[1]
-    dev = q.device
-    if out is None:
-        out = torch.empty((n_q, 64, 512), dtype=torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
-    _dev(out, torch.float32, "out")
-    _dev(lse, torch.float32, "lse")
-    need = sparse_attn_workspace(n_q, K)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    n_q, K = _attn_args(q, kv_cache, q_base, topk, swa_start, swa_len)
+    _need(swa, "swa")
+    _dev(swa, torch.bfloat16, "swa", (None, 512))
+    out, lse, workspace = _attn_outputs(out, lse, want_lse, workspace, n_q, K, q.device, stream)
     _check("csa2_sparse_attn", _L.csa2_sparse_attn(
         _ptr(q), _ptr(kv_cache), _ptr(q_base), _ptr(topk), K, _ptr(swa), _ptr(swa_start), _ptr(swa_len),
-        float(scale), _ptr(out), _ptr(lse), n_q, _ptr(workspace), ws_bytes, _stream(stream)))
+        float(scale), _ptr(out), _ptr(lse), n_q, _ptr(workspace), _bytes(workspace), _stream(stream)))
     return out, lse
 
 
 def swa_pack_fp8(rows, out=None, dst_rows=None, stream=None):
     """bf16 window rows [n, 512] -> FP8 window rows uint8 [n, 584] (or into `out` at dst_rows)."""
-    _dev(rows, torch.bfloat16, "rows", 2)
-    _dev(dst_rows, torch.int64, "dst_rows", 1)
+    _dev(rows, torch.bfloat16, "rows", (None, 512))
     n = rows.shape[0]
-    if out is None:
-        out = torch.empty((n, SWA_FP8_ROW_BYTES), dtype=torch.uint8, device=rows.device)
-    _dev(out, torch.uint8, "out")
-    if dst_rows is None and out.numel() < n * SWA_FP8_ROW_BYTES:
-        raise ValueError("out too small")
-    if dst_rows is not None and dst_rows.numel() != n:
-        raise ValueError("dst_rows must hold one row index per input row")
+    _dev(dst_rows, torch.int64, "dst_rows", (n,))
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n, SWA_FP8_ROW_BYTES), dtype=torch.uint8, device=rows.device)
+    _cache(out, "out", SWA_FP8_ROW_BYTES)
+    if dst_rows is None and out.shape[0] < n:
+        raise ValueError("out needs a row per input row")
     _check("csa2_swa_pack_fp8", _L.csa2_swa_pack_fp8(_ptr(rows), n, _ptr(dst_rows), _ptr(out), _stream(stream)))
     return out
 
@@ -406,27 +475,11 @@ def sparse_attn_swa_fp8(q, kv_cache, q_base, topk, swa8, swa_start, swa_len, swa
                         scale: float = DEFAULT_SCALE, out=None, lse=None, want_lse: bool = True,
                         workspace=None, stream=None):
     """sparse_attn with the window read from FP8 window rows (optionally per-sequence rings)."""
-    _dev(q, torch.bfloat16, "q", 3)
-    _dev(kv_cache, torch.uint8, "kv_cache")
-    _dev(q_base, torch.int64, "q_base", 1)
-    _dev(topk, torch.int32, "topk", 2)
-    _dev(swa8, torch.uint8, "swa8")
-    _dev(swa_start, torch.int64, "swa_start", 1)
-    _dev(swa_len, torch.int32, "swa_len", 1)
-    n_q = q.shape[0]
-    K = topk.shape[1]
-    dev = q.device
-    if out is None:
-        out = torch.empty((n_q, 64, 512), dtype=torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
-    _dev(out, torch.float32, "out")
-    _dev(lse, torch.float32, "lse")
-    need = sparse_attn_workspace(n_q, K)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    n_q, K = _attn_args(q, kv_cache, q_base, topk, swa_start, swa_len)
+    _cache(swa8, "swa8", SWA_FP8_ROW_BYTES)
+    out, lse, workspace = _attn_outputs(out, lse, want_lse, workspace, n_q, K, q.device, stream)
     _check("csa2_sparse_attn_swa_fp8", _L.csa2_sparse_attn_swa_fp8(
         _ptr(q), _ptr(kv_cache), _ptr(q_base), _ptr(topk), K, _ptr(swa8), int(swa_ring), _ptr(swa_start),
-        _ptr(swa_len), float(scale), _ptr(out), _ptr(lse), n_q, _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(swa_len), float(scale), _ptr(out), _ptr(lse), n_q, _ptr(workspace), _bytes(workspace),
+        _stream(stream)))
     return out, lse

@@ -37,7 +37,8 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
     const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
     const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
     const void* __restrict__ q_in, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
-    const int32_t* __restrict__ q_nvis, int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
+    const int32_t* __restrict__ q_nvis, int32_t width, float* __restrict__ scores, float* __restrict__ block_max,
+    int64_t w_stride) {
   const int t = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   if (blockIdx.x >= kAppendWgs) {
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
   __shared__ EntryShared sh;
   const int32_t nvis = q_nvis[t];
   const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
-  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
+  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
                     idx_cache, sh);
   score_tiles<false, kFp4Q, kNewestSlots>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
                                           block_max, t, wave, kWaves, sh.idx_row);
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void append_index_packq_kernel(
     const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
     const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
     const uint16_t* __restrict__ q_bf16, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
-    const int32_t* __restrict__ q_nvis, int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
+    const int32_t* __restrict__ q_nvis, int32_t width, float* __restrict__ scores, float* __restrict__ block_max,
+    int64_t w_stride) {
   const int t = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   __shared__ __attribute__((aligned(16))) uint8_t q_rec[kIdxHeads * kIdxBytes];
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void append_index_packq_kernel(
   __shared__ EntryShared sh;
   const int32_t nvis = q_nvis[t];
   const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
-  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
+  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
                     idx_cache, sh);
   score_tiles<false, true, kNewestSlots>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
                                          block_max, t, wave, kWaves, sh.idx_row, q_rec);
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
     const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
     uint8_t* __restrict__ mean_cache, const int64_t* __restrict__ mean_base, const void* __restrict__ q_in,
     const float* __restrict__ head_w, const int64_t* __restrict__ q_base, const int32_t* __restrict__ q_nvis,
-    int32_t width, float* __restrict__ scores, float* __restrict__ block_max) {
+    int32_t width, float* __restrict__ scores, float* __restrict__ block_max, int64_t w_stride) {
   const int t = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   if (blockIdx.x >= kAppendWgs) {
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
   __shared__ MeanEntryShared sh;
   const int32_t nvis = q_nvis[t];
   const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
-  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
+  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
                     idx_cache, sh.e);
   if (nvis > 0 && threadIdx.x < 16) {  // lane 4g + sub: channels 32g + 8sub .. + 7
     const int g = threadIdx.x >> 2, sub = threadIdx.x & 3;
@@ -146,21 +148,8 @@ __global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
                                                 scores, block_max, t, wave, kWaves, sh.mean_row);
 }
 
-// workgroups of a kernel of this file that fit on the device at once (queried per device)
-template <typename Kernel>
-int resident_workgroups(Kernel kernel, int (&cached)[64]) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu <= 0)
-      per_cu = 2;
-    cached[dev] = cus * per_cu;
-  }
-  return cached[dev];
-}
-int resident_entry[64], resident_packq[64], resident_mean[64];
+// workgroups of each kernel of this file that fit on the device at once (per device)
+std::atomic<int> resident_entry[kMaxDevices], resident_packq[kMaxDevices], resident_mean[kMaxDevices];
 
 // workgroups along x: the append workgroup, then the scan's share of one round of resident
 // workgroups (at least one, at most what the row's tiles can use)
@@ -173,12 +162,17 @@ int64_t grid_x(int resident, int32_t n_q, int32_t width) {
   return kAppendWgs + scan_x;
 }
 
+// floats from one query's pooling-weight rows to the next: 0 for the static [m, 512] weights,
+// m * 512 for per-token weights [n_q * m, 512]
+int64_t weight_stride(int m, int per_token_w) { return (per_token_w && m > 1) ? (int64_t)m * kD : 0; }
+
 // the checks both fused calls share
 template <bool kFp4Q>
-int check_args(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs, const uint16_t* w_idx,
-               uint8_t* kv_cache, uint8_t* idx_cache, const void* q, const float* head_w, const int64_t* q_base,
-               const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores, float* block_max) {
-  if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
+int check_args(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,
+               const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const void* q, const float* head_w,
+               const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
+               float* block_max) {
+  if (n_q < 0 || width < 0 || (per_token_w != 0 && per_token_w != 1)) return CSA2_ERR_INVALID_ARG;
   if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
   if (width == 0) return CSA2_ERR_INVALID_ARG;  // every query appends into a visible slot
@@ -199,99 +193,99 @@ int check_args(const uint16_t* latent, int m, const float* pool_w, const float* 
 }
 
 template <bool kFp4Q>
-int append_index_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
+int append_index_entry(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,
                        const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const void* q,
                        const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
                        float* scores, float* block_max, void* stream) {
-  const int rc = check_args<kFp4Q>(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
+  const int rc = check_args<kFp4Q>(latent, m, pool_w, per_token_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
                                   n_q, width, scores, block_max);
   if (rc != CSA2_OK || n_q == 0) return rc;
-  const int64_t gx = grid_x(resident_workgroups(append_index_kernel<false>, resident_entry), n_q, width);
+  const int64_t gx = grid_x(resident_workgroups(append_index_kernel<false>, kThreads, resident_entry), n_q, width);
   hipLaunchKernelGGL(append_index_kernel<kFp4Q>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads),
                      0, (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w,
-                     q_base, q_nvis, width, scores, block_max);
+                     q_base, q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
   return check_launch();
 }
 
-int append_index_packq_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
+int append_index_packq_entry(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,
                              const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const uint16_t* q,
                              const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q,
                              int32_t width, float* scores, float* block_max, void* stream) {
-  const int rc = check_args<false>(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
+  const int rc = check_args<false>(latent, m, pool_w, per_token_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
                                    n_q, width, scores, block_max);
   if (rc != CSA2_OK || n_q == 0) return rc;
-  const int64_t gx = grid_x(resident_workgroups(append_index_packq_kernel, resident_packq), n_q, width);
+  const int64_t gx = grid_x(resident_workgroups(append_index_packq_kernel, kThreads, resident_packq), n_q, width);
   hipLaunchKernelGGL(append_index_packq_kernel, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
                      (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
-                     q_nvis, width, scores, block_max);
+                     q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
   return check_launch();
 }
 
 template <bool kFp4Q>
-int append_mean_index_entry(const uint16_t* latent, int m, const float* pool_w, const float* rope_cs,
+int append_mean_index_entry(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,
                             const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, uint8_t* mean_cache,
                             const int64_t* mean_base, const void* q, const float* head_w, const int64_t* q_base,
                             const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores, float* block_max,
                             void* stream) {
-  const int rc = check_args<kFp4Q>(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
+  const int rc = check_args<kFp4Q>(latent, m, pool_w, per_token_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
                                   n_q, width, scores, block_max);
   if (rc != CSA2_OK || n_q == 0) return rc;
   if (!mean_cache || !mean_base || (reinterpret_cast<uintptr_t>(mean_cache) & 15)) return CSA2_ERR_INVALID_ARG;
-  const int64_t gx = grid_x(resident_workgroups(append_mean_index_kernel<false>, resident_mean), n_q, width);
+  const int64_t gx = grid_x(resident_workgroups(append_mean_index_kernel<false>, kThreads, resident_mean), n_q, width);
   hipLaunchKernelGGL(append_mean_index_kernel<kFp4Q>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
                      (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, mean_cache,
-                     mean_base, q, head_w, q_base, q_nvis, width, scores, block_max);
+                     mean_base, q, head_w, q_base, q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
   return check_launch();
 }
 
 }  // namespace
 }  // namespace csa2
 
-extern "C" int csa2_append_index_score(const uint16_t* latent_bf16, int m, const float* pool_w, const float* rope_cs,
+extern "C" int csa2_append_index_score(const uint16_t* latent_bf16, int m, const float* pool_w, int per_token_w, const float* rope_cs,
                                        const uint16_t* w_idx_bf16, uint8_t* kv_cache, uint8_t* idx_cache,
                                        const uint16_t* q_idx_bf16, const float* head_w, const int64_t* q_base,
                                        const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
                                        float* block_max, void* stream) {
-  return csa2::append_index_entry<false>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_idx_bf16,
+  return csa2::append_index_entry<false>(latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_idx_bf16,
                                          head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
 }
 
-extern "C" int csa2_append_index_score_fp4q(const uint16_t* latent_bf16, int m, const float* pool_w,
+extern "C" int csa2_append_index_score_fp4q(const uint16_t* latent_bf16, int m, const float* pool_w, int per_token_w,
                                             const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
                                             uint8_t* idx_cache, const uint8_t* q_fp4, const float* head_w,
                                             const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
                                             float* scores, float* block_max, void* stream) {
-  return csa2::append_index_entry<true>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_fp4,
+  return csa2::append_index_entry<true>(latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_fp4,
                                         head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
 }
 
-extern "C" int csa2_append_index_score_packq(const uint16_t* latent_bf16, int m, const float* pool_w,
+extern "C" int csa2_append_index_score_packq(const uint16_t* latent_bf16, int m, const float* pool_w, int per_token_w,
                                              const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
                                              uint8_t* idx_cache, const uint16_t* q_idx_bf16, const float* head_w,
                                              const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
                                              float* scores, float* block_max, void* stream) {
-  return csa2::append_index_packq_entry(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_idx_bf16,
+  return csa2::append_index_packq_entry(latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_idx_bf16,
                                         head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
 }
 
-extern "C" int csa2_append_mean_index_score(const uint16_t* latent_bf16, int m, const float* pool_w,
+extern "C" int csa2_append_mean_index_score(const uint16_t* latent_bf16, int m, const float* pool_w, int per_token_w,
                                             const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
                                             uint8_t* idx_cache, uint8_t* mean_cache, const int64_t* mean_base,
                                             const uint16_t* q_idx_bf16, const float* head_w, const int64_t* q_base,
                                             const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
                                             float* block_max, void* stream) {
-  return csa2::append_mean_index_entry<false>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+  return csa2::append_mean_index_entry<false>(latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
                                               mean_cache, mean_base, q_idx_bf16, head_w, q_base, q_nvis, n_q, width,
                                               scores, block_max, stream);
 }
 
-extern "C" int csa2_append_mean_index_score_fp4q(const uint16_t* latent_bf16, int m, const float* pool_w,
+extern "C" int csa2_append_mean_index_score_fp4q(const uint16_t* latent_bf16, int m, const float* pool_w, int per_token_w,
                                                  const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
                                                  uint8_t* idx_cache, uint8_t* mean_cache, const int64_t* mean_base,
                                                  const uint8_t* q_fp4, const float* head_w, const int64_t* q_base,
                                                  const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
                                                  float* block_max, void* stream) {
-  return csa2::append_mean_index_entry<true>(latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+  return csa2::append_mean_index_entry<true>(latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
                                              mean_cache, mean_base, q_fp4, head_w, q_base, q_nvis, n_q, width, scores,
                                              block_max, stream);
 }

@@ -24,7 +24,7 @@ template <int kEnt>
 __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
     const uint16_t* __restrict__ latent, int64_t n_entries, int m, const float* __restrict__ pool_w,
     const float* __restrict__ rope_cs, const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out,
-    uint8_t* __restrict__ idx_out, const int64_t* __restrict__ dst_rows) {
+    uint8_t* __restrict__ idx_out, const int64_t* __restrict__ dst_rows, int64_t w_stride) {
   __shared__ float s_c[kEnt][kD];          // rotated fp32 entries
   __shared__ float s_k[kEnt][kIdxDim];     // projected indexer keys
   __shared__ uint16_t s_w[2][kWChunk][kIdxDim + 8];  // W_idx^T chunks (bf16 bits)
@@ -52,7 +52,9 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
         }
       }
     } else {
-      // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded
+      // a_i = w_i / (w_0 + w_1); c = a_0 x_0 + a_1 x_1, each product and sum rounded; the
+      // weights are the entry's own rows when they are per token (w_stride = 2 * 512)
+      const float* pw = pool_w + j * w_stride;
       const uint4* s0 = reinterpret_cast<const uint4*>(latent + (2 * j) * kD + ch0);
       const uint4* s1 = reinterpret_cast<const uint4*>(latent + (2 * j + 1) * kD + ch0);
 #pragma unroll
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
 #pragma unroll
         for (int q = 0; q < 8; q++) {
           const int ch = ch0 + 8 * v + q;
-          const float w0 = pool_w[ch], w1 = pool_w[kD + ch];
+          const float w0 = pw[ch], w1 = pw[kD + ch];
           const float ws = w0 + w1;
           const float a0 = w0 / ws, a1 = w1 / ws;
           const uint32_t xa = (q & 1) ? (a4[q >> 1] >> 16) : (a4[q >> 1] & 0xFFFFu);
@@ -210,11 +212,11 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
 __global__ __launch_bounds__(64) void compress_few_kernel(
     const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
     const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_out, uint8_t* __restrict__ idx_out,
-    const int64_t* __restrict__ dst_rows) {
+    const int64_t* __restrict__ dst_rows, int64_t w_stride) {
   __shared__ FewShared sh;
   const int64_t j = blockIdx.x;
   const int64_t row = dst_rows != nullptr ? dst_rows[j] : j;
-  compress_few_entry(latent + j * m * kD, m, pool_w, rope_cs + j * kDRope, w_idx, blockIdx.y * kFewOut, row, kv_out,
+  compress_few_entry(latent + j * m * kD, m, pool_w + j * w_stride, rope_cs + j * kDRope, w_idx, blockIdx.y * kFewOut, row, kv_out,
                      idx_out, sh);
 }
 
@@ -223,10 +225,10 @@ __global__ __launch_bounds__(64) void compress_few_kernel(
 
 namespace {
 int launch_compress(const uint16_t* latent_bf16, int64_t n_entries, int m, const float* pool_w,
-                    const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_out, uint8_t* idx_out,
+                    int per_token_w, const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_out, uint8_t* idx_out,
                     const int64_t* dst_rows, void* stream) {
   using namespace csa2;
-  if (n_entries < 0) return CSA2_ERR_INVALID_ARG;
+  if (n_entries < 0 || (per_token_w != 0 && per_token_w != 1)) return CSA2_ERR_INVALID_ARG;
   if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
   if (n_entries == 0) return CSA2_OK;
   if (!latent_bf16 || !rope_cs || !w_idx_bf16 || !kv_out || !idx_out) return CSA2_ERR_INVALID_ARG;
@@ -237,33 +239,36 @@ int launch_compress(const uint16_t* latent_bf16, int64_t n_entries, int m, const
   if ((reinterpret_cast<uintptr_t>(rope_cs) | reinterpret_cast<uintptr_t>(pool_w)) & 3 ||
       reinterpret_cast<uintptr_t>(dst_rows) & 7)
     return CSA2_ERR_INVALID_ARG;
+  // floats from one entry's weight rows to the next: 0 for the static [m, 512] weights
+  const int64_t w_stride = (per_token_w && m > 1) ? (int64_t)m * kD : 0;
   if (n_entries <= 64) {
     hipLaunchKernelGGL(compress_few_kernel, dim3((unsigned)n_entries, kIdxDim / kFewOut), dim3(64), 0,
-                       (hipStream_t)stream, latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_out, idx_out, dst_rows);
+                       (hipStream_t)stream, latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_out, idx_out, dst_rows,
+                       w_stride);
   } else {
     const int64_t grid = (n_entries + 15) / 16;
     if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(compress_pack_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0,
                        (hipStream_t)stream, latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16,
-                       kv_out, idx_out, dst_rows);
+                       kv_out, idx_out, dst_rows, w_stride);
   }
   return check_launch();
 }
 }  // namespace
 
 extern "C" int csa2_compress_pack(const uint16_t* latent_bf16, int64_t n_entries, int m,
-                                  const float* pool_w, const float* rope_cs,
+                                  const float* pool_w, int per_token_w, const float* rope_cs,
                                   const uint16_t* w_idx_bf16, uint8_t* kv_out, uint8_t* idx_out,
                                   void* stream) {
-  return launch_compress(latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16, kv_out, idx_out, nullptr,
+  return launch_compress(latent_bf16, n_entries, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_out, idx_out, nullptr,
                          stream);
 }
 
 extern "C" int csa2_compress_append(const uint16_t* latent_bf16, int64_t n_entries, int m,
-                                    const float* pool_w, const float* rope_cs,
+                                    const float* pool_w, int per_token_w, const float* rope_cs,
                                     const uint16_t* w_idx_bf16, const int64_t* dst_rows,
                                     uint8_t* kv_cache, uint8_t* idx_cache, void* stream) {
   if (!dst_rows && n_entries > 0) return CSA2_ERR_INVALID_ARG;
-  return launch_compress(latent_bf16, n_entries, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+  return launch_compress(latent_bf16, n_entries, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
                          dst_rows, stream);
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/csa2.h"
 
 namespace csa2 {
@@ -100,5 +102,27 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 inline int check_launch() { return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+// Workgroups of `threads` threads of `kernel` that fit on the current device at once, for
+// grids sized to one round of resident workgroups.  Computed on a device's first call and
+// kept in `cache` (one slot per device, zero = not known yet).  The figure is the same
+// whichever call computes it, and the slots are atomics, so concurrent first calls on any
+// threads may both compute and store it without a data race.
+constexpr int kMaxDevices = 64;
+template <typename Kernel>
+int resident_workgroups(Kernel kernel, int threads, std::atomic<int> (&cache)[kMaxDevices]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
+      per_cu = 2;
+    v = cus * per_cu;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 }  // namespace csa2

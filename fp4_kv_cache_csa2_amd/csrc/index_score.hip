@@ -27,22 +27,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
 }  // namespace csa2
 
 namespace {
-// workgroups of index_score_kernel that fit on the device at once (queried per device)
-int resident_workgroups() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csa2::index_score_kernel<false, false>, csa2::kThreads,
-                                                     0) != hipSuccess ||
-        per_cu <= 0)
-      per_cu = 2;
-    cached[dev] = cus * per_cu;
-  }
-  return cached[dev];
-}
+// workgroups of index_score_kernel that fit on the device at once (per device)
+std::atomic<int> resident_index[csa2::kMaxDevices];
 
 // argument checks and launch shared by the bf16-query and MXFP4-query entry points
 template <bool kFp4Q>
@@ -76,7 +62,7 @@ int index_score_entry(const void* q, const float* head_w, const uint8_t* idx_cac
                                    scores, block_max, stream);
   }
   // one full round of resident workgroups; each wave strides over its query's tiles
-  int64_t grid_x = (resident_workgroups() + n_q - 1) / n_q;
+  int64_t grid_x = (resident_workgroups(index_score_kernel<false, false>, kThreads, resident_index) + n_q - 1) / n_q;
   const int64_t max_x = (ntiles + kWaves - 1) / kWaves;
   if (grid_x > max_x) grid_x = max_x;
   if (grid_x < 1) grid_x = 1;

@@ -66,20 +66,17 @@ class GlobalBranch:
         ws = max(csa2.block_topk_workspace(n_seq, width, M, K), csa2.block_topk_workspace(n_seq, 8 * M, M, K))
         self.ws_sel = torch.zeros(max(ws, 4), dtype=torch.uint8, device=dev)  # left zeroed by every call
         self.ws_att = torch.empty(max(csa2.sparse_attn_workspace(n_seq, K), 16), dtype=torch.uint8, device=dev)
-        self._cached = {}
+        # the per-token device state of eager decoding, refilled in place for every token
+        self._state = TokenState(self, None)
 
     def set_params(self, c, pool_w, w_idx):
         self.params[c] = (pool_w.contiguous(), w_idx.contiguous())
 
-    def _const(self, key, make):
-        """Small device tensors (visible counts, append rows, RoPE rows) made once per key."""
-        t = self._cached.get(key)
-        if t is None:
-            t = self._cached[key] = make()
-        return t
-
-    def _nvis(self, n):
-        return self._const(("nvis", n), lambda: torch.full((self.n_seq,), n, dtype=torch.int32, device=self.dev))
+    def token_state(self, p):
+        """The device tensors one token at position p reads (visible counts, the appended
+        entries' RoPE rows and cache rows), owned by the caller: a HIP graph captured from
+        decode_token(p, ..., state=s) stays valid while s lives."""
+        return TokenState(self, p)
 
     def fill(self, c, latents, first_entry=0, chunk_tokens=1 << 19):
         """Bulk-pack entries first_entry .. of cache c from latents bf16 [n_seq, tokens, 512]."""
@@ -97,12 +94,23 @@ class GlobalBranch:
                                    w_idx, kv_out=self.kv[c][row:], idx_out=self.ix[c][row:])
         self.n[c] = max(self.n[c], first_entry + tokens // m)
 
-    def decode_token(self, p, new_latents, inputs, outs, lses=None):
+    def decode_token(self, p, new_latents, inputs, outs, lses=None, state=None):
         """One token at position p.  new_latents[c]: bf16 [n_seq * m_c, 512], the m_c newest
         latents of cache c's source (read only when p completes an entry).  inputs[l]: dict
         of device tensors q, swa, swa_start, swa_len, plus q_idx, head_w for Full and Reindex
-        layers.  outs[l] / lses[l]: outputs of layer l."""
-        K, M, ns = self.K, self.M, self.n_seq
+        layers.  outs[l] / lses[l]: outputs of layer l.  state: token_state(p) for a call that
+        is captured into a graph; by default the branch's own state tensors are refilled in
+        place (no device memory is allocated per token)."""
+        K, M = self.K, self.M
+        for c in RATIO:  # the entries this token completes become visible
+            m = RATIO[c]
+            if (p + 1) % m == 0:
+                self.n[c] = max(self.n[c], (p + 1) // m)
+        if state is None:
+            state = self._state
+            state.refill(p)
+        elif state.p != p or state.n != self.n:
+            raise ValueError("state was made for another position")
         for layer, (mode, c) in enumerate(layer_plan()):
             if mode == "swa":
                 continue
@@ -110,12 +118,10 @@ class GlobalBranch:
             if mode == "full":
                 m = RATIO[c]
                 j = (p + 1) // m - 1 if (p + 1) % m == 0 else None  # this token completes entry j of cache c
-                if j is not None:
-                    self.n[c] = max(self.n[c], j + 1)
                 n = self.n[c]
-                nvis = self._nvis(n)
+                nvis = state.nvis[c]
                 if j is not None:
-                    cs = self._const(("rope", c, j), lambda: csa2.rope_table(np.full(ns, m * j, np.int64)).to(self.dev))
+                    cs = state.rope[c]
                     pool_w, w_idx = self.params[c]
                 if j is not None and j == n - 1:
                     # the new entry is the newest visible one: append it and score in one launch
@@ -124,14 +130,14 @@ class GlobalBranch:
                                             scores=self._row_view(n), block_max=self._bmax_view(n))
                 else:
                     if j is not None:
-                        rows = self._const(("rows", c, j), lambda: self.base[c] + j)
-                        csa2.compress_append(new_latents[c], m, pool_w, cs, w_idx, rows, self.kv[c], self.ix[c])
+                        csa2.compress_append(new_latents[c], m, pool_w, cs, w_idx, state.rows[c], self.kv[c],
+                                             self.ix[c])
                     csa2.index_score(inp["q_idx"], inp["head_w"], self.ix[c], self.base[c], nvis, n,
                                      scores=self._row_view(n), block_max=self._bmax_view(n))
                 csa2.block_topk(self._row_view(n), nvis, K=K, M=M, block_max=self._bmax_view(n),
                                 pool_out=self.pool, topk_out=self.topk, workspace=self.ws_sel)
             elif mode == "reindex":
-                nvis = self._nvis(self.n[c])
+                nvis = state.nvis[c]
                 csa2.index_score(inp["q_idx"], inp["head_w"], self.ix[c], self.base[c], nvis, 8 * M,
                                  pool_blocks=self.pool, scores=self.scores_r)
                 csa2.block_topk(self.scores_r, nvis, K=K, pool_blocks=self.pool, topk_out=self.topk,
@@ -141,9 +147,39 @@ class GlobalBranch:
                              want_lse=lses is not None, workspace=self.ws_att)
 
     def _row_view(self, n):
-        """A dense [n_seq, n] score buffer (the kernels take rows of exactly `width` floats)."""
-        return self._const(("scores", n), lambda: self.scores.view(-1)[:self.n_seq * n].view(self.n_seq, n))
+        """A dense [n_seq, n] view of the score buffer (the kernels take rows of exactly `width`
+        floats); a view allocates no device memory."""
+        return self.scores.view(-1)[:self.n_seq * n].view(self.n_seq, n)
 
     def _bmax_view(self, n):
         nb = (n + 7) // 8
-        return self._const(("bmax", n), lambda: self.bmax.view(-1)[:self.n_seq * nb].view(self.n_seq, nb))
+        return self.bmax.view(-1)[:self.n_seq * nb].view(self.n_seq, nb)
+
+
+class TokenState:
+    """Device tensors of one decoding token at position p: per cache the visible count of
+    every sequence (int32 [n_seq]), and for the caches this token appends to, the new entry's
+    RoPE row (fp32 [n_seq, 64]) and its cache row in every sequence (int64 [n_seq])."""
+
+    def __init__(self, branch, p):
+        self.b = branch
+        ns, dev = branch.n_seq, branch.dev
+        self.nvis = {c: torch.zeros(ns, dtype=torch.int32, device=dev) for c in RATIO}
+        self.rope = {c: torch.zeros((ns, 64), dtype=torch.float32, device=dev) for c in RATIO}
+        self.rows = {c: torch.zeros(ns, dtype=torch.int64, device=dev) for c in RATIO}
+        self.p, self.n = None, None
+        if p is not None:
+            self.refill(p)
+
+    def refill(self, p):
+        """Rewrites the tensors in place for position p (stream-ordered after the launches
+        that read their previous values), with the visible counts after p's appends."""
+        b = self.b
+        self.n = {c: max(b.n[c], (p + 1) // m) if (p + 1) % m == 0 else b.n[c] for c, m in RATIO.items()}
+        for c, m in RATIO.items():
+            self.nvis[c].fill_(self.n[c])
+            if (p + 1) % m == 0:
+                j = (p + 1) // m - 1
+                self.rope[c].copy_(csa2.rope_table(np.full(b.n_seq, m * j, np.int64)))
+                torch.add(b.base[c], j, out=self.rows[c])
+        self.p = p

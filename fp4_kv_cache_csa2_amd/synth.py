@@ -105,19 +105,25 @@ def query_inputs(seed: int, n_q: int, q_idx_scale: float | None = None,
     return DecodeInputs(q_idx, head_w, q, swa, np.asarray(swa_start, np.int64), np.asarray(swa_len, np.int32))
 
 
-def random_caches(seed: int, n_entries: int):
+def random_caches(seed: int, n_entries: int, spread_scales: bool = False):
     """Directly drawn packed caches with the entry structure of the pages' formats.
 
     Main KV: 256 uniform payload bytes + 32 E4M3 scale bytes uniform in [0x20, 0x38]
     (scales 0.125 .. 1.0).  Indexer K: 64 uniform payload bytes + 4 E8M0 scale bytes
-    uniform in [124, 127] (2^-3 .. 2^0)."""
+    uniform in [124, 127] (2^-3 .. 2^0).
+
+    spread_scales: the scale bytes cover every non-negative finite E4M3 code (0x00 .. 0x7E:
+    0, the subnormals 2^-9 .. and up to 448) and the E8M0 codes 16 .. 240 (2^-111 .. 2^113:
+    the widest band whose scores stay finite in fp32 with this module's query scale)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     kv = np.empty((n_entries, KV_BYTES), np.uint8)
     kv[:, :256] = rng.integers(0, 256, (n_entries, 256), dtype=np.uint8)
-    kv[:, 256:] = rng.integers(0x20, 0x39, (n_entries, 32), dtype=np.uint8)
+    lo, hi = (0x00, 0x7F) if spread_scales else (0x20, 0x39)
+    kv[:, 256:] = rng.integers(lo, hi, (n_entries, 32), dtype=np.uint8)
     ix = np.empty((n_entries, IDX_BYTES), np.uint8)
     ix[:, :64] = rng.integers(0, 256, (n_entries, 64), dtype=np.uint8)
-    ix[:, 64:] = rng.integers(124, 128, (n_entries, 4), dtype=np.uint8)
+    lo, hi = (16, 241) if spread_scales else (124, 128)
+    ix[:, 64:] = rng.integers(lo, hi, (n_entries, 4), dtype=np.uint8)
     return kv, ix
 
 

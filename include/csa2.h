@@ -10,8 +10,11 @@
  * General contract
  *   - Tensor pointers are DEVICE pointers owned by the caller unless a parameter says
  *     "host".  Arrays are dense and row-major.  bf16 values travel as uint16 bit
- *     patterns.  The library never allocates, frees or synchronises device memory and
- *     keeps no mutable global state; calls on different streams are independent.
+ *     patterns.  The library never allocates, frees or synchronises device memory.  Its
+ *     only host-side global state is a per-device cache of occupancy figures (how many
+ *     workgroups of a kernel fit on the device), held in atomics and written with the same
+ *     value by whichever call computes it first; calls on different streams and host
+ *     threads are independent.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call
  *     is asynchronous on it.  A kernel fault surfaces at the caller's next sync.
  *   - Return value: CSA2_OK (0) or a negative status.  Argument errors are detected on
@@ -56,7 +59,7 @@ enum {
   CSA2_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
 };
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 int csa2_abi_version(void);
 const char *csa2_status_string(int status);
@@ -86,17 +89,20 @@ int csa2_rope_table(const int64_t *pos, int64_t n, double theta, float *out);
  *   saturating at 6), sign bit only on non-zero codes; E8M0 code = floor(log2 amax) - 2
  *   + 127 clamped to [0, 254] (0 when amax = 0).  The output bytes are bit-exact.
  *
- *   latent_bf16 [n_entries*m, 512]; pool_w fp32 [m, 512] (not read when m = 1; weights
- *   must be >= 0 with a positive sum per channel, which is not checked);
+ *   latent_bf16 [n_entries*m, 512]; pool_w fp32 (not read when m = 1; weights must be >= 0
+ *   with a positive sum per channel, which is not checked): per_token_w = 0 -> static
+ *   per-channel weights [m, 512] shared by every entry; per_token_w = 1 -> one weight row per
+ *   latent token, [n_entries*m, 512], row m*j + i weighting latent m*j + i (per-token gates:
+ *   [DF] §4.2 notes the pooling weights may be projected from the input; same formula);
  *   rope_cs fp32 [n_entries, 64] (cos[32], sin[32] at each entry's position, e.g. from
  *   csa2_rope_table); w_idx_bf16 [128, 512];
  *   kv_out [n_entries, 288] and idx_out [n_entries, 68] receive the packed entries.
  *   n_entries = 0 is a no-op.  Errors: INVALID_ARG (NULL, n < 0, misaligned outputs),
- *   UNSUPPORTED (m not 1 or 2).
+ *   UNSUPPORTED (m not 1 or 2); INVALID_ARG also for per_token_w not 0 or 1.
  */
 int csa2_compress_pack(const uint16_t *latent_bf16, int64_t n_entries, int m,
-                       const float *pool_w, const float *rope_cs, const uint16_t *w_idx_bf16,
-                       uint8_t *kv_out, uint8_t *idx_out, void *stream);
+                       const float *pool_w, int per_token_w, const float *rope_cs,
+                       const uint16_t *w_idx_bf16, uint8_t *kv_out, uint8_t *idx_out, void *stream);
 
 /*
  * csa2_compress_append -- csa2_compress_pack writing entry i to cache row dst_rows[i].
@@ -109,8 +115,8 @@ int csa2_compress_pack(const uint16_t *latent_bf16, int64_t n_entries, int m,
  *   Errors: as csa2_compress_pack, and INVALID_ARG for a NULL dst_rows.
  */
 int csa2_compress_append(const uint16_t *latent_bf16, int64_t n_entries, int m, const float *pool_w,
-                         const float *rope_cs, const uint16_t *w_idx_bf16, const int64_t *dst_rows,
-                         uint8_t *kv_cache, uint8_t *idx_cache, void *stream);
+                         int per_token_w, const float *rope_cs, const uint16_t *w_idx_bf16,
+                         const int64_t *dst_rows, uint8_t *kv_cache, uint8_t *idx_cache, void *stream);
 
 /*
  * csa2_index_score -- lightning-indexer scores over the MXFP4 indexer-K cache.
@@ -178,7 +184,9 @@ int csa2_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8
  *   entry and then scores that tile, while the others score every other tile.
  *
  *   Query t appends one entry: latent_bf16 rows [t*m, t*m + m) (bf16 [n_q*m, 512],
- *   16-byte aligned), pool_w fp32 [m, 512] (not read when m = 1), rope_cs fp32 [n_q, 64]
+ *   16-byte aligned), pool_w fp32 [m, 512] (per_token_w = 0) or [n_q*m, 512] with rows
+ *   [t*m, t*m + m) weighting query t's latents (per_token_w = 1; neither is read when m = 1),
+ *   rope_cs fp32 [n_q, 64]
  *   (the entry's cos[32], sin[32]), w_idx_bf16 [128, 512] (16-byte aligned), written to
  *   row q_base[t] + q_nvis[t] - 1 of kv_cache [rows, 288] and idx_cache [rows, 68]
  *   (16-byte aligned bases); q_nvis[t] counts the new entry.  Queries must append to
@@ -187,9 +195,11 @@ int csa2_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8
  *   csa2_index_score in Full mode (no pool), with the same results bit for bit; the
  *   cache bytes are those of csa2_compress_append.
  *   Errors: INVALID_ARG (NULL required pointer, n_q < 0, width <= 0 with n_q > 0,
- *   misalignment), UNSUPPORTED (m not 1 or 2, n_q > 65535, width > 2^23).
+ *   misalignment, per_token_w not 0 or 1), UNSUPPORTED (m not 1 or 2, n_q > 65535,
+ *   width > 2^23).
  */
-int csa2_append_index_score(const uint16_t *latent_bf16, int m, const float *pool_w, const float *rope_cs,
+int csa2_append_index_score(const uint16_t *latent_bf16, int m, const float *pool_w, int per_token_w,
+                            const float *rope_cs,
                             const uint16_t *w_idx_bf16, uint8_t *kv_cache, uint8_t *idx_cache,
                             const uint16_t *q_idx_bf16, const float *head_w, const int64_t *q_base,
                             const int32_t *q_nvis, int32_t n_q, int32_t width, float *scores,
@@ -200,7 +210,7 @@ int csa2_append_index_score(const uint16_t *latent_bf16, int m, const float *poo
  *   (q_fp4 [n_q, 32, 68], 4-byte aligned, from csa2_quantize_q_mxfp4): the scores of
  *   csa2_index_score_fp4q.  Every other argument, result and error as above.
  */
-int csa2_append_index_score_fp4q(const uint16_t *latent_bf16, int m, const float *pool_w,
+int csa2_append_index_score_fp4q(const uint16_t *latent_bf16, int m, const float *pool_w, int per_token_w,
                                  const float *rope_cs, const uint16_t *w_idx_bf16, uint8_t *kv_cache,
                                  uint8_t *idx_cache, const uint8_t *q_fp4, const float *head_w,
                                  const int64_t *q_base, const int32_t *q_nvis, int32_t n_q, int32_t width,
@@ -214,7 +224,8 @@ int csa2_append_index_score_fp4q(const uint16_t *latent_bf16, int m, const float
  *   not written out.  Arguments, results and errors are those of csa2_append_index_score
  *   (q_idx_bf16 [n_q, 32, 128], 16-byte aligned).
  */
-int csa2_append_index_score_packq(const uint16_t *latent_bf16, int m, const float *pool_w, const float *rope_cs,
+int csa2_append_index_score_packq(const uint16_t *latent_bf16, int m, const float *pool_w, int per_token_w,
+                                  const float *rope_cs,
                                   const uint16_t *w_idx_bf16, uint8_t *kv_cache, uint8_t *idx_cache,
                                   const uint16_t *q_idx_bf16, const float *head_w, const int64_t *q_base,
                                   const int32_t *q_nvis, int32_t n_q, int32_t width, float *scores,
@@ -288,8 +299,8 @@ int csa2_block_mean_pack(const uint8_t *idx_cache, const int64_t *seq_base, cons
  *   older entries from idx_cache, the new one as just packed) and scores that tile, while
  *   the others score every other tile of block means.
  *
- *   The appended entry (latent_bf16, m, pool_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
- *   q_base, q_nvis) is that of csa2_append_index_score: row q_base[t] + q_nvis[t] - 1, with
+ *   The appended entry (latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache,
+ *   idx_cache, q_base, q_nvis) is that of csa2_append_index_score: row q_base[t] + q_nvis[t] - 1, with
  *   q_nvis[t] counting it.  Block b of query t covers its entries 8b .. 8b + 7 (rows
  *   q_base[t] + 8b ..); its record is mean_cache row mean_base[t] + b (int64 [n_q];
  *   mean_cache [rows, 68], 16-byte aligned), and the call rewrites that of block
@@ -301,7 +312,8 @@ int csa2_block_mean_pack(const uint8_t *idx_cache, const int64_t *seq_base, cons
  *   Errors: those of csa2_append_index_score, and INVALID_ARG for a NULL or misaligned
  *   mean_cache or a NULL mean_base.
  */
-int csa2_append_mean_index_score(const uint16_t *latent_bf16, int m, const float *pool_w, const float *rope_cs,
+int csa2_append_mean_index_score(const uint16_t *latent_bf16, int m, const float *pool_w, int per_token_w,
+                                 const float *rope_cs,
                                  const uint16_t *w_idx_bf16, uint8_t *kv_cache, uint8_t *idx_cache,
                                  uint8_t *mean_cache, const int64_t *mean_base, const uint16_t *q_idx_bf16,
                                  const float *head_w, const int64_t *q_base, const int32_t *q_nvis, int32_t n_q,
@@ -313,7 +325,7 @@ int csa2_append_mean_index_score(const uint16_t *latent_bf16, int m, const float
  *   Every other argument, result and error as above.
  */
 int csa2_append_mean_index_score_fp4q(const uint16_t *latent_bf16, int m, const float *pool_w,
-                                      const float *rope_cs, const uint16_t *w_idx_bf16, uint8_t *kv_cache,
+                                      int per_token_w, const float *rope_cs, const uint16_t *w_idx_bf16, uint8_t *kv_cache,
                                       uint8_t *idx_cache, uint8_t *mean_cache, const int64_t *mean_base,
                                       const uint8_t *q_fp4, const float *head_w, const int64_t *q_base,
                                       const int32_t *q_nvis, int32_t n_q, int32_t width, float *scores,

@@ -155,7 +155,7 @@ void csa2o_compress_pack(const uint16_t *latent, int64_t n_entries, int m, const
      * are static per channel ([m, 512]) or, with per_token_w, one row per latent token
      * ([n_entries * m, 512]: the gate of token m j + i is row m j + i), the same formula
      * ([DF] §4.2 remarks that the pooling weights may be projected from the input). */
-    const float *w = per_token_w ? pool_w + (j * m) * D_LAT : pool_w;
+    const float *w = (per_token_w && m > 1) ? pool_w + (j * m) * D_LAT : pool_w;
     for (int ch = 0; ch < D_LAT; ch++) {
       const uint16_t *x = latent + (j * m) * D_LAT + ch;
       if (m == 1) {

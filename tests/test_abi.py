@@ -40,22 +40,23 @@ def test_binding_names_match_header():
 
 def test_version_and_status_strings(lib):
     lib.csa2_status_string.restype = ctypes.c_char_p
-    assert lib.csa2_abi_version() == 1
+    assert lib.csa2_abi_version() == 2
     for st in (0, -1, -2, -3, -4):
         assert lib.csa2_status_string(st)
 
 
 def test_host_validation_rejects_before_launch(lib):
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    lib.csa2_compress_pack.argtypes = [vp, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.csa2_compress_pack.argtypes = [vp, i64, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp]
     lib.csa2_index_score.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.csa2_block_topk.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.csa2_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, i32, vp, sz, vp]
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
-    assert lib.csa2_compress_pack(fake, 4, 3, fake, fake, fake, fake, fake, None) == -2
-    assert lib.csa2_compress_pack(fake, -1, 2, fake, fake, fake, fake, fake, None) == -1
-    assert lib.csa2_compress_pack(None, 4, 2, fake, fake, fake, fake, fake, None) == -1
-    assert lib.csa2_compress_pack(fake, 0, 2, None, None, None, None, None, None) == 0
+    assert lib.csa2_compress_pack(fake, 4, 3, fake, 0, fake, fake, fake, fake, None) == -2
+    assert lib.csa2_compress_pack(fake, -1, 2, fake, 0, fake, fake, fake, fake, None) == -1
+    assert lib.csa2_compress_pack(None, 4, 2, fake, 0, fake, fake, fake, fake, None) == -1
+    assert lib.csa2_compress_pack(fake, 4, 2, fake, 2, fake, fake, fake, fake, None) == -1  # per_token_w 0 or 1
+    assert lib.csa2_compress_pack(fake, 0, 2, None, 0, None, None, None, None, None) == 0
     assert lib.csa2_index_score(fake, fake, fake, fake, fake, fake, 4096, 1, 8 * 4096, fake, None, None) == -2
     assert lib.csa2_index_score(fake, fake, fake, fake, fake, fake, 16, 1, 100, fake, None, None) == -1
     assert lib.csa2_index_score(None, fake, fake, fake, fake, None, 0, 1, 100, fake, None, None) == -1
@@ -88,13 +89,14 @@ def test_fp8_window_entry_points_validate_before_launch(lib):
 
 def test_compress_append_validates_before_launch(lib):
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    lib.csa2_compress_append.argtypes = [vp, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+    lib.csa2_compress_append.argtypes = [vp, i64, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp]
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
-    assert lib.csa2_compress_append(fake, 4, 1, None, fake, fake, None, fake, fake, None) == -1  # no rows
-    assert lib.csa2_compress_append(fake, 4, 3, fake, fake, fake, fake, fake, fake, None) == -2
-    assert lib.csa2_compress_append(fake, 4, 1, None, fake, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake,
+    assert lib.csa2_compress_append(fake, 4, 1, None, 0, fake, fake, None, fake, fake, None) == -1  # no rows
+    assert lib.csa2_compress_append(fake, 4, 3, fake, 0, fake, fake, fake, fake, fake, None) == -2
+    assert lib.csa2_compress_append(fake, 4, 1, None, 0, fake, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake,
                                     None) == -1  # rows not 8-B aligned
-    assert lib.csa2_compress_append(fake, 0, 1, None, None, None, None, None, None, None) == 0
+    assert lib.csa2_compress_append(fake, 4, 2, fake, -1, fake, fake, fake, fake, fake, None) == -1
+    assert lib.csa2_compress_append(fake, 0, 1, None, 0, None, None, None, None, None, None) == 0
 
 
 def test_fp4_query_entry_points_validate_before_launch(lib):
@@ -144,11 +146,11 @@ def test_append_index_entry_points_validate_before_launch(lib):
     for name, q_align in (("csa2_append_index_score", 16), ("csa2_append_index_score_fp4q", 4),
                           ("csa2_append_index_score_packq", 16)):
         fn = getattr(lib, name)
-        fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp]
+        fn.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp]
 
-        def call(latent=f, m=2, pool_w=f, rope=f, w=f, kv=f, ix=f, q=f, hw=f, base=f, nvis=f, n_q=4,
+        def call(latent=f, m=2, pool_w=f, per_token=0, rope=f, w=f, kv=f, ix=f, q=f, hw=f, base=f, nvis=f, n_q=4,
                  width=1 << 19, scores=f, bmax=f):
-            return fn(latent, m, pool_w, rope, w, kv, ix, q, hw, base, nvis, n_q, width, scores, bmax, None)
+            return fn(latent, m, pool_w, per_token, rope, w, kv, ix, q, hw, base, nvis, n_q, width, scores, bmax, None)
 
         assert call(n_q=0, latent=None, pool_w=None, q=None) == 0
         assert call(n_q=-1) == -1
@@ -162,6 +164,7 @@ def test_append_index_entry_points_validate_before_launch(lib):
         assert call(ix=f + 4) == -1
         assert call(q=f + q_align // 2) == -1
         assert call(bmax=f + 2) == -1
+        assert call(per_token=3) == -1
 
 
 def test_append_mean_index_entry_points_validate_before_launch(lib):
@@ -169,11 +172,13 @@ def test_append_mean_index_entry_points_validate_before_launch(lib):
     f = 1 << 20  # never dereferenced: validation fails first
     for name, q_align in (("csa2_append_mean_index_score", 16), ("csa2_append_mean_index_score_fp4q", 4)):
         fn = getattr(lib, name)
-        fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp]
+        fn.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
+                       vp]
 
-        def call(latent=f, m=2, pool_w=f, rope=f, w=f, kv=f, ix=f, mc=f, mbase=f, q=f, hw=f, base=f, nvis=f, n_q=4,
-                 width=1 << 16, scores=f, bmax=f):
-            return fn(latent, m, pool_w, rope, w, kv, ix, mc, mbase, q, hw, base, nvis, n_q, width, scores, bmax, None)
+        def call(latent=f, m=2, pool_w=f, per_token=0, rope=f, w=f, kv=f, ix=f, mc=f, mbase=f, q=f, hw=f, base=f,
+                 nvis=f, n_q=4, width=1 << 16, scores=f, bmax=f):
+            return fn(latent, m, pool_w, per_token, rope, w, kv, ix, mc, mbase, q, hw, base, nvis, n_q, width, scores,
+                      bmax, None)
 
         assert call(n_q=0, latent=None, mc=None, q=None) == 0
         assert call(n_q=-1) == -1
@@ -188,3 +193,4 @@ def test_append_mean_index_entry_points_validate_before_launch(lib):
         assert call(ix=f + 4) == -1
         assert call(q=f + q_align // 2) == -1
         assert call(scores=f + 2) == -1
+        assert call(per_token=2) == -1

@@ -177,3 +177,27 @@ def test_fused_decode_1m_b4(c, fp4):
         else:
             r = oracle.index_score(q, k.d.head_w[t:t + 1], sub, np.zeros(1, np.int64), np.array([32], np.int32), 32)
         check_scores(s[t:t + 1, lo:], r)
+
+
+def test_fused_per_token_weights(c):
+    """The fused append with per-token pooling weights ([n_q*2, 512]) equals the separate
+    per-token compress_append + index_score, and its appended bytes equal the oracle's."""
+    nvis, width, m = [1000, 8, 9, 33, 1, 4096], 4096, 2
+    log("append_index per-token weights")
+    k = Case(c, 560, nvis, width, m)
+    w_tok = synth.softplus_weights(np.random.default_rng(561), k.n_q * m)
+    kv, ix = dev(k.kv), dev(k.ix)
+    c.compress_append(bf16(k.ci.latent), m, dev(w_tok), dev(k.cs), bf16(k.ci.w_idx), dev(k.dst), kv, ix)
+    s_ref, b_ref = c.index_score(bf16(k.d.q_idx), dev(k.d.head_w), ix, dev(k.base), dev(k.nvis), width)
+    kv2, ix2 = dev(k.kv), dev(k.ix)
+    s, b = c.append_index_score(bf16(k.ci.latent), m, dev(w_tok), dev(k.cs), bf16(k.ci.w_idx), kv2, ix2,
+                                bf16(k.d.q_idx), dev(k.d.head_w), dev(k.base), dev(k.nvis), width)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kv2), host(kv)) and np.array_equal(host(ix2), host(ix))
+    assert np.array_equal(host(s).view(np.uint32), host(s_ref).view(np.uint32))
+    assert np.array_equal(host(b).view(np.uint32), host(b_ref).view(np.uint32))
+    kv_o, ix_o = oracle.compress_pack(k.ci.latent, m, w_tok, oracle.rope_table(k.pos), k.ci.w_idx)
+    got_kv, got_ix = host(kv2), host(ix2)
+    for t in range(k.n_q):
+        if k.dst[t] >= 0:
+            assert np.array_equal(got_kv[k.dst[t]], kv_o[t]) and np.array_equal(got_ix[k.dst[t]], ix_o[t]), t

@@ -124,9 +124,9 @@ def _oracle_check_query(t, d, ix, base, nvis, n_per_seq, got, M=2048, K=512):
                                np.array([nb], np.int32), nbw)
     check_scores(s_blk_g[t:t + 1], s_blk)
     pool = oracle.pool_from_block_scores(s_blk, nvis[t:t + 1], M=M)
-    diff = check_selection(pool_g[t], pool[0], lambda ids: s_blk[0, ids].astype(np.float64), "hisa pool")
-    if diff:
-        return
+    check_selection(pool_g[t], pool[0], lambda ids: s_blk[0, ids].astype(np.float64), "hisa pool")
+    # stage-wise: the oracle's token-level stage scores the GPU's pool once it has passed its check
+    pool = pool_g[t:t + 1]
     s_c = oracle.index_score(d.q_idx[t:t + 1], d.head_w[t:t + 1], ix, base[t:t + 1], nvis[t:t + 1], 8 * M,
                              pool_blocks=pool)
     check_scores(s_c_g[t:t + 1], s_c)
