@@ -49,6 +49,7 @@ _L.csa2_append_mean_index_score_fp4q.argtypes = _L.csa2_append_mean_index_score.
 _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
 _L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+_L.csa2_block_topk_noalloc.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32]
 _L.csa2_sparse_attn_workspace.restype = _sz
 _L.csa2_sparse_attn.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp, _sz, _vp]
@@ -60,9 +61,11 @@ SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_co
            "csa2_index_score", "csa2_block_topk_workspace", "csa2_block_topk",
            "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8",
            "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q", "csa2_block_mean_pack", "csa2_append_index_score",
-           "csa2_append_index_score_fp4q", "csa2_append_index_score_packq", "csa2_append_mean_index_score", "csa2_append_mean_index_score_fp4q")
+           "csa2_append_index_score_fp4q", "csa2_append_index_score_packq", "csa2_append_mean_index_score",
+           "csa2_append_mean_index_score_fp4q", "csa2_block_topk_noalloc")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 DEFAULT_SCALE = 512 ** -0.5
 SWA_FP8_ROW_BYTES = 584
 ROPE_THETA = 160000.0
@@ -388,6 +391,37 @@ def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool
     _check("csa2_block_topk", _L.csa2_block_topk(
         _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(pool_blocks), 8, M, K,
         _ptr(pool_out), _ptr(topk_out), _ptr(workspace), _bytes(workspace), _stream(stream)))
+    return pool_out, topk_out
+
+
+def block_topk_noalloc(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool_blocks=None,
+                       pool_out=None, topk_out=None, stream=None):
+    """block_topk through the allocation-free entry point (the library's fixed scratch array,
+    NOALLOC_SCRATCH_BYTES per GPU): the outputs must be given, so the call allocates nothing;
+    pool_out None with topk_out given skips the pool, topk_out None is the pool-only mode.
+    Calls that overlap in time on one GPU must not be issued."""
+    if scores is not None:
+        _dev(scores, torch.float32, "scores", (None, None))
+        n_q, width = scores.shape
+    else:
+        _need(block_max, "block_max")
+        _dev(block_max, torch.float32, "block_max", (None, None))
+        n_q, width = block_max.shape[0], 8 * block_max.shape[1]
+    _need(q_nvis, "q_nvis")
+    _dev(q_nvis, torch.int32, "q_nvis", (n_q,))
+    _dev(block_max, torch.float32, "block_max", (n_q, (width + 7) // 8))
+    if pool_blocks is not None:
+        _dev(pool_blocks, torch.int32, "pool_blocks", (n_q, None))
+        M = pool_blocks.shape[1]
+        if width != 8 * M or block_max is not None or pool_out is not None:
+            raise ValueError("candidate mode: scores [n_q, 8 * M], no block_max and no pool output")
+    if pool_out is None and topk_out is None:
+        raise ValueError("give pool_out, topk_out or both")
+    _dev(pool_out, torch.int32, "pool_out", (n_q, M))
+    _dev(topk_out, torch.int32, "topk_out", (n_q, K))
+    _check("csa2_block_topk_noalloc", _L.csa2_block_topk_noalloc(
+        _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(pool_blocks), 8, M, K, _ptr(pool_out),
+        _ptr(topk_out), _stream(stream)))
     return pool_out, topk_out
 
 

@@ -35,6 +35,8 @@
 //               selects straight from the full row instead, with the same exact rules.
 // The histogram region of the workspace must be zero before the first call; every call
 // leaves it zero.
+#include <mutex>
+
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -950,11 +952,21 @@ extern "C" size_t csa2_block_topk_workspace(int32_t n_q, int32_t width, int32_t 
   return a.total > b.total ? a.total : b.total;
 }
 
-extern "C" int csa2_block_topk(const float* scores, const float* block_max, int32_t n_q,
-                               int32_t width, const int32_t* q_nvis, const int32_t* pool_blocks,
-                               int32_t block, int32_t M, int32_t K, int32_t* pool_out,
-                               int32_t* topk_out, void* workspace, size_t ws_bytes, void* stream) {
-  using namespace csa2;
+namespace csa2 {
+namespace {
+
+// Zeroes n 32-bit words (the histogram region of an allocation-free call; a kernel rather
+// than a memset, so the call may be captured into a HIP graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Argument checks of both selection entry points, before anything is launched or looked
+// up; the workspace itself is checked by the caller.  kProceed: arguments valid, work to do.
+constexpr int kProceed = 1;
+int block_topk_check(const float* scores, const float* block_max, int32_t n_q, int32_t width, const int32_t* q_nvis,
+                     const int32_t* pool_blocks, int32_t block, int32_t M, int32_t K, const int32_t* pool_out,
+                     const int32_t* topk_out) {
   if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
   if (block != kBlock || M < 1 || M > kMaxPool || K < 1 || K > kMaxTopK) return CSA2_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
@@ -965,11 +977,22 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   if (cand && (pool_out || block_max || (int64_t)width != 8LL * M)) return CSA2_ERR_INVALID_ARG;
   if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(block_max) |
-       reinterpret_cast<uintptr_t>(topk_out) | reinterpret_cast<uintptr_t>(pool_out) |
-       reinterpret_cast<uintptr_t>(workspace)) & 3)
+       reinterpret_cast<uintptr_t>(topk_out) | reinterpret_cast<uintptr_t>(pool_out)) & 3)
     return CSA2_ERR_INVALID_ARG;
+  if (make_layout(n_q, width, M, cand).G > kMaxG) return CSA2_ERR_UNSUPPORTED;  // rows longer than 2^20 blocks
+  return kProceed;
+}
+
+// The three launches (after block_topk_check), shared by csa2_block_topk (the caller's
+// workspace) and csa2_block_topk_noalloc (the fixed scratch array, whose histogram region is
+// cleared first).
+int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, int32_t width, const int32_t* q_nvis,
+                      const int32_t* pool_blocks, int32_t M, int32_t K, int32_t* pool_out, int32_t* topk_out,
+                      void* workspace, size_t ws_bytes, bool clear_hist, void* stream) {
+  const bool cand = pool_blocks != nullptr;
+  const bool want_topk = topk_out != nullptr;
+  if (reinterpret_cast<uintptr_t>(workspace) & 3) return CSA2_ERR_INVALID_ARG;
   const Layout L = make_layout(n_q, width, M, cand);
-  if (L.G > kMaxG) return CSA2_ERR_UNSUPPORTED;  // rows longer than 2^20 blocks
   if (!workspace || ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
   char* w = (char*)workspace;
   Ws ws;
@@ -985,6 +1008,13 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   const float* bm = block_max ? block_max : ws.bm;
   const bool want_pool = pool_out != nullptr;
   hipStream_t s = (hipStream_t)stream;
+  if (clear_hist) {
+    const int64_t words = (int64_t)n_q * kBins;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                       dim3(256), 0, s, ws.hist, words);
+    const int st = check_launch();
+    if (st != CSA2_OK) return st;
+  }
   const int32_t G1 = (L.G * kSlice + kHSlice - 1) / kHSlice;
   if (cand)
     hipLaunchKernelGGL(topk_hist_kernel<true>, dim3(G1, n_q), dim3(kHThreads), 0, s, scores, block_max, width, q_nvis,
@@ -1010,4 +1040,65 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
     hipLaunchKernelGGL(topk_final_kernel<false>, gf, dim3(kFThreads), 0, s, want_pool, want_topk, scores, bm, width,
                        q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
   return check_launch();
+}
+
+}  // namespace
+}  // namespace csa2
+
+extern "C" int csa2_block_topk(const float* scores, const float* block_max, int32_t n_q,
+                               int32_t width, const int32_t* q_nvis, const int32_t* pool_blocks,
+                               int32_t block, int32_t M, int32_t K, int32_t* pool_out,
+                               int32_t* topk_out, void* workspace, size_t ws_bytes, void* stream) {
+  const int st = csa2::block_topk_check(scores, block_max, n_q, width, q_nvis, pool_blocks, block, M, K, pool_out,
+                                        topk_out);
+  if (st != csa2::kProceed) return st;
+  return csa2::block_topk_launch(scores, block_max, n_q, width, q_nvis, pool_blocks, M, K, pool_out, topk_out,
+                                 workspace, ws_bytes, false, stream);
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// csa2_block_topk for callers that cannot allocate device memory (code under HIP graph capture,
+// serving loops that forbid hipMalloc): its workspace is this fixed array, one copy per device,
+// held until the process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress, once per device, and only that
+// address is passed to kernels.
+
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<uintptr_t> scratch_addr[csa2::kMaxDevices];
+std::mutex scratch_setup;
+
+// The device address of `scratch` on the current device (0 on a HIP error), looked up on the
+// device's first call with that device current.
+uintptr_t scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= csa2::kMaxDevices) return 0;
+  uintptr_t a = scratch_addr[dev].load(std::memory_order_acquire);
+  if (a != 0) return a;
+  std::lock_guard<std::mutex> lock(scratch_setup);
+  a = scratch_addr[dev].load(std::memory_order_relaxed);
+  if (a == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return 0;
+    a = reinterpret_cast<uintptr_t>(ptr);
+    scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  return a;
+}
+}  // namespace
+
+extern "C" int csa2_block_topk_noalloc(const float* scores, const float* block_max, int32_t n_q, int32_t width,
+                                       const int32_t* q_nvis, const int32_t* pool_blocks, int32_t block, int32_t M,
+                                       int32_t K, int32_t* pool_out, int32_t* topk_out, void* stream) {
+  using namespace csa2;
+  // argument errors first (the checks of csa2_block_topk), then the size limit, then set-up
+  const int st = block_topk_check(scores, block_max, n_q, width, q_nvis, pool_blocks, block, M, K, pool_out,
+                                  topk_out);
+  if (st != kProceed) return st;
+  if (csa2_block_topk_workspace(n_q, width, M, K) > (size_t)CSA2_NOALLOC_SCRATCH_BYTES) return CSA2_ERR_SCRATCH;
+  const uintptr_t a = scratch_address();
+  if (a == 0) return CSA2_ERR_HIP;
+  return block_topk_launch(scores, block_max, n_q, width, q_nvis, pool_blocks, M, K, pool_out, topk_out,
+                           reinterpret_cast<void*>(a), CSA2_NOALLOC_SCRATCH_BYTES, true, stream);
 }

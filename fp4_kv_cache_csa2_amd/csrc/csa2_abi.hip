@@ -12,6 +12,7 @@ extern "C" const char* csa2_status_string(int status) {
     case CSA2_ERR_UNSUPPORTED: return "unsupported configuration";
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_HIP: return "HIP runtime error at launch";
+    case CSA2_ERR_SCRATCH: return "problem larger than the fixed scratch array of the allocation-free call";
     default: return "unknown status";
   }
 }

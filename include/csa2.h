@@ -56,7 +56,8 @@ enum {
   CSA2_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer        */
   CSA2_ERR_UNSUPPORTED = -2, /* a method constant outside what the library builds */
   CSA2_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required         */
-  CSA2_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+  CSA2_ERR_HIP = -4,         /* the HIP runtime reported an error at launch        */
+  CSA2_ERR_SCRATCH = -5      /* larger than the fixed scratch array of a _noalloc call */
 };
 
 #define CSA2_ABI_VERSION 2
@@ -247,10 +248,11 @@ int csa2_append_index_score_packq(const uint16_t *latent_bf16, int m, const floa
  *   csa2_index_score candidate mode; pool_out must be NULL.
  *   topk_out [n_q, K]: selected entry ids (relative to the sequence) ascending, -1 pad.
  *   workspace: device scratch of at least csa2_block_topk_workspace(n_q, width, M, K)
- *   bytes, 4-byte aligned.  Its histogram region must be all zero before the first call
- *   (allocate it zero-filled); every call that completes leaves it zero again, so one
- *   buffer can be reused by consecutive calls on the same stream.  Calls that overlap in
- *   time must not share a workspace.
+ *   bytes, 4-byte aligned.  Its histogram region, the first n_q * 16 KiB, must be all zero
+ *   before the call (allocate the buffer zero-filled); every call that completes leaves that
+ *   region zero again, so one buffer can be reused by consecutive calls on the same stream
+ *   with the same or a smaller n_q (a larger n_q needs its larger region zeroed again).
+ *   Calls that overlap in time must not share a workspace.
  *   Errors: INVALID_ARG, UNSUPPORTED (block != 8, M > 2048, K > 512, K < 1, M < 1, rows
  *   longer than 2^20 blocks), WORKSPACE (workspace missing or too small).
  */
@@ -263,6 +265,24 @@ int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, in
                     const int32_t *q_nvis, const int32_t *pool_blocks, int32_t block,
                     int32_t M, int32_t K, int32_t *pool_out, int32_t *topk_out,
                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * csa2_block_topk_noalloc -- csa2_block_topk that allocates nothing and takes no workspace,
+ *   for callers that cannot allocate device memory: code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid hipMalloc.  The workspace is a fixed device array
+ *   of CSA2_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the process
+ *   ends); each call first clears its histogram region with a kernel (no memset), so the
+ *   call may be captured.  Every call on one GPU shares that GPU's array: calls that overlap
+ *   in time on one GPU (other streams, other host threads) race and must not be issued.
+ *   Arguments, modes, results and errors are those of csa2_block_topk without workspace and
+ *   ws_bytes, plus CSA2_ERR_SCRATCH when csa2_block_topk_workspace(n_q, width, M, K)
+ *   exceeds CSA2_NOALLOC_SCRATCH_BYTES (e.g. 4 rows of 2^20 entries fit; 4096 prefill rows
+ *   of 34816 do not), and CSA2_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20)
+int csa2_block_topk_noalloc(const float *scores, const float *block_max, int32_t n_q, int32_t width,
+                            const int32_t *q_nvis, const int32_t *pool_blocks, int32_t block, int32_t M,
+                            int32_t K, int32_t *pool_out, int32_t *topk_out, void *stream);
 
 /*
  * csa2_block_mean_pack -- HISA's block-mean indexer keys.

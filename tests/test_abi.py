@@ -194,3 +194,20 @@ def test_append_mean_index_entry_points_validate_before_launch(lib):
         assert call(q=f + q_align // 2) == -1
         assert call(scores=f + 2) == -1
         assert call(per_token=2) == -1
+
+
+def test_block_topk_noalloc_validates_before_launch(lib):
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    fn = lib.csa2_block_topk_noalloc
+    fn.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert fn(fake, None, -1, 100, fake, None, 8, 2048, 512, None, fake, None) == -1
+    assert fn(fake, None, 1, 100, fake, None, 4, 2048, 512, None, fake, None) == -2
+    assert fn(fake, None, 1, 100, fake, None, 8, 2048, 513, None, fake, None) == -2
+    assert fn(None, None, 1, 100, fake, None, 8, 2048, 512, None, fake, None) == -1
+    assert fn(fake, None, 0, 100, fake, None, 8, 2048, 512, None, fake, None) == 0
+    # larger than the fixed array (4096 prefill rows): rejected on the host, nothing launched
+    assert fn(fake, None, 4096, 34816, fake, None, 8, 2048, 512, None, fake, None) == -5
+    lib.csa2_status_string.restype = ctypes.c_char_p
+    assert b"scratch" in lib.csa2_status_string(-5)
+
