@@ -19,8 +19,14 @@ token's layers run inside one graph; `ms_per_step_one_step_graphs` is the same K
 one graph launch per step; `stages_us` times each stage of the step alone and
 `replaced_stages_us` the separate append and scan launches the fused stage replaces;
 `roofline` prices the dominant kernel (the fused append + scan) at 68 algorithmic bytes
-per scored entry against 8 TB/s, timed with HIP events on the launch stream; `cpu_baseline`
-times the oracle (plain C, one host thread) on the same per-query work.  `roofline.traffic`
+per scored entry against 8 TB/s, timed with HIP events on the launch stream;
+`roofline_step` prices the whole step (scan, selection, attention: 68 B per scored entry plus
+each query's attention bytes) and `roofline_step_128k` the 128K batch-16 step (Full + Reindex
++ 3 Reuse) the same way; `step_us_p10_p50_p90` is the spread of single graph replays;
+`ms_per_step_5_copies` repeats the step over 5 batch copies (a cache control);
+`peaks_measured` holds a 1 GiB device copy and a bf16 GEMM beside the published peaks;
+`cpu_baseline` times the oracle (plain C) on the same per-query work, one instance per host
+thread, with the one-thread figure, the thread count and the CPU model.  `roofline.traffic`
 is the HBM bytes per launch of that kernel from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
 (each scaled by what the counter reads for a torch copy of known size), read from
 profiles/append_index_traffic.json and reported only while the kernel's sources still hash
@@ -53,6 +59,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--tokens", type=int, default=1048576, help="tokens per sequence")
     p.add_argument("--no-secondary", action="store_true", help="skip the other seeded workloads")
+    p.add_argument("--no-peaks", action="store_true", help="skip the copy / GEMM peak measurements")
+    p.add_argument("--no-control", action="store_true", help="skip the 5-copy cache control")
     p.add_argument("--calibration-copy-mib", type=int, default=0,
                    help="run one device copy of this many MiB before timing (counter calibration)")
     return p.parse_args()
@@ -107,25 +115,101 @@ def make_batch(csa2, torch, copy_id, n_seq, tokens, m, chunk_tokens=1 << 19, ext
                 q=q.contiguous(), swa=swa.contiguous(), layers=layers)
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_threads():
+    """Host threads the all-core leg may use: the process's CPU affinity, capped by the
+    thread budget the environment sets (OMP_NUM_THREADS) when there is one."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
 def cpu_baseline(n_entries, n_q):
-    """The oracle as it stands, one host thread, on n_q full 1M-context decode queries."""
+    """The oracle as it stands (plain C behind ctypes, which releases the interpreter lock
+    during each call), on full 1M-context decode queries: each query is the whole path
+    (compress of the newest entry, scoring of every entry, block/Top-K selection, attention).
+    Timed on one host thread for n_q queries, then with one oracle instance per host thread
+    on independent queries (two per thread)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     from fp4_kv_cache_csa2_amd import synth
     kv, ix = synth.random_caches(99, n_entries)
     ci = synth.compress_inputs(98, 1, 2)
     d = synth.query_inputs(97, 1)
     cs = oracle.rope_table(np.array([2 * (n_entries - 1)], np.int64))
-    t0 = time.perf_counter()
-    for _ in range(n_q):
+
+    def one_query(_=None):
         oracle.compress_pack(ci.latent, 2, ci.pool_w, cs, ci.w_idx)
         s = oracle.index_score(d.q_idx, d.head_w, ix, [0], [n_entries], n_entries)
         _, tk = oracle.block_topk(s, [n_entries])
         oracle.sparse_attn(d.q, kv, [0], tk, d.swa, d.swa_start, d.swa_len)
-    dt = time.perf_counter() - t0
-    return {"value": n_q / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_q} decode queries x {n_entries} entries (full per-query path: compress of the "
-                      f"newest entry, index over every entry, block/Top-K select, attention), "
-                      f"{dt:.1f} s on one host thread"}
+
+    t0 = time.perf_counter()
+    for _ in range(n_q):
+        one_query()
+    dt1 = time.perf_counter() - t0
+    threads = _host_threads()
+    n_all = 2 * threads
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(one_query, range(n_all)))
+        dt_all = time.perf_counter() - t0
+    return {"value": round(n_all / dt_all, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_all} decode queries x {n_entries} entries, one oracle instance per host thread "
+                      f"({threads} threads, {dt_all:.1f} s wall); each query the full path: compress of the newest "
+                      f"entry, index over every entry, block/Top-K selection, attention",
+            "single_thread": {"value": round(n_q / dt1, 3), "unit": "queries/s", "cores": 1,
+                              "sample": f"{n_q} queries, {dt1:.1f} s on one host thread"},
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def measure_peaks(torch):
+    """What this GPU reaches on plain library work, beside the published peaks: a device copy
+    of 1 GiB (read + write bytes per second) and a bf16 8192^3 matrix product (hipBLASLt
+    through torch), each the median of 5 timed repetitions with HIP events."""
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    nb = 1 << 30
+    src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * nb / t_copy / 1e9, 1), "copy_bytes": nb,
+            "bf16_gemm_TFLOPs": round(2 * n ** 3 / t_mm / 1e12, 1), "gemm_shape": [n, n, n],
+            "published": {"hbm_GBps": HBM_PEAK_GBS, "bf16_dense_TFLOPs": 2500.0}}
 
 
 class Decode1M:
@@ -204,6 +288,15 @@ class Decode1M:
                     torch.bfloat16).contiguous()
             torch.cuda.synchronize()
 
+    def add_copies(self, total):
+        """More batch copies (the same recipe, further seeds) up to `total`, for the cache control."""
+        torch, csa2 = self.torch, self.csa2
+        while len(self.copies) < total:
+            c = make_batch(csa2, torch, len(self.copies), self.n_seq, self.tokens, self.m, extra_layers=self.extra)
+            self.copies.append(c)
+            self.cs_new.append(c["cs_last"].expand(self.n_seq, 64).contiguous())
+        torch.cuda.synchronize()
+
     def run_stage(self, ci, st):
         """One stage of the step for batch copy ci, on torch's current stream."""
         c, csa2, n = self.copies[ci], self.csa2, self.n
@@ -258,6 +351,24 @@ class Decode1M:
                              out=self.out, lse=self.lse, workspace=self.ws_att)
 
 
+def attn_bytes_per_query(K=512, swa=128):
+    """Algorithmic bytes of one query's attention: the K gathered 288-byte entries, the window
+    rows (1 KiB of bf16 each), the query (64 x 512 bf16) and the output (64 x 512 fp32)."""
+    return K * 288 + swa * 1024 + 64 * 512 * 2 + 64 * 512 * 4
+
+
+def step_bytes(n_seq, n_entries, reindex_pool=0, attn_layers=1):
+    """Algorithmic bytes of a decode step: the indexer scan (68 B per visible entry per query),
+    a Reindex layer's pool (68 B per candidate), and each attention layer."""
+    return n_seq * (n_entries * 68 + reindex_pool * 68 + attn_layers * attn_bytes_per_query())
+
+
+def roofline(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": int(nbytes), "us_per_step": round(us, 2)}
+
+
 FUSED = -1  # the stage that appends and scores in one launch (csa2_append_index_score)
 FUSED_HISA = -2  # HISA's append + newest block mean + scan of the means (csa2_append_mean_index_score)
 STAGE_NAMES = {FUSED: "append_index_score", FUSED_HISA: "append_mean_index_score", 0: "compress_newest",
@@ -290,11 +401,16 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
         graphs[i % NCOPY].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    res = {"queries_per_s": round(n_seq * steps / wall, 1), "us_per_step": round(wall * 1e6 / steps, 2),
+    us = wall * 1e6 / steps
+    res = {"queries_per_s": round(n_seq * steps / wall, 1), "us_per_step": round(us, 2),
            "sequences": n_seq, "tokens_per_sequence": tokens, "compress_ratio": m, "entries_per_sequence": wl.n,
            "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else ""),
            "window": "FP8 rings (append + attend)" if fp8_window else "bf16",
            "indexer_query": "MXFP4 (packed inside the fused launch)" if fp4q else "bf16"}
+    if not hisa and not fp8_window:
+        # the whole step against the HBM roofline: Full scan, Reindex pool, every attention layer
+        nbytes = step_bytes(n_seq, wl.n, reindex_pool=8 * wl.M if extra_layers else 0, attn_layers=1 + extra_layers)
+        res["roofline_step"] = roofline(nbytes, us)
     if hisa:
         # recall of the exact Top-K (the Full layer's, over every entry) by HISA's Top-K, on the
         # last replayed copy's inputs
@@ -505,6 +621,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    peaks = None if args.no_peaks else measure_peaks(torch)
     wl = Decode1M(torch, csa2, args.tokens)
     n_seq, m, tokens, n, K, M = wl.n_seq, wl.m, wl.tokens, wl.n, wl.K, wl.M
     step = wl.step_stages  # the fused append + scan, selection, attention
@@ -588,6 +705,36 @@ def main():
         b.record()
         torch.cuda.synchronize()
         st_us[st] = a.elapsed_time(b) * 1e3 / (stage_rounds * reps)
+    # spread of the step time: HIP events around single replays of the multi-step graph
+    per_step = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        multi_graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per_step.append(a.elapsed_time(b) * 1e3 / NCOPY)
+    p10, p50, p90 = (float(np.percentile(per_step, q)) for q in (10, 50, 90))
+    # cache control: the same step rotating over 5 batch copies (186 MB of caches each), so
+    # any reuse of the 256 MB Infinity Cache between steps is further away; an equal time per
+    # step means the 3-copy figure is not served from it
+    ms_5 = None
+    if not args.no_control:
+        wl.add_copies(5)
+        g5 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g5, stream=cap):
+            for ci in range(5):
+                for st in step:
+                    run_stage(ci, st)
+        g5.replay()
+        torch.cuda.synchronize()
+        reps5 = max(1, args.steps // 5)
+        t0 = time.perf_counter()
+        for _ in range(reps5):
+            g5.replay()
+        torch.cuda.synchronize()
+        ms_5 = (time.perf_counter() - t0) * 1e3 / (5 * reps5)
+        del g5
     # the dominant kernel: the fused append + scan; its algorithmic bytes are the scan's
     idx_us = st_us[FUSED]
     idx_bytes = n_seq * n * 68
@@ -609,6 +756,11 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": idx_bytes},
+        # the whole step (scan + selection + attention) against the same roofline
+        "roofline_step": roofline(step_bytes(n_seq, n), ms_per_step * 1e3),
+        "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+        "ms_per_step_5_copies": None if ms_5 is None else round(ms_5, 4),
+        "peaks_measured": peaks,
     }
     if not args.no_secondary:
         # the other seeded workloads, each in its own graphs after the timed region above
@@ -626,6 +778,8 @@ def main():
             "prefill_chunk4096_hist65536_m2": time_prefill(torch, csa2),
         }
         line["secondary"] = sec
+        # the 128K batch-16 step (Full + Reindex + 3 Reuse) is the metric's other context
+        line["roofline_step_128k"] = sec["decode_128k_b16_m1"]["roofline_step"]
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(n, n_seq)
