@@ -6,23 +6,31 @@
 // over the selected main-KV entries and the layer's SWA KV).  FP4 is storage only: the
 // entries are dequantised before the matmuls ([ZB] §2.4.4).
 //
-// Design.  A workgroup of 4 waves serves one query; wave w owns heads 16w .. 16w+15.
-// Keys are processed in chunks of 64: the selected entries (gathered 288-byte rows,
-// prefetched one chunk ahead) and the window rows are decoded once into LDS as f16, row
-// major (exact: an E2M1 code times an E4M3 scale has at most 6 significant bits; bf16
-// window values are exact in f16's normal range).  QK^T reads the key rows directly; PV
-// takes its key-major operand from the same tile with transposing LDS reads
-// (ds_read_b64_tr_b16), so no second copy is stored.  Both matmuls run on
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation; the softmax is online across chunks in
-// fp32.  For small batches the key chunks of a query are split across workgroups and a
-// merge kernel combines the partial (o, m, l) exactly like flash-decoding.
+// Design.  A workgroup of 4 waves serves one query, 16 of its 64 heads and a run of its key
+// chunks (64 keys each: the selected entries, gathered 288-byte rows, then the window rows);
+// the chunks' rows are fetched a chunk ahead into registers and decoded once into one
+// row-major bf16 LDS tile.  For small batches a query's chunks are split across workgroups
+// (one chunk each at batch 4: the chain of dependent loads per workgroup stays short), each
+// writing an unnormalised partial (o, m, l) that a merge kernel combines exactly like
+// flash-decoding; large batches run every chunk of a head group in one workgroup.  Every key value is exact in bf16: an E2M1 code times an E4M3 scale has at
+// most 6 significant bits, an FP8 window value 4, a bf16 window value is one; the query is
+// bf16 as given.  So QK^T has exact products for inputs of any magnitude, with fp32 sums.
+//   QK^T  wave w scores keys 16w .. 16w + 15 of the chunk for the 16 heads
+//         (v_mfma_f32_16x16x32_bf16, the query in registers as 16 A fragments).
+//   softmax  online across chunks in fp32; the chunk's per-head maximum and the exponentials'
+//         row sums are combined across the 4 waves through LDS in a fixed order, so every wave
+//         holds the same running maximum and sum.
+//   PV    wave w accumulates output dims 128w .. 128w + 127 over the chunk's 64 keys.  The
+//         probabilities go to LDS as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), which
+//         represent p to about 2^-17 relative, and each part is one MFMA; the key-major value
+//         operand comes from the same tile by transposing LDS reads (ds_read_b64_tr_b16).
+// The grid is ordered so that the workgroups of a query land on one XCD (workgroups are
+// dealt to the 8 XCDs round-robin): its head groups gather the same keys, which the XCD's L2
+// then serves, and its splits' partials stay in that L2 for the merge.
 //
 // The window rows come either as bf16 rows or as 584-byte FP8 window rows (the window KV
 // kept in FP8, [ZB] §2.4.4; DeepSeek-V4's FP8 KV entry, [ZB] §3.1 and [DF] §4.6), read
-// consecutively or from per-sequence ring buffers.  An FP8 row decodes exactly into f16
-// (an E4M3 value times a power-of-two scale has 4 significant bits) as long as the
-// products stay in f16's range (groups with amax >= 2^-10 or so; smaller groups lose their
-// smallest values to f16 underflow).
+// consecutively or from per-sequence ring buffers.
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -30,38 +38,48 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 64;
-constexpr int kKStride = kD + 8;        // f16 elements per key row in LDS (1040 B: 8-B aligned rows)
-constexpr int kPStride = kChunk + 8;
+constexpr int kHeadGroup = 16;                   // heads per workgroup
+constexpr int kGroups = kHeads / kHeadGroup;     // workgroups per query
+constexpr int kChunk = 64;                       // keys per chunk
+constexpr int kKStride = kD + 8;                 // bf16 per key row in LDS (1040 B: 8-B aligned rows)
+constexpr int kPStride = kChunk + 8;             // bf16 per probability row
+constexpr int kXcds = 8;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));  // 16 B at an 8-B boundary
 
-
 struct __attribute__((aligned(16))) AttnShared {
-  _Float16 k[kChunk * kKStride] __attribute__((aligned(16)));  // decoded keys, row-major [key][dim]
-  _Float16 p[kWaves * 16 * kPStride] __attribute__((aligned(16)));  // per-wave probabilities [head][key]
+  __bf16 k[kChunk * kKStride] __attribute__((aligned(16)));   // decoded keys, row-major [key][dim]
+  __bf16 p[2][kHeadGroup * kPStride] __attribute__((aligned(16)));  // probabilities, hi and lo parts
+  float cmax[kWaves][kHeadGroup];  // per wave: the chunk's maximum logit of each head
+  float csum[kWaves][kHeadGroup];  // per wave: the chunk's exponential sum of each head
   int32_t valid[kChunk];
 };
 
-// Raw bytes of one key slot for one thread (a quarter of a key), prefetched a chunk ahead:
-// a selected entry's 64 payload bytes and 8 E4M3 scale bytes, or a window row's quarter
-// (256 bytes of bf16, or 144 bytes of an FP8 row: 112 code bytes, 32 bf16 bytes), with the
-// FP8 row's 8-byte scale word.  The scale words of both kinds sit in sw, so the two loads
-// that fill it write one place (with different array slots the compiler merged them into
-// a store at a computed index, which put the array in scratch memory).
+// Raw bytes of one key slot for one thread (a quarter of a key), fetched a chunk ahead: a
+// selected entry's 64 payload bytes and 8 E4M3 scale bytes, or a window row's quarter (256
+// bytes of bf16, or 144 bytes of an FP8 row: 112 code bytes, 32 bf16 bytes), with the FP8
+// row's 8-byte scale word.  The scale words of both kinds sit in sw, so the loads that fill it
+// write one place (different array slots made the compiler move the array to scratch).
 struct KeyRaw {
   uint4 d[16];
   uint2 sw;
-  int kind;       // 0 empty, 1 selected entry, 2 window row
+  int kind;  // 0 empty, 1 selected entry, 2 window row
 };
 
-// Gather and decode of one query's keys: thread (kk, qq) of a 256-thread workgroup handles
-// quarter qq (dims 128 qq .. 128 qq + 127) of key slot kk of every 64-key chunk.  Keys 0 .. K-1 are the selected entries
+__device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
+  // both values are exact in bf16 here (at most 8 significant bits), so the rounding of the
+  // conversion never acts
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Gather and decode of one query's keys: thread (kk, qq) handles quarter qq (dims 128 qq ..
+// 128 qq + 127) of key slot kk of every 64-key chunk.  Keys 0 .. K-1 are the selected entries
 // (topk ids relative to the sequence's first cache row), keys K .. K + nswa - 1 the window
-// rows.  Window rows are bf16 rows, or 584-byte FP8 rows (kFp8Win), read consecutively or
-// from per-sequence rings.
+// rows: bf16 rows, or 584-byte FP8 rows (kFp8Win), read consecutively or from per-sequence
+// rings.
 template <bool kFp8Win>
 struct KeyStager {
   const uint8_t* kv_cache;
@@ -85,14 +103,14 @@ struct KeyStager {
       if (woff < 0) woff += swa_ring;
       wseg = swa_start - woff;
     }
-    // wave qq stages quarter qq of all 64 keys: consecutive lanes write consecutive key
-    // rows, which start 4 banks apart, so the 16-byte LDS stores of a wave do not conflict
+    // wave qq stages quarter qq of all 64 keys: consecutive lanes write consecutive key rows,
+    // which start 4 banks apart, so the 16-byte LDS stores of a wave do not conflict
     kk = tid & 63;
     qq = tid >> 6;
   }
 
-  // the selected-entry id of this thread's key slot in chunk c (a window row or past the
-  // end: -1), read straight into a register so the key loads need no barrier
+  // the selected-entry id of this thread's key slot in chunk c (a window row or past the end:
+  // -1), read straight into a register so the key loads need no barrier
   __device__ __forceinline__ int32_t load_id(int c) const {
     const int x = c * kChunk + kk;
     return x < K ? topk_row[x] : -1;
@@ -144,41 +162,35 @@ struct KeyStager {
     }
   }
 
-  // decode to f16 (exact) and store the key quarter row-major in LDS
+  // decode to bf16 (exact) and store the key quarter row-major in LDS
   __device__ __forceinline__ void stage(const KeyRaw& r, AttnShared& sh) const {
-    _Float16* krow = sh.k + kk * kKStride + 128 * qq;
+    __bf16* krow = sh.k + kk * kKStride + 128 * qq;
     if (r.kind == 1) {
-      // v_cvt_scalef32_pk_f16_fp4 applies only a power-of-two scale, so the codes convert
-      // at scale 1 and a packed f16 multiply applies the E4M3 scale (exact: at most 6
-      // significant bits, inside f16's normal range)
-      // the 8 E4M3 scales of this quarter as f16 (every E4M3 value is exact in f16)
-      f16x2 sc2[4];
-      sc2[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.x, 1.0f, false);
-      sc2[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.x, 1.0f, true);
-      sc2[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.y, 1.0f, false);
-      sc2[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sw.y, 1.0f, true);
+      // the 8 E4M3 scales of this quarter: the codes convert at scale 1 (v_cvt_scalef32 applies
+      // only a power-of-two scale) and each value is multiplied by its group's scale in fp32
+      const uint32_t sw[2] = {r.sw.x, r.sw.y};
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const uint32_t wd[4] = {r.d[v].x, r.d[v].y, r.d[v].z, r.d[v].w};
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
           const int grp = 2 * v + (q4 >> 1);  // local group of 16 dims
-          const _Float16 S = sc2[grp >> 1][grp & 1];
-          const f16x2 S2 = {S, S};
-          const f16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 0) * S2;
-          const f16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 1) * S2;
-          const f16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 2) * S2;
-          const f16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q4], 1.0f, 3) * S2;
-          const f16x8 pk = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-          *reinterpret_cast<f16x8*>(krow + 32 * v + 8 * q4) = pk;
+          const float S = e4m3_value((sw[grp >> 2] >> (8 * (grp & 3))) & 255u);
+          const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q4], 1.0f, 0);
+          const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q4], 1.0f, 1);
+          const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q4], 1.0f, 2);
+          const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q4], 1.0f, 3);
+          *reinterpret_cast<uint4*>(krow + 32 * v + 8 * q4) =
+              make_uint4(bf16x2_of(f0[0] * S, f0[1] * S), bf16x2_of(f1[0] * S, f1[1] * S), bf16x2_of(f2[0] * S, f2[1] * S),
+                         bf16x2_of(f3[0] * S, f3[1] * S));
         }
       }
     } else if (r.kind == 2) {
       if constexpr (kFp8Win) {
         // this thread decodes NoPE dims 112 qq .. 112 qq + 111 (codes at the same byte
-        // offsets) and RoPE dims 448 + 16 qq .. + 15 (bf16 at bytes 448 + 32 qq)
+        // offsets) and RoPE dims 448 + 16 qq .. + 15 (bf16 at bytes 448 + 32 qq, copied)
         const uint64_t scb = (uint64_t)r.sw.x | ((uint64_t)r.sw.y << 32);
-        _Float16* kq = sh.k + kk * kKStride;
+        __bf16* kq = sh.k + kk * kKStride;
 #pragma unroll
         for (int j = 0; j < 7; j++) {
           const uint4 c4 = r.d[j];
@@ -187,47 +199,25 @@ struct KeyStager {
           for (int h = 0; h < 2; h++) {
             const int grp = (112 * qq + 16 * j + 8 * h) >> 6;  // scale group of these 8 dims
             const uint32_t code = (uint32_t)(scb >> (8 * grp)) & 255u;
-            const _Float16 X = (_Float16)__builtin_ldexpf(1.0f, (int)code - 127);
-            const f16x2 X2 = {X, X};
-            const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, false) * X2;
-            const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h], 1.0f, true) * X2;
-            const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, false) * X2;
-            const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[2 * h + 1], 1.0f, true) * X2;
-            const f16x8 pk = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-            *reinterpret_cast<f16x8*>(kq + 112 * qq + 16 * j + 8 * h) = pk;
+            const float X = __builtin_ldexpf(1.0f, (int)code - 127);  // a power of two: exact
+            const f32x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[2 * h], 1.0f, false);
+            const f32x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[2 * h], 1.0f, true);
+            const f32x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[2 * h + 1], 1.0f, false);
+            const f32x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[2 * h + 1], 1.0f, true);
+            *reinterpret_cast<uint4*>(kq + 112 * qq + 16 * j + 8 * h) =
+                make_uint4(bf16x2_of(a0[0] * X, a0[1] * X), bf16x2_of(a1[0] * X, a1[1] * X),
+                           bf16x2_of(a2[0] * X, a2[1] * X), bf16x2_of(a3[0] * X, a3[1] * X));
           }
         }
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-          const uint4 u4 = r.d[7 + j];
-          const uint32_t u[4] = {u4.x, u4.y, u4.z, u4.w};
-          f16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            pk[2 * e] = (_Float16)bf16_bits_to_f32(u[e] & 0xFFFFu);
-            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(u[e] >> 16);
-          }
-          *reinterpret_cast<f16x8*>(kq + kDNope + 16 * qq + 8 * j) = pk;
-        }
+        for (int j = 0; j < 2; j++) *reinterpret_cast<uint4*>(kq + kDNope + 16 * qq + 8 * j) = r.d[7 + j];
       } else {
 #pragma unroll
-        for (int v = 0; v < 16; v++) {
-          const uint32_t wd[4] = {r.d[v].x, r.d[v].y, r.d[v].z, r.d[v].w};
-          f16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            pk[2 * e] = (_Float16)bf16_bits_to_f32(wd[e] & 0xFFFFu);
-            pk[2 * e + 1] = (_Float16)bf16_bits_to_f32(wd[e] >> 16);
-          }
-          *reinterpret_cast<f16x8*>(krow + 8 * v) = pk;
-        }
+        for (int v = 0; v < 16; v++) *reinterpret_cast<uint4*>(krow + 8 * v) = r.d[v];
       }
     } else {
-      f16x8 z;
 #pragma unroll
-      for (int e = 0; e < 8; e++) z[e] = (_Float16)0.0f;
-#pragma unroll
-      for (int v = 0; v < 16; v++) *reinterpret_cast<f16x8*>(krow + 8 * v) = z;
+      for (int v = 0; v < 16; v++) *reinterpret_cast<uint4*>(krow + 8 * v) = make_uint4(0u, 0u, 0u, 0u);
     }
     if (qq == 0) sh.valid[kk] = r.kind != 0 ? 1 : 0;
   }
@@ -259,50 +249,44 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_cache,
     const int64_t* __restrict__ q_base, const int32_t* __restrict__ topk, int32_t K,
     const void* __restrict__ swa_v, int64_t swa_ring, const int64_t* __restrict__ swa_start,
-    const int32_t* __restrict__ swa_len, float scale, int32_t n_chunks, int32_t chunks_per_split,
+    const int32_t* __restrict__ swa_len, float scale, int32_t n_q, int32_t n_chunks, int32_t chunks_per_split,
     int32_t n_splits, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
   __shared__ AttnShared sh;
-  const int t = blockIdx.y, split = blockIdx.x;
+  // workgroup -> (query, head group, split): x deals a query's 4 head groups to one XCD, and y
+  // (the split) keeps that XCD because gridDim.x is a multiple of 8
+  const int L = blockIdx.x;
+  const int s = L / kXcds;
+  const int t = (s / kGroups) * kXcds + L % kXcds, hg = s % kGroups;
+  const int split = blockIdx.y;
+  if (t >= n_q) return;
+  const int c_begin = split * chunks_per_split;
+  const int c_end = min(c_begin + chunks_per_split, n_chunks);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
-  const int c_begin = split * chunks_per_split;
-  const int c_end = min(c_begin + chunks_per_split, n_chunks);
-  KeyStager<kFp8Win> ks(kv_cache, topk + (int64_t)t * K, K, swa_v, swa_ring, q_base[t], swa_start[t], swa_len[t],
-                         tid);
+  const int h0 = kHeadGroup * hg;  // first head of the group
+  KeyStager<kFp8Win> ks(kv_cache, topk + (int64_t)t * K, K, swa_v, swa_ring, q_base[t], swa_start[t], swa_len[t], tid);
 
-  // Loads go out in dependency order so that their round trips overlap: this thread's
-  // entry ids of the first two chunks, the query, then the first chunk's key rows (which
-  // wait only for the first id), and the query is converted after the key loads are out.
+  // Loads go out in dependency order so that their round trips overlap: this thread's entry
+  // ids of the first two chunks, the query, then the first chunk's key rows.
   int32_t id_next = c_begin < c_end ? ks.load_id(c_begin) : -1;
   int32_t id_after = c_begin + 1 < c_end ? ks.load_id(c_begin + 1) : -1;
   __builtin_amdgcn_sched_barrier(0);
-  // query fragments: head 16w + i, dims 32s + 8g .. +7, as f16 (exact in the normal range)
-  uint4 qraw[16];
+  // query fragments (A of QK^T): head h0 + i, dims 32s + 8g .. +7, bf16 as given
+  bf16x8 qa[16];
   {
-    const uint16_t* qh = q + ((int64_t)t * kHeads + 16 * w + i) * kD + 8 * g;
+    const uint16_t* qh = q + ((int64_t)t * kHeads + h0 + i) * kD + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 16; s++) qraw[s] = *reinterpret_cast<const uint4*>(qh + 32 * s);
+    for (int sd = 0; sd < 16; sd++) qa[sd] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qh + 32 * sd));
   }
   __builtin_amdgcn_sched_barrier(0);
   KeyRaw raw;
   if (c_begin < c_end) ks.fetch(c_begin, id_next, raw);
-  __builtin_amdgcn_sched_barrier(0);
-  f16x8 qa[16];
-#pragma unroll
-  for (int s = 0; s < 16; s++) {
-    const uint32_t wd[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      qa[s][2 * v] = (_Float16)bf16_bits_to_f32(wd[v] & 0xFFFFu);
-      qa[s][2 * v + 1] = (_Float16)bf16_bits_to_f32(wd[v] >> 16);
-    }
-  }
 
-  f32x4 o[32];
+  f32x4 o[8];  // output dims 128w + 16dt + i, heads 4g + r
 #pragma unroll
-  for (int d = 0; d < 32; d++) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < 8; d++) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[4], l_run[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
@@ -313,149 +297,128 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   for (int c = c_begin; c < c_end; c++) {
     __syncthreads();  // the previous chunk's LDS reads are done
     ks.stage(raw, sh);
-    if (c + 1 < c_end) {  // next chunk's gather overlaps this chunk's math; its id was loaded a chunk ago
+    if (c + 1 < c_end) {  // the next chunk's gather overlaps this chunk's math
       ks.fetch(c + 1, id_after, raw);
       id_after = c + 2 < c_end ? ks.load_id(c + 2) : -1;
     }
     __syncthreads();
 
-    // ---- S = Q K^T for 4 tiles of 16 keys
-    f32x4 sacc[4];
+    // ---- S = Q K^T for keys 16w .. 16w + 15 of the chunk (lane: heads 4g + r, key 16w + i)
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // groups of 4 dim steps: the group's 16 B fragments are read before its 16 MFMAs, so the
-    // reads overlap one another instead of each MFMA waiting for its own LDS round trip
+    for (int s0 = 0; s0 < 16; s0 += 8) {
+      bf16x8 kb[8];
 #pragma unroll
-    for (int s0 = 0; s0 < 16; s0 += 4) {
-      f16x8 kb[4][4];
-#pragma unroll
-      for (int s = 0; s < 4; s++) {
-#pragma unroll
-        for (int kt = 0; kt < 4; kt++)
-          kb[s][kt] = *reinterpret_cast<const f16x8*>(sh.k + (16 * kt + i) * kKStride + 32 * (s0 + s) + 8 * g);
-      }
+      for (int sd = 0; sd < 8; sd++)
+        kb[sd] = *reinterpret_cast<const bf16x8*>(sh.k + (16 * w + i) * kKStride + 32 * (s0 + sd) + 8 * g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-#pragma unroll
-        for (int kt = 0; kt < 4; kt++)
-          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s0 + s], kb[s][kt], sacc[kt], 0, 0, 0);
-      }
+      for (int sd = 0; sd < 8; sd++) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s0 + sd], kb[sd], sacc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- online softmax over this chunk; lane holds rows (heads) 4g + r, column (key) 16kt + i
-    float pv[4][4];
-    float cmax[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) cmax[r] = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
-      const bool ok = sh.valid[16 * kt + i] != 0;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        pv[kt][r] = ok ? sacc[kt][r] * scale : -__builtin_inff();
-        cmax[r] = __builtin_fmaxf(cmax[r], pv[kt][r]);
-      }
-    }
-    float alpha[4];
+    // ---- the chunk's maximum per head across the 4 waves
+    const bool ok = sh.valid[16 * w + i] != 0;
+    float lg[4], cm[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const float mn = __builtin_fmaxf(m_run[r], row16_max(cmax[r]));
-      alpha[r] = (mn == -__builtin_inff()) ? 1.0f : __expf(m_run[r] - mn);
-      float rs = 0.0f;
+      lg[r] = ok ? sacc[r] * scale : -__builtin_inff();
+      cm[r] = row16_max(lg[r]);
+    }
+    if (i == 0) {
 #pragma unroll
-      for (int kt = 0; kt < 4; kt++) {
-        const float p = (pv[kt][r] == -__builtin_inff()) ? 0.0f : __expf(pv[kt][r] - mn);
-        pv[kt][r] = p;
-        rs += p;
-      }
-      l_run[r] = l_run[r] * alpha[r] + row16_sum(rs);
-      m_run[r] = mn;
+      for (int r = 0; r < 4; r++) sh.cmax[w][4 * g + r] = cm[r];
+    }
+    __syncthreads();
+    float alpha[4], mn[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int h = 4 * g + r;
+      const float cmx = __builtin_fmaxf(__builtin_fmaxf(sh.cmax[0][h], sh.cmax[1][h]),
+                                        __builtin_fmaxf(sh.cmax[2][h], sh.cmax[3][h]));
+      mn[r] = __builtin_fmaxf(m_run[r], cmx);
+      alpha[r] = (mn[r] == -__builtin_inff()) ? 1.0f : __expf(m_run[r] - mn[r]);
+    }
+    // ---- probabilities of this wave's 16 keys, as bf16 hi + lo parts, and their row sums
+    float ps[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float p = (lg[r] == -__builtin_inff()) ? 0.0f : __expf(lg[r] - mn[r]);
+      const __bf16 hi = (__bf16)p;
+      const __bf16 lo = (__bf16)(p - (float)hi);
+      sh.p[0][(4 * g + r) * kPStride + 16 * w + i] = hi;
+      sh.p[1][(4 * g + r) * kPStride + 16 * w + i] = lo;
+      ps[r] = row16_sum(p);
+    }
+    if (i == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) sh.csum[w][4 * g + r] = ps[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int h = 4 * g + r;
+      l_run[r] = l_run[r] * alpha[r] + (((sh.csum[0][h] + sh.csum[1][h]) + sh.csum[2][h]) + sh.csum[3][h]);
+      m_run[r] = mn[r];
     }
     // rescale O only when some head's running maximum moved (later chunks rarely move it)
     if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f || alpha[2] != 1.0f || alpha[3] != 1.0f)) {
 #pragma unroll
-      for (int d = 0; d < 32; d++) {
+      for (int d = 0; d < 8; d++) {
 #pragma unroll
         for (int r = 0; r < 4; r++) o[d][r] *= alpha[r];
       }
     }
-    _Float16* pw = sh.p + w * 16 * kPStride;
+    // ---- O[:, 128w ..] += P V over the chunk's 64 keys: A = P [head i][keys 32ks + 8g ..],
+    // B = V [keys][dim 128w + 16dt + i] by two transposing LDS reads of 4 keys each
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
+    for (int ks2 = 0; ks2 < 2; ks2++) {
+      const bf16x8 ph = *reinterpret_cast<const bf16x8*>(&sh.p[0][i * kPStride + 32 * ks2 + 8 * g]);
+      const bf16x8 pl = *reinterpret_cast<const bf16x8*>(&sh.p[1][i * kPStride + 32 * ks2 + 8 * g]);
+      const int kb0 = 32 * ks2 + 8 * g + (i >> 2);
+      s16x4 lo4[8], hi4[8];
 #pragma unroll
-      for (int r = 0; r < 4; r++) pw[(4 * g + r) * kPStride + 16 * kt + i] = (_Float16)pv[kt][r];
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P stores are in LDS
-    __builtin_amdgcn_wave_barrier();
-    // ---- O += P V.  A = P [head i][keys 32ks + 8g ..].  B = V[keys][dim 16dt + i]: two
-    // transposing LDS reads give this lane 8 consecutive keys of its dim from the row-major tile
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      const f16x8 pa = *reinterpret_cast<const f16x8*>(pw + i * kPStride + 32 * ks + 8 * g);
-      const int kb = 32 * ks + 8 * g + (i >> 2);
-      // groups of 8 dim tiles: 16 transposing reads, then the group's 8 MFMAs
-#pragma unroll
-      for (int dt0 = 0; dt0 < 32; dt0 += 8) {
-        s16x4 lo[8], hi[8];
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-          const _Float16* p0 = sh.k + kb * kKStride + 16 * (dt0 + u) + 4 * (i & 3);
-          lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0));
-          hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0 + 4 * kKStride));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-          const f16x8 vb = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo[u], hi[u], 0, 1, 2, 3, 4, 5, 6, 7));
-          o[dt0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt0 + u], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int dt = 0; dt < 8; dt++) {
+        const __bf16* p0 = sh.k + kb0 * kKStride + 128 * w + 16 * dt + 4 * (i & 3);
+        lo4[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0));
+        hi4[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0 + 4 * kKStride));
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4[dt], hi4[dt], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- epilogue: lane holds O[head 16w + 4g + r][dim 16dt + i].  The rows go out through
-  // the (now idle) key tile in LDS: each wave writes its 16 heads x 256 dims in fp32, then
-  // reads back whole rows as float4, so every global store instruction covers 1 KB.
+  // ---- epilogue: lane holds O[head h0 + 4g + r][dim 128w + 16dt + i]; rows of 16 floats.
+  // One split: the normalised output and lse.  Several: this split's unnormalised o and its
+  // (m, l) per head, slot (t, split, head) of the workspace.
   const bool single = n_splits == 1;
   const int64_t slot = (int64_t)t * n_splits + split;
-  float scale_r[4];
+  float inv[4];
 #pragma unroll
-  for (int r = 0; r < 4; r++) scale_r[r] = single ? (l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f) : 1.0f;
-  if (i == 0) {
+  for (int r = 0; r < 4; r++) inv[r] = single ? (l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f) : 1.0f;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int h = h0 + 4 * g + r;
+    float* orow = (single ? out + ((int64_t)t * kHeads + h) * kD : ws_o + (slot * kHeads + h) * kD) + 128 * w + i;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) orow[16 * dt] = o[dt][r] * inv[r];
+  }
+  if (w == 0 && i == 0) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int h = 16 * w + 4 * g + r;
-      if (single) {
-        if (lse != nullptr)
-          lse[(int64_t)t * kHeads + h] = l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
-      } else {
+      const int h = h0 + 4 * g + r;
+      if (!single) {
         ws_ml[(slot * kHeads + h) * 2 + 0] = m_run[r];
         ws_ml[(slot * kHeads + h) * 2 + 1] = l_run[r];
+      } else if (lse != nullptr) {
+        lse[(int64_t)t * kHeads + h] = l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
       }
     }
-  }
-  constexpr int kOStride = 256 + 4;  // floats per staged row (padding spreads the banks)
-  float* stage_o = reinterpret_cast<float*>(sh.k) + w * 16 * kOStride;  // 16.3 KB per wave
-  float* orow0 = single ? out + ((int64_t)t * kHeads + 16 * w) * kD : ws_o + (slot * kHeads + 16 * w) * kD;
-  __syncthreads();  // every wave is done reading the key tile
-#pragma unroll
-  for (int half = 0; half < 2; half++) {
-#pragma unroll
-    for (int dt = 0; dt < 16; dt++) {
-#pragma unroll
-      for (int r = 0; r < 4; r++) stage_o[(4 * g + r) * kOStride + 16 * dt + i] = o[16 * half + dt][r] * scale_r[r];
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows are in LDS
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int row = 0; row < 16; row++) {
-      const float4 v = *reinterpret_cast<const float4*>(stage_o + row * kOStride + 4 * lane);
-      *reinterpret_cast<float4*>(orow0 + (int64_t)row * kD + 256 * half + 4 * lane) = v;
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next half overwrites the rows
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -484,25 +447,27 @@ __global__ __launch_bounds__(128) void sparse_attn_merge_kernel(const float* __r
 #pragma unroll
   for (int s = 0; s < kMaxSplits; s++)
     if (s < n_splits && l[s] > 0.0f) M = __builtin_fmaxf(M, m[s]);
-  float L = 0.0f;
+  float Lsum = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int s = 0; s < kMaxSplits; s++) {
     if (s < n_splits && l[s] > 0.0f) {
       const float e = __expf(m[s] - M);
-      L += l[s] * e;
+      Lsum += l[s] * e;
       acc.x += v[s].x * e;
       acc.y += v[s].y * e;
       acc.z += v[s].z * e;
       acc.w += v[s].w * e;
     }
   }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
   reinterpret_cast<float4*>(out + ((int64_t)t * kHeads + h) * kD)[tid] =
       make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (lse != nullptr && tid == 0) lse[(int64_t)t * kHeads + h] = L > 0.0f ? M + __logf(L) : -__builtin_inff();
+  if (lse != nullptr && tid == 0) lse[(int64_t)t * kHeads + h] = Lsum > 0.0f ? M + __logf(Lsum) : -__builtin_inff();
 }
 
+// How a query's chunks are split: enough workgroups to cover the GPU at small batches (one
+// chunk each at batch 4), none at large batches.
 struct Plan {
   int32_t n_chunks, chunks_per_split, n_splits;
 };
@@ -510,7 +475,8 @@ struct Plan {
 Plan make_plan(int32_t n_q, int32_t K) {
   Plan p;
   p.n_chunks = (K + kMaxSwa + kChunk - 1) / kChunk;
-  int32_t want = (512 + n_q - 1) / (n_q > 0 ? n_q : 1);
+  const int32_t wgs = kGroups * (n_q > 0 ? n_q : 1);
+  int32_t want = (512 + wgs - 1) / wgs;
   if (want < 1) want = 1;
   if (want > p.n_chunks) want = p.n_chunks;
   p.chunks_per_split = (p.n_chunks + want - 1) / want;
@@ -544,7 +510,7 @@ int launch_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache, const in
   if (!q_bf16 || !kv_cache || !q_base || !swa || !swa_start || !swa_len || !out)
     return CSA2_ERR_INVALID_ARG;
   if (K > 0 && !topk) return CSA2_ERR_INVALID_ARG;
-  if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
+  if (n_q > (1 << 24)) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(q_bf16) | reinterpret_cast<uintptr_t>(kv_cache) |
        reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(workspace)) & 15)
     return CSA2_ERR_INVALID_ARG;
@@ -554,14 +520,18 @@ int launch_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache, const in
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   float* ws_o = (float*)workspace;
   float* ws_ml = need > 0 ? ws_o + (size_t)n_q * p.n_splits * kHeads * kD : nullptr;
-  hipLaunchKernelGGL(sparse_attn_kernel<kFp8Win>, dim3(p.n_splits, n_q), dim3(kThreads), 0,
-                     (hipStream_t)stream, q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start,
-                     swa_len, scale, p.n_chunks, p.chunks_per_split, p.n_splits, out, lse, ws_o,
-                     ws_ml);
+  // 4 head groups per query, dealt so that a query's workgroups land on one XCD
+  const int64_t groups = ((int64_t)n_q + kXcds - 1) / kXcds;
+  const int64_t grid = groups * kXcds * kGroups;
+  if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(sparse_attn_kernel<kFp8Win>, dim3((unsigned)grid, (unsigned)p.n_splits), dim3(kThreads), 0,
+                     (hipStream_t)stream, q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start, swa_len, scale,
+                     n_q, p.n_chunks, p.chunks_per_split, p.n_splits, out, lse, ws_o, ws_ml);
   int st = check_launch();
   if (st != CSA2_OK || p.n_splits <= 1) return st;
-  hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3(kHeads, n_q), dim3(128), 0, (hipStream_t)stream,
-                     ws_o, ws_ml, p.n_splits, out, lse);
+  if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;  // (not reached: splits only for small batches)
+  hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3(kHeads, n_q), dim3(128), 0, (hipStream_t)stream, ws_o, ws_ml,
+                     p.n_splits, out, lse);
   return check_launch();
 }
 
@@ -573,8 +543,8 @@ extern "C" int csa2_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache,
                                 const uint16_t* swa_bf16, const int64_t* swa_start,
                                 const int32_t* swa_len, float scale, float* out, float* lse,
                                 int32_t n_q, void* workspace, size_t ws_bytes, void* stream) {
-  return csa2::launch_sparse_attn<false>(q_bf16, kv_cache, q_base, topk, K, swa_bf16, 0, swa_start,
-                                         swa_len, scale, out, lse, n_q, workspace, ws_bytes, stream);
+  return csa2::launch_sparse_attn<false>(q_bf16, kv_cache, q_base, topk, K, swa_bf16, 0, swa_start, swa_len, scale,
+                                         out, lse, n_q, workspace, ws_bytes, stream);
 }
 
 extern "C" int csa2_sparse_attn_swa_fp8(const uint16_t* q_bf16, const uint8_t* kv_cache,
@@ -583,6 +553,6 @@ extern "C" int csa2_sparse_attn_swa_fp8(const uint16_t* q_bf16, const uint8_t* k
                                         const int64_t* swa_start, const int32_t* swa_len, float scale,
                                         float* out, float* lse, int32_t n_q, void* workspace,
                                         size_t ws_bytes, void* stream) {
-  return csa2::launch_sparse_attn<true>(q_bf16, kv_cache, q_base, topk, K, swa8, swa_ring, swa_start,
-                                        swa_len, scale, out, lse, n_q, workspace, ws_bytes, stream);
+  return csa2::launch_sparse_attn<true>(q_bf16, kv_cache, q_base, topk, K, swa8, swa_ring, swa_start, swa_len, scale,
+                                        out, lse, n_q, workspace, ws_bytes, stream);
 }

@@ -364,8 +364,14 @@ int csa2_append_mean_index_score_fp4q(const uint16_t *latent_bf16, int m, const 
  *   scale: logit scale (1/sqrt(512) is the library's documented default reading);
  *   out fp32 [n_q, 64, 512]; lse: NULL or fp32 [n_q, 64], natural-log partition
  *   function (max logit + log sum exp); a query with no keys gets out = 0, lse = -inf.
- *   workspace: csa2_sparse_attn_workspace(n_q, K) bytes, 16-byte aligned (may be NULL when
- *   that size is 0).  Pointers q_bf16, kv_cache, swa_bf16 and out are 16-byte aligned.
+ *   Numerics: every key value is exact in bf16 (E2M1 x E4M3, FP8 window values, bf16 rows)
+ *   and q is used as given, so the logits' products are exact for inputs of any finite
+ *   magnitude, summed in fp32; the probabilities enter the value sum as two bf16 parts
+ *   (about 2^-17 relative), accumulated in fp32.
+ *   workspace: csa2_sparse_attn_workspace(n_q, K) bytes, 16-byte aligned, caller-owned,
+ *   contents on entry ignored (may be NULL when that size is 0).  Small batches split each
+ *   query's keys over several workgroups whose partial sums land here before a merge; large
+ *   batches need none.  Pointers q_bf16, kv_cache, swa_bf16 and out are 16-byte aligned.
  *   Errors: INVALID_ARG, UNSUPPORTED (K > 512), WORKSPACE.
  */
 size_t csa2_sparse_attn_workspace(int32_t n_q, int32_t K);
@@ -394,8 +400,7 @@ int csa2_swa_pack_fp8(const uint16_t *rows_bf16, int64_t n, const int64_t *dst_r
  *   t is swa_start[t] + r; R >= 128 = the buffer is a sequence of rings of R rows (one per
  *   sequence) and the window wraps inside the ring that holds swa_start[t]:
  *     row = s + (swa_start[t] - s + r) mod R,  s = swa_start[t] - swa_start[t] mod R.
- *   Decoding is exact in f16 for window values of magnitude 2^-14 .. 65504 (groups whose
- *   smallest codes fall below f16's range lose them to underflow).
+ *   The FP8 window values decode exactly into bf16 (4 significant bits times a power of two).
  *   Errors: INVALID_ARG (also 0 < swa_ring < 128), UNSUPPORTED (K > 512), WORKSPACE.
  */
 int csa2_sparse_attn_swa_fp8(const uint16_t *q_bf16, const uint8_t *kv_cache, const int64_t *q_base,

@@ -67,6 +67,10 @@ def test_host_validation_rejects_before_launch(lib):
                                 None, 0, None) == -2
     assert lib.csa2_sparse_attn(fake, fake, fake, fake, 512, fake, fake, fake, 0.04, fake, None, 1,
                                 None, 0, None) == -3
+    assert lib.csa2_sparse_attn(ctypes.c_void_p((1 << 20) + 8), fake, fake, fake, 512, fake, fake, fake, 0.04, fake,
+                                None, 1, fake, 1 << 30, None) == -1  # q not 16-B aligned
+    assert lib.csa2_sparse_attn_workspace(4, 512) > 0  # small batches split a query's keys
+    assert lib.csa2_sparse_attn_workspace(1 << 16, 512) == 0  # large ones do not
 
 
 def test_fp8_window_entry_points_validate_before_launch(lib):

@@ -236,6 +236,47 @@ def test_sparse_attn(c, n_q, K, n_entries, seed):
     assert np.allclose(host(lse)[fin], lse_ref[fin], atol=2e-3)
 
 
+def test_sparse_attn_extreme_ranges(c):
+    """Inputs outside f16's range, which bf16 holds exactly: query heads scaled by 1e5, by 1e-6
+    and mixed (+-1e5 beside +-1e-6 in one head), window rows scaled by 2^-20 (values below
+    2^-14) and by 2^16 (above 65504), with FP4 entries of every E4M3 scale; the FP8-window
+    variant on the same rows.  Against the oracle at the attention tolerance."""
+    log("sparse_attn extreme ranges")
+    n_q, K, n_entries = 3, 512, 3000
+    kv, _ = synth.random_caches(70, n_entries, spread_scales=True)
+    d = synth.query_inputs(71, n_q)
+    q = synth.bf16_bits_to_f32(d.q).copy()
+    q[:, 0] *= np.float32(1e5)
+    q[:, 1] *= np.float32(1e-6)
+    q[:, 2, 0::2] *= np.float32(1e5)
+    q[:, 2, 1::2] *= np.float32(1e-6)
+    q[0, 3:] *= np.float32(1e-6)  # query 0: every other head tiny too
+    qb = synth.f32_to_bf16_bits(q)
+    swa = synth.bf16_bits_to_f32(d.swa).copy()
+    swa[0:40] *= np.float32(2.0 ** -20)
+    swa[130:170] *= np.float32(2.0 ** -20)
+    swa[40:60] *= np.float32(2.0 ** 16)
+    swab = synth.f32_to_bf16_bits(swa)
+    rng = np.random.default_rng(72)
+    topk = np.stack([np.sort(rng.choice(n_entries, K, replace=False)) for _ in range(n_q)]).astype(np.int32)
+    base = np.zeros(n_q, np.int64)
+    ref, lse_ref = oracle.sparse_attn(qb, kv, base, topk, swab, d.swa_start, d.swa_len)
+    out, lse = c.sparse_attn(bf16(qb), dev(kv), dev(base), dev(topk), bf16(swab), dev(d.swa_start), dev(d.swa_len))
+    torch.cuda.synchronize()
+    out = host(out)
+    assert np.all(np.isfinite(out)), "outputs stay finite"
+    rel = check_attn(out, ref)
+    log(f"  bf16 window: max rel err {rel:.2e}")
+    assert np.allclose(host(lse), lse_ref, rtol=1e-5, atol=2e-3)
+    swa8 = oracle.swa_fp8_pack(swab)
+    ref8, _ = oracle.sparse_attn_swa_fp8(qb, kv, base, topk, swa8, d.swa_start, d.swa_len)
+    out8, _ = c.sparse_attn_swa_fp8(bf16(qb), dev(kv), dev(base), dev(topk), dev(swa8), dev(d.swa_start),
+                                    dev(d.swa_len))
+    torch.cuda.synchronize()
+    rel8 = check_attn(host(out8), ref8)
+    log(f"  FP8 window: max rel err {rel8:.2e}")
+
+
 def test_sparse_attn_empty_query(c):
     log("sparse_attn empty")
     kv, _ = synth.random_caches(40, 64)
@@ -341,3 +382,33 @@ def test_block_topk_workspace_reuse_and_1m_rows(c):
     torch.cuda.synchronize()
     assert np.array_equal(host(topk), topk_ref)
     assert int(ws[: 4 * 4096 * 4].view(torch.int32).abs().sum().item()) == 0, "histogram not returned to zero"
+
+
+def _block_maxima(s, nvis):
+    n_q, width = s.shape
+    nbw = (width + 7) // 8
+    pad = np.full((n_q, nbw * 8), -np.inf, np.float32)
+    sv = np.where(np.isnan(s), -np.inf, s)
+    for t, nv in enumerate(nvis):
+        pad[t, :min(nv, width)] = sv[t, :min(nv, width)]
+    return pad.reshape(n_q, nbw, 8).max(axis=2)
+
+
+@pytest.mark.parametrize("width,seed,tie", [(524288, 64, 0.0), (524288, 65, 0.05), (600000, 66, 0.0)])
+def test_block_topk_given_block_maxima_long_rows(c, width, seed, tie):
+    """Full mode with the caller's block maxima at the 1M-context decode width (65536 blocks,
+    the single-launch path) and past it (75000 blocks: the multi-kernel path), against the
+    oracle bit for bit, with ragged visible counts and ties."""
+    log(f"block_topk with block maxima width={width}")
+    K, M = 512, 2048
+    nvis = np.array([width, width - 1, 400001, 17], np.int32)
+    s = synth.random_scores(seed, 4, width, tie_frac=tie)
+    pool_ref, topk_ref = oracle.block_topk(s, nvis, K=K, M=M)
+    pool, topk = c.block_topk(dev(s), dev(nvis), K=K, M=M, block_max=dev(_block_maxima(s, nvis)))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(pool), pool_ref), "pool differs"
+    assert np.array_equal(host(topk), topk_ref), "topk differs"
+    # the Top-K alone (no pool), as a prefill call would ask
+    _, topk2 = c.block_topk(dev(s), dev(nvis), K=K, M=M, block_max=dev(_block_maxima(s, nvis)), want_pool=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(topk2), topk_ref), "topk alone differs"
