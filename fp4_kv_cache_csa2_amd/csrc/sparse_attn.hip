@@ -24,9 +24,10 @@
 //         probabilities go to LDS as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), which
 //         represent p to about 2^-17 relative, and each part is one MFMA; the key-major value
 //         operand comes from the same tile by transposing LDS reads (ds_read_b64_tr_b16).
-// The grid is ordered so that the workgroups of a query land on one XCD (workgroups are
-// dealt to the 8 XCDs round-robin): its head groups gather the same keys, which the XCD's L2
-// then serves, and its splits' partials stay in that L2 for the merge.
+// The grid spreads its work over all 8 XCDs (workgroups are dealt to them round-robin): a
+// batch smaller than 8 queries must not leave XCDs idle while others run a second round of
+// workgroups.  Without splits, a query's 4 head groups share an XCD and gather the same keys
+// through its L2.
 //
 // The window rows come either as bf16 rows or as 584-byte FP8 window rows (the window KV
 // kept in FP8, [ZB] §2.4.4; DeepSeek-V4's FP8 KV entry, [ZB] §3.1 and [DF] §4.6), read
@@ -44,6 +45,7 @@ constexpr int kChunk = 64;                       // keys per chunk
 constexpr int kKStride = kD + 8;                 // bf16 per key row in LDS (1040 B: 8-B aligned rows)
 constexpr int kPStride = kChunk + 8;             // bf16 per probability row
 constexpr int kXcds = 8;
+constexpr int kCUs = 256;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -253,12 +255,19 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     int32_t n_splits, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
   __shared__ AttnShared sh;
-  // workgroup -> (query, head group, split): x deals a query's 4 head groups to one XCD, and y
-  // (the split) keeps that XCD because gridDim.x is a multiple of 8
+  // workgroup -> (query, head group, split).  Workgroups are dealt to the 8 XCDs round-robin,
+  // so slot j of XCD x is workgroup 8j + x.  A unit's workgroups take consecutive slots of one
+  // XCD: with splits, a unit is a (query, head group) and its workgroups are the splits; without,
+  // a unit is a query and its workgroups are the 4 head groups, which gather the same keys
+  // through one L2.  Units go round-robin over the XCDs, so every XCD gets work even for a
+  // batch of 1.
   const int L = blockIdx.x;
-  const int s = L / kXcds;
-  const int t = (s / kGroups) * kXcds + L % kXcds, hg = s % kGroups;
-  const int split = blockIdx.y;
+  const int x = L % kXcds, j = L / kXcds;
+  const int per = n_splits > 1 ? n_splits : kGroups;
+  const int unit = (j / per) * kXcds + x, k = j % per;
+  const int t = n_splits > 1 ? unit / kGroups : unit;
+  const int hg = n_splits > 1 ? unit % kGroups : k;
+  const int split = n_splits > 1 ? k : 0;
   if (t >= n_q) return;
   const int c_begin = split * chunks_per_split;
   const int c_end = min(c_begin + chunks_per_split, n_chunks);
@@ -306,14 +315,14 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
     // ---- S = Q K^T for keys 16w .. 16w + 15 of the chunk (lane: heads 4g + r, key 16w + i)
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s0 = 0; s0 < 16; s0 += 8) {
-      bf16x8 kb[8];
+    for (int s0 = 0; s0 < 16; s0 += 4) {
+      bf16x8 kb[4];
 #pragma unroll
-      for (int sd = 0; sd < 8; sd++)
+      for (int sd = 0; sd < 4; sd++)
         kb[sd] = *reinterpret_cast<const bf16x8*>(sh.k + (16 * w + i) * kKStride + 32 * (s0 + sd) + 8 * g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int sd = 0; sd < 8; sd++) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s0 + sd], kb[sd], sacc, 0, 0, 0);
+      for (int sd = 0; sd < 4; sd++) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s0 + sd], kb[sd], sacc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- the chunk's maximum per head across the 4 waves
@@ -466,8 +475,9 @@ __global__ __launch_bounds__(128) void sparse_attn_merge_kernel(const float* __r
   if (lse != nullptr && tid == 0) lse[(int64_t)t * kHeads + h] = Lsum > 0.0f ? M + __logf(Lsum) : -__builtin_inff();
 }
 
-// How a query's chunks are split: enough workgroups to cover the GPU at small batches (one
-// chunk each at batch 4), none at large batches.
+// How a query's chunks are split: at most one workgroup per CU (a workgroup's registers and
+// LDS allow one per CU), all of them running at once -- one chunk each at batch 4 -- and no
+// splits once the batch alone fills the GPU.
 struct Plan {
   int32_t n_chunks, chunks_per_split, n_splits;
 };
@@ -476,7 +486,7 @@ Plan make_plan(int32_t n_q, int32_t K) {
   Plan p;
   p.n_chunks = (K + kMaxSwa + kChunk - 1) / kChunk;
   const int32_t wgs = kGroups * (n_q > 0 ? n_q : 1);
-  int32_t want = (512 + wgs - 1) / wgs;
+  int32_t want = kCUs / wgs;
   if (want < 1) want = 1;
   if (want > p.n_chunks) want = p.n_chunks;
   p.chunks_per_split = (p.n_chunks + want - 1) / want;
@@ -520,11 +530,12 @@ int launch_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache, const in
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   float* ws_o = (float*)workspace;
   float* ws_ml = need > 0 ? ws_o + (size_t)n_q * p.n_splits * kHeads * kD : nullptr;
-  // 4 head groups per query, dealt so that a query's workgroups land on one XCD
-  const int64_t groups = ((int64_t)n_q + kXcds - 1) / kXcds;
-  const int64_t grid = groups * kXcds * kGroups;
+  // units (see the kernel) rounded up to whole rows of 8, times the workgroups per unit
+  const int64_t units = p.n_splits > 1 ? (int64_t)n_q * kGroups : (int64_t)n_q;
+  const int64_t per = p.n_splits > 1 ? p.n_splits : kGroups;
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds * per;
   if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(sparse_attn_kernel<kFp8Win>, dim3((unsigned)grid, (unsigned)p.n_splits), dim3(kThreads), 0,
+  hipLaunchKernelGGL(sparse_attn_kernel<kFp8Win>, dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start, swa_len, scale,
                      n_q, p.n_chunks, p.chunks_per_split, p.n_splits, out, lse, ws_o, ws_ml);
   int st = check_launch();

@@ -210,7 +210,8 @@ def test_block_topk_candidate_mode_exact(c):
 
 # ------------------------------------------------------------------ sparse attention
 @pytest.mark.parametrize("n_q,K,n_entries,seed", [(1, 512, 4096, 30), (4, 512, 3000, 31), (3, 100, 500, 32),
-                                                   (600, 512, 2048, 33)])
+                                                   (600, 512, 2048, 33), (16, 512, 4096, 34), (32, 300, 2048, 35),
+                                                   (33, 512, 2048, 36)])
 def test_sparse_attn(c, n_q, K, n_entries, seed):
     log(f"sparse_attn n_q={n_q} K={K}")
     kv, _ = synth.random_caches(seed, n_entries)
@@ -275,6 +276,30 @@ def test_sparse_attn_extreme_ranges(c):
     torch.cuda.synchronize()
     rel8 = check_attn(host(out8), ref8)
     log(f"  FP8 window: max rel err {rel8:.2e}")
+
+
+def test_sparse_attn_workspace_reuse(c):
+    """One workspace, never cleared, serves calls of different batch sizes in a row (different
+    split counts, so the partials of one call lie where another's would): every output matches
+    the oracle."""
+    log("sparse_attn workspace reuse")
+    K, n_entries = 512, 3000
+    kv, _ = synth.random_caches(80, n_entries)
+    kv_d = dev(kv)
+    sizes = [4, 16, 1, 32, 8, 4]
+    ws = torch.full((max(c.sparse_attn_workspace(n, K) for n in sizes),), 0x7F, dtype=torch.uint8, device="cuda")
+    for j, n_q in enumerate(sizes):
+        d = synth.query_inputs(81 + j, n_q)
+        rng = np.random.default_rng(90 + j)
+        topk = np.stack([np.sort(rng.choice(n_entries, K, replace=False)) for _ in range(n_q)]).astype(np.int32)
+        base = np.zeros(n_q, np.int64)
+        ref, lse_ref = oracle.sparse_attn(d.q, kv, base, topk, d.swa, d.swa_start, d.swa_len)
+        out, lse = c.sparse_attn(bf16(d.q), kv_d, dev(base), dev(topk), bf16(d.swa), dev(d.swa_start),
+                                 dev(d.swa_len), workspace=ws)
+        torch.cuda.synchronize()
+        rel = check_attn(host(out), ref)
+        log(f"  n_q={n_q}: max rel err {rel:.2e}")
+        assert np.allclose(host(lse), lse_ref, atol=2e-3)
 
 
 def test_sparse_attn_empty_query(c):
