@@ -437,9 +437,16 @@ constexpr int kMaxSplits = (kMaxTopK + kMaxSwa + kChunk - 1) / kChunk;
 
 __global__ __launch_bounds__(128) void sparse_attn_merge_kernel(const float* __restrict__ ws_o,
                                                                 const float* __restrict__ ws_ml,
-                                                                int32_t n_splits, float* __restrict__ out,
+                                                                int32_t n_splits, int32_t n_q,
+                                                                float* __restrict__ out,
                                                                 float* __restrict__ lse) {
-  const int t = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+  // workgroup -> (query, head) on the XCD that ran the head's (query, head group) unit in the
+  // attention launch (the same dealing: slot j of XCD x, 16 heads per unit), so the partials
+  // it reads were written through that XCD's L2
+  const int L = blockIdx.x, x = L % kXcds, j = L / kXcds;
+  const int unit = (j / kHeadGroup) * kXcds + x;
+  const int t = unit / kGroups, h = (unit % kGroups) * kHeadGroup + j % kHeadGroup, tid = threadIdx.x;
+  if (t >= n_q) return;
   float m[kMaxSplits], l[kMaxSplits];
   float4 v[kMaxSplits];
 #pragma unroll
@@ -540,9 +547,9 @@ int launch_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache, const in
                      n_q, p.n_chunks, p.chunks_per_split, p.n_splits, out, lse, ws_o, ws_ml);
   int st = check_launch();
   if (st != CSA2_OK || p.n_splits <= 1) return st;
-  if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;  // (not reached: splits only for small batches)
-  hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3(kHeads, n_q), dim3(128), 0, (hipStream_t)stream, ws_o, ws_ml,
-                     p.n_splits, out, lse);
+  const int64_t merge_grid = (units + kXcds - 1) / kXcds * kXcds * kHeadGroup;
+  hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3((unsigned)merge_grid), dim3(128), 0, (hipStream_t)stream, ws_o,
+                     ws_ml, p.n_splits, n_q, out, lse);
   return check_launch();
 }
 
