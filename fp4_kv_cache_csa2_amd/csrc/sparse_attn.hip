@@ -59,6 +59,13 @@ struct __attribute__((aligned(16))) AttnShared {
   int32_t valid[kChunk];
 };
 
+// The all-heads kernel's shared block: the same key tile, and each wave's own probabilities.
+struct __attribute__((aligned(16))) WideShared {
+  __bf16 k[kChunk * kKStride] __attribute__((aligned(16)));
+  __bf16 p[kWaves][2][kHeadGroup * kPStride] __attribute__((aligned(16)));  // per wave: hi, lo
+  int32_t valid[kChunk];
+};
+
 // Raw bytes of one key slot for one thread (a quarter of a key), fetched a chunk ahead: a
 // selected entry's 64 payload bytes and 8 E4M3 scale bytes, or a window row's quarter (256
 // bytes of bf16, or 144 bytes of an FP8 row: 112 code bytes, 32 bf16 bytes), with the FP8
@@ -164,8 +171,10 @@ struct KeyStager {
     }
   }
 
-  // decode to bf16 (exact) and store the key quarter row-major in LDS
-  __device__ __forceinline__ void stage(const KeyRaw& r, AttnShared& sh) const {
+  // decode to bf16 (exact) and store the key quarter row-major in LDS (sh: either
+  // kernel's shared block, each with the key tile k and the slot flags valid)
+  template <class Shared>
+  __device__ __forceinline__ void stage(const KeyRaw& r, Shared& sh) const {
     __bf16* krow = sh.k + kk * kKStride + 128 * qq;
     if (r.kind == 1) {
       // the 8 E4M3 scales of this quarter: the codes convert at scale 1 (v_cvt_scalef32 applies
@@ -431,6 +440,189 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   }
 }
 
+// All 64 heads of a query in one workgroup, every chunk of its keys: wave w owns heads
+// 16w .. 16w + 15 and all 512 output dims, so the 4 waves share one decoded key tile per
+// chunk and each runs its softmax alone (no cross-wave exchange, two barriers per chunk).
+// Used when the batch alone fills the GPU (no key splits), where a quarter of the
+// workgroups, each decoding a chunk once for 64 heads, beats one workgroup per head group.
+// The arithmetic per (head, key) is the head-group kernel's: exact bf16 QK^T products,
+// fp32 sums, online fp32 softmax, P as bf16 hi + lo parts in PV.
+template <bool kFp8Win>
+__global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_cache,
+    const int64_t* __restrict__ q_base, const int32_t* __restrict__ topk, int32_t K,
+    const void* __restrict__ swa_v, int64_t swa_ring, const int64_t* __restrict__ swa_start,
+    const int32_t* __restrict__ swa_len, float scale, int32_t n_q, int32_t n_chunks, float* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ WideShared sh;
+  const int t = blockIdx.x;
+  if (t >= n_q) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  KeyStager<kFp8Win> ks(kv_cache, topk + (int64_t)t * K, K, swa_v, swa_ring, q_base[t], swa_start[t], swa_len[t], tid);
+
+  int32_t id_next = n_chunks > 0 ? ks.load_id(0) : -1;
+  int32_t id_after = n_chunks > 1 ? ks.load_id(1) : -1;
+  __builtin_amdgcn_sched_barrier(0);
+  // query fragments (A of QK^T): head 16w + i, dims 32s + 8g .. +7, bf16 as given
+  bf16x8 qa[16];
+  {
+    const uint16_t* qh = q + ((int64_t)t * kHeads + 16 * w + i) * kD + 8 * g;
+#pragma unroll
+    for (int sd = 0; sd < 16; sd++) qa[sd] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qh + 32 * sd));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  KeyRaw raw;
+  if (n_chunks > 0) ks.fetch(0, id_next, raw);
+
+  f32x4 o[32];  // output dims 16dt + i, heads 16w + 4g + r
+#pragma unroll
+  for (int d = 0; d < 32; d++) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    m_run[r] = -__builtin_inff();
+    l_run[r] = 0.0f;
+  }
+  __bf16* ph_w = sh.p[w][0];
+  __bf16* pl_w = sh.p[w][1];
+
+  for (int c = 0; c < n_chunks; c++) {
+    __syncthreads();  // the previous chunk's LDS reads are done
+    ks.stage(raw, sh);
+    if (c + 1 < n_chunks) {  // the next chunk's gather overlaps this chunk's math
+      ks.fetch(c + 1, id_after, raw);
+      id_after = c + 2 < n_chunks ? ks.load_id(c + 2) : -1;
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T for the chunk's 4 tiles of 16 keys (lane: heads 4g + r, key 16kt + i)
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < 16; s0 += 2) {
+      bf16x8 kb[2][4];
+#pragma unroll
+      for (int sd = 0; sd < 2; sd++) {
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+          kb[sd][kt] = *reinterpret_cast<const bf16x8*>(sh.k + (16 * kt + i) * kKStride + 32 * (s0 + sd) + 8 * g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sd = 0; sd < 2; sd++) {
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s0 + sd], kb[sd][kt], sacc[kt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- online softmax over the chunk, within the wave
+    float lg[4][4], cm[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) cm[r] = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+      const bool ok = sh.valid[16 * kt + i] != 0;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        lg[kt][r] = ok ? sacc[kt][r] * scale : -__builtin_inff();
+        cm[r] = __builtin_fmaxf(cm[r], lg[kt][r]);
+      }
+    }
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float mn = __builtin_fmaxf(m_run[r], row16_max(cm[r]));
+      alpha[r] = (mn == -__builtin_inff()) ? 1.0f : __expf(m_run[r] - mn);
+      float rs = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; kt++) {
+        const float pr = (lg[kt][r] == -__builtin_inff()) ? 0.0f : __expf(lg[kt][r] - mn);
+        const __bf16 hi = (__bf16)pr;
+        const __bf16 lo = (__bf16)(pr - (float)hi);
+        ph_w[(4 * g + r) * kPStride + 16 * kt + i] = hi;
+        pl_w[(4 * g + r) * kPStride + 16 * kt + i] = lo;
+        rs += pr;
+      }
+      l_run[r] = l_run[r] * alpha[r] + row16_sum(rs);
+      m_run[r] = mn;
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f || alpha[2] != 1.0f || alpha[3] != 1.0f)) {
+#pragma unroll
+      for (int d = 0; d < 32; d++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) o[d][r] *= alpha[r];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P stores are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // ---- O += P V over the chunk's 64 keys: A = P [head i][keys 32ks + 8g ..] (hi, lo),
+    // B = V [keys][dim 16dt + i] by two transposing LDS reads of 4 keys each
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ks2++) {
+      const bf16x8 ph = *reinterpret_cast<const bf16x8*>(ph_w + i * kPStride + 32 * ks2 + 8 * g);
+      const bf16x8 pl = *reinterpret_cast<const bf16x8*>(pl_w + i * kPStride + 32 * ks2 + 8 * g);
+      const int kb0 = 32 * ks2 + 8 * g + (i >> 2);
+#pragma unroll
+      for (int dt0 = 0; dt0 < 32; dt0 += 8) {
+        s16x4 lo4[8], hi4[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const __bf16* p0 = sh.k + kb0 * kKStride + 16 * (dt0 + u) + 4 * (i & 3);
+          lo4[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0));
+          hi4[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p0 + 4 * kKStride));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4[u], hi4[u], 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dt0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[dt0 + u], 0, 0, 0);
+          o[dt0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[dt0 + u], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds O[head 16w + 4g + r][dim 16dt + i].  The rows go out through
+  // the idle key tile: each wave stages its 16 heads x 256 dims in fp32, then reads whole
+  // rows back as float4, so every global store instruction writes 1 KB.
+  float inv[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) inv[r] = l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f;
+  if (lse != nullptr && i == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      lse[(int64_t)t * kHeads + 16 * w + 4 * g + r] =
+          l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
+  }
+  constexpr int kOStride = 256 + 4;  // floats per staged row (the padding spreads the banks)
+  static_assert(kWaves * 16 * kOStride * 4 <= (int)sizeof(sh.k), "staged rows fit in the key tile");
+  float* stage_o = reinterpret_cast<float*>(sh.k) + w * 16 * kOStride;
+  float* orow0 = out + ((int64_t)t * kHeads + 16 * w) * kD;
+  __syncthreads();  // every wave is done reading the key tile
+#pragma unroll
+  for (int half = 0; half < 2; half++) {
+#pragma unroll
+    for (int dt = 0; dt < 16; dt++) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) stage_o[(4 * g + r) * kOStride + 16 * dt + i] = o[16 * half + dt][r] * inv[r];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int row = 0; row < 16; row++) {
+      const float4 v = *reinterpret_cast<const float4*>(stage_o + row * kOStride + 4 * lane);
+      *reinterpret_cast<float4*>(orow0 + (int64_t)row * kD + 256 * half + 4 * lane) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next half overwrites the rows
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Combine the split partials of one (query, head): out = sum_s o_s e^(m_s - M) / L.  Every
 // split's (m, l) and o slice load at once (splits <= kMaxSplits), then one pass combines.
 constexpr int kMaxSplits = (kMaxTopK + kMaxSwa + kChunk - 1) / kChunk;
@@ -537,6 +729,12 @@ int launch_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache, const in
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   float* ws_o = (float*)workspace;
   float* ws_ml = need > 0 ? ws_o + (size_t)n_q * p.n_splits * kHeads * kD : nullptr;
+  if (p.n_splits == 1) {  // the batch fills the GPU: one workgroup per query, all 64 heads
+    hipLaunchKernelGGL(sparse_attn_wide_kernel<kFp8Win>, dim3((unsigned)n_q), dim3(kThreads), 0, (hipStream_t)stream,
+                       q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start, swa_len, scale, n_q, p.n_chunks,
+                       out, lse);
+    return check_launch();
+  }
   // units (see the kernel) rounded up to whole rows of 8, times the workgroups per unit
   const int64_t units = p.n_splits > 1 ? (int64_t)n_q * kGroups : (int64_t)n_q;
   const int64_t per = p.n_splits > 1 ? p.n_splits : kGroups;

@@ -237,13 +237,14 @@ def test_sparse_attn(c, n_q, K, n_entries, seed):
     assert np.allclose(host(lse)[fin], lse_ref[fin], atol=2e-3)
 
 
-def test_sparse_attn_extreme_ranges(c):
+@pytest.mark.parametrize("n_q", [3, 40])  # 40: a batch with no key splits (the all-heads kernel)
+def test_sparse_attn_extreme_ranges(c, n_q):
     """Inputs outside f16's range, which bf16 holds exactly: query heads scaled by 1e5, by 1e-6
     and mixed (+-1e5 beside +-1e-6 in one head), window rows scaled by 2^-20 (values below
     2^-14) and by 2^16 (above 65504), with FP4 entries of every E4M3 scale; the FP8-window
     variant on the same rows.  Against the oracle at the attention tolerance."""
-    log("sparse_attn extreme ranges")
-    n_q, K, n_entries = 3, 512, 3000
+    log(f"sparse_attn extreme ranges n_q={n_q}")
+    K, n_entries = 512, 3000
     kv, _ = synth.random_caches(70, n_entries, spread_scales=True)
     d = synth.query_inputs(71, n_q)
     q = synth.bf16_bits_to_f32(d.q).copy()
