@@ -50,6 +50,10 @@ _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
 _L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 _L.csa2_block_topk_noalloc.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+_L.csa2_block_topk_rescore_workspace.argtypes = [_i32, _i32, _i32, _i32]
+_L.csa2_block_topk_rescore_workspace.restype = _sz
+_L.csa2_block_topk_rescore.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz,
+                                       _vp]
 _L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32]
 _L.csa2_sparse_attn_workspace.restype = _sz
 _L.csa2_sparse_attn.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp, _sz, _vp]
@@ -62,7 +66,8 @@ SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_co
            "csa2_sparse_attn_workspace", "csa2_sparse_attn", "csa2_swa_pack_fp8", "csa2_sparse_attn_swa_fp8",
            "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q", "csa2_block_mean_pack", "csa2_append_index_score",
            "csa2_append_index_score_fp4q", "csa2_append_index_score_packq", "csa2_append_mean_index_score",
-           "csa2_append_mean_index_score_fp4q", "csa2_block_topk_noalloc")
+           "csa2_append_mean_index_score_fp4q", "csa2_block_topk_noalloc", "csa2_block_topk_rescore_workspace",
+           "csa2_block_topk_rescore")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -215,9 +220,9 @@ def _query_rows(q_base, q_nvis, n_q):
     _dev(q_nvis, torch.int32, "q_nvis", (n_q,))
 
 
-def _score_outputs(scores, block_max, want_block_max, n_q, width, dev, stream, full_mode=True):
+def _score_outputs(scores, block_max, want_block_max, n_q, width, dev, stream, full_mode=True, want_scores=True):
     with _on(stream):
-        if scores is None:
+        if scores is None and want_scores:
             scores = torch.empty((n_q, width), dtype=torch.float32, device=dev)
         if block_max is None and want_block_max and full_mode:
             block_max = torch.empty((n_q, (width + 7) // 8), dtype=torch.float32, device=dev)
@@ -276,19 +281,24 @@ def _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q):
 
 def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q_idx, head_w, q_base, q_nvis,
                        width: int, scores=None, block_max=None, want_block_max: bool = True, stream=None,
-                       pack_q: bool = False):
+                       pack_q: bool = False, want_scores: bool = True):
     """Appends query t's newest entry (latent bf16 [n_q*m, 512]) at cache row
     q_base[t] + q_nvis[t] - 1, then scores every visible entry: compress_append followed by
     Full-mode index_score, in one launch.  q_idx is bf16 [n_q, 32, 128] or MXFP4 uint8
     [n_q, 32, 68] (from quantize_q_mxfp4); pack_q=True with a bf16 q_idx packs it to MXFP4
     inside the launch (quantize_q_mxfp4 followed by the MXFP4-query call).  pool_w: fp32
-    [m, 512], or [n_q*m, 512] for one weight row per latent token."""
+    [m, 512], or [n_q*m, 512] for one weight row per latent token.  want_scores=False (bf16
+    query): the block maxima alone are written and scores comes back None (the selection then
+    uses block_topk_rescore)."""
     fp4 = isinstance(q_idx, torch.Tensor) and q_idx.dtype == torch.uint8
     if pack_q and fp4:
         raise ValueError("pack_q takes a bf16 q_idx")
+    if not want_scores and (fp4 or pack_q or scores is not None or not want_block_max):
+        raise ValueError("want_scores=False takes a bf16 q_idx, no scores buffer and the block maxima")
     n_q, _ = _index_args(q_idx, "fp4" if fp4 else "bf16", head_w, idx_cache, q_base, q_nvis, width, None)
     per_token = _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q)
-    scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_idx.device, stream)
+    scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_idx.device, stream,
+                                       want_scores=want_scores)
     name = "csa2_append_index_score" + ("_fp4q" if fp4 else "_packq" if pack_q else "")
     fn = getattr(_L, name)
     _check(name, fn(
@@ -441,6 +451,44 @@ def block_mean_pack(idx_cache, seq_base, seq_n, n_blocks: int, mean_cache, mean_
         _ptr(idx_cache), _ptr(seq_base), _ptr(seq_n), _ptr(first_block), n_seq, n_blocks, _ptr(mean_cache),
         _ptr(mean_base), _stream(stream)))
     return mean_cache
+
+
+def block_topk_rescore_workspace(n_q: int, width: int, M: int, K: int) -> int:
+    return int(_L.csa2_block_topk_rescore_workspace(n_q, width, M, K))
+
+
+def block_topk_rescore(block_max, q_nvis, q_idx, head_w, idx_cache, q_base, width: int, K: int = 512,
+                       M: int = 2048, want_pool: bool = True, pool_out=None, topk_out=None, workspace=None,
+                       stream=None):
+    """(pool [n_q, M] or None, topk [n_q, K]): Full-mode selection from the block maxima
+    [n_q, ceil(width/8)], re-scoring the candidate entries from the indexer cache (bf16
+    q_idx [n_q, 32, 128], head_w [n_q, 32], idx_cache [rows, 68], q_base [n_q]); the result
+    of block_topk on the score row the scan would have written.  A given workspace must hold
+    block_topk_rescore_workspace(...) bytes and start zeroed (every call leaves it so)."""
+    _need(block_max, "block_max")
+    _dev(block_max, torch.float32, "block_max", (None, (width + 7) // 8))
+    n_q = block_max.shape[0]
+    dev = block_max.device
+    _need(q_nvis, "q_nvis")
+    _dev(q_nvis, torch.int32, "q_nvis", (n_q,))
+    _index_args(q_idx, "bf16", head_w, idx_cache, q_base, q_nvis, width, None)
+    if q_idx.shape[0] != n_q:
+        raise ValueError("q_idx needs one query per block_max row")
+    with _on(stream):
+        if pool_out is None and want_pool:
+            pool_out = torch.empty((n_q, M), dtype=torch.int32, device=dev)
+        if topk_out is None:
+            topk_out = torch.empty((n_q, K), dtype=torch.int32, device=dev)
+        if workspace is None:  # the histogram region must start zeroed; every call leaves it zeroed
+            workspace = torch.zeros(max(block_topk_rescore_workspace(n_q, width, M, K), 4), dtype=torch.uint8,
+                                    device=dev)
+    _dev(pool_out, torch.int32, "pool_out", (n_q, M))
+    _dev(topk_out, torch.int32, "topk_out", (n_q, K))
+    _dev(workspace, workspace.dtype, "workspace")
+    _check("csa2_block_topk_rescore", _L.csa2_block_topk_rescore(
+        _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(q_idx), _ptr(head_w), _ptr(idx_cache), _ptr(q_base), M, K,
+        _ptr(pool_out), _ptr(topk_out), _ptr(workspace), _bytes(workspace), _stream(stream)))
+    return pool_out, topk_out
 
 
 def sparse_attn_workspace(n_q: int, K: int) -> int:

@@ -32,7 +32,8 @@ using namespace idx;
 
 constexpr int kAppendWgs = 1;  // append workgroups per query
 
-template <bool kFp4Q>
+// kScores = false (bf16 query): block maxima only, the score row is not written
+template <bool kFp4Q, bool kScores = true>
 __global__ __launch_bounds__(kThreads) void append_index_kernel(
     const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
     const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
@@ -42,9 +43,10 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
   const int t = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   if (blockIdx.x >= kAppendWgs) {
-    score_tiles<false, kFp4Q, kOlderSlots>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
-                                           block_max, t, (int32_t)(blockIdx.x - kAppendWgs) * kWaves + wave,
-                                           (int32_t)(gridDim.x - kAppendWgs) * kWaves);
+    score_tiles<false, kFp4Q, kOlderSlots, false, kScores>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width,
+                                                           scores, block_max, t,
+                                                           (int32_t)(blockIdx.x - kAppendWgs) * kWaves + wave,
+                                                           (int32_t)(gridDim.x - kAppendWgs) * kWaves);
     return;
   }
   __shared__ EntryShared sh;
@@ -52,8 +54,8 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
   const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
   compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
                     idx_cache, sh);
-  score_tiles<false, kFp4Q, kNewestSlots>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
-                                          block_max, t, wave, kWaves, sh.idx_row);
+  score_tiles<false, kFp4Q, kNewestSlots, false, kScores>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width,
+                                                          scores, block_max, t, wave, kWaves, sh.idx_row);
 }
 
 // The query of t packed to MXFP4 into LDS by the whole workgroup, by the rules of
@@ -149,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
 }
 
 // workgroups of each kernel of this file that fit on the device at once (per device)
-std::atomic<int> resident_entry[kMaxDevices], resident_packq[kMaxDevices], resident_mean[kMaxDevices];
+std::atomic<int> resident_entry[kMaxDevices], resident_entry_max[kMaxDevices], resident_packq[kMaxDevices],
+    resident_mean[kMaxDevices];
 
 // workgroups along x: the append workgroup, then the scan's share of one round of resident
 // workgroups (at least one, at most what the row's tiles can use)
@@ -171,14 +174,14 @@ template <bool kFp4Q>
 int check_args(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,
                const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const void* q, const float* head_w,
                const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width, float* scores,
-               float* block_max) {
+               float* block_max, bool maxima_only_ok = false) {
   if (n_q < 0 || width < 0 || (per_token_w != 0 && per_token_w != 1)) return CSA2_ERR_INVALID_ARG;
   if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
   if (width == 0) return CSA2_ERR_INVALID_ARG;  // every query appends into a visible slot
-  if (!latent || !rope_cs || !w_idx || !kv_cache || !idx_cache || !q || !head_w || !q_base || !q_nvis ||
-      !scores)
+  if (!latent || !rope_cs || !w_idx || !kv_cache || !idx_cache || !q || !head_w || !q_base || !q_nvis)
     return CSA2_ERR_INVALID_ARG;
+  if (!scores && !(maxima_only_ok && block_max)) return CSA2_ERR_INVALID_ARG;  // NULL scores: maxima only
   if (m == 2 && !pool_w) return CSA2_ERR_INVALID_ARG;
   if (n_q > 65535 || width > kMaxIndexWidth) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(w_idx) |
@@ -198,8 +201,16 @@ int append_index_entry(const uint16_t* latent, int m, const float* pool_w, int p
                        const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
                        float* scores, float* block_max, void* stream) {
   const int rc = check_args<kFp4Q>(latent, m, pool_w, per_token_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
-                                  n_q, width, scores, block_max);
+                                  n_q, width, scores, block_max, !kFp4Q);
   if (rc != CSA2_OK || n_q == 0) return rc;
+  if (!kFp4Q && !scores) {  // block maxima only
+    const int64_t gx =
+        grid_x(resident_workgroups(append_index_kernel<false, false>, kThreads, resident_entry_max), n_q, width);
+    hipLaunchKernelGGL((append_index_kernel<false, false>), dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
+                       (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
+                       q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
+    return check_launch();
+  }
   const int64_t gx = grid_x(resident_workgroups(append_index_kernel<false>, kThreads, resident_entry), n_q, width);
   hipLaunchKernelGGL(append_index_kernel<kFp4Q>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads),
                      0, (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w,

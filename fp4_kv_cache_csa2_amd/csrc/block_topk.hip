@@ -38,6 +38,7 @@
 #include <mutex>
 
 #include "csa2_device.hpp"
+#include "index_tiles.hpp"
 
 namespace csa2 {
 namespace {
@@ -484,10 +485,21 @@ struct Ws {
   int32_t* cnt_b;    // [n_q][G] per-workgroup lengths of list B
   int32_t* ids_a;    // [n_q][G * kSlice]
   uint32_t* keys_a;
-  int32_t* ids_b;    // [n_q][G * kSegB]
+  int32_t* ids_b;    // [n_q][G * seg_b]
   uint32_t* keys_b;
   float* bm;         // [n_q][nbw] block maxima when the caller gives none
   int32_t G;
+  int32_t seg_b;     // list-B slots per K2 workgroup: kSegB, or every slot of its slice when re-scoring
+};
+
+// Re-scoring mode (Full mode without a score row): list B's entries are scored from the
+// indexer cache by the scan's own tile arithmetic (idx::mfma_bf16_tile, idx::head_sum), so
+// their keys are the bits the scan would have written.
+struct Rescore {
+  const uint16_t* q;         // bf16 indexer query [n_q, 32, 128]
+  const float* head_w;       // [n_q, 32]
+  const uint8_t* idx_cache;  // [rows, 68]; query t's entry j at row q_base[t] + j
+  const int64_t* q_base;
 };
 
 // ------------------------------------------------------------------ K1: histogram
@@ -554,10 +566,11 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
 // hold K entries at or above that edge, so every Top-K entry keeps its key.
 constexpr int kItemsPerLane = kSlice / kGThreads;
 
-template <bool cand>
+template <bool cand, bool kRescore = false>
 __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
     bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
-    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
+    const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws,
+    Rescore rsc) {
   __shared__ int32_t s_wave[kGThreads / 64];
   __shared__ int32_t s_cnt[2][kGThreads / 64];
   __shared__ int32_t s_bnd[2];
@@ -645,24 +658,63 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
   if (cand || !want_topk) return;  // pool-only mode needs no list B
   __syncthreads();
   // ---- list B: of every candidate block, the entries whose keys reach the floor, in
-  // order.  Slots (8 per block) go in chunks of 1024: wave w scores slots 256w .. 256w+255
+  // order.  Slots (8 per block) go in chunks of 1024: wave w takes slots 256w .. 256w+255
   // of the chunk (4 rounds of 64), and the chunk's survivors append after the last ones.
+  // Re-scoring computes each round's 64 keys as two 32-entry tiles (lane (n, g) of tile h
+  // scores slot 64u + 32h + n; lane L takes slot 64u + L from tile L / 32).
   const int nslots = ncb * kBlock;
   constexpr int kSlotRounds = kSegB / kGThreads;
-  int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * kSegB;
-  uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * kSegB;
+  const int seg_b = ws.seg_b;
+  int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * seg_b;
+  uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * seg_b;
+  __amdgpu_buffer_rsrc_t rs_cache;
+  if constexpr (kRescore)
+    rs_cache = __builtin_amdgcn_make_buffer_rsrc((void*)(rsc.idx_cache + rsc.q_base[t] * kIdxBytes), (short)0,
+                                                 r.n * kIdxBytes, 0x00020000);
+  constexpr int32_t kPast = 1 << 30;  // a byte offset past the cache buffer's end
   int nbv = 0;
   for (int c0 = 0; c0 < nslots; c0 += kSegB) {
     uint32_t bk[kSlotRounds];
     uint64_t bf[kSlotRounds];
     int cw = 0;
+    if constexpr (kRescore) {
+      // the query's fragments and head weights (lane (n, g) as in the scan) go out with the
+      // candidate rows, only in workgroups that have candidates
+      const int n = lane & 31, gg = lane >> 5;
+      bf16x8 qa[8];
+      float qw[16];
+      idx::load_query_bf16(rsc.q, rsc.head_w, t, n, gg, qa, qw);
+      idx::RawTile rt[kSlotRounds][2];
 #pragma unroll
-    for (int u = 0; u < kSlotRounds; u++) {  // every score load of the chunk in flight at once
-      const int c = c0 + 256 * wave + 64 * u + lane;
-      const int32_t j = c < nslots ? s_cb[c >> 3] * kBlock + (c & 7) : 0;
-      const float v = (c < nslots && j < r.n) ? r.scores[j] : 0.0f;
-      const uint32_t k = (c < nslots && j < r.n) ? order_key(v) : 0u;
-      bk[u] = k >= floor_key ? k : 0u;
+      for (int u = 0; u < kSlotRounds; u++) {  // every row load of the chunk in flight at once
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int cs = c0 + 256 * wave + 64 * u + 32 * h + n;
+          const int32_t j = cs < nslots ? s_cb[cs >> 3] * kBlock + (cs & 7) : 0;
+          rt[u][h].valid = cs < nslots && j < r.n;
+          idx::load_row_share(rs_cache, rt[u][h].valid ? j * kIdxBytes : kPast, gg, rt[u][h]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSlotRounds; u++) {
+        const int base = c0 + 256 * wave + 64 * u;  // wave-uniform
+        float sc0 = 0.0f, sc1 = 0.0f;
+        if (base < nslots) sc0 = idx::head_sum(idx::mfma_bf16_tile(qa, rt[u][0], gg), qw, rt[u][0].valid);
+        if (base + 32 < nslots) sc1 = idx::head_sum(idx::mfma_bf16_tile(qa, rt[u][1], gg), qw, rt[u][1].valid);
+        const int c = base + lane;
+        const int32_t j = c < nslots ? s_cb[c >> 3] * kBlock + (c & 7) : 0;
+        const uint32_t k = (c < nslots && j < r.n) ? order_key(lane < 32 ? sc0 : sc1) : 0u;
+        bk[u] = k >= floor_key ? k : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSlotRounds; u++) {  // every score load of the chunk in flight at once
+        const int c = c0 + 256 * wave + 64 * u + lane;
+        const int32_t j = c < nslots ? s_cb[c >> 3] * kBlock + (c & 7) : 0;
+        const float v = (c < nslots && j < r.n) ? r.scores[j] : 0.0f;
+        const uint32_t k = (c < nslots && j < r.n) ? order_key(v) : 0u;
+        bk[u] = k >= floor_key ? k : 0u;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kSlotRounds; u++) {
@@ -678,7 +730,7 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
       tot += s_cnt[0][w];
     }
     __syncthreads();  // s_cnt is rewritten by the next chunk
-    if (nbv + tot > kSegB) {  // segment overflow: the finalize falls back to the full row
+    if (nbv + tot > seg_b) {  // segment overflow (only without re-scoring): the finalize falls back to the full row
       if (tid == 0) ws.cnt_b[(int64_t)t * G + g] = kListCap + 1;
       return;
     }
@@ -730,7 +782,7 @@ struct FinShared {
 // 1 takes the Top-K from list B (Full mode) or list A (candidate mode).  Each reads the
 // matching histogram, returns it to zero, gathers its list (a superset of the selection
 // in ascending id order) and refines the boundary bin's low 20 bits over it.
-template <bool cand>
+template <bool cand, bool kRescore = false>
 __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
     bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ bm, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws,
@@ -744,7 +796,7 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   const bool use_a = role == 0 || cand;
   uint32_t* gh = ws.hist + (int64_t)t * kBins;
   const int32_t* cnts = (use_a ? ws.cnt_a : ws.cnt_b) + (int64_t)t * G;
-  const int64_t seg_stride = use_a ? kSlice : kSegB;
+  const int64_t seg_stride = use_a ? kSlice : ws.seg_b;
   const int32_t* lids = (use_a ? ws.ids_a : ws.ids_b) + (int64_t)t * G * seg_stride;
   const uint32_t* lkeys = (use_a ? ws.keys_a : ws.keys_b) + (int64_t)t * G * seg_stride;
   const int want = role == 0 ? M - 1 : K;
@@ -892,6 +944,30 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
     cnt = block_select([&](int i) { return r.item_key(i); }, r.items(), M - 1, sh.s, sh.sel);
   } else if (cand) {
     cnt = block_select([&](int i) { return r.item_key(i); }, r.items(), K, sh.s, sh.sel);
+  } else if constexpr (kRescore) {
+    // list B is longer than the LDS list (massive ties): select straight from its segments
+    // in global memory (list position i lies in the segment whose offset range holds it),
+    // then turn the chosen positions into entry ids
+    auto seg_of = [&](int i) {
+      int lo = 0, hi = G;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sh.seg_off[mid] <= i) lo = mid;
+        else hi = mid;
+      }
+      return lo;
+    };
+    cnt = block_select(
+        [&](int i) {
+          const int sg = seg_of(i);
+          return lkeys[(int64_t)sg * seg_stride + (i - sh.seg_off[sg])];
+        },
+        total, K, sh.s, sh.sel);
+    __syncthreads();
+    for (int i = tid; i < cnt; i += kFThreads) {
+      const int p = sh.sel[i], sg = seg_of(p);
+      sh.sel[i] = lids[(int64_t)sg * seg_stride + (p - sh.seg_off[sg])];
+    }
   } else {
     cnt = block_select([&](int j) { return r.entry_key(j); }, r.n, K, sh.s, sh.sel);
   }
@@ -917,11 +993,11 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
 }
 
 struct Layout {
-  int32_t G;
+  int32_t G, seg_b;
   size_t hist, cnt_a, cnt_b, ids_a, keys_a, ids_b, keys_b, bm, total;  // byte offsets
 };
 
-Layout make_layout(int32_t n_q, int32_t width, int32_t M, bool cand) {
+Layout make_layout(int32_t n_q, int32_t width, int32_t M, bool cand, bool rescore = false) {
   Layout L;
   const int64_t nbw = (width + kBlock - 1) / kBlock;
   const int64_t items = cand ? 8LL * M : nbw;
@@ -934,8 +1010,9 @@ Layout make_layout(int32_t n_q, int32_t width, int32_t M, bool cand) {
   L.ids_a = L.cnt_b + nq * G * 4;
   L.keys_a = L.ids_a + nq * G * kSlice * 4;
   L.ids_b = L.keys_a + nq * G * kSlice * 4;
-  L.keys_b = L.ids_b + (cand ? 0 : nq * G * kSegB * 4);
-  L.bm = L.keys_b + (cand ? 0 : nq * G * kSegB * 4);
+  L.seg_b = rescore ? kSlice * kBlock : kSegB;
+  L.keys_b = L.ids_b + (cand ? 0 : nq * G * L.seg_b * 4);
+  L.bm = L.keys_b + (cand ? 0 : nq * G * L.seg_b * 4);
   L.total = L.bm + (cand ? 0 : nq * (size_t)nbw * 4);
   return L;
 }
@@ -988,11 +1065,12 @@ int block_topk_check(const float* scores, const float* block_max, int32_t n_q, i
 // cleared first).
 int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, int32_t width, const int32_t* q_nvis,
                       const int32_t* pool_blocks, int32_t M, int32_t K, int32_t* pool_out, int32_t* topk_out,
-                      void* workspace, size_t ws_bytes, bool clear_hist, void* stream) {
+                      void* workspace, size_t ws_bytes, bool clear_hist, void* stream,
+                      const Rescore* rsc = nullptr) {
   const bool cand = pool_blocks != nullptr;
   const bool want_topk = topk_out != nullptr;
   if (reinterpret_cast<uintptr_t>(workspace) & 3) return CSA2_ERR_INVALID_ARG;
-  const Layout L = make_layout(n_q, width, M, cand);
+  const Layout L = make_layout(n_q, width, M, cand, rsc != nullptr);
   if (!workspace || ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
   char* w = (char*)workspace;
   Ws ws;
@@ -1005,6 +1083,8 @@ int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, 
   ws.keys_b = (uint32_t*)(w + L.keys_b);
   ws.bm = cand ? nullptr : (float*)(w + L.bm);
   ws.G = L.G;
+  ws.seg_b = L.seg_b;
+  const Rescore rs = rsc ? *rsc : Rescore{nullptr, nullptr, nullptr, nullptr};
   const float* bm = block_max ? block_max : ws.bm;
   const bool want_pool = pool_out != nullptr;
   hipStream_t s = (hipStream_t)stream;
@@ -1026,16 +1106,22 @@ int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, 
   if (st != CSA2_OK) return st;
   if (cand)
     hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(L.G, n_q), dim3(kGThreads), 0, s, want_pool, want_topk, scores,
-                       bm, width, q_nvis, pool_blocks, M, K, ws);
+                       bm, width, q_nvis, pool_blocks, M, K, ws, rs);
+  else if (rsc)
+    hipLaunchKernelGGL((topk_collect_kernel<false, true>), dim3(L.G, n_q), dim3(kGThreads), 0, s, want_pool, want_topk,
+                       scores, bm, width, q_nvis, pool_blocks, M, K, ws, rs);
   else
     hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(L.G, n_q), dim3(kGThreads), 0, s, want_pool, want_topk, scores,
-                       bm, width, q_nvis, pool_blocks, M, K, ws);
+                       bm, width, q_nvis, pool_blocks, M, K, ws, rs);
   st = check_launch();
   if (st != CSA2_OK) return st;
   const dim3 gf((!cand && want_pool && want_topk) ? 2 : 1, n_q);
   if (cand)
     hipLaunchKernelGGL(topk_final_kernel<true>, gf, dim3(kFThreads), 0, s, want_pool, want_topk, scores, bm, width,
                        q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
+  else if (rsc)
+    hipLaunchKernelGGL((topk_final_kernel<false, true>), gf, dim3(kFThreads), 0, s, want_pool, want_topk, scores, bm,
+                       width, q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
   else
     hipLaunchKernelGGL(topk_final_kernel<false>, gf, dim3(kFThreads), 0, s, want_pool, want_topk, scores, bm, width,
                        q_nvis, pool_blocks, M, K, ws, pool_out, topk_out);
@@ -1054,6 +1140,34 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   if (st != csa2::kProceed) return st;
   return csa2::block_topk_launch(scores, block_max, n_q, width, q_nvis, pool_blocks, M, K, pool_out, topk_out,
                                  workspace, ws_bytes, false, stream);
+}
+
+extern "C" size_t csa2_block_topk_rescore_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K) {
+  (void)K;
+  if (n_q <= 0 || width < 0 || M < 1) return 0;
+  return csa2::make_layout(n_q, width, M, false, true).total;
+}
+
+extern "C" int csa2_block_topk_rescore(const float* block_max, int32_t n_q, int32_t width, const int32_t* q_nvis,
+                                       const uint16_t* q_idx_bf16, const float* head_w, const uint8_t* idx_cache,
+                                       const int64_t* q_base, int32_t M, int32_t K, int32_t* pool_out,
+                                       int32_t* topk_out, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csa2;
+  if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
+  if (M < 1 || M > kMaxPool || K < 1 || K > kMaxTopK) return CSA2_ERR_UNSUPPORTED;
+  if (n_q == 0) return CSA2_OK;
+  if (!block_max || !q_nvis || !q_idx_bf16 || !head_w || !idx_cache || !q_base || !topk_out)
+    return CSA2_ERR_INVALID_ARG;
+  if (n_q > 65535 || width > kMaxIndexWidth) return CSA2_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q_idx_bf16) | reinterpret_cast<uintptr_t>(idx_cache)) & 15)
+    return CSA2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(block_max) | reinterpret_cast<uintptr_t>(head_w) |
+       reinterpret_cast<uintptr_t>(topk_out) | reinterpret_cast<uintptr_t>(pool_out)) & 3)
+    return CSA2_ERR_INVALID_ARG;
+  if (make_layout(n_q, width, M, false, true).G > kMaxG) return CSA2_ERR_UNSUPPORTED;
+  const Rescore rsc{q_idx_bf16, head_w, idx_cache, q_base};
+  return block_topk_launch(nullptr, block_max, n_q, width, q_nvis, nullptr, M, K, pool_out, topk_out, workspace,
+                           ws_bytes, false, stream, &rsc);
 }
 
 // ------------------------------------------------------------------ allocation-free variant

@@ -48,6 +48,64 @@ constexpr int kRawBuf = 0x00020000;        // buffer descriptor word 3: raw 32-b
 // kAllSlots writes, with the same arithmetic per slot.
 enum : int { kAllSlots = 0, kOlderSlots = 1, kNewestSlots = 2 };
 
+// ---- the per-tile arithmetic of the bf16 query, in pieces that the selection's
+// re-scoring of single entries calls too (the same operations in the same order give the
+// same bits): lane (n, g) of a wave works on entry n of a 32-entry tile, dims 64g .. 64g + 63.
+
+// the query fragments of lane (n, g) (head n, dims 64g .. 64g + 63: eight bf16x8 A fragments)
+// and the head weights of the accumulator rows it holds (row 8(r/4) + 4g + r%4)
+__device__ __forceinline__ void load_query_bf16(const uint16_t* __restrict__ q, const float* __restrict__ head_w,
+                                                int t, int n, int g, bf16x8 (&a)[8], float (&wr)[16]) {
+  const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
+#pragma unroll
+  for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
+  typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+  const f32x4_a4* wp = reinterpret_cast<const f32x4_a4*>(head_w + (int64_t)t * kIdxHeads);
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const f32x4_a4 v = wp[2 * c + g];  // rows 8c + 4g .. 8c + 4g + 3
+#pragma unroll
+    for (int r = 0; r < 4; r++) wr[4 * c + r] = v[r];
+  }
+}
+
+// lane (n, g)'s share of one indexer row at byte offset off of the buffer (32 payload bytes
+// and the scale word; an offset past the buffer's end reads zeros)
+__device__ __forceinline__ void load_row_share(__amdgpu_buffer_rsrc_t rs, int32_t off, int g, RawTile& r) {
+  r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g, 0, 0));
+  r.hi = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g + 16, 0, 0));
+  r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 64, 0, 0);
+}
+
+// q . k for the tile on v_mfma_f32_32x32x16_bf16: the entry's FP4 codes become exact bf16
+// B fragments with their E8M0 scale (v_cvt_scalef32_pk_bf16_fp4)
+__device__ __forceinline__ f32x16 mfma_bf16_tile(const bf16x8 (&a)[8], const RawTile& cur, int g) {
+  f32x16 acc = {};
+  const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
+  const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
+  const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3], cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    const bf16x8 b = cvt_fp4x8(words[s], s < 4 ? x0 : x1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// ReLU, head weight and the sum over the 32 heads of the tile's accumulators (four short
+// chains over this lane's 16 heads, then the other lane half's): both halves of the wave
+// end with entry n's score, or -inf for an invalid slot
+__device__ __forceinline__ float head_sum(const f32x16& acc, const float (&wr)[16], bool valid) {
+  float part[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    part[c] = wr[4 * c] * relu(acc[4 * c]);
+#pragma unroll
+    for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], relu(acc[4 * c + r]), part[c]);
+  }
+  return masked_score(sum_halves((part[0] + part[1]) + (part[2] + part[3])), valid);
+}
+
 // kPool: Reindex layers score their candidate pool (entry j of slot p is block
 // pool_blocks[p / 8] * 8 + p % 8); Full layers score entries 0 .. width-1 directly.
 // kFp4Q: the indexer query arrives in MXFP4 (each head vector a 68-byte record like an
@@ -57,7 +115,8 @@ enum : int { kAllSlots = 0, kOlderSlots = 1, kNewestSlots = 2 };
 // kMeans: the rows scored are HISA's block means (one per 8 entries); q_nvis counts
 // entries and the row's visible means are ceil(q_nvis[t] / 8).
 // The wave is tile `first` of the grid-stride order with stride `tstride` (wave-uniform).
-template <bool kPool, bool kFp4Q, int kPart, bool kMeans = false>
+// kScores = false leaves the score row unwritten (block maxima only; scores may be NULL).
+template <bool kPool, bool kFp4Q, int kPart, bool kMeans = false, bool kScores = true>
 __device__ __forceinline__ void score_tiles(
     const void* __restrict__ q_in, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
@@ -95,7 +154,7 @@ __device__ __forceinline__ void score_tiles(
   if (nvis <= 0) {  // nothing visible: the row is all -inf
     for (int32_t k = 0; k < nt; k++) {
       const int32_t p = tile_of(k) * kTile + n;  // (nothing visible: no newest tile)
-      if (g == 0 && p < width) srow[p] = -__builtin_inff();
+      if (kScores && g == 0 && p < width) srow[p] = -__builtin_inff();
       if (block_max != nullptr && g == 0 && (n & 7) == 0 && p < width)
         block_max[(int64_t)t * nbw + (p >> 3)] = -__builtin_inff();
     }
@@ -151,9 +210,7 @@ __device__ __forceinline__ void score_tiles(
       fresh = tile_of(k) * kTile + n == nvis - 1;
       if (fresh) off = kOut;
     }
-    r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, off + 32 * g, 0, 0));
-    r.hi = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, off + 32 * g + 16, 0, 0));
-    r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs_cache, off + 64, 0, 0);
+    load_row_share(rs_cache, off, g, r);
     if constexpr (kPart == kNewestSlots) {
       if (fresh) {
         r.lo = *reinterpret_cast<const u32x4_a4*>(fresh_row + 32 * g);
@@ -163,35 +220,20 @@ __device__ __forceinline__ void score_tiles(
     }
   };
   auto process = [&](const RawTile& cur, int32_t k) {
-    f32x16 acc = {};
+    f32x16 acc;
     if constexpr (kFp4Q) {
-      acc = mfma_fp4_tile(qa, qsc, cur.lo, cur.hi, cur.sc >> (16 * g), acc);
+      acc = mfma_fp4_tile(qa, qsc, cur.lo, cur.hi, cur.sc >> (16 * g), f32x16{});
     } else {
-      const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
-      const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
-      const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3],
-                                 cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
-#pragma unroll
-      for (int s = 0; s < 8; s++) {
-        const bf16x8 b = cvt_fp4x8(words[s], s < 4 ? x0 : x1);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
-      }
+      acc = mfma_bf16_tile(a, cur, g);
     }
-    // ReLU, head weight and the sum over this lane's 16 heads as four short chains
-    float part[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      part[c] = wr[4 * c] * relu(acc[4 * c]);
-#pragma unroll
-      for (int r = 1; r < 4; r++) part[c] = __builtin_fmaf(wr[4 * c + r], relu(acc[4 * c + r]), part[c]);
-    }
-    const float sc = masked_score(sum_halves((part[0] + part[1]) + (part[2] + part[3])), cur.valid);
+    const float sc = head_sum(acc, wr, cur.valid);
     // both lane halves hold the entry's score and all 8 lanes of a block its maximum; one
     // lane writes each value and the others aim past the buffer's end, so their stores
     // are dropped without a branch (as are slots past the row's end)
     const int32_t p = tile_of(k) * kTile + n;
     const bool drop = dead(k);  // wave-uniform
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, (g || drop) ? kOut : 4 * p, 0, 0);
+    if constexpr (kScores)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, (g || drop) ? kOut : 4 * p, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax,
                                           ((g | (n & 7)) || drop) ? kOut : 4 * (p >> 3), 0, 0);
   };
@@ -206,19 +248,16 @@ __device__ __forceinline__ void score_tiles(
       load_fp4_query(q_rec != nullptr ? q_rec + n * kIdxBytes
                                       : static_cast<const uint8_t*>(q_in) + ((int64_t)t * kIdxHeads + n) * kIdxBytes,
                      g, qa, qsc);
+      typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+      const f32x4_a4* wp = reinterpret_cast<const f32x4_a4*>(head_w + (int64_t)t * kIdxHeads);
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const f32x4_a4 v = wp[2 * c + g];  // rows 8c + 4g .. 8c + 4g + 3
+#pragma unroll
+        for (int r = 0; r < 4; r++) wr[4 * c + r] = v[r];
+      }
     } else {
-      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_in) +
-                                                       ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
-#pragma unroll
-      for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
-    }
-    typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-    const f32x4_a4* wp = reinterpret_cast<const f32x4_a4*>(head_w + (int64_t)t * kIdxHeads);
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const f32x4_a4 v = wp[2 * c + g];  // rows 8c + 4g .. 8c + 4g + 3
-#pragma unroll
-      for (int r = 0; r < 4; r++) wr[4 * c + r] = v[r];
+      load_query_bf16(static_cast<const uint16_t*>(q_in), head_w, t, n, g, a, wr);
     }
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -60,7 +60,7 @@ enum {
   CSA2_ERR_SCRATCH = -5      /* larger than the fixed scratch array of a _noalloc call */
 };
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 int csa2_abi_version(void);
 const char *csa2_status_string(int status);
@@ -194,7 +194,10 @@ int csa2_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8
  *   distinct rows.  A query with q_nvis[t] <= 0 appends nothing and gets an all -inf row.
  *   q_idx_bf16, head_w, q_base, q_nvis, width, scores and block_max are those of
  *   csa2_index_score in Full mode (no pool), with the same results bit for bit; the
- *   cache bytes are those of csa2_compress_append.
+ *   cache bytes are those of csa2_compress_append.  scores may be NULL when block_max is
+ *   given: the block maxima alone are written, and csa2_block_topk_rescore selects from them
+ *   by re-scoring the few entries it needs (no score row crosses HBM; at the 1M-context
+ *   batch-4 decode this saves 0.9 us of the scan and costs about 2 us of selection).
  *   Errors: INVALID_ARG (NULL required pointer, n_q < 0, width <= 0 with n_q > 0,
  *   misalignment, per_token_w not 0 or 1), UNSUPPORTED (m not 1 or 2, n_q > 65535,
  *   width > 2^23).
@@ -209,7 +212,8 @@ int csa2_append_index_score(const uint16_t *latent_bf16, int m, const float *poo
 /*
  * csa2_append_index_score_fp4q -- csa2_append_index_score with the indexer query in MXFP4
  *   (q_fp4 [n_q, 32, 68], 4-byte aligned, from csa2_quantize_q_mxfp4): the scores of
- *   csa2_index_score_fp4q.  Every other argument, result and error as above.
+ *   csa2_index_score_fp4q.  Every other argument, result and error as above, except that
+ *   scores is required.
  */
 int csa2_append_index_score_fp4q(const uint16_t *latent_bf16, int m, const float *pool_w, int per_token_w,
                                  const float *rope_cs, const uint16_t *w_idx_bf16, uint8_t *kv_cache,
@@ -265,6 +269,33 @@ int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, in
                     const int32_t *q_nvis, const int32_t *pool_blocks, int32_t block,
                     int32_t M, int32_t K, int32_t *pool_out, int32_t *topk_out,
                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * csa2_block_topk_rescore -- csa2_block_topk in Full mode without a score row: the
+ *   selection of [ZB] §2.3.4 / [DF] §4.7 over the scores s(t, j) of [ZB] §3.3.2, from the
+ *   block maxima that csa2_append_index_score (scores = NULL) or csa2_index_score wrote.
+ *   The pool needs only the maxima; the Top-K needs the scores of the entries of the
+ *   candidate blocks (those whose maximum reaches the histogram bin of the K-th largest
+ *   older-block maximum, and the newest block), and these few are computed again from
+ *   the indexer cache with the scan's own tile arithmetic, bit for bit the scores
+ *   csa2_index_score would have written.  Results: those of csa2_block_topk given that
+ *   score row, bit for bit.
+ *   block_max fp32 [n_q, ceil(width/8)] (4-byte aligned); q_nvis, width as csa2_block_topk;
+ *   q_idx_bf16 [n_q, 32, 128] (16-byte aligned), head_w fp32 [n_q, 32], idx_cache
+ *   [rows, 68] (16-byte aligned) and q_base [n_q]: the scan's inputs (query t's entry j at
+ *   row q_base[t] + j); M, K, pool_out (NULL: no pool), topk_out (required) as
+ *   csa2_block_topk.  workspace: csa2_block_topk_rescore_workspace(n_q, width, M, K) bytes,
+ *   4-byte aligned, histogram region zero before the first call and left zero by every
+ *   call, as csa2_block_topk's (a 1M-context batch of 4 needs 21 MB: each K2 workgroup's
+ *   list segment holds every entry of its slice, so no list overflows).
+ *   Errors: INVALID_ARG (NULL required pointer, misalignment), UNSUPPORTED (M, K out of
+ *   range, width > 2^23, n_q > 65535), WORKSPACE.
+ */
+size_t csa2_block_topk_rescore_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K);
+int csa2_block_topk_rescore(const float *block_max, int32_t n_q, int32_t width, const int32_t *q_nvis,
+                            const uint16_t *q_idx_bf16, const float *head_w, const uint8_t *idx_cache,
+                            const int64_t *q_base, int32_t M, int32_t K, int32_t *pool_out, int32_t *topk_out,
+                            void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * csa2_block_topk_noalloc -- csa2_block_topk that allocates nothing and takes no workspace,

@@ -40,7 +40,7 @@ def test_binding_names_match_header():
 
 def test_version_and_status_strings(lib):
     lib.csa2_status_string.restype = ctypes.c_char_p
-    assert lib.csa2_abi_version() == 2
+    assert lib.csa2_abi_version() == 3
     for st in (0, -1, -2, -3, -4):
         assert lib.csa2_status_string(st)
 
@@ -90,6 +90,39 @@ def test_fp8_window_entry_points_validate_before_launch(lib):
     assert attn(fake, fake, fake, fake, 512, ctypes.c_void_p((1 << 20) + 4), 0, fake, fake, 0.04, fake, None, 1,
                 None, 0, None) == -1
     assert attn(fake, fake, fake, fake, 512, fake, 128, fake, fake, 0.04, fake, None, 1, None, 0, None) == -3
+
+
+def test_rescore_selection_and_maxima_only_scan_validate_before_launch(lib):
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    f = lib.csa2_block_topk_rescore
+    f.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.csa2_block_topk_rescore_workspace.argtypes = [i32, i32, i32, i32]
+    lib.csa2_block_topk_rescore_workspace.restype = sz
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    need = lib.csa2_block_topk_rescore_workspace(4, 1 << 19, 2048, 512)
+    # every list-B segment holds its whole slice: 64 workgroups x 8192 slots x 8 B per query
+    assert need >= 4 * 64 * 8192 * 8
+    assert need > lib.csa2_block_topk_rescore_workspace(1, 1 << 19, 2048, 512)
+    args = [fake, 4, 1 << 19, fake, fake, fake, fake, fake, 2048, 512, fake, fake, fake, need, None]
+    assert f(*args[:13], 16, None) == -3  # workspace too small
+    assert f(*[None] + args[1:]) == -1  # block_max missing
+    assert f(*args[:4], None, *args[5:]) == -1  # query missing
+    assert f(*args[:11], None, *args[12:]) == -1  # topk_out required
+    assert f(*args[:4], odd, *args[5:]) == -1  # q not 16-B aligned
+    assert f(*args[:6], odd, *args[7:]) == -1  # idx_cache not 16-B aligned
+    assert f(*args[:8], 4096, *args[9:]) == -2  # M > 2048
+    assert f(*args[:9], 513, *args[10:]) == -2  # K > 512
+    assert f(*args[:2], (1 << 23) + 8, *args[3:]) == -2  # rows longer than 2^23 entries
+    assert f(None, 0, 0, None, None, None, None, None, 2048, 512, None, None, None, 0, None) == 0  # nothing to do
+    # the fused scan: scores may be NULL only with the bf16 query and the block maxima
+    for name in ("csa2_append_index_score", "csa2_append_index_score_fp4q", "csa2_append_index_score_packq"):
+        g = getattr(lib, name)
+        g.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp]
+        a = [fake, 2, fake, 0, fake, fake, fake, fake, fake, fake, fake, fake, 4, 1 << 19]
+        assert g(*a, None, None, None) == -1, name  # neither scores nor block maxima
+        if name != "csa2_append_index_score":
+            assert g(*a, None, fake, None) == -1, name  # the MXFP4-query scans write scores
 
 
 def test_compress_append_validates_before_launch(lib):
@@ -161,7 +194,9 @@ def test_append_index_entry_points_validate_before_launch(lib):
         assert call(n_q=-1) == -1
         assert call(m=3) == -2
         assert call(width=0) == -1
-        assert call(scores=None) == -1
+        assert call(scores=None, bmax=None) == -1
+        if name != "csa2_append_index_score":  # only the bf16-query scan may write block maxima alone
+            assert call(scores=None) == -1
         assert call(pool_w=None) == -1
         assert call(n_q=70000) == -2
         assert call(width=(1 << 23) + 1) == -2
