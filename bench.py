@@ -432,7 +432,7 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
     return res
 
 
-def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=3):
+def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=10):
     """The chunked-prefill workload, one launch per stage timed with HIP events: compress the
     chunk's 2048 new entries from latents, causal scoring of 4096 queries over <= 34816
     entries, per-query Top-512, attention for every query.  The history caches are drawn
