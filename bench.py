@@ -407,6 +407,28 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
            "layers": "Full" + (f" + Reindex + {extra_layers - 1} Reuse" if extra_layers else ""),
            "window": "FP8 rings (append + attend)" if fp8_window else "bf16",
            "indexer_query": "MXFP4 (packed inside the fused launch)" if fp4q else "bf16"}
+    if extra_layers:
+        # each stage of the step alone: HIP events around graphs of back-to-back launches
+        names = {FUSED: "append_index_score", 2: "block_topk", 3: "sparse_attn_full", 4: "reindex_index_score",
+                 5: "reindex_block_topk", 6: "sparse_attn_reindex"}
+        res["stages_us"] = {}
+        for st in wl.step_stages:
+            reps = 4 * NCOPY
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for r in range(reps):
+                    wl.run_stage(r % NCOPY, st)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(3):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            res["stages_us"][names.get(st, f"sparse_attn_reuse{st - 6}")] = round(a.elapsed_time(b) * 1e3 / (3 * reps),
+                                                                                  2)
+            del g
     if not hisa and not fp8_window:
         # the whole step against the HBM roofline: Full scan, Reindex pool, every attention layer
         nbytes = step_bytes(n_seq, wl.n, reindex_pool=8 * wl.M if extra_layers else 0, attn_layers=1 + extra_layers)

@@ -10,11 +10,14 @@
  * General contract
  *   - Tensor pointers are DEVICE pointers owned by the caller unless a parameter says
  *     "host".  Arrays are dense and row-major.  bf16 values travel as uint16 bit
- *     patterns.  The library never allocates, frees or synchronises device memory.  Its
- *     only host-side global state is a per-device cache of occupancy figures (how many
- *     workgroups of a kernel fit on the device), held in atomics and written with the same
- *     value by whichever call computes it first; calls on different streams and host
- *     threads are independent.
+ *     patterns.  The library never allocates, frees or synchronises device memory at run
+ *     time.  Its global state: on each GPU, the fixed 32 MiB scratch array of
+ *     csa2_block_topk_noalloc (a __device__ array that exists from library load to process
+ *     end; only that call uses it); on the host, per-device caches of occupancy figures (how
+ *     many workgroups of a kernel fit on the device) and of that array's device address,
+ *     held in atomics and written with the same value by whichever call computes them
+ *     first.  Calls on different streams and host threads are independent, except that
+ *     overlapping csa2_block_topk_noalloc calls on one GPU share its array.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call
  *     is asynchronous on it.  A kernel fault surfaces at the caller's next sync.
  *   - Return value: CSA2_OK (0) or a negative status.  Argument errors are detected on
