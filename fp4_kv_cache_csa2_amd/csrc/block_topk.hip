@@ -30,7 +30,7 @@
 //               The list-A roles read K1's histogram (the count above the boundary bin
 //               and the bin's own count), return it to zero, and refine only the boundary
 //               bin's low 20 bits; the list-B role starts below the common leading bits of
-//               its keys.  Keys are held in registers (one barrier per 8-bit radix
+//               its keys.  Keys are held in registers (one barrier per 10-bit radix
 //               pass).  If a list overflows LDS (massive ties), K3
 //               selects straight from the full row instead, with the same exact rules.
 // The histogram region of the workspace must be zero before the first call; every call
@@ -238,8 +238,12 @@ constexpr int kPer = kListCap / kFThreads;  // list keys per K3 thread, held in 
 constexpr int kBinsPer = kBins / kFThreads; // histogram bins per K3 thread
 constexpr int kSegPer = kMaxG / kFThreads;  // K2 segments per K3 thread
 
+constexpr int kLDigit = 10;                 // bits resolved per radix pass of the list selection
+constexpr int kLBins = 1 << kLDigit;         // its digit histogram
+constexpr int kLPerLane = kLBins / 64;       // bins per lane of the wave that scans it
+
 struct ListScratch {
-  uint32_t hist[3][256];  // digit histograms, rotated so no pass waits to clear one
+  uint32_t hist[3][kLBins] __attribute__((aligned(16)));  // digit histograms, rotated so no pass waits to clear one
   int32_t wcnt[2][kFWaves];
   uint32_t red[3][kFWaves];
   int32_t dec[4];  // a pass's decision: digit (-1: take every matching key), remain, eq_total, total
@@ -267,9 +271,9 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
   remain = __builtin_amdgcn_readfirstlane(remain);
   eq_total = __builtin_amdgcn_readfirstlane(eq_total);
   n = __builtin_amdgcn_readfirstlane(n);
-  if (tid < 256) {
-    s.hist[0][tid] = 0u;
-    s.hist[1][tid] = 0u;
+  for (int b = tid; b < kLBins; b += kFThreads) {
+    s.hist[0][b] = 0u;
+    s.hist[1][b] = 0u;
   }
   const int seg = (n + kFWaves - 1) / kFWaves;
   const int lo = min(n, wave * seg);
@@ -326,10 +330,10 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
   }
   __syncthreads();
   for (int p = 0; shift > 0 && (eq_total < 0 || remain < eq_total); p++) {
-    const int nshift = max(shift - 8, 0);
+    const int nshift = max(shift - kLDigit, 0);
     const uint32_t dmask = (1u << (shift - nshift)) - 1u;
     uint32_t* h = s.hist[p % 3];
-    if (tid < 256) s.hist[(p + 1) % 3][tid] = 0u;  // last read two passes ago
+    for (int b = tid; b < kLBins; b += kFThreads) s.hist[(p + 1) % 3][b] = 0u;  // last read two passes ago
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
       if (64 * j >= len) continue;  // uniform: the wave's remaining slots are empty
@@ -338,25 +342,34 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
     }
     __syncthreads();
     if (wave == 0) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      uint32_t c[4], local = 0;
+      // lane l owns the kLPerLane digits below kLBins - kLPerLane * l (descending), read as
+      // 16-byte words: once for their sum, once for the search (fewer live registers)
+      const int hi_bin = kLBins - 1 - kLPerLane * lane;
+      const uint4* hw = reinterpret_cast<const uint4*>(h + hi_bin + 1 - kLPerLane);
+      uint32_t local = 0;
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        c[q] = h[255 - 4 * lane - q];
-        local += c[q];
+      for (int v = 0; v < kLPerLane / 4; v++) {
+        const uint4 w4 = hw[v];
+        local += (w4.x + w4.y) + (w4.z + w4.w);
       }
       const uint32_t incl = wave_incl_scan(local);
       const int total = __builtin_amdgcn_readlane((int)incl, 63);
       uint32_t above = incl - local;
       int hit = -1, hit_rem = 0, hit_cnt = 0;
+      asm volatile("" ::: "memory");  // read the words again below instead of keeping them
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        if ((int)above < remain && remain <= (int)(above + c[q])) {
-          hit = 255 - 4 * lane - q;
-          hit_rem = remain - (int)above;
-          hit_cnt = (int)c[q];
+      for (int v = kLPerLane / 4 - 1; v >= 0; v--) {  // descending digits: word v from its top
+        const uint4 w4 = hw[v];
+        const uint32_t cw[4] = {w4.w, w4.z, w4.y, w4.x};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          if ((int)above < remain && remain <= (int)(above + cw[e])) {
+            hit = hi_bin + 1 - kLPerLane + 4 * v + 3 - e;
+            hit_rem = remain - (int)above;
+            hit_cnt = (int)cw[e];
+          }
+          above += cw[e];
         }
-        above += c[q];
       }
       const uint64_t hb = __ballot(hit >= 0);
       const int src = hb == 0ull ? 0 : __ffsll((unsigned long long)hb) - 1;
