@@ -262,8 +262,11 @@ struct ListScratch {
 // is a burst of LDS atomics, a barrier, wave 0's scan of the 256 digit counts and a
 // second barrier that hands its decision to every wave (sixteen waves repeating the scan
 // would queue four deep on each SIMD).
-__device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t prefix, uint32_t mask, int shift,
-                                           int remain, int eq_total, ListScratch& s, int32_t* out, uint32_t* thr) {
+// The same selection with the keys given by key_of(i) (any source: LDS, or global memory
+// read straight into registers) and up to kP keys per thread (n <= kP * 1024).
+template <int kP, class KeyFn>
+__device__ __forceinline__ int list_select_g(KeyFn key_of, int n, uint32_t prefix, uint32_t mask, int shift,
+                                             int remain, int eq_total, ListScratch& s, int32_t* out, uint32_t* thr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   prefix = __builtin_amdgcn_readfirstlane(prefix);
   mask = __builtin_amdgcn_readfirstlane(mask);
@@ -283,14 +286,14 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
     __syncthreads();
     return 0;
   }
-  uint32_t kr[kPer];
+  uint32_t kr[kP];
 #pragma unroll
-  for (int j = 0; j < kPer; j++) kr[j] = (64 * j + lane < len) ? keys[lo + 64 * j + lane] : 0u;
+  for (int j = 0; j < kP; j++) kr[j] = (64 * j + lane < len) ? key_of(lo + 64 * j + lane) : 0u;
   if (mask == 0u) {
     // smallest and largest non-zero key, and their count
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, cnt = 0u;
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
+    for (int j = 0; j < kP; j++) {
       if (64 * j >= len) continue;
       const uint32_t key = kr[j];
       kmin = min(kmin, key != 0u ? key : 0xFFFFFFFFu);
@@ -335,7 +338,7 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
     uint32_t* h = s.hist[p % 3];
     for (int b = tid; b < kLBins; b += kFThreads) s.hist[(p + 1) % 3][b] = 0u;  // last read two passes ago
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
+    for (int j = 0; j < kP; j++) {
       if (64 * j >= len) continue;  // uniform: the wave's remaining slots are empty
       const uint32_t key = kr[j];
       if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> nshift) & dmask], 1u);
@@ -404,7 +407,7 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int gt = 0, eq = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; j++) {
+  for (int j = 0; j < kP; j++) {
     if (64 * j >= len) continue;
     const uint32_t key = kr[j];
     gt += __popcll(__ballot(key != 0u && (key & mask) > prefix));
@@ -425,7 +428,7 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
   int run_eq = __builtin_amdgcn_readlane((int)e_before, wave);
   int run_sel = __builtin_amdgcn_readlane((int)(s_incl - s_l), wave);
 #pragma unroll
-  for (int j = 0; j < kPer; j++) {
+  for (int j = 0; j < kP; j++) {
     if (64 * j >= len) continue;
     const uint32_t key = kr[j];
     const bool is_eq = key != 0u && (key & mask) == prefix;
@@ -439,6 +442,12 @@ __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t
   }
   __syncthreads();
   return total_sel;
+}
+
+// list_select_g over keys held in LDS (the finalize's gathered list)
+__device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t prefix, uint32_t mask, int shift,
+                                           int remain, int eq_total, ListScratch& s, int32_t* out, uint32_t* thr) {
+  return list_select_g<kPer>([&](int i) { return keys[i]; }, n, prefix, mask, shift, remain, eq_total, s, out, thr);
 }
 
 // Per-query view of the selection problem shared by the three kernels.
@@ -1005,6 +1014,87 @@ __global__ __launch_bounds__(kFThreads) void topk_final_kernel(
   }
 }
 
+// ------------------------------------------------------------------ one-launch path for short rows
+
+// Rows of at most 4096 ranking items (4 keys per thread) take the whole selection in one
+// launch: one 1024-thread workgroup per query and role reads the keys
+// straight from the scores (or block maxima) into registers and runs list_select_g.  The
+// pool role ranks the older blocks by their maxima (the caller's, or computed here as K1
+// does) and appends the newest block; the Top-K role ranks every visible entry in Full mode
+// (the global Top-K equals the Top-K inside the pool) or the pool's slots in candidate
+// mode.  The results are those of the three-kernel path bit for bit.  (Measured: one
+// workgroup holding 16-32 keys per thread is slower than the three launches -- the 32K-entry
+// decode step 68.5 against 51.8 us, a 16384-slot candidate pool 19.6 against 17.0 us -- while
+// the 2048-entry step gains 5 us.)
+constexpr int kSmallPer = 4;
+constexpr int kSmallMax = kSmallPer * kFThreads;  // 4096 keys
+
+struct SmallShared {
+  int32_t sel[kMaxPool];
+  ListScratch ls;
+};
+
+template <bool cand>
+__global__ __launch_bounds__(kFThreads) void topk_small_kernel(
+    bool want_pool, bool want_topk, const float* __restrict__ scores, const float* __restrict__ block_max,
+    int32_t width, const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K,
+    int32_t* __restrict__ pool_out, int32_t* __restrict__ topk_out) {
+  __shared__ SmallShared sh;
+  const int t = blockIdx.y, tid = threadIdx.x;
+  const int role = !want_topk ? 0 : ((cand || !want_pool) ? 1 : (int)blockIdx.x);
+  const Row r = make_row(t, cand, scores, block_max, width, q_nvis, pool_blocks, M, K);
+  uint32_t thr;
+  if constexpr (!cand) {  // (candidate mode has no pool role)
+  if (role == 0) {
+    // the pool: the top M-1 older blocks (every one when there are no more), ascending, then
+    // the newest block
+    const int nold = max(r.nb - 1, 0);
+    const bool take_all = nold <= M - 1;
+    int cnt = nold;
+    if (!take_all) {
+      if (block_max != nullptr) {
+        cnt = list_select_g<kSmallPer>([&](int b) { return order_key(r.bm[b]); }, nold, 0u, 0u, 32, M - 1, -1, sh.ls,
+                                       sh.sel, &thr);
+      } else {  // the block's maximum from its entries (NaN never wins, as in K1)
+        cnt = list_select_g<kSmallPer>(
+            [&](int b) {
+              float v[kBlock];
+#pragma unroll
+              for (int o = 0; o < kBlock; o++) v[o] = r.scores[b * kBlock + o];  // older blocks are whole
+              float mx = -__builtin_inff();
+#pragma unroll
+              for (int o = 0; o < kBlock; o++) mx = v[o] > mx ? v[o] : mx;
+              return order_key(mx);
+            },
+            nold, 0u, 0u, 32, M - 1, -1, sh.ls, sh.sel, &thr);
+      }
+    }
+    int32_t* po = pool_out + (int64_t)t * M;
+    const int npool = r.nb > 0 ? cnt + 1 : 0;
+    for (int i = tid; i < M; i += kFThreads) {
+      int32_t v = -1;
+      if (i < cnt) v = take_all ? i : sh.sel[i];
+      else if (i == cnt && npool > 0) v = r.nb - 1;
+      po[i] = v;
+    }
+    return;
+  }
+  }
+  int cnt;
+  if constexpr (cand) {
+    cnt = list_select_g<kSmallPer>([&](int i) { return r.item_key(i); }, r.items(), 0u, 0u, 32, K, -1, sh.ls, sh.sel,
+                                   &thr);
+  } else {
+    cnt = list_select_g<kSmallPer>([&](int j) { return order_key(r.scores[j]); }, r.n, 0u, 0u, 32, K, -1, sh.ls,
+                                   sh.sel, &thr);
+  }
+  int32_t* tk = topk_out + (int64_t)t * K;
+  for (int i = tid; i < K; i += kFThreads) {
+    const int32_t p = i < cnt ? sh.sel[i] : -1;
+    tk[i] = p < 0 ? -1 : (cand ? r.pool[p >> 3] * kBlock + (p & 7) : p);
+  }
+}
+
 struct Layout {
   int32_t G, seg_b;
   size_t hist, cnt_a, cnt_b, ids_a, keys_a, ids_b, keys_b, bm, total;  // byte offsets
@@ -1065,6 +1155,9 @@ int block_topk_check(const float* scores, const float* block_max, int32_t n_q, i
   // pool-only mode (no Top-K): the pool from the caller's block scores; scores may be NULL
   if (!q_nvis || (want_topk ? !scores : (cand || !pool_out || !block_max))) return CSA2_ERR_INVALID_ARG;
   if (cand && (pool_out || block_max || (int64_t)width != 8LL * M)) return CSA2_ERR_INVALID_ARG;
+  // a Full-mode Top-K is taken as the row's global Top-K, which is the Top-K inside the pool
+  // only when the M - 1 older pool blocks' maxima alone outrank every entry outside the pool
+  if (!cand && want_topk && M - 1 < K) return CSA2_ERR_UNSUPPORTED;
   if (n_q > 65535) return CSA2_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(block_max) |
        reinterpret_cast<uintptr_t>(topk_out) | reinterpret_cast<uintptr_t>(pool_out)) & 3)
@@ -1101,6 +1194,20 @@ int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, 
   const float* bm = block_max ? block_max : ws.bm;
   const bool want_pool = pool_out != nullptr;
   hipStream_t s = (hipStream_t)stream;
+  // short rows (every key fits in one workgroup's registers): the one-launch path
+  const int64_t nbw = ((int64_t)width + kBlock - 1) / kBlock;
+  const bool small = rsc == nullptr && (cand ? 8LL * M <= kSmallMax
+                                              : (want_topk ? width <= kSmallMax : nbw - 1 <= kSmallMax));
+  if (small) {
+    const dim3 gs((!cand && want_pool && want_topk) ? 2 : 1, n_q);
+    if (cand)
+      hipLaunchKernelGGL(topk_small_kernel<true>, gs, dim3(kFThreads), 0, s, want_pool, want_topk, scores, block_max,
+                         width, q_nvis, pool_blocks, M, K, pool_out, topk_out);
+    else
+      hipLaunchKernelGGL(topk_small_kernel<false>, gs, dim3(kFThreads), 0, s, want_pool, want_topk, scores, block_max,
+                         width, q_nvis, pool_blocks, M, K, pool_out, topk_out);
+    return check_launch();
+  }
   if (clear_hist) {
     const int64_t words = (int64_t)n_q * kBins;
     hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
@@ -1167,7 +1274,7 @@ extern "C" int csa2_block_topk_rescore(const float* block_max, int32_t n_q, int3
                                        int32_t* topk_out, void* workspace, size_t ws_bytes, void* stream) {
   using namespace csa2;
   if (n_q < 0 || width < 0) return CSA2_ERR_INVALID_ARG;
-  if (M < 1 || M > kMaxPool || K < 1 || K > kMaxTopK) return CSA2_ERR_UNSUPPORTED;
+  if (M < 1 || M > kMaxPool || K < 1 || K > kMaxTopK || M - 1 < K) return CSA2_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
   if (!block_max || !q_nvis || !q_idx_bf16 || !head_w || !idx_cache || !q_base || !topk_out)
     return CSA2_ERR_INVALID_ARG;

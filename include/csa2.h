@@ -261,7 +261,10 @@ int csa2_append_index_score_packq(const uint16_t *latent_bf16, int m, const floa
  *   with the same or a smaller n_q (a larger n_q needs its larger region zeroed again).
  *   Calls that overlap in time must not share a workspace.
  *   Errors: INVALID_ARG, UNSUPPORTED (block != 8, M > 2048, K > 512, K < 1, M < 1, rows
- *   longer than 2^20 blocks), WORKSPACE (workspace missing or too small).
+ *   longer than 2^20 blocks, Full mode with a Top-K and M - 1 < K: the Top-K is computed as
+ *   the row's global Top-K, which equals the Top-K inside the pool only when the maxima of
+ *   the M - 1 older pool blocks outrank every entry outside it), WORKSPACE (workspace
+ *   missing or too small).
  */
 size_t csa2_block_topk_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K);
 /*   Pool-only mode (topk_out == NULL, Full mode): the pool alone, built from the caller's
@@ -292,7 +295,7 @@ int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, in
  *   call, as csa2_block_topk's (a 1M-context batch of 4 needs 21 MB: each K2 workgroup's
  *   list segment holds every entry of its slice, so no list overflows).
  *   Errors: INVALID_ARG (NULL required pointer, misalignment), UNSUPPORTED (M, K out of
- *   range, width > 2^23, n_q > 65535), WORKSPACE.
+ *   range or M - 1 < K, width > 2^23, n_q > 65535), WORKSPACE.
  */
 size_t csa2_block_topk_rescore_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K);
 int csa2_block_topk_rescore(const float *block_max, int32_t n_q, int32_t width, const int32_t *q_nvis,

@@ -63,6 +63,9 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.csa2_block_topk(fake, None, 1, 100, fake, None, 4, 2048, 512, None, fake, None, 0, None) == -2
     assert lib.csa2_block_topk(fake, None, 1, 100, fake, None, 8, 2048, 513, None, fake, None, 0, None) == -2
     assert lib.csa2_block_topk(fake, None, 1, 200000, fake, None, 8, 2048, 512, None, fake, None, 0, None) == -3
+    # a Full-mode Top-K needs M - 1 >= K (the global Top-K is the Top-K inside the pool only then)
+    assert lib.csa2_block_topk(fake, None, 1, 200000, fake, None, 8, 64, 64, fake, fake, fake, 1 << 30, None) == -2
+    assert lib.csa2_block_topk(fake, None, 1, 200000, fake, None, 8, 65, 64, fake, fake, None, 0, None) == -3
     assert lib.csa2_sparse_attn(fake, fake, fake, fake, 600, fake, fake, fake, 0.04, fake, None, 1,
                                 None, 0, None) == -2
     assert lib.csa2_sparse_attn(fake, fake, fake, fake, 512, fake, fake, fake, 0.04, fake, None, 1,

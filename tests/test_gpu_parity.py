@@ -170,6 +170,12 @@ def test_index_score_candidate_mode(c):
     (12345, [12345, 700, 5, 0], 100, 64, 0.1, 0, 0.01, 15),
     (200000, [200000, 150007], 2048, 512, 0.05, 0, 0.0, 16),
     (34816, [34816, 32769], 2048, 512, 0.0, 0, 0.0, 17),
+    # rows of at most 4096 entries take the one-launch path: its boundary, ties, few levels, NaN
+    (4096, [4096, 4095, 2049, 9], 2048, 512, 0.3, 0, 0.02, 18),
+    (4096, [4096, 3000], 300, 256, 0.0, 3, 0.0, 19),
+    (4097, [4097, 4096], 2048, 512, 0.0, 3, 0.0, 20),
+    (16384, [16384, 16000, 0], 65, 64, 0.0, 0, 0.0, 23),  # M - 1 = K, the smallest pool allowed
+    (3000, [3000, 100], 513, 512, 0.5, 0, 0.05, 24),
 ])
 def test_block_topk_full_mode_exact(c, width, nvis, M, K, tie, levels, nan, seed):
     log(f"block_topk full width={width} nvis={nvis} M={M} K={K}")
@@ -191,17 +197,20 @@ def test_block_topk_full_mode_exact(c, width, nvis, M, K, tie, levels, nan, seed
         assert np.array_equal(host(topk), topk_ref), "topk differs"
 
 
-def test_block_topk_candidate_mode_exact(c):
-    log("block_topk candidate mode")
-    n_q, M, K = 3, 2048, 512
+@pytest.mark.parametrize("M,levels,seed", [(2048, 0, 21), (2048, 4, 25), (512, 0, 26), (64, 2, 27)])
+def test_block_topk_candidate_mode_exact(c, M, levels, seed):
+    """Candidate mode (the Reindex layer's pool of M blocks): pools of up to 512 blocks take the
+    one-launch path, larger ones the three launches."""
+    log(f"block_topk candidate mode M={M} levels={levels}")
+    n_q, K = 3, 512
     nvis = np.array([131072, 131070, 9000], np.int32)
     pool = np.full((n_q, M), -1, np.int32)
-    rng = np.random.default_rng(21)
+    rng = np.random.default_rng(seed)
     for t in range(n_q):
         nb = -(-nvis[t] // 8)
-        k = min(M, nb)
+        k = min(M, nb) - (t == 1)  # one pool with a -1 slot
         pool[t, :k] = np.sort(rng.choice(nb, k, replace=False))
-    s = synth.random_scores(22, n_q, 8 * M, tie_frac=0.1)
+    s = synth.random_scores(seed + 1, n_q, 8 * M, tie_frac=0.1, levels=levels)
     _, topk_ref = oracle.block_topk(s, nvis, K=K, pool_blocks=pool)
     _, topk = c.block_topk(dev(s), dev(nvis), K=K, pool_blocks=dev(pool))
     torch.cuda.synchronize()

@@ -135,7 +135,7 @@ def test_decode_schedule_memory_stays_flat():
     from fp4_kv_cache_csa2_amd import schedule as gsched
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    n_seq, tokens, K, M = 2, 64, 16, 8
+    n_seq, tokens, K, M = 2, 64, 16, 17
     cap = tokens + 320
     g = gsched.GlobalBranch(n_seq, {c: cap for c in gsched.RATIO}, K=K, M=M)
     for i, c in enumerate(gsched.RATIO):
