@@ -78,8 +78,10 @@ def make_batch(csa2, torch, copy_id, n_seq, tokens, m, chunk_tokens=1 << 19, ext
     z = torch.randn((m, 512), generator=gen, device=dev, dtype=torch.float32)
     pool_w = torch.nn.functional.softplus(z).contiguous()
     w_idx = (torch.randn((128, 512), generator=gen, device=dev) / 512 ** 0.5).to(torch.bfloat16).contiguous()
+    tile = csa2.IDX_TILE_ENTRIES
+    assert n % tile == 0 and chunk_tokens % (tile * m) == 0  # sequences and chunks start indexer tiles
     kv = torch.empty((n_seq * n, 288), dtype=torch.uint8, device=dev)
-    ix = torch.empty((n_seq * n, 68), dtype=torch.uint8, device=dev)
+    ix = torch.empty((n_seq * n // tile, csa2.IDX_TILE_BYTES), dtype=torch.uint8, device=dev)
     last_lat = torch.empty((n_seq, m, 512), dtype=torch.bfloat16, device=dev)
     pos_all = np.arange(n, dtype=np.int64) * m
     cs_all = csa2.rope_table(pos_all).to(dev)
@@ -91,7 +93,7 @@ def make_batch(csa2, torch, copy_id, n_seq, tokens, m, chunk_tokens=1 << 19, ext
             xb = x.to(torch.bfloat16).contiguous()
             e0 = t0 // m
             csa2.compress_pack(xb, m, pool_w, cs_all[e0:e0 + tl // m], w_idx,
-                               kv_out=kv[s * n + e0:], idx_out=ix[s * n + e0:])
+                               kv_out=kv[s * n + e0:], idx_out=ix[(s * n + e0) // tile:])
             if t0 + tl == tokens:
                 last_lat[s] = xb[-m:]
         del x, xb
@@ -270,7 +272,8 @@ class Decode1M:
             self.s_blk = torch.empty((n_seq, self.nbw), dtype=torch.float32, device=dev)
             self.scores_c = torch.empty((n_seq, 8 * M), dtype=torch.float32, device=dev)
             for c in self.copies:
-                c["means"] = torch.empty((n_seq * self.nbw, 68), dtype=torch.uint8, device=dev)
+                c["means"] = torch.empty((csa2.idx_tiles_for(n_seq * self.nbw), csa2.IDX_TILE_BYTES),
+                                         dtype=torch.uint8, device=dev)
                 csa2.block_mean_pack(c["ix"], self.q_base, self.q_nvis, self.nbw, c["means"], self.mbase)
             torch.cuda.synchronize()
         if fp8_window:
@@ -467,8 +470,10 @@ def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=10):
     g.manual_seed(5)
     kv = torch.randint(0, 256, (n, 288), dtype=torch.uint8, device=dev, generator=g)
     kv[:, 256:] = 0x30
-    ix = torch.randint(0, 256, (n, 68), dtype=torch.uint8, device=dev, generator=g)
-    ix[:, 64:] = 126
+    assert hist % csa2.IDX_TILE_ENTRIES == 0  # the chunk's new entries start an indexer tile
+    ix = torch.randint(0, 256, (csa2.idx_tiles_for(n), csa2.IDX_TILE_BYTES), dtype=torch.uint8, device=dev,
+                       generator=g)
+    ix[:, 2048:] = 126  # every entry's four E8M0 scale bytes
     nvis = torch.from_numpy(synth.prefill_nvis(hist_tokens, chunk, m)).to(dev)
     q_idx = (torch.randn((chunk, 32, 128), device=dev, generator=g) / 128 ** 0.5).to(torch.bfloat16)
     head_w = torch.randn((chunk, 32), device=dev, generator=g) / 32 ** 0.5
@@ -491,7 +496,7 @@ def time_prefill(torch, csa2, hist_tokens=65536, chunk=4096, m=2, reps=10):
     wsa = torch.empty(max(16, csa2.sparse_attn_workspace(chunk, 512)), dtype=torch.uint8, device=dev)
     stages = {
         "compress_2048_entries": lambda: csa2.compress_pack(lat, m, pool_w, cs, w_idx, kv_out=kv[hist:],
-                                                           idx_out=ix[hist:]),
+                                                           idx_out=ix[hist // csa2.IDX_TILE_ENTRIES:]),
         "index_4096_queries": lambda: csa2.index_score(q_idx, head_w, ix, base, nvis, n, scores=scores,
                                                        want_block_max=False),
         "select_4096_queries": lambda: csa2.block_topk(scores, nvis, want_pool=False, topk_out=topk, workspace=ws),

@@ -173,9 +173,25 @@ def _cache(t, name, row_bytes):
     _dev(t, torch.uint8, name, (None, row_bytes))
 
 
+# The indexer-K cache (and HISA's block-mean cache) is a tensor of tiles: uint8 [n_tiles, 2176],
+# 32 entries per tile (include/csa2.h gives the byte layout); entry j lives in tile j // 32.
+IDX_TILE_ENTRIES = 32
+IDX_TILE_BYTES = 2176
+
+
+def idx_tiles_for(n_entries: int) -> int:
+    """Tiles an indexer-K cache needs to hold entries 0 .. n_entries - 1."""
+    return (n_entries + IDX_TILE_ENTRIES - 1) // IDX_TILE_ENTRIES
+
+
+def _idx_cache(t, name):
+    _cache(t, name, IDX_TILE_BYTES)
+
+
 def compress_pack(latent, m: int, pool_w, rope_cs, w_idx, kv_out=None, idx_out=None, stream=None):
-    """latent bf16 [n*m, 512] -> (kv uint8 [n, 288], idx uint8 [n, 68]); outputs may be given
-    (at least n rows).  pool_w: fp32 [m, 512], or [n*m, 512] for one weight row per token."""
+    """latent bf16 [n*m, 512] -> (kv uint8 [n, 288], idx uint8 [idx_tiles_for(n), 2176]); outputs
+    may be given (room for at least n entries).  pool_w: fp32 [m, 512], or [n*m, 512] for one
+    weight row per token."""
     n = _latent_rows(latent, m)
     per_token = _pool_weights(pool_w, m, n * m)
     _dev(rope_cs, torch.float32, "rope_cs", (None, 64))
@@ -184,11 +200,11 @@ def compress_pack(latent, m: int, pool_w, rope_cs, w_idx, kv_out=None, idx_out=N
         if kv_out is None:
             kv_out = torch.empty((n, 288), dtype=torch.uint8, device=latent.device)
         if idx_out is None:
-            idx_out = torch.empty((n, 68), dtype=torch.uint8, device=latent.device)
+            idx_out = torch.empty((idx_tiles_for(n), IDX_TILE_BYTES), dtype=torch.uint8, device=latent.device)
     _cache(kv_out, "kv_out", 288)
-    _cache(idx_out, "idx_out", 68)
-    if rope_cs.shape[0] < n or kv_out.shape[0] < n or idx_out.shape[0] < n:
-        raise ValueError("rope_cs, kv_out and idx_out need a row per entry")
+    _idx_cache(idx_out, "idx_out")
+    if rope_cs.shape[0] < n or kv_out.shape[0] < n or idx_out.shape[0] * IDX_TILE_ENTRIES < n:
+        raise ValueError("rope_cs, kv_out and idx_out need room for every entry")
     _check("csa2_compress_pack", _L.csa2_compress_pack(
         _ptr(latent), n, m, _ptr(pool_w), per_token, _ptr(rope_cs), _ptr(w_idx), _ptr(kv_out), _ptr(idx_out),
         _stream(stream)))
@@ -205,7 +221,7 @@ def compress_append(latent, m: int, pool_w, rope_cs, w_idx, dst_rows, kv_cache, 
     _need(dst_rows, "dst_rows")
     _dev(dst_rows, torch.int64, "dst_rows", (n,))
     _cache(kv_cache, "kv_cache", 288)
-    _cache(idx_cache, "idx_cache", 68)
+    _idx_cache(idx_cache, "idx_cache")
     if rope_cs.shape[0] < n:
         raise ValueError("rope_cs must cover every new entry")
     _check("csa2_compress_append", _L.csa2_compress_append(
@@ -240,7 +256,7 @@ def _index_args(q, q_kind, head_w, idx_cache, q_base, q_nvis, width, pool_blocks
         _dev(q, torch.bfloat16, "q_idx", (None, 32, 128))
     n_q = q.shape[0]
     _dev(head_w, torch.float32, "head_w", (n_q, 32))
-    _cache(idx_cache, "idx_cache", 68)
+    _idx_cache(idx_cache, "idx_cache")
     _query_rows(q_base, q_nvis, n_q)
     M = 0
     if pool_blocks is not None:
@@ -275,7 +291,7 @@ def _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q):
         raise ValueError("rope_cs must cover every new entry")
     _dev(w_idx, torch.bfloat16, "w_idx", (128, 512))
     _cache(kv_cache, "kv_cache", 288)
-    _cache(idx_cache, "idx_cache", 68)
+    _idx_cache(idx_cache, "idx_cache")
     return per_token
 
 
@@ -318,7 +334,7 @@ def append_mean_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, id
     fp4 = isinstance(q_idx, torch.Tensor) and q_idx.dtype == torch.uint8
     n_q, _ = _index_args(q_idx, "fp4" if fp4 else "bf16", head_w, idx_cache, q_base, q_nvis, width, None)
     per_token = _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q)
-    _cache(mean_cache, "mean_cache", 68)
+    _idx_cache(mean_cache, "mean_cache")
     _need(mean_base, "mean_base")
     _dev(mean_base, torch.int64, "mean_base", (n_q,))
     scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_idx.device, stream)
@@ -438,8 +454,8 @@ def block_topk_noalloc(scores, q_nvis, K: int = 512, M: int = 2048, block_max=No
 def block_mean_pack(idx_cache, seq_base, seq_n, n_blocks: int, mean_cache, mean_base, first_block=None,
                     stream=None):
     """HISA block-mean records of blocks first_block[s] .. + n_blocks - 1 into mean_cache."""
-    _cache(idx_cache, "idx_cache", 68)
-    _cache(mean_cache, "mean_cache", 68)
+    _idx_cache(idx_cache, "idx_cache")
+    _idx_cache(mean_cache, "mean_cache")
     _need(seq_base, "seq_base")
     n_seq = seq_base.numel()
     for t, name, dt in ((seq_base, "seq_base", torch.int64), (seq_n, "seq_n", torch.int32),
@@ -462,7 +478,7 @@ def block_topk_rescore(block_max, q_nvis, q_idx, head_w, idx_cache, q_base, widt
                        stream=None):
     """(pool [n_q, M] or None, topk [n_q, K]): Full-mode selection from the block maxima
     [n_q, ceil(width/8)], re-scoring the candidate entries from the indexer cache (bf16
-    q_idx [n_q, 32, 128], head_w [n_q, 32], idx_cache [rows, 68], q_base [n_q]); the result
+    q_idx [n_q, 32, 128], head_w [n_q, 32], idx_cache [n_tiles, 2176], q_base [n_q]); the result
     of block_topk on the score row the scan would have written.  A given workspace must hold
     block_topk_rescore_workspace(...) bytes and start zeroed (every call leaves it so)."""
     _need(block_max, "block_max")

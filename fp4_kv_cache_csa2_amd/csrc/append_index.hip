@@ -135,15 +135,10 @@ __global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
     const int32_t b = (nvis - 1) / kBlock;  // the newest block
     const int cnt = nvis - b * kBlock;
     uint32_t code;
-    const uint32_t word =
-        block_mean_word(idx_cache + (q_base[t] + (int64_t)b * kBlock) * kIdxBytes, cnt, sh.e.idx_row, g, sub, code);
-    uint8_t* dst = mean_cache + (mean_base[t] + b) * kIdxBytes;
-    *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
+    const uint32_t word = block_mean_word(idx_cache, q_base[t] + (int64_t)b * kBlock, cnt, sh.e.idx_row, g, sub, code);
+    idx_store_word(mean_cache, mean_base[t] + b, g, sub, word, code);
     *reinterpret_cast<uint32_t*>(&sh.mean_row[16 * g + 4 * sub]) = word;
-    if (sub == 0) {
-      dst[64 + g] = (uint8_t)code;
-      sh.mean_row[64 + g] = (uint8_t)code;
-    }
+    if (sub == 0) sh.mean_row[64 + g] = (uint8_t)code;
   }
   __syncthreads();
   score_tiles<false, kFp4Q, kNewestSlots, true>(q_in, head_w, mean_cache, mean_base, q_nvis, nullptr, 0, width,

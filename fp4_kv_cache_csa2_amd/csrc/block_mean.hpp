@@ -5,23 +5,27 @@
 // sum of the block's exact dequantised keys in ascending position order, divided once (IEEE)
 // by the entry count, packed in the indexer-K format (MXFP4: E2M1 codes, one E8M0 scale per
 // 32 channels).  Lane 4g + sub of the 16 builds channels 32g + 8sub .. 32g + 8sub + 7: its
-// payload word (byte offset 16g + 4sub) and its group's scale code (byte 64 + g).
+// payload word (bytes 4sub .. 4sub + 3 of plane g) and its group's scale code.
 #pragma once
 #include "csa2_device.hpp"
 
 namespace csa2 {
 
-// rows: the block's first indexer row; cnt: its entries (1 .. 8); last: where the block's
-// last entry is read from (its cache row, or a copy the caller has just packed).  The lanes
-// 4g .. 4g + 3 of one group must run together (the scale is their common maximum).
-__device__ __forceinline__ uint32_t block_mean_word(const uint8_t* rows, int cnt, const uint8_t* last, int g,
-                                                   int sub, uint32_t& code) {
+// cache: the indexer-K cache (tile layout); first: the block's first entry; cnt: its entries
+// (1 .. 8); last: NULL, or a 68-byte record (64 payload bytes in channel order, then the 4
+// scale bytes) of the block's last entry that the caller has just packed and that is read
+// from there instead of the cache.  The lanes 4g .. 4g + 3 of one group must run together
+// (the scale is their common maximum).
+__device__ __forceinline__ uint32_t block_mean_word(const uint8_t* cache, int64_t first, int cnt, const uint8_t* last,
+                                                   int g, int sub, uint32_t& code) {
 #pragma clang fp contract(off)  // the same IEEE operations, in the same order, as the definition
   float sum[8];
   for (int e = 0; e < cnt; e++) {  // ascending positions: the fp32 running sum
-    const uint8_t* row = e == cnt - 1 ? last : rows + e * kIdxBytes;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 16 * g + 4 * sub);
-    const float X = __builtin_ldexpf(1.0f, (int)row[64 + g] - 127);
+    const bool rec = last != nullptr && e == cnt - 1;
+    const uint32_t w = rec ? *reinterpret_cast<const uint32_t*>(last + 16 * g + 4 * sub)
+                           : *reinterpret_cast<const uint32_t*>(cache + idx_plane_off(first + e, g) + 4 * sub);
+    const uint32_t sc = rec ? last[64 + g] : cache[idx_scale_off(first + e) + g];
+    const float X = __builtin_ldexpf(1.0f, (int)sc - 127);
 #pragma unroll
     for (int q = 0; q < 8; q++) {
       const uint32_t c = (w >> (4 * q)) & 15u;

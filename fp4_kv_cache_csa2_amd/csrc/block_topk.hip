@@ -520,7 +520,7 @@ struct Ws {
 struct Rescore {
   const uint16_t* q;         // bf16 indexer query [n_q, 32, 128]
   const float* head_w;       // [n_q, 32]
-  const uint8_t* idx_cache;  // [rows, 68]; query t's entry j at row q_base[t] + j
+  const uint8_t* idx_cache;  // tile layout; query t's entry j is entry q_base[t] + j
   const int64_t* q_base;
 };
 
@@ -690,10 +690,8 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
   int32_t* bid = ws.ids_b + ((int64_t)t * G + g) * seg_b;
   uint32_t* bkey = ws.keys_b + ((int64_t)t * G + g) * seg_b;
   __amdgpu_buffer_rsrc_t rs_cache;
-  if constexpr (kRescore)
-    rs_cache = __builtin_amdgcn_make_buffer_rsrc((void*)(rsc.idx_cache + rsc.q_base[t] * kIdxBytes), (short)0,
-                                                 r.n * kIdxBytes, 0x00020000);
-  constexpr int32_t kPast = 1 << 30;  // a byte offset past the cache buffer's end
+  int32_t rel0 = 0;  // the sequence's first entry, counted from the resource's first tile
+  if constexpr (kRescore) rs_cache = idx::idx_rsrc(rsc.idx_cache, rsc.q_base[t], r.n, rel0);
   int nbv = 0;
   for (int c0 = 0; c0 < nslots; c0 += kSegB) {
     uint32_t bk[kSlotRounds];
@@ -714,7 +712,7 @@ __global__ __launch_bounds__(kGThreads) void topk_collect_kernel(
           const int cs = c0 + 256 * wave + 64 * u + 32 * h + n;
           const int32_t j = cs < nslots ? s_cb[cs >> 3] * kBlock + (cs & 7) : 0;
           rt[u][h].valid = cs < nslots && j < r.n;
-          idx::load_row_share(rs_cache, rt[u][h].valid ? j * kIdxBytes : kPast, gg, rt[u][h]);
+          idx::load_entry_share<0>(rs_cache, rt[u][h].valid ? rel0 + j : -1, gg, rt[u][h]);
         }
       }
 #pragma unroll

@@ -171,12 +171,7 @@ __device__ __forceinline__ void compress_few_entry(const uint16_t* __restrict__ 
   if (lane < 4) {  // the MXFP4 group of these 32 outputs: 4 lanes, 8 outputs each
     uint32_t code;
     const uint32_t word = pack_idx8(&sh.k[8 * lane], code);
-    if (row >= 0) {
-      const int gg = o0 / 32;  // the group's index in the row
-      uint8_t* dst = idx_out + row * kIdxBytes;
-      *reinterpret_cast<uint32_t*>(dst + 16 * gg + 4 * lane) = word;
-      if (lane == 0) dst[64 + gg] = (uint8_t)code;
-    }
+    if (row >= 0) idx_store_word(idx_out, row, o0 / 32, lane, word, code);  // group o0 / 32 of the row
   }
 }
 
@@ -232,11 +227,7 @@ __device__ __forceinline__ void compress_entry_wg(const uint16_t* __restrict__ l
     const uint32_t word = pack_idx8(&sh.k[32 * g + 8 * sub], code);
     *reinterpret_cast<uint32_t*>(&sh.idx_row[16 * g + 4 * sub]) = word;
     if (sub == 0) sh.idx_row[64 + g] = (uint8_t)code;
-    if (row >= 0) {
-      uint8_t* dst = idx_out + row * kIdxBytes;
-      *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
-      if (sub == 0) dst[64 + g] = (uint8_t)code;
-    }
+    if (row >= 0) idx_store_word(idx_out, row, g, sub, word, code);
   }
   __syncthreads();
 }

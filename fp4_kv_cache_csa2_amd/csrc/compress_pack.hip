@@ -198,11 +198,7 @@ __global__ __launch_bounds__(kThreads) void compress_pack_kernel(
 #pragma unroll
     for (int q = 0; q < 8; q++) word |= e2m1_encode(v[q], X) << (4 * q);
     const int64_t row = j < n_entries ? out_row(j) : -1;
-    if (row >= 0) {
-      uint8_t* dst = idx_out + row * kIdxBytes;
-      *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
-      if (sub == 0) dst[64 + g] = (uint8_t)code;
-    }
+    if (row >= 0) idx_store_word(idx_out, row, g, sub, word, code);
   }
 }
 

@@ -32,6 +32,40 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
+// The indexer-K cache in HBM: tiles of 32 entries, 2176 bytes each.  Entry j sits in tile
+// j / 32 at slot e = j % 32.  Its payload bytes 16p .. 16p + 15 (plane p = 0 .. 3: the E2M1
+// codes of channels 32p .. 32p + 31, one MX group) are at byte 512p + 16e of the tile and its
+// four E8M0 scale bytes at byte 2048 + 4e.  Each plane of a tile is one contiguous 512-byte
+// run, so a wave reads a whole tile with two fully coalesced 1 KB loads and one 128-byte
+// load, and no cache line is fetched twice.
+constexpr int kIdxTileEntries = 32;
+constexpr int kIdxTileBytes = 2176;
+constexpr int kIdxPlaneBytes = 512;
+constexpr int kIdxScaleOff = 2048;
+
+// byte offset of plane p of entry j, and of its scale word (j >= 0, within one buffer of
+// fewer than 2^31 bytes for the 32-bit forms)
+__host__ __device__ __forceinline__ constexpr int64_t idx_plane_off(int64_t j, int p) {
+  return (j >> 5) * kIdxTileBytes + kIdxPlaneBytes * p + 16 * (j & 31);
+}
+__host__ __device__ __forceinline__ constexpr int64_t idx_scale_off(int64_t j) {
+  return (j >> 5) * kIdxTileBytes + kIdxScaleOff + 4 * (j & 31);
+}
+__host__ __device__ __forceinline__ constexpr int32_t idx_plane_off32(int32_t j, int p) {
+  return (j >> 5) * kIdxTileBytes + kIdxPlaneBytes * p + 16 * (j & 31);
+}
+__host__ __device__ __forceinline__ constexpr int32_t idx_scale_off32(int32_t j) {
+  return (j >> 5) * kIdxTileBytes + kIdxScaleOff + 4 * (j & 31);
+}
+
+// one writer lane of an indexer-K record: the payload word of channels 32g + 8sub .. + 7
+// (bytes 4sub .. 4sub + 3 of plane g) and, from lane sub = 0, group g's E8M0 code
+__device__ __forceinline__ void idx_store_word(uint8_t* cache, int64_t j, int g, int sub, uint32_t word,
+                                               uint32_t code) {
+  *reinterpret_cast<uint32_t*>(cache + idx_plane_off(j, g) + 4 * sub) = word;
+  if (sub == 0) cache[idx_scale_off(j) + g] = (uint8_t)code;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // E2M1 magnitude code -> value (exact), 3-bit code.

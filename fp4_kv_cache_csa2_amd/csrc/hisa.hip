@@ -32,13 +32,10 @@ __global__ __launch_bounds__(kThreads) void block_mean_pack_kernel(
   const int32_t b = (first_block ? first_block[s] : 0) + i;
   // the 16 lanes of a record share b: they leave together
   if (i >= n_blocks || b < 0 || (int64_t)b * kBlock >= n) return;
-  const uint8_t* rows = idx_cache + (seq_base[s] + (int64_t)b * kBlock) * kIdxBytes;
   const int cnt = min(kBlock, n - b * kBlock);
   uint32_t code;
-  const uint32_t word = block_mean_word(rows, cnt, rows + (cnt - 1) * kIdxBytes, g, sub, code);
-  uint8_t* dst = mean_cache + (mean_base[s] + b) * kIdxBytes;
-  *reinterpret_cast<uint32_t*>(dst + 16 * g + 4 * sub) = word;
-  if (sub == 0) dst[64 + g] = (uint8_t)code;
+  const uint32_t word = block_mean_word(idx_cache, seq_base[s] + (int64_t)b * kBlock, cnt, nullptr, g, sub, code);
+  idx_store_word(mean_cache, mean_base[s] + b, g, sub, word, code);
 }
 
 }  // namespace

@@ -26,8 +26,8 @@ __device__ __forceinline__ float e8m0_scale(uint32_t code) {
   return __builtin_ldexpf(1.0f, (int)code - 127);
 }
 
-// indexer rows are 68 bytes, so a row's 16-byte pieces are only 4-byte aligned; gfx950
-// serves dword-aligned global dwordx4 loads
+// 68-byte records (the MXFP4 query, the record an append has just packed) leave their
+// 16-byte pieces only 4-byte aligned; gfx950 serves dword-aligned dwordx4 loads
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 
@@ -35,32 +35,38 @@ typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef int32_t fp4x32 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
+// The scoring kernels give lane (n, g) of a wave, for entry (or head) n, the MX groups g and
+// 2 + g: channels 32g .. 32g + 31 and 64 + 32g .. 64 + 32g + 31, which are planes g and 2 + g
+// of an indexer-K tile.  Both operands of a contraction use the same channel split, so the
+// dot products are those of the natural channel order.
+
 // One 32-entry tile of q . k on the block-scaled FP4 MFMA (32 heads x 32 entries x 64 dims
-// per instruction).  Lane (n, g) holds, for both operands, the 64 codes of dims
-// 64g .. 64g + 63 of its head / entry as two 32-code MX blocks (blocks 2g and 2g + 1, each
-// block one instruction) and the row's scale word shifted so that byte 0 is block 2g's E8M0
-// code and byte 1 block 2g + 1's.  Operand A is the query, B the entries.  The dot products
-// are the MX definition: E2M1 values times 2^(code - 127), exact products, fp32 sums.
+// per instruction).  Lane (n, g) holds, for both operands, its two 32-code MX groups (g in
+// the first instruction, 2 + g in the second) and the scale word shifted right by 8g, so
+// that byte 0 is group g's E8M0 code and byte 2 group 2 + g's.  Operand A is the query, B the
+// entries.  The dot products are the MX definition: E2M1 values times 2^(code - 127), exact
+// products, fp32 sums.
 __device__ __forceinline__ f32x16 mfma_fp4_tile(const fp4x32 (&qa)[2], uint32_t qsc, const u32x4_a4& lo,
                                                 const u32x4_a4& hi, uint32_t ksc, f32x16 acc) {
   const i32x8 a0 = {qa[0][0], qa[0][1], qa[0][2], qa[0][3], 0, 0, 0, 0};
   const i32x8 a1 = {qa[1][0], qa[1][1], qa[1][2], qa[1][3], 0, 0, 0, 0};
   const i32x8 b0 = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
   const i32x8 b1 = {(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3], 0, 0, 0, 0};
-  // format 4 = E2M1 for both operands; scale byte 0 (block 2g), then byte 1 (block 2g + 1)
+  // format 4 = E2M1 for both operands; scale byte 0 (group g), then byte 2 (group 2 + g)
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, acc, 4, 4, 0, (int)qsc, 0, (int)ksc);
-  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, acc, 4, 4, 1, (int)qsc, 1, (int)ksc);
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, acc, 4, 4, 2, (int)qsc, 2, (int)ksc);
   return acc;
 }
 
-// the MXFP4 query record of one head (68 B: 64 code bytes, 4 E8M0 bytes): lane group g
-// takes code bytes 32g .. 32g + 31 and the scale bytes of blocks 2g, 2g + 1
+// the MXFP4 query record of one head (68 B: 64 code bytes in channel order, 4 E8M0 bytes):
+// lane group g takes code bytes 16g .. 16g + 15 and 32 + 16g .. 32 + 16g + 15 (groups g and
+// 2 + g) and the scale word shifted right by 8g
 __device__ __forceinline__ void load_fp4_query(const uint8_t* rec, int g, fp4x32 (&qa)[2], uint32_t& qsc) {
-  const u32x4_a4 lo = *reinterpret_cast<const u32x4_a4*>(rec + 32 * g);
-  const u32x4_a4 hi = *reinterpret_cast<const u32x4_a4*>(rec + 32 * g + 16);
+  const u32x4_a4 lo = *reinterpret_cast<const u32x4_a4*>(rec + 16 * g);
+  const u32x4_a4 hi = *reinterpret_cast<const u32x4_a4*>(rec + 32 + 16 * g);
   qa[0] = fp4x32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
   qa[1] = fp4x32{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  qsc = *reinterpret_cast<const uint32_t*>(rec + 64) >> (16 * g);
+  qsc = *reinterpret_cast<const uint32_t*>(rec + 64) >> (8 * g);
 }
 
 // MXFP4 packing of 8 channels of a 32-channel group held by 4 consecutive lanes (the OCP
@@ -93,11 +99,48 @@ __device__ __forceinline__ uint32_t mxfp4_pack8(const uint4 raw, uint32_t& code)
 // Vector memory operations complete in issue order, so this waits for all but the n youngest.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// lane (n, g)'s share of one indexer-K entry: planes g (lo) and 2 + g (hi) and the entry's
+// whole scale word
 struct RawTile {
   u32x4_a4 lo, hi;
   uint32_t sc;
   bool valid;
 };
+
+// buffer cache-policy bits of the loads: 0, or kLoadStream (non-temporal) for bytes that one
+// wave reads once (the decode scan's stream; each tile line is touched by one load)
+constexpr int kLoadStream = 2;
+
+// Loads lane (n, g)'s share of entry r of a tile-layout buffer resource (r counts entries from
+// the buffer's first tile); r < 0 reads past the buffer's end, which returns zeros.
+template <int kAux>
+__device__ __forceinline__ void load_entry_share(__amdgpu_buffer_rsrc_t rs, int32_t r, int g, RawTile& t) {
+  constexpr int32_t kPastEnd = 1 << 30;
+  const int32_t off = r >= 0 ? idx_plane_off32(r, g) : kPastEnd;
+  const int32_t soff = r >= 0 ? idx_scale_off32(r) : kPastEnd;
+  t.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kAux));
+  t.hi = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 2 * kIdxPlaneBytes, 0, kAux));
+  t.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, kAux);
+}
+
+// lane (n, g)'s share of a 68-byte record (64 payload bytes in channel order, then the scale
+// word), e.g. one an append has just packed into LDS
+__device__ __forceinline__ void load_record_share(const uint8_t* rec, int g, RawTile& t) {
+  t.lo = *reinterpret_cast<const u32x4_a4*>(rec + 16 * g);
+  t.hi = *reinterpret_cast<const u32x4_a4*>(rec + 32 + 16 * g);
+  t.sc = *reinterpret_cast<const uint32_t*>(rec + 64);
+}
+
+// A buffer resource over the tiles that hold entries first .. first + n - 1 of a tile-layout
+// cache (n >= 0), and the index, counted from the resource's first tile, of entry `first`.
+// Loads of entries past the last of those tiles return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t idx_rsrc(const uint8_t* cache, int64_t first, int32_t n,
+                                                          int32_t& first_rel) {
+  first_rel = (int32_t)(first & 31);
+  const int32_t tiles = n > 0 ? (first_rel + n + 31) >> 5 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (first >> 5) * kIdxTileBytes), (short)0,
+                                           tiles * kIdxTileBytes, 0x00020000);
+}
 
 // max(a, b) as one v_med3_f32 (the median of a, b and FLT_MAX): a NaN operand is ignored
 // like fmaxf does, without the quieting instructions fmaxf costs on these operands; +inf
@@ -132,8 +175,8 @@ __device__ __forceinline__ float sum_halves(float v) {
 
 }  // namespace idx
 
-// longest score row (entries) of csa2_index_score: byte offsets into a sequence's cache
-// (68 B per entry) stay below 2^31
+// longest score row (entries) of csa2_index_score: byte offsets into a sequence's tiles
+// (2176 B per 32 entries) stay below 2^30, where the kernels' past-the-end offset lies
 constexpr int32_t kMaxIndexWidth = 1 << 23;
 
 // batches of at least this many Full-mode queries take the many-query kernel

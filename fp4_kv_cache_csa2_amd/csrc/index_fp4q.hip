@@ -129,18 +129,17 @@ __global__ __launch_bounds__(kThreads) void index_score_mq_fp4q_kernel(
   };
 
   if (shared && max_nvis > 0) {
-    // the sequence's rows that some query of the block sees, as a buffer resource: loads
-    // past its end (the ragged last tile, the pipeline's overrun) return zeros
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(idx_cache + base0 * kIdxBytes), (short)0, max_nvis * kIdxBytes,
-                                          kRawBuf);
+    // the tiles of the sequence's entries that some query of the block sees, as a buffer
+    // resource; entries past the visible ones (the ragged last tile, the pipeline's
+    // overrun) read past its end, which returns zeros
+    int32_t rel0;
+    const __amdgpu_buffer_rsrc_t rs = idx_rsrc(idx_cache, base0, max_nvis, rel0);
     const int32_t tend = max(min(tile1, (max_nvis + kTile - 1) / kTile), tile0);
     const int32_t nt = tend - tile0;
     auto load = [&](int32_t k, RawTile& r) {
-      const int32_t off = (k * kTile + n) * kIdxBytes;
-      r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g, 0, 0));
-      r.hi = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g + 16, 0, 0));
-      r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 64, 0, 0) >> (16 * g);
+      const int32_t p = k * kTile + n;
+      load_entry_share<0>(rs, p < max_nvis ? rel0 + p : -1, g, r);  // L2-hot: every query block reads it
+      r.sc >>= 8 * g;
     };
     auto process = [&](const RawTile& cur, int32_t k) {
       f32x16 acc[kFqQPW];
@@ -179,17 +178,15 @@ __global__ __launch_bounds__(kThreads) void index_score_mq_fp4q_kernel(
 #pragma unroll
   for (int j = 0; j < kFqQPW; j++) {
     const int64_t base = s_base[wave * kFqQPW + j];
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(idx_cache + (nv[j] > 0 ? base : 0) * kIdxBytes), (short)0, nv[j] * kIdxBytes, kRawBuf);
+    int32_t rel0;
+    const __amdgpu_buffer_rsrc_t rs = idx_rsrc(idx_cache, nv[j] > 0 ? base : 0, nv[j], rel0);
     for (int32_t k = tile0; k < tile1; k++) {
       f32x16 acc = {};
       if (k * kTile < nv[j]) {
-        const int32_t off = (k * kTile + n) * kIdxBytes;
-        const u32x4_a4 lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g, 0, 0));
-        const u32x4_a4 hi =
-            __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g + 16, 0, 0));
-        const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 64, 0, 0) >> (16 * g);
-        acc = mfma_fp4_tile(qa[j], qsc[j], lo, hi, sc, acc);
+        const int32_t p = k * kTile + n;
+        RawTile r;
+        load_entry_share<0>(rs, p < nv[j] ? rel0 + p : -1, g, r);
+        acc = mfma_fp4_tile(qa[j], qsc[j], r.lo, r.hi, r.sc >> (8 * g), acc);
       }
       finish(j, acc, k);
     }

@@ -62,8 +62,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     max_nvis = max(max_nvis, s_nvis[j]);
     shared = shared && s_base[j] == base0;
   }
-  // this wave's queries: A fragments (head n, dims 64g + 8s ..), visible counts and output
-  // rows as buffer resources (empty for a padding slot, so its stores are dropped)
+  // this wave's queries: A fragments (head n, the scan's channel split: dims 32g + 8s for
+  // s < 4, 64 + 32g + 8(s - 4) after), visible counts and output rows as buffer resources
+  // (empty for a padding slot, so its stores are dropped)
   constexpr int32_t kOut = 1 << 30;  // a byte offset past every buffer's end
   bf16x8 a[kMqQPW][8];
   int32_t nv[kMqQPW];
@@ -76,9 +77,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const bool real = t < n_q;
     const int tt = real ? t : qb0;  // a padding slot reads a real query and writes nothing
     nv[j] = real ? s_nvis[wave * kMqQPW + j] : 0;
-    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)tt * kIdxHeads + n) * kIdxDim + 64 * g);
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((int64_t)tt * kIdxHeads + n) * kIdxDim + 32 * g);
 #pragma unroll
-    for (int s = 0; s < 8; s++) a[j][s] = __builtin_bit_cast(bf16x8, qp[s]);
+    for (int s = 0; s < 8; s++) a[j][s] = __builtin_bit_cast(bf16x8, qp[s < 4 ? s : s + 4]);
     rs_s[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)tt * width, (short)0, real ? width * 4 : 0, kRawBuf);
     rs_b[j] = __builtin_amdgcn_make_buffer_rsrc(kBmax ? (void*)(block_max + (int64_t)tt * nbw) : (void*)scores,
                                                 (short)0, (kBmax && real) ? nbw * 4 : 0, kRawBuf);
@@ -106,20 +107,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   };
 
   if (shared && max_nvis > 0) {
-    // wave w decodes MFMA steps 2w and 2w+1 of every tile: lane (n, g) takes payload bytes
-    // 32g + 8w .. +7 of entry n and the E8M0 byte of that 32-dim group
-    const uint8_t* last_row = idx_cache + (base0 + max_nvis - 1) * kIdxBytes;
-    struct Raw { u32x2_a4 w; uint32_t sc; };
+    // wave w decodes MFMA steps 2w and 2w+1 of every tile: lane (n, g) takes bytes
+    // 8(w % 2) .. + 7 of plane g + 2(w / 2) of entry n (16 channels) and that group's E8M0 byte
+    const int plane = g + 2 * (wave >> 1);
+    struct Raw { uint2 w; uint32_t sc; };
     auto load = [&](int32_t k, Raw& r) {
       const int32_t p = k * kTile + n;
-      const uint8_t* row = p < max_nvis ? idx_cache + (base0 + p) * kIdxBytes : last_row;
-      r.w = *reinterpret_cast<const u32x2_a4*>(row + 32 * g + 8 * wave);
-      r.sc = row[64 + 2 * g + (wave >= 2 ? 1 : 0)];
+      const int64_t j = base0 + (p < max_nvis ? p : max_nvis - 1);  // past the visible rows: the last one
+      r.w = *reinterpret_cast<const uint2*>(idx_cache + idx_plane_off(j, plane) + 8 * (wave & 1));
+      r.sc = idx_cache[idx_scale_off(j) + plane];
     };
     auto stage = [&](const Raw& r, int buf) {
       const float x = e8m0_scale(r.sc);
-      s_b[buf][2 * wave][lane] = cvt_fp4x8(r.w[0], x);
-      s_b[buf][2 * wave + 1][lane] = cvt_fp4x8(r.w[1], x);
+      s_b[buf][2 * wave][lane] = cvt_fp4x8(r.w.x, x);
+      s_b[buf][2 * wave + 1][lane] = cvt_fp4x8(r.w.y, x);
     };
     // tiles that some query of the block can see
     const int32_t tend = min(tile1, (max_nvis + kTile - 1) / kTile);
@@ -172,18 +173,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const int t = tq[j];
     if (t >= n_q) continue;
     const int64_t base = s_base[wave * kMqQPW + j];
-    const uint8_t* last_row = idx_cache + (base + max(nv[j], 1) - 1) * kIdxBytes;
     for (int32_t k = tile0; k < tile1; k++) {
       const int32_t p = k * kTile + n;
       f32x16 acc = {};
       if (nv[j] > 0 && k * kTile < nv[j]) {
-        const uint8_t* row = p < nv[j] ? idx_cache + (base + p) * kIdxBytes : last_row;
-        const u32x4_a4 lo = *reinterpret_cast<const u32x4_a4*>(row + 32 * g);
-        const u32x4_a4 hi = *reinterpret_cast<const u32x4_a4*>(row + 32 * g + 16);
-        const uint32_t scw = *reinterpret_cast<const uint32_t*>(row + 64);
-        const float x0 = e8m0_scale((scw >> (16 * g)) & 255u);
-        const float x1 = e8m0_scale((scw >> (16 * g + 8)) & 255u);
-        const uint32_t words[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int64_t e = base + (p < nv[j] ? p : nv[j] - 1);  // past the visible rows: the last one
+        const uint4 lo = *reinterpret_cast<const uint4*>(idx_cache + idx_plane_off(e, g));
+        const uint4 hi = *reinterpret_cast<const uint4*>(idx_cache + idx_plane_off(e, 2 + g));
+        const uint32_t scw = *reinterpret_cast<const uint32_t*>(idx_cache + idx_scale_off(e));
+        const float x0 = e8m0_scale((scw >> (8 * g)) & 255u);
+        const float x1 = e8m0_scale((scw >> (8 * g + 16)) & 255u);
+        const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
         for (int s = 0; s < 8; s++)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][s], cvt_fp4x8(words[s], s < 4 ? x0 : x1), acc, 0, 0, 0);

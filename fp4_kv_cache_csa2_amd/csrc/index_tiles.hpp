@@ -9,16 +9,17 @@
 // Design.  One wavefront owns one query and streams tiles of 32 entries.  The 32 heads
 // x 128 dims contraction runs on v_mfma_f32_32x32x16_bf16 with the heads as the M
 // dimension: the query sits in registers as eight A fragments for the whole scan, and
-// each tile's B fragments are built in registers straight from the packed bytes: every
-// lane loads 32 contiguous payload bytes of one entry (half of its 64) plus the 4-byte
-// scale word, and v_cvt_scalef32_pk_bf16_fp4 turns two E2M1 nibbles and their E8M0
-// power-of-two scale into two exact bf16 values.  The K dimension is permuted so that
-// lane group g and step s hold dims 64g + 8s .. 64g + 8s + 7 for both operands, which
-// leaves the dot products unchanged and makes each lane's bytes contiguous.  ReLU, the
-// head weights and the head sum run on the accumulator registers; a 32-lane swap
-// finishes the sum.  HBM traffic per entry is its 68 bytes plus 4.5 bytes of output.  The
-// waves of the grid walk a query's tiles in grid-stride order, so the whole grid streams
-// one front of the row at a time.
+// each tile's B fragments are built in registers straight from the packed bytes: lane
+// (n, g) loads planes g and 2 + g of entry n (32 payload bytes) plus its scale word, and
+// v_cvt_scalef32_pk_bf16_fp4 turns two E2M1 nibbles and their E8M0 power-of-two scale
+// into two exact bf16 values.  The K dimension is split the same way for both operands
+// (lane group g and step s hold dims 32g + 8s .. + 7 for s < 4 and 64 + 32g + 8(s - 4) ..
+// + 7 after), which leaves the dot products unchanged.  In the tile layout a wave's three
+// loads of a tile are two contiguous 1 KB runs and one 128-byte run, each line fetched
+// once, so the decode stream goes out non-temporal.  ReLU, the head weights and the head
+// sum run on the accumulator registers; a 32-lane swap finishes the sum.  HBM traffic per
+// entry is its 68 bytes plus 4.5 bytes of output.  The waves of the grid walk a query's
+// tiles in grid-stride order, so the whole grid streams one front of the row at a time.
 //
 // Streaming.  All cache reads and score writes go through buffer resources whose sizes
 // bound the row: loads past the end return zeros and stores past the end are dropped.
@@ -34,7 +35,7 @@ namespace csa2 {
 namespace idx {
 
 #ifndef CSA2_INDEX_DEPTH
-#define CSA2_INDEX_DEPTH 5
+#define CSA2_INDEX_DEPTH 4
 #endif
 constexpr int kDepth = CSA2_INDEX_DEPTH;  // tiles in flight per wave
 constexpr int kRawBuf = 0x00020000;        // buffer descriptor word 3: raw 32-bit dwords
@@ -52,13 +53,14 @@ enum : int { kAllSlots = 0, kOlderSlots = 1, kNewestSlots = 2 };
 // re-scoring of single entries calls too (the same operations in the same order give the
 // same bits): lane (n, g) of a wave works on entry n of a 32-entry tile, dims 64g .. 64g + 63.
 
-// the query fragments of lane (n, g) (head n, dims 64g .. 64g + 63: eight bf16x8 A fragments)
-// and the head weights of the accumulator rows it holds (row 8(r/4) + 4g + r%4)
+// the query fragments of lane (n, g) (head n, dims 32g + 8s .. + 7 for steps s < 4 and
+// 64 + 32g + 8(s - 4) .. + 7 after: eight bf16x8 A fragments) and the head weights of the
+// accumulator rows it holds (row 8(r/4) + 4g + r%4)
 __device__ __forceinline__ void load_query_bf16(const uint16_t* __restrict__ q, const float* __restrict__ head_w,
                                                 int t, int n, int g, bf16x8 (&a)[8], float (&wr)[16]) {
-  const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)t * kIdxHeads + n) * kIdxDim + 64 * g);
+  const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)t * kIdxHeads + n) * kIdxDim + 32 * g);
 #pragma unroll
-  for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s]);
+  for (int s = 0; s < 8; s++) a[s] = __builtin_bit_cast(bf16x8, qp[s < 4 ? s : s + 4]);
   typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
   const f32x4_a4* wp = reinterpret_cast<const f32x4_a4*>(head_w + (int64_t)t * kIdxHeads);
 #pragma unroll
@@ -69,20 +71,12 @@ __device__ __forceinline__ void load_query_bf16(const uint16_t* __restrict__ q, 
   }
 }
 
-// lane (n, g)'s share of one indexer row at byte offset off of the buffer (32 payload bytes
-// and the scale word; an offset past the buffer's end reads zeros)
-__device__ __forceinline__ void load_row_share(__amdgpu_buffer_rsrc_t rs, int32_t off, int g, RawTile& r) {
-  r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g, 0, 0));
-  r.hi = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * g + 16, 0, 0));
-  r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 64, 0, 0);
-}
-
 // q . k for the tile on v_mfma_f32_32x32x16_bf16: the entry's FP4 codes become exact bf16
 // B fragments with their E8M0 scale (v_cvt_scalef32_pk_bf16_fp4)
 __device__ __forceinline__ f32x16 mfma_bf16_tile(const bf16x8 (&a)[8], const RawTile& cur, int g) {
   f32x16 acc = {};
-  const float x0 = e8m0_scale((cur.sc >> (16 * g)) & 255u);
-  const float x1 = e8m0_scale((cur.sc >> (16 * g + 8)) & 255u);
+  const float x0 = e8m0_scale((cur.sc >> (8 * g)) & 255u);       // group g
+  const float x1 = e8m0_scale((cur.sc >> (8 * g + 16)) & 255u);  // group 2 + g
   const uint32_t words[8] = {cur.lo[0], cur.lo[1], cur.lo[2], cur.lo[3], cur.hi[0], cur.hi[1], cur.hi[2], cur.hi[3]};
 #pragma unroll
   for (int s = 0; s < 8; s++) {
@@ -170,14 +164,14 @@ __device__ __forceinline__ void score_tiles(
   uint32_t qsc = 0;
   float wr[16];
 
-  // Buffer resources bound the sequence's visible cache rows, the score row and the
-  // block-max row (empty when block_max is NULL): loads past the end return zeros and
+  // Buffer resources bound the tiles of the sequence's visible entries, the score row and
+  // the block-max row (empty when block_max is NULL): loads past the end return zeros and
   // stores past the end are dropped,
   // so the streaming loop below needs no branches (and the compiler's memory-counter
   // waits stay exact).  Offsets are 32-bit: the host limits width to 2^23 entries.
   const int32_t nv = min(nvis, kMaxIndexWidth);  // rows past 2^23 are never addressed
-  const __amdgpu_buffer_rsrc_t rs_cache =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(idx_cache + base * kIdxBytes), (short)0, nv * kIdxBytes, kRawBuf);
+  int32_t rel0;  // the sequence's first entry, counted from the resource's first tile
+  const __amdgpu_buffer_rsrc_t rs_cache = idx_rsrc(idx_cache, base, nv, rel0);
   const __amdgpu_buffer_rsrc_t rs_score = __builtin_amdgcn_make_buffer_rsrc(srow, (short)0, width * 4, kRawBuf);
   const __amdgpu_buffer_rsrc_t rs_bmax = __builtin_amdgcn_make_buffer_rsrc(
       block_max != nullptr ? (void*)(block_max + (int64_t)t * nbw) : (void*)srow, (short)0,
@@ -186,7 +180,8 @@ __device__ __forceinline__ void score_tiles(
       kPool ? (void*)(pool_blocks + (int64_t)t * M) : (void*)srow, (short)0, kPool ? M * 4 : 0, kRawBuf);
   constexpr int32_t kOut = 1 << 30;  // a byte offset past every buffer's end
 
-  // byte offset of this lane's cache row in tile k (past the end when the slot is empty)
+  // this lane's entry of tile k, counted from the resource's first tile (-1 when the slot is
+  // empty: its loads read past the end and return zeros)
   auto row_off = [&](int32_t k, bool& valid) -> int32_t {
     const int32_t p = tile_of(k) * kTile + n;
     int32_t j;
@@ -199,30 +194,29 @@ __device__ __forceinline__ void score_tiles(
       j = p;
       valid = p < nv && !dead(k);
     }
-    return valid ? j * kIdxBytes : kOut;
+    return valid ? rel0 + j : -1;
   };
+  // a Full row streams every tile once (non-temporal loads); a candidate pool gathers blocks
+  // whose tiles may share scale lines
+  constexpr int kAux = kPool ? 0 : kLoadStream;
   auto load = [&](int32_t k, RawTile& r) {
-    int32_t off = row_off(k, r.valid);
+    int32_t e = row_off(k, r.valid);
     // kNewestSlots: the entry at slot nvis - 1 was packed by this workgroup, which holds its
-    // row in fresh_row; it is taken from there and not read back from the cache
+    // record in fresh_row; it is taken from there and not read back from the cache
     bool fresh = false;
     if constexpr (kPart == kNewestSlots) {
       fresh = tile_of(k) * kTile + n == nvis - 1;
-      if (fresh) off = kOut;
+      if (fresh) e = -1;
     }
-    load_row_share(rs_cache, off, g, r);
+    load_entry_share<kAux>(rs_cache, e, g, r);
     if constexpr (kPart == kNewestSlots) {
-      if (fresh) {
-        r.lo = *reinterpret_cast<const u32x4_a4*>(fresh_row + 32 * g);
-        r.hi = *reinterpret_cast<const u32x4_a4*>(fresh_row + 32 * g + 16);
-        r.sc = *reinterpret_cast<const uint32_t*>(fresh_row + 64);
-      }
+      if (fresh) load_record_share(fresh_row, g, r);
     }
   };
   auto process = [&](const RawTile& cur, int32_t k) {
     f32x16 acc;
     if constexpr (kFp4Q) {
-      acc = mfma_fp4_tile(qa, qsc, cur.lo, cur.hi, cur.sc >> (16 * g), f32x16{});
+      acc = mfma_fp4_tile(qa, qsc, cur.lo, cur.hi, cur.sc >> (8 * g), f32x16{});
     } else {
       acc = mfma_bf16_tile(a, cur, g);
     }

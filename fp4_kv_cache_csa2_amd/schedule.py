@@ -47,13 +47,15 @@ class GlobalBranch:
     each; sequence s owns rows s * cap_c ...) and the scratch of one decoding token."""
 
     def __init__(self, n_seq, caps, K=512, M=2048, device="cuda"):
-        # capacities are rounded up to 4 entries, so every sequence's first indexer row
-        # (68 B each) starts 16-byte aligned, as the bulk packer requires of its output
-        caps = {c: (v + 3) // 4 * 4 for c, v in caps.items()}
+        # capacities are rounded up to whole tiles of 32 entries, so every sequence's first
+        # indexer entry starts a tile of the indexer cache and bulk packing can write from there
+        tile = csa2.IDX_TILE_ENTRIES
+        caps = {c: (v + tile - 1) // tile * tile for c, v in caps.items()}
         self.n_seq, self.caps, self.K, self.M = n_seq, caps, K, M
         dev = self.dev = torch.device(device)
         self.kv = {c: torch.zeros((n_seq * caps[c], 288), dtype=torch.uint8, device=dev) for c in RATIO}
-        self.ix = {c: torch.zeros((n_seq * caps[c], 68), dtype=torch.uint8, device=dev) for c in RATIO}
+        self.ix = {c: torch.zeros((n_seq * caps[c] // tile, csa2.IDX_TILE_BYTES), dtype=torch.uint8, device=dev)
+                   for c in RATIO}
         self.n = {c: 0 for c in RATIO}
         self.params = {}
         self.base = {c: torch.arange(n_seq, dtype=torch.int64, device=dev) * caps[c] for c in RATIO}
@@ -83,7 +85,8 @@ class GlobalBranch:
         m = RATIO[c]
         pool_w, w_idx = self.params[c]
         tokens = latents.shape[1]
-        assert first_entry % 4 == 0 and chunk_tokens % (4 * m) == 0  # 16-B aligned indexer rows
+        tile = csa2.IDX_TILE_ENTRIES
+        assert first_entry % tile == 0 and chunk_tokens % (tile * m) == 0  # whole indexer tiles
         for s in range(self.n_seq):
             for t0 in range(0, tokens, chunk_tokens):
                 tl = min(chunk_tokens, tokens - t0)
@@ -91,7 +94,7 @@ class GlobalBranch:
                 pos = np.arange(e0, e0 + tl // m, dtype=np.int64) * m
                 row = s * self.caps[c] + e0
                 csa2.compress_pack(latents[s, t0:t0 + tl].contiguous(), m, pool_w, csa2.rope_table(pos).to(self.dev),
-                                   w_idx, kv_out=self.kv[c][row:], idx_out=self.ix[c][row:])
+                                   w_idx, kv_out=self.kv[c][row:], idx_out=self.ix[c][row // tile:])
         self.n[c] = max(self.n[c], first_entry + tokens // m)
 
     def decode_token(self, p, new_latents, inputs, outs, lses=None, state=None):

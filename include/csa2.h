@@ -31,9 +31,16 @@
  *   main KV  (288 B): bytes 0..255 hold 512 E2M1 codes, channel 2b in the low nibble
  *            of byte b (sign in the nibble's bit 3); bytes 256..287 hold one OCP E4M3
  *            scale per 16 channels.  Rows must be 16-byte aligned (288 = 18 x 16).
- *   indexer K (68 B): bytes 0..63 hold 128 E2M1 codes in the same nibble order, bytes
- *            64..67 one E8M0 scale per 32 channels (MXFP4).  The cache base must be
- *            16-byte aligned; rows are then 4-byte aligned.
+ *   indexer K (68 B per entry): 128 E2M1 codes in the same nibble order (64 payload
+ *            bytes) and one E8M0 scale per 32 channels (MXFP4, 4 bytes).  The cache
+ *            holds entries in tiles of 32 (2176 B per tile, tile t = entries 32t .. 32t +
+ *            31): payload bytes 16p .. 16p + 15 of the tile's entry e (plane p = 0..3, the
+ *            codes of channels 32p .. 32p + 31) at tile byte 512p + 16e, its 4 scale bytes
+ *            at tile byte 2048 + 4e.  Entry j is thus at tile j / 32, slot j % 32, and a
+ *            cache holding entries 0 .. n - 1 takes ceil(n / 32) x 2176 bytes.  A 68-byte
+ *            record (the MXFP4 query of csa2_quantize_q_mxfp4) is the same entry as 64
+ *            payload bytes in channel order followed by the 4 scale bytes.  The cache base
+ *            must be 16-byte aligned.  HISA's block-mean cache uses the same layout.
  *   FP8 window row (584 B; the window KV kept in FP8, [ZB] §2.4.4, in DeepSeek-V4's FP8
  *            KV entry layout, [ZB] §3.1 and [DF] §4.6 equation 448 x 1 + 64 x 2 + 8):
  *            bytes 0..447 OCP E4M3 codes of channels 0..447; bytes 448..575 the bf16 bits
@@ -63,7 +70,7 @@ enum {
   CSA2_ERR_SCRATCH = -5      /* larger than the fixed scratch array of a _noalloc call */
 };
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 int csa2_abi_version(void);
 const char *csa2_status_string(int status);
@@ -100,7 +107,8 @@ int csa2_rope_table(const int64_t *pos, int64_t n, double theta, float *out);
  *   [DF] §4.2 notes the pooling weights may be projected from the input; same formula);
  *   rope_cs fp32 [n_entries, 64] (cos[32], sin[32] at each entry's position, e.g. from
  *   csa2_rope_table); w_idx_bf16 [128, 512];
- *   kv_out [n_entries, 288] and idx_out [n_entries, 68] receive the packed entries.
+ *   kv_out [n_entries, 288] and idx_out (an indexer-K cache in the tile layout, room for
+ *   entries 0 .. n_entries - 1: ceil(n_entries / 32) tiles) receive the packed entries.
  *   n_entries = 0 is a no-op.  Errors: INVALID_ARG (NULL, n < 0, misaligned outputs),
  *   UNSUPPORTED (m not 1 or 2); INVALID_ARG also for per_token_w not 0 or 1.
  */
@@ -109,7 +117,8 @@ int csa2_compress_pack(const uint16_t *latent_bf16, int64_t n_entries, int m,
                        const uint16_t *w_idx_bf16, uint8_t *kv_out, uint8_t *idx_out, void *stream);
 
 /*
- * csa2_compress_append -- csa2_compress_pack writing entry i to cache row dst_rows[i].
+ * csa2_compress_append -- csa2_compress_pack writing entry i to cache entry dst_rows[i]
+ *   (main-KV row dst_rows[i]; indexer-K entry dst_rows[i] of the tile layout).
  *   [DF] §4.3: a Full layer writes its own main KV and indexer K; a decoding token at
  *   position p completes an entry of a ratio-m cache when p + 1 is a multiple of m, and
  *   the batch's new entries land at each sequence's next row, which need not be adjacent.
@@ -130,8 +139,10 @@ int csa2_compress_append(const uint16_t *latent_bf16, int64_t n_entries, int m, 
  *     s(t, j) = sum_{h<32} head_w[t,h] * max(0, q_idx[t,h,:] . k^_j)
  *   with k^_j the exact dequantisation of entry j, bf16 products, fp32 accumulation.
  *
- *   q_idx_bf16 [n_q, 32, 128]; head_w fp32 [n_q, 32]; idx_cache flat [rows, 68];
- *   q_base int64 [n_q]: cache row of entry 0 of query t's sequence;
+ *   q_idx_bf16 [n_q, 32, 128]; head_w fp32 [n_q, 32]; idx_cache: the indexer-K cache in
+ *   the tile layout; q_base int64 [n_q]: cache entry of entry 0 of query t's sequence (a
+ *   sequence need not start a tile; entries of other sequences in a shared tile are not
+ *   read);
  *   q_nvis int32 [n_q]: visible entries of query t (entries 0 .. nvis-1);
  *   pool_blocks: NULL  -> Full mode: scores[t, j] for j < nvis, -inf for nvis <= j < width;
  *                [n_q, M] int32 block ids (-1 = empty) -> candidate mode: scores[t, 8s+o]
@@ -192,7 +203,7 @@ int csa2_index_score_fp4q(const uint8_t *q_fp4, const float *head_w, const uint8
  *   [t*m, t*m + m) weighting query t's latents (per_token_w = 1; neither is read when m = 1),
  *   rope_cs fp32 [n_q, 64]
  *   (the entry's cos[32], sin[32]), w_idx_bf16 [128, 512] (16-byte aligned), written to
- *   row q_base[t] + q_nvis[t] - 1 of kv_cache [rows, 288] and idx_cache [rows, 68]
+ *   entry q_base[t] + q_nvis[t] - 1 of kv_cache [rows, 288] and of idx_cache (tile layout)
  *   (16-byte aligned bases); q_nvis[t] counts the new entry.  Queries must append to
  *   distinct rows.  A query with q_nvis[t] <= 0 appends nothing and gets an all -inf row.
  *   q_idx_bf16, head_w, q_base, q_nvis, width, scores and block_max are those of
@@ -287,9 +298,9 @@ int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, in
  *   csa2_index_score would have written.  Results: those of csa2_block_topk given that
  *   score row, bit for bit.
  *   block_max fp32 [n_q, ceil(width/8)] (4-byte aligned); q_nvis, width as csa2_block_topk;
- *   q_idx_bf16 [n_q, 32, 128] (16-byte aligned), head_w fp32 [n_q, 32], idx_cache
- *   [rows, 68] (16-byte aligned) and q_base [n_q]: the scan's inputs (query t's entry j at
- *   row q_base[t] + j); M, K, pool_out (NULL: no pool), topk_out (required) as
+ *   q_idx_bf16 [n_q, 32, 128] (16-byte aligned), head_w fp32 [n_q, 32], idx_cache (tile
+ *   layout, 16-byte aligned) and q_base [n_q]: the scan's inputs (query t's entry j is
+ *   cache entry q_base[t] + j); M, K, pool_out (NULL: no pool), topk_out (required) as
  *   csa2_block_topk.  workspace: csa2_block_topk_rescore_workspace(n_q, width, M, K) bytes,
  *   4-byte aligned, histogram region zero before the first call and left zero by every
  *   call, as csa2_block_topk's (a 1M-context batch of 4 needs 21 MB: each K2 workgroup's
@@ -328,13 +339,15 @@ int csa2_block_topk_noalloc(const float *scores, const float *block_max, int32_t
  *   updated for the newest block only while decoding; the block means are scored with the
  *   same indexer query and head weights and the best blocks expanded for token-level
  *   scoring.  Record b of sequence s, for the entries e = 8b .. min(8b + 8, n_s) - 1 at cache
- *   rows seq_base[s] + e: the fp32 sum of their exact dequantised keys in ascending order,
+ *   entries seq_base[s] + e: the fp32 sum of their exact dequantised keys in ascending order,
  *   divided once (IEEE) by their count, packed in the indexer-K format (68 B, MXFP4 rules
  *   of csa2_compress_pack).  Bit-exact.
- *   idx_cache: indexer-K rows (4-byte aligned); seq_base int64 [n_seq], seq_n int32 [n_seq]
+ *   idx_cache: the indexer-K cache (tile layout, 4-byte aligned); seq_base int64 [n_seq],
+ *   seq_n int32 [n_seq]
  *   (entries of sequence s); first_block: NULL (0) or int32 [n_seq]; the call writes blocks
  *   first_block[s] .. first_block[s] + n_blocks - 1 that hold at least one entry, to
- *   mean_cache rows mean_base[s] + b (int64 [n_seq]; mean_cache 4-byte aligned).  A decode
+ *   entries mean_base[s] + b of mean_cache (int64 [n_seq]; mean_cache in the tile layout,
+ *   4-byte aligned).  A decode
  *   step passes first_block = (n_s - 1) / 8 and n_blocks = 1.  Scoring the block means is
  *   csa2_index_score over mean_cache with q_nvis = ceil(n / 8); the pool is csa2_block_topk's
  *   pool-only mode on those scores; the final Top-K is candidate mode inside it.
@@ -357,10 +370,10 @@ int csa2_block_mean_pack(const uint8_t *idx_cache, const int64_t *seq_base, cons
  *   the others score every other tile of block means.
  *
  *   The appended entry (latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache,
- *   idx_cache, q_base, q_nvis) is that of csa2_append_index_score: row q_base[t] + q_nvis[t] - 1, with
- *   q_nvis[t] counting it.  Block b of query t covers its entries 8b .. 8b + 7 (rows
- *   q_base[t] + 8b ..); its record is mean_cache row mean_base[t] + b (int64 [n_q];
- *   mean_cache [rows, 68], 16-byte aligned), and the call rewrites that of block
+ *   idx_cache, q_base, q_nvis) is that of csa2_append_index_score: entry q_base[t] + q_nvis[t] - 1,
+ *   with q_nvis[t] counting it.  Block b of query t covers its entries 8b .. 8b + 7 (cache
+ *   entries q_base[t] + 8b ..); its record is entry mean_base[t] + b of mean_cache (int64
+ *   [n_q]; mean_cache in the tile layout, 16-byte aligned), and the call rewrites that of block
  *   (q_nvis[t] - 1) / 8 by the rules of csa2_block_mean_pack.  The scores are those of
  *   csa2_index_score over mean_cache with q_base = mean_base and ceil(q_nvis[t] / 8)
  *   visible rows: scores fp32 [n_q, width] and block_max (NULL, or fp32 [n_q,

@@ -8,6 +8,8 @@ largest magnitude; attention outputs within 2e-3 max relative error, row-normwis
 import numpy as np
 import torch
 
+from fp4_kv_cache_csa2_amd import layout
+
 SEL_RTOL = 1e-4
 ATTN_TOL = 2e-3
 SCORE_TOL = 2e-5
@@ -23,6 +25,24 @@ def dev(a):
 
 def host(t):
     return t.cpu().numpy()
+
+
+def dev_ix(rec):
+    """A device indexer-K (or block-mean) cache in the kernels' tile layout holding the given
+    68-byte records as entries 0 .. n - 1."""
+    return dev(layout.records_to_tiles(rec))
+
+
+def host_ix(t, n=None):
+    """Entries 0 .. n - 1 (default: every slot) of a device tile-layout cache as 68-byte records."""
+    a = host(t)
+    return layout.tiles_to_records(a, a.shape[0] * layout.TILE_ENTRIES if n is None else n)
+
+
+def ix_tensor(n, fill=0):
+    """A device tile-layout cache with room for n entries, every byte set to fill."""
+    tiles = (n + layout.TILE_ENTRIES - 1) // layout.TILE_ENTRIES
+    return torch.full((tiles, layout.TILE_BYTES), fill, dtype=torch.uint8, device="cuda")
 
 
 def check_scores(got, ref, nvis=None):

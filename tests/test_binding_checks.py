@@ -60,31 +60,32 @@ def expect_bad(lib, fn, **kw):
 def test_compress_checks(fake):
     n, m = 8, 2
     good = dict(latent=z((n * m, 512), BF), m=m, pool_w=z((m, 512), F32), rope_cs=z((n, 64), F32),
-                w_idx=z((128, 512), BF), kv_out=z((n, 288), U8), idx_out=z((n, 68), U8))
+                w_idx=z((128, 512), BF), kv_out=z((n, 288), U8), idx_out=z((1, 2176), U8))
     expect_ok(fake, csa2.compress_pack, **good)
     expect_ok(fake, csa2.compress_pack, **{**good, "pool_w": z((n * m, 512), F32)})  # per-token weights
     for k, v in (("latent", z((n * m + 1, 512), BF)), ("latent", z((n * m, 256), BF)), ("pool_w", z((3, 512), F32)),
                  ("pool_w", None), ("rope_cs", z((n - 1, 64), F32)), ("w_idx", z((128, 511), BF)),
-                 ("kv_out", z((n - 1, 288), U8)), ("idx_out", z((n, 64), U8)), ("pool_w", z((m, 512), torch.float64)),
+                 ("kv_out", z((n - 1, 288), U8)), ("idx_out", z((n, 68), U8)), ("idx_out", z((0, 2176), U8)),
+                 ("pool_w", z((m, 512), torch.float64)),
                  ("latent", z((512, n * m), BF).t())):
         expect_bad(fake, csa2.compress_pack, **{**good, k: v})
     app = dict(latent=good["latent"], m=m, pool_w=good["pool_w"], rope_cs=good["rope_cs"], w_idx=good["w_idx"],
-               dst_rows=z((n,), I64), kv_cache=z((100, 288), U8), idx_cache=z((100, 68), U8))
+               dst_rows=z((n,), I64), kv_cache=z((100, 288), U8), idx_cache=z((4, 2176), U8))
     expect_ok(fake, csa2.compress_append, **app)
     for k, v in (("dst_rows", z((n + 1,), I64)), ("dst_rows", None), ("kv_cache", z((100, 68), U8)),
-                 ("idx_cache", z((100 * 68,), U8))):
+                 ("idx_cache", z((4 * 2176,), U8)), ("idx_cache", z((100, 68), U8))):
         expect_bad(fake, csa2.compress_append, **{**app, k: v})
 
 
 def test_index_score_checks(fake):
     n_q, width, M = 3, 1000, 16
-    good = dict(q_idx=z((n_q, 32, 128), BF), head_w=z((n_q, 32), F32), idx_cache=z((5000, 68), U8),
+    good = dict(q_idx=z((n_q, 32, 128), BF), head_w=z((n_q, 32), F32), idx_cache=z((157, 2176), U8),
                 q_base=z((n_q,), I64), q_nvis=z((n_q,), I32), width=width, scores=z((n_q, width), F32),
                 block_max=z((n_q, (width + 7) // 8), F32))
     expect_ok(fake, csa2.index_score, **good)
     for k, v in (("q_idx", z((n_q, 32, 64), BF)), ("head_w", z((n_q + 1, 32), F32)), ("q_base", z((n_q - 1,), I64)),
                  ("q_nvis", z((n_q,), I64)), ("scores", z((n_q, width - 1), F32)),
-                 ("block_max", z((n_q, width // 8 - 1), F32)), ("idx_cache", z((5000, 72), U8))):
+                 ("block_max", z((n_q, width // 8 - 1), F32)), ("idx_cache", z((5000, 68), U8))):
         expect_bad(fake, csa2.index_score, **{**good, k: v})
     cand = {**good, "width": 8 * M, "pool_blocks": z((n_q, M), I32), "scores": z((n_q, 8 * M), F32),
             "block_max": None, "want_block_max": False}
@@ -102,7 +103,7 @@ def test_index_score_checks(fake):
 def test_append_index_checks(fake):
     n_q, m, width = 4, 2, 4096
     good = dict(latent=z((n_q * m, 512), BF), m=m, pool_w=z((m, 512), F32), rope_cs=z((n_q, 64), F32),
-                w_idx=z((128, 512), BF), kv_cache=z((width * n_q, 288), U8), idx_cache=z((width * n_q, 68), U8),
+                w_idx=z((128, 512), BF), kv_cache=z((width * n_q, 288), U8), idx_cache=z((width * n_q // 32, 2176), U8),
                 q_idx=z((n_q, 32, 128), BF), head_w=z((n_q, 32), F32), q_base=z((n_q,), I64),
                 q_nvis=z((n_q,), I32), width=width)
     expect_ok(fake, csa2.append_index_score, **good)
@@ -113,10 +114,10 @@ def test_append_index_checks(fake):
                  ("scores", z((n_q, width + 1), F32)), ("block_max", z((n_q, 1), F32)),
                  ("q_idx", z((n_q, 32, 60), U8))):
         expect_bad(fake, csa2.append_index_score, **{**good, k: v})
-    mean = {**good, "mean_cache": z((width, 68), U8), "mean_base": z((n_q,), I64)}
+    mean = {**good, "mean_cache": z((width // 32, 2176), U8), "mean_base": z((n_q,), I64)}
     expect_ok(fake, csa2.append_mean_index_score, **mean)
     expect_bad(fake, csa2.append_mean_index_score, **{**mean, "mean_base": z((n_q + 1,), I64)})
-    expect_bad(fake, csa2.append_mean_index_score, **{**mean, "mean_cache": z((width, 67), U8)})
+    expect_bad(fake, csa2.append_mean_index_score, **{**mean, "mean_cache": z((width, 68), U8)})
 
 
 def test_block_topk_checks(fake):
@@ -140,11 +141,11 @@ def test_block_topk_checks(fake):
 
 def test_block_mean_pack_checks(fake):
     n_seq = 3
-    good = dict(idx_cache=z((800, 68), U8), seq_base=z((n_seq,), I64), seq_n=z((n_seq,), I32), n_blocks=4,
-                mean_cache=z((100, 68), U8), mean_base=z((n_seq,), I64))
+    good = dict(idx_cache=z((25, 2176), U8), seq_base=z((n_seq,), I64), seq_n=z((n_seq,), I32), n_blocks=4,
+                mean_cache=z((4, 2176), U8), mean_base=z((n_seq,), I64))
     expect_ok(fake, csa2.block_mean_pack, **good)
     for k, v in (("seq_n", z((n_seq + 1,), I32)), ("mean_base", z((n_seq,), I32)), ("first_block", z((1,), I32)),
-                 ("mean_cache", z((100, 64), U8))):
+                 ("mean_cache", z((100, 68), U8))):
         expect_bad(fake, csa2.block_mean_pack, **{**good, k: v})
 
 

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import synth
-from tests.gpu_util import bf16, check_scores, dev, host
+from tests.gpu_util import bf16, check_scores, dev, dev_ix, host, host_ix
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ class Case:
 
 
 def _separate(c, k, fp4):
-    kv, ix = dev(k.kv), dev(k.ix)
+    kv, ix = dev(k.kv), dev_ix(k.ix)
     c.compress_append(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), dev(k.dst), kv, ix)
     q = c.quantize_q_mxfp4(bf16(k.d.q_idx)) if fp4 else bf16(k.d.q_idx)
     score = c.index_score_fp4q if fp4 else c.index_score
@@ -60,7 +60,7 @@ def _separate(c, k, fp4):
 def _fused(c, k, fp4, kv=None, ix=None, pack_q=False):
     """fp4 with pack_q: the bf16 query goes in and the launch packs it to MXFP4 itself."""
     kv = dev(k.kv) if kv is None else kv
-    ix = dev(k.ix) if ix is None else ix
+    ix = dev_ix(k.ix) if ix is None else ix
     q = c.quantize_q_mxfp4(bf16(k.d.q_idx)) if fp4 and not pack_q else bf16(k.d.q_idx)
     s, b = c.append_index_score(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), kv, ix, q,
                                 dev(k.d.head_w), dev(k.base), dev(k.nvis), k.width, pack_q=pack_q)
@@ -132,7 +132,7 @@ def test_fused_against_the_oracle(c, fp4):
     k = Case(c, 530, nvis, width, m)
     kv, ix, s, b = _fused(c, k, fp4)
     torch.cuda.synchronize()
-    kv, ix, s, b = host(kv), host(ix), host(s), host(b)
+    kv, ix, s, b = host(kv), host_ix(ix), host(s), host(b)
     kv_ref, ix_ref = oracle.compress_pack(k.ci.latent, m, k.ci.pool_w, oracle.rope_table(k.pos), k.ci.w_idx)
     for t in range(k.n_q):
         r = k.dst[t]
@@ -165,7 +165,7 @@ def test_fused_decode_1m_b4(c, fp4):
     torch.cuda.synchronize()
     _same(ref, got)
     # the newest tile of each row against the oracle (the rest is the plain scan, equal above)
-    ix = host(got[1])
+    ix = host_ix(got[1])
     s = host(got[2])
     lo = n - 32
     for t in range(n_q):
@@ -186,10 +186,10 @@ def test_fused_per_token_weights(c):
     log("append_index per-token weights")
     k = Case(c, 560, nvis, width, m)
     w_tok = synth.softplus_weights(np.random.default_rng(561), k.n_q * m)
-    kv, ix = dev(k.kv), dev(k.ix)
+    kv, ix = dev(k.kv), dev_ix(k.ix)
     c.compress_append(bf16(k.ci.latent), m, dev(w_tok), dev(k.cs), bf16(k.ci.w_idx), dev(k.dst), kv, ix)
     s_ref, b_ref = c.index_score(bf16(k.d.q_idx), dev(k.d.head_w), ix, dev(k.base), dev(k.nvis), width)
-    kv2, ix2 = dev(k.kv), dev(k.ix)
+    kv2, ix2 = dev(k.kv), dev_ix(k.ix)
     s, b = c.append_index_score(bf16(k.ci.latent), m, dev(w_tok), dev(k.cs), bf16(k.ci.w_idx), kv2, ix2,
                                 bf16(k.d.q_idx), dev(k.d.head_w), dev(k.base), dev(k.nvis), width)
     torch.cuda.synchronize()
@@ -197,7 +197,7 @@ def test_fused_per_token_weights(c):
     assert np.array_equal(host(s).view(np.uint32), host(s_ref).view(np.uint32))
     assert np.array_equal(host(b).view(np.uint32), host(b_ref).view(np.uint32))
     kv_o, ix_o = oracle.compress_pack(k.ci.latent, m, w_tok, oracle.rope_table(k.pos), k.ci.w_idx)
-    got_kv, got_ix = host(kv2), host(ix2)
+    got_kv, got_ix = host(kv2), host_ix(ix2)
     for t in range(k.n_q):
         if k.dst[t] >= 0:
             assert np.array_equal(got_kv[k.dst[t]], kv_o[t]) and np.array_equal(got_ix[k.dst[t]], ix_o[t]), t

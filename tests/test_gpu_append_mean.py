@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import synth
-from tests.gpu_util import bf16, check_scores, dev, host
+from tests.gpu_util import bf16, check_scores, dev, dev_ix, host, host_ix
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,7 @@ def _q(c, k, fp4):
 
 
 def _separate(c, k, fp4, want_bmax):
-    kv, ix, mc = dev(k.kv), dev(k.ix), dev(k.means)
+    kv, ix, mc = dev(k.kv), dev_ix(k.ix), dev_ix(k.means)
     c.compress_append(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), dev(k.dst), kv, ix)
     c.block_mean_pack(ix, dev(k.base), dev(k.nvis), 1, mc, dev(k.mbase), first_block=dev(k.newest))
     score = c.index_score_fp4q if fp4 else c.index_score
@@ -66,7 +66,7 @@ def _separate(c, k, fp4, want_bmax):
 
 
 def _fused(c, k, fp4, want_bmax, state=None):
-    kv, ix, mc = (dev(k.kv), dev(k.ix), dev(k.means)) if state is None else state
+    kv, ix, mc = (dev(k.kv), dev_ix(k.ix), dev_ix(k.means)) if state is None else state
     s, b = c.append_mean_index_score(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), kv, ix,
                                      mc, dev(k.mbase), _q(c, k, fp4), dev(k.d.head_w), dev(k.base), dev(k.nvis),
                                      k.width, want_block_max=want_bmax)
@@ -116,7 +116,8 @@ def test_fused_against_the_oracle(c, fp4):
     nvis, width, m = CASES[0]
     log(f"append_mean_index vs oracle fp4={fp4}")
     k = Case(c, 640, nvis, width, m)
-    kv, ix, mc, s, b = (host(x) for x in _fused(c, k, fp4, True))
+    kv, ix, mc, s, b = _fused(c, k, fp4, True)
+    kv, ix, mc, s, b = host(kv), host_ix(ix), host_ix(mc), host(s), host(b)
     kv_ref, ix_ref = oracle.compress_pack(k.ci.latent, m, k.ci.pool_w, oracle.rope_table(k.pos), k.ci.w_idx)
     touched = []
     for t in range(k.n_q):
@@ -151,7 +152,7 @@ def test_fused_decode_1m_b4(c):
     got = _fused(c, k, False, False)
     torch.cuda.synchronize()
     _same(ref, got)
-    mc, s = host(got[2]), host(got[3])
+    mc, s = host_ix(got[2]), host(got[3])
     nb = n // 8
     for t in range(n_q):  # the tile of block means holding the new record against the oracle
         sub = mc[k.mbase[t] + nb - 32:k.mbase[t] + nb]

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import synth
-from tests.gpu_util import bf16, check_scores, check_selection, dev, host
+from tests.gpu_util import bf16, check_scores, check_selection, dev, dev_ix, host
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +94,7 @@ def test_index_score_fp4q_full_mode(c, n_q, n, width_pad, seed):
     qf_ref = oracle.quantize_q_mxfp4(d.q_idx)
     ref = oracle.index_score_fp4q(qf_ref, d.head_w, ix, base, nvis, width)
     qf = c.quantize_q_mxfp4(bf16(d.q_idx))
-    s, bm = c.index_score_fp4q(qf, dev(d.head_w), dev(ix), dev(base), dev(nvis), width)
+    s, bm = c.index_score_fp4q(qf, dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), width)
     torch.cuda.synchronize()
     assert np.array_equal(host(qf), qf_ref)
     s, bm = host(s), host(bm)
@@ -127,7 +127,7 @@ def test_index_score_fp4q_many_queries(c, shared):
     qf_ref = oracle.quantize_q_mxfp4(d.q_idx)
     ref = oracle.index_score_fp4q(qf_ref, d.head_w, ix, base, nvis, width)
     for want_bm in (True, False):
-        s, bm = c.index_score_fp4q(dev(qf_ref), dev(d.head_w), dev(ix), dev(base), dev(nvis), width,
+        s, bm = c.index_score_fp4q(dev(qf_ref), dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), width,
                                    want_block_max=want_bm)
         torch.cuda.synchronize()
         s = host(s)
@@ -152,7 +152,7 @@ def test_index_score_fp4q_candidate_mode(c):
         pool[t, :k] = np.sort(np.append(sel, nb - 1))
     qf_ref = oracle.quantize_q_mxfp4(d.q_idx)
     ref = oracle.index_score_fp4q(qf_ref, d.head_w, ix, base, nvis, 8 * M, pool_blocks=pool)
-    s, _ = c.index_score_fp4q(dev(qf_ref), dev(d.head_w), dev(ix), dev(base), dev(nvis), 8 * M,
+    s, _ = c.index_score_fp4q(dev(qf_ref), dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), 8 * M,
                               pool_blocks=dev(pool))
     torch.cuda.synchronize()
     check_scores(host(s), ref)
@@ -171,7 +171,7 @@ def test_index_score_fp4q_spread_scales(c):
         nvis = np.full(n_q, n, np.int32)
         qf_ref = oracle.quantize_q_mxfp4(qb)
         ref = oracle.index_score_fp4q(qf_ref, hw, ix, base, nvis, n)
-        s, _ = c.index_score_fp4q(dev(qf_ref), dev(hw), dev(ix), dev(base), dev(nvis), n, want_block_max=False)
+        s, _ = c.index_score_fp4q(dev(qf_ref), dev(hw), dev_ix(ix), dev(base), dev(nvis), n, want_block_max=False)
         torch.cuda.synchronize()
         check_scores(host(s), ref)
 
@@ -190,7 +190,7 @@ def test_prefill_chunk4096_fp4q(c):
     base = np.zeros(chunk, np.int64)
     log("prefill fp4q: GPU pack + score + select")
     qf = c.quantize_q_mxfp4(bf16(d.q_idx))
-    s, _ = c.index_score_fp4q(qf, dev(d.head_w), dev(ix), dev(base), dev(nvis), n, want_block_max=False)
+    s, _ = c.index_score_fp4q(qf, dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), n, want_block_max=False)
     _, topk = c.block_topk(s, dev(nvis), K=512, M=2048, want_pool=False)
     torch.cuda.synchronize()
     qf, s, topk = host(qf), host(s), host(topk)
@@ -215,7 +215,7 @@ def test_decode_1m_fp4q_query(c):
     nvis = np.full(n_q, n, np.int32)
     log("decode 1M fp4q: GPU pack + score + select")
     qf = c.quantize_q_mxfp4(bf16(d.q_idx))
-    s, bm = c.index_score_fp4q(qf, dev(d.head_w), dev(ix), dev(base), dev(nvis), n)
+    s, bm = c.index_score_fp4q(qf, dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), n)
     _, topk = c.block_topk(s, dev(nvis), K=512, M=2048, block_max=bm, want_pool=False)
     torch.cuda.synchronize()
     s, bm, topk = host(s), host(bm), host(topk)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import synth
-from tests.gpu_util import bf16, check_scores, check_selection, dev, host
+from tests.gpu_util import bf16, check_scores, check_selection, dev, dev_ix, host, host_ix, ix_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +45,10 @@ def test_block_mean_pack_bit_exact(c):
     nbs = [-(-n // 8) for n in lens]
     mbase = np.concatenate([[0], np.cumsum(nbs)[:-1]]).astype(np.int64)
     ref = np.concatenate([oracle.block_mean_pack(ix[b:b + n]) for b, n in zip(base, lens)])
-    out = torch.full((sum(nbs), 68), 0xAB, dtype=torch.uint8, device="cuda")
-    c.block_mean_pack(dev(ix), dev(base), dev(np.array(lens, np.int32)), max(nbs), out, dev(mbase))
+    out = ix_tensor(sum(nbs), 0xAB)
+    c.block_mean_pack(dev_ix(ix), dev(base), dev(np.array(lens, np.int32)), max(nbs), out, dev(mbase))
     torch.cuda.synchronize()
-    got = host(out)
+    got = host_ix(out, sum(nbs))
     bad = np.flatnonzero(np.any(got != ref, axis=1))
     assert bad.size == 0, f"{bad.size} records differ, first {bad[:8]}"
 
@@ -62,14 +62,14 @@ def test_block_mean_decode_update_touches_only_the_newest_block(c):
     nb_max = 1024 // 8
     mbase = np.arange(n_seq, dtype=np.int64) * nb_max
     lens = np.array([n0, n0 + 5, n0 + 13], np.int32)
-    out = torch.zeros((n_seq * nb_max, 68), dtype=torch.uint8, device="cuda")
-    c.block_mean_pack(dev(ix), dev(base), dev(lens), nb_max, out, dev(mbase))
-    before = host(out).copy()
+    out = ix_tensor(n_seq * nb_max)
+    c.block_mean_pack(dev_ix(ix), dev(base), dev(lens), nb_max, out, dev(mbase))
+    before = host_ix(out).copy()
     lens2 = lens + 1
     first = ((lens2 - 1) // 8).astype(np.int32)
-    c.block_mean_pack(dev(ix), dev(base), dev(lens2), 1, out, dev(mbase), first_block=dev(first))
+    c.block_mean_pack(dev_ix(ix), dev(base), dev(lens2), 1, out, dev(mbase), first_block=dev(first))
     torch.cuda.synchronize()
-    after = host(out)
+    after = host_ix(out)
     for s in range(n_seq):
         ref = oracle.block_mean_pack(ix[base[s]:base[s] + lens2[s]])
         rows = slice(mbase[s], mbase[s] + len(ref))
@@ -101,7 +101,7 @@ def _gpu_hisa(c, d, ix_d, base, nvis, n_per_seq, M=2048, K=512):
     """GPU HISA chain for sequences of n_per_seq cache rows each (row base[t] is entry 0)."""
     n_q = len(base)
     nbw = -(-n_per_seq // 8)
-    means = torch.empty((n_q * nbw, 68), dtype=torch.uint8, device="cuda")
+    means = ix_tensor(n_q * nbw)
     mbase = np.arange(n_q, dtype=np.int64) * nbw
     c.block_mean_pack(ix_d, dev(base), dev(nvis), nbw, means, dev(mbase))
     nb_vis = ((nvis + 7) // 8).astype(np.int32)
@@ -110,7 +110,7 @@ def _gpu_hisa(c, d, ix_d, base, nvis, n_per_seq, M=2048, K=512):
     s_c, _ = c.index_score(bf16(d.q_idx), dev(d.head_w), ix_d, dev(base), dev(nvis), 8 * M, pool_blocks=pool)
     _, tk = c.block_topk(s_c, dev(nvis), K=K, pool_blocks=pool)
     torch.cuda.synchronize()
-    return host(means), host(s_blk), host(pool), host(s_c), host(tk)
+    return host_ix(means), host(s_blk), host(pool), host(s_c), host(tk)
 
 
 def _oracle_check_query(t, d, ix, base, nvis, n_per_seq, got, M=2048, K=512):
@@ -143,7 +143,7 @@ def test_hisa_chain_small(c):
     d = synth.query_inputs(77, n_q)
     base = np.arange(n_q, dtype=np.int64) * n
     nvis = np.array([n, n - 3, 2001], np.int32)
-    got = _gpu_hisa(c, d, dev(ix), base, nvis, n, M=M, K=K)
+    got = _gpu_hisa(c, d, dev_ix(ix), base, nvis, n, M=M, K=K)
     for t in range(n_q):
         _oracle_check_query(t, d, ix, base, nvis, n, got, M=M, K=K)
 
@@ -156,6 +156,6 @@ def test_hisa_chain_decode_1m_b4(c):
     base = np.arange(n_q, dtype=np.int64) * n
     nvis = np.full(n_q, n, np.int32)
     log("hisa chain 1M: GPU")
-    got = _gpu_hisa(c, d, dev(ix), base, nvis, n)
+    got = _gpu_hisa(c, d, dev_ix(ix), base, nvis, n)
     log("hisa chain 1M: oracle for query 1")
     _oracle_check_query(1, d, ix, base, nvis, n, got)

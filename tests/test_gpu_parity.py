@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import synth
-from tests.gpu_util import bf16, check_attn, check_scores, check_selection, dev, host
+from tests.gpu_util import bf16, check_attn, check_scores, check_selection, dev, dev_ix, host, host_ix, ix_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,8 @@ def test_compress_pack_bit_exact(c, n, m, seed):
                              bf16(ci.w_idx))
     torch.cuda.synchronize()
     assert np.array_equal(host(kv), kv_ref), f"main KV bytes differ in {np.sum(np.any(host(kv) != kv_ref, 1))} entries"
-    assert np.array_equal(host(ix), ix_ref), f"indexer bytes differ in {np.sum(np.any(host(ix) != ix_ref, 1))} entries"
+    assert np.array_equal(host_ix(ix, n), ix_ref), (
+        f"indexer bytes differ in {np.sum(np.any(host_ix(ix, n) != ix_ref, 1))} entries")
 
 
 @pytest.mark.parametrize("n,seed", [(1000, 20), (37, 21), (64, 22), (65, 23)])
@@ -54,13 +55,13 @@ def test_compress_pack_per_token_weights(c, n, seed):
                              bf16(ci.w_idx))
     rows = np.arange(n, dtype=np.int64)[::-1].copy() + 5  # reversed rows after 5 untouched ones
     kv_a = torch.zeros((n + 5, 288), dtype=torch.uint8, device="cuda")
-    ix_a = torch.zeros((n + 8, 68), dtype=torch.uint8, device="cuda")
+    ix_a = ix_tensor(n + 8)
     c.compress_append(bf16(ci.latent), m, dev(w_tok), dev(c.rope_table(ci.positions).numpy()), bf16(ci.w_idx),
                       dev(rows), kv_a, ix_a)
     torch.cuda.synchronize()
-    assert np.array_equal(host(kv), kv_ref) and np.array_equal(host(ix), ix_ref)
-    assert np.array_equal(host(kv_a)[rows], kv_ref) and np.array_equal(host(ix_a)[rows], ix_ref)
-    assert not host(kv_a)[:5].any() and not host(ix_a)[:5].any()
+    assert np.array_equal(host(kv), kv_ref) and np.array_equal(host_ix(ix, n), ix_ref)
+    assert np.array_equal(host(kv_a)[rows], kv_ref) and np.array_equal(host_ix(ix_a)[rows], ix_ref)
+    assert not host(kv_a)[:5].any() and not host_ix(ix_a)[:5].any()
 
 
 def test_compress_pack_edge_values(c):
@@ -83,7 +84,7 @@ def test_compress_pack_edge_values(c):
     kv, ix = c.compress_pack(bf16(lat), 1, pw, dev(c.rope_table(pos).numpy()), bf16(w))
     torch.cuda.synchronize()
     assert np.array_equal(host(kv), kv_ref)
-    assert np.array_equal(host(ix), ix_ref)
+    assert np.array_equal(host_ix(ix, n), ix_ref)
 
 
 # ------------------------------------------------------------------ index scores
@@ -96,7 +97,7 @@ def test_index_score_full_mode(c, n_q, n, width_pad, seed):
     nvis = np.array([n - (7 * t) % max(n // 3, 1) for t in range(n_q)], np.int32)
     width = n + width_pad
     ref = oracle.index_score(d.q_idx, d.head_w, ix, base, nvis, width)
-    s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), dev(base), dev(nvis), width)
+    s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), width)
     torch.cuda.synchronize()
     s, bm = host(s), host(bm)
     check_scores(s, ref)
@@ -131,7 +132,7 @@ def test_index_score_many_queries(c, shared):
         nvis[3] = 0
         width = n
     ref = oracle.index_score(d.q_idx, d.head_w, ix, base, nvis, width)
-    s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), dev(base), dev(nvis), width)
+    s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), width)
     torch.cuda.synchronize()
     s, bm = host(s), host(bm)
     check_scores(s, ref)
@@ -156,7 +157,7 @@ def test_index_score_candidate_mode(c):
         sel = np.sort(rng.choice(nb - 1, k - 1, replace=False))
         pool[t, :k] = np.sort(np.append(sel, nb - 1))
     ref = oracle.index_score(d.q_idx, d.head_w, ix, base, nvis, 8 * M, pool_blocks=pool)
-    s, _ = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), dev(base), dev(nvis), 8 * M,
+    s, _ = c.index_score(bf16(d.q_idx), dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), 8 * M,
                          pool_blocks=dev(pool))
     torch.cuda.synchronize()
     check_scores(host(s), ref)
@@ -342,7 +343,7 @@ def _decode_chain(c, ci, m, n_q, seeds, nvis_list, M=2048, K=512):
     pool, topk = c.block_topk(s, dev(nvis), K=K, M=M, block_max=bm)
     out, _ = c.sparse_attn(bf16(d.q), kv, dev(base), topk, bf16(d.swa), dev(d.swa_start), dev(d.swa_len))
     torch.cuda.synchronize()
-    assert np.array_equal(host(kv), kv_ref) and np.array_equal(host(ix), ix_ref)
+    assert np.array_equal(host(kv), kv_ref) and np.array_equal(host_ix(ix, len(ix_ref)), ix_ref)
     check_scores(host(s), s_ref)
     same = 0
     g_pool, g_topk, g_out = host(pool), host(topk), host(out)
@@ -385,7 +386,7 @@ def test_determinism(c):
     nvis = dev(np.full(n_q, n, np.int32))
     outs = []
     for _ in range(2):
-        s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), base, nvis, n)
+        s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), dev_ix(ix), base, nvis, n)
         pool, topk = c.block_topk(s, nvis, block_max=bm)
         out, lse = c.sparse_attn(bf16(d.q), dev(kv), base, topk, bf16(d.swa), dev(d.swa_start), dev(d.swa_len))
         torch.cuda.synchronize()

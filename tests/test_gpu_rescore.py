@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import synth
-from tests.gpu_util import bf16, dev, host
+from tests.gpu_util import bf16, dev, dev_ix, host
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def test_rescore_equals_score_row_selection(c, n_q, n, width_pad, seed, spread):
     if n_q > 2:
         nvis[2] = 0  # an empty row
     width = n + width_pad
-    pool, topk, pool_r, topk_r, s = _both_paths(c, d, dev(ix), dev(base), dev(nvis), width)
+    pool, topk, pool_r, topk_r, s = _both_paths(c, d, dev_ix(ix), dev(base), dev(nvis), width)
     assert np.array_equal(pool_r, pool) and np.array_equal(topk_r, topk)
     # and the oracle's selection over the same score row
     pool_o, topk_o = oracle.block_topk(s, nvis, K=512, M=2048)
@@ -72,7 +72,7 @@ def test_rescore_tie_heavy_row_beyond_the_lds_list(c):
     d = synth.query_inputs(13, n_q)
     base = np.arange(n_q, dtype=np.int64) * n
     nvis = np.array([n, n - 5], np.int32)
-    pool, topk, pool_r, topk_r, s = _both_paths(c, d, dev(ix_full), dev(base), dev(nvis), n)
+    pool, topk, pool_r, topk_r, s = _both_paths(c, d, dev_ix(ix_full), dev(base), dev(nvis), n)
     assert np.array_equal(pool_r, pool) and np.array_equal(topk_r, topk)
     pool_o, topk_o = oracle.block_topk(s, nvis, K=512, M=2048)
     assert np.array_equal(topk_r, topk_o) and np.array_equal(pool_r, pool_o)
@@ -90,11 +90,11 @@ def test_many_query_scores_equal_decode_kernel_scores(c):
     d = synth.query_inputs(22, n_q)
     base = np.zeros(n_q, np.int64)
     nvis = np.array([n - 37 * t for t in range(n_q)], np.int32)
-    s_all, bm_all = c.index_score(bf16(d.q_idx), dev(d.head_w), dev(ix), dev(base), dev(nvis), n)
+    s_all, bm_all = c.index_score(bf16(d.q_idx), dev(d.head_w), dev_ix(ix), dev(base), dev(nvis), n)
     parts = []
     for t0 in range(0, n_q, 24):
         sl = slice(t0, t0 + 24)
-        s_p, _ = c.index_score(bf16(d.q_idx[sl]), dev(d.head_w[sl]), dev(ix), dev(base[sl]), dev(nvis[sl]), n)
+        s_p, _ = c.index_score(bf16(d.q_idx[sl]), dev(d.head_w[sl]), dev_ix(ix), dev(base[sl]), dev(nvis[sl]), n)
         parts.append(host(s_p))
     torch.cuda.synchronize()
     assert np.array_equal(host(s_all).view(np.uint32), np.concatenate(parts).view(np.uint32))
@@ -116,7 +116,7 @@ def test_fused_scan_maxima_only_then_rescore(c, m):
     cs = dev(c.rope_table(pos).numpy())
     outs = []
     for want_scores in (True, False):
-        kv_d, ix_d = dev(kv), dev(ix)
+        kv_d, ix_d = dev(kv), dev_ix(ix)
         s, bm = c.append_index_score(bf16(ci.latent), m, dev(ci.pool_w), cs, bf16(ci.w_idx), kv_d, ix_d,
                                      bf16(d.q_idx), dev(d.head_w), dev(base), dev(nvis), width,
                                      want_scores=want_scores)

@@ -9,7 +9,7 @@ import torch
 import oracle
 from fp4_kv_cache_csa2_amd import synth
 from oracle import schedule as osched
-from tests.gpu_util import bf16, check_attn, dev, host
+from tests.gpu_util import bf16, check_attn, dev, dev_ix, host, host_ix
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def test_decode_schedule_two_tokens():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     n_seq, tokens, K, M = 2, 2000, 32, 40
-    cap = tokens + 4
+    cap = 2016  # whole tiles of 32 entries (the branch rounds its capacities to tiles), room for 2 tokens
     rng = np.random.default_rng(5)
     ocs = osched.SeqCaches(n_seq, cap)
     g = gsched.GlobalBranch(n_seq, {c: cap for c in gsched.RATIO}, K=K, M=M)
@@ -45,7 +45,7 @@ def test_decode_schedule_two_tokens():
         g.fill(c, bf16(lat))
     torch.cuda.synchronize()
     for c in osched.CACHE_RATIO:
-        assert np.array_equal(host(g.kv[c]), ocs.kv[c]) and np.array_equal(host(g.ix[c]), ocs.ix[c]), c
+        assert np.array_equal(host(g.kv[c]), ocs.kv[c]) and np.array_equal(host_ix(g.ix[c]), ocs.ix[c]), c
     layers = [l for l, (mo, _) in enumerate(osched.layer_plan()) if mo != "swa"]
     assert layers == gsched.csa2_layers()
     for p in (tokens, tokens + 1):
@@ -65,7 +65,7 @@ def test_decode_schedule_two_tokens():
         ref = osched.decode_token(ocs, p, new, params, inputs, K=K, M=M)
         assert g.n == ocs.n
         for c in osched.CACHE_RATIO:
-            assert np.array_equal(host(g.kv[c]), ocs.kv[c]) and np.array_equal(host(g.ix[c]), ocs.ix[c]), c
+            assert np.array_equal(host(g.kv[c]), ocs.kv[c]) and np.array_equal(host_ix(g.ix[c]), ocs.ix[c]), c
         for l in layers:
             rel = check_attn(host(outs[l]), ref[l][0])
             assert np.allclose(host(lses[l]), ref[l][1], atol=2e-3), f"layer {l} lse"
@@ -84,7 +84,7 @@ def test_decode_schedule_full_size_k512_m2048():
         pytest.skip("no GPU")
     n_seq, K, M = 2, 512, 2048
     n_hist = {"enc0": 20000, "enc1": 20000, "enc2": 20000, "dec": 40001}
-    cap = 40004
+    cap = 40032  # whole tiles of 32 entries
     rng = np.random.default_rng(9)
     ocs = osched.SeqCaches(n_seq, cap)
     g = gsched.GlobalBranch(n_seq, {c: cap for c in gsched.RATIO}, K=K, M=M)
@@ -98,7 +98,7 @@ def test_decode_schedule_full_size_k512_m2048():
         ocs.kv[c][:], ocs.ix[c][:] = kv, ix
         ocs.n[c] = n_hist[c]
         g.kv[c].copy_(dev(kv))
-        g.ix[c].copy_(dev(ix))
+        g.ix[c].copy_(dev_ix(ix))
         g.n[c] = n_hist[c]
         ci = synth.compress_inputs(90 + i, 1, osched.CACHE_RATIO[c])
         params[c] = (ci.pool_w, ci.w_idx)
@@ -122,7 +122,7 @@ def test_decode_schedule_full_size_k512_m2048():
         ref = osched.decode_token(ocs, p, new, params, inputs, K=K, M=M)
         assert g.n == ocs.n
         for c in osched.CACHE_RATIO:
-            assert np.array_equal(host(g.kv[c]), ocs.kv[c]) and np.array_equal(host(g.ix[c]), ocs.ix[c]), c
+            assert np.array_equal(host(g.kv[c]), ocs.kv[c]) and np.array_equal(host_ix(g.ix[c]), ocs.ix[c]), c
         for l in layers:
             check_attn(host(outs[l]), ref[l][0])
             assert np.allclose(host(lses[l]), ref[l][1], atol=2e-3), f"layer {l} lse"

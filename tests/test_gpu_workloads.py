@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import synth
-from tests.gpu_util import bf16, check_attn, check_scores, check_selection, dev, host
+from tests.gpu_util import bf16, check_attn, check_scores, check_selection, dev, dev_ix, host, host_ix
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def test_decode_1m_b4_m2(c):
     base = np.arange(n_q, dtype=np.int64) * n
     nvis = np.full(n_q, n, np.int32)
     log("decode 1M: GPU path")
-    kv_d, ix_d = dev(kv), dev(ix)
+    kv_d, ix_d = dev(kv), dev_ix(ix)
     s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), ix_d, dev(base), dev(nvis), n)
     pool, topk = c.block_topk(s, dev(nvis), K=K, M=M, block_max=bm)
     out, _ = c.sparse_attn(bf16(d.q), kv_d, dev(base), topk, bf16(d.swa), dev(d.swa_start), dev(d.swa_len))
@@ -96,7 +96,7 @@ def test_decode_1m_spread_scales(c):
     d = synth.query_inputs(314, n_q)
     base = np.arange(n_q, dtype=np.int64) * n
     nvis = np.full(n_q, n, np.int32)
-    kv_d, ix_d = dev(kv), dev(ix)
+    kv_d, ix_d = dev(kv), dev_ix(ix)
     s, bm = c.index_score(bf16(d.q_idx), dev(d.head_w), ix_d, dev(base), dev(nvis), n)
     pool, topk = c.block_topk(s, dev(nvis), K=K, M=M, block_max=bm)
     out, _ = c.sparse_attn(bf16(d.q), kv_d, dev(base), topk, bf16(d.swa), dev(d.swa_start), dev(d.swa_len))
@@ -120,7 +120,7 @@ def test_decode_128k_b16_full_reindex_reuse(c):
     reuse = [synth.query_inputs(205 + i, n_q) for i in range(3)]
     base = np.arange(n_q, dtype=np.int64) * n
     nvis = np.full(n_q, n, np.int32)
-    kv_d, ix_d, base_d, nvis_d = dev(kv), dev(ix), dev(base), dev(nvis)
+    kv_d, ix_d, base_d, nvis_d = dev(kv), dev_ix(ix), dev(base), dev(nvis)
     log("128K: GPU Full layer")
     s, bm = c.index_score(bf16(full.q_idx), dev(full.head_w), ix_d, base_d, nvis_d, n)
     pool, topk_f = c.block_topk(s, nvis_d, K=K, M=M, block_max=bm)
@@ -175,13 +175,14 @@ def test_prefill_chunk4096_hist65536_m2(c):
     kv, ix = synth.random_caches(404, n)
     ci = synth.compress_inputs(405, n_new, m, first_entry=hist_entries)
     kv_new_ref, ix_new_ref = oracle.compress_pack(ci.latent, m, ci.pool_w, oracle.rope_table(ci.positions), ci.w_idx)
-    kv_d, ix_d = dev(kv), dev(ix)
+    kv_d, ix_d = dev(kv), dev_ix(ix)
     log("prefill: GPU compress of the chunk into the caches")
+    t0 = hist_entries // 32  # the history ends at a tile boundary: the chunk's entries start a tile
     c.compress_pack(bf16(ci.latent), m, dev(ci.pool_w), dev(c.rope_table(ci.positions).numpy()), bf16(ci.w_idx),
-                    kv_out=kv_d[hist_entries:], idx_out=ix_d[hist_entries:])
+                    kv_out=kv_d[hist_entries:], idx_out=ix_d[t0:])
     torch.cuda.synchronize()
     assert np.array_equal(host(kv_d[hist_entries:]), kv_new_ref)
-    assert np.array_equal(host(ix_d[hist_entries:]), ix_new_ref)
+    assert np.array_equal(host_ix(ix_d[t0:], n_new), ix_new_ref)
     kv[hist_entries:], ix[hist_entries:] = kv_new_ref, ix_new_ref
     nvis = synth.prefill_nvis(2 * hist_entries, chunk, m)
     d = synth.query_inputs(406, chunk, swa_rows=chunk + 127, swa_start=np.arange(chunk, dtype=np.int64),
