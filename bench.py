@@ -607,7 +607,7 @@ def time_schedule(torch, csa2, tokens=1 << 20, n_seq=4, steps=10, warmup=2):
 # the sources the fused append + scan kernel is built from
 INDEX_SRCS = [os.path.join(ROOT, "fp4_kv_cache_csa2_amd", "csrc", f)
               for f in ("append_index.hip", "index_tiles.hpp", "index_common.hpp", "compress_few.hpp",
-                        "csa2_device.hpp")]
+                        "block_mean.hpp", "csa2_device.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_index_traffic.json")
 
 

@@ -35,7 +35,7 @@ namespace csa2 {
 namespace idx {
 
 #ifndef CSA2_INDEX_DEPTH
-#define CSA2_INDEX_DEPTH 4
+#define CSA2_INDEX_DEPTH 3
 #endif
 constexpr int kDepth = CSA2_INDEX_DEPTH;  // tiles in flight per wave
 constexpr int kRawBuf = 0x00020000;        // buffer descriptor word 3: raw 32-bit dwords
