@@ -199,7 +199,29 @@ __device__ __forceinline__ void score_tiles(
   // a Full row streams every tile once (non-temporal loads); a candidate pool gathers blocks
   // whose tiles may share scale lines
   constexpr int kAux = kPool ? 0 : kLoadStream;
+  // A Full row's tiles (not a pool, not the single newest tile) put lane (n, g)'s bytes at the
+  // same place in every tile, so each load and store takes a per-lane offset fixed for the
+  // whole scan plus one wave-uniform offset per tile (the buffer instructions' scalar
+  // offset): the address arithmetic stays off the vector ALU.
+  constexpr bool kFast = !kPool && kPart != kNewestSlots;
+  const int32_t e_lane = rel0 + n;  // entry slot n of tile 0, from the resource's first tile (< 63)
+  const int32_t vo_plane = (e_lane >> 5) * kIdxTileBytes + kIdxPlaneBytes * g + 16 * (e_lane & 31);
+  const int32_t vo_scale = (e_lane >> 5) * kIdxTileBytes + kIdxScaleOff + 4 * (e_lane & 31);
+  const int32_t vo_score = g ? kOut : 4 * n;                   // one lane per score,
+  const int32_t vo_bmax = (g | (n & 7)) ? kOut : 4 * (n >> 3);  // one per block maximum
   auto load = [&](int32_t k, RawTile& r) {
+    if constexpr (kFast) {
+      const int32_t T = tile_of(k);                        // wave-uniform
+      const int32_t left = dead(k) ? 0 : nv - T * kTile;  // visible slots of the tile (may be <= 0)
+      r.valid = n < left;
+      const int32_t soff = T * kIdxTileBytes;
+      const int32_t vp = r.valid ? vo_plane : kOut, vs = r.valid ? vo_scale : kOut;
+      r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, vp, soff, kAux));
+      r.hi = __builtin_bit_cast(u32x4_a4,
+                                __builtin_amdgcn_raw_buffer_load_b128(rs_cache, vp, soff + 2 * kIdxPlaneBytes, kAux));
+      r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs_cache, vs, soff, kAux);
+      return;
+    }
     int32_t e = row_off(k, r.valid);
     // kNewestSlots: the entry at slot nvis - 1 was packed by this workgroup, which holds its
     // record in fresh_row; it is taken from there and not read back from the cache
@@ -224,8 +246,16 @@ __device__ __forceinline__ void score_tiles(
     // both lane halves hold the entry's score and all 8 lanes of a block its maximum; one
     // lane writes each value and the others aim past the buffer's end, so their stores
     // are dropped without a branch (as are slots past the row's end)
-    const int32_t p = tile_of(k) * kTile + n;
     const bool drop = dead(k);  // wave-uniform
+    if constexpr (kFast) {
+      const int32_t T = tile_of(k);
+      if constexpr (kScores)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, vo_score, drop ? kOut : T * (4 * kTile), 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax, vo_bmax,
+                                            drop ? kOut : T * (4 * kTile / kBlock), 0);
+      return;
+    }
+    const int32_t p = tile_of(k) * kTile + n;
     if constexpr (kScores)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, (g || drop) ? kOut : 4 * p, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax,
