@@ -249,21 +249,25 @@ struct ListScratch {
   int32_t dec[4];  // a pass's decision: digit (-1: take every matching key), remain, eq_total, total
 };
 
-// Exact selection over a list of at most kListCap keys in LDS by the K3 workgroup.  The
-// list is in ascending id order and ties go to the earlier position.  The caller may pass
-// what it already knows: every key whose bits under `mask` exceed `prefix` is selected,
-// and `remain` more are wanted among the `eq_total` keys equal to `prefix` under `mask`
+// Exact selection over a list of at most kListCap keys by the K3 workgroup.  The list is
+// in ascending id order and ties go to the earlier position.  The caller may pass what it
+// already knows: every key whose bits under `mask` exceed `prefix` is selected, and
+// `remain` more are wanted among the `eq_total` keys equal to `prefix` under `mask`
 // (eq_total < 0: not known); `shift` is the number of low bits not yet resolved.  With
 // mask == 0 the search starts below the common leading bits of the smallest and largest
 // key, so the first digit does not pile every key into one histogram bin.  Zero keys are
-// never selected.  Writes the chosen positions ascending to out[], returns their number,
-// and sets *thr to a lower bound of every selected key (the resolved prefix).  Wave w
-// owns the contiguous run [w*seg, (w+1)*seg) and holds it in registers, so a radix pass
-// is a burst of LDS atomics, a barrier, wave 0's scan of the 256 digit counts and a
-// second barrier that hands its decision to every wave (sixteen waves repeating the scan
-// would queue four deep on each SIMD).
-// The same selection with the keys given by key_of(i) (any source: LDS, or global memory
-// read straight into registers) and up to kP keys per thread (n <= kP * 1024).
+// never selected.  Writes the chosen positions ascending to out[], returns their number
+// (to every thread), and sets *thr to a lower bound of every selected key (the resolved
+// prefix).  Wave w owns the contiguous run [w*seg, (w+1)*seg) of the list, seg a whole
+// number of rounds of 64, and holds it in registers, so a radix pass is a burst of LDS
+// atomics, a barrier, wave 0's scan of the 1024 digit counts and a second barrier that
+// hands its decision to every wave (sixteen waves repeating the scan would queue four deep
+// on each SIMD).  Spreading the list over all 16 waves keeps every wave's chain of
+// atomics and ballots short: the same selection on the fewest waves that hold the list
+// (one wave for the Top-K role's ~700 keys, with no barriers in its passes) measured
+// 20.9 against 19.6 us per selection call.
+// key_of(i) gives key i from any source (LDS, or global memory read straight into
+// registers); n <= kP * 1024.
 template <int kP, class KeyFn>
 __device__ __forceinline__ int list_select_g(KeyFn key_of, int n, uint32_t prefix, uint32_t mask, int shift,
                                              int remain, int eq_total, ListScratch& s, int32_t* out, uint32_t* thr) {
@@ -278,169 +282,170 @@ __device__ __forceinline__ int list_select_g(KeyFn key_of, int n, uint32_t prefi
     s.hist[0][b] = 0u;
     s.hist[1][b] = 0u;
   }
-  const int seg = (n + kFWaves - 1) / kFWaves;
-  const int lo = min(n, wave * seg);
-  const int len = __builtin_amdgcn_readfirstlane(min(n, lo + seg) - lo);  // wave-uniform
-  *thr = 0u;
   if (remain <= 0 || n <= 0) {
     __syncthreads();
+    *thr = 0u;
     return 0;
   }
+  const int seg = ((n + kFWaves - 1) / kFWaves + 63) & ~63;
+  const int lo = min(n, wave * seg);
+  const int len = __builtin_amdgcn_readfirstlane(min(n, lo + seg) - lo);  // wave-uniform
   uint32_t kr[kP];
 #pragma unroll
   for (int j = 0; j < kP; j++) kr[j] = (64 * j + lane < len) ? key_of(lo + 64 * j + lane) : 0u;
-  if (mask == 0u) {
-    // smallest and largest non-zero key, and their count
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, cnt = 0u;
+  __syncthreads();  // the histograms are zero before any wave adds to them
+
+  const int total_sel = [&]() -> int {
+    if (mask == 0u) {
+      // smallest and largest non-zero key, and their count
+      uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, cnt = 0u;
+#pragma unroll
+      for (int j = 0; j < kP; j++) {
+        if (64 * j >= len) continue;
+        const uint32_t key = kr[j];
+        kmin = min(kmin, key != 0u ? key : 0xFFFFFFFFu);
+        kmax = max(kmax, key);
+        cnt += key != 0u ? 1u : 0u;
+      }
+      kmin = wave_min_u32(kmin);
+      kmax = wave_max_u32(kmax);
+      cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), 63);
+      if (lane == 0) {
+        s.red[0][wave] = kmin;
+        s.red[1][wave] = kmax;
+        s.red[2][wave] = cnt;
+      }
+      __syncthreads();
+      kmin = 0xFFFFFFFFu;
+      kmax = 0u;
+      cnt = 0u;
+#pragma unroll
+      for (int w = 0; w < kFWaves; w++) {
+        kmin = min(kmin, s.red[0][w]);
+        kmax = max(kmax, s.red[1][w]);
+        cnt += s.red[2][w];
+      }
+      kmin = __builtin_amdgcn_readfirstlane(kmin);
+      kmax = __builtin_amdgcn_readfirstlane(kmax);
+      cnt = __builtin_amdgcn_readfirstlane(cnt);
+      if (cnt == 0u) return 0;  // workgroup-uniform
+      const int common = kmin == kmax ? 32 : __builtin_clz(kmin ^ kmax);
+      mask = common == 0 ? 0u : (common == 32 ? 0xFFFFFFFFu : ~0u << (32 - common));
+      prefix = kmax & mask;
+      shift = 32 - common;
+      eq_total = (int)cnt;
+    }
+    for (int p = 0; shift > 0 && (eq_total < 0 || remain < eq_total); p++) {
+      const int nshift = max(shift - kLDigit, 0);
+      const uint32_t dmask = (1u << (shift - nshift)) - 1u;
+      uint32_t* h = s.hist[p % 3];
+      for (int b = tid; b < kLBins; b += kFThreads) s.hist[(p + 1) % 3][b] = 0u;  // last read two passes ago
+#pragma unroll
+      for (int j = 0; j < kP; j++) {
+        if (64 * j >= len) continue;  // uniform: the wave's remaining slots are empty
+        const uint32_t key = kr[j];
+        if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> nshift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l owns the kLPerLane digits below kLBins - kLPerLane * l (descending), read as
+        // 16-byte words: once for their sum, once for the search (fewer live registers)
+        const int hi_bin = kLBins - 1 - kLPerLane * lane;
+        const uint4* hw = reinterpret_cast<const uint4*>(h + hi_bin + 1 - kLPerLane);
+        uint32_t local = 0;
+#pragma unroll
+        for (int v = 0; v < kLPerLane / 4; v++) {
+          const uint4 w4 = hw[v];
+          local += (w4.x + w4.y) + (w4.z + w4.w);
+        }
+        const uint32_t incl = wave_incl_scan(local);
+        const int total = __builtin_amdgcn_readlane((int)incl, 63);
+        uint32_t above = incl - local;
+        int hit = -1, hit_rem = 0, hit_cnt = 0;
+        asm volatile("" ::: "memory");  // read the words again below instead of keeping them
+#pragma unroll
+        for (int v = kLPerLane / 4 - 1; v >= 0; v--) {  // descending digits: word v from its top
+          const uint4 w4 = hw[v];
+          const uint32_t cw[4] = {w4.w, w4.z, w4.y, w4.x};
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            if ((int)above < remain && remain <= (int)(above + cw[e])) {
+              hit = hi_bin + 1 - kLPerLane + 4 * v + 3 - e;
+              hit_rem = remain - (int)above;
+              hit_cnt = (int)cw[e];
+            }
+            above += cw[e];
+          }
+        }
+        const uint64_t hb = __ballot(hit >= 0);
+        const int src = hb == 0ull ? 0 : __ffsll((unsigned long long)hb) - 1;
+        // the lane reads run with the whole wave active: under a lane-0 branch the compiler
+        // may compute hit and its companions for lane 0 alone
+        const int d0 = hb == 0ull ? -1 : __builtin_amdgcn_readlane(hit, src);
+        const int d1 = __builtin_amdgcn_readlane(hit_rem, src);
+        const int d2 = __builtin_amdgcn_readlane(hit_cnt, src);
+        if (lane == 0) {
+          s.dec[0] = d0;
+          s.dec[1] = d1;
+          s.dec[2] = d2;
+          s.dec[3] = total;
+        }
+      }
+      __syncthreads();
+      const int dd = __builtin_amdgcn_readfirstlane(s.dec[0]);
+      if (dd < 0) {  // fewer matching keys than wanted: take them all
+        remain = eq_total = __builtin_amdgcn_readfirstlane(s.dec[3]);
+        break;
+      }
+      const uint32_t d = (uint32_t)dd;
+      remain = __builtin_amdgcn_readfirstlane(s.dec[1]);
+      eq_total = __builtin_amdgcn_readfirstlane(s.dec[2]);
+      prefix |= d << nshift;
+      mask |= dmask << nshift;
+      shift = nshift;
+    }
+    const bool all_eq = eq_total >= 0 && remain >= eq_total;
+    // ordered compaction: counts per wave, then each wave writes its run of the output
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < kP; j++) {
       if (64 * j >= len) continue;
       const uint32_t key = kr[j];
-      kmin = min(kmin, key != 0u ? key : 0xFFFFFFFFu);
-      kmax = max(kmax, key);
-      cnt += key != 0u ? 1u : 0u;
+      gt += __popcll(__ballot(key != 0u && (key & mask) > prefix));
+      eq += __popcll(__ballot(key != 0u && (key & mask) == prefix));
     }
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), 63);
     if (lane == 0) {
-      s.red[0][wave] = kmin;
-      s.red[1][wave] = kmax;
-      s.red[2][wave] = cnt;
+      s.wcnt[0][wave] = gt;
+      s.wcnt[1][wave] = eq;
     }
     __syncthreads();
-    kmin = 0xFFFFFFFFu;
-    kmax = 0u;
-    cnt = 0u;
-#pragma unroll
-    for (int w = 0; w < kFWaves; w++) {
-      kmin = min(kmin, s.red[0][w]);
-      kmax = max(kmax, s.red[1][w]);
-      cnt += s.red[2][w];
-    }
-    kmin = __builtin_amdgcn_readfirstlane(kmin);
-    kmax = __builtin_amdgcn_readfirstlane(kmax);
-    cnt = __builtin_amdgcn_readfirstlane(cnt);
-    if (cnt == 0u) {
-      __syncthreads();
-      return 0;
-    }
-    const int common = kmin == kmax ? 32 : __builtin_clz(kmin ^ kmax);
-    mask = common == 0 ? 0u : (common == 32 ? 0xFFFFFFFFu : ~0u << (32 - common));
-    prefix = kmax & mask;
-    shift = 32 - common;
-    eq_total = (int)cnt;
-  }
-  __syncthreads();
-  for (int p = 0; shift > 0 && (eq_total < 0 || remain < eq_total); p++) {
-    const int nshift = max(shift - kLDigit, 0);
-    const uint32_t dmask = (1u << (shift - nshift)) - 1u;
-    uint32_t* h = s.hist[p % 3];
-    for (int b = tid; b < kLBins; b += kFThreads) s.hist[(p + 1) % 3][b] = 0u;  // last read two passes ago
+    const uint32_t e_l = lane < kFWaves ? (uint32_t)s.wcnt[1][lane] : 0u;
+    const uint32_t e_incl = wave_incl_scan(e_l);
+    const uint32_t e_before = e_incl - e_l;
+    const uint32_t take = all_eq ? e_l : (uint32_t)max(0, min((int)e_l, remain - (int)e_before));
+    const uint32_t s_l = lane < kFWaves ? (uint32_t)s.wcnt[0][lane] + take : 0u;
+    const uint32_t s_incl = wave_incl_scan(s_l);
+    const int tot_sel = __builtin_amdgcn_readlane((int)s_incl, kFWaves - 1);
+    int run_eq = __builtin_amdgcn_readlane((int)e_before, wave);
+    int run_sel = __builtin_amdgcn_readlane((int)(s_incl - s_l), wave);
 #pragma unroll
     for (int j = 0; j < kP; j++) {
-      if (64 * j >= len) continue;  // uniform: the wave's remaining slots are empty
+      if (64 * j >= len) continue;
       const uint32_t key = kr[j];
-      if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> nshift) & dmask], 1u);
+      const bool is_eq = key != 0u && (key & mask) == prefix;
+      const uint64_t eqb = __ballot(is_eq);
+      const bool sel = key != 0u && ((key & mask) > prefix ||
+                                     (is_eq && (all_eq || run_eq + __popcll(eqb & lt) < remain)));
+      const uint64_t selb = __ballot(sel);
+      if (sel) out[run_sel + __popcll(selb & lt)] = lo + 64 * j + lane;
+      run_eq += __popcll(eqb);
+      run_sel += __popcll(selb);
     }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l owns the kLPerLane digits below kLBins - kLPerLane * l (descending), read as
-      // 16-byte words: once for their sum, once for the search (fewer live registers)
-      const int hi_bin = kLBins - 1 - kLPerLane * lane;
-      const uint4* hw = reinterpret_cast<const uint4*>(h + hi_bin + 1 - kLPerLane);
-      uint32_t local = 0;
-#pragma unroll
-      for (int v = 0; v < kLPerLane / 4; v++) {
-        const uint4 w4 = hw[v];
-        local += (w4.x + w4.y) + (w4.z + w4.w);
-      }
-      const uint32_t incl = wave_incl_scan(local);
-      const int total = __builtin_amdgcn_readlane((int)incl, 63);
-      uint32_t above = incl - local;
-      int hit = -1, hit_rem = 0, hit_cnt = 0;
-      asm volatile("" ::: "memory");  // read the words again below instead of keeping them
-#pragma unroll
-      for (int v = kLPerLane / 4 - 1; v >= 0; v--) {  // descending digits: word v from its top
-        const uint4 w4 = hw[v];
-        const uint32_t cw[4] = {w4.w, w4.z, w4.y, w4.x};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          if ((int)above < remain && remain <= (int)(above + cw[e])) {
-            hit = hi_bin + 1 - kLPerLane + 4 * v + 3 - e;
-            hit_rem = remain - (int)above;
-            hit_cnt = (int)cw[e];
-          }
-          above += cw[e];
-        }
-      }
-      const uint64_t hb = __ballot(hit >= 0);
-      const int src = hb == 0ull ? 0 : __ffsll((unsigned long long)hb) - 1;
-      // the lane reads run with the whole wave active: under a lane-0 branch the compiler
-      // may compute hit and its companions for lane 0 alone
-      const int d0 = hb == 0ull ? -1 : __builtin_amdgcn_readlane(hit, src);
-      const int d1 = __builtin_amdgcn_readlane(hit_rem, src);
-      const int d2 = __builtin_amdgcn_readlane(hit_cnt, src);
-      if (lane == 0) {
-        s.dec[0] = d0;
-        s.dec[1] = d1;
-        s.dec[2] = d2;
-        s.dec[3] = total;
-      }
-    }
-    __syncthreads();
-    const int dd = __builtin_amdgcn_readfirstlane(s.dec[0]);
-    if (dd < 0) {  // fewer matching keys than wanted: take them all
-      remain = eq_total = __builtin_amdgcn_readfirstlane(s.dec[3]);
-      break;
-    }
-    const uint32_t d = (uint32_t)dd;
-    remain = __builtin_amdgcn_readfirstlane(s.dec[1]);
-    eq_total = __builtin_amdgcn_readfirstlane(s.dec[2]);
-    prefix |= d << nshift;
-    mask |= dmask << nshift;
-    shift = nshift;
-  }
+    return tot_sel;
+  }();
+  __syncthreads();  // out[] is complete before its readers
   *thr = prefix;
-  const bool all_eq = eq_total >= 0 && remain >= eq_total;
-  // ordered compaction: counts per wave, then each wave writes its run of the output
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int j = 0; j < kP; j++) {
-    if (64 * j >= len) continue;
-    const uint32_t key = kr[j];
-    gt += __popcll(__ballot(key != 0u && (key & mask) > prefix));
-    eq += __popcll(__ballot(key != 0u && (key & mask) == prefix));
-  }
-  if (lane == 0) {
-    s.wcnt[0][wave] = gt;
-    s.wcnt[1][wave] = eq;
-  }
-  __syncthreads();
-  const uint32_t e_l = lane < kFWaves ? (uint32_t)s.wcnt[1][lane] : 0u;
-  const uint32_t e_incl = wave_incl_scan(e_l);
-  const uint32_t e_before = e_incl - e_l;
-  const uint32_t take = all_eq ? e_l : (uint32_t)max(0, min((int)e_l, remain - (int)e_before));
-  const uint32_t s_l = lane < kFWaves ? (uint32_t)s.wcnt[0][lane] + take : 0u;
-  const uint32_t s_incl = wave_incl_scan(s_l);
-  const int total_sel = __builtin_amdgcn_readlane((int)s_incl, kFWaves - 1);
-  int run_eq = __builtin_amdgcn_readlane((int)e_before, wave);
-  int run_sel = __builtin_amdgcn_readlane((int)(s_incl - s_l), wave);
-#pragma unroll
-  for (int j = 0; j < kP; j++) {
-    if (64 * j >= len) continue;
-    const uint32_t key = kr[j];
-    const bool is_eq = key != 0u && (key & mask) == prefix;
-    const uint64_t eqb = __ballot(is_eq);
-    const bool sel = key != 0u && ((key & mask) > prefix ||
-                                   (is_eq && (all_eq || run_eq + __popcll(eqb & lt) < remain)));
-    const uint64_t selb = __ballot(sel);
-    if (sel) out[run_sel + __popcll(selb & lt)] = lo + 64 * j + lane;
-    run_eq += __popcll(eqb);
-    run_sel += __popcll(selb);
-  }
-  __syncthreads();
   return total_sel;
 }
 
