@@ -46,8 +46,8 @@ namespace {
 constexpr int kBins = 4096;        // 12-bit histogram digit
 constexpr int kBinShift = 20;
 constexpr int kSlice = 1024;       // keys per workgroup in K2
-constexpr int kHSlice = 8192;      // keys per workgroup in K1 (fewer global histogram adds)
-constexpr int kHThreads = 1024;    // K1 workgroup size
+constexpr int kHSlice = 4096;      // keys per workgroup in K1 (8192 with 1024 threads: 0.45 us slower per call)
+constexpr int kHThreads = 512;     // K1 workgroup size
 constexpr int kGThreads = 256;     // K1 / K2 workgroup size
 constexpr int kFThreads = 1024;    // K3 workgroup size
 constexpr int kFWaves = kFThreads / 64;
