@@ -449,10 +449,15 @@ __device__ __forceinline__ int list_select_g(KeyFn key_of, int n, uint32_t prefi
   return total_sel;
 }
 
-// list_select_g over keys held in LDS (the finalize's gathered list)
+// list_select_g over keys held in LDS (the finalize's gathered list), instantiated for the
+// fewest 64-key rounds per wave that hold the list (n is workgroup-uniform)
 __device__ __forceinline__ int list_select(const uint32_t* keys, int n, uint32_t prefix, uint32_t mask, int shift,
                                            int remain, int eq_total, ListScratch& s, int32_t* out, uint32_t* thr) {
-  return list_select_g<kPer>([&](int i) { return keys[i]; }, n, prefix, mask, shift, remain, eq_total, s, out, thr);
+  auto key_of = [&](int i) { return keys[i]; };
+  if (n <= 1 * kFThreads) return list_select_g<1>(key_of, n, prefix, mask, shift, remain, eq_total, s, out, thr);
+  if (n <= 2 * kFThreads) return list_select_g<2>(key_of, n, prefix, mask, shift, remain, eq_total, s, out, thr);
+  if (n <= 4 * kFThreads) return list_select_g<4>(key_of, n, prefix, mask, shift, remain, eq_total, s, out, thr);
+  return list_select_g<kPer>(key_of, n, prefix, mask, shift, remain, eq_total, s, out, thr);
 }
 
 // Per-query view of the selection problem shared by the three kernels.
