@@ -46,8 +46,12 @@ namespace {
 constexpr int kBins = 4096;        // 12-bit histogram digit
 constexpr int kBinShift = 20;
 constexpr int kSlice = 1024;       // keys per workgroup in K2
-constexpr int kHSlice = 4096;      // keys per workgroup in K1 (8192 with 1024 threads: 0.45 us slower per call)
-constexpr int kHThreads = 512;     // K1 workgroup size
+// K1 workgroups: 4096 keys on 512 threads for a few long rows (8192 on 1024: 0.45 us slower
+// per 1M x 4 decode call), 8192 keys on 1024 threads for many rows (4096 on 512: 0.49 ->
+// 0.69 ms for 4096 causal prefill rows of up to 34816 entries)
+constexpr int kHSlice = 4096, kHThreads = 512;
+constexpr int kHSliceWide = 8192, kHThreadsWide = 1024;
+constexpr int kHWideRows = 64;     // rows from which K1 takes the wide workgroups
 constexpr int kGThreads = 256;     // K1 / K2 workgroup size
 constexpr int kFThreads = 1024;    // K3 workgroup size
 constexpr int kFWaves = kFThreads / 64;
@@ -536,19 +540,19 @@ struct Rescore {
 
 // ------------------------------------------------------------------ K1: histogram
 
-template <bool cand>
-__global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
+template <bool cand, int kSl, int kTh>
+__global__ __launch_bounds__(kTh) void topk_hist_kernel(
     const float* __restrict__ scores, const float* __restrict__ block_max, int32_t width,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M, int32_t K, Ws ws) {
   __shared__ uint32_t h[kBins];
   const int t = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   const int32_t nbw = (width + kBlock - 1) / kBlock;
   Row r = make_row(t, cand, scores, block_max ? block_max : ws.bm, width, q_nvis, pool_blocks, M, K);
-  const int32_t lo = g * kHSlice;
+  const int32_t lo = g * kSl;
   if (!cand && block_max == nullptr) {
     // block maxima from the scores (NaN never wins a comparison, so it ranks as -inf)
     float* bmw = ws.bm + (int64_t)t * nbw;
-    for (int32_t b = lo + tid; b < min(lo + kHSlice, r.nb); b += kHThreads) {
+    for (int32_t b = lo + tid; b < min(lo + kSl, r.nb); b += kTh) {
       float v[kBlock];
 #pragma unroll
       for (int o = 0; o < kBlock; o++) {  // the block's loads in flight together (j < n for o = 0)
@@ -563,15 +567,15 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
     }
     __syncthreads();
   }
-  const int32_t hi = min(lo + kHSlice, r.items());
+  const int32_t hi = min(lo + kSl, r.items());
   if (lo >= hi) return;
-  for (int b = tid; b < kBins; b += kHThreads) h[b] = 0;
+  for (int b = tid; b < kBins; b += kTh) h[b] = 0;
   __syncthreads();
-  constexpr int kPerH = kHSlice / kHThreads;
+  constexpr int kPerH = kSl / kTh;
   uint32_t keys[kPerH];
 #pragma unroll
   for (int u = 0; u < kPerH; u++) {  // every key load in flight at once
-    const int32_t i = lo + u * kHThreads + tid;
+    const int32_t i = lo + u * kTh + tid;
     keys[u] = r.item_key_clamped(i, hi);
   }
 #pragma unroll
@@ -579,10 +583,10 @@ __global__ __launch_bounds__(kHThreads) void topk_hist_kernel(
   __syncthreads();
   uint32_t* gh = ws.hist + (int64_t)t * kBins;
   if (gridDim.x == 1) {  // the only workgroup of its row: plain stores (the region starts zeroed)
-    for (int b = tid; b < kBins; b += kHThreads)
+    for (int b = tid; b < kBins; b += kTh)
       if (h[b]) gh[b] = h[b];
   } else {
-    for (int b = tid; b < kBins; b += kHThreads)
+    for (int b = tid; b < kBins; b += kTh)
       if (h[b]) atomicAdd(&gh[b], h[b]);
   }
 }
@@ -1223,12 +1227,21 @@ int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, 
     const int st = check_launch();
     if (st != CSA2_OK) return st;
   }
-  const int32_t G1 = (L.G * kSlice + kHSlice - 1) / kHSlice;
-  if (cand)
-    hipLaunchKernelGGL(topk_hist_kernel<true>, dim3(G1, n_q), dim3(kHThreads), 0, s, scores, block_max, width, q_nvis,
+  const bool wide = n_q >= kHWideRows;
+  const int32_t sl = wide ? kHSliceWide : kHSlice;
+  const int32_t G1 = (L.G * kSlice + sl - 1) / sl;
+  const dim3 g1(G1, n_q), b1(wide ? kHThreadsWide : kHThreads);
+  if (cand && wide)
+    hipLaunchKernelGGL((topk_hist_kernel<true, kHSliceWide, kHThreadsWide>), g1, b1, 0, s, scores, block_max, width,
+                       q_nvis, pool_blocks, M, K, ws);
+  else if (cand)
+    hipLaunchKernelGGL((topk_hist_kernel<true, kHSlice, kHThreads>), g1, b1, 0, s, scores, block_max, width, q_nvis,
                        pool_blocks, M, K, ws);
+  else if (wide)
+    hipLaunchKernelGGL((topk_hist_kernel<false, kHSliceWide, kHThreadsWide>), g1, b1, 0, s, scores, block_max, width,
+                       q_nvis, pool_blocks, M, K, ws);
   else
-    hipLaunchKernelGGL(topk_hist_kernel<false>, dim3(G1, n_q), dim3(kHThreads), 0, s, scores, block_max, width, q_nvis,
+    hipLaunchKernelGGL((topk_hist_kernel<false, kHSlice, kHThreads>), g1, b1, 0, s, scores, block_max, width, q_nvis,
                        pool_blocks, M, K, ws);
   int st = check_launch();
   if (st != CSA2_OK) return st;

@@ -364,6 +364,7 @@ void csa2o_block_topk(const float *scores, int32_t n_q, int32_t width, const int
     int64_t nc = 0;
     if (!pool_blocks) {
       if (nvis > width) nvis = width; /* a row holds at most width scores */
+      if (nvis < 0) nvis = 0;         /* a negative count sees nothing */
       /* g_r = max of block r over visible positions (padding = -inf) */
       int32_t nb = (nvis + block - 1) / block;
       ranked_t *g = (ranked_t *)malloc(sizeof(ranked_t) * (size_t)(nb > 0 ? nb : 1));
@@ -416,6 +417,7 @@ void csa2o_topk_bruteforce(const float *scores, int32_t n_q, int32_t width, cons
   ranked_t *cand = (ranked_t *)malloc(sizeof(ranked_t) * (size_t)(width > 0 ? width : 1));
   for (int32_t t = 0; t < n_q; t++) {
     int32_t n = q_nvis[t] < width ? q_nvis[t] : width;
+    if (n < 0) n = 0;
     for (int32_t j = 0; j < n; j++) {
       cand[j].key = rank_key(scores[(int64_t)t * width + j]);
       cand[j].id = j;

@@ -218,6 +218,36 @@ def test_block_topk_candidate_mode_exact(c, M, levels, seed):
     assert np.array_equal(host(topk), topk_ref)
 
 
+
+@pytest.mark.parametrize("mode", ["full", "candidate"])
+def test_block_topk_many_rows_exact(c, mode):
+    """72 rows (from 64 rows on, the histogram pass takes 1024-thread workgroups of 8192 keys),
+    each long enough for several such workgroups: full mode on 100000-wide rows with causal,
+    ragged visible counts, and candidate mode with 2048-block pools (16384 keys per row).
+    Bit for bit against the oracle."""
+    log(f"block_topk many rows, {mode} mode")
+    n_q, K, M = 72, 512, 2048
+    rng = np.random.default_rng(70)
+    if mode == "full":
+        width = 100000
+        nvis = (width - 19 * np.arange(n_q)[::-1] ** 2).astype(np.int32)  # 4221 .. 100000
+        nvis[5], nvis[6], nvis[7] = 0, 4097, -3
+        s = synth.random_scores(71, n_q, width, tie_frac=0.05)
+        pool_ref, topk_ref = oracle.block_topk(s, nvis, K=K, M=M)
+        pool, topk = c.block_topk(dev(s), dev(nvis), K=K, M=M)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(pool), pool_ref), "pool differs"
+        assert np.array_equal(host(topk), topk_ref), "topk differs"
+    else:
+        nvis = np.full(n_q, 131072, np.int32)
+        pool = np.stack([np.sort(rng.choice(16384, M, replace=False)) for _ in range(n_q)]).astype(np.int32)
+        pool[3, -7:] = -1
+        s = synth.random_scores(72, n_q, 8 * M, tie_frac=0.1, levels=0)
+        _, topk_ref = oracle.block_topk(s, nvis, K=K, pool_blocks=pool)
+        _, topk = c.block_topk(dev(s), dev(nvis), K=K, pool_blocks=dev(pool))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(topk), topk_ref)
+
 # ------------------------------------------------------------------ sparse attention
 @pytest.mark.parametrize("n_q,K,n_entries,seed", [(1, 512, 4096, 30), (4, 512, 3000, 31), (3, 100, 500, 32),
                                                    (600, 512, 2048, 33), (16, 512, 4096, 34), (32, 300, 2048, 35),

@@ -345,6 +345,11 @@ def test_pool_size_bound_and_short_rows():
     assert np.sum(pool[2] >= 0) == 16 and 37 in pool[2]
     # 15 full blocks plus the newest block, of which only positions 296..299 are visible
     assert np.sum(topk[2] >= 0) == 15 * 8 + 4
+    # a negative visible count sees nothing, as a zero count does
+    pool_n, topk_n = oracle.block_topk(s, np.array([-9, -1, 300], np.int32), K=512, M=16)
+    assert np.all(pool_n[:2] == -1) and np.all(topk_n[:2] == -1)
+    assert np.array_equal(pool_n[2], pool[2]) and np.array_equal(topk_n[2], topk[2])
+    assert np.all(oracle.topk_bruteforce(s, np.array([-3, 0, 0], np.int32), 512) == -1)
 
 
 # ------------------------------------------------------------------ stage 4: attention
