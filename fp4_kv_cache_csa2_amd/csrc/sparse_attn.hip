@@ -9,10 +9,12 @@
 // Design.  A workgroup of 4 waves serves one query, 16 of its 64 heads and a run of its key
 // chunks (64 keys each: the selected entries, gathered 288-byte rows, then the window rows);
 // the chunks' rows are fetched a chunk ahead into registers and decoded once into one
-// row-major bf16 LDS tile.  For small batches a query's chunks are split across workgroups
-// (one chunk each at batch 4: the chain of dependent loads per workgroup stays short), each
-// writing an unnormalised partial (o, m, l) that a merge kernel combines exactly like
-// flash-decoding; large batches run every chunk of a head group in one workgroup.  Every key value is exact in bf16: an E2M1 code times an E4M3 scale has at
+// row-major bf16 LDS tile.  A query's chunks are split across workgroups (one chunk each at
+// batch 4: the chain of dependent loads per workgroup stays short), each writing an
+// unnormalised partial (o, m, l) that a merge kernel combines exactly like flash-decoding.
+// From 8 queries on, one workgroup serves all 64 heads of a (query, split), so each chunk is
+// decoded once per query; once the batch alone fills the CUs there are no splits.
+// Every key value is exact in bf16: an E2M1 code times an E4M3 scale has at
 // most 6 significant bits, an FP8 window value 4, a bf16 window value is one; the query is
 // bf16 as given.  So QK^T has exact products for inputs of any magnitude, with fp32 sums.
 //   QK^T  wave w scores keys 16w .. 16w + 15 of the chunk for the 16 heads
@@ -452,18 +454,25 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_cache,
     const int64_t* __restrict__ q_base, const int32_t* __restrict__ topk, int32_t K,
     const void* __restrict__ swa_v, int64_t swa_ring, const int64_t* __restrict__ swa_start,
-    const int32_t* __restrict__ swa_len, float scale, int32_t n_q, int32_t n_chunks, float* __restrict__ out,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ swa_len, float scale, int32_t n_q, int32_t n_chunks, int32_t chunks_per_split,
+    int32_t n_splits, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml) {
   __shared__ WideShared sh;
-  const int t = blockIdx.x;
+  // workgroup -> (query, split): a query's splits take consecutive slots of one XCD (slot j
+  // of XCD x is workgroup 8j + x) and queries go round-robin over the XCDs
+  const int L = blockIdx.x;
+  const int x = L % kXcds, j = L / kXcds;
+  const int t = (j / n_splits) * kXcds + x, split = j % n_splits;
   if (t >= n_q) return;
+  const int c_begin = split * chunks_per_split;
+  const int c_end = min(c_begin + chunks_per_split, n_chunks);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
   KeyStager<kFp8Win> ks(kv_cache, topk + (int64_t)t * K, K, swa_v, swa_ring, q_base[t], swa_start[t], swa_len[t], tid);
 
-  int32_t id_next = n_chunks > 0 ? ks.load_id(0) : -1;
-  int32_t id_after = n_chunks > 1 ? ks.load_id(1) : -1;
+  int32_t id_next = c_begin < c_end ? ks.load_id(c_begin) : -1;
+  int32_t id_after = c_begin + 1 < c_end ? ks.load_id(c_begin + 1) : -1;
   __builtin_amdgcn_sched_barrier(0);
   // query fragments (A of QK^T): head 16w + i, dims 32s + 8g .. +7, bf16 as given
   bf16x8 qa[16];
@@ -474,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
   KeyRaw raw;
-  if (n_chunks > 0) ks.fetch(0, id_next, raw);
+  if (c_begin < c_end) ks.fetch(c_begin, id_next, raw);
 
   f32x4 o[32];  // output dims 16dt + i, heads 16w + 4g + r
 #pragma unroll
@@ -488,12 +497,12 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(
   __bf16* ph_w = sh.p[w][0];
   __bf16* pl_w = sh.p[w][1];
 
-  for (int c = 0; c < n_chunks; c++) {
+  for (int c = c_begin; c < c_end; c++) {
     __syncthreads();  // the previous chunk's LDS reads are done
     ks.stage(raw, sh);
-    if (c + 1 < n_chunks) {  // the next chunk's gather overlaps this chunk's math
+    if (c + 1 < c_end) {  // the next chunk's gather overlaps this chunk's math
       ks.fetch(c + 1, id_after, raw);
-      id_after = c + 2 < n_chunks ? ks.load_id(c + 2) : -1;
+      id_after = c + 2 < c_end ? ks.load_id(c + 2) : -1;
     }
     __syncthreads();
 
@@ -587,22 +596,32 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(
     }
   }
 
-  // ---- epilogue: lane holds O[head 16w + 4g + r][dim 16dt + i].  The rows go out through
-  // the idle key tile: each wave stages its 16 heads x 256 dims in fp32, then reads whole
-  // rows back as float4, so every global store instruction writes 1 KB.
+  // ---- epilogue: lane holds O[head 16w + 4g + r][dim 16dt + i].  One split: the normalised
+  // output and lse.  Several: this split's unnormalised o and its (m, l) per head, slot
+  // (t, split, head) of the workspace.  The rows go out through the idle key tile: each wave
+  // stages its 16 heads x 256 dims in fp32, then reads whole rows back as float4, so every
+  // global store instruction writes 1 KB.
+  const bool single = n_splits == 1;
+  const int64_t slot = (int64_t)t * n_splits + split;
   float inv[4];
 #pragma unroll
-  for (int r = 0; r < 4; r++) inv[r] = l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f;
-  if (lse != nullptr && i == 0) {
+  for (int r = 0; r < 4; r++) inv[r] = single ? (l_run[r] > 0.0f ? 1.0f / l_run[r] : 0.0f) : 1.0f;
+  if (i == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; r++)
-      lse[(int64_t)t * kHeads + 16 * w + 4 * g + r] =
-          l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
+    for (int r = 0; r < 4; r++) {
+      const int h = 16 * w + 4 * g + r;
+      if (!single) {
+        ws_ml[(slot * kHeads + h) * 2 + 0] = m_run[r];
+        ws_ml[(slot * kHeads + h) * 2 + 1] = l_run[r];
+      } else if (lse != nullptr) {
+        lse[(int64_t)t * kHeads + h] = l_run[r] > 0.0f ? m_run[r] + __logf(l_run[r]) : -__builtin_inff();
+      }
+    }
   }
   constexpr int kOStride = 256 + 4;  // floats per staged row (the padding spreads the banks)
   static_assert(kWaves * 16 * kOStride * 4 <= (int)sizeof(sh.k), "staged rows fit in the key tile");
   float* stage_o = reinterpret_cast<float*>(sh.k) + w * 16 * kOStride;
-  float* orow0 = out + ((int64_t)t * kHeads + 16 * w) * kD;
+  float* orow0 = (single ? out + (int64_t)t * kHeads * kD : ws_o + slot * kHeads * kD) + (int64_t)16 * w * kD;
   __syncthreads();  // every wave is done reading the key tile
 #pragma unroll
   for (int half = 0; half < 2; half++) {
@@ -627,17 +646,21 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(
 // split's (m, l) and o slice load at once (splits <= kMaxSplits), then one pass combines.
 constexpr int kMaxSplits = (kMaxTopK + kMaxSwa + kChunk - 1) / kChunk;
 
+// kUnitHeads: heads per unit of the attention launch, 16 for the head-group kernel (a unit is a
+// (query, head group)), 64 for the all-heads kernel (a unit is a query).
+template <int kUnitHeads>
 __global__ __launch_bounds__(128) void sparse_attn_merge_kernel(const float* __restrict__ ws_o,
                                                                 const float* __restrict__ ws_ml,
                                                                 int32_t n_splits, int32_t n_q,
                                                                 float* __restrict__ out,
                                                                 float* __restrict__ lse) {
-  // workgroup -> (query, head) on the XCD that ran the head's (query, head group) unit in the
-  // attention launch (the same dealing: slot j of XCD x, 16 heads per unit), so the partials
-  // it reads were written through that XCD's L2
+  // workgroup -> (query, head) on the XCD that ran the head's unit in the attention launch (the
+  // same dealing: slot j of XCD x, kUnitHeads heads per unit), so the partials it reads were
+  // written through that XCD's L2
+  constexpr int kUnitsPerQuery = kHeads / kUnitHeads;
   const int L = blockIdx.x, x = L % kXcds, j = L / kXcds;
-  const int unit = (j / kHeadGroup) * kXcds + x;
-  const int t = unit / kGroups, h = (unit % kGroups) * kHeadGroup + j % kHeadGroup, tid = threadIdx.x;
+  const int unit = (j / kUnitHeads) * kXcds + x;
+  const int t = unit / kUnitsPerQuery, h = (unit % kUnitsPerQuery) * kUnitHeads + j % kUnitHeads, tid = threadIdx.x;
   if (t >= n_q) return;
   float m[kMaxSplits], l[kMaxSplits];
   float4 v[kMaxSplits];
@@ -674,17 +697,23 @@ __global__ __launch_bounds__(128) void sparse_attn_merge_kernel(const float* __r
   if (lse != nullptr && tid == 0) lse[(int64_t)t * kHeads + h] = Lsum > 0.0f ? M + __logf(Lsum) : -__builtin_inff();
 }
 
-// How a query's chunks are split: at most one workgroup per CU (a workgroup's registers and
-// LDS allow one per CU), all of them running at once -- one chunk each at batch 4 -- and no
-// splits once the batch alone fills the GPU.
+// How a query's chunks are split.  From kWideFrom queries on, the all-heads kernel: one
+// workgroup per (query, split), each chunk decoded once for all 64 heads, with as many splits
+// as fill the CUs once (none once the batch alone fills them).  Below, the head-group kernel:
+// 4 workgroups per (query, split), at most one workgroup per CU (a workgroup's registers
+// and LDS allow one per CU), all of them running at once -- one chunk each at batch 4.
+constexpr int32_t kWideFrom = 8;
+
 struct Plan {
   int32_t n_chunks, chunks_per_split, n_splits;
+  bool wide;
 };
 
 Plan make_plan(int32_t n_q, int32_t K) {
   Plan p;
   p.n_chunks = (K + kMaxSwa + kChunk - 1) / kChunk;
-  const int32_t wgs = kGroups * (n_q > 0 ? n_q : 1);
+  p.wide = n_q >= kWideFrom;
+  const int32_t wgs = (p.wide ? 1 : kGroups) * (n_q > 0 ? n_q : 1);
   int32_t want = kCUs / wgs;
   if (want < 1) want = 1;
   if (want > p.n_chunks) want = p.n_chunks;
@@ -729,25 +758,31 @@ int launch_sparse_attn(const uint16_t* q_bf16, const uint8_t* kv_cache, const in
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   float* ws_o = (float*)workspace;
   float* ws_ml = need > 0 ? ws_o + (size_t)n_q * p.n_splits * kHeads * kD : nullptr;
-  if (p.n_splits == 1) {  // the batch fills the GPU: one workgroup per query, all 64 heads
-    hipLaunchKernelGGL(sparse_attn_wide_kernel<kFp8Win>, dim3((unsigned)n_q), dim3(kThreads), 0, (hipStream_t)stream,
-                       q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start, swa_len, scale, n_q, p.n_chunks,
-                       out, lse);
-    return check_launch();
-  }
-  // units (see the kernel) rounded up to whole rows of 8, times the workgroups per unit
-  const int64_t units = p.n_splits > 1 ? (int64_t)n_q * kGroups : (int64_t)n_q;
-  const int64_t per = p.n_splits > 1 ? p.n_splits : kGroups;
+  // units (see the kernels) rounded up to whole rows of 8, times the workgroups per unit: the
+  // all-heads kernel's unit is a query with its splits; the head-group kernel's is a (query,
+  // head group) with its splits, or without splits a query with its 4 head groups
+  const bool hg_units = !p.wide && p.n_splits > 1;
+  const int64_t units = hg_units ? (int64_t)n_q * kGroups : (int64_t)n_q;
+  const int64_t per = (p.wide || hg_units) ? p.n_splits : kGroups;
   const int64_t grid = (units + kXcds - 1) / kXcds * kXcds * per;
   if (grid > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(sparse_attn_kernel<kFp8Win>, dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)stream, q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start, swa_len, scale,
-                     n_q, p.n_chunks, p.chunks_per_split, p.n_splits, out, lse, ws_o, ws_ml);
+  if (p.wide)
+    hipLaunchKernelGGL(sparse_attn_wide_kernel<kFp8Win>, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start, swa_len, scale, n_q, p.n_chunks,
+                       p.chunks_per_split, p.n_splits, out, lse, ws_o, ws_ml);
+  else
+    hipLaunchKernelGGL(sparse_attn_kernel<kFp8Win>, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       q_bf16, kv_cache, q_base, topk, K, swa, swa_ring, swa_start, swa_len, scale, n_q, p.n_chunks,
+                       p.chunks_per_split, p.n_splits, out, lse, ws_o, ws_ml);
   int st = check_launch();
   if (st != CSA2_OK || p.n_splits <= 1) return st;
-  const int64_t merge_grid = (units + kXcds - 1) / kXcds * kXcds * kHeadGroup;
-  hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3((unsigned)merge_grid), dim3(128), 0, (hipStream_t)stream, ws_o,
-                     ws_ml, p.n_splits, n_q, out, lse);
+  const int64_t merge_grid = (units + kXcds - 1) / kXcds * kXcds * (p.wide ? kHeads : kHeadGroup);
+  if (p.wide)
+    hipLaunchKernelGGL(sparse_attn_merge_kernel<kHeads>, dim3((unsigned)merge_grid), dim3(128), 0, (hipStream_t)stream,
+                       ws_o, ws_ml, p.n_splits, n_q, out, lse);
+  else
+    hipLaunchKernelGGL(sparse_attn_merge_kernel<kHeadGroup>, dim3((unsigned)merge_grid), dim3(128), 0,
+                       (hipStream_t)stream, ws_o, ws_ml, p.n_splits, n_q, out, lse);
   return check_launch();
 }
 

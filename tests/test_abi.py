@@ -74,7 +74,7 @@ def test_host_validation_rejects_before_launch(lib):
                                 None, 1, fake, 1 << 30, None) == -1  # q not 16-B aligned
     assert lib.csa2_sparse_attn_workspace(4, 512) > 0  # small batches split a query's keys
     assert lib.csa2_sparse_attn_workspace(1 << 16, 512) == 0  # large ones do not
-    assert lib.csa2_sparse_attn_workspace(32, 512) > 0 and lib.csa2_sparse_attn_workspace(33, 512) == 0
+    assert lib.csa2_sparse_attn_workspace(128, 512) > 0 and lib.csa2_sparse_attn_workspace(129, 512) == 0
 
 
 def test_fp8_window_entry_points_validate_before_launch(lib):

@@ -277,7 +277,9 @@ def test_sparse_attn(c, n_q, K, n_entries, seed):
     assert np.allclose(host(lse)[fin], lse_ref[fin], atol=2e-3)
 
 
-@pytest.mark.parametrize("n_q", [3, 40])  # 40: a batch with no key splits (the all-heads kernel)
+# 3: the head-group kernel with key splits; 40: the all-heads kernel with key splits;
+# 260: the all-heads kernel without splits (the batch alone fills the CUs)
+@pytest.mark.parametrize("n_q", [3, 40, 260])
 def test_sparse_attn_extreme_ranges(c, n_q):
     """Inputs outside f16's range, which bf16 holds exactly: query heads scaled by 1e5, by 1e-6
     and mixed (+-1e5 beside +-1e-6 in one head), window rows scaled by 2^-20 (values below
