@@ -5,12 +5,15 @@
 // §2.4.4) and then scores every visible entry for the step's query ([ZB] §3.3.2, §2.3.4; [DF]
 // §4.7).  Only the scores of the tile of 32 slots holding the new entry depend on it, so one
 // launch does both:
-//   - workgroup 0 of query t compresses the newest entry of t's sequence into row
-//     q_base[t] + q_nvis[t] - 1 (compress_entry_wg of compress_few.hpp), then scores that
-//     tile, taking the new entry's indexer row from its own LDS (index_tiles.hpp,
-//     kNewestSlots);
+//   - one workgroup per query t compresses the newest entry of t's sequence into row
+//     q_base[t] + q_nvis[t] - 1 (compress_entry_lds / compress_entry_wg of compress_few.hpp),
+//     then scores that tile, taking the new entry's indexer row from its own LDS
+//     (index_tiles.hpp, kNewestSlots);
 //   - the other workgroups score every other tile of t's row and read none of that tile's
 //     entries (kOlderSlots).
+// The bf16-query launch uses workgroups of 12 waves that fill a CU each
+// (append_index_wide_kernel); the MXFP4-query and HISA launches use 4-wave workgroups, the
+// append workgroup being x = 0 of row t.
 // No workgroup reads what another writes, so there is no cross-workgroup synchronisation
 // (a device-scope fence here costs a write-back of the L2 while the scan streams).  The
 // bytes and scores are those of csa2_compress_append followed by csa2_index_score: the
@@ -32,7 +35,7 @@ using namespace idx;
 
 constexpr int kAppendWgs = 1;  // append workgroups per query
 
-// kScores = false (bf16 query): block maxima only, the score row is not written
+// The MXFP4-query launch (the bf16 one is append_index_wide_kernel below).
 template <bool kFp4Q, bool kScores = true>
 __global__ __launch_bounds__(kThreads) void append_index_kernel(
     const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
@@ -56,6 +59,49 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
                     idx_cache, sh);
   score_tiles<false, kFp4Q, kNewestSlots, false, kScores>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width,
                                                           scores, block_max, t, wave, kWaves, sh.idx_row);
+}
+
+// The bf16-query launch in workgroups of 12 waves, which fill a CU each (3 waves per SIMD):
+// the waves sharing a SIMD then belong to one workgroup, dispatched together, so none of them
+// is favoured for being older (with three 4-wave workgroups per CU the last-dispatched third
+// of the scan finished about 6 us after the first on the 1M-context batch-4 step), and each
+// append workgroup has a CU to itself and its W_idx rows in LDS (compress_entry_lds).
+// Workgroups 0 .. n_q - 1 append query t = blockIdx.x's entry and score the tile holding it
+// (first wave); workgroup n_q + s scans tiles j, j + per_q, ... of query s % n_q (j = s / n_q),
+// its waves claiming them one at a time: the 3 waves sharing a SIMD are still issued oldest
+// first, and with equal static shares the youngest third finished about 6 us after the oldest.
+constexpr int kWideWaves = 12;
+constexpr int kWideThreads = 64 * kWideWaves;
+
+template <bool kScores>
+__global__ __launch_bounds__(kWideThreads) void append_index_wide_kernel(
+    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
+    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
+    const void* __restrict__ q_in, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
+    const int32_t* __restrict__ q_nvis, int32_t n_q, int32_t width, float* __restrict__ scores,
+    float* __restrict__ block_max, int64_t w_stride, int32_t per_q) {
+  const int L = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  if (L >= n_q) {  // tiles j, j + per_q, ... of query t, claimed one at a time by the 12 waves
+    __shared__ uint32_t claim;
+    if (threadIdx.x == 0) claim = 0u;
+    __syncthreads();
+    const int s = L - n_q, t = s % n_q, j = s / n_q;
+    score_tiles<false, false, kOlderSlots, false, kScores, true>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0,
+                                                                 width, scores, block_max, t, j, per_q, nullptr,
+                                                                 nullptr, &claim);
+    return;
+  }
+  const int t = L;
+  __shared__ EntryShared sh;
+  __shared__ WRows wl;
+  const int32_t nvis = q_nvis[t];
+  const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
+  compress_entry_lds<kWideWaves>(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride, rope_cs + (int64_t)t * kDRope,
+                                 w_idx, row, kv_cache, idx_cache, sh, wl);
+  if (wave != 0) return;  // the newest tile is one tile: one wave scores it
+  score_tiles<false, false, kNewestSlots, false, kScores>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width,
+                                                          scores, block_max, t, 0, 1, sh.idx_row);
 }
 
 // The query of t packed to MXFP4 into LDS by the whole workgroup, by the rules of
@@ -146,8 +192,19 @@ __global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
 }
 
 // workgroups of each kernel of this file that fit on the device at once (per device)
-std::atomic<int> resident_entry[kMaxDevices], resident_entry_max[kMaxDevices], resident_packq[kMaxDevices],
-    resident_mean[kMaxDevices];
+std::atomic<int> resident_entry[kMaxDevices], resident_entry_max[kMaxDevices], resident_fp4q[kMaxDevices],
+    resident_packq[kMaxDevices], resident_mean[kMaxDevices];
+
+// scan workgroups per query of append_index_wide_kernel: the resident workgroups left after the
+// n_q append workgroups, shared evenly (at least one, at most what the row's tiles can use)
+int32_t wide_per_q(int resident, int32_t n_q, int32_t width) {
+  const int32_t ntiles = (width + kTile - 1) / kTile;
+  int64_t per_q = (resident - (int64_t)n_q) / n_q;
+  const int64_t max_q = (ntiles + kWideWaves - 1) / kWideWaves;
+  if (per_q > max_q) per_q = max_q;
+  if (per_q < 1) per_q = 1;
+  return (int32_t)per_q;
+}
 
 // workgroups along x: the append workgroup, then the scan's share of one round of resident
 // workgroups (at least one, at most what the row's tiles can use)
@@ -198,19 +255,28 @@ int append_index_entry(const uint16_t* latent, int m, const float* pool_w, int p
   const int rc = check_args<kFp4Q>(latent, m, pool_w, per_token_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
                                   n_q, width, scores, block_max, !kFp4Q);
   if (rc != CSA2_OK || n_q == 0) return rc;
-  if (!kFp4Q && !scores) {  // block maxima only
-    const int64_t gx =
-        grid_x(resident_workgroups(append_index_kernel<false, false>, kThreads, resident_entry_max), n_q, width);
-    hipLaunchKernelGGL((append_index_kernel<false, false>), dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
+  if constexpr (!kFp4Q) {  // bf16 query: whole-CU workgroups (with scores NULL, block maxima only)
+    const int32_t per_q =
+        scores ? wide_per_q(resident_workgroups(append_index_wide_kernel<true>, kWideThreads, resident_entry), n_q, width)
+               : wide_per_q(resident_workgroups(append_index_wide_kernel<false>, kWideThreads, resident_entry_max), n_q,
+                            width);
+    const int64_t grid = (int64_t)n_q * (1 + per_q);
+    if (scores)
+      hipLaunchKernelGGL(append_index_wide_kernel<true>, dim3((unsigned)grid), dim3(kWideThreads), 0, (hipStream_t)stream,
+                         latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis, n_q, width,
+                         scores, block_max, weight_stride(m, per_token_w), per_q);
+    else
+      hipLaunchKernelGGL(append_index_wide_kernel<false>, dim3((unsigned)grid), dim3(kWideThreads), 0,
+                         (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
+                         q_nvis, n_q, width, scores, block_max, weight_stride(m, per_token_w), per_q);
+    return check_launch();
+  } else {
+    const int64_t gx = grid_x(resident_workgroups(append_index_kernel<true>, kThreads, resident_fp4q), n_q, width);
+    hipLaunchKernelGGL(append_index_kernel<true>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
                        (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
                        q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
     return check_launch();
   }
-  const int64_t gx = grid_x(resident_workgroups(append_index_kernel<false>, kThreads, resident_entry), n_q, width);
-  hipLaunchKernelGGL(append_index_kernel<kFp4Q>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads),
-                     0, (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w,
-                     q_base, q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
-  return check_launch();
 }
 
 int append_index_packq_entry(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,

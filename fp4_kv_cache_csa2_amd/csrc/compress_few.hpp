@@ -14,6 +14,8 @@
 // 512-step chain from LDS and lanes 0 .. 3 pack the 32 outputs (one MXFP4 group).
 // compress_entry_wg: one workgroup per entry and all 128 outputs, each chain reading its
 // W_idx row from global memory; it keeps the packed indexer row in LDS for its caller.
+// compress_entry_lds: the same for a workgroup that holds its CU alone, with every W_idx row
+// copied into LDS at the start.
 #pragma once
 #include "csa2_device.hpp"
 
@@ -230,6 +232,74 @@ __device__ __forceinline__ void compress_entry_wg(const uint16_t* __restrict__ l
     if (row >= 0) idx_store_word(idx_out, row, g, sub, word, code);
   }
   __syncthreads();
+}
+
+// A workgroup barrier that waits only for this wave's LDS accesses (s_waitcnt lgkmcnt(0)),
+// not for its outstanding global loads and stores as __syncthreads' release fence does; the
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// W_idx in LDS, one 1 KB row per output, rows 1040 bytes apart so that the 64 chains of a wave
+// (one row each) read different banks
+constexpr int kWRowBytes = 2 * kD + 16;
+struct WRows {
+  __attribute__((aligned(16))) uint8_t r[kIdxDim * kWRowBytes];
+};
+
+// compress_entry_wg for a workgroup of kWavesWg >= 4 waves that holds its CU alone (its LDS
+// takes most of the CU), so that the 128 KB of W_idx have the CU's memory path to themselves:
+// waves 3 .. kWavesWg - 1 copy the rows into wl (one direct-to-LDS instruction per 1 KB row,
+// every one issued at the start), the first wave pools, rotates and packs the main KV while
+// they land, and waves 1 and 2 run output o = tid - 64's chain from LDS (the same chain8
+// order as compress_entry_wg, so the bytes are the same).  Every wave calls it and passes
+// three barriers; it returns with the packed indexer row in sh.idx_row.  The cache stores are
+// not waited for.
+template <int kWavesWg>
+__device__ __forceinline__ void compress_entry_lds(const uint16_t* __restrict__ lat, int m,
+                                                   const float* __restrict__ pool_w, const float* __restrict__ cs,
+                                                   const uint16_t* __restrict__ w_idx, int64_t row,
+                                                   uint8_t* __restrict__ kv_out, uint8_t* __restrict__ idx_out,
+                                                   EntryShared& sh, WRows& wl) {
+  static_assert(kWavesWg >= 4, "a pooling wave, two chain waves and at least one copying wave");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave >= 3) {  // copy rows wave - 3, wave - 3 + (kWavesWg - 3), ...
+    for (int r = wave - 3; r < kIdxDim; r += kWavesWg - 3)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(w_idx + (int64_t)r * kD + 8 * lane),
+          (void __attribute__((address_space(3)))*)&wl.r[r * kWRowBytes], 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed
+    lds_barrier();                  // 1: the pooled entry and every row are in LDS
+    lds_barrier();                  // 2
+    lds_barrier();                  // 3
+  } else if (wave == 0) {
+    float c[8];
+    pool_rope8(lat, m, pool_w, cs, tid, c);
+    *reinterpret_cast<float4*>(&sh.c[8 * tid]) = make_float4(c[0], c[1], c[2], c[3]);
+    *reinterpret_cast<float4*>(&sh.c[8 * tid + 4]) = make_float4(c[4], c[5], c[6], c[7]);
+    lds_barrier();  // 1
+    pack_kv8(c, tid, row >= 0 ? kv_out + row * kKvBytes : nullptr);
+    lds_barrier();  // 2: every output is in sh.k
+    if (tid < 16) {  // group g = tid / 4: outputs 32g + 8 sub .. + 7
+      const int g = tid >> 2, sub = tid & 3;
+      uint32_t code;
+      const uint32_t word = pack_idx8(&sh.k[32 * g + 8 * sub], code);
+      *reinterpret_cast<uint32_t*>(&sh.idx_row[16 * g + 4 * sub]) = word;
+      if (sub == 0) sh.idx_row[64 + g] = (uint8_t)code;
+      if (row >= 0) idx_store_word(idx_out, row, g, sub, word, code);
+    }
+    lds_barrier();  // 3: sh.idx_row is complete
+  } else {  // waves 1 and 2: output o's chain
+    const int o = tid - 64;
+    lds_barrier();  // 1
+    const uint8_t* wr = &wl.r[o * kWRowBytes];
+    float a = 0.0f;
+#pragma unroll 8
+    for (int v = 0; v < kD / 8; v++) a = chain8(a, *reinterpret_cast<const uint4*>(wr + 16 * v), &sh.c[8 * v]);
+    sh.k[o] = a;
+    lds_barrier();  // 2
+    lds_barrier();  // 3
+  }
 }
 
 }  // namespace csa2

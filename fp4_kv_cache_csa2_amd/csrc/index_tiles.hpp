@@ -110,14 +110,20 @@ __device__ __forceinline__ float head_sum(const f32x16& acc, const float (&wr)[1
 // entries and the row's visible means are ceil(q_nvis[t] / 8).
 // The wave is tile `first` of the grid-stride order with stride `tstride` (wave-uniform).
 // kScores = false leaves the score row unwritten (block maxima only; scores may be NULL).
-template <bool kPool, bool kFp4Q, int kPart, bool kMeans = false, bool kScores = true>
+// kClaim: `first` and `tstride` describe the workgroup's tiles (first + c * tstride), and its
+// waves claim c = 0, 1, ... from the LDS counter *claim (zero before the first claim), so a
+// wave that the SIMD serves more often scans more tiles (waves sharing a SIMD are issued
+// oldest first).
+template <bool kPool, bool kFp4Q, int kPart, bool kMeans = false, bool kScores = true, bool kClaim = false>
 __device__ __forceinline__ void score_tiles(
     const void* __restrict__ q_in, const float* __restrict__ head_w,
     const uint8_t* __restrict__ idx_cache, const int64_t* __restrict__ q_base,
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
     int32_t width, float* __restrict__ scores, float* __restrict__ block_max, int t, int32_t first,
-    int32_t tstride, const uint8_t* fresh_row = nullptr, const uint8_t* q_rec = nullptr) {
+    int32_t tstride, const uint8_t* fresh_row = nullptr, const uint8_t* q_rec = nullptr,
+    uint32_t* claim = nullptr) {
   static_assert(!kPool || kPart == kAllSlots, "a candidate pool is scored whole");
+  static_assert(!kClaim || (!kPool && kPart != kNewestSlots), "claimed tiles: a Full row's older tiles");
   // tiles in flight per wave: the newest-tile part visits one tile
   constexpr int kPipe = kPart == kNewestSlots ? 1 : kDepth;
   const int lane = threadIdx.x & 63;
@@ -145,8 +151,11 @@ __device__ __forceinline__ void score_tiles(
   const int32_t nbw = (width + kBlock - 1) / kBlock;
   float* srow = scores + (int64_t)t * width;
 
-  if (nvis <= 0) {  // nothing visible: the row is all -inf
-    for (int32_t k = 0; k < nt; k++) {
+  if (nvis <= 0) {  // nothing visible: the row is all -inf (claimed tiles: the waves split the list statically)
+    const int32_t nt0 = kClaim ? (first < n_list ? (n_list - first + tstride - 1) / tstride : 0) : nt;
+    const int32_t k_begin = kClaim ? (int32_t)(threadIdx.x >> 6) : 0;
+    const int32_t k_step = kClaim ? (int32_t)(blockDim.x >> 6) : 1;
+    for (int32_t k = k_begin; k < nt0; k += k_step) {
       const int32_t p = tile_of(k) * kTile + n;  // (nothing visible: no newest tile)
       if (kScores && g == 0 && p < width) srow[p] = -__builtin_inff();
       if (block_max != nullptr && g == 0 && (n & 7) == 0 && p < width)
@@ -209,6 +218,17 @@ __device__ __forceinline__ void score_tiles(
   const int32_t vo_scale = (e_lane >> 5) * kIdxTileBytes + kIdxScaleOff + 4 * (e_lane & 31);
   const int32_t vo_score = g ? kOut : 4 * n;                   // one lane per score,
   const int32_t vo_bmax = (g | (n & 7)) ? kOut : 4 * (n >> 3);  // one per block maximum
+  // a Full row's older tile T (wave-uniform; T < 0: no tile, its loads return zeros)
+  auto load_tile = [&](int32_t T, RawTile& r) {
+    const int32_t left = (T < 0 || (kPart == kOlderSlots && T == t_new)) ? 0 : nv - T * kTile;  // visible slots
+    r.valid = n < left;
+    const int32_t soff = T < 0 ? 0 : T * kIdxTileBytes;
+    const int32_t vp = r.valid ? vo_plane : kOut, vs = r.valid ? vo_scale : kOut;
+    r.lo = __builtin_bit_cast(u32x4_a4, __builtin_amdgcn_raw_buffer_load_b128(rs_cache, vp, soff, kAux));
+    r.hi = __builtin_bit_cast(u32x4_a4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rs_cache, vp, soff + 2 * kIdxPlaneBytes, kAux));
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs_cache, vs, soff, kAux);
+  };
   auto load = [&](int32_t k, RawTile& r) {
     if constexpr (kFast) {
       const int32_t T = tile_of(k);                        // wave-uniform
@@ -234,6 +254,21 @@ __device__ __forceinline__ void score_tiles(
     if constexpr (kPart == kNewestSlots) {
       if (fresh) load_record_share(fresh_row, g, r);
     }
+  };
+  // the scores of a Full row's older tile T >= 0 (the newest tile's stores are dropped)
+  auto process_tile = [&](const RawTile& cur, int32_t T) {
+    f32x16 acc;
+    if constexpr (kFp4Q) {
+      acc = mfma_fp4_tile(qa, qsc, cur.lo, cur.hi, cur.sc >> (8 * g), f32x16{});
+    } else {
+      acc = mfma_bf16_tile(a, cur, g);
+    }
+    const float sc = head_sum(acc, wr, cur.valid);
+    const bool drop = kPart == kOlderSlots && T == t_new;  // wave-uniform
+    if constexpr (kScores)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, vo_score, drop ? kOut : T * (4 * kTile), 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax, vo_bmax,
+                                          drop ? kOut : T * (4 * kTile / kBlock), 0);
   };
   auto process = [&](const RawTile& cur, int32_t k) {
     f32x16 acc;
@@ -291,6 +326,36 @@ __device__ __forceinline__ void score_tiles(
   // (the scheduling barriers keep the tiles' loads in tile order, so each tile's wait
   // counts only older loads)
   RawTile pipe[kPipe];
+  if constexpr (kClaim) {
+    // claim c of the workgroup's list is tile first + c * tstride while c < n_wg; a wave's
+    // claims only grow, so its first claim past the end ends its loop
+    const int32_t n_wg = first < n_list ? (n_list - first + tstride - 1) / tstride : 0;
+    auto claim_tile = [&]() -> int32_t {
+      uint32_t c = 0;
+      if (lane == 0) c = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      c = __builtin_amdgcn_readfirstlane(c);
+      return c < (uint32_t)n_wg ? first + (int32_t)c * tstride : -1;
+    };
+    int32_t T[kPipe];
+#pragma unroll
+    for (int u = 0; u < kPipe; u++) {
+      T[u] = claim_tile();
+      load_tile(T[u], pipe[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPipe * 3));
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kPipe; u++) {
+        if (T[u] < 0) return;  // wave-uniform: every later claim is past the end too
+        process_tile(pipe[u], T[u]);
+        __builtin_amdgcn_s_setprio(2);
+        T[u] = claim_tile();
+        load_tile(T[u], pipe[u]);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < kPipe; u++) {
     load(u, pipe[u]);
