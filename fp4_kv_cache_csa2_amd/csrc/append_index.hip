@@ -67,9 +67,10 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
 // of the scan finished about 6 us after the first on the 1M-context batch-4 step), and each
 // append workgroup has a CU to itself and its W_idx rows in LDS (compress_entry_lds).
 // Workgroups 0 .. n_q - 1 append query t = blockIdx.x's entry and score the tile holding it
-// (first wave); workgroup n_q + s scans tiles j, j + per_q, ... of query s % n_q (j = s / n_q),
-// its waves claiming them one at a time: the 3 waves sharing a SIMD are still issued oldest
-// first, and with equal static shares the youngest third finished about 6 us after the oldest.
+// (first wave); workgroup n_q + s scans the groups of 4 tiles j, j + per_q, ... of query
+// s % n_q (j = s / n_q), its waves claiming the tiles one at a time: the 3 waves sharing a SIMD
+// are still issued oldest first, and with equal static shares the youngest third finished
+// about 6 us after the oldest.
 constexpr int kWideWaves = 12;
 constexpr int kWideThreads = 64 * kWideWaves;
 
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kWideThreads) void append_index_wide_kernel(
     float* __restrict__ block_max, int64_t w_stride, int32_t per_q) {
   const int L = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  if (L >= n_q) {  // tiles j, j + per_q, ... of query t, claimed one at a time by the 12 waves
+  if (L >= n_q) {  // groups of 4 tiles j, j + per_q, ... of query t, claimed a tile at a time
     __shared__ uint32_t claim;
     if (threadIdx.x == 0) claim = 0u;
     __syncthreads();
@@ -196,7 +197,7 @@ std::atomic<int> resident_entry[kMaxDevices], resident_entry_max[kMaxDevices], r
     resident_packq[kMaxDevices], resident_mean[kMaxDevices];
 
 // scan workgroups per query of append_index_wide_kernel: the resident workgroups left after the
-// n_q append workgroups, shared evenly (at least one, at most what the row's tiles can use)
+// n_q append workgroups, shared evenly (at least one, at most one per 3 groups of 4 tiles)
 int32_t wide_per_q(int resident, int32_t n_q, int32_t width) {
   const int32_t ntiles = (width + kTile - 1) / kTile;
   int64_t per_q = (resident - (int64_t)n_q) / n_q;

@@ -110,10 +110,12 @@ __device__ __forceinline__ float head_sum(const f32x16& acc, const float (&wr)[1
 // entries and the row's visible means are ceil(q_nvis[t] / 8).
 // The wave is tile `first` of the grid-stride order with stride `tstride` (wave-uniform).
 // kScores = false leaves the score row unwritten (block maxima only; scores may be NULL).
-// kClaim: `first` and `tstride` describe the workgroup's tiles (first + c * tstride), and its
-// waves claim c = 0, 1, ... from the LDS counter *claim (zero before the first claim), so a
-// wave that the SIMD serves more often scans more tiles (waves sharing a SIMD are issued
-// oldest first).
+// kClaim: `first` and `tstride` describe the workgroup's tiles in groups of 4 consecutive
+// tiles (groups first, first + tstride, ...), and its waves claim c = 0, 1, ... from the LDS
+// counter *claim (zero before the first claim): claim c is tile 4 (first + (c / 4) tstride) +
+// c % 4.  A wave that the SIMD serves more often scans more tiles (waves sharing a SIMD are
+// issued oldest first), and the 4 block maxima of a group (one 16-byte store each) fill a
+// 64-byte line from one workgroup, so one L2 writes the line back whole.
 template <bool kPool, bool kFp4Q, int kPart, bool kMeans = false, bool kScores = true, bool kClaim = false>
 __device__ __forceinline__ void score_tiles(
     const void* __restrict__ q_in, const float* __restrict__ head_w,
@@ -151,12 +153,13 @@ __device__ __forceinline__ void score_tiles(
   const int32_t nbw = (width + kBlock - 1) / kBlock;
   float* srow = scores + (int64_t)t * width;
 
+  // kClaim: tile of the workgroup's claim c (increasing with c)
+  auto claim_tile_of = [&](int32_t c) -> int32_t { return 4 * (first + (c >> 2) * tstride) + (c & 3); };
   if (nvis <= 0) {  // nothing visible: the row is all -inf (claimed tiles: the waves split the list statically)
-    const int32_t nt0 = kClaim ? (first < n_list ? (n_list - first + tstride - 1) / tstride : 0) : nt;
     const int32_t k_begin = kClaim ? (int32_t)(threadIdx.x >> 6) : 0;
     const int32_t k_step = kClaim ? (int32_t)(blockDim.x >> 6) : 1;
-    for (int32_t k = k_begin; k < nt0; k += k_step) {
-      const int32_t p = tile_of(k) * kTile + n;  // (nothing visible: no newest tile)
+    for (int32_t k = k_begin; kClaim ? claim_tile_of(k) < n_list : k < nt; k += k_step) {
+      const int32_t p = (kClaim ? claim_tile_of(k) : tile_of(k)) * kTile + n;  // (nothing visible: no newest tile)
       if (kScores && g == 0 && p < width) srow[p] = -__builtin_inff();
       if (block_max != nullptr && g == 0 && (n & 7) == 0 && p < width)
         block_max[(int64_t)t * nbw + (p >> 3)] = -__builtin_inff();
@@ -327,14 +330,14 @@ __device__ __forceinline__ void score_tiles(
   // counts only older loads)
   RawTile pipe[kPipe];
   if constexpr (kClaim) {
-    // claim c of the workgroup's list is tile first + c * tstride while c < n_wg; a wave's
-    // claims only grow, so its first claim past the end ends its loop
-    const int32_t n_wg = first < n_list ? (n_list - first + tstride - 1) / tstride : 0;
+    // a wave's claims only grow, and so do their tiles: its first claim past the row's end
+    // ends its loop
     auto claim_tile = [&]() -> int32_t {
       uint32_t c = 0;
       if (lane == 0) c = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       c = __builtin_amdgcn_readfirstlane(c);
-      return c < (uint32_t)n_wg ? first + (int32_t)c * tstride : -1;
+      const int32_t T = c < (uint32_t)n_list ? claim_tile_of((int32_t)c) : n_list;  // c < n_list: no overflow
+      return T < n_list ? T : -1;
     };
     int32_t T[kPipe];
 #pragma unroll
