@@ -720,18 +720,21 @@ def main():
     torch.cuda.synchronize()
     ms_single = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # ---- stage timings: HIP events around graphs of back-to-back launches of one stage
-    stage_rounds = 3
+    # ---- stage timings: HIP events around graphs of back-to-back launches of one stage, the
+    # median over 7 replays
+    stage_samples = 7
     st_us = {}
     for st, g in zip(timed, stage_graph):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(stage_rounds):
+        samples = []
+        for _ in range(stage_samples):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
             g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        st_us[st] = a.elapsed_time(b) * 1e3 / (stage_rounds * reps)
+            b.record()
+            torch.cuda.synchronize()
+            samples.append(a.elapsed_time(b) * 1e3 / reps)
+        st_us[st] = float(np.median(samples))
     # spread of the step time: HIP events around single replays of the multi-step graph
     per_step = []
     for _ in range(20):
