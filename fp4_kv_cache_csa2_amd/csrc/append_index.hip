@@ -192,9 +192,56 @@ __global__ __launch_bounds__(kThreads) void append_mean_index_kernel(
                                                 scores, block_max, t, wave, kWaves, sh.mean_row);
 }
 
+// HISA's bf16-query decode launch in whole-CU workgroups, as append_index_wide_kernel: n_q
+// append workgroups (compress_entry_lds, then the first wave re-packs the newest block's mean
+// record and scores the tile of block means holding it), then per_q scan workgroups per query
+// over groups of 4 tiles of block means, their waves claiming the tiles.
+__global__ __launch_bounds__(kWideThreads) void append_mean_index_wide_kernel(
+    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
+    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
+    uint8_t* __restrict__ mean_cache, const int64_t* __restrict__ mean_base, const void* __restrict__ q_in,
+    const float* __restrict__ head_w, const int64_t* __restrict__ q_base, const int32_t* __restrict__ q_nvis,
+    int32_t n_q, int32_t width, float* __restrict__ scores, float* __restrict__ block_max, int64_t w_stride,
+    int32_t per_q) {
+  const int L = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  if (L >= n_q) {
+    __shared__ uint32_t claim;
+    if (threadIdx.x == 0) claim = 0u;
+    __syncthreads();
+    const int s = L - n_q, t = s % n_q, j = s / n_q;
+    score_tiles<false, false, kOlderSlots, true, true, true>(q_in, head_w, mean_cache, mean_base, q_nvis, nullptr, 0,
+                                                             width, scores, block_max, t, j, per_q, nullptr, nullptr,
+                                                             &claim);
+    return;
+  }
+  const int t = L;
+  __shared__ MeanEntryShared sh;
+  __shared__ WRows wl;
+  const int32_t nvis = q_nvis[t];
+  const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
+  compress_entry_lds<kWideWaves>(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride, rope_cs + (int64_t)t * kDRope,
+                                 w_idx, row, kv_cache, idx_cache, sh.e, wl);
+  if (wave != 0) return;
+  if (nvis > 0 && threadIdx.x < 16) {  // lane 4g + sub: channels 32g + 8sub .. + 7
+    const int g = threadIdx.x >> 2, sub = threadIdx.x & 3;
+    const int32_t b = (nvis - 1) / kBlock;  // the newest block
+    const int cnt = nvis - b * kBlock;
+    uint32_t code;
+    const uint32_t word = block_mean_word(idx_cache, q_base[t] + (int64_t)b * kBlock, cnt, sh.e.idx_row, g, sub, code);
+    idx_store_word(mean_cache, mean_base[t] + b, g, sub, word, code);
+    *reinterpret_cast<uint32_t*>(&sh.mean_row[16 * g + 4 * sub]) = word;
+    if (sub == 0) sh.mean_row[64 + g] = (uint8_t)code;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the record is in LDS for this wave's reads
+  __builtin_amdgcn_wave_barrier();
+  score_tiles<false, false, kNewestSlots, true>(q_in, head_w, mean_cache, mean_base, q_nvis, nullptr, 0, width, scores,
+                                                block_max, t, 0, 1, sh.mean_row);
+}
+
 // workgroups of each kernel of this file that fit on the device at once (per device)
 std::atomic<int> resident_entry[kMaxDevices], resident_entry_max[kMaxDevices], resident_fp4q[kMaxDevices],
-    resident_packq[kMaxDevices], resident_mean[kMaxDevices];
+    resident_packq[kMaxDevices], resident_mean[kMaxDevices], resident_mean_fp4q[kMaxDevices];
 
 // scan workgroups per query of append_index_wide_kernel: the resident workgroups left after the
 // n_q append workgroups, shared evenly (at least one, at most one per 3 groups of 4 tiles)
@@ -304,11 +351,22 @@ int append_mean_index_entry(const uint16_t* latent, int m, const float* pool_w, 
                                   n_q, width, scores, block_max);
   if (rc != CSA2_OK || n_q == 0) return rc;
   if (!mean_cache || !mean_base || (reinterpret_cast<uintptr_t>(mean_cache) & 15)) return CSA2_ERR_INVALID_ARG;
-  const int64_t gx = grid_x(resident_workgroups(append_mean_index_kernel<false>, kThreads, resident_mean), n_q, width);
-  hipLaunchKernelGGL(append_mean_index_kernel<kFp4Q>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
-                     (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, mean_cache,
-                     mean_base, q, head_w, q_base, q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
-  return check_launch();
+  if constexpr (!kFp4Q) {  // bf16 query: whole-CU workgroups over the block means
+    const int32_t per_q =
+        wide_per_q(resident_workgroups(append_mean_index_wide_kernel, kWideThreads, resident_mean), n_q, width);
+    const int64_t grid = (int64_t)n_q * (1 + per_q);
+    hipLaunchKernelGGL(append_mean_index_wide_kernel, dim3((unsigned)grid), dim3(kWideThreads), 0, (hipStream_t)stream,
+                       latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, mean_cache, mean_base, q, head_w,
+                       q_base, q_nvis, n_q, width, scores, block_max, weight_stride(m, per_token_w), per_q);
+    return check_launch();
+  } else {
+    const int64_t gx =
+        grid_x(resident_workgroups(append_mean_index_kernel<true>, kThreads, resident_mean_fp4q), n_q, width);
+    hipLaunchKernelGGL(append_mean_index_kernel<true>, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
+                       (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, mean_cache,
+                       mean_base, q, head_w, q_base, q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
+    return check_launch();
+  }
 }
 
 }  // namespace
