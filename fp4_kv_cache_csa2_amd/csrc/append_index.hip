@@ -108,17 +108,16 @@ __global__ __launch_bounds__(kWideThreads) void append_index_wide_kernel(
 // The query of t packed to MXFP4 into LDS by the whole workgroup, by the rules of
 // csa2_quantize_q_mxfp4 (mxfp4_pack8): 512 (head, group of 32 channels, quarter) tasks over
 // the 256 threads, 4 consecutive lanes per group.
+__device__ __forceinline__ void pack_query_task(const uint16_t* __restrict__ q, uint8_t* rec, int task) {
+  const int v = task >> 4, grp = (task >> 2) & 3, sub = task & 3;
+  uint32_t code;
+  const uint32_t word = mxfp4_pack8(*reinterpret_cast<const uint4*>(q + v * kIdxDim + 32 * grp + 8 * sub), code);
+  *reinterpret_cast<uint32_t*>(rec + v * kIdxBytes + 16 * grp + 4 * sub) = word;
+  if (sub == 0) rec[v * kIdxBytes + 64 + grp] = (uint8_t)code;
+}
 __device__ __forceinline__ void pack_query_lds(const uint16_t* __restrict__ q, uint8_t* rec) {
 #pragma unroll
-  for (int it = 0; it < kIdxHeads * 16 / kThreads; it++) {
-    const int task = it * kThreads + threadIdx.x;
-    const int v = task >> 4, grp = (task >> 2) & 3, sub = task & 3;
-    uint32_t code;
-    const uint32_t word =
-        mxfp4_pack8(*reinterpret_cast<const uint4*>(q + v * kIdxDim + 32 * grp + 8 * sub), code);
-    *reinterpret_cast<uint32_t*>(rec + v * kIdxBytes + 16 * grp + 4 * sub) = word;
-    if (sub == 0) rec[v * kIdxBytes + 64 + grp] = (uint8_t)code;
-  }
+  for (int it = 0; it < kIdxHeads * 16 / kThreads; it++) pack_query_task(q, rec, it * kThreads + threadIdx.x);
   __syncthreads();
 }
 
@@ -147,6 +146,43 @@ __global__ __launch_bounds__(kThreads) void append_index_packq_kernel(
                     idx_cache, sh);
   score_tiles<false, true, kNewestSlots>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
                                          block_max, t, wave, kWaves, sh.idx_row, q_rec);
+}
+
+// The MXFP4-query step with the query packed inside the launch (append_index_packq_kernel) in
+// whole-CU workgroups of 12 waves, as append_index_wide_kernel: every workgroup packs the
+// query into LDS (the first 512 threads, one task each), n_q append workgroups, then per_q
+// claimed-tile scan workgroups per query (32.6 -> 29.3 us per launch on the 1M-context
+// batch-4 step; 16-wave workgroups, 4 waves per SIMD, spilled 7 registers and ran no faster).
+template <int kWavesWg>
+__global__ __launch_bounds__(64 * kWavesWg) void append_index_packq_wide_kernel(
+    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
+    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
+    const uint16_t* __restrict__ q_bf16, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
+    const int32_t* __restrict__ q_nvis, int32_t n_q, int32_t width, float* __restrict__ scores,
+    float* __restrict__ block_max, int64_t w_stride, int32_t per_q) {
+  const int L = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int t = L < n_q ? L : (L - n_q) % n_q;
+  __shared__ __attribute__((aligned(16))) uint8_t q_rec[kIdxHeads * kIdxBytes];
+  __shared__ uint32_t claim;
+  if (threadIdx.x < kIdxHeads * 16) pack_query_task(q_bf16 + (int64_t)t * kIdxHeads * kIdxDim, q_rec, threadIdx.x);
+  if (threadIdx.x == 0) claim = 0u;
+  __syncthreads();
+  if (L >= n_q) {
+    score_tiles<false, true, kOlderSlots, false, true, true>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0,
+                                                             width, scores, block_max, t, (L - n_q) / n_q, per_q,
+                                                             nullptr, q_rec, &claim);
+    return;
+  }
+  __shared__ EntryShared sh;
+  __shared__ WRows wl;
+  const int32_t nvis = q_nvis[t];
+  const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
+  compress_entry_lds<kWavesWg>(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride,
+                                  rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache, idx_cache, sh, wl);
+  if (wave != 0) return;
+  score_tiles<false, true, kNewestSlots>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
+                                         block_max, t, 0, 1, sh.idx_row, q_rec);
 }
 
 struct MeanEntryShared {
@@ -334,10 +370,13 @@ int append_index_packq_entry(const uint16_t* latent, int m, const float* pool_w,
   const int rc = check_args<false>(latent, m, pool_w, per_token_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis,
                                    n_q, width, scores, block_max);
   if (rc != CSA2_OK || n_q == 0) return rc;
-  const int64_t gx = grid_x(resident_workgroups(append_index_packq_kernel, kThreads, resident_packq), n_q, width);
-  hipLaunchKernelGGL(append_index_packq_kernel, dim3((unsigned)gx, (unsigned)n_q), dim3(kThreads), 0,
+  const int32_t per_q =
+      wide_per_q(resident_workgroups(append_index_packq_wide_kernel<kWideWaves>, 64 * kWideWaves, resident_packq), n_q,
+                 width);
+  const int64_t grid = (int64_t)n_q * (1 + per_q);
+  hipLaunchKernelGGL(append_index_packq_wide_kernel<kWideWaves>, dim3((unsigned)grid), dim3(64 * kWideWaves), 0,
                      (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
-                     q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
+                     q_nvis, n_q, width, scores, block_max, weight_stride(m, per_token_w), per_q);
   return check_launch();
 }
 

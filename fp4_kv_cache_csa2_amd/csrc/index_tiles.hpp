@@ -356,6 +356,7 @@ __device__ __forceinline__ void score_tiles(
         T[u] = claim_tile();
         load_tile(T[u], pipe[u]);
         __builtin_amdgcn_s_setprio(0);
+        if constexpr (kFp4Q) __builtin_amdgcn_sched_barrier(0);  // tiles' loads in tile order
       }
     }
   }
