@@ -105,9 +105,9 @@ __global__ __launch_bounds__(kWideThreads) void append_index_wide_kernel(
                                                           scores, block_max, t, 0, 1, sh.idx_row);
 }
 
-// The query of t packed to MXFP4 into LDS by the whole workgroup, by the rules of
-// csa2_quantize_q_mxfp4 (mxfp4_pack8): 512 (head, group of 32 channels, quarter) tasks over
-// the 256 threads, 4 consecutive lanes per group.
+// One of the 512 tasks (head, group of 32 channels, quarter) of packing the query of t to
+// MXFP4 into LDS by the rules of csa2_quantize_q_mxfp4 (mxfp4_pack8), 4 consecutive lanes per
+// group.
 __device__ __forceinline__ void pack_query_task(const uint16_t* __restrict__ q, uint8_t* rec, int task) {
   const int v = task >> 4, grp = (task >> 2) & 3, sub = task & 3;
   uint32_t code;
@@ -115,44 +115,13 @@ __device__ __forceinline__ void pack_query_task(const uint16_t* __restrict__ q, 
   *reinterpret_cast<uint32_t*>(rec + v * kIdxBytes + 16 * grp + 4 * sub) = word;
   if (sub == 0) rec[v * kIdxBytes + 64 + grp] = (uint8_t)code;
 }
-__device__ __forceinline__ void pack_query_lds(const uint16_t* __restrict__ q, uint8_t* rec) {
-#pragma unroll
-  for (int it = 0; it < kIdxHeads * 16 / kThreads; it++) pack_query_task(q, rec, it * kThreads + threadIdx.x);
-  __syncthreads();
-}
 
-// append_index_kernel<true> with the bf16 query packed inside the launch: every workgroup
-// packs it into LDS first (a few hundred bytes of work), which saves the packer's launch
-__global__ __launch_bounds__(kThreads) void append_index_packq_kernel(
-    const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
-    const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
-    const uint16_t* __restrict__ q_bf16, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
-    const int32_t* __restrict__ q_nvis, int32_t width, float* __restrict__ scores, float* __restrict__ block_max,
-    int64_t w_stride) {
-  const int t = blockIdx.y;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  __shared__ __attribute__((aligned(16))) uint8_t q_rec[kIdxHeads * kIdxBytes];
-  pack_query_lds(q_bf16 + (int64_t)t * kIdxHeads * kIdxDim, q_rec);
-  if (blockIdx.x >= kAppendWgs) {
-    score_tiles<false, true, kOlderSlots>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
-                                          block_max, t, (int32_t)(blockIdx.x - kAppendWgs) * kWaves + wave,
-                                          (int32_t)(gridDim.x - kAppendWgs) * kWaves, nullptr, q_rec);
-    return;
-  }
-  __shared__ EntryShared sh;
-  const int32_t nvis = q_nvis[t];
-  const int64_t row = nvis > 0 ? q_base[t] + nvis - 1 : -1;  // nothing visible: nothing appended
-  compress_entry_wg(latent + (int64_t)t * m * kD, m, pool_w + t * w_stride, rope_cs + (int64_t)t * kDRope, w_idx, row, kv_cache,
-                    idx_cache, sh);
-  score_tiles<false, true, kNewestSlots>(q_bf16, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width, scores,
-                                         block_max, t, wave, kWaves, sh.idx_row, q_rec);
-}
-
-// The MXFP4-query step with the query packed inside the launch (append_index_packq_kernel) in
-// whole-CU workgroups of 12 waves, as append_index_wide_kernel: every workgroup packs the
-// query into LDS (the first 512 threads, one task each), n_q append workgroups, then per_q
-// claimed-tile scan workgroups per query (32.6 -> 29.3 us per launch on the 1M-context
-// batch-4 step; 16-wave workgroups, 4 waves per SIMD, spilled 7 registers and ran no faster).
+// The MXFP4-query step with the bf16 query packed inside the launch (which saves the packer's
+// launch), in whole-CU workgroups of 12 waves as append_index_wide_kernel: every workgroup
+// packs the query into LDS (the first 512 threads, one task each, by the rules of
+// csa2_quantize_q_mxfp4), n_q append workgroups, then per_q claimed-tile scan workgroups per
+// query (32.6 -> 29.3 us per launch on the 1M-context batch-4 step against 4-wave workgroups
+// at 4 per CU; 16-wave workgroups, 4 waves per SIMD, spilled 7 registers and ran no faster).
 template <int kWavesWg>
 __global__ __launch_bounds__(64 * kWavesWg) void append_index_packq_wide_kernel(
     const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
