@@ -3,7 +3,7 @@ MXFP4-query twin): bit for bit what csa2_compress_append followed by csa2_index_
 produce (cache bytes, scores, block maxima), the appended bytes against the oracle's
 compressor, the scores against the oracle's indexer over the updated cache, two calls in a
 row, ragged rows, an empty row, rows whose newest entry opens a block or a tile, rows
-shorter or longer than the score width, 70 queries at once, the MXFP4 query packed inside
+shorter or longer than the score width, 70 and 300 queries at once, the MXFP4 query packed inside
 the launch (special scales included), and the 1M-context batch-4 decode in the launch geometry the bench uses.  The appended rows start out holding other bytes,
 so a score computed from stale bytes would show."""
 import dataclasses
@@ -83,6 +83,8 @@ CASES = [
     ([5000, 4999, 4993, 4992], 5000, 2),
     ([900, 850, 800, 799, 33], 800, 2),        # rows longer than the width: the new entry has no slot
     ([200 - (i % 9) for i in range(70)], 256, 1),  # 70 queries, one sequence each
+    # 300 queries: more workgroups than fit on the device at once (several rounds)
+    ([96 + (i % 31) for i in range(300)], 128, 2),
 ]
 
 

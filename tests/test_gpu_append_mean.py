@@ -91,6 +91,8 @@ CASES = [
     ([256, 257, 255, 264, 2048], 300, 1),      # the newest mean at a tile edge (slots 31 and 32)
     ([900, 850, 800, 257], 100, 2),            # more visible means than the width: no newest slot scored
     ([1600 - 3 * (i % 11) for i in range(70)], 200, 1),  # 70 queries
+    # 300 queries: more workgroups than fit on the device at once (several rounds)
+    ([400 - (i % 13) for i in range(300)], 64, 2),
 ]
 
 
