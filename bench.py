@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-secondary", action="store_true", help="skip the other seeded workloads")
     p.add_argument("--no-peaks", action="store_true", help="skip the copy / GEMM peak measurements")
     p.add_argument("--no-control", action="store_true", help="skip the 5-copy cache control")
+    p.add_argument("--no-handoff", action="store_true",
+                   help="the selection takes its own first pass instead of the fused launch counting it")
     p.add_argument("--calibration-copy-mib", type=int, default=0,
                    help="run one device copy of this many MiB before timing (counter calibration)")
     return p.parse_args()
@@ -220,8 +222,12 @@ class Decode1M:
     it, attend) and Reuse layers (attend with the Reindex indices)."""
 
     def __init__(self, torch, csa2, tokens, n_seq=4, m=2, K=512, M=2048, ncopy=NCOPY, extra_layers=0,
-                 fp8_window=False, fp4q=False, hisa=False):
+                 fp8_window=False, fp4q=False, hisa=False, handoff=True):
         self.torch, self.csa2 = torch, csa2
+        # handoff (bf16 query, no HISA): the fused launch also counts the selection's first pass
+        # into the selection workspace (csa2_append_index_score_sel) and the selection skips it
+        # (csa2_block_topk_prebuilt)
+        self.handoff = handoff and not (fp4q or hisa)
         self.fp8 = fp8_window
         self.fp4q = fp4q
         self.hisa = hisa
@@ -245,6 +251,8 @@ class Decode1M:
         self.lse = torch.empty((n_seq, 64), dtype=torch.float32, device=dev)
         # the selection workspace starts zeroed and every call leaves its histogram zeroed
         self.ws_sel = torch.zeros(max(4, csa2.block_topk_workspace(n_seq, n, M, K)), dtype=torch.uint8, device=dev)
+        # the fused stage timed on its own counts into this region, which no selection reads
+        self.ws_hist_alone = torch.zeros(n_seq * 4096 * 4, dtype=torch.uint8, device=dev)
         self.ws_att = torch.empty(max(1, csa2.sparse_attn_workspace(n_seq, K)), dtype=torch.uint8, device=dev)
         # the step appends each sequence's newest entry into its cache slot, the last visible row
         # (the batch's caches were packed from the same latents, so every replay rewrites the same
@@ -300,15 +308,17 @@ class Decode1M:
             self.cs_new.append(c["cs_last"].expand(self.n_seq, 64).contiguous())
         torch.cuda.synchronize()
 
-    def run_stage(self, ci, st):
-        """One stage of the step for batch copy ci, on torch's current stream."""
+    def run_stage(self, ci, st, alone=False):
+        """One stage of the step for batch copy ci, on torch's current stream (alone: the fused
+        stage timed by itself, counting into a region no selection reads)."""
         c, csa2, n = self.copies[ci], self.csa2, self.n
         if st == FUSED:  # append each sequence's newest entry and score every entry, one launch
             # (with the MXFP4 query, the launch packs the bf16 query itself)
+            sel_ws = (self.ws_hist_alone if alone else self.ws_sel) if self.handoff else None
             csa2.append_index_score(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"],
                                     self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], c["q_idx"], c["head_w"],
                                     self.q_base, self.q_nvis, n, scores=self.scores, block_max=self.bmax,
-                                    pack_q=self.fp4q)
+                                    pack_q=self.fp4q, sel_workspace=sel_ws)
         elif st == FUSED_HISA:  # append, re-pack the newest block's mean, score the block means
             csa2.append_mean_index_score(c["last_lat"].view(self.n_seq * self.m, 512), self.m, c["pool_w"],
                                          self.cs_new[ci], c["w_idx"], c["kv"], c["ix"], c["means"], self.mbase,
@@ -332,6 +342,9 @@ class Decode1M:
             csa2.index_score(c["q_idx"], c["head_w"], c["ix"], self.q_base, self.q_nvis, n, scores=self.scores,
                              block_max=self.bmax)
         elif st == 2:
+            csa2.block_topk(self.scores, self.q_nvis, K=self.K, M=self.M, block_max=self.bmax, pool_out=self.pool,
+                            topk_out=self.topk, workspace=self.ws_sel, hist_ready=self.handoff)
+        elif st == SEL_FULL:  # the selection with its own first pass (valid on its own)
             csa2.block_topk(self.scores, self.q_nvis, K=self.K, M=self.M, block_max=self.bmax, pool_out=self.pool,
                             topk_out=self.topk, workspace=self.ws_sel)
         elif st == 3 and self.fp8:
@@ -374,6 +387,7 @@ def roofline(nbytes, us):
 
 FUSED = -1  # the stage that appends and scores in one launch (csa2_append_index_score)
 FUSED_HISA = -2  # HISA's append + newest block mean + scan of the means (csa2_append_mean_index_score)
+SEL_FULL = -3  # the selection with its own first pass (the step's selection skips it after the fused stage)
 STAGE_NAMES = {FUSED: "append_index_score", FUSED_HISA: "append_mean_index_score", 0: "compress_newest",
                1: "index_score", 2: "block_topk", 3: "sparse_attn"}
 
@@ -414,23 +428,32 @@ def time_decode(torch, csa2, tokens, n_seq, m, extra_layers=0, steps=20, warmup=
         # each stage of the step alone: HIP events around graphs of back-to-back launches
         names = {FUSED: "append_index_score", 2: "block_topk", 3: "sparse_attn_full", 4: "reindex_index_score",
                  5: "reindex_block_topk", 6: "sparse_attn_reindex"}
+        # (with the handoff the Full selection reads the counts of the fused launch before it:
+        # it is timed as a graph of both minus one of the fused launch alone)
         res["stages_us"] = {}
+        us_of = {}
         for st in wl.step_stages:
             reps = 4 * NCOPY
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 for r in range(reps):
-                    wl.run_stage(r % NCOPY, st)
+                    if st == 2 and wl.handoff:
+                        wl.run_stage(r % NCOPY, FUSED)
+                    wl.run_stage(r % NCOPY, st, alone=True)
             g.replay()
             torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(3):
+            samples = []
+            for _ in range(7):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
                 g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            res["stages_us"][names.get(st, f"sparse_attn_reuse{st - 6}")] = round(a.elapsed_time(b) * 1e3 / (3 * reps),
-                                                                                  2)
+                b.record()
+                torch.cuda.synchronize()
+                samples.append(a.elapsed_time(b) * 1e3 / reps)
+            us_of[st] = float(np.median(samples))
+            if st == 2 and wl.handoff:
+                us_of[st] -= us_of[FUSED]
+            res["stages_us"][names.get(st, f"sparse_attn_reuse{st - 6}")] = round(us_of[st], 2)
             del g
     if not hisa and not fp8_window:
         # the whole step against the HBM roofline: Full scan, Reindex pool, every attention layer
@@ -649,11 +672,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     peaks = None if args.no_peaks else measure_peaks(torch)
-    wl = Decode1M(torch, csa2, args.tokens)
+    wl = Decode1M(torch, csa2, args.tokens, handoff=not args.no_handoff)
     n_seq, m, tokens, n, K, M = wl.n_seq, wl.m, wl.tokens, wl.n, wl.K, wl.M
     step = wl.step_stages  # the fused append + scan, selection, attention
-    # stages timed on their own: the step's, and the two launches the fused stage replaces
-    timed = step + [0, 1]
+    # stages timed on their own: the step's, the selection with its own first pass, and the
+    # two launches the fused stage replaces.  With the handoff the step's selection reads the
+    # counts of the fused launch before it, so it is timed as a graph of both minus one of the
+    # fused launch alone.
+    timed = step + [SEL_FULL, 0, 1]
+    alone = [st for st in timed if not (wl.handoff and st == 2)]
     run_stage = wl.run_stage
     for i in range(args.warmup):  # eager warm-up
         for st in timed:
@@ -680,12 +707,20 @@ def main():
     # per-stage graphs of back-to-back launches (rotating copies) for the stage timings
     reps = 4 * NCOPY
     stage_graph = []
-    for st in timed:
+    for st in alone:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             for r in range(reps):
-                run_stage(r % NCOPY, st)
+                run_stage(r % NCOPY, st, alone=True)
         stage_graph.append(g)
+    pair_graph = None
+    if wl.handoff:
+        pair_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pair_graph, stream=cap):
+            for r in range(reps):
+                run_stage(r % NCOPY, FUSED)
+                run_stage(r % NCOPY, 2)
+        stage_graph.append(pair_graph)
     for i in range(2 * NCOPY):
         step_graph[i % NCOPY].replay()
     multi_graph.replay()
@@ -724,7 +759,7 @@ def main():
     # median over 7 replays
     stage_samples = 7
     st_us = {}
-    for st, g in zip(timed, stage_graph):
+    for st, g in zip(alone + (["pair"] if pair_graph is not None else []), stage_graph):
         samples = []
         for _ in range(stage_samples):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -735,6 +770,8 @@ def main():
             torch.cuda.synchronize()
             samples.append(a.elapsed_time(b) * 1e3 / reps)
         st_us[st] = float(np.median(samples))
+    if pair_graph is not None:
+        st_us[2] = st_us.pop("pair") - st_us[FUSED]
     # spread of the step time: HIP events around single replays of the multi-step graph
     per_step = []
     for _ in range(20):
@@ -779,6 +816,8 @@ def main():
                    "pool_blocks": M, "block": 8, "topk": K, "heads": 64, "head_dim": 512,
                    "swa": 128, "batch_copies": NCOPY},
         "stages_us": {STAGE_NAMES[st]: round(float(st_us[st]), 2) for st in step},
+        "first_pass_in_fused_launch": wl.handoff,
+        "block_topk_with_first_pass_us": round(float(st_us[SEL_FULL]), 2),
         "replaced_stages_us": {STAGE_NAMES[st]: round(float(st_us[st]), 2) for st in (0, 1)},
         "gpu_ms_timed_region": round(gpu_ms, 4), "wall_s_timed_region": round(wall_s, 4),
         "steps_per_graph": NCOPY, "ms_per_step_one_step_graphs": round(ms_single, 4),
@@ -794,7 +833,7 @@ def main():
     }
     if not args.no_secondary:
         # the other seeded workloads, each in its own graphs after the timed region above
-        del step_graph, stage_graph, multi_graph, wl
+        del step_graph, stage_graph, multi_graph, pair_graph, wl
         torch.cuda.empty_cache()
         print("[bench] secondary workloads", file=sys.stderr, flush=True)
         sec = {

@@ -42,6 +42,7 @@ _L.csa2_block_mean_pack.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _v
 _L.csa2_append_index_score.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _i32, _i32, _vp, _vp, _vp]
 _L.csa2_append_index_score_fp4q.argtypes = _L.csa2_append_index_score.argtypes
+_L.csa2_append_index_score_sel.argtypes = _L.csa2_append_index_score.argtypes[:-1] + [_vp, _sz, _vp]
 _L.csa2_append_index_score_packq.argtypes = _L.csa2_append_index_score.argtypes
 _L.csa2_append_mean_index_score.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
@@ -50,6 +51,7 @@ _L.csa2_block_topk_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_workspace.restype = _sz
 _L.csa2_block_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 _L.csa2_block_topk_noalloc.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+_L.csa2_block_topk_prebuilt.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 _L.csa2_block_topk_rescore_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _L.csa2_block_topk_rescore_workspace.restype = _sz
 _L.csa2_block_topk_rescore.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz,
@@ -67,7 +69,7 @@ SYMBOLS = ("csa2_abi_version", "csa2_status_string", "csa2_rope_table", "csa2_co
            "csa2_quantize_q_mxfp4", "csa2_index_score_fp4q", "csa2_block_mean_pack", "csa2_append_index_score",
            "csa2_append_index_score_fp4q", "csa2_append_index_score_packq", "csa2_append_mean_index_score",
            "csa2_append_mean_index_score_fp4q", "csa2_block_topk_noalloc", "csa2_block_topk_rescore_workspace",
-           "csa2_block_topk_rescore")
+           "csa2_block_topk_rescore", "csa2_append_index_score_sel", "csa2_block_topk_prebuilt")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -297,7 +299,7 @@ def _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q):
 
 def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q_idx, head_w, q_base, q_nvis,
                        width: int, scores=None, block_max=None, want_block_max: bool = True, stream=None,
-                       pack_q: bool = False, want_scores: bool = True):
+                       pack_q: bool = False, want_scores: bool = True, sel_workspace=None):
     """Appends query t's newest entry (latent bf16 [n_q*m, 512]) at cache row
     q_base[t] + q_nvis[t] - 1, then scores every visible entry: compress_append followed by
     Full-mode index_score, in one launch.  q_idx is bf16 [n_q, 32, 128] or MXFP4 uint8
@@ -305,8 +307,13 @@ def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cac
     inside the launch (quantize_q_mxfp4 followed by the MXFP4-query call).  pool_w: fp32
     [m, 512], or [n_q*m, 512] for one weight row per latent token.  want_scores=False (bf16
     query): the block maxima alone are written and scores comes back None (the selection then
-    uses block_topk_rescore)."""
+    uses block_topk_rescore).  sel_workspace (bf16 query): the workspace of the block_topk
+    call that follows (histogram region zeroed, as every block_topk call leaves it), into
+    which the launch also counts the older blocks' maxima; that call then passes
+    hist_ready=True and skips its first pass."""
     fp4 = isinstance(q_idx, torch.Tensor) and q_idx.dtype == torch.uint8
+    if sel_workspace is not None and (fp4 or pack_q or not want_block_max):
+        raise ValueError("sel_workspace takes a bf16 q_idx and the block maxima")
     if pack_q and fp4:
         raise ValueError("pack_q takes a bf16 q_idx")
     if not want_scores and (fp4 or pack_q or scores is not None or not want_block_max):
@@ -315,6 +322,13 @@ def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cac
     per_token = _append_args(latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, n_q)
     scores, block_max = _score_outputs(scores, block_max, want_block_max, n_q, width, q_idx.device, stream,
                                        want_scores=want_scores)
+    if sel_workspace is not None:
+        _dev(sel_workspace, sel_workspace.dtype, "sel_workspace")
+        _check("csa2_append_index_score_sel", _L.csa2_append_index_score_sel(
+            _ptr(latent), m, _ptr(pool_w), per_token, _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache),
+            _ptr(q_idx), _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width, _ptr(scores), _ptr(block_max),
+            _ptr(sel_workspace), _bytes(sel_workspace), _stream(stream)))
+        return scores, block_max
     name = "csa2_append_index_score" + ("_fp4q" if fp4 else "_packq" if pack_q else "")
     fn = getattr(_L, name)
     _check(name, fn(
@@ -378,11 +392,15 @@ def block_topk_workspace(n_q: int, width: int, M: int, K: int) -> int:
 
 def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool_blocks=None,
                want_pool: bool = True, pool_out=None, topk_out=None, workspace=None, stream=None,
-               want_topk: bool = True):
+               want_topk: bool = True, hist_ready: bool = False):
     """(pool [n_q, M] or None, topk [n_q, K] or None): Full mode when pool_blocks is None.
     want_topk=False is the pool-only mode: the pool from block_max [n_q, nbw] (the caller's
     block scores); scores may then be None (the row width is 8 * nbw).  A given workspace
-    must hold block_topk_workspace(...) bytes and start zeroed (every call leaves it so)."""
+    must hold block_topk_workspace(...) bytes and start zeroed (every call leaves it so).
+    hist_ready=True (Full mode, block_max and workspace given): append_index_score with
+    sel_workspace=workspace already counted the first pass (csa2_block_topk_prebuilt)."""
+    if hist_ready and (pool_blocks is not None or block_max is None or workspace is None):
+        raise ValueError("hist_ready takes Full mode, block_max and the workspace the counts went into")
     _dev(scores, torch.float32, "scores", (None, None))
     if scores is not None:
         n_q, width = scores.shape
@@ -414,6 +432,11 @@ def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool
     _dev(pool_out, torch.int32, "pool_out", (n_q, M))
     _dev(topk_out, torch.int32, "topk_out", (n_q, K))
     _dev(workspace, workspace.dtype, "workspace")
+    if hist_ready:
+        _check("csa2_block_topk_prebuilt", _L.csa2_block_topk_prebuilt(
+            _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), 8, M, K, _ptr(pool_out), _ptr(topk_out),
+            _ptr(workspace), _bytes(workspace), _stream(stream)))
+        return pool_out, topk_out
     _check("csa2_block_topk", _L.csa2_block_topk(
         _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), _ptr(pool_blocks), 8, M, K,
         _ptr(pool_out), _ptr(topk_out), _ptr(workspace), _bytes(workspace), _stream(stream)))

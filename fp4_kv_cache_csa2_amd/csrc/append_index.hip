@@ -71,26 +71,48 @@ __global__ __launch_bounds__(kThreads) void append_index_kernel(
 // s % n_q (j = s / n_q), its waves claiming the tiles one at a time: the 3 waves sharing a SIMD
 // are still issued oldest first, and with equal static shares the youngest third finished
 // about 6 us after the oldest.
+// kHist: the launch also counts every query's older block maxima into hist (kSelBins bins per
+// query, as the selection's first pass: csa2_append_index_score_sel): a scan workgroup counts
+// its tiles' blocks in LDS and adds its non-zero bins at its end, the append workgroup adds the
+// older blocks of the tile it scores.
 constexpr int kWideWaves = 12;
 constexpr int kWideThreads = 64 * kWideWaves;
 
-template <bool kScores>
+template <bool kScores, bool kHist = false>
 __global__ __launch_bounds__(kWideThreads) void append_index_wide_kernel(
     const uint16_t* __restrict__ latent, int m, const float* __restrict__ pool_w, const float* __restrict__ rope_cs,
     const uint16_t* __restrict__ w_idx, uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ idx_cache,
     const void* __restrict__ q_in, const float* __restrict__ head_w, const int64_t* __restrict__ q_base,
     const int32_t* __restrict__ q_nvis, int32_t n_q, int32_t width, float* __restrict__ scores,
-    float* __restrict__ block_max, int64_t w_stride, int32_t per_q) {
+    float* __restrict__ block_max, int64_t w_stride, int32_t per_q, uint32_t* __restrict__ hist) {
   const int L = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   if (L >= n_q) {  // groups of 4 tiles j, j + per_q, ... of query t, claimed a tile at a time
-    __shared__ uint32_t claim;
-    if (threadIdx.x == 0) claim = 0u;
-    __syncthreads();
     const int s = L - n_q, t = s % n_q, j = s / n_q;
-    score_tiles<false, false, kOlderSlots, false, kScores, true>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0,
-                                                                 width, scores, block_max, t, j, per_q, nullptr,
-                                                                 nullptr, &claim);
+    __shared__ uint32_t claim;
+    if constexpr (kHist) {
+      __shared__ uint32_t lh[kSelBins];
+      for (int b = threadIdx.x; b < kSelBins; b += kWideThreads) lh[b] = 0u;
+      if (threadIdx.x == 0) claim = 0u;
+      __syncthreads();
+      score_tiles<false, false, kOlderSlots, false, kScores, true>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr,
+                                                                   0, width, scores, block_max, t, j, per_q, nullptr,
+                                                                   nullptr, &claim, lh);
+      __syncthreads();
+      // the query's workgroups end together: each starts its pass over the bins at its own
+      // offset, so their adds to one bin do not all arrive at once
+      uint32_t* gh = hist + (int64_t)t * kSelBins;
+      for (int i = threadIdx.x; i < kSelBins; i += kWideThreads) {
+        const int b = (i + 64 * j) & (kSelBins - 1);
+        if (lh[b]) atomicAdd(&gh[b], lh[b]);
+      }
+    } else {
+      if (threadIdx.x == 0) claim = 0u;
+      __syncthreads();
+      score_tiles<false, false, kOlderSlots, false, kScores, true>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr,
+                                                                   0, width, scores, block_max, t, j, per_q, nullptr,
+                                                                   nullptr, &claim);
+    }
     return;
   }
   const int t = L;
@@ -102,7 +124,8 @@ __global__ __launch_bounds__(kWideThreads) void append_index_wide_kernel(
                                  w_idx, row, kv_cache, idx_cache, sh, wl);
   if (wave != 0) return;  // the newest tile is one tile: one wave scores it
   score_tiles<false, false, kNewestSlots, false, kScores>(q_in, head_w, idx_cache, q_base, q_nvis, nullptr, 0, width,
-                                                          scores, block_max, t, 0, 1, sh.idx_row);
+                                                          scores, block_max, t, 0, 1, sh.idx_row, nullptr, nullptr,
+                                                          nullptr, kHist ? hist + (int64_t)t * kSelBins : nullptr);
 }
 
 // One of the 512 tasks (head, group of 32 channels, quarter) of packing the query of t to
@@ -246,7 +269,8 @@ __global__ __launch_bounds__(kWideThreads) void append_mean_index_wide_kernel(
 
 // workgroups of each kernel of this file that fit on the device at once (per device)
 std::atomic<int> resident_entry[kMaxDevices], resident_entry_max[kMaxDevices], resident_fp4q[kMaxDevices],
-    resident_packq[kMaxDevices], resident_mean[kMaxDevices], resident_mean_fp4q[kMaxDevices];
+    resident_packq[kMaxDevices], resident_mean[kMaxDevices], resident_mean_fp4q[kMaxDevices],
+    resident_sel[kMaxDevices], resident_sel_max[kMaxDevices];
 
 // scan workgroups per query of append_index_wide_kernel: the resident workgroups left after the
 // n_q append workgroups, shared evenly (at least one, at most one per 3 groups of 4 tiles)
@@ -317,11 +341,11 @@ int append_index_entry(const uint16_t* latent, int m, const float* pool_w, int p
     if (scores)
       hipLaunchKernelGGL(append_index_wide_kernel<true>, dim3((unsigned)grid), dim3(kWideThreads), 0, (hipStream_t)stream,
                          latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base, q_nvis, n_q, width,
-                         scores, block_max, weight_stride(m, per_token_w), per_q);
+                         scores, block_max, weight_stride(m, per_token_w), per_q, nullptr);
     else
       hipLaunchKernelGGL(append_index_wide_kernel<false>, dim3((unsigned)grid), dim3(kWideThreads), 0,
                          (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
-                         q_nvis, n_q, width, scores, block_max, weight_stride(m, per_token_w), per_q);
+                         q_nvis, n_q, width, scores, block_max, weight_stride(m, per_token_w), per_q, nullptr);
     return check_launch();
   } else {
     const int64_t gx = grid_x(resident_workgroups(append_index_kernel<true>, kThreads, resident_fp4q), n_q, width);
@@ -330,6 +354,36 @@ int append_index_entry(const uint16_t* latent, int m, const float* pool_w, int p
                        q_nvis, width, scores, block_max, weight_stride(m, per_token_w));
     return check_launch();
   }
+}
+
+int append_index_sel_entry(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,
+                           const uint16_t* w_idx, uint8_t* kv_cache, uint8_t* idx_cache, const uint16_t* q,
+                           const float* head_w, const int64_t* q_base, const int32_t* q_nvis, int32_t n_q,
+                           int32_t width, float* scores, float* block_max, void* sel_ws, size_t sel_ws_bytes,
+                           void* stream) {
+  const int rc = check_args<false>(latent, m, pool_w, per_token_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
+                                   q_nvis, n_q, width, scores, block_max, true);
+  if (rc != CSA2_OK || n_q == 0) return rc;
+  if (!block_max) return CSA2_ERR_INVALID_ARG;  // the histogram counts the block maxima written
+  if (!sel_ws || (reinterpret_cast<uintptr_t>(sel_ws) & 3)) return CSA2_ERR_INVALID_ARG;
+  if (sel_ws_bytes < (size_t)n_q * kSelBins * sizeof(uint32_t)) return CSA2_ERR_WORKSPACE;
+  uint32_t* hist = static_cast<uint32_t*>(sel_ws);  // the selection workspace starts with the histogram rows
+  if (scores) {
+    const int32_t per_q =
+        wide_per_q(resident_workgroups(append_index_wide_kernel<true, true>, kWideThreads, resident_sel), n_q, width);
+    const int64_t grid = (int64_t)n_q * (1 + per_q);
+    hipLaunchKernelGGL((append_index_wide_kernel<true, true>), dim3((unsigned)grid), dim3(kWideThreads), 0,
+                       (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
+                       q_nvis, n_q, width, scores, block_max, weight_stride(m, per_token_w), per_q, hist);
+  } else {
+    const int32_t per_q = wide_per_q(
+        resident_workgroups(append_index_wide_kernel<false, true>, kWideThreads, resident_sel_max), n_q, width);
+    const int64_t grid = (int64_t)n_q * (1 + per_q);
+    hipLaunchKernelGGL((append_index_wide_kernel<false, true>), dim3((unsigned)grid), dim3(kWideThreads), 0,
+                       (hipStream_t)stream, latent, m, pool_w, rope_cs, w_idx, kv_cache, idx_cache, q, head_w, q_base,
+                       q_nvis, n_q, width, scores, block_max, weight_stride(m, per_token_w), per_q, hist);
+  }
+  return check_launch();
 }
 
 int append_index_packq_entry(const uint16_t* latent, int m, const float* pool_w, int per_token_w, const float* rope_cs,
@@ -387,6 +441,17 @@ extern "C" int csa2_append_index_score(const uint16_t* latent_bf16, int m, const
                                        float* block_max, void* stream) {
   return csa2::append_index_entry<false>(latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache, q_idx_bf16,
                                          head_w, q_base, q_nvis, n_q, width, scores, block_max, stream);
+}
+
+extern "C" int csa2_append_index_score_sel(const uint16_t* latent_bf16, int m, const float* pool_w, int per_token_w,
+                                           const float* rope_cs, const uint16_t* w_idx_bf16, uint8_t* kv_cache,
+                                           uint8_t* idx_cache, const uint16_t* q_idx_bf16, const float* head_w,
+                                           const int64_t* q_base, const int32_t* q_nvis, int32_t n_q, int32_t width,
+                                           float* scores, float* block_max, void* sel_workspace, size_t sel_ws_bytes,
+                                           void* stream) {
+  return csa2::append_index_sel_entry(latent_bf16, m, pool_w, per_token_w, rope_cs, w_idx_bf16, kv_cache, idx_cache,
+                                      q_idx_bf16, head_w, q_base, q_nvis, n_q, width, scores, block_max, sel_workspace,
+                                      sel_ws_bytes, stream);
 }
 
 extern "C" int csa2_append_index_score_fp4q(const uint16_t* latent_bf16, int m, const float* pool_w, int per_token_w,

@@ -43,8 +43,8 @@
 namespace csa2 {
 namespace {
 
-constexpr int kBins = 4096;        // 12-bit histogram digit
-constexpr int kBinShift = 20;
+constexpr int kBins = kSelBins;        // 12-bit histogram digit
+constexpr int kBinShift = kSelBinShift;
 constexpr int kSlice = 1024;       // keys per workgroup in K2
 // K1 workgroups: 4096 keys on 512 threads for a few long rows (8192 on 1024: 0.45 us slower
 // per 1M x 4 decode call), 8192 keys on 1024 threads for many rows (4096 on 512: 0.49 ->
@@ -1179,12 +1179,13 @@ int block_topk_check(const float* scores, const float* block_max, int32_t n_q, i
 }
 
 // The three launches (after block_topk_check), shared by csa2_block_topk (the caller's
-// workspace) and csa2_block_topk_noalloc (the fixed scratch array, whose histogram region is
-// cleared first).
+// workspace), csa2_block_topk_noalloc (the fixed scratch array, whose histogram region is
+// cleared first) and csa2_block_topk_prebuilt (hist_ready: the histogram region already holds
+// K1's counts, so K1 is skipped; the one-launch path for short rows clears the region instead).
 int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, int32_t width, const int32_t* q_nvis,
                       const int32_t* pool_blocks, int32_t M, int32_t K, int32_t* pool_out, int32_t* topk_out,
                       void* workspace, size_t ws_bytes, bool clear_hist, void* stream,
-                      const Rescore* rsc = nullptr) {
+                      const Rescore* rsc = nullptr, bool hist_ready = false) {
   const bool cand = pool_blocks != nullptr;
   const bool want_topk = topk_out != nullptr;
   if (reinterpret_cast<uintptr_t>(workspace) & 3) return CSA2_ERR_INVALID_ARG;
@@ -1218,6 +1219,11 @@ int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, 
     else
       hipLaunchKernelGGL(topk_small_kernel<false>, gs, dim3(kFThreads), 0, s, want_pool, want_topk, scores, block_max,
                          width, q_nvis, pool_blocks, M, K, pool_out, topk_out);
+    int st0 = check_launch();
+    if (st0 != CSA2_OK || !hist_ready) return st0;
+    const int64_t words = (int64_t)n_q * kBins;  // the prebuilt counts are not read: clear them
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                       dim3(256), 0, s, ws.hist, words);
     return check_launch();
   }
   if (clear_hist) {
@@ -1227,24 +1233,27 @@ int block_topk_launch(const float* scores, const float* block_max, int32_t n_q, 
     const int st = check_launch();
     if (st != CSA2_OK) return st;
   }
-  const bool wide = n_q >= kHWideRows;
-  const int32_t sl = wide ? kHSliceWide : kHSlice;
-  const int32_t G1 = (L.G * kSlice + sl - 1) / sl;
-  const dim3 g1(G1, n_q), b1(wide ? kHThreadsWide : kHThreads);
-  if (cand && wide)
-    hipLaunchKernelGGL((topk_hist_kernel<true, kHSliceWide, kHThreadsWide>), g1, b1, 0, s, scores, block_max, width,
-                       q_nvis, pool_blocks, M, K, ws);
-  else if (cand)
-    hipLaunchKernelGGL((topk_hist_kernel<true, kHSlice, kHThreads>), g1, b1, 0, s, scores, block_max, width, q_nvis,
-                       pool_blocks, M, K, ws);
-  else if (wide)
-    hipLaunchKernelGGL((topk_hist_kernel<false, kHSliceWide, kHThreadsWide>), g1, b1, 0, s, scores, block_max, width,
-                       q_nvis, pool_blocks, M, K, ws);
-  else
-    hipLaunchKernelGGL((topk_hist_kernel<false, kHSlice, kHThreads>), g1, b1, 0, s, scores, block_max, width, q_nvis,
-                       pool_blocks, M, K, ws);
-  int st = check_launch();
-  if (st != CSA2_OK) return st;
+  if (!hist_ready) {
+    const bool wide = n_q >= kHWideRows;
+    const int32_t sl = wide ? kHSliceWide : kHSlice;
+    const int32_t G1 = (L.G * kSlice + sl - 1) / sl;
+    const dim3 g1(G1, n_q), b1(wide ? kHThreadsWide : kHThreads);
+    if (cand && wide)
+      hipLaunchKernelGGL((topk_hist_kernel<true, kHSliceWide, kHThreadsWide>), g1, b1, 0, s, scores, block_max, width,
+                         q_nvis, pool_blocks, M, K, ws);
+    else if (cand)
+      hipLaunchKernelGGL((topk_hist_kernel<true, kHSlice, kHThreads>), g1, b1, 0, s, scores, block_max, width, q_nvis,
+                         pool_blocks, M, K, ws);
+    else if (wide)
+      hipLaunchKernelGGL((topk_hist_kernel<false, kHSliceWide, kHThreadsWide>), g1, b1, 0, s, scores, block_max, width,
+                         q_nvis, pool_blocks, M, K, ws);
+    else
+      hipLaunchKernelGGL((topk_hist_kernel<false, kHSlice, kHThreads>), g1, b1, 0, s, scores, block_max, width, q_nvis,
+                         pool_blocks, M, K, ws);
+    const int st1 = check_launch();
+    if (st1 != CSA2_OK) return st1;
+  }
+  int st = CSA2_OK;
   if (cand)
     hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(L.G, n_q), dim3(kGThreads), 0, s, want_pool, want_topk, scores,
                        bm, width, q_nvis, pool_blocks, M, K, ws, rs);
@@ -1281,6 +1290,17 @@ extern "C" int csa2_block_topk(const float* scores, const float* block_max, int3
   if (st != csa2::kProceed) return st;
   return csa2::block_topk_launch(scores, block_max, n_q, width, q_nvis, pool_blocks, M, K, pool_out, topk_out,
                                  workspace, ws_bytes, false, stream);
+}
+
+extern "C" int csa2_block_topk_prebuilt(const float* scores, const float* block_max, int32_t n_q, int32_t width,
+                                        const int32_t* q_nvis, int32_t block, int32_t M, int32_t K, int32_t* pool_out,
+                                        int32_t* topk_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (n_q > 0 && !block_max) return CSA2_ERR_INVALID_ARG;  // the counts were taken from these maxima
+  const int st = csa2::block_topk_check(scores, block_max, n_q, width, q_nvis, nullptr, block, M, K, pool_out,
+                                        topk_out);
+  if (st != csa2::kProceed) return st;
+  return csa2::block_topk_launch(scores, block_max, n_q, width, q_nvis, nullptr, M, K, pool_out, topk_out, workspace,
+                                 ws_bytes, false, stream, nullptr, true);
 }
 
 extern "C" size_t csa2_block_topk_rescore_workspace(int32_t n_q, int32_t width, int32_t M, int32_t K) {

@@ -124,6 +124,12 @@ __device__ __forceinline__ uint32_t e8m0_scale_code(float amax) {
   return (uint32_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
 }
 
+// The selection's first pass counts the ranking keys (order_key) of a row's items in
+// kSelBins bins of their top 12 bits; the decode scan can count its block maxima the same way
+// (csa2_append_index_score_sel).
+constexpr int kSelBins = 4096;
+constexpr int kSelBinShift = 20;
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); NaN ranks as -inf.
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) f = -__builtin_inff();

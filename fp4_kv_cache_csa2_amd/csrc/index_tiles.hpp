@@ -110,6 +110,9 @@ __device__ __forceinline__ float head_sum(const f32x16& acc, const float (&wr)[1
 // entries and the row's visible means are ceil(q_nvis[t] / 8).
 // The wave is tile `first` of the grid-stride order with stride `tstride` (wave-uniform).
 // kScores = false leaves the score row unwritten (block maxima only; scores may be NULL).
+// lhist (kClaim, LDS) / ghist (kNewestSlots, global): when given, each older block maximum
+// written (every block of the row but the one holding entry min(nvis, width) - 1) is also
+// counted in bin order_key(max) >> kSelBinShift, as the selection's first pass counts it.
 // kClaim: `first` and `tstride` describe the workgroup's tiles in groups of 4 consecutive
 // tiles (groups first, first + tstride, ...), and its waves claim c = 0, 1, ... from the LDS
 // counter *claim (zero before the first claim): claim c is tile 4 (first + (c / 4) tstride) +
@@ -123,7 +126,7 @@ __device__ __forceinline__ void score_tiles(
     const int32_t* __restrict__ q_nvis, const int32_t* __restrict__ pool_blocks, int32_t M,
     int32_t width, float* __restrict__ scores, float* __restrict__ block_max, int t, int32_t first,
     int32_t tstride, const uint8_t* fresh_row = nullptr, const uint8_t* q_rec = nullptr,
-    uint32_t* claim = nullptr) {
+    uint32_t* claim = nullptr, uint32_t* lhist = nullptr, uint32_t* ghist = nullptr) {
   static_assert(!kPool || kPart == kAllSlots, "a candidate pool is scored whole");
   static_assert(!kClaim || (!kPool && kPart != kNewestSlots), "claimed tiles: a Full row's older tiles");
   // tiles in flight per wave: the newest-tile part visits one tile
@@ -270,8 +273,13 @@ __device__ __forceinline__ void score_tiles(
     const bool drop = kPart == kOlderSlots && T == t_new;  // wave-uniform
     if constexpr (kScores)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, vo_score, drop ? kOut : T * (4 * kTile), 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax, vo_bmax,
-                                          drop ? kOut : T * (4 * kTile / kBlock), 0);
+    const float bmx = max8_lanes(sc);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bmx), rs_bmax, vo_bmax, drop ? kOut : T * (4 * kTile / kBlock),
+                                          0);
+    // every visible block of an older tile is an older block (the newest is in tile t_new)
+    if (lhist != nullptr && !drop && (g | (n & 7)) == 0 && T * kTile + n < nv)
+      __hip_atomic_fetch_add(&lhist[order_key(bmx) >> kSelBinShift], 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
   };
   auto process = [&](const RawTile& cur, int32_t k) {
     f32x16 acc;
@@ -296,8 +304,14 @@ __device__ __forceinline__ void score_tiles(
     const int32_t p = tile_of(k) * kTile + n;
     if constexpr (kScores)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_score, (g || drop) ? kOut : 4 * p, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8_lanes(sc)), rs_bmax,
-                                          ((g | (n & 7)) || drop) ? kOut : 4 * (p >> 3), 0, 0);
+    const float bmx = max8_lanes(sc);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bmx), rs_bmax, ((g | (n & 7)) || drop) ? kOut : 4 * (p >> 3),
+                                          0, 0);
+    if constexpr (kPart == kNewestSlots) {  // the newest tile's older blocks
+      const int32_t nw = min(nvis, width);
+      if (ghist != nullptr && (g | (n & 7)) == 0 && p < nw && (p >> 3) < (nw - 1) >> 3)
+        atomicAdd(&ghist[order_key(bmx) >> kSelBinShift], 1u);
+    }
   };
 
   // The query and head weights are loaded first, then the first kPipe tiles, and a wait

@@ -70,7 +70,7 @@ enum {
   CSA2_ERR_SCRATCH = -5      /* larger than the fixed scratch array of a _noalloc call */
 };
 
-#define CSA2_ABI_VERSION 4
+#define CSA2_ABI_VERSION 5
 
 int csa2_abi_version(void);
 const char *csa2_status_string(int status);
@@ -224,6 +224,26 @@ int csa2_append_index_score(const uint16_t *latent_bf16, int m, const float *poo
                             float *block_max, void *stream);
 
 /*
+ * csa2_append_index_score_sel -- csa2_append_index_score (bf16 query) that also takes the
+ *   first pass of the selection that follows it ([ZB] §2.3.4 / [DF] §4.7, csa2_block_topk in
+ *   Full mode): the count of every query's older blocks (all blocks of its row but the one
+ *   holding entry min(q_nvis[t], width) - 1) by the top 12 bits of their maximum's ranking
+ *   key, added into the histogram region of a csa2_block_topk workspace, so that
+ *   csa2_block_topk_prebuilt on the scores and maxima this call writes skips that pass.
+ *   sel_workspace: the workspace of that selection call (csa2_block_topk_workspace(n_q,
+ *   width, M, K) bytes, at least n_q * 16 KiB, 4-byte aligned) with its histogram region
+ *   zero on entry, as every csa2_block_topk call leaves it; block_max is required (scores
+ *   may be NULL, as above).  Every other argument, result and error as
+ *   csa2_append_index_score; WORKSPACE when sel_ws_bytes < n_q * 16 KiB.
+ */
+int csa2_append_index_score_sel(const uint16_t *latent_bf16, int m, const float *pool_w, int per_token_w,
+                                const float *rope_cs, const uint16_t *w_idx_bf16, uint8_t *kv_cache,
+                                uint8_t *idx_cache, const uint16_t *q_idx_bf16, const float *head_w,
+                                const int64_t *q_base, const int32_t *q_nvis, int32_t n_q, int32_t width,
+                                float *scores, float *block_max, void *sel_workspace, size_t sel_ws_bytes,
+                                void *stream);
+
+/*
  * csa2_append_index_score_fp4q -- csa2_append_index_score with the indexer query in MXFP4
  *   (q_fp4 [n_q, 32, 68], 4-byte aligned, from csa2_quantize_q_mxfp4): the scores of
  *   csa2_index_score_fp4q.  Every other argument, result and error as above, except that
@@ -286,6 +306,17 @@ int csa2_block_topk(const float *scores, const float *block_max, int32_t n_q, in
                     const int32_t *q_nvis, const int32_t *pool_blocks, int32_t block,
                     int32_t M, int32_t K, int32_t *pool_out, int32_t *topk_out,
                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * csa2_block_topk_prebuilt -- csa2_block_topk in Full mode (pool_blocks NULL, block_max
+ *   required) whose workspace's histogram region already holds the counts of its first pass,
+ *   added by csa2_append_index_score_sel for these block maxima and visible counts: the call
+ *   skips that pass.  Results bit for bit those of csa2_block_topk; it leaves the histogram
+ *   region zero, as csa2_block_topk does.  Arguments and errors as csa2_block_topk.
+ */
+int csa2_block_topk_prebuilt(const float *scores, const float *block_max, int32_t n_q, int32_t width,
+                             const int32_t *q_nvis, int32_t block, int32_t M, int32_t K, int32_t *pool_out,
+                             int32_t *topk_out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * csa2_block_topk_rescore -- csa2_block_topk in Full mode without a score row: the

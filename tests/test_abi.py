@@ -40,7 +40,7 @@ def test_binding_names_match_header():
 
 def test_version_and_status_strings(lib):
     lib.csa2_status_string.restype = ctypes.c_char_p
-    assert lib.csa2_abi_version() == 4
+    assert lib.csa2_abi_version() == 5
     for st in (0, -1, -2, -3, -4):
         assert lib.csa2_status_string(st)
 

@@ -4,7 +4,9 @@ produce (cache bytes, scores, block maxima), the appended bytes against the orac
 compressor, the scores against the oracle's indexer over the updated cache, two calls in a
 row, ragged rows, an empty row, rows whose newest entry opens a block or a tile, rows
 shorter or longer than the score width, 70 and 300 queries at once, the MXFP4 query packed inside
-the launch (special scales included), and the 1M-context batch-4 decode in the launch geometry the bench uses.  The appended rows start out holding other bytes,
+the launch (special scales included), the variant that also counts the selection's first pass
+(csa2_append_index_score_sel, then csa2_block_topk_prebuilt), and the 1M-context batch-4
+decode in the launch geometry the bench uses.  The appended rows start out holding other bytes,
 so a score computed from stale bytes would show."""
 import dataclasses
 
@@ -106,6 +108,74 @@ def test_fused_equals_append_then_score(c, ci, fp4, pack_q):
     again = _fused(c, k, fp4, kv=got[0], ix=got[1], pack_q=pack_q)
     torch.cuda.synchronize()
     _same(ref, again)
+
+
+def _host_hist(block_max, nvis, width):
+    """The selection's first-pass counts from the block maxima: per query, its older blocks
+    (all but the one holding entry min(nvis, width) - 1) binned by the top 12 bits of the
+    order-preserving key of their maximum (NaN ranks as -inf)."""
+    bm = host(block_max).astype(np.float32)
+    n_q = bm.shape[0]
+    out = np.zeros((n_q, 4096), np.int64)
+    for t in range(n_q):
+        nw = min(int(nvis[t]), width)
+        if nw <= 0:
+            continue
+        older = (nw - 1) // 8  # blocks 0 .. older - 1
+        v = np.where(np.isnan(bm[t, :older]), -np.inf, bm[t, :older]).astype(np.float32).view(np.uint32)
+        key = np.where(v & 0x80000000, ~v, v | 0x80000000).astype(np.uint32)
+        out[t] = np.bincount(key >> 20, minlength=4096)
+    return out
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_fused_sel_counts_and_prebuilt_selection(c, ci):
+    """csa2_append_index_score_sel: the same bytes, scores and maxima as csa2_append_index_score,
+    and the selection workspace's histogram rows hold exactly the first-pass counts of the
+    maxima it wrote; csa2_block_topk_prebuilt on that workspace gives block_topk's pool and
+    Top-K bit for bit (the short-row path included) and leaves the histogram region zero."""
+    nvis, width, m = CASES[ci]
+    M, K = (64, 32) if width < 4096 else (256, 128)
+    log(f"append_index_sel nvis[:4]={nvis[:4]} n_q={len(nvis)} width={width} m={m} M={M} K={K}")
+    k = Case(c, 600 + 10 * ci, nvis, width, m)
+    ref = _fused(c, k, False)
+    ws = torch.zeros(c.block_topk_workspace(k.n_q, width, M, K), dtype=torch.uint8, device="cuda")
+    kv, ix = dev(k.kv), dev_ix(k.ix)
+    s, b = c.append_index_score(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), kv, ix,
+                                bf16(k.d.q_idx), dev(k.d.head_w), dev(k.base), dev(k.nvis), width, sel_workspace=ws)
+    torch.cuda.synchronize()
+    _same(ref, (kv, ix, s, b))
+    hist = host(ws[: k.n_q * 4096 * 4].view(torch.int32)).reshape(k.n_q, 4096)
+    want = _host_hist(b, k.nvis, width)
+    bad = np.argwhere(hist != want)
+    assert bad.size == 0, f"histogram counts differ at {bad[:4].tolist()}"
+    pool_ref, topk_ref = c.block_topk(ref[2], dev(k.nvis), K=K, M=M, block_max=ref[3])
+    pool, topk = c.block_topk(s, dev(k.nvis), K=K, M=M, block_max=b, workspace=ws, hist_ready=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(pool), host(pool_ref)) and np.array_equal(host(topk), host(topk_ref))
+    assert int(ws[: k.n_q * 4096 * 4].view(torch.int32).abs().sum().item()) == 0, "histogram region not zero"
+
+
+def test_fused_sel_decode_1m_b4(c):
+    """The first-pass counts at the bench's geometry (4 x 524288 entries, M = 2048, K = 512):
+    exact counts, and the prebuilt selection equal to block_topk's."""
+    n, n_q, M, K = 524288, 4, 2048, 512
+    log("append_index_sel 1M: drawing caches")
+    k = Case(c, 620, [n, n - 1, n - 8, n - 9], n, 2)
+    ref = _fused(c, k, False)
+    ws = torch.zeros(c.block_topk_workspace(n_q, n, M, K), dtype=torch.uint8, device="cuda")
+    kv, ix = dev(k.kv), dev_ix(k.ix)
+    s, b = c.append_index_score(bf16(k.ci.latent), k.m, dev(k.ci.pool_w), dev(k.cs), bf16(k.ci.w_idx), kv, ix,
+                                bf16(k.d.q_idx), dev(k.d.head_w), dev(k.base), dev(k.nvis), n, sel_workspace=ws)
+    torch.cuda.synchronize()
+    _same(ref, (kv, ix, s, b))
+    hist = host(ws[: n_q * 4096 * 4].view(torch.int32)).reshape(n_q, 4096)
+    assert np.array_equal(hist, _host_hist(b, k.nvis, n)), "histogram counts differ"
+    pool_ref, topk_ref = c.block_topk(ref[2], dev(k.nvis), K=K, M=M, block_max=ref[3])
+    pool, topk = c.block_topk(s, dev(k.nvis), K=K, M=M, block_max=b, workspace=ws, hist_ready=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(pool), host(pool_ref)) and np.array_equal(host(topk), host(topk_ref))
+    assert int(ws[: n_q * 4096 * 4].view(torch.int32).abs().sum().item()) == 0, "histogram region not zero"
 
 
 def test_query_packed_in_launch_takes_every_scale_path(c):
