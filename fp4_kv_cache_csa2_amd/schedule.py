@@ -126,11 +126,14 @@ class GlobalBranch:
                 if j is not None:
                     cs = state.rope[c]
                     pool_w, w_idx = self.params[c]
-                if j is not None and j == n - 1:
-                    # the new entry is the newest visible one: append it and score in one launch
+                fused = j is not None and j == n - 1
+                if fused:
+                    # the new entry is the newest visible one: append it and score in one launch,
+                    # which also counts the selection's first pass into its workspace
                     csa2.append_index_score(new_latents[c], m, pool_w, cs, w_idx, self.kv[c], self.ix[c],
                                             inp["q_idx"], inp["head_w"], self.base[c], nvis, n,
-                                            scores=self._row_view(n), block_max=self._bmax_view(n))
+                                            scores=self._row_view(n), block_max=self._bmax_view(n),
+                                            sel_workspace=self.ws_sel)
                 else:
                     if j is not None:
                         csa2.compress_append(new_latents[c], m, pool_w, cs, w_idx, state.rows[c], self.kv[c],
@@ -138,7 +141,7 @@ class GlobalBranch:
                     csa2.index_score(inp["q_idx"], inp["head_w"], self.ix[c], self.base[c], nvis, n,
                                      scores=self._row_view(n), block_max=self._bmax_view(n))
                 csa2.block_topk(self._row_view(n), nvis, K=K, M=M, block_max=self._bmax_view(n),
-                                pool_out=self.pool, topk_out=self.topk, workspace=self.ws_sel)
+                                pool_out=self.pool, topk_out=self.topk, workspace=self.ws_sel, hist_ready=fused)
             elif mode == "reindex":
                 nvis = state.nvis[c]
                 csa2.index_score(inp["q_idx"], inp["head_w"], self.ix[c], self.base[c], nvis, 8 * M,
