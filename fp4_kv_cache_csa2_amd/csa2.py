@@ -324,6 +324,9 @@ def append_index_score(latent, m: int, pool_w, rope_cs, w_idx, kv_cache, idx_cac
                                        want_scores=want_scores)
     if sel_workspace is not None:
         _dev(sel_workspace, sel_workspace.dtype, "sel_workspace")
+        if _bytes(sel_workspace) < n_q * 4096 * 4:
+            raise ValueError(f"sel_workspace: at least {n_q * 4096 * 4} bytes (the histogram rows), "
+                             f"got {_bytes(sel_workspace)}")
         _check("csa2_append_index_score_sel", _L.csa2_append_index_score_sel(
             _ptr(latent), m, _ptr(pool_w), per_token, _ptr(rope_cs), _ptr(w_idx), _ptr(kv_cache), _ptr(idx_cache),
             _ptr(q_idx), _ptr(head_w), _ptr(q_base), _ptr(q_nvis), n_q, width, _ptr(scores), _ptr(block_max),
@@ -433,6 +436,8 @@ def block_topk(scores, q_nvis, K: int = 512, M: int = 2048, block_max=None, pool
     _dev(topk_out, torch.int32, "topk_out", (n_q, K))
     _dev(workspace, workspace.dtype, "workspace")
     if hist_ready:
+        if _bytes(workspace) < need:
+            raise ValueError(f"workspace: block_topk_workspace gives {need} bytes, got {_bytes(workspace)}")
         _check("csa2_block_topk_prebuilt", _L.csa2_block_topk_prebuilt(
             _ptr(scores), _ptr(block_max), n_q, width, _ptr(q_nvis), 8, M, K, _ptr(pool_out), _ptr(topk_out),
             _ptr(workspace), _bytes(workspace), _stream(stream)))

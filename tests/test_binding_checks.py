@@ -114,6 +114,14 @@ def test_append_index_checks(fake):
                  ("scores", z((n_q, width + 1), F32)), ("block_max", z((n_q, 1), F32)),
                  ("q_idx", z((n_q, 32, 60), U8))):
         expect_bad(fake, csa2.append_index_score, **{**good, k: v})
+    # the variant that counts the selection's first pass: bf16 query, block maxima, a large
+    # enough selection workspace
+    sel = {**good, "sel_workspace": z((n_q * 4096 * 4,), U8)}
+    expect_ok(fake, csa2.append_index_score, **sel)
+    assert fake.calls[-1] == "csa2_append_index_score_sel"
+    for k, v in (("q_idx", z((n_q, 32, 68), U8)), ("pack_q", True), ("want_block_max", False),
+                 ("sel_workspace", z((n_q * 4096 * 4 - 4,), U8))):
+        expect_bad(fake, csa2.append_index_score, **{**sel, k: v})
     mean = {**good, "mean_cache": z((width // 32, 2176), U8), "mean_base": z((n_q,), I64)}
     expect_ok(fake, csa2.append_mean_index_score, **mean)
     expect_bad(fake, csa2.append_mean_index_score, **{**mean, "mean_base": z((n_q + 1,), I64)})
@@ -133,6 +141,14 @@ def test_block_topk_checks(fake):
     expect_ok(fake, csa2.block_topk, **cand)
     expect_bad(fake, csa2.block_topk, **{**cand, "scores": z((n_q, 8 * M + 8), F32)})
     expect_bad(fake, csa2.block_topk, **{**cand, "pool_blocks": z((n_q + 1, M), I32)})
+    # the selection after the first-pass handoff: Full mode, block maxima and a full workspace
+    ws = z((csa2.block_topk_workspace(n_q, width, M, K),), U8)
+    pre = {**good, "workspace": ws, "hist_ready": True}
+    expect_ok(fake, csa2.block_topk, **pre)
+    assert fake.calls[-1] == "csa2_block_topk_prebuilt"
+    for k, v in (("block_max", None), ("workspace", None), ("workspace", z((ws.numel() - 4,), U8))):
+        expect_bad(fake, csa2.block_topk, **{**pre, k: v})
+    expect_bad(fake, csa2.block_topk, **{**cand, "workspace": ws, "hist_ready": True})
     pool_only = dict(scores=None, q_nvis=z((n_q,), I32), K=K, M=M, block_max=z((n_q, 500), F32),
                      pool_out=z((n_q, M), I32), want_topk=False)
     expect_ok(fake, csa2.block_topk, **pool_only)
